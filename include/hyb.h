@@ -1,0 +1,227 @@
+/*
+ * hyb.h - C ABI of the MI355X (gfx950) hybrid compressed/sparse + sliding-window attention step.
+ *
+ * The method (DeepSeek-V4-style hybrid attention) is described on these pages:
+ *   [vLLM]  "Day-0 support for DeepSeek V4 Pro and Flash on vLLM" - the "four moves" list
+ *           (shared K/V + inverse RoPE; c4a / c128a KV compression; DeepSeek Sparse Attention
+ *           over compressed tokens; short sliding window), the fp8 attention cache / fp4 indexer
+ *           cache remark, and the "vLLM side" list (one logical block of 256 native positions
+ *           for every compression rate; fused compressor + RMSNorm + RoPE + cache insert; fused
+ *           Q-norm + KV RoPE + K insert).
+ *   [SGLang] "DeepSeek-V4 launch review" (SGLang/Miles day-0 blog), section "Shadow Radix":
+ *           each layer is sliding-window attention over the newest 128 raw tokens plus either
+ *           C4 (top-512 sparse over 4:1 compressed KV) or C128 (dense over 128:1 compressed KV);
+ *           each compression layer keeps its in-progress compression state in a state pool.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a device pointer unless it says "host". The caller owns all memory:
+ *     inputs, outputs, pools, block tables, state and workspace. The library never allocates,
+ *     frees or synchronises, keeps no global mutable state (apart from a thread-local error
+ *     string) and is re-entrant.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Return value: HYB_OK, or an error code. All argument checks run on the host before any
+ *     HIP call, so a non-OK status means nothing was enqueued and outputs are untouched
+ *     (HYB_ELAUNCH: a launch failed; earlier kernels of the same call may have run).
+ *     hyb_last_error() describes the most recent failure on the calling thread.
+ *   - Faults inside kernels surface at the caller's next synchronisation. Kernels never
+ *     dereference a block whose table entry is negative or >= num_blocks: such entries are
+ *     treated as absent (skipped on write, masked out on read).
+ *   - Positions are absolute, 0-based raw-token positions. A query at position p sees the
+ *     raw window [max(0, p - window + 1), p] and the compressed entries 0 .. n_vis(p) - 1 with
+ *     n_vis(p) = ceil(max(0, p - window + 1) / ratio) (every complete group that holds at least
+ *     one position older than the window).
+ *   - RoPE rotates the last rope_dim dims in adjacent pairs: pair i = (D - rope_dim + 2i,
+ *     D - rope_dim + 2i + 1) turns by pos * rope_base^(-2i / rope_dim). Angles are formed and
+ *     reduced in double precision.
+ */
+#ifndef HYB_H
+#define HYB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYB_ABI_VERSION 1
+
+/* [vLLM] "vLLM side": one logical block = 256 native (raw) positions for every compression
+ * rate, i.e. 256 raw entries, 64 C4 entries or 2 C128 entries. */
+#define HYB_BLOCK_POSITIONS 256
+/* Largest top-k the selector supports ([SGLang] "Shadow Radix" uses k = 512). */
+#define HYB_KMAX 2048
+
+typedef enum hyb_status {
+  HYB_OK = 0,
+  HYB_EINVAL = 1,     /* bad argument (NULL pointer, size, ratio, dtype mismatch, ...) */
+  HYB_ENOTSUP = 2,    /* valid but not implemented (dtype / shape combination) */
+  HYB_EWORKSPACE = 3, /* workspace missing or smaller than the *_workspace_bytes() result */
+  HYB_ELAUNCH = 4     /* a HIP launch failed */
+} hyb_status;
+
+/* Element storage types. FP8_E4M3 = OCP E4M3 ("fn": no inf, max 448) with one float32 scale per
+ * entry; FP4_E2M1 = OCP MX E2M1 with one E8M0 scale byte per 32 elements (value =
+ * e2m1 * 2^(scale - 127)). [vLLM]: "fp8 attention cache + fp4 indexer cache". */
+typedef enum hyb_dtype {
+  HYB_F32 = 0,
+  HYB_BF16 = 1,
+  HYB_FP8_E4M3 = 2,
+  HYB_FP4_E2M1 = 3
+} hyb_dtype;
+
+/* Compressor pooling of the r raw tokens of a group: arithmetic mean, or softmax over one scalar
+ * logit per raw position followed by the weighted sum. */
+typedef enum hyb_pool_mode { HYB_POOL_MEAN = 0, HYB_POOL_SOFTMAX_GATE = 1 } hyb_pool_mode;
+
+/* A paged pool ([vLLM] "unified hybrid KV cache"; [SGLang] "three heterogeneous KV pools").
+ * Entry g of a pool with compression `ratio` lives in logical block floor(g * ratio / 256), slot
+ * g mod (256 / ratio). Physical layout, all row-major, contiguous:
+ *   data  F32/BF16: [num_blocks][256/ratio][dim] elements
+ *         FP8_E4M3: [num_blocks][256/ratio][dim] bytes
+ *         FP4_E2M1: [num_blocks][256/ratio][dim/2] bytes, element 2j in the low nibble of byte j
+ *   scale FP8_E4M3: float [num_blocks][256/ratio];  FP4_E2M1: uint8 [num_blocks][256/ratio][dim/32];
+ *         NULL otherwise.
+ *   block_table: int32 [batch][max_blocks], logical -> physical block, negative = absent.
+ * The descriptor itself is read on the host during the call and may be freed afterwards. */
+typedef struct hyb_paged {
+  void* data;
+  void* scale;
+  const int32_t* block_table;
+  int32_t dtype;      /* hyb_dtype */
+  int32_t dim;
+  int32_t ratio;      /* 1 (raw sliding-window entries), 4 (C4) or 128 (C128) */
+  int32_t num_blocks; /* physical blocks in data */
+  int32_t max_blocks; /* columns of block_table */
+  int32_t reserved;   /* must be 0 */
+} hyb_paged;
+
+int32_t hyb_abi_version(void);
+const char* hyb_status_str(int32_t status);
+/* Thread-local description of the last non-OK status returned on this thread (host string,
+ * owned by the library, valid until the next call on the thread). */
+const char* hyb_last_error(void);
+
+/* --------------------------------------------------------------------------------------------
+ * hyb_compress - KV compressor: pool -> RMSNorm -> RoPE -> paged insert, with a state ring.
+ * [vLLM] "c4a / c128a KV compression" and the fused "compressor + RMSNorm + RoPE + cache insert";
+ * [SGLang] "Shadow Radix": in-progress groups wait in a per-layer compression-state pool.
+ *
+ * New raw tokens x[cu_seqlens[b] .. cu_seqlens[b+1]) of sequence b sit at positions
+ * start_pos[b] + i. Every group g = floor(pos / ratio) completed by them is written to `out` as
+ *   entry g = RoPE(RMSNorm(Pool(x_{g*r} .. x_{g*r+r-1})), g*r + r - 1),
+ * RMSNorm over all dim dims with eps and unit gain, the pool per `mode`. Tokens of a group that
+ * started in an earlier call are read from the state ring; the tokens of the trailing incomplete
+ * group are written to it (slot = pos mod ratio). One call serves decode (one token per sequence)
+ * and chunked prefill; calls for one sequence must come in position order.
+ *   x             [T][dim], x_dtype F32 or BF16 (T = cu_seqlens[batch])
+ *   gate_logits   float [T] for HYB_POOL_SOFTMAX_GATE; NULL for HYB_POOL_MEAN
+ *   cu_seqlens    int32 [batch + 1], non-decreasing, cu_seqlens[0] = 0
+ *   start_pos     int32 [batch], position of each sequence's first new token
+ *   max_new_tokens host bound on cu_seqlens[b+1] - cu_seqlens[b] (sizes the grid)
+ *   state         float [batch][ratio][dim] raw tokens of the in-progress group
+ *   state_logits  float [batch][ratio] (gate mode), NULL for mean
+ *   out           host descriptor of the C4 / C128 pool (ratio 4 or 128, dtype F32 or BF16,
+ *                 dim = x's dim, block_table rows indexed by b)
+ * ------------------------------------------------------------------------------------------ */
+int32_t hyb_compress(const void* x, int32_t x_dtype, const float* gate_logits,
+                     const int32_t* cu_seqlens, const int32_t* start_pos, int32_t batch,
+                     int32_t max_new_tokens, float* state, float* state_logits, int32_t mode,
+                     const hyb_paged* out, int32_t rope_dim, double rope_base, float eps,
+                     void* stream);
+
+/* --------------------------------------------------------------------------------------------
+ * hyb_swa_insert - raw sliding-window entries s_t = RoPE(x_t, t) (no norm) written to the raw
+ * pool (ratio 1) at position t. The "KV RoPE + K insert" step of [vLLM]'s fused-kernel list.
+ * Arguments as in hyb_compress; swa->dtype F32 or BF16.
+ * ------------------------------------------------------------------------------------------ */
+int32_t hyb_swa_insert(const void* x, int32_t x_dtype, const int32_t* cu_seqlens,
+                       const int32_t* start_pos, int32_t batch, int32_t max_new_tokens,
+                       const hyb_paged* swa, int32_t rope_dim, double rope_base, void* stream);
+
+/* --------------------------------------------------------------------------------------------
+ * hyb_index_score - indexer scores over the visible compressed entries.
+ * [vLLM] "DeepSeek Sparse Attention over compressed tokens"; [SGLang] "indexer top-k".
+ *   score[i][g] = sum_h w[i][h] * max(0, q_idx[i][h] . key_g), g = 0 .. n_vis(q_pos[i]) - 1,
+ * keys from `idx_pool` rows of sequence q_seq[i]. Entries g >= n_vis are not written.
+ *   q_idx   [n_q][n_heads][idx_pool->dim], q_dtype F32 or BF16
+ *   w       float [n_q][n_heads]
+ *   q_seq   int32 [n_q] (NULL = identity);  q_pos int32 [n_q]
+ *   max_pos host bound on q_pos;  scores float [n_q][scores_ld], scores_ld >= n_vis(max_pos)
+ * idx_pool: dtype F32, BF16 or FP4_E2M1 (dim % 32 == 0), ratio 4 or 128.
+ * ------------------------------------------------------------------------------------------ */
+int32_t hyb_index_score(const void* q_idx, int32_t q_dtype, const float* w, const int32_t* q_seq,
+                        const int32_t* q_pos, int32_t n_q, int32_t n_heads, int32_t max_pos,
+                        int32_t window, const hyb_paged* idx_pool, float* scores,
+                        int64_t scores_ld, void* stream);
+
+/* --------------------------------------------------------------------------------------------
+ * hyb_topk - exact top-k per row: the first min(k, len[i]) indices of row i under the order
+ * (score descending, index ascending), -0.0 equal to +0.0, written ascending and padded with -1.
+ * [SGLang] "Shadow Radix": C4 keeps the top-512 compressed entries.
+ *   scores float [n_q][scores_ld];  lengths int32 [n_q] (valid prefix of each row, <= max_len)
+ *   out_idx int32 [n_q][k];  1 <= k <= HYB_KMAX.  Scores must not be NaN.
+ * ------------------------------------------------------------------------------------------ */
+int32_t hyb_topk(const float* scores, int64_t scores_ld, const int32_t* lengths, int32_t n_q,
+                 int32_t max_len, int32_t k, int32_t* out_idx, void* stream);
+
+/* --------------------------------------------------------------------------------------------
+ * hyb_index_topk - hyb_index_score followed by hyb_topk over n_vis(q_pos[i]) entries; the
+ * scores live in the workspace (size from hyb_index_topk_workspace_bytes with the same n_q,
+ * max_pos, window and ratio).
+ * ------------------------------------------------------------------------------------------ */
+size_t hyb_index_topk_workspace_bytes(int32_t n_q, int32_t max_pos, int32_t window,
+                                      int32_t ratio);
+int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const int32_t* q_seq,
+                       const int32_t* q_pos, int32_t n_q, int32_t n_heads, int32_t max_pos,
+                       int32_t window, const hyb_paged* idx_pool, int32_t k, int32_t* out_idx,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------------
+ * hyb_attn_decode - one query token per sequence, p = seq_lens[b] - 1.
+ * [vLLM] "Shared K/V + inverse RoPE", "short sliding window"; [SGLang] "Shadow Radix": SWA over
+ * the newest `window` raw tokens plus either the selected C4 entries (topk_idx != NULL, sparse)
+ * or every visible compressed entry (topk_idx == NULL, dense; the C128 case).
+ * Per head h, with keys kappa_j = the raw window entries (positions ascending) then the chosen
+ * compressed entries:  z_j = softmax_scale * q_h . kappa_j,  o_h = sum_j softmax(z)_j kappa_j
+ * (values are the keys: one shared K=V head), then out_h = RoPE(o_h, -p).
+ *   q        [batch][n_heads][dim] already rotated at p;  q_dtype F32 or BF16
+ *   seq_lens int32 [batch] (>= 1);  max_seq_len host bound on seq_lens
+ *   swa      raw pool (ratio 1);  comp compressed pool (ratio 4 or 128); same dtype, dim as q;
+ *            pool dtype F32 (q F32), BF16 or FP8_E4M3 (q BF16)
+ *   topk_idx int32 [batch][k] entries of comp (negative = unused), or NULL
+ *   out      [batch][n_heads][dim], out_dtype F32 or BF16
+ *   workspace size from hyb_attn_decode_workspace_bytes with the same batch, n_heads, dim,
+ *            max_seq_len, comp ratio, k (0 when topk_idx is NULL) and window.
+ * ------------------------------------------------------------------------------------------ */
+size_t hyb_attn_decode_workspace_bytes(int32_t batch, int32_t n_heads, int32_t dim,
+                                       int32_t max_seq_len, int32_t comp_ratio, int32_t k,
+                                       int32_t window);
+int32_t hyb_attn_decode(const void* q, int32_t q_dtype, const int32_t* seq_lens, int32_t batch,
+                        int32_t n_heads, int32_t max_seq_len, const hyb_paged* swa,
+                        const hyb_paged* comp, const int32_t* topk_idx, int32_t k, int32_t window,
+                        float softmax_scale, int32_t rope_dim, double rope_base, void* out,
+                        int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------------
+ * hyb_attn_prefill - causal attention for a chunk of query tokens: query i of sequence q_seq[i]
+ * at position q_pos[i] attends to its own window and its own top-k row (or, with topk_idx NULL,
+ * to every compressed entry visible at q_pos[i]). Same arithmetic and pools as hyb_attn_decode.
+ *   q [n_q][n_heads][dim] rotated at q_pos;  q_seq int32 [n_q] (NULL = identity);  q_pos int32 [n_q]
+ *   max_pos host bound on q_pos;  topk_idx int32 [n_q][k] or NULL;  out [n_q][n_heads][dim]
+ * ------------------------------------------------------------------------------------------ */
+size_t hyb_attn_prefill_workspace_bytes(int32_t n_q, int32_t n_heads, int32_t dim,
+                                        int32_t max_pos, int32_t comp_ratio, int32_t k,
+                                        int32_t window);
+int32_t hyb_attn_prefill(const void* q, int32_t q_dtype, const int32_t* q_seq,
+                         const int32_t* q_pos, int32_t n_q, int32_t n_heads, int32_t max_pos,
+                         const hyb_paged* swa, const hyb_paged* comp, const int32_t* topk_idx,
+                         int32_t k, int32_t window, float softmax_scale, int32_t rope_dim,
+                         double rope_base, void* out, int32_t out_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYB_H */

@@ -26,5 +26,6 @@ torch.float8_e4m3fn), hand-computed values and brute force. Functions or reading
 pin are marked "parity unpinned" in their docstrings.
 """
 
-from .formats import bf16_bits_to_f64, e4m3fn_to_f64, e2m1_to_f64, e8m0_to_f64  # noqa: F401
+from .formats import (bf16_bits_to_f64, e2m1_to_f64, e4m3fn_to_f64, e8m0_to_f64,  # noqa: F401
+                      round_to_bf16_bits)
 from .hyb_oracle import *  # noqa: F401,F403

@@ -23,6 +23,15 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def round_to_bf16_bits(x) -> np.ndarray:
+    """float64 -> bfloat16 bit patterns: first to the nearest float32, then round-to-nearest-even
+    on the upper 16 bits (how a bf16 cache stores a value computed in wider precision)."""
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    nan = np.isnan(np.asarray(x, dtype=np.float64))
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return np.where(nan, np.uint16(0x7FC0), r)
+
+
 def e4m3fn_to_f64(code) -> np.ndarray:
     """OCP FP8 E4M3 codes (uint8) -> float64. Exact."""
     c = np.asarray(code).astype(np.uint8).astype(np.int64)

@@ -30,12 +30,13 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from .formats import bf16_bits_to_f64, e4m3fn_to_f64, unpack_fp4_row
+from .formats import bf16_bits_to_f64, e4m3fn_to_f64, round_to_bf16_bits, unpack_fp4_row
 
 __all__ = [
     "BLOCK_POSITIONS",
     "OraclePool",
     "pool_entries",
+    "logical_pool",
     "rope",
     "rmsnorm",
     "pool_tokens",
@@ -67,6 +68,7 @@ class OraclePool:
     """A paged pool as stored.
 
     data:  f32  -> float32 [num_blocks, 256 // ratio, dim]
+           f64  -> float64, same shape (values kept unrounded)
            bf16 -> uint16 bit patterns, same shape
            fp8  -> uint8 E4M3 codes, same shape; scale float32 [num_blocks, 256 // ratio]
            fp4  -> uint8 packed pairs [num_blocks, 256 // ratio, dim // 2];
@@ -82,6 +84,31 @@ class OraclePool:
     scale: Optional[np.ndarray] = None
 
 
+def logical_pool(entries_per_seq, ratio: int, dtype: str = "f64") -> OraclePool:
+    """Lay out per-sequence logical entry arrays [n_b, dim] as a pool with blocks in order.
+
+    dtype "f64" keeps the values; "bf16" stores them rounded to bfloat16 (nearest-even).
+    """
+    per_block = BLOCK_POSITIONS // ratio
+    dim = int(np.asarray(entries_per_seq[0]).shape[1])
+    nblk = [max(1, -(-len(e) // per_block)) for e in entries_per_seq]
+    total = sum(nblk)
+    data = np.zeros((total, per_block, dim), np.float64)
+    table = np.full((len(entries_per_seq), max(nblk)), -1, np.int32)
+    nxt = 0
+    for b, e in enumerate(entries_per_seq):
+        e = np.asarray(e, np.float64)
+        for lb in range(nblk[b]):
+            table[b, lb] = nxt
+            chunk = e[lb * per_block:(lb + 1) * per_block]
+            data[nxt, :len(chunk)] = chunk
+            nxt += 1
+    if dtype == "bf16":
+        return OraclePool(data=round_to_bf16_bits(data), dtype="bf16", dim=dim, ratio=ratio,
+                          block_table=table)
+    return OraclePool(data=data, dtype="f64", dim=dim, ratio=ratio, block_table=table)
+
+
 def pool_entries(pool: OraclePool, seq: int, gs: Sequence[int]) -> np.ndarray:
     """Entries g of sequence ``seq`` as float64 [len(gs), dim].
 
@@ -94,7 +121,7 @@ def pool_entries(pool: OraclePool, seq: int, gs: Sequence[int]) -> np.ndarray:
         phys = int(pool.block_table[seq, lb])
         if phys < 0:
             raise ValueError(f"entry {g} of sequence {seq} lies in an absent block")
-        if pool.dtype == "f32":
+        if pool.dtype in ("f32", "f64"):
             out[n] = pool.data[phys, slot].astype(np.float64)
         elif pool.dtype == "bf16":
             out[n] = bf16_bits_to_f64(pool.data[phys, slot])

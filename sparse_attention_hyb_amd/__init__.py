@@ -1,1 +1,246 @@
-"""MI355X-native hybrid compressed/sparse + sliding-window attention (binding added with the C ABI)."""
+"""MI355X-native hybrid compressed/sparse + sliding-window attention.
+
+Thin Python binding of the C ABI in ``include/hyb.h`` (libhyb.so, HIP kernels for gfx950).
+Each function has the C entry point's name and only marshals arguments: torch tensors become
+device pointers, pools become ``hyb_paged`` descriptors, the current torch stream is passed
+through. Every step of the method runs in the library's kernels. Without the built library
+every call raises: there is no fallback.
+
+Pools are any object with the attributes ``data``, ``scale``, ``block_table`` (torch tensors),
+``dtype`` ('f32' | 'bf16' | 'fp8' | 'fp4'), ``dim`` and ``ratio`` - e.g.
+``sparse_attention_hyb_amd.workloads.PagedTensors``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyb.so")
+
+HYB_OK, HYB_EINVAL, HYB_ENOTSUP, HYB_EWORKSPACE, HYB_ELAUNCH = 0, 1, 2, 3, 4
+F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
+POOL_MEAN, POOL_SOFTMAX_GATE = 0, 1
+BLOCK_POSITIONS = 256
+KMAX = 2048
+DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp4": FP4_E2M1}
+
+EXPORTS = (
+    "hyb_abi_version", "hyb_status_str", "hyb_last_error", "hyb_compress", "hyb_swa_insert",
+    "hyb_index_score", "hyb_topk", "hyb_index_topk_workspace_bytes", "hyb_index_topk",
+    "hyb_attn_decode_workspace_bytes", "hyb_attn_decode", "hyb_attn_prefill_workspace_bytes",
+    "hyb_attn_prefill",
+)
+
+
+class HybError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [{status}]")
+        self.status = status
+
+
+class hyb_paged(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("dim", ctypes.c_int32),
+        ("ratio", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+_P, _I32, _I64, _SZ, _D, _F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                               ctypes.c_double, ctypes.c_float)
+_PP = ctypes.POINTER(hyb_paged)
+_SIGS = {
+    "hyb_abi_version": (_I32, []),
+    "hyb_status_str": (ctypes.c_char_p, [_I32]),
+    "hyb_last_error": (ctypes.c_char_p, []),
+    "hyb_compress": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _P, _P, _I32, _PP, _I32, _D, _F, _P]),
+    "hyb_swa_insert": (_I32, [_P, _I32, _P, _P, _I32, _I32, _PP, _I32, _D, _P]),
+    "hyb_index_score": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _PP, _P, _I64, _P]),
+    "hyb_topk": (_I32, [_P, _I64, _P, _I32, _I32, _I32, _P, _P]),
+    "hyb_index_topk_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "hyb_index_topk": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _PP, _I32, _P, _P, _SZ, _P]),
+    "hyb_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "hyb_attn_decode": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F, _I32,
+                               _D, _P, _I32, _P, _SZ, _P]),
+    "hyb_attn_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "hyb_attn_prefill": (_I32, [_P, _I32, _P, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F,
+                                _I32, _D, _P, _I32, _P, _SZ, _P]),
+}
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libhyb.so (built by ``python -m sparse_attention_hyb_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"libhyb.so is not built ({p}); run python -m sparse_attention_hyb_amd.build")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != HYB_OK:
+        lib = load()
+        raise HybError(status, lib.hyb_last_error().decode() or lib.hyb_status_str(status).decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _tdtype(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"tensor dtype {t.dtype} is not float32 or bfloat16")
+
+
+def paged(pool) -> hyb_paged:
+    """Pool object -> hyb_paged descriptor (keeps no reference: hold the tensors yourself)."""
+    return hyb_paged(
+        data=_ptr(pool.data), scale=_ptr(pool.scale), block_table=_ptr(pool.block_table),
+        dtype=DTYPE_CODES[pool.dtype], dim=int(pool.dim), ratio=int(pool.ratio),
+        num_blocks=int(pool.data.shape[0]), max_blocks=int(pool.block_table.shape[1]), reserved=0)
+
+
+def _empty_workspace(nbytes: int, device):
+    import torch
+    return torch.empty(max(1, int(nbytes)), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------------------------
+def hyb_abi_version() -> int:
+    return load().hyb_abi_version()
+
+
+def hyb_compress(x, cu_seqlens, start_pos, max_new_tokens: int, state, out_pool, rope_dim: int,
+                 rope_base: float = 10000.0, eps: float = 1e-6, gate_logits=None,
+                 state_logits=None, stream=None) -> None:
+    """Compressor: see hyb_compress in include/hyb.h. Mean pooling unless gate_logits is given."""
+    mode = POOL_SOFTMAX_GATE if gate_logits is not None else POOL_MEAN
+    d = paged(out_pool)
+    _check(load().hyb_compress(_ptr(x), _tdtype(x), _ptr(gate_logits), _ptr(cu_seqlens),
+                               _ptr(start_pos), int(start_pos.shape[0]), int(max_new_tokens),
+                               _ptr(state), _ptr(state_logits), mode, ctypes.byref(d),
+                               int(rope_dim), float(rope_base), float(eps), _stream(stream)))
+
+
+def hyb_swa_insert(x, cu_seqlens, start_pos, max_new_tokens: int, swa_pool, rope_dim: int,
+                   rope_base: float = 10000.0, stream=None) -> None:
+    d = paged(swa_pool)
+    _check(load().hyb_swa_insert(_ptr(x), _tdtype(x), _ptr(cu_seqlens), _ptr(start_pos),
+                                 int(start_pos.shape[0]), int(max_new_tokens), ctypes.byref(d),
+                                 int(rope_dim), float(rope_base), _stream(stream)))
+
+
+def hyb_index_score(q_idx, w, q_pos, max_pos: int, idx_pool, scores, window: int = 128,
+                    q_seq=None, stream=None) -> None:
+    d = paged(idx_pool)
+    _check(load().hyb_index_score(_ptr(q_idx), _tdtype(q_idx), _ptr(w), _ptr(q_seq), _ptr(q_pos),
+                                  int(q_idx.shape[0]), int(q_idx.shape[1]), int(max_pos),
+                                  int(window), ctypes.byref(d), _ptr(scores),
+                                  int(scores.stride(0)), _stream(stream)))
+
+
+def hyb_topk(scores, lengths, max_len: int, k: int, out_idx, stream=None) -> None:
+    _check(load().hyb_topk(_ptr(scores), int(scores.stride(0)), _ptr(lengths),
+                           int(scores.shape[0]), int(max_len), int(k), _ptr(out_idx),
+                           _stream(stream)))
+
+
+def hyb_index_topk_workspace_bytes(n_q: int, max_pos: int, window: int, ratio: int) -> int:
+    return int(load().hyb_index_topk_workspace_bytes(int(n_q), int(max_pos), int(window), int(ratio)))
+
+
+def hyb_index_topk(q_idx, w, q_pos, max_pos: int, idx_pool, k: int, out_idx, window: int = 128,
+                   q_seq=None, workspace=None, stream=None) -> None:
+    n_q = int(q_idx.shape[0])
+    need = hyb_index_topk_workspace_bytes(n_q, max_pos, window, idx_pool.ratio)
+    if workspace is None:
+        workspace = _empty_workspace(need, q_idx.device)
+    d = paged(idx_pool)
+    _check(load().hyb_index_topk(_ptr(q_idx), _tdtype(q_idx), _ptr(w), _ptr(q_seq), _ptr(q_pos),
+                                 n_q, int(q_idx.shape[1]), int(max_pos), int(window),
+                                 ctypes.byref(d), int(k), _ptr(out_idx), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def hyb_attn_decode_workspace_bytes(batch: int, n_heads: int, dim: int, max_seq_len: int,
+                                    comp_ratio: int, k: int, window: int = 128) -> int:
+    return int(load().hyb_attn_decode_workspace_bytes(int(batch), int(n_heads), int(dim),
+                                                      int(max_seq_len), int(comp_ratio), int(k),
+                                                      int(window)))
+
+
+def hyb_attn_decode(q, seq_lens, max_seq_len: int, swa_pool, comp_pool, out, topk_idx=None,
+                    k: int = 0, window: int = 128, softmax_scale: Optional[float] = None,
+                    rope_dim: int = 64, rope_base: float = 10000.0, workspace=None,
+                    stream=None) -> None:
+    b, h, dim = (int(s) for s in q.shape)
+    if topk_idx is not None and not k:
+        k = int(topk_idx.shape[1])
+    scale = float(softmax_scale) if softmax_scale is not None else dim ** -0.5
+    if workspace is None:
+        need = hyb_attn_decode_workspace_bytes(b, h, dim, max_seq_len, comp_pool.ratio,
+                                               k if topk_idx is not None else 0, window)
+        workspace = _empty_workspace(need, q.device)
+    ds, dc = paged(swa_pool), paged(comp_pool)
+    _check(load().hyb_attn_decode(_ptr(q), _tdtype(q), _ptr(seq_lens), b, h, int(max_seq_len),
+                                  ctypes.byref(ds), ctypes.byref(dc), _ptr(topk_idx), int(k),
+                                  int(window), scale, int(rope_dim), float(rope_base), _ptr(out),
+                                  _tdtype(out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def hyb_attn_prefill_workspace_bytes(n_q: int, n_heads: int, dim: int, max_pos: int,
+                                     comp_ratio: int, k: int, window: int = 128) -> int:
+    return int(load().hyb_attn_prefill_workspace_bytes(int(n_q), int(n_heads), int(dim),
+                                                       int(max_pos), int(comp_ratio), int(k),
+                                                       int(window)))
+
+
+def hyb_attn_prefill(q, q_pos, max_pos: int, swa_pool, comp_pool, out, topk_idx=None, k: int = 0,
+                     q_seq=None, window: int = 128, softmax_scale: Optional[float] = None,
+                     rope_dim: int = 64, rope_base: float = 10000.0, workspace=None,
+                     stream=None) -> None:
+    n_q, h, dim = (int(s) for s in q.shape)
+    if topk_idx is not None and not k:
+        k = int(topk_idx.shape[1])
+    scale = float(softmax_scale) if softmax_scale is not None else dim ** -0.5
+    if workspace is None:
+        need = hyb_attn_prefill_workspace_bytes(n_q, h, dim, max_pos, comp_pool.ratio,
+                                                k if topk_idx is not None else 0, window)
+        workspace = _empty_workspace(need, q.device)
+    ds, dc = paged(swa_pool), paged(comp_pool)
+    _check(load().hyb_attn_prefill(_ptr(q), _tdtype(q), _ptr(q_seq), _ptr(q_pos), n_q, h,
+                                   int(max_pos), ctypes.byref(ds), ctypes.byref(dc),
+                                   _ptr(topk_idx), int(k), int(window), scale, int(rope_dim),
+                                   float(rope_base), _ptr(out), _tdtype(out), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -1,0 +1,118 @@
+// Device-side helpers shared by the HIP kernels of the hybrid attention library (gfx950 only).
+//
+// Storage formats (OCP E4M3 with a float32 scale per entry, OCP MX E2M1 with an E8M0 scale per
+// 32 elements), the paged-pool address rule (one logical block = 256 native positions for every
+// compression rate, per the "vLLM side" list of the vLLM DeepSeek-V4 day-0 post), the visibility
+// rule and RoPE angles (formed and reduced in double precision).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hyb_internal.h"
+
+namespace hyb {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round-to-nearest-even float -> bf16 bits (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two floats -> packed bf16x2 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+}
+
+// OCP E4M3 (no inf, max 448, NaN = S.1111.111) -> float, exact. Normal codes map straight onto a
+// bf16 bit pattern (exponent + 120, mantissa << 4); subnormals are m * 2^-9.
+__device__ __forceinline__ float fp8_to_f32(uint32_t c) {
+  uint32_t u = c & 0x7fu;
+  float mag = (u >= 8u) ? __uint_as_float(((u << 4) + 0x3c00u) << 16) : (float)u * 0x1p-9f;
+  if (u == 0x7fu) mag = __builtin_nanf("");
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// E4M3 code -> bf16 bits, exact (every finite E4M3 value is a bf16 value).
+__device__ __forceinline__ uint32_t fp8_to_bf16(uint32_t c) {
+  return __float_as_uint(fp8_to_f32(c)) >> 16;
+}
+
+// OCP MX E2M1 nibble -> float (without its block scale): 0, .5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float fp4_to_f32(uint32_t nib) {
+  uint32_t m = nib & 7u;
+  float mag = (m < 2u) ? 0.5f * (float)m
+                       : __uint_as_float((((m >> 1) + 126u) << 23) | ((m & 1u) << 22));
+  return (nib & 8u) ? -mag : mag;
+}
+
+// E8M0 scale byte -> 2^(e - 127) (255 is not produced by the quantiser; it decodes as inf here).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return e == 0u ? 0x1p-127f : __uint_as_float(e << 23);
+}
+
+// Index of entry g of sequence `seq` in the flattened [num_blocks * per_block] entry array, or -1
+// when its block is absent or out of range (then nothing is read or written).
+__device__ __forceinline__ int64_t entry_index(const PoolDev& p, int seq, int g) {
+  if (g < 0) return -1;
+  int lb = g / p.per_block;
+  if (lb >= p.max_blocks) return -1;
+  int phys = p.block_table[(int64_t)seq * p.max_blocks + lb];
+  if (phys < 0 || phys >= p.num_blocks) return -1;
+  return (int64_t)phys * p.per_block + (g - lb * p.per_block);
+}
+
+__device__ __forceinline__ int window_start(int p, int window) {
+  int ws = p - window + 1;
+  return ws > 0 ? ws : 0;
+}
+
+// Compressed entries visible to a query at position p: ceil(window_start / ratio).
+__device__ __forceinline__ int n_visible(int p, int ratio, int window) {
+  return (window_start(p, window) + ratio - 1) / ratio;
+}
+
+// cos / sin of pos * base^(-2i / rope_dim), formed and reduced in double precision.
+__device__ __forceinline__ void rope_cs(double pos, int i, int rope_dim, double base, float* c,
+                                        float* s) {
+  double theta = exp(-2.0 * (double)i / (double)rope_dim * log(base));
+  double sn, cs;
+  sincos(pos * theta, &sn, &cs);
+  *c = (float)cs;
+  *s = (float)sn;
+}
+
+// Query i -> (sequence, position).
+__device__ __forceinline__ void query_at(const QueryDev& q, int i, int* seq, int* pos) {
+  if (q.seq_lens) {
+    *seq = i;
+    *pos = q.seq_lens[i] - 1;
+  } else {
+    *seq = q.q_seq ? q.q_seq[i] : i;
+    *pos = q.q_pos[i];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace hyb

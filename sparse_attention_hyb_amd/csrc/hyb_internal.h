@@ -1,0 +1,126 @@
+// Internal interface between the C-ABI front end (hyb_api.cpp) and the HIP kernels.
+// Plain structs passed to kernels by value, and one launcher per kernel family. Launchers
+// assume validated arguments and return the hipError_t of their launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hyb {
+
+// A paged pool as the kernels see it (see hyb_paged in include/hyb.h).
+struct PoolDev {
+  uint8_t* data;
+  const void* scale;
+  const int32_t* block_table;
+  int32_t dtype;
+  int32_t dim;
+  int32_t ratio;
+  int32_t num_blocks;
+  int32_t max_blocks;
+  int32_t per_block;     // 256 / ratio
+  int64_t entry_bytes;   // bytes of one entry in data
+};
+
+// Query i -> (sequence, position): decode form (seq_lens != nullptr: seq = i, p = len - 1) or
+// prefill form (seq = q_seq ? q_seq[i] : i, p = q_pos[i]).
+struct QueryDev {
+  const int32_t* seq_lens;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+};
+
+enum Dtype : int32_t { F32 = 0, BF16 = 1, FP8 = 2, FP4 = 3 };
+
+// ---- compressor and raw-window insert -------------------------------------------------------
+struct CompressArgs {
+  const void* x;
+  int32_t x_dtype;
+  const float* gate;
+  const int32_t* cu_seqlens;
+  const int32_t* start_pos;
+  int32_t batch;
+  int32_t max_new_tokens;
+  float* state;
+  float* state_logits;
+  int32_t mode;
+  PoolDev out;
+  int32_t rope_dim;
+  double rope_base;
+  float eps;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+hipError_t launch_swa_insert(const CompressArgs& a, hipStream_t s);
+
+// ---- indexer scores -------------------------------------------------------------------------
+struct ScoreArgs {
+  const void* q;
+  int32_t q_dtype;
+  const float* w;
+  QueryDev qd;
+  int32_t n_q;
+  int32_t n_heads;
+  int32_t max_pos;
+  int32_t window;
+  PoolDev pool;
+  float* scores;
+  int64_t ld;
+};
+hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s);
+
+// ---- top-k ----------------------------------------------------------------------------------
+// Row lengths come from `lengths` or, if null, from n_visible(p_i, ratio, window) of the queries.
+struct TopkArgs {
+  const float* scores;
+  int64_t ld;
+  const int32_t* lengths;
+  QueryDev qd;
+  int32_t ratio;
+  int32_t window;
+  int32_t n_q;
+  int32_t max_len;
+  int32_t k;
+  int32_t* out;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+// ---- attention ------------------------------------------------------------------------------
+struct AttnArgs {
+  const void* q;
+  int32_t q_dtype;
+  QueryDev qd;
+  int32_t n_q;
+  int32_t n_heads;
+  int32_t dim;
+  PoolDev swa;
+  PoolDev comp;
+  const int32_t* topk;
+  int32_t k;
+  int32_t window;
+  float scale;
+  int32_t rope_dim;
+  double rope_base;
+  void* out;
+  int32_t out_dtype;
+  int32_t max_keys;   // host bound on keys per query (window + compressed)
+  // split-K plan (filled by plan_attention)
+  int32_t n_split;
+  int32_t chunk;      // keys per split
+  int32_t use_mfma;
+  float* part_o;      // [n_q][n_split][dim][n_heads]
+  float* part_ml;     // [n_q][n_split][2][n_heads]
+};
+
+// Split plan and workspace size for an attention call; identical for sizing and for launching.
+struct AttnPlan {
+  int32_t use_mfma;
+  int32_t n_split;
+  int32_t chunk;
+  size_t ws_bytes;
+};
+AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_keys,
+                        int32_t q_dtype, int32_t pool_dtype);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace hyb

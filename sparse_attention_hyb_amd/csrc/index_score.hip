@@ -1,0 +1,181 @@
+// Indexer scores over the visible compressed entries:
+//   score[i][g] = sum_h w[i][h] * max(0, q_idx[i][h] . key_g).
+// Method: vLLM DeepSeek-V4 day-0 post ("DeepSeek Sparse Attention over compressed tokens"; fp4
+// indexer cache) and the SGLang DeepSeek-V4 day-0 blog ("Shadow Radix": C4 keeps the top-512 of
+// the indexer's scores).
+//
+// Two kernels:
+//  * score_mfma: 64 heads x 128 dims, bf16 query, bf16 or fp4 (E2M1 + E8M0 per 32) keys. The
+//    step streams every visible key once (the step's dominant HBM traffic), so each wave reads
+//    its 32-key tiles straight into MFMA operand registers: no LDS round trip. S = Q . K^T runs on
+//    v_mfma_f32_32x32x16_bf16 with the 64 heads as the M dimension (two 32-row blocks) and the 32
+//    keys as N; each lane then owns one key column and 32 of its heads, so the ReLU-weighted head
+//    sum is 32 in-lane FMAs plus one cross-half add.
+//  * score_generic: any (heads x dim) <= 8192, fp32 / bf16 / fp4 - one thread per key.
+#include "common.h"
+
+namespace hyb {
+
+constexpr int kScoreKeysPerBlock = 1024;  // keys per workgroup in the MFMA kernel
+constexpr int kMfmaHeads = 64;
+constexpr int kMfmaDim = 128;
+
+__device__ __forceinline__ float canonical_zero(float v) { return v == 0.0f ? 0.0f : v; }
+
+// Eight E2M1 nibbles (one 32-bit word, element 0 in the low nibble) times a power-of-two block
+// scale -> eight bf16 values, exactly.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float sc) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float lo = fp4_to_f32((w >> (8 * j)) & 0xfu) * sc;
+    float hi = fp4_to_f32((w >> (8 * j + 4)) & 0xfu) * sc;
+    r[j] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <bool kFp4>
+__global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
+  const int i = blockIdx.y;
+  int seq, p;
+  query_at(a.qd, i, &seq, &p);
+  // rows hold n_visible(max_pos) scores; a query past max_pos is clamped to that width
+  const int nv = min(n_visible(p, a.pool.ratio, a.window), n_visible(a.max_pos, a.pool.ratio, a.window));
+  const int base = blockIdx.x * kScoreKeysPerBlock;
+  if (base >= nv) return;
+  const int end = min(nv, base + kScoreKeysPerBlock);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 31;
+  const int hf = lane >> 5;
+
+  // The contraction index d is split as d = 64*hf + 8*s + e for K-step s (0..7) and element e of
+  // a lane's 8-wide operand; query and keys use the same split, so each lane holds 64 contiguous
+  // dims of its row.
+  bf16x8 qa[2][8];
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)i * kMfmaHeads * kMfmaDim;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qa[mb][s] = *reinterpret_cast<const bf16x8*>(q + (32 * mb + col) * kMfmaDim + 64 * hf + 8 * s);
+  // weights of the 32 (head) rows this lane accumulates: row = 32*mb + 8*(r/4) + 4*hf + r%4
+  float wv[2][16];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      wv[mb][r] = a.w[(int64_t)i * kMfmaHeads + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3)];
+
+  float* out = a.scores + (int64_t)i * a.ld;
+  for (int t0 = base + wave * 32; t0 < end; t0 += 128) {
+    const int g = t0 + col;
+    const int64_t idx = g < end ? entry_index(a.pool, seq, g) : -1;
+    bf16x8 kb[8];
+    if (idx >= 0) {
+      if constexpr (!kFp4) {
+        const uint16_t* row =
+            reinterpret_cast<const uint16_t*>(a.pool.data + idx * a.pool.entry_bytes) + 64 * hf;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) kb[s] = *reinterpret_cast<const bf16x8*>(row + 8 * s);
+      } else {
+        const uint8_t* row = a.pool.data + idx * a.pool.entry_bytes + 32 * hf;
+        const uint8_t* scl = reinterpret_cast<const uint8_t*>(a.pool.scale) + idx * 4 + 2 * hf;
+        u32x4 w0 = *reinterpret_cast<const u32x4*>(row);
+        u32x4 w1 = *reinterpret_cast<const u32x4*>(row + 16);
+        const float s0 = e8m0_to_f32(scl[0]), s1 = e8m0_to_f32(scl[1]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kb[s] = fp4x8_to_bf16x8(w0[s], s0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kb[4 + s] = fp4x8_to_bf16x8(w1[s], s1);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) kb[s] = bf16x8{};
+    }
+    f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb[s], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb[s], acc1, 0, 0, 0);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      part = fmaf(wv[0][r], fmaxf(acc0[r], 0.f), part);
+      part = fmaf(wv[1][r], fmaxf(acc1[r], 0.f), part);
+    }
+    part += __shfl_xor(part, 32, 64);
+    if (hf == 0 && g < end) out[g] = canonical_zero(part);
+  }
+}
+
+// One thread per key; query rows and weights staged in LDS as float.
+__global__ __launch_bounds__(256) void score_generic(ScoreArgs a) {
+  extern __shared__ float sm[];
+  const int i = blockIdx.y;
+  int seq, p;
+  query_at(a.qd, i, &seq, &p);
+  const int nv = min(n_visible(p, a.pool.ratio, a.window), n_visible(a.max_pos, a.pool.ratio, a.window));
+  const int base = blockIdx.x * 256;
+  if (base >= nv) return;
+  const int H = a.n_heads, Dk = a.pool.dim;
+  float* qs = sm;
+  float* ws = sm + H * Dk;
+  for (int e = threadIdx.x; e < H * Dk; e += 256) {
+    int64_t off = (int64_t)i * H * Dk + e;
+    qs[e] = a.q_dtype == F32 ? reinterpret_cast<const float*>(a.q)[off]
+                             : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[off]);
+  }
+  for (int h = threadIdx.x; h < H; h += 256) ws[h] = a.w[(int64_t)i * H + h];
+  __syncthreads();
+  const int g = base + threadIdx.x;
+  if (g >= nv) return;
+  const int64_t idx = entry_index(a.pool, seq, g);
+  if (idx < 0) return;
+  const uint8_t* row = a.pool.data + idx * a.pool.entry_bytes;
+  float total = 0.f;
+  for (int h = 0; h < H; ++h) {
+    float dot = 0.f;
+    for (int d = 0; d < Dk; ++d) {
+      float kd;
+      if (a.pool.dtype == F32) {
+        kd = reinterpret_cast<const float*>(row)[d];
+      } else if (a.pool.dtype == BF16) {
+        kd = bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[d]);
+      } else {
+        uint32_t byte = row[d >> 1];
+        uint32_t nib = (d & 1) ? (byte >> 4) : (byte & 0xfu);
+        const uint8_t* scl = reinterpret_cast<const uint8_t*>(a.pool.scale) + idx * (Dk / 32);
+        kd = fp4_to_f32(nib) * e8m0_to_f32(scl[d >> 5]);
+      }
+      dot = fmaf(qs[h * Dk + d], kd, dot);
+    }
+    total = fmaf(ws[h], fmaxf(dot, 0.f), total);
+  }
+  a.scores[(int64_t)i * a.ld + g] = canonical_zero(total);
+}
+
+hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s) {
+  const int max_nv = (a.max_pos - a.window + 1 > 0)
+                         ? (a.max_pos - a.window + 1 + a.pool.ratio - 1) / a.pool.ratio
+                         : 0;
+  if (max_nv == 0 || a.n_q == 0) return hipSuccess;
+  const bool mfma = a.n_heads == kMfmaHeads && a.pool.dim == kMfmaDim && a.q_dtype == BF16 &&
+                    (a.pool.dtype == BF16 || a.pool.dtype == FP4);
+  if (mfma) {
+    dim3 grid((max_nv + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock, a.n_q);
+    if (a.pool.dtype == BF16)
+      hipLaunchKernelGGL(score_mfma<false>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(score_mfma<true>, grid, dim3(256), 0, s, a);
+  } else {
+    dim3 grid((max_nv + 255) / 256, a.n_q);
+    size_t lds = sizeof(float) * ((size_t)a.n_heads * a.pool.dim + a.n_heads);
+    hipLaunchKernelGGL(score_generic, grid, dim3(256), lds, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hyb

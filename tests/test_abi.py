@@ -1,0 +1,155 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, and its host
+validation returns the documented status before any HIP call (so fake device pointers are never
+dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_hyb_amd as hyb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000001000   # never dereferenced: every call below fails (or no-ops) in host checks
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hyb.LIB_PATH):
+        pytest.skip("libhyb.so not built")
+    return hyb.load()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hyb.h")).read()
+    return sorted(set(re.findall(r"^(?:int32_t|size_t|const char\*)\s+(hyb_\w+)\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(hyb.EXPORTS) == names
+
+
+def test_version_and_status_strings(lib):
+    assert lib.hyb_abi_version() == 1
+    assert [lib.hyb_status_str(i).decode() for i in range(5)] == [
+        "HYB_OK", "HYB_EINVAL", "HYB_ENOTSUP", "HYB_EWORKSPACE", "HYB_ELAUNCH"]
+
+
+def pool(dtype=hyb.BF16, dim=512, ratio=4, scale=True, data=FAKE, reserved=0):
+    return hyb.hyb_paged(data=data, scale=FAKE if scale else None, block_table=FAKE, dtype=dtype,
+                         dim=dim, ratio=ratio, num_blocks=8, max_blocks=8, reserved=reserved)
+
+
+def decode(lib, swa=None, comp=None, q_dtype=hyb.BF16, topk=None, k=0, window=128, ws=1 << 40,
+           heads=64, scale=0.04, max_len=1000, rope_dim=64, q=FAKE):
+    swa = swa or pool(ratio=1)
+    comp = comp or pool(ratio=128)
+    return lib.hyb_attn_decode(q, q_dtype, FAKE, 4, heads, max_len, ctypes.byref(swa),
+                               ctypes.byref(comp), topk, k, window, scale, rope_dim, 10000.0,
+                               FAKE, hyb.BF16, FAKE, ws, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), hyb.HYB_EINVAL),
+    (dict(swa=pool(ratio=4)), hyb.HYB_EINVAL),                       # raw pool must be ratio 1
+    (dict(comp=pool(ratio=1)), hyb.HYB_EINVAL),                      # compressed: 4 or 128
+    (dict(comp=pool(ratio=128, dtype=hyb.F32)), hyb.HYB_EINVAL),     # pools share a dtype
+    (dict(comp=pool(ratio=128, dim=256)), hyb.HYB_EINVAL),           # pools share a dim
+    (dict(swa=pool(ratio=1, dtype=hyb.FP8_E4M3), comp=pool(ratio=128, dtype=hyb.FP8_E4M3),
+          q_dtype=hyb.F32), hyb.HYB_ENOTSUP),                        # fp8 needs a bf16 query
+    (dict(swa=pool(ratio=1, dtype=hyb.FP8_E4M3, scale=False),
+          comp=pool(ratio=128, dtype=hyb.FP8_E4M3)), hyb.HYB_EINVAL),  # fp8 needs scales
+    (dict(swa=pool(ratio=1, dtype=hyb.FP4_E2M1), comp=pool(ratio=128, dtype=hyb.FP4_E2M1)),
+     hyb.HYB_ENOTSUP),
+    (dict(topk=FAKE, k=0), hyb.HYB_EINVAL),
+    (dict(topk=FAKE, k=hyb.KMAX + 1), hyb.HYB_EINVAL),
+    (dict(window=0), hyb.HYB_EINVAL),
+    (dict(scale=0.0), hyb.HYB_EINVAL),
+    (dict(rope_dim=63), hyb.HYB_EINVAL),
+    (dict(rope_dim=600), hyb.HYB_EINVAL),
+    (dict(heads=0), hyb.HYB_EINVAL),
+    (dict(ws=16), hyb.HYB_EWORKSPACE),
+    (dict(swa=pool(ratio=1, dim=256), comp=pool(ratio=128, dim=256)), hyb.HYB_ENOTSUP),
+    (dict(swa=pool(ratio=1, reserved=3)), hyb.HYB_EINVAL),
+    (dict(swa=pool(ratio=1, data=None)), hyb.HYB_EINVAL),
+])
+def test_attn_decode_validation(lib, kw, code):
+    assert decode(lib, **kw) == code
+    assert lib.hyb_last_error().decode().startswith("hyb_attn_decode")
+
+
+def test_attn_workspace_sizes(lib):
+    # C4 decode, 16 x 64 heads x 512 dims, 640 keys: 10 splits of 64 keys
+    ws = lib.hyb_attn_decode_workspace_bytes(16, 64, 512, 131072, 4, 512, 128)
+    assert ws == 16 * 10 * (512 * 64 + 2 * 64) * 4
+    assert lib.hyb_attn_decode_workspace_bytes(0, 64, 512, 10, 4, 512, 128) == 0
+    assert lib.hyb_attn_prefill_workspace_bytes(4096, 64, 512, 69631, 4, 512, 128) >= \
+        4096 * (512 * 64 + 128) * 4
+
+
+def test_prefill_validation(lib):
+    s, c = pool(ratio=1), pool(ratio=4)
+    st = lib.hyb_attn_prefill(FAKE, hyb.BF16, None, None, 4, 64, 100, ctypes.byref(s),
+                              ctypes.byref(c), None, 0, 128, 0.04, 64, 1e4, FAKE, hyb.BF16,
+                              FAKE, 1 << 40, None)
+    assert st == hyb.HYB_EINVAL  # q_pos is required
+    st = lib.hyb_attn_prefill(FAKE, hyb.BF16, None, FAKE, 0, 64, 100, ctypes.byref(s),
+                              ctypes.byref(c), None, 0, 128, 0.04, 64, 1e4, FAKE, hyb.BF16,
+                              None, 0, None)
+    assert st == hyb.HYB_OK      # zero queries: nothing to do, nothing launched
+
+
+def test_compress_validation(lib):
+    out = pool(ratio=4)
+
+    def call(x=FAKE, mode=hyb.POOL_MEAN, gate=None, st_logits=None, o=out, rope=64, batch=2,
+             maxnew=4, eps=1e-6, x_dtype=hyb.BF16, state=FAKE):
+        return lib.hyb_compress(x, x_dtype, gate, FAKE, FAKE, batch, maxnew, state, st_logits,
+                                mode, ctypes.byref(o), rope, 1e4, eps, None)
+
+    assert call(x=None) == hyb.HYB_EINVAL
+    assert call(state=None) == hyb.HYB_EINVAL
+    assert call(mode=7) == hyb.HYB_EINVAL
+    assert call(mode=hyb.POOL_SOFTMAX_GATE) == hyb.HYB_EINVAL         # logits missing
+    assert call(o=pool(ratio=1)) == hyb.HYB_EINVAL
+    assert call(o=pool(ratio=4, dtype=hyb.FP8_E4M3)) == hyb.HYB_ENOTSUP
+    assert call(o=pool(ratio=4, dim=4096)) == hyb.HYB_ENOTSUP
+    assert call(rope=3) == hyb.HYB_EINVAL
+    assert call(eps=-1.0) == hyb.HYB_EINVAL
+    assert call(x_dtype=hyb.FP8_E4M3) == hyb.HYB_ENOTSUP
+    assert call(batch=-1) == hyb.HYB_EINVAL
+    assert call(batch=0) == hyb.HYB_OK
+    assert call(maxnew=0) == hyb.HYB_OK
+    s = pool(ratio=1)
+    assert lib.hyb_swa_insert(FAKE, hyb.BF16, FAKE, FAKE, 2, 4, ctypes.byref(pool(ratio=4)), 64,
+                              1e4, None) == hyb.HYB_EINVAL
+    assert lib.hyb_swa_insert(FAKE, hyb.BF16, FAKE, FAKE, 0, 4, ctypes.byref(s), 64, 1e4,
+                              None) == hyb.HYB_OK
+
+
+def test_index_validation(lib):
+    ip = pool(ratio=4, dim=128)
+
+    def call(k=512, ws=1 << 40, heads=64, q_dtype=hyb.BF16, p=ip, w=FAKE):
+        return lib.hyb_index_topk(FAKE, q_dtype, w, None, FAKE, 16, heads, 131071, 128,
+                                  ctypes.byref(p), k, FAKE, FAKE, ws, None)
+
+    assert call(k=0) == hyb.HYB_EINVAL
+    assert call(k=hyb.KMAX + 1) == hyb.HYB_EINVAL
+    assert call(ws=100) == hyb.HYB_EWORKSPACE
+    assert call(w=None) == hyb.HYB_EINVAL
+    assert call(p=pool(ratio=1, dim=128)) == hyb.HYB_EINVAL
+    assert call(p=pool(ratio=4, dim=100, dtype=hyb.FP4_E2M1)) == hyb.HYB_EINVAL
+    assert call(p=pool(ratio=4, dim=128, dtype=hyb.FP8_E4M3)) == hyb.HYB_ENOTSUP
+    assert call(heads=128, p=pool(ratio=4, dim=128, dtype=hyb.F32)) == hyb.HYB_ENOTSUP
+    assert lib.hyb_index_topk_workspace_bytes(16, 131071, 128, 4) == 16 * 32768 * 4
+    assert lib.hyb_topk(FAKE, 10, FAKE, 4, 20, 8, FAKE, None) == hyb.HYB_EINVAL   # ld < max_len
+    assert lib.hyb_topk(FAKE, 20, FAKE, 4, 20, 0, FAKE, None) == hyb.HYB_EINVAL   # k = 0
+    assert lib.hyb_topk(None, 20, FAKE, 4, 20, 8, FAKE, None) == hyb.HYB_EINVAL
+    assert lib.hyb_index_score(FAKE, hyb.BF16, FAKE, None, FAKE, 16, 64, 131071, 128,
+                               ctypes.byref(ip), FAKE, 100, None) == hyb.HYB_EINVAL  # ld too small

@@ -116,3 +116,13 @@ def test_fp4_ties_round_to_even():
     p, s = quantize_fp4_rows(v)
     back = unpack_fp4_row(p[0].numpy(), s[0].numpy(), 32)[:8]
     assert back.tolist() == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0]
+
+
+def test_round_to_bf16_matches_torch_on_float32_values():
+    from oracle.formats import round_to_bf16_bits
+    g = torch.Generator().manual_seed(3)
+    x = torch.cat([torch.randn(100000, generator=g) * 10,
+                   torch.tensor([0.0, -0.0, 1.0, 1.00390625, 1.005859375, 65504.0, 3e38, 1e-40])])
+    ours = round_to_bf16_bits(x.numpy().astype(np.float64))
+    ref = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
