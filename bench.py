@@ -1,0 +1,397 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the hybrid C4/C128 + sliding-window attention step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+
+A step is one pass of the whole decode path over one batch:
+  C4 layer (headline, 16 sequences x 131072 tokens): compress the new token into the C4 pool,
+  indexer scores over every visible C4 entry, top-512, sparse attention over the 128-token window
+  plus the selected entries, combine + inverse RoPE.
+  C128 layer (32 sequences x 2^20 tokens, pool built by compressing raw tokens with softmax gates):
+  compress the new token, dense attention over the window plus every visible C128 entry.
+Inputs are resident in HBM; R replicas of every cache are cycled so the 256 MiB Infinity Cache
+cannot hold a step's working set. Prints one JSON line (rank 0) with the headline metric, the
+roofline of the dominant kernel (indexer scores, timed with HIP events on its stream inside the
+timed region) and the float64 oracle timed on the host on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-attn decode query-tokens/s and % peak HBM GB/s at 128K/1M ctx"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=8, help="cache replicas cycled per step (C4)")
+    ap.add_argument("--no-c128", action="store_true", help="skip the 1M-context C128 layer")
+    ap.add_argument("--all", action="store_true", help="also time chunked prefill and the quantised mixed batch")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------------------------------
+def time_loop(torch, step, n_steps, warmup, n_rep, events=None):
+    for i in range(warmup):
+        step(i % n_rep, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        step(i % n_rep, events[i] if events else None)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def c4_sparse(torch, hyb, W, BM, args):
+    B, L, R = 16, 131072, max(1, args.replicas)
+    dev = "cuda"
+    reps = []
+    for r in range(R):
+        wl = W.sparse_decode(dev, seed=r)
+        g = W.generator(2, r, 99, dev)
+        p = L - 1
+        nv = BM.n_visible(p, 4, wl.window)
+        reps.append(dict(
+            wl=wl,
+            qpos=(wl.seq_lens - 1).contiguous(),
+            lengths=torch.full((B,), nv, dtype=torch.int32, device=dev),   # request metadata
+            scores=torch.empty(B, (nv + 63) // 64 * 64, dtype=torch.float32, device=dev),
+            topk=torch.empty(B, wl.k, dtype=torch.int32, device=dev),
+            out=torch.empty_like(wl.q),
+            ws=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, L, 4, wl.k), dtype=torch.uint8, device=dev),
+            x_new=W.to_storage(W.randn((B, 512), g, dev), "bf16"),
+            cu=torch.arange(0, B + 1, dtype=torch.int32, device=dev),
+            start=torch.full((B,), L - 1, dtype=torch.int32, device=dev),
+            state=W.randn((B, 4, 512), g, dev),
+        ))
+    nv = BM.n_visible(L - 1, 4, 128)
+
+    def step(r, ev):
+        d = reps[r]
+        wl = d["wl"]
+        hyb.hyb_compress(d["x_new"], d["cu"], d["start"], 1, d["state"], wl.comp, 64)
+        if ev:
+            ev[0].record()
+        hyb.hyb_index_score(wl.idx_q, wl.idx_w, d["qpos"], L - 1, wl.idx_pool, d["scores"])
+        if ev:
+            ev[1].record()
+        hyb.hyb_topk(d["scores"], d["lengths"], nv, wl.k, d["topk"])
+        hyb.hyb_attn_decode(wl.q, wl.seq_lens, L, wl.swa, wl.comp, d["out"], topk_idx=d["topk"],
+                            k=wl.k, workspace=d["ws"])
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    secs = time_loop(torch, step, args.steps, args.warmup, R, events)
+    score_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
+    per_tok = BM.decode_query_bytes(L, ratio=4, sparse=True)
+    comp_b = BM.compress_decode_bytes(4)
+    step_bytes = B * (per_tok.total + comp_b)
+    score_bytes = B * BM.index_score_bytes(L)
+    ms = secs * 1e3 / args.steps
+    res = dict(
+        value=B * args.steps / secs, ms_per_step=ms, step_bytes=step_bytes,
+        hbm_frac_step=step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        score_kernel_ms=score_ms, score_bytes=score_bytes,
+        score_gbs=score_bytes / (score_ms * 1e-3) / 1e9,
+    )
+    return res, reps[0]
+
+
+def c128_dense(torch, hyb, W, BM, args):
+    B, L, D = 32, 1 << 20, 512
+    R = 4
+    dev = "cuda"
+    wl0 = W.dense_decode(dev, seed=0, fill_comp=False)
+    state = torch.zeros(B, 128, D, device=dev)
+    st_l = torch.zeros(B, 128, device=dev)
+    cu = torch.arange(0, (B + 1) * W.RAW_CHUNK, W.RAW_CHUNK, dtype=torch.int32, device=dev)
+    comp_secs = 0.0
+    for c in range(L // W.RAW_CHUNK):
+        xs, ls = zip(*[W.raw_chunk(3, 0, b, c, D, dev) for b in range(B)])
+        x, lg = torch.cat(xs), torch.cat(ls)
+        del xs, ls
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        hyb.hyb_compress(x, cu, torch.full((B,), c * W.RAW_CHUNK, dtype=torch.int32, device=dev),
+                         W.RAW_CHUNK, state, wl0.comp, 64, gate_logits=lg, state_logits=st_l)
+        torch.cuda.synchronize()
+        comp_secs += time.perf_counter() - t0
+    raw_bytes = B * L * D * 2
+    reps = [wl0]
+    for r in range(1, R):   # same contents at other addresses, different block placement
+        wl = W.dense_decode(dev, seed=r, fill_comp=False)
+        wl.comp.data.copy_(wl0.comp.data)
+        wl.comp.block_table.copy_(wl0.comp.block_table)
+        reps.append(wl)
+    g = W.generator(3, 0, 99, dev)
+    extra = [dict(out=torch.empty_like(w.q),
+                  ws=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, D, L, 128, 0), dtype=torch.uint8, device=dev),
+                  x_new=W.to_storage(W.randn((B, D), g, dev), "bf16"),
+                  lg_new=W.randn((B,), g, dev),
+                  state=W.randn((B, 128, D), g, dev), st_l=W.randn((B, 128), g, dev),
+                  cu=torch.arange(0, B + 1, dtype=torch.int32, device=dev),
+                  start=torch.full((B,), L - 1, dtype=torch.int32, device=dev)) for w in reps]
+
+    def step(r, ev):
+        w, e = reps[r], extra[r]
+        hyb.hyb_compress(e["x_new"], e["cu"], e["start"], 1, e["state"], w.comp, 64,
+                         gate_logits=e["lg_new"], state_logits=e["st_l"])
+        if ev:
+            ev[0].record()
+        hyb.hyb_attn_decode(w.q, w.seq_lens, L, w.swa, w.comp, e["out"], workspace=e["ws"])
+        if ev:
+            ev[1].record()
+
+    n = max(args.steps // 2, 20)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+    secs = time_loop(torch, step, n, max(args.warmup // 2, 5), R, events)
+    attn_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
+    per_tok = BM.decode_query_bytes(L, ratio=128, sparse=False)
+    step_bytes = B * (per_tok.total + BM.compress_decode_bytes(128))
+    ms = secs * 1e3 / n
+    attn_bytes = B * per_tok.total
+    return dict(
+        value=B * n / secs, unit="query-tokens/s", ms_per_step=ms, steps=n,
+        hbm_frac_step=step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        attn_ms=attn_ms, attn_gbs=attn_bytes / (attn_ms * 1e-3) / 1e9,
+        attn_tflops=B * BM.attention_flops(8191 + 128) / (attn_ms * 1e-3) / 1e12,
+        compress_raw_gbs=raw_bytes / comp_secs / 1e9,
+        config={"workload": "c128_dense_decode", "batch": B, "context": L, "heads": 64, "dim": D,
+                "window": 128, "replicas": R, "pool": "bf16, built by softmax-gate compression of raw tokens"},
+    )
+
+
+def prefill(torch, hyb, W, BM, args):
+    dev = "cuda"
+    wl = W.chunked_prefill(dev, seed=0)
+    D, n = wl.q.shape[2], wl.n_new
+    cu, st = torch.tensor([0, n], dtype=torch.int32, device=dev), torch.tensor([wl.prior], dtype=torch.int32, device=dev)
+    s4 = torch.zeros(1, 4, D, device=dev)
+    s128, l128 = torch.zeros(1, 128, D, device=dev), torch.zeros(1, 128, device=dev)
+    max_pos = wl.prior + n - 1
+    topk = torch.empty(n, wl.k, dtype=torch.int32, device=dev)
+    out = torch.empty_like(wl.q)
+    ws_i = torch.empty(hyb.hyb_index_topk_workspace_bytes(n, max_pos, 128, 4), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(hyb.hyb_attn_prefill_workspace_bytes(n, 64, D, max_pos, 4, wl.k), dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step():
+        ev[0].record()
+        hyb.hyb_swa_insert(wl.x_new, cu, st, n, wl.swa, 64)
+        hyb.hyb_compress(wl.x_new, cu, st, n, s4, wl.c4, 64)
+        hyb.hyb_compress(wl.x_new, cu, st, n, s128, wl.c128, 64, gate_logits=wl.gate_new, state_logits=l128)
+        ev[1].record()
+        hyb.hyb_index_topk(wl.idx_q, wl.idx_w, wl.q_pos, max_pos, wl.idx_pool, wl.k, topk, q_seq=wl.q_seq, workspace=ws_i)
+        ev[2].record()
+        hyb.hyb_attn_prefill(wl.q, wl.q_pos, max_pos, wl.swa, wl.c4, out, topk_idx=topk, k=wl.k, q_seq=wl.q_seq, workspace=ws_a)
+        ev[3].record()
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    reps = 5
+    t = [0.0, 0.0, 0.0]
+    for _ in range(reps):
+        step()
+        torch.cuda.synchronize()
+        for j in range(3):
+            t[j] += ev[j].elapsed_time(ev[j + 1]) / reps
+    fi, fa = BM.prefill_flops(range(wl.prior, wl.prior + n))
+    return dict(
+        ms_total=sum(t), ms_compress_insert=t[0], ms_index_topk=t[1], ms_attention=t[2],
+        indexer_tflops=fi / (t[1] * 1e-3) / 1e12, attention_tflops=fa / (t[2] * 1e-3) / 1e12,
+        mfma_frac=(fi + fa) / ((t[1] + t[2]) * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        query_tokens_per_s=n / (sum(t) * 1e-3),
+        config={"workload": "chunked_prefill", "prior": wl.prior, "chunk": n, "heads": 64, "dim": D, "topk": wl.k},
+    )
+
+
+def quant_mixed(torch, hyb, W, BM, args):
+    dev = "cuda"
+    c4, c128 = W.quantized_mixed(dev, seed=0)
+    B = c4.batch
+    lens = c4.seq_lens_host
+    max_len = max(lens)
+    topk = torch.empty(B, c4.k, dtype=torch.int32, device=dev)
+    o4, o128 = torch.empty_like(c4.q), torch.empty_like(c128.q)
+    qpos = (c4.seq_lens - 1).contiguous()
+    ws_i = torch.empty(hyb.hyb_index_topk_workspace_bytes(B, max_len - 1, 128, 4), dtype=torch.uint8, device=dev)
+    ws4 = torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, max_len, 4, c4.k), dtype=torch.uint8, device=dev)
+    ws128 = torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, max_len, 128, 0), dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def step():
+        ev[0].record()
+        hyb.hyb_index_topk(c4.idx_q, c4.idx_w, qpos, max_len - 1, c4.idx_pool, c4.k, topk, workspace=ws_i)
+        hyb.hyb_attn_decode(c4.q, c4.seq_lens, max_len, c4.swa, c4.comp, o4, topk_idx=topk, k=c4.k, workspace=ws4)
+        ev[1].record()
+        hyb.hyb_attn_decode(c128.q, c128.seq_lens, max_len, c128.swa, c128.comp, o128, workspace=ws128)
+        ev[2].record()
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    reps = 10
+    t4 = t128 = 0.0
+    for _ in range(reps):
+        step()
+        torch.cuda.synchronize()
+        t4 += ev[0].elapsed_time(ev[1]) / reps
+        t128 += ev[1].elapsed_time(ev[2]) / reps
+    b4 = sum(BM.decode_query_bytes(L, ratio=4, sparse=True, dtype="fp8", idx_dtype="fp4").total for L in lens)
+    b128 = sum(BM.decode_query_bytes(L, ratio=128, sparse=False, dtype="fp8").total for L in lens)
+    return dict(
+        c4_ms=t4, c4_query_tokens_per_s=B / (t4 * 1e-3), c4_hbm_frac=b4 / (t4 * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        c128_ms=t128, c128_query_tokens_per_s=B / (t128 * 1e-3),
+        c128_hbm_frac=b128 / (t128 * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        config={"workload": "quantized_mixed_decode", "batch": B, "lengths": "log-uniform 4096..2^20 (seed 0)",
+                "mean_len": sum(lens) / B, "attn_cache": "fp8 e4m3 + fp32 scale per entry",
+                "indexer_cache": "fp4 e2m1 + e8m0 per 32"},
+    )
+
+
+# ------------------------------------------------------------------------------------------
+def cpu_baseline(torch, W, BM, rep, budget):
+    """The float64 oracle, as it stands, on the same C4 decode step (compress the new token,
+    indexer, top-k, attention), sequence by sequence until the time budget is spent."""
+    import numpy as np
+    import oracle as O
+
+    def opool(pt):
+        data = pt.data.detach().cpu()
+        data = data.view(torch.int16).numpy().view(np.uint16) if pt.dtype == "bf16" else data.numpy()
+        return O.OraclePool(data=data, dtype=pt.dtype, dim=pt.dim, ratio=pt.ratio,
+                            block_table=pt.block_table.cpu().numpy(),
+                            scale=None if pt.scale is None else pt.scale.cpu().numpy())
+
+    wl = rep["wl"]
+    swa, comp, ip = opool(wl.swa), opool(wl.comp), opool(wl.idx_pool)
+    q = wl.q.cpu().double().numpy()
+    iq, iw = wl.idx_q.cpu().double().numpy(), wl.idx_w.cpu().double().numpy()
+    x_new = rep["x_new"].cpu().double().numpy()
+    state = rep["state"].cpu().double().numpy()
+    scale = 1.0 / math.sqrt(wl.dim)
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(wl.batch):
+        L = wl.seq_lens_host[b]
+        p = L - 1
+        toks = np.concatenate([state[b, :3], x_new[b][None]])
+        O.compressed_entry(toks, None, p // 4, 4, "mean", 64, 1e4, 1e-6)
+        nv = O.n_visible(p, 4, 128)
+        sc = O.indexer_scores(iq[b], iw[b], O.pool_entries(ip, b, range(nv)))
+        sel = O.topk_select(sc, wl.k)
+        O.hybrid_query(q[b], p, b, swa, comp, 128, scale, 64, 1e4, sel)
+        done += 1
+        if time.perf_counter() - t0 > budget:
+            break
+    secs = time.perf_counter() - t0
+    threads = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            threads = max(blas)
+    except Exception:
+        pass
+    return {"value": done / secs, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of 16 sequences of the C4 decode step (131072-token contexts), "
+                      f"one at a time, {secs:.1f} s, numpy float64"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (no sharding or collectives); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_attention_hyb_amd as hyb
+    from sparse_attention_hyb_amd import bytes_model as BM
+    from sparse_attention_hyb_amd import workloads as W
+
+    hyb.load()
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 3 x 1 GiB device copies done")
+
+    log("C4 sparse decode: building 8 replicas")
+    res, rep0 = c4_sparse(torch, hyb, W, BM, args)
+    log(f"C4 sparse decode: {res['value']:.0f} q-tok/s, {res['ms_per_step'] * 1e3:.1f} us/step, "
+        f"score kernel {res['score_kernel_ms'] * 1e3:.1f} us = {res['score_gbs']:.0f} GB/s")
+    extra = {}
+    if not args.no_c128:
+        log("C128 dense decode: compressing 32 x 2^20 raw tokens, then timing")
+        extra["c128_dense_decode_1M"] = c128_dense(torch, hyb, W, BM, args)
+        log(f"C128: {extra['c128_dense_decode_1M']['value']:.0f} q-tok/s")
+    if args.all:
+        log("chunked prefill")
+        extra["chunked_prefill"] = prefill(torch, hyb, W, BM, args)
+        log("quantised mixed decode")
+        extra["quantized_mixed_decode"] = quant_mixed(torch, hyb, W, BM, args)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("oracle CPU baseline")
+        cpu = cpu_baseline(torch, W, BM, rep0, args.cpu_budget)
+    line = {
+        "metric": METRIC,
+        "value": res["value"],
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c4_sparse_decode", "batch": 16, "context": 131072, "heads": 64,
+                   "dim": 512, "rope_dims": 64, "indexer": "64 heads x 128, bf16", "topk": 512,
+                   "window": 128, "replicas": args.replicas,
+                   "step": "compress new token + indexer scores + top-512 + sparse attention + combine/inverse RoPE"},
+        "hbm_frac_step": res["hbm_frac_step"],
+        "step_bytes": res["step_bytes"],
+        "roofline": {"kernel": "score_mfma (indexer scores)", "bound": "hbm",
+                     "achieved": res["score_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": res["score_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "avg_launch_us": res["score_kernel_ms"] * 1e3,
+                     "bytes_per_launch": res["score_bytes"]},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -91,7 +91,7 @@ typedef struct hyb_paged {
   int32_t dtype;      /* hyb_dtype */
   int32_t dim;
   int32_t ratio;      /* 1 (raw sliding-window entries), 4 (C4) or 128 (C128) */
-  int32_t num_blocks; /* physical blocks in data */
+  int32_t num_blocks; /* physical blocks in data; num_blocks * 256/ratio < 2^31 */
   int32_t max_blocks; /* columns of block_table */
   int32_t reserved;   /* must be 0 */
 } hyb_paged;

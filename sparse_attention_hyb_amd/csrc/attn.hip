@@ -23,6 +23,8 @@
 //        back transposed.
 // fp8 pools: codes are widened to bf16 exactly; the per-entry scale multiplies the score before
 // the softmax and the probability before PV (so no rounding of scaled values).
+#include <type_traits>
+
 #include "common.h"
 
 namespace hyb {
@@ -30,7 +32,6 @@ namespace hyb {
 constexpr int kMH = 64;         // heads in the MFMA kernel
 constexpr int kMD = 512;        // dims in the MFMA kernel
 constexpr int kKT = 32;         // keys per tile in the MFMA kernel
-constexpr int kKRow = kMD + 8;  // LDS row pitch of the K tile (bf16 elements)
 constexpr int kGenTile = 64;    // keys per tile in the generic kernel
 constexpr int kMaxSplit = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -176,141 +177,235 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+
+constexpr int kSeg = 2048;           // keys whose entry indices are resolved per segment
+constexpr int kPitch = kMD + 16;     // LDS row pitch of a K tile (bf16): 1056 B, 8 banks per row
+
+// One wave's quarter (64 of the 512 dims per lane-half) of one 32-key tile, held in registers
+// between its global load and its use.
+template <bool kFp8>
+struct Stage;
+template <>
+struct Stage<false> {
+  bf16x8 v[8];
+  float sc;
+  int valid;
+};
+template <>
+struct Stage<true> {
+  u32x4 v[4];
+  float sc;
+  int valid;
+};
+
+__device__ __forceinline__ bf16x8 lds_tr_pair(const uint16_t* p0, const uint16_t* p1) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+  u32x4 w;
+  w[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  w[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  w[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  w[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// MFMA attention. Work of one workgroup: query i, keys [split*chunk, (split+1)*chunk) of its list.
+// Waves form a 2 x 2 grid: hh = head half (32 heads), dh = dim half (256 dims). Wave (hh, dh)
+// loads only dim quarter qd = 2*dh + hh of every key (each key byte is fetched once per
+// workgroup), three tiles deep in registers; the quarter is written to the LDS tile, where the
+// partner wave of the same dim half picks it up for its QK and all waves read it transposed for PV.
 template <bool kFp8>
 __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ktile[kKT * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[2 * kKT * kPitch];
   __shared__ float sx[4][16][64];
-  __shared__ float kscale[kKT];
-  __shared__ int kvalid[kKT];
+  __shared__ int32_t kidx[kSeg];
+  __shared__ float kscale[2 * kKT];
+  __shared__ int kvalid[2 * kKT];
 
   const int i = blockIdx.y, sp = blockIdx.x;
   const QueryKeys qk = query_keys(a, i);
   const int j_begin = sp * a.chunk, j_end = min(qk.n_keys, j_begin + a.chunk);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
   const int hh = wave >> 1, dh = wave & 1;
+  const int qd = 2 * dh + hh;          // the dim quarter this wave loads
+  const int oq = 2 * dh + (1 - hh);    // the partner's quarter
 
-  // Q^T as the QK B operand: column h = 32*hh + col; dims d = 256*dh + 128*hf + 8*s + e
+  // Q^T as the QK B operand (column = head 32*hh + col). K-step s covers quarter 2*dh + s/8,
+  // dims 128*quarter + 64*hf + 8*(s%8) + [0, 8): the same split the K operand uses.
   bf16x8 qb[16];
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
-                           ((int64_t)i * kMH + 32 * hh + col) * kMD + 256 * dh + 128 * hf;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)i * kMH + 32 * hh + col) * kMD;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + 8 * s);
+    for (int s = 0; s < 16; ++s)
+      qb[s] = *reinterpret_cast<const bf16x8*>(qrow + 128 * (2 * dh + (s >> 3)) + 64 * hf + 8 * (s & 7));
   }
   f32x16 o[8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) o[mb] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
+  const int lane_off = 128 * qd + 64 * hf;   // first dim of this lane's staged run
 
-  for (int j0 = j_begin; j0 < j_end; j0 += kKT) {
-    // ---- this lane's key row: key j0 + col, dims 256*dh + 128*hf + [0, 128)
-    const int j = j0 + col;
-    KeyRef kr{-1, 0};
-    if (j < j_end) kr = resolve_key(a, i, qk.seq, qk.ws, qk.n_win, qk.nv, j);
-    const PoolDev& P = kr.comp ? a.comp : a.swa;
-    bf16x8 ka[16];
-    float ksc = 1.f;
-    if (kr.idx >= 0) {
-      if constexpr (!kFp8) {
-        const uint16_t* row =
-            reinterpret_cast<const uint16_t*>(P.data + kr.idx * P.entry_bytes) + 256 * dh + 128 * hf;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) ka[s] = *reinterpret_cast<const bf16x8*>(row + 8 * s);
-      } else {
-        const uint8_t* row = P.data + kr.idx * P.entry_bytes + 256 * dh + 128 * hf;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          u32x4 w = *reinterpret_cast<const u32x4*>(row + 16 * s);
-          ka[2 * s] = fp8x8_to_bf16x8(w[0], w[1]);
-          ka[2 * s + 1] = fp8x8_to_bf16x8(w[2], w[3]);
-        }
-        ksc = reinterpret_cast<const float*>(P.scale)[kr.idx];
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 16; ++s) ka[s] = bf16x8{};
-    }
-    // ---- QK over this wave's 256 dims
-    f32x16 st = {};
-#pragma unroll
-    for (int s = 0; s < 16; ++s) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qb[s], st, 0, 0, 0);
-    // ---- share: partial scores, the K tile (natural layout), key scale and validity
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sx[wave][r][lane] = st[r];
-    if (hf == hh) {
-      uint16_t* dst = ktile + col * kKRow + 256 * dh + 128 * hh;
-#pragma unroll
-      for (int s = 0; s < 16; ++s) *reinterpret_cast<bf16x8*>(dst + 8 * s) = ka[s];
-    }
-    if (wave == 0 && hf == 0) {
-      kscale[col] = ksc;
-      kvalid[col] = kr.idx >= 0;
+  for (int seg = j_begin; seg < j_end; seg += kSeg) {
+    const int nseg = min(kSeg, j_end - seg);
+    __syncthreads();   // readers of the previous segment's index table are done
+    for (int jj = tid; jj < nseg; jj += 256) {
+      KeyRef r = resolve_key(a, i, qk.seq, qk.ws, qk.n_win, qk.nv, seg + jj);
+      kidx[jj] = (int32_t)r.idx;
     }
     __syncthreads();
+    const int n_tiles = (nseg + kKT - 1) / kKT;
+
+    auto load = [&](Stage<kFp8>& st, int tt) {
+      const int jl = tt * kKT + col;
+      const int idx = jl < nseg ? kidx[jl] : -1;
+      st.valid = idx >= 0;
+      st.sc = 1.f;
+      if (idx >= 0) {
+        const PoolDev& P = (seg + jl) < qk.n_win ? a.swa : a.comp;
+        if constexpr (!kFp8) {
+          const uint16_t* row = reinterpret_cast<const uint16_t*>(P.data + (int64_t)idx * P.entry_bytes) + lane_off;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st[r] += sx[wave ^ 1][r][lane];
-    // ---- online softmax for head 32*hh + col; this lane's keys are 8*(r/4) + 4*hf + r%4
-    float z[16];
-    float mx = -INFINITY;
+          for (int c = 0; c < 8; ++c) st.v[c] = *reinterpret_cast<const bf16x8*>(row + 8 * c);
+        } else {
+          const uint8_t* row = P.data + (int64_t)idx * P.entry_bytes + lane_off;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
-      float v = st[r] * sl2;
-      if constexpr (kFp8) v *= kscale[key];
-      z[r] = kvalid[key] ? v : -INFINITY;
-      mx = fmaxf(mx, z[r]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float ref = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - ref);
-    float psum = 0.f;
-    float pr[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = exp2f(z[r] - ref);
-      psum += e;
-      if constexpr (kFp8) {
-        pr[r] = e * kscale[8 * (r >> 2) + 4 * hf + (r & 3)];
+          for (int c = 0; c < 4; ++c) st.v[c] = *reinterpret_cast<const u32x4*>(row + 16 * c);
+          st.sc = reinterpret_cast<const float*>(P.scale)[idx];
+        }
       } else {
-        pr[r] = e;
+#pragma unroll
+        for (int c = 0; c < (kFp8 ? 4 : 8); ++c) st.v[c] = std::remove_reference_t<decltype(st.v[0])>{};
       }
-    }
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    };
+
+    auto own = [&](const Stage<kFp8>& st, int c) -> bf16x8 {
+      if constexpr (!kFp8) {
+        return st.v[c];
+      } else {
+        const u32x4 w = st.v[c >> 1];
+        return (c & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+      }
+    };
+
+    auto process = [&](const Stage<kFp8>& st, int tt) {
+      const int kb = tt & 1;
+      uint16_t* kt = ktile + kb * kKT * kPitch;
+      // ---- publish this wave's quarter of the tile (natural [key][dim] layout)
+      {
+        uint16_t* dst = kt + col * kPitch + lane_off;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+        for (int c = 0; c < 8; ++c) *reinterpret_cast<bf16x8*>(dst + 8 * c) = own(st, c);
+      }
+      if (wave == 0 && hf == 0) {
+        kvalid[kb * kKT + col] = st.valid;
+        kscale[kb * kKT + col] = st.sc;
+      }
+      __syncthreads();
+      // ---- QK over this wave's dim half: own quarter from registers, partner's from LDS
+      f32x16 sacc = {};
+      const uint16_t* other = kt + col * kPitch + 128 * oq + 64 * hf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
-    // ---- PV: B operand = probabilities (element e of step t <-> key 16t + 8(e/4) + 4hf + e%4)
-    bf16x8 pb[2];
+      for (int s = 0; s < 16; ++s) {
+        const bf16x8 ka = ((s >> 3) == hh) ? own(st, s & 7)
+                                           : *reinterpret_cast<const bf16x8*>(other + 8 * (s & 7));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sacc, 0, 0, 0);
+      }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      u32x4 w;
+      for (int r = 0; r < 16; ++r) sx[wave][r][lane] = sacc[r];
+      __syncthreads();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(pr[8 * t + 2 * e], pr[8 * t + 2 * e + 1]);
-      pb[t] = __builtin_bit_cast(bf16x8, w);
-    }
+      for (int r = 0; r < 16; ++r) sacc[r] += sx[wave ^ 1][r][lane];
+      // ---- online softmax for head 32*hh + col; this lane's keys are 8*(r/4) + 4*hf + r%4
+      float z[16];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const int d = 256 * dh + 32 * mb + col;
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * kKT + 8 * (r >> 2) + 4 * hf + (r & 3);
+        float v = sacc[r] * sl2;
+        if constexpr (kFp8) v *= kscale[key];
+        z[r] = kvalid[key] ? v : -INFINITY;
+        mx = fmaxf(mx, z[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float ref = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m_run - ref);
+      float psum = 0.f;
+      float pr[16];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int r = 0; r < 16; ++r) {
+        const float e = exp2f(z[r] - ref);
+        psum += e;
+        if constexpr (kFp8) {
+          pr[r] = e * kscale[kb * kKT + 8 * (r >> 2) + 4 * hf + (r & 3)];
+        } else {
+          pr[r] = e;
+        }
+      }
+      psum += __shfl_xor(psum, 32, 64);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+      // ---- PV: B = probabilities (element e of K-step t <-> key 16t + 8(e/4) + 4hf + e%4),
+      //      A = K^T read transposed from LDS: lane j of each 16-lane group points at key
+      //      k0 + j/4, dims d0 + 4*(j%4), and receives keys k0..k0+3 of dim d0 + j.
+      bf16x8 pb[2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
         u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k0 = 16 * t + 8 * ((2 * e) >> 2) + 4 * hf + ((2 * e) & 3);
-          const int k1 = 16 * t + 8 * ((2 * e + 1) >> 2) + 4 * hf + ((2 * e + 1) & 3);
-          w[e] = (uint32_t)ktile[k0 * kKRow + d] | ((uint32_t)ktile[k1 * kKRow + d] << 16);
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(pr[8 * t2 + 2 * e], pr[8 * t2 + 2 * e + 1]);
+        pb[t2] = __builtin_bit_cast(bf16x8, w);
+      }
+      const int i16 = lane & 15;
+      const int gcol = (col >> 4) * 16 + 4 * (i16 & 3);
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const int d0 = 256 * dh + 32 * mb + gcol;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const int k0 = 16 * t2 + 4 * hf + (i16 >> 2);
+          const bf16x8 af = lds_tr_pair(kt + k0 * kPitch + d0, kt + (k0 + 8) * kPitch + d0);
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[t2], o[mb], 0, 0, 0);
         }
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[t], o[mb],
-                                                        0, 0, 0);
+      }
+    };
+
+    // Global loads run kDepth - 1 tiles ahead of the tile being processed (register budget:
+    // two staged bf16 tiles, or three fp8 ones, fit beside Q and the O accumulators).
+    if constexpr (kFp8) {
+      Stage<kFp8> s0, s1, s2;
+      load(s0, 0);
+      if (n_tiles > 1) load(s1, 1);
+      for (int t = 0; t < n_tiles; t += 3) {
+        if (t + 2 < n_tiles) load(s2, t + 2);
+        process(s0, t);
+        if (t + 1 >= n_tiles) break;
+        if (t + 3 < n_tiles) load(s0, t + 3);
+        process(s1, t + 1);
+        if (t + 2 >= n_tiles) break;
+        if (t + 4 < n_tiles) load(s1, t + 4);
+        process(s2, t + 2);
+      }
+    } else {
+      Stage<kFp8> s0, s1;
+      load(s0, 0);
+      for (int t = 0; t < n_tiles; t += 2) {
+        if (t + 1 < n_tiles) load(s1, t + 1);
+        process(s0, t);
+        if (t + 1 >= n_tiles) break;
+        if (t + 2 < n_tiles) load(s0, t + 2);
+        process(s1, t + 1);
       }
     }
-    __syncthreads();
   }
   // ---- partials: O^T rows d = 256*dh + 32*mb + 8*(r/4) + 4*hf + r%4, column h = 32*hh + col
   float* po = a.part_o + ((int64_t)i * a.n_split + sp) * kMD * kMH;
@@ -332,14 +427,18 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // Combine: merge split partials, inverse RoPE at the query position, cast.
+// Grid (dim slice of 64, query): each workgroup reads its 64 dims x all heads of every split.
 // ------------------------------------------------------------------------------------------
+constexpr int kCombineDims = 64;
+
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
-  const int i = blockIdx.x;
+  const int i = blockIdx.y;
+  const int d0 = blockIdx.x * kCombineDims;
   const int H = a.n_heads, D = a.dim, ns = a.n_split;
   int seq, p;
   query_at(a.qd, i, &seq, &p);
   __shared__ float wsplit[kMaxSplit * 128];
-  __shared__ float rc[64], rs[64];
+  __shared__ float rc[kCombineDims / 2], rs[kCombineDims / 2];
   const float* pml = a.part_ml + (int64_t)i * ns * 2 * H;
   for (int h = threadIdx.x; h < H; h += 256) {
     float M = -INFINITY;
@@ -355,13 +454,18 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
       wsplit[s * H + h] = ms == -INFINITY ? 0.f : expf(ms - M) * inv;
     }
   }
-  const int half = a.rope_dim / 2;
-  for (int t = threadIdx.x; t < half; t += 256) rope_cs(-(double)p, t, a.rope_dim, a.rope_base, &rc[t], &rs[t]);
+  const int rope_lo = D - a.rope_dim;
+  const int dend = min(D, d0 + kCombineDims);
+  for (int t = threadIdx.x; t < kCombineDims / 2; t += 256) {
+    const int d = d0 + 2 * t;
+    if (d >= rope_lo && d < dend)
+      rope_cs(-(double)p, (d - rope_lo) >> 1, a.rope_dim, a.rope_base, &rc[t], &rs[t]);
+  }
   __syncthreads();
   const float* po = a.part_o + (int64_t)i * ns * D * H;
-  const int rope_lo = D - a.rope_dim;
-  for (int e = threadIdx.x; e < (D / 2) * H; e += 256) {
-    const int h = e % H, d = 2 * (e / H);
+  const int npair = (dend - d0) / 2;
+  for (int e = threadIdx.x; e < npair * H; e += 256) {
+    const int h = e % H, t = e / H, d = d0 + 2 * t;
     float v0 = 0.f, v1 = 0.f;
     for (int s = 0; s < ns; ++s) {
       const float wgt = wsplit[s * H + h];
@@ -369,7 +473,6 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
       v1 = fmaf(wgt, po[((int64_t)s * D + d + 1) * H + h], v1);
     }
     if (d >= rope_lo) {
-      const int t = (d - rope_lo) >> 1;
       const float z0 = v0 * rc[t] - v1 * rs[t];
       const float z1 = v0 * rs[t] + v1 * rc[t];
       v0 = z0;
@@ -400,6 +503,13 @@ AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_k
   ns = ns < 1 ? 1 : ns;
   int chunk = (max_keys + ns - 1) / ns;
   chunk = (chunk + tile - 1) / tile * tile;
+  if (pl.use_mfma && chunk > kSeg && ns < kMaxSplit) {
+    // one index-table segment per workgroup when the split count allows it
+    ns = (max_keys + kSeg - 1) / kSeg;
+    ns = ns > kMaxSplit ? kMaxSplit : ns;
+    chunk = (max_keys + ns - 1) / ns;
+    chunk = (chunk + tile - 1) / tile * tile;
+  }
   if (chunk < tile) chunk = tile;
   ns = (max_keys + chunk - 1) / chunk;
   if (ns < 1) ns = 1;
@@ -424,7 +534,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine, dim3(a.n_q), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_combine, dim3((a.dim + kCombineDims - 1) / kCombineDims, a.n_q), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

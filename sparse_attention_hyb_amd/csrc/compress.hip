@@ -92,29 +92,34 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
     float acc[kMaxPairsPerThread][2];
 #pragma unroll
     for (int j = 0; j < kMaxPairsPerThread; ++j) acc[j][0] = acc[j][1] = 0.f;
-    for (int t = gstart; t < gstart + r; ++t) {
-      const float wt = wts[t - gstart];
-      if (t < s0) {
-        const float* row = a.state + ((int64_t)b * r + (t - gstart)) * D;
+    // tokens of the group that arrived in earlier calls come from the state ring, the rest from
+    // x; both loops are unrolled so a thread keeps several row loads in flight
+    const int n_state = max(0, min(s0, gstart + r) - gstart);
+#pragma unroll 8
+    for (int t = 0; t < n_state; ++t) {
+      const float wt = wts[t];
+      const float* row = a.state + ((int64_t)b * r + t) * D;
 #pragma unroll
-        for (int j = 0; j < kMaxPairsPerThread; ++j) {
-          int pi = tid + j * kCompressThreads;
-          if (pi < npairs) {
-            float2 v = load_pair<float>(row, 2 * pi);
-            acc[j][0] = fmaf(wt, v.x, acc[j][0]);
-            acc[j][1] = fmaf(wt, v.y, acc[j][1]);
-          }
+      for (int j = 0; j < kMaxPairsPerThread; ++j) {
+        int pi = tid + j * kCompressThreads;
+        if (pi < npairs) {
+          float2 v = load_pair<float>(row, 2 * pi);
+          acc[j][0] = fmaf(wt, v.x, acc[j][0]);
+          acc[j][1] = fmaf(wt, v.y, acc[j][1]);
         }
-      } else {
-        const T* row = x + (int64_t)(c0 + t - s0) * D;
+      }
+    }
+#pragma unroll 8
+    for (int t = n_state; t < r; ++t) {
+      const float wt = wts[t];
+      const T* row = x + (int64_t)(c0 + gstart + t - s0) * D;
 #pragma unroll
-        for (int j = 0; j < kMaxPairsPerThread; ++j) {
-          int pi = tid + j * kCompressThreads;
-          if (pi < npairs) {
-            float2 v = load_pair<T>(row, 2 * pi);
-            acc[j][0] = fmaf(wt, v.x, acc[j][0]);
-            acc[j][1] = fmaf(wt, v.y, acc[j][1]);
-          }
+      for (int j = 0; j < kMaxPairsPerThread; ++j) {
+        int pi = tid + j * kCompressThreads;
+        if (pi < npairs) {
+          float2 v = load_pair<T>(row, 2 * pi);
+          acc[j][0] = fmaf(wt, v.x, acc[j][0]);
+          acc[j][1] = fmaf(wt, v.y, acc[j][1]);
         }
       }
     }

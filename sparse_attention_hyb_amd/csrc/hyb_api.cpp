@@ -56,6 +56,8 @@ int check_pool(const hyb_paged* p, const char* op, const char* name, bool fp8_ok
   if (p->dim <= 0 || p->dim % 2) return fail(HYB_EINVAL, "%s: %s.dim %d must be positive and even", op, name, p->dim);
   if (p->num_blocks <= 0 || p->max_blocks <= 0)
     return fail(HYB_EINVAL, "%s: %s needs num_blocks > 0 and max_blocks > 0", op, name);
+  if ((int64_t)p->num_blocks * (HYB_BLOCK_POSITIONS / (r > 0 ? r : 1)) >= (1LL << 31))
+    return fail(HYB_EINVAL, "%s: %s holds 2^31 entries or more", op, name);
   switch (p->dtype) {
     case HYB_F32:
     case HYB_BF16:

@@ -12,6 +12,8 @@
 //    keys as N; each lane then owns one key column and 32 of its heads, so the ReLU-weighted head
 //    sum is 32 in-lane FMAs plus one cross-half add.
 //  * score_generic: any (heads x dim) <= 8192, fp32 / bf16 / fp4 - one thread per key.
+#include <type_traits>
+
 #include "common.h"
 
 namespace hyb {
@@ -69,36 +71,59 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
       wv[mb][r] = a.w[(int64_t)i * kMfmaHeads + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3)];
 
   float* out = a.scores + (int64_t)i * a.ld;
-  for (int t0 = base + wave * 32; t0 < end; t0 += 128) {
+  // Each wave walks 32-key tiles with stride 128; the next tile's keys are loaded while the
+  // current one is multiplied. fp4 tiles stay packed (32 B + 2 scale bytes per lane) until used.
+  struct KeysBf16 {
+    bf16x8 v[8];
+  };
+  struct KeysFp4 {
+    u32x4 w0, w1;
+    float s0, s1;
+  };
+  using Keys = std::conditional_t<kFp4, KeysFp4, KeysBf16>;
+  auto load = [&](Keys& kb, int t0) {
     const int g = t0 + col;
     const int64_t idx = g < end ? entry_index(a.pool, seq, g) : -1;
-    bf16x8 kb[8];
-    if (idx >= 0) {
-      if constexpr (!kFp4) {
+    if constexpr (!kFp4) {
+      if (idx >= 0) {
         const uint16_t* row =
             reinterpret_cast<const uint16_t*>(a.pool.data + idx * a.pool.entry_bytes) + 64 * hf;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) kb[s] = *reinterpret_cast<const bf16x8*>(row + 8 * s);
+        for (int s = 0; s < 8; ++s)
+          kb.v[s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(row + 8 * s));
       } else {
-        const uint8_t* row = a.pool.data + idx * a.pool.entry_bytes + 32 * hf;
-        const uint8_t* scl = reinterpret_cast<const uint8_t*>(a.pool.scale) + idx * 4 + 2 * hf;
-        u32x4 w0 = *reinterpret_cast<const u32x4*>(row);
-        u32x4 w1 = *reinterpret_cast<const u32x4*>(row + 16);
-        const float s0 = e8m0_to_f32(scl[0]), s1 = e8m0_to_f32(scl[1]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kb[s] = fp4x8_to_bf16x8(w0[s], s0);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kb[4 + s] = fp4x8_to_bf16x8(w1[s], s1);
+        for (int s = 0; s < 8; ++s) kb.v[s] = bf16x8{};
       }
     } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) kb[s] = bf16x8{};
+      if (idx >= 0) {
+        const uint8_t* row = a.pool.data + idx * a.pool.entry_bytes + 32 * hf;
+        const uint8_t* scl = reinterpret_cast<const uint8_t*>(a.pool.scale) + idx * 4 + 2 * hf;
+        kb.w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row));
+        kb.w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 16));
+        kb.s0 = e8m0_to_f32(scl[0]);
+        kb.s1 = e8m0_to_f32(scl[1]);
+      } else {
+        kb.w0 = u32x4{};
+        kb.w1 = u32x4{};
+        kb.s0 = kb.s1 = 0.f;
+      }
     }
+  };
+  auto operand = [&](const Keys& kb, int s) -> bf16x8 {
+    if constexpr (!kFp4) {
+      return kb.v[s];
+    } else {
+      return s < 4 ? fp4x8_to_bf16x8(kb.w0[s], kb.s0) : fp4x8_to_bf16x8(kb.w1[s - 4], kb.s1);
+    }
+  };
+  auto score = [&](const Keys& kb, int t0) {
     f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb[s], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb[s], acc1, 0, 0, 0);
+      const bf16x8 b = operand(kb, s);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], b, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], b, acc1, 0, 0, 0);
     }
     float part = 0.f;
 #pragma unroll
@@ -107,7 +132,18 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
       part = fmaf(wv[1][r], fmaxf(acc1[r], 0.f), part);
     }
     part += __shfl_xor(part, 32, 64);
+    const int g = t0 + col;
     if (hf == 0 && g < end) out[g] = canonical_zero(part);
+  };
+  Keys ka, kc;
+  int t0 = base + wave * 32;
+  if (t0 < end) load(ka, t0);
+  for (; t0 < end; t0 += 256) {
+    if (t0 + 128 < end) load(kc, t0 + 128);
+    score(ka, t0);
+    if (t0 + 128 >= end) break;
+    if (t0 + 256 < end) load(ka, t0 + 256);
+    score(kc, t0 + 128);
   }
 }
 

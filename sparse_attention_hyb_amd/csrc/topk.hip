@@ -4,11 +4,12 @@
 // compressed entries chosen by the indexer); vLLM day-0 post ("DeepSeek Sparse Attention over
 // compressed tokens").
 //
-// One 1024-thread workgroup per row. Scores become order-preserving 32-bit keys; three radix
-// passes (11 + 11 + 10 bits, histograms in LDS) find the k-th largest key T and how many of the
-// keys equal to T are taken (the lowest-indexed ones). A final pass gives each thread a contiguous
-// index range, counts "> T" and "== T" there, scans both counts across the workgroup and writes
-// the chosen indices at their scanned offsets - so the output is ascending without a sort.
+// One 1024-thread workgroup per row. Scores become order-preserving 32-bit keys held in
+// registers (32 consecutive scores per thread); three radix passes (11 + 11 + 10 bits,
+// histograms in LDS) find the k-th largest key T and how many of the keys equal to T are taken
+// (the lowest-indexed ones). Because every thread owns a contiguous index range, one workgroup
+// scan of its "> T" and "== T" counts gives each chosen index its output slot directly - the
+// output is ascending without a sort.
 #include "common.h"
 
 namespace hyb {
@@ -45,6 +46,12 @@ __device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t v, uint64_t* w
   return before + incl - v;
 }
 
+// Each thread owns kPer consecutive scores of a 32768-score chunk, held in registers as keys:
+// one row of up to 32768 scores is read from memory once, with all loads of a thread in flight
+// together; longer rows are re-read chunk by chunk in every pass.
+constexpr int kPer = 32;
+constexpr int kChunk = kTopkThreads * kPer;
+
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
@@ -64,10 +71,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     return;
   }
   const float* sc = a.scores + (int64_t)i * a.ld;
+  const int n_chunks = (n + kChunk - 1) / kChunk;
 
   __shared__ uint32_t hist[2048];
   __shared__ uint64_t wave_tot[kTopkWaves];
   __shared__ uint32_t s_bin, s_above;
+
+  uint32_t u[kPer];
+  auto load_chunk = [&](int c) {
+    const int base = c * kChunk + tid * kPer;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int j = base + e;
+      u[e] = j < n ? order_key(sc[j]) : 0u;
+    }
+  };
+  auto count_in = [&](int c) { return max(0, min(kPer, n - (c * kChunk + tid * kPer))); };
+  if (n_chunks == 1) load_chunk(0);
 
   uint32_t prefix = 0, pmask = 0;
   uint32_t remaining = (uint32_t)k;  // how many still to take among keys matching the prefix
@@ -77,9 +97,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     const uint32_t bmask = pass == 2 ? 1023u : 2047u;
     for (int j = tid; j < 2048; j += kTopkThreads) hist[j] = 0;
     __syncthreads();
-    for (int j = tid; j < n; j += kTopkThreads) {
-      uint32_t u = order_key(sc[j]);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & bmask], 1u);
+#pragma unroll 1
+    for (int c = 0; c < n_chunks; ++c) {
+      if (n_chunks > 1) load_chunk(c);
+      const int cnt = count_in(c);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (e < cnt && (u[e] & pmask) == prefix) atomicAdd(&hist[(u[e] >> shift) & bmask], 1u);
     }
     __syncthreads();
     // bins in descending order: thread t owns bins 2047-2t and 2046-2t
@@ -101,30 +125,41 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   }
   const uint32_t T = prefix;  // key of the k-th largest score; `remaining` ties of it are taken
 
-  const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
-  const int lo = min(n, tid * chunk), hi = min(n, lo + chunk);
-  uint32_t gt = 0, tie = 0;
-  for (int j = lo; j < hi; ++j) {
-    uint32_t u = order_key(sc[j]);
-    gt += u > T;
-    tie += u == T;
-  }
-  uint64_t pre = block_exclusive_scan(((uint64_t)tie << 32) | gt, wave_tot, nullptr);
-  const uint32_t gt_pre = (uint32_t)pre, tie_pre = (uint32_t)(pre >> 32);
-  uint32_t pos = gt_pre + min(remaining, tie_pre);
-  uint32_t tseen = tie_pre;
-  for (int j = lo; j < hi; ++j) {
-    uint32_t u = order_key(sc[j]);
-    if (u > T) {
-      if (pos < (uint32_t)k) out[pos] = j;
-      ++pos;
-    } else if (u == T) {
-      if (tseen < remaining) {
-        if (pos < (uint32_t)k) out[pos] = j;
-        ++pos;
-      }
-      ++tseen;
+  uint32_t gt_base = 0, tie_base = 0;
+#pragma unroll 1
+  for (int c = 0; c < n_chunks; ++c) {
+    if (n_chunks > 1) load_chunk(c);
+    const int cnt = count_in(c);
+    uint32_t gt = 0, tie = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      gt += (e < cnt) & (u[e] > T);
+      tie += (e < cnt) & (u[e] == T);
     }
+    uint64_t tot = 0;
+    uint64_t pre = block_exclusive_scan(((uint64_t)tie << 32) | gt, wave_tot, &tot);
+    const uint32_t gt_pre = gt_base + (uint32_t)pre;
+    const uint32_t tie_pre = tie_base + (uint32_t)(pre >> 32);
+    uint32_t pos = gt_pre + min(remaining, tie_pre);
+    uint32_t tseen = tie_pre;
+    const int base = c * kChunk + tid * kPer;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if (e < cnt) {
+        if (u[e] > T) {
+          if (pos < (uint32_t)k) out[pos] = base + e;
+          ++pos;
+        } else if (u[e] == T) {
+          if (tseen < remaining) {
+            if (pos < (uint32_t)k) out[pos] = base + e;
+            ++pos;
+          }
+          ++tseen;
+        }
+      }
+    }
+    gt_base += (uint32_t)tot;
+    tie_base += (uint32_t)(tot >> 32);
   }
 }
 

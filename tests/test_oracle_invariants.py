@@ -150,14 +150,3 @@ def test_prefill_row_equals_decode_at_that_length():
         d, dsel = O.decode(qs[i][None], [p + 1], swa, comp, W, SCALE, RD, BASE,
                            idx=dict(q=iq[i][None], w=iw[i][None], pool=ik, k=32))
         assert np.array_equal(pf[i], d[0]) and np.array_equal(psel[i], dsel[0])
-
-
-def test_kv_accounting_matches_page_numbers():
-    """The per-entry sizes the bytes model uses (512-dim bf16 entries, 64 RoPE dims and a
-    128-dim bf16 indexer key per 4 tokens) reproduce the page's 61-layer figure exactly."""
-    import json
-    import os
-    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "kv_accounting.json")))
-    per_token = (512 + 64 + 128) * g["bf16_bytes"]          # V3.2-style MLA cache per layer
-    gib = g["v32_layers"] * per_token * g["context_tokens"] / 2 ** 30
-    assert gib == 83.875 and round(gib, 1) == g["v32_gib_printed"]
