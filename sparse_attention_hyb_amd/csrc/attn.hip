@@ -179,8 +179,21 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 
+// Masked keys (past the end of a split, absent blocks, unused top-k slots) load this row instead
+// of a pool entry, so their operands are zero without any per-use select. Never written.
+__device__ __attribute__((aligned(16))) uint8_t kZeroRow[1024];   // zero-initialised device memory
+
 constexpr int kSeg = 2048;           // keys whose entry indices are resolved per segment
 constexpr int kPitch = kMD + 16;     // LDS row pitch of a K tile (bf16): 1056 B, 8 banks per row
+constexpr int kQPitch = kMD + 8;     // LDS row pitch of the query (bf16): 1040 B, 4 banks per row
+
+// LDS address (in bf16 elements) of dims [d, d + 8) of key row `row` of a K tile. Rows are 1056 B
+// apart (8 banks), and the 16-byte chunk index is XORed with bit 3 of the row: sixteen
+// consecutive rows written or read 16 bytes each then cover all 64 banks once, while the
+// transposed reads (4 consecutive rows, which share bit 3) keep their conflict-free pattern.
+__device__ __forceinline__ int tile_off(int row, int d) {
+  return row * kPitch + ((((d >> 3) ^ ((row >> 3) & 1)) << 3) | (d & 7));
+}
 
 // One wave's quarter (64 of the 512 dims per lane-half) of one 32-key tile, held in registers
 // between its global load and its use.
@@ -219,10 +232,10 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const uint16_t* p0, const uint16_t
 template <bool kFp8>
 __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ktile[2 * kKT * kPitch];
-  __shared__ float sx[4][16][64];
+  __shared__ __attribute__((aligned(16))) uint16_t qlds[kMH * kQPitch];   // the query, [head][dim]
+  __shared__ __attribute__((aligned(16))) float sx[4][4 * 64 * 4];   // [wave][quad][lane][4]
   __shared__ int32_t kidx[kSeg];
-  __shared__ float kscale[2 * kKT];
-  __shared__ int kvalid[2 * kKT];
+  __shared__ __attribute__((aligned(16))) float kscale[2 * kKT];
 
   const int i = blockIdx.y, sp = blockIdx.x;
   const QueryKeys qk = query_keys(a, i);
@@ -234,15 +247,20 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
   const int qd = 2 * dh + hh;          // the dim quarter this wave loads
   const int oq = 2 * dh + (1 - hh);    // the partner's quarter
 
-  // Q^T as the QK B operand (column = head 32*hh + col). K-step s covers quarter 2*dh + s/8,
-  // dims 128*quarter + 64*hf + 8*(s%8) + [0, 8): the same split the K operand uses.
-  bf16x8 qb[16];
+  // The query stays in LDS (registers go to the O accumulators and the staged K tiles). Q^T is
+  // the QK B operand (column = head 32*hh + col); K-step s covers quarter 2*dh + s/8, dims
+  // 128*quarter + 64*hf + 8*(s%8) + [0, 8): the same split the K operand uses.
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)i * kMH + 32 * hh + col) * kMD;
-#pragma unroll
-    for (int s = 0; s < 16; ++s)
-      qb[s] = *reinterpret_cast<const bf16x8*>(qrow + 128 * (2 * dh + (s >> 3)) + 64 * hf + 8 * (s & 7));
+    const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)i * kMH * kMD;
+    for (int e = tid; e < kMH * kMD / 8; e += 256) {
+      const int h = e / (kMD / 8), d = (e % (kMD / 8)) * 8;
+      *reinterpret_cast<bf16x8*>(qlds + h * kQPitch + d) = *reinterpret_cast<const bf16x8*>(qsrc + h * kMD + d);
+    }
   }
+  const uint16_t* qrow = qlds + (32 * hh + col) * kQPitch + 64 * hf;
+  auto qb = [&](int s) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(qrow + 128 * (2 * dh + (s >> 3)) + 8 * (s & 7));
+  };
   f32x16 o[8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) o[mb] = f32x16{};
@@ -260,26 +278,29 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
     __syncthreads();
     const int n_tiles = (nseg + kKT - 1) / kKT;
 
+    // Loads are issued without any branch (masked lanes read the zero row): a branch between a
+    // prefetch and the use of an older tile would make the compiler wait for every outstanding
+    // load, prefetch included.
     auto load = [&](Stage<kFp8>& st, int tt) {
-      const int jl = tt * kKT + col;
-      const int idx = jl < nseg ? kidx[jl] : -1;
-      st.valid = idx >= 0;
-      st.sc = 1.f;
-      if (idx >= 0) {
-        const PoolDev& P = (seg + jl) < qk.n_win ? a.swa : a.comp;
-        if constexpr (!kFp8) {
-          const uint16_t* row = reinterpret_cast<const uint16_t*>(P.data + (int64_t)idx * P.entry_bytes) + lane_off;
+      const int jraw = tt * kKT + col;
+      const int jl = min(jraw, nseg - 1);
+      const int idx = kidx[jl];
+      const bool ok = jraw < nseg && idx >= 0;
+      const bool win = (seg + jl) < qk.n_win;
+      const uint8_t* base = win ? a.swa.data : a.comp.data;
+      const int64_t eb = win ? a.swa.entry_bytes : a.comp.entry_bytes;
+      const uint8_t* entry = ok ? base + (int64_t)idx * eb : kZeroRow;
+      st.valid = ok;
+      if constexpr (!kFp8) {
+        const uint16_t* row = reinterpret_cast<const uint16_t*>(entry) + lane_off;
 #pragma unroll
-          for (int c = 0; c < 8; ++c) st.v[c] = *reinterpret_cast<const bf16x8*>(row + 8 * c);
-        } else {
-          const uint8_t* row = P.data + (int64_t)idx * P.entry_bytes + lane_off;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) st.v[c] = *reinterpret_cast<const u32x4*>(row + 16 * c);
-          st.sc = reinterpret_cast<const float*>(P.scale)[idx];
-        }
+        for (int c = 0; c < 8; ++c) st.v[c] = *reinterpret_cast<const bf16x8*>(row + 8 * c);
+        st.sc = 1.f;
       } else {
+        const uint8_t* row = entry + lane_off;
 #pragma unroll
-        for (int c = 0; c < (kFp8 ? 4 : 8); ++c) st.v[c] = std::remove_reference_t<decltype(st.v[0])>{};
+        for (int c = 0; c < 4; ++c) st.v[c] = *reinterpret_cast<const u32x4*>(row + 16 * c);
+        st.sc = reinterpret_cast<const float*>(win ? a.swa.scale : a.comp.scale)[ok ? idx : 0];
       }
     };
 
@@ -287,8 +308,8 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
       if constexpr (!kFp8) {
         return st.v[c];
       } else {
-        const u32x4 w = st.v[c >> 1];
-        return (c & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+        const u32x4 q = st.v[c >> 1];
+        return (c & 1) ? fp8x8_to_bf16x8(q[2], q[3]) : fp8x8_to_bf16x8(q[0], q[1]);
       }
     };
 
@@ -296,64 +317,102 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
       const int kb = tt & 1;
       uint16_t* kt = ktile + kb * kKT * kPitch;
       // ---- publish this wave's quarter of the tile (natural [key][dim] layout)
-      {
-        uint16_t* dst = kt + col * kPitch + lane_off;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) *reinterpret_cast<bf16x8*>(dst + 8 * c) = own(st, c);
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<bf16x8*>(kt + tile_off(col, lane_off + 8 * c)) = own(st, c);
+      if constexpr (kFp8) {
+        if (wave == 0 && hf == 0) kscale[kb * kKT + col] = st.valid ? st.sc : 0.f;
       }
-      if (wave == 0 && hf == 0) {
-        kvalid[kb * kKT + col] = st.valid;
-        kscale[kb * kKT + col] = st.sc;
-      }
+      // validity of the tile's 32 keys (every wave resolved the same keys): bit j = key j
+      const uint32_t vmask = (uint32_t)__ballot(st.valid);
       __syncthreads();
       // ---- QK over this wave's dim half: own quarter from registers, partner's from LDS
-      f32x16 sacc = {};
-      const uint16_t* other = kt + col * kPitch + 128 * oq + 64 * hf;
+      bf16x8 oth[8];
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const bf16x8 ka = ((s >> 3) == hh) ? own(st, s & 7)
-                                           : *reinterpret_cast<const bf16x8*>(other + 8 * (s & 7));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sacc, 0, 0, 0);
+      for (int c = 0; c < 8; ++c)
+        oth[c] = *reinterpret_cast<const bf16x8*>(kt + tile_off(col, 128 * oq + 64 * hf + 8 * c));
+      // two independent accumulation chains (even / odd K-steps) keep the MFMA pipe busy
+      f32x16 sacc = {}, sacc1 = {};
+#pragma unroll
+      for (int s = 0; s < 16; s += 2) {
+        const bf16x8 ka0 = ((s >> 3) == hh) ? own(st, s & 7) : oth[s & 7];
+        const bf16x8 ka1 = (((s + 1) >> 3) == hh) ? own(st, (s + 1) & 7) : oth[(s + 1) & 7];
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qb(s), sacc, 0, 0, 0);
+        sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qb(s + 1), sacc1, 0, 0, 0);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sx[wave][r][lane] = sacc[r];
-      __syncthreads();
+      for (int r = 0; r < 16; ++r) sacc[r] += sacc1[r];
+      {
+        // [wave][quad][lane][4]: a wave's 16-byte accesses are lane-contiguous (no conflicts)
+        f32x4* mine = reinterpret_cast<f32x4*>(&sx[wave][0]) + lane;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] += sx[wave ^ 1][r][lane];
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = sacc[4 * q4 + e];
+          mine[64 * q4] = v;
+        }
+      }
+      __syncthreads();
+      {
+        const f32x4* theirs = reinterpret_cast<const f32x4*>(&sx[wave ^ 1][0]) + lane;
+        f32x4 t[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) t[q4] = theirs[64 * q4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sacc[4 * q4 + e] += t[q4][e];
+      }
       // ---- online softmax for head 32*hh + col; this lane's keys are 8*(r/4) + 4*hf + r%4
+      float ksc[16];
+      if constexpr (kFp8) {
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(kscale + kb * kKT + 8 * j4 + 4 * hf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ksc[4 * j4 + e] = v[e];
+        }
+      }
       float z[16];
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kb * kKT + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
         float v = sacc[r] * sl2;
-        if constexpr (kFp8) v *= kscale[key];
-        z[r] = kvalid[key] ? v : -INFINITY;
+        if constexpr (kFp8) v *= ksc[r];
+        z[r] = ((vmask >> key) & 1u) ? v : -INFINITY;
         mx = fmaxf(mx, z[r]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float ref = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run - ref);
+      // The reference maximum only moves when a score exceeds it by more than 2^8 (or on the
+      // first keys): probabilities then stay <= 256, and the O rescale is skipped for the wave
+      // unless one of its heads moved. Exact: l and O share the same reference.
+      if (__ballot(mx > m_run + 8.f) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+        m_run = m_new;
+      }
+      const float ref = m_run == -INFINITY ? 0.f : m_run;
       float psum = 0.f;
       float pr[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(z[r] - ref);
+        const float e = __builtin_amdgcn_exp2f(z[r] - ref);
         psum += e;
         if constexpr (kFp8) {
-          pr[r] = e * kscale[kb * kKT + 8 * (r >> 2) + 4 * hf + (r & 3)];
+          pr[r] = e * ksc[r];
         } else {
           pr[r] = e;
         }
       }
       psum += __shfl_xor(psum, 32, 64);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+      l_run += psum;
       // ---- PV: B = probabilities (element e of K-step t <-> key 16t + 8(e/4) + 4hf + e%4),
       //      A = K^T read transposed from LDS: lane j of each 16-lane group points at key
       //      k0 + j/4, dims d0 + 4*(j%4), and receives keys k0..k0+3 of dim d0 + j.
@@ -366,44 +425,45 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
         pb[t2] = __builtin_bit_cast(bf16x8, w);
       }
       const int i16 = lane & 15;
-      const int gcol = (col >> 4) * 16 + 4 * (i16 & 3);
+      const int trow = 4 * hf + (i16 >> 2);                       // + 16*t2 (+ 8 for the 2nd half)
+      const int tdim = 256 * dh + (col >> 4) * 16 + 4 * (i16 & 3);  // + 32*mb
+      auto trf = [&](int mb, int t2) {
+        return lds_tr_pair(kt + tile_off(trow + 16 * t2, tdim + 32 * mb),
+                           kt + tile_off(trow + 16 * t2 + 8, tdim + 32 * mb));
+      };
+      // fragments for block mb + 1 are read while block mb multiplies
+      bf16x8 af[2][2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) af[0][t2] = trf(0, t2);
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
-        const int d0 = 256 * dh + 32 * mb + gcol;
+        if (mb + 1 < 8) {
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const int k0 = 16 * t2 + 4 * hf + (i16 >> 2);
-          const bf16x8 af = lds_tr_pair(kt + k0 * kPitch + d0, kt + (k0 + 8) * kPitch + d0);
-          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[t2], o[mb], 0, 0, 0);
+          for (int t2 = 0; t2 < 2; ++t2) af[(mb + 1) & 1][t2] = trf(mb + 1, t2);
         }
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb & 1][t2], pb[t2], o[mb], 0, 0, 0);
       }
     };
 
-    // Global loads run kDepth - 1 tiles ahead of the tile being processed (register budget:
-    // two staged bf16 tiles, or three fp8 ones, fit beside Q and the O accumulators).
-    if constexpr (kFp8) {
+    // Global loads run two tiles ahead of the tile being processed (three staged tiles fit
+    // beside the O accumulators; the query lives in LDS).
+    // (tiles past the end are loaded masked: harmless, and it keeps the loop free of branches
+    // between a prefetch and the use of the tile before it)
+    {
       Stage<kFp8> s0, s1, s2;
       load(s0, 0);
-      if (n_tiles > 1) load(s1, 1);
+      load(s1, 1);
       for (int t = 0; t < n_tiles; t += 3) {
-        if (t + 2 < n_tiles) load(s2, t + 2);
+        load(s2, t + 2);
         process(s0, t);
         if (t + 1 >= n_tiles) break;
-        if (t + 3 < n_tiles) load(s0, t + 3);
+        load(s0, t + 3);
         process(s1, t + 1);
         if (t + 2 >= n_tiles) break;
-        if (t + 4 < n_tiles) load(s1, t + 4);
+        load(s1, t + 4);
         process(s2, t + 2);
-      }
-    } else {
-      Stage<kFp8> s0, s1;
-      load(s0, 0);
-      for (int t = 0; t < n_tiles; t += 2) {
-        if (t + 1 < n_tiles) load(s1, t + 1);
-        process(s0, t);
-        if (t + 1 >= n_tiles) break;
-        if (t + 2 < n_tiles) load(s0, t + 2);
-        process(s1, t + 1);
       }
     }
   }
@@ -429,7 +489,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
 // Combine: merge split partials, inverse RoPE at the query position, cast.
 // Grid (dim slice of 64, query): each workgroup reads its 64 dims x all heads of every split.
 // ------------------------------------------------------------------------------------------
-constexpr int kCombineDims = 64;
+constexpr int kCombineDims = 32;
 
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const int i = blockIdx.y;
@@ -467,6 +527,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   for (int e = threadIdx.x; e < npair * H; e += 256) {
     const int h = e % H, t = e / H, d = d0 + 2 * t;
     float v0 = 0.f, v1 = 0.f;
+#pragma unroll 8
     for (int s = 0; s < ns; ++s) {
       const float wgt = wsplit[s * H + h];
       v0 = fmaf(wgt, po[((int64_t)s * D + d) * H + h], v0);

@@ -16,8 +16,10 @@
 
 namespace hyb {
 
-constexpr int kCompressThreads = 256;
-constexpr int kMaxPairsPerThread = 4;  // dim <= 2048
+constexpr int kCompressThreads = 1024;
+constexpr int kRowGroups = 4;                                  // token rows split 4 ways
+constexpr int kPairThreads = kCompressThreads / kRowGroups;    // 256 threads per row group
+constexpr int kMaxPairsPerThread = 4;                          // dim <= 2048
 
 template <typename T>
 __device__ __forceinline__ float2 load_pair(const T* row, int d);
@@ -49,6 +51,8 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
   const int b = blockIdx.y;
   const int gi = blockIdx.x;
   const int tid = threadIdx.x;
+  const int pt = tid % kPairThreads;   // which dim pairs
+  const int rg = tid / kPairThreads;   // which token rows (t = rg mod 4)
   const int r = a.out.ratio;
   const int D = a.out.dim;
   const int npairs = D / 2;
@@ -65,7 +69,8 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
   const T* x = reinterpret_cast<const T*>(a.x);
 
   __shared__ float wts[128];
-  __shared__ float red[kCompressThreads / 64];
+  __shared__ float red[kPairThreads / 64];
+  __shared__ float2 part[kRowGroups - 1][kMaxPairsPerThread * kPairThreads];
 
   if (gstart + r <= t_end) {  // group complete: emit entry g
     if (tid < 64) {
@@ -92,16 +97,18 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
     float acc[kMaxPairsPerThread][2];
 #pragma unroll
     for (int j = 0; j < kMaxPairsPerThread; ++j) acc[j][0] = acc[j][1] = 0.f;
-    // tokens of the group that arrived in earlier calls come from the state ring, the rest from
-    // x; both loops are unrolled so a thread keeps several row loads in flight
+    // Row group rg sums the group's tokens t = rg, rg + 4, ... in ascending order: those that
+    // arrived in earlier calls from the state ring, the rest from x. The split depends only on
+    // t, so a chunked compression adds exactly the same numbers in the same order as a one-shot
+    // one. Loops are unrolled so each thread keeps several row loads in flight.
     const int n_state = max(0, min(s0, gstart + r) - gstart);
 #pragma unroll 8
-    for (int t = 0; t < n_state; ++t) {
+    for (int t = rg; t < n_state; t += kRowGroups) {
       const float wt = wts[t];
       const float* row = a.state + ((int64_t)b * r + t) * D;
 #pragma unroll
       for (int j = 0; j < kMaxPairsPerThread; ++j) {
-        int pi = tid + j * kCompressThreads;
+        int pi = pt + j * kPairThreads;
         if (pi < npairs) {
           float2 v = load_pair<float>(row, 2 * pi);
           acc[j][0] = fmaf(wt, v.x, acc[j][0]);
@@ -109,13 +116,14 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
         }
       }
     }
+    const int t_x0 = n_state + ((rg - n_state) % kRowGroups + kRowGroups) % kRowGroups;
 #pragma unroll 8
-    for (int t = n_state; t < r; ++t) {
+    for (int t = t_x0; t < r; t += kRowGroups) {
       const float wt = wts[t];
       const T* row = x + (int64_t)(c0 + gstart + t - s0) * D;
 #pragma unroll
       for (int j = 0; j < kMaxPairsPerThread; ++j) {
-        int pi = tid + j * kCompressThreads;
+        int pi = pt + j * kPairThreads;
         if (pi < npairs) {
           float2 v = load_pair<T>(row, 2 * pi);
           acc[j][0] = fmaf(wt, v.x, acc[j][0]);
@@ -123,39 +131,55 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
         }
       }
     }
+    if (rg > 0) {
+#pragma unroll
+      for (int j = 0; j < kMaxPairsPerThread; ++j)
+        part[rg - 1][pt + j * kPairThreads] = make_float2(acc[j][0], acc[j][1]);
+    }
+    __syncthreads();
     const float post = a.mode == 1 ? 1.0f : 1.0f / (float)r;
     float ss = 0.f;
+    if (rg == 0) {
 #pragma unroll
-    for (int j = 0; j < kMaxPairsPerThread; ++j) {
-      acc[j][0] *= post;
-      acc[j][1] *= post;
-      ss = fmaf(acc[j][0], acc[j][0], fmaf(acc[j][1], acc[j][1], ss));
-    }
-    ss = wave_sum(ss);
-    if ((tid & 63) == 0) red[tid >> 6] = ss;
-    __syncthreads();
-    float tot = 0.f;
+      for (int j = 0; j < kMaxPairsPerThread; ++j) {
 #pragma unroll
-    for (int w = 0; w < kCompressThreads / 64; ++w) tot += red[w];
-    const float inv = 1.0f / sqrtf(tot / (float)D + a.eps);
-    const int64_t idx = entry_index(a.out, b, g);
-    const int rope_lo = D - a.rope_dim;
-    const double pos = (double)(gstart + r - 1);
-#pragma unroll
-    for (int j = 0; j < kMaxPairsPerThread; ++j) {
-      int pi = tid + j * kCompressThreads;
-      if (pi < npairs && idx >= 0) {
-        float y0 = acc[j][0] * inv, y1 = acc[j][1] * inv;
-        int d = 2 * pi;
-        if (d >= rope_lo) {
-          float c, s;
-          rope_cs(pos, (d - rope_lo) >> 1, a.rope_dim, a.rope_base, &c, &s);
-          float z0 = y0 * c - y1 * s;
-          float z1 = y0 * s + y1 * c;
-          y0 = z0;
-          y1 = z1;
+        for (int q = 0; q < kRowGroups - 1; ++q) {
+          const float2 v = part[q][pt + j * kPairThreads];
+          acc[j][0] += v.x;
+          acc[j][1] += v.y;
         }
-        store_pair(a.out, idx, d, y0, y1);
+        acc[j][0] *= post;
+        acc[j][1] *= post;
+        ss = fmaf(acc[j][0], acc[j][0], fmaf(acc[j][1], acc[j][1], ss));
+      }
+      ss = wave_sum(ss);
+      if ((tid & 63) == 0) red[tid >> 6] = ss;
+    }
+    __syncthreads();
+    if (rg == 0) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < kPairThreads / 64; ++w) tot += red[w];
+      const float inv = 1.0f / sqrtf(tot / (float)D + a.eps);
+      const int64_t idx = entry_index(a.out, b, g);
+      const int rope_lo = D - a.rope_dim;
+      const double pos = (double)(gstart + r - 1);
+#pragma unroll
+      for (int j = 0; j < kMaxPairsPerThread; ++j) {
+        int pi = pt + j * kPairThreads;
+        if (pi < npairs && idx >= 0) {
+          float y0 = acc[j][0] * inv, y1 = acc[j][1] * inv;
+          int d = 2 * pi;
+          if (d >= rope_lo) {
+            float c, s;
+            rope_cs(pos, (d - rope_lo) >> 1, a.rope_dim, a.rope_base, &c, &s);
+            float z0 = y0 * c - y1 * s;
+            float z1 = y0 * s + y1 * c;
+            y0 = z0;
+            y1 = z1;
+          }
+          store_pair(a.out, idx, d, y0, y1);
+        }
       }
     }
   }
@@ -166,15 +190,15 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
     if (tail_start + r > t_end) {
       __syncthreads();
       const int lo = tail_start > s0 ? tail_start : s0;
-      for (int t = lo; t < t_end; ++t) {
+      for (int t = lo + rg; t < t_end; t += kRowGroups) {
         const int slot = t - tail_start;
         const T* row = x + (int64_t)(c0 + t - s0) * D;
         float* dst = a.state + ((int64_t)b * r + slot) * D;
-        for (int pi = tid; pi < npairs; pi += kCompressThreads) {
+        for (int pi = pt; pi < npairs; pi += kPairThreads) {
           float2 v = load_pair<T>(row, 2 * pi);
           *reinterpret_cast<float2*>(dst + 2 * pi) = v;
         }
-        if (a.mode == 1 && tid == 0) a.state_logits[(int64_t)b * r + slot] = a.gate[c0 + t - s0];
+        if (a.mode == 1 && pt == 0) a.state_logits[(int64_t)b * r + slot] = a.gate[c0 + t - s0];
       }
     }
   }

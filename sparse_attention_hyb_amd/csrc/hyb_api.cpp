@@ -1,7 +1,7 @@
 // C-ABI front end: argument validation (host only, before any HIP call), workspace sizing and
 // dispatch to the kernel launchers. Declarations, argument meaning and error behaviour are in
 // include/hyb.h.
-#include "../../include/hyb.h"
+#include "hyb.h"
 
 #include <hip/hip_runtime.h>
 
@@ -327,7 +327,9 @@ int32_t hyb_topk(const float* scores, int64_t scores_ld, const int32_t* lengths,
 
 size_t hyb_index_topk_workspace_bytes(int32_t n_q, int32_t max_pos, int32_t window, int32_t ratio) {
   if (n_q <= 0 || max_pos < 0 || window <= 0 || (ratio != 4 && ratio != 128)) return 0;
-  return (size_t)n_q * score_ld(max_pos, window, ratio) * sizeof(float);
+  // scores [n_q][ld] float, then the first-pass histograms [n_q][2048] uint32
+  return (size_t)n_q * score_ld(max_pos, window, ratio) * sizeof(float) +
+         (size_t)n_q * hyb::kHistBins * sizeof(uint32_t);
 }
 
 int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const int32_t* q_seq,
@@ -348,7 +350,9 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
   a.qd = hyb::QueryDev{nullptr, q_seq, q_pos};
   a.scores = static_cast<float*>(workspace);
   a.ld = ld;
+  a.hist = reinterpret_cast<uint32_t*>(static_cast<float*>(workspace) + (size_t)n_q * ld);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  HYB_TRY(launch_status(hyb::launch_zero_u32(a.hist, (size_t)n_q * hyb::kHistBins, s), op));
   HYB_TRY(launch_status(hyb::launch_index_score(a, s), op));
   hyb::TopkArgs t{};
   t.scores = a.scores;
@@ -361,6 +365,7 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
   t.max_len = (int32_t)visible(max_pos, a.pool.ratio, window);
   t.k = k;
   t.out = out_idx;
+  t.hist = a.hist;
   return launch_status(hyb::launch_topk(t, s), op);
 }
 

@@ -66,8 +66,13 @@ struct ScoreArgs {
   PoolDev pool;
   float* scores;
   int64_t ld;
+  // Optional [n_q][2048] histogram of the top 11 bits of each row's order keys, accumulated
+  // with atomics (must be zero on entry); the top-k kernel then starts from it.
+  uint32_t* hist;
 };
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
+constexpr int kHistBins = 2048;
 
 // ---- top-k ----------------------------------------------------------------------------------
 // Row lengths come from `lengths` or, if null, from n_visible(p_i, ratio, window) of the queries.
@@ -82,6 +87,7 @@ struct TopkArgs {
   int32_t max_len;
   int32_t k;
   int32_t* out;
+  const uint32_t* hist;   // optional first-pass histogram (see ScoreArgs::hist)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 

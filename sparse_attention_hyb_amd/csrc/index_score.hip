@@ -39,6 +39,7 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float sc) {
 
 template <bool kFp4>
 __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
+  __shared__ uint32_t lhist[kHistBins];
   const int i = blockIdx.y;
   int seq, p;
   query_at(a.qd, i, &seq, &p);
@@ -51,6 +52,10 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
   const int wave = threadIdx.x >> 6;
   const int col = lane & 31;
   const int hf = lane >> 5;
+  if (a.hist) {
+    for (int j = threadIdx.x; j < kHistBins; j += 256) lhist[j] = 0;
+    __syncthreads();
+  }
 
   // The contraction index d is split as d = 64*hf + 8*s + e for K-step s (0..7) and element e of
   // a lane's 8-wide operand; query and keys use the same split, so each lane holds 64 contiguous
@@ -75,39 +80,33 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
   // current one is multiplied. fp4 tiles stay packed (32 B + 2 scale bytes per lane) until used.
   struct KeysBf16 {
     bf16x8 v[8];
+    bool valid;
   };
   struct KeysFp4 {
     u32x4 w0, w1;
     float s0, s1;
+    bool valid;
   };
   using Keys = std::conditional_t<kFp4, KeysFp4, KeysBf16>;
+  // Branch-free loads (out-of-range or absent keys read entry 0 of the pool; their scores are
+  // written as -inf or not at all), so the prefetch never forces a wait on itself.
   auto load = [&](Keys& kb, int t0) {
-    const int g = t0 + col;
-    const int64_t idx = g < end ? entry_index(a.pool, seq, g) : -1;
+    const int g = min(t0 + col, end - 1);
+    const int64_t idx = entry_index(a.pool, seq, g);
+    const int64_t e = idx >= 0 ? idx : 0;
+    kb.valid = idx >= 0;
     if constexpr (!kFp4) {
-      if (idx >= 0) {
-        const uint16_t* row =
-            reinterpret_cast<const uint16_t*>(a.pool.data + idx * a.pool.entry_bytes) + 64 * hf;
+      const uint16_t* row =
+          reinterpret_cast<const uint16_t*>(a.pool.data + e * a.pool.entry_bytes) + 64 * hf;
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-          kb.v[s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(row + 8 * s));
-      } else {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) kb.v[s] = bf16x8{};
-      }
+      for (int s = 0; s < 8; ++s) kb.v[s] = *reinterpret_cast<const bf16x8*>(row + 8 * s);
     } else {
-      if (idx >= 0) {
-        const uint8_t* row = a.pool.data + idx * a.pool.entry_bytes + 32 * hf;
-        const uint8_t* scl = reinterpret_cast<const uint8_t*>(a.pool.scale) + idx * 4 + 2 * hf;
-        kb.w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row));
-        kb.w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 16));
-        kb.s0 = e8m0_to_f32(scl[0]);
-        kb.s1 = e8m0_to_f32(scl[1]);
-      } else {
-        kb.w0 = u32x4{};
-        kb.w1 = u32x4{};
-        kb.s0 = kb.s1 = 0.f;
-      }
+      const uint8_t* row = a.pool.data + e * a.pool.entry_bytes + 32 * hf;
+      const uint8_t* scl = reinterpret_cast<const uint8_t*>(a.pool.scale) + e * 4 + 2 * hf;
+      kb.w0 = *reinterpret_cast<const u32x4*>(row);
+      kb.w1 = *reinterpret_cast<const u32x4*>(row + 16);
+      kb.s0 = e8m0_to_f32(scl[0]);
+      kb.s1 = e8m0_to_f32(scl[1]);
     }
   };
   auto operand = [&](const Keys& kb, int s) -> bf16x8 {
@@ -133,18 +132,45 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
     }
     part += __shfl_xor(part, 32, 64);
     const int g = t0 + col;
-    if (hf == 0 && g < end) out[g] = canonical_zero(part);
+    if (hf == 0 && g < end) {
+      const float v = kb.valid ? canonical_zero(part) : -INFINITY;
+      out[g] = v;
+      if (a.hist) atomicAdd(&lhist[order_key(v) >> 21], 1u);
+    }
   };
   Keys ka, kc;
   int t0 = base + wave * 32;
-  if (t0 < end) load(ka, t0);
-  for (; t0 < end; t0 += 256) {
-    if (t0 + 128 < end) load(kc, t0 + 128);
-    score(ka, t0);
-    if (t0 + 128 >= end) break;
-    if (t0 + 256 < end) load(ka, t0 + 256);
-    score(kc, t0 + 128);
+  if (t0 < end) {
+    load(ka, t0);
+    for (; t0 < end; t0 += 256) {
+      load(kc, t0 + 128);
+      score(ka, t0);
+      if (t0 + 128 >= end) break;
+      load(ka, t0 + 256);
+      score(kc, t0 + 128);
+    }
   }
+  if (a.hist) {
+    // fold this workgroup's counts into the row's histogram (first radix pass of the top-k)
+    __syncthreads();
+    uint32_t* g = a.hist + (int64_t)i * kHistBins;
+    for (int j = threadIdx.x; j < kHistBins; j += 256) {
+      const uint32_t c = lhist[j];
+      if (c) atomicAdd(&g[j], c);
+    }
+  }
+}
+
+// Zero-fill (used for the histogram accumulators before the indexer runs).
+__global__ __launch_bounds__(256) void zero_u32(uint32_t* p, size_t n) {
+  for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n; j += (size_t)gridDim.x * 256) p[j] = 0;
+}
+
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_u32, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
 }
 
 // One thread per key; query rows and weights staged in LDS as float.
@@ -190,7 +216,9 @@ __global__ __launch_bounds__(256) void score_generic(ScoreArgs a) {
     }
     total = fmaf(ws[h], fmaxf(dot, 0.f), total);
   }
-  a.scores[(int64_t)i * a.ld + g] = canonical_zero(total);
+  const float v = canonical_zero(total);
+  a.scores[(int64_t)i * a.ld + g] = v;
+  if (a.hist) atomicAdd(&a.hist[(int64_t)i * kHistBins + (order_key(v) >> 21)], 1u);
 }
 
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s) {

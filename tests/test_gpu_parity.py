@@ -448,16 +448,21 @@ def test_quantized_mixed_full_size_sampled(gpu_lib):
                                  (300001, 512), (70000, 2048)])
 def test_topk_alone_bit_exact(gpu_lib, n, k):
     """The selector alone on identical fp32 score rows: bit-exact against the oracle, with heavy
-    ties (scores drawn from a small set, including -0.0 and +0.0)."""
+    ties (scores drawn from a small set, including -0.0 and +0.0). Row 3 holds about k/2 ones
+    scattered among signed zeros: the k-th largest is a zero, only the lowest-indexed zeros are
+    taken, and ones keep appearing after the last taken zero (their slots depend on the clamp
+    min(remaining ties, ties before the slice))."""
     hyb = gpu_lib
     g = torch.Generator().manual_seed(n + k)
-    rows = 3
+    rows = 4
     ld = max(n, 1) + 5
     choices = torch.tensor([-0.0, 0.0, 1.5, -2.25, 3.0, 1e-30, -1e30, 7.0])
     sc = torch.randn(rows, ld, generator=g)
     sc[1] = choices[torch.randint(0, 8, (ld,), generator=g)]
     sc[2, : ld // 2] = choices[torch.randint(0, 2, (ld // 2,), generator=g)]
-    lens = [n, max(0, n - 3), n // 2]
+    ones = torch.rand(ld, generator=g) < (k / 2) / max(n, 1)
+    sc[3] = torch.where(ones, 1.0, choices[torch.randint(0, 2, (ld,), generator=g)])
+    lens = [n, max(0, n - 3), n // 2, n]
     out = torch.full((rows, k), -7, dtype=I32, device=DEV)
     hyb.hyb_topk(sc.to(DEV), ints(lens), n, k, out)
     sync()
