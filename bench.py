@@ -33,6 +33,25 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_mfma_c4_128k_hbm_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the indexer score kernel from the committed counter summary, or None
+    when the kernel's sources have changed since the counters were taken (hash mismatch)."""
+    import hashlib
+    try:
+        line = next(l for l in open(TRAFFIC_PROFILE) if l.startswith("traffic-json:"))
+    except (OSError, StopIteration):
+        return None
+    rec = json.loads(line.split(":", 1)[1])
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, "sparse_attention_hyb_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return rec["traffic_bytes"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -384,7 +403,8 @@ def main():
         "step_bytes": res["step_bytes"],
         "roofline": {"kernel": "score_mfma (indexer scores)", "bound": "hbm",
                      "achieved": res["score_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": res["score_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "frac": res["score_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "traffic_unit": "bytes per launch (FETCH_SIZE x 2 + WRITE_SIZE, copy-calibrated)",
                      "avg_launch_us": res["score_kernel_ms"] * 1e3,
                      "bytes_per_launch": res["score_bytes"]},
         "cpu_baseline": cpu,
