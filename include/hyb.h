@@ -143,7 +143,8 @@ int32_t hyb_swa_insert(const void* x, int32_t x_dtype, const int32_t* cu_seqlens
  * hyb_index_score - indexer scores over the visible compressed entries.
  * [vLLM] "DeepSeek Sparse Attention over compressed tokens"; [SGLang] "indexer top-k".
  *   score[i][g] = sum_h w[i][h] * max(0, q_idx[i][h] . key_g), g = 0 .. n_vis(q_pos[i]) - 1,
- * keys from `idx_pool` rows of sequence q_seq[i]. Entries g >= n_vis are not written.
+ * keys from `idx_pool` rows of sequence q_seq[i]; an entry whose block is absent scores -inf.
+ * Entries g >= n_vis are not written.
  *   q_idx   [n_q][n_heads][idx_pool->dim], q_dtype F32 or BF16
  *   w       float [n_q][n_heads]
  *   q_seq   int32 [n_q] (NULL = identity);  q_pos int32 [n_q]
@@ -168,7 +169,9 @@ int32_t hyb_topk(const float* scores, int64_t scores_ld, const int32_t* lengths,
 /* --------------------------------------------------------------------------------------------
  * hyb_index_topk - hyb_index_score followed by hyb_topk over n_vis(q_pos[i]) entries; the
  * scores live in the workspace (size from hyb_index_topk_workspace_bytes with the same n_q,
- * max_pos, window and ratio).
+ * max_pos, window and ratio) as order keys, next to per-block histograms that the indexer
+ * counts for the selector's first radix pass. The workspace needs no initialisation; its
+ * contents are undefined after the call.
  * ------------------------------------------------------------------------------------------ */
 size_t hyb_index_topk_workspace_bytes(int32_t n_q, int32_t max_pos, int32_t window,
                                       int32_t ratio);

@@ -325,11 +325,19 @@ int32_t hyb_topk(const float* scores, int64_t scores_ld, const int32_t* lengths,
   return launch_status(hyb::launch_topk(a, static_cast<hipStream_t>(stream)), op);
 }
 
+// Workspace of hyb_index_topk: order keys [n_q][ld] (uint32), then the indexer's partial
+// histograms [n_q][part_ld][kTopBins] (uint16), part_ld = ld / kScorePartKeys rounded up.
+static size_t topk_part_ld(int64_t ld) {
+  return (size_t)((ld + hyb::kScorePartKeys - 1) / hyb::kScorePartKeys);
+}
+static size_t topk_ws_bytes(int32_t n_q, int64_t ld) {
+  return (size_t)n_q * ld * sizeof(uint32_t) +
+         (size_t)n_q * topk_part_ld(ld) * hyb::kTopBins * sizeof(uint16_t);
+}
+
 size_t hyb_index_topk_workspace_bytes(int32_t n_q, int32_t max_pos, int32_t window, int32_t ratio) {
   if (n_q <= 0 || max_pos < 0 || window <= 0 || (ratio != 4 && ratio != 128)) return 0;
-  // scores [n_q][ld] float, then the first-pass histograms [n_q][2048] uint32
-  return (size_t)n_q * score_ld(max_pos, window, ratio) * sizeof(float) +
-         (size_t)n_q * hyb::kHistBins * sizeof(uint32_t);
+  return topk_ws_bytes(n_q, (int64_t)score_ld(max_pos, window, ratio));
 }
 
 int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const int32_t* q_seq,
@@ -350,9 +358,9 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
   a.qd = hyb::QueryDev{nullptr, q_seq, q_pos};
   a.scores = static_cast<float*>(workspace);
   a.ld = ld;
-  a.hist = reinterpret_cast<uint32_t*>(static_cast<float*>(workspace) + (size_t)n_q * ld);
+  a.part_hist = reinterpret_cast<uint16_t*>(static_cast<uint32_t*>(workspace) + (size_t)n_q * ld);
+  a.part_ld = (int32_t)topk_part_ld(ld);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  HYB_TRY(launch_status(hyb::launch_zero_u32(a.hist, (size_t)n_q * hyb::kHistBins, s), op));
   HYB_TRY(launch_status(hyb::launch_index_score(a, s), op));
   hyb::TopkArgs t{};
   t.scores = a.scores;
@@ -365,7 +373,8 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
   t.max_len = (int32_t)visible(max_pos, a.pool.ratio, window);
   t.k = k;
   t.out = out_idx;
-  t.hist = a.hist;
+  t.part_hist = a.part_hist;
+  t.part_ld = a.part_ld;
   return launch_status(hyb::launch_topk(t, s), op);
 }
 

@@ -66,13 +66,16 @@ struct ScoreArgs {
   PoolDev pool;
   float* scores;
   int64_t ld;
-  // Optional [n_q][2048] histogram of the top 11 bits of each row's order keys, accumulated
-  // with atomics (must be zero on entry); the top-k kernel then starts from it.
-  uint32_t* hist;
+  // Optional, for the selector that follows: each workgroup's histogram of the top kTopBits
+  // bits of the order keys of its kScorePartKeys keys, [n_q][part_ld][kTopBins] uint16; the rows
+  // then hold the order keys (uint32 bits) instead of the float scores.
+  uint16_t* part_hist;
+  int32_t part_ld;
 };
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s);
-hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
-constexpr int kHistBins = 2048;
+constexpr int kTopBits = 10;                  // the selector's first radix pass (then 11 + 11)
+constexpr int kTopBins = 1 << kTopBits;
+constexpr int kScorePartKeys = 1024;          // keys per partial histogram (one indexer workgroup)
 
 // ---- top-k ----------------------------------------------------------------------------------
 // Row lengths come from `lengths` or, if null, from n_visible(p_i, ratio, window) of the queries.
@@ -87,7 +90,10 @@ struct TopkArgs {
   int32_t max_len;
   int32_t k;
   int32_t* out;
-  const uint32_t* hist;   // optional first-pass histogram (see ScoreArgs::hist)
+  // Optional (after the indexer, see ScoreArgs::part_hist): the rows hold order keys and these
+  // partial histograms give the first radix pass.
+  const uint16_t* part_hist;
+  int32_t part_ld;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 

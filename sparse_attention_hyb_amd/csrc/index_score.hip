@@ -12,13 +12,16 @@
 //    keys as N; each lane then owns one key column and 32 of its heads, so the ReLU-weighted head
 //    sum is 32 in-lane FMAs plus one cross-half add.
 //  * score_generic: any (heads x dim) <= 8192, fp32 / bf16 / fp4 - one thread per key.
+// Both can also count, per workgroup of kScorePartKeys keys, a histogram of the top kTopBits bits of
+// the scores' order keys for the selector that follows (then the rows hold the order keys): the first
+// radix pass of the top-k rides along with the score stream.
 #include <type_traits>
 
 #include "common.h"
 
 namespace hyb {
 
-constexpr int kScoreKeysPerBlock = 1024;  // keys per workgroup in the MFMA kernel
+constexpr int kScoreKeysPerBlock = kScorePartKeys;  // keys per workgroup
 constexpr int kMfmaHeads = 64;
 constexpr int kMfmaDim = 128;
 
@@ -37,9 +40,22 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float sc) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// Writes a workgroup's LDS histogram (counts <= kScorePartKeys) as its uint16 partial histogram:
+// 256 threads, kTopBins / 256 bins each.
+__device__ __forceinline__ void store_part_hist(const ScoreArgs& a, const uint32_t* lhist, int i,
+                                                int blk) {
+  static_assert(kTopBins == 4 * 256, "four bins per thread");
+  __syncthreads();
+  const int t = threadIdx.x;
+  uint2 w;
+  w.x = lhist[4 * t] | (lhist[4 * t + 1] << 16);
+  w.y = lhist[4 * t + 2] | (lhist[4 * t + 3] << 16);
+  *reinterpret_cast<uint2*>(a.part_hist + ((int64_t)i * a.part_ld + blk) * kTopBins + 4 * t) = w;
+}
+
 template <bool kFp4>
 __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
-  __shared__ uint32_t lhist[kHistBins];
+  __shared__ uint32_t lhist[kTopBins];
   const int i = blockIdx.y;
   int seq, p;
   query_at(a.qd, i, &seq, &p);
@@ -52,8 +68,8 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
   const int wave = threadIdx.x >> 6;
   const int col = lane & 31;
   const int hf = lane >> 5;
-  if (a.hist) {
-    for (int j = threadIdx.x; j < kHistBins; j += 256) lhist[j] = 0;
+  if (a.part_hist) {
+    for (int j = threadIdx.x; j < kTopBins; j += 256) lhist[j] = 0;
     __syncthreads();
   }
 
@@ -134,8 +150,13 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
     const int g = t0 + col;
     if (hf == 0 && g < end) {
       const float v = kb.valid ? canonical_zero(part) : -INFINITY;
-      out[g] = v;
-      if (a.hist) atomicAdd(&lhist[order_key(v) >> 21], 1u);
+      if (a.part_hist) {
+        const uint32_t key = order_key(v);
+        reinterpret_cast<uint32_t*>(out)[g] = key;
+        atomicAdd(&lhist[key >> (32 - kTopBits)], 1u);
+      } else {
+        out[g] = v;
+      }
     }
   };
   Keys ka, kc;
@@ -150,37 +171,19 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
       score(kc, t0 + 128);
     }
   }
-  if (a.hist) {
-    // fold this workgroup's counts into the row's histogram (first radix pass of the top-k)
-    __syncthreads();
-    uint32_t* g = a.hist + (int64_t)i * kHistBins;
-    for (int j = threadIdx.x; j < kHistBins; j += 256) {
-      const uint32_t c = lhist[j];
-      if (c) atomicAdd(&g[j], c);
-    }
-  }
+  if (a.part_hist) store_part_hist(a, lhist, i, blockIdx.x);
 }
 
-// Zero-fill (used for the histogram accumulators before the indexer runs).
-__global__ __launch_bounds__(256) void zero_u32(uint32_t* p, size_t n) {
-  for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n; j += (size_t)gridDim.x * 256) p[j] = 0;
-}
-
-hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  const size_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(zero_u32, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
-
-// One thread per key; query rows and weights staged in LDS as float.
+// One thread per key (workgroups of kScorePartKeys keys, four per thread); query rows and weights
+// staged in LDS as float.
 __global__ __launch_bounds__(256) void score_generic(ScoreArgs a) {
   extern __shared__ float sm[];
+  __shared__ uint32_t lhist[kTopBins];
   const int i = blockIdx.y;
   int seq, p;
   query_at(a.qd, i, &seq, &p);
   const int nv = min(n_visible(p, a.pool.ratio, a.window), n_visible(a.max_pos, a.pool.ratio, a.window));
-  const int base = blockIdx.x * 256;
+  const int base = blockIdx.x * kScorePartKeys;
   if (base >= nv) return;
   const int H = a.n_heads, Dk = a.pool.dim;
   float* qs = sm;
@@ -191,34 +194,46 @@ __global__ __launch_bounds__(256) void score_generic(ScoreArgs a) {
                              : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[off]);
   }
   for (int h = threadIdx.x; h < H; h += 256) ws[h] = a.w[(int64_t)i * H + h];
+  if (a.part_hist)
+    for (int j = threadIdx.x; j < kTopBins; j += 256) lhist[j] = 0;
   __syncthreads();
-  const int g = base + threadIdx.x;
-  if (g >= nv) return;
-  const int64_t idx = entry_index(a.pool, seq, g);
-  if (idx < 0) return;
-  const uint8_t* row = a.pool.data + idx * a.pool.entry_bytes;
-  float total = 0.f;
-  for (int h = 0; h < H; ++h) {
-    float dot = 0.f;
-    for (int d = 0; d < Dk; ++d) {
-      float kd;
-      if (a.pool.dtype == F32) {
-        kd = reinterpret_cast<const float*>(row)[d];
-      } else if (a.pool.dtype == BF16) {
-        kd = bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[d]);
-      } else {
-        uint32_t byte = row[d >> 1];
-        uint32_t nib = (d & 1) ? (byte >> 4) : (byte & 0xfu);
-        const uint8_t* scl = reinterpret_cast<const uint8_t*>(a.pool.scale) + idx * (Dk / 32);
-        kd = fp4_to_f32(nib) * e8m0_to_f32(scl[d >> 5]);
+  for (int r = 0; r < kScorePartKeys / 256; ++r) {
+    const int g = base + threadIdx.x + 256 * r;
+    if (g >= nv) break;
+    const int64_t idx = entry_index(a.pool, seq, g);
+    float v = -INFINITY;
+    if (idx >= 0) {
+      const uint8_t* row = a.pool.data + idx * a.pool.entry_bytes;
+      float total = 0.f;
+      for (int h = 0; h < H; ++h) {
+        float dot = 0.f;
+        for (int d = 0; d < Dk; ++d) {
+          float kd;
+          if (a.pool.dtype == F32) {
+            kd = reinterpret_cast<const float*>(row)[d];
+          } else if (a.pool.dtype == BF16) {
+            kd = bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[d]);
+          } else {
+            uint32_t byte = row[d >> 1];
+            uint32_t nib = (d & 1) ? (byte >> 4) : (byte & 0xfu);
+            const uint8_t* scl = reinterpret_cast<const uint8_t*>(a.pool.scale) + idx * (Dk / 32);
+            kd = fp4_to_f32(nib) * e8m0_to_f32(scl[d >> 5]);
+          }
+          dot = fmaf(qs[h * Dk + d], kd, dot);
+        }
+        total = fmaf(ws[h], fmaxf(dot, 0.f), total);
       }
-      dot = fmaf(qs[h * Dk + d], kd, dot);
+      v = canonical_zero(total);
     }
-    total = fmaf(ws[h], fmaxf(dot, 0.f), total);
+    if (a.part_hist) {
+      const uint32_t key = order_key(v);
+      reinterpret_cast<uint32_t*>(a.scores)[(int64_t)i * a.ld + g] = key;
+      atomicAdd(&lhist[key >> (32 - kTopBits)], 1u);
+    } else {
+      a.scores[(int64_t)i * a.ld + g] = v;
+    }
   }
-  const float v = canonical_zero(total);
-  a.scores[(int64_t)i * a.ld + g] = v;
-  if (a.hist) atomicAdd(&a.hist[(int64_t)i * kHistBins + (order_key(v) >> 21)], 1u);
+  if (a.part_hist) store_part_hist(a, lhist, i, blockIdx.x);
 }
 
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s) {
@@ -235,7 +250,7 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s) {
     else
       hipLaunchKernelGGL(score_mfma<true>, grid, dim3(256), 0, s, a);
   } else {
-    dim3 grid((max_nv + 255) / 256, a.n_q);
+    dim3 grid((max_nv + kScorePartKeys - 1) / kScorePartKeys, a.n_q);
     size_t lds = sizeof(float) * ((size_t)a.n_heads * a.pool.dim + a.n_heads);
     hipLaunchKernelGGL(score_generic, grid, dim3(256), lds, s, a);
   }

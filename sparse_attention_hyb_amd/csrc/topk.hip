@@ -5,11 +5,17 @@
 // compressed tokens").
 //
 // One 1024-thread workgroup per row. Scores become order-preserving 32-bit keys held in
-// registers (32 consecutive scores per thread); three radix passes (11 + 11 + 10 bits,
-// histograms in LDS) find the k-th largest key T and how many of the keys equal to T are taken
-// (the lowest-indexed ones). Because every thread owns a contiguous index range, one workgroup
-// scan of its "> T" and "== T" counts gives each chosen index its output slot directly - the
-// output is ascending without a sort.
+// registers (32 consecutive scores per thread). Three radix passes (10 + 11 + 11 bits, histograms
+// in LDS) find the k-th largest key T and how many of the keys equal to T are taken (the
+// lowest-indexed ones). The first pass either comes from the indexer (per-workgroup partial
+// histograms written while it scored the row, which then holds order keys) or is counted here.
+// Because every thread owns a contiguous index range, one workgroup scan of its "> T" and "== T"
+// counts gives each chosen index its output slot directly - the output is ascending without a sort.
+//
+// Short list: after the first pass only keys whose top 10 bits are >= b0 (those of the k-th key)
+// can be chosen. When they number at most kListCap (the common case: the keys above bin b0 plus
+// those in it), they are compacted with their indices into LDS in index order and the other two
+// passes and the final selection run over that list instead of over every key of the row.
 #include "common.h"
 
 namespace hyb {
@@ -36,6 +42,50 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
   return before + incl - v;
 }
 
+// Histograms live in LDS with one padding word after every 32 bins: bin b at hp(b). A lane that
+// reads 32 consecutive bins then starts 33 words after its neighbour, so the 64 lanes of a wave
+// hit 64 different banks.
+__device__ __forceinline__ int hp(uint32_t b) { return (int)(b + (b >> 5)); }
+constexpr int kHistWords = 2048 + 2048 / 32;   // padded 2048-bin histogram
+
+// Bin holding the `remaining`-th largest key of an nbins-bin histogram (nbins = 1024 or 2048,
+// bins in ascending key order) and the number of keys in the bins above it. Wave 0 searches:
+// lane l sums the 32-bin group [nbins - 32(l+1), nbins - 32l), one wave scan finds the group
+// that holds the bin, a second scan over that group's 32 bins (one per lane, descending) finds
+// the bin. The result reaches every thread through LDS (one barrier). The histogram must hold at
+// least `remaining` keys.
+__device__ __forceinline__ void select_bin(const uint32_t* hist, int nbins, uint32_t remaining,
+                                           uint32_t* res, uint32_t* bin, uint32_t* above) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int groups = nbins >> 5;
+    uint32_t sum = 0;
+    if (lane < groups) {
+      const uint32_t* g = hist + 33 * (groups - 1 - lane);
+#pragma unroll
+      for (int m = 0; m < 32; ++m) sum += g[m];
+    }
+    const uint32_t incl = wave_inclusive_scan(sum);
+    const uint32_t excl = incl - sum;
+    const uint64_t own = __ballot(excl < remaining && incl >= remaining);
+    const int grp = own ? __builtin_ctzll(own) : 0;
+    const uint32_t grp_above = (uint32_t)__builtin_amdgcn_readlane((int)excl, grp);
+    const int top = nbins - 1 - 32 * grp;
+    const uint32_t c = lane < 32 ? hist[hp(top - lane)] : 0u;
+    const uint32_t incl2 = wave_inclusive_scan(c) + grp_above;
+    const uint32_t excl2 = incl2 - c;
+    const uint64_t hit = __ballot(lane < 32 && excl2 < remaining && incl2 >= remaining);
+    const int j = hit ? __builtin_ctzll(hit) : 0;
+    if (lane == j) {
+      res[0] = (uint32_t)(top - j);
+      res[1] = excl2;
+    }
+  }
+  __syncthreads();
+  *bin = res[0];
+  *above = res[1];
+}
+
 // Each thread owns kPer consecutive scores of a chunk of kChunk, held in registers as keys. A
 // chunk is fetched with coalesced 16-byte loads and redistributed through LDS (row pitch padded
 // to 36 words so the per-thread reads do not collide in banks); rows longer than one chunk are
@@ -44,9 +94,29 @@ constexpr int kPer = 32;
 constexpr int kChunk = kTopkThreads * kPer;
 constexpr int kStagePitch = kPer + 4;  // words per thread's slice in the staging area
 
-// Dynamic LDS: staging [kTopkThreads][kStagePitch] words (also reused for the per-wave
-// histograms of the first pass: kTopkWaves x 2048 words), then hist[2048].
-constexpr size_t kTopkLds = sizeof(uint32_t) * ((size_t)kTopkThreads * kStagePitch + kHistBins);
+// Dynamic LDS: staging [kTopkThreads][kStagePitch] words (reused for the per-wave histograms of a
+// counted first pass, kTopkWaves x kTopWords, and for the short list), then the histogram.
+constexpr int kTopWords = kTopBins + kTopBins / 32;   // padded first-pass histogram
+constexpr size_t kTopkLds = sizeof(uint32_t) * ((size_t)kTopkThreads * kStagePitch + kHistWords);
+static_assert(kTopkWaves * kTopWords <= kTopkThreads * kStagePitch, "per-wave histograms fit");
+static_assert(kTopBins == kTopkThreads, "the counted first pass merges one bin per thread");
+constexpr int kShift0 = 32 - kTopBits;       // 22: first pass = key bits 22..31
+constexpr int kBits12 = kShift0 / 2;         // 11: second pass bits 11..21, third 0..10
+constexpr int kListCap = 16384;   // short-list entries: keys then indices in the staging area
+static_assert(2 * kListCap <= kTopkThreads * kStagePitch, "short list fits the staging area");
+
+// Row length of query i.
+__device__ __forceinline__ int topk_row_len(const TopkArgs& a, int i) {
+  int n;
+  if (a.lengths) {
+    n = a.lengths[i];
+  } else {
+    int seq, p;
+    query_at(a.qd, i, &seq, &p);
+    n = n_visible(p, a.ratio, a.window);
+  }
+  return max(0, min(n, a.max_len));
+}
 
 // kMulti: rows may exceed one chunk (launched when max_len > kChunk); the single-chunk form keeps
 // the row in registers from the start and needs far fewer registers.
@@ -56,20 +126,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   uint32_t* stage = tk_lds;
   uint32_t* hist = tk_lds + kTopkThreads * kStagePitch;
   __shared__ uint32_t wave_tot[kTopkWaves];
-  __shared__ uint32_t s_bin, s_above;
+  __shared__ uint32_t sel_res[2];
 
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  int n;
-  if (a.lengths) {
-    n = a.lengths[i];
-  } else {
-    int seq, p;
-    query_at(a.qd, i, &seq, &p);
-    n = n_visible(p, a.ratio, a.window);
-  }
-  n = max(0, min(n, a.max_len));
+  const int n = topk_row_len(a, i);
   const int k = a.k;
   int* out = a.out + (int64_t)i * k;
   if (n <= k) {
@@ -77,30 +139,69 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     return;
   }
   const float* sc = a.scores + (int64_t)i * a.ld;
+  const bool keys_in = a.part_hist != nullptr;   // the indexer stored order keys
   const bool aligned16 = ((reinterpret_cast<uintptr_t>(sc) & 15u) == 0);
   const int n_chunks = kMulti ? (n + kChunk - 1) / kChunk : 1;
 
+  // First-pass histogram from the indexer's partials (kTopBins uint16 bins = 512 words each):
+  // thread t reads word t % 512 (bins 2w, 2w+1) of partials t / 512 + 2j. The loads of the
+  // first kPartsInFlight partials are issued before the row's own loads (clamped, not branched)
+  // and consumed after them, so both are in flight together.
+  constexpr int kPartWords = kTopBins / 2;
+  constexpr int kPartGroups = kTopkThreads / kPartWords;            // 2
+  constexpr int kPartsInFlight = kChunk / kScorePartKeys;            // 32
+  constexpr int kPartLoads = kPartsInFlight / kPartGroups;           // 16 per thread
+  const int nb = keys_in ? (n + kScorePartKeys - 1) / kScorePartKeys : 0;
+  const int pwd = tid % kPartWords, pg = tid / kPartWords;
+  const uint32_t* ph =
+      keys_in ? reinterpret_cast<const uint32_t*>(a.part_hist + (int64_t)i * a.part_ld * kTopBins) + pwd
+              : nullptr;
+  uint32_t pw[kPartLoads];
+  if (keys_in) {
+#pragma unroll
+    for (int q = 0; q < kPartLoads; ++q)
+      pw[q] = ph[(int64_t)min(pg + kPartGroups * q, nb - 1) * kPartWords];
+  }
+  for (int j = tid; j < kHistWords; j += kTopkThreads) hist[j] = 0;   // before the first pass
+
+  // Row loads never branch per lane (a branch between a load and its use makes the compiler wait
+  // for every load in flight): 16-byte loads from addresses clamped into the row's ld, or, for
+  // unaligned rows, 4-byte loads clamped into [0, n); elements past n are masked to key 0.
+  const bool vec_ok = aligned16 && (a.ld & 3) == 0 && a.ld >= 4;
+  const int vec_last = (int)min<int64_t>(a.ld - 4, INT32_MAX - 4);
   uint32_t u[kPer];
   auto load_chunk = [&](int c) {
     const int base = c * kChunk;
     __syncthreads();  // the staging area may still hold histograms or the previous chunk
     // coalesced: thread t moves elements base + 4*(t + 1024*q) .. +3 for q = 0..7
+    u32x4 v[kPer / 4];
+    if (vec_ok) {
+#pragma unroll
+      for (int q = 0; q < kPer / 4; ++q) {
+        const int j = base + 4 * (tid + kTopkThreads * q);
+        const f32x4 f = *reinterpret_cast<const f32x4*>(sc + min(j, vec_last));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = keys_in ? __float_as_uint(f[e]) : order_key(f[e]);
+          v[q][e] = j + e < n ? key : 0u;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kPer / 4; ++q) {
+        const int j = base + 4 * (tid + kTopkThreads * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float f = sc[min(j + e, n - 1)];
+          const uint32_t key = keys_in ? __float_as_uint(f) : order_key(f);
+          v[q][e] = j + e < n ? key : 0u;
+        }
+      }
+    }
 #pragma unroll
     for (int q = 0; q < kPer / 4; ++q) {
-      const int j = base + 4 * (tid + kTopkThreads * q);
-      u32x4 v;
-      if (aligned16 && j + 3 < n) {
-        const f32x4 f = *reinterpret_cast<const f32x4*>(sc + j);
-        v[0] = order_key(f[0]);
-        v[1] = order_key(f[1]);
-        v[2] = order_key(f[2]);
-        v[3] = order_key(f[3]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = j + e < n ? order_key(sc[j + e]) : 0u;
-      }
-      const int jj = j - base;  // element within the chunk: owner thread jj / 32, slot jj % 32
-      *reinterpret_cast<u32x4*>(stage + (jj / kPer) * kStagePitch + (jj % kPer)) = v;
+      const int jj = 4 * (tid + kTopkThreads * q);  // owner thread jj / 32, slot jj % 32
+      *reinterpret_cast<u32x4*>(stage + (jj / kPer) * kStagePitch + (jj % kPer)) = v[q];
     }
     __syncthreads();
 #pragma unroll
@@ -126,100 +227,150 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   };
   if (!kMulti || n_chunks == 1) load_chunk(0);
 
-  uint32_t prefix = 0, pmask = 0;
-  uint32_t remaining = (uint32_t)k;  // how many still to take among keys matching the prefix
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t bmask = pass == 2 ? 1023u : 2047u;
-    if (pass == 0 && a.hist) {
-      // the indexer already counted the top 11 bits of every score of this row
-      __syncthreads();
-      const uint32_t* g = a.hist + (int64_t)i * kHistBins;
-      for (int j = tid; j < kHistBins; j += kTopkThreads) hist[j] = g[j];
-      __syncthreads();
-    } else {
-      // the first pass counts into per-wave histograms (the busiest bins would otherwise
-      // serialise atomics of all waves) laid over the staging area, once its data is in registers
-      const bool private_hist = pass == 0 && n_chunks == 1;
-      uint32_t* h = private_hist ? stage + wave * kHistBins : hist;
-      __syncthreads();
-      if (private_hist) {
-        for (int j = lane; j < kHistBins; j += 64) h[j] = 0;
-      } else {
-        for (int j = tid; j < kHistBins; j += kTopkThreads) hist[j] = 0;
-      }
-      __syncthreads();
-#pragma unroll 1
-      for (int c = 0; c < n_chunks; ++c) {
-        if (kMulti && n_chunks > 1) load_chunk(c);
-        uint32_t m = match_mask(valid_mask(c), pmask, prefix);
-        if (pass == 0) {
+  // ---- first pass (top kTopBits bits)
+  if (keys_in) {
+    uint32_t h0 = 0, h1 = 0;
 #pragma unroll
-          for (int e = 0; e < kPer; ++e)
-            if ((m >> e) & 1u) atomicAdd(&h[u[e] >> shift], 1u);
-        } else {
-          // later passes see few matching keys: visit only those
-          while (m) {
-            const int e = __builtin_ctz(m);
-            m &= m - 1;
-            uint32_t ue = 0;
+    for (int q = 0; q < kPartLoads; ++q) {
+      const uint32_t on = pg + kPartGroups * q < nb ? 0xffffffffu : 0u;
+      h0 += pw[q] & 0xffffu & on;
+      h1 += (pw[q] >> 16) & on;
+    }
+    for (int b = pg + kPartsInFlight; b < nb; b += kPartGroups) {   // rows longer than one chunk
+      const uint32_t w = ph[(int64_t)b * kPartWords];
+      h0 += w & 0xffffu;
+      h1 += w >> 16;
+    }
+    if (kMulti && n_chunks > 1) __syncthreads();   // no staging barrier since the clearing
+    atomicAdd(&hist[hp(2 * pwd)], h0);
+    atomicAdd(&hist[hp(2 * pwd + 1)], h1);
+    __syncthreads();
+  } else {
+    // counted into per-wave histograms (the busiest bins would otherwise serialise atomics of all
+    // waves) laid over the staging area, once its data is in registers
+    const bool private_hist = n_chunks == 1;
+    uint32_t* h = private_hist ? stage + wave * kTopWords : hist;
+    __syncthreads();
+    if (private_hist) {
+      for (int j = lane; j < kTopWords; j += 64) h[j] = 0;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 0; c < n_chunks; ++c) {
+      if (kMulti && n_chunks > 1) load_chunk(c);
+      const uint32_t m = valid_mask(c);
 #pragma unroll
-            for (int q = 0; q < kPer; ++q) ue = q == e ? u[q] : ue;
-            atomicAdd(&h[(ue >> shift) & bmask], 1u);
-          }
+      for (int e = 0; e < kPer; ++e)
+        if ((m >> e) & 1u) atomicAdd(&h[hp(u[e] >> kShift0)], 1u);
+    }
+    __syncthreads();
+    if (private_hist) {
+      const int j = hp(tid);   // kTopBins == kTopkThreads: one bin per thread
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < kTopkWaves; ++w) t += stage[w * kTopWords + j];
+      hist[j] = t;
+      __syncthreads();
+    }
+  }
+  uint32_t b0, above0;
+  select_bin(hist, kTopBins, (uint32_t)k, sel_res, &b0, &above0);
+  uint32_t prefix = b0 << kShift0, pmask = ~0u << kShift0;
+  uint32_t remaining = (uint32_t)k - above0;   // still to take among keys matching the prefix
+
+  // ---- short list (single chunk): keys whose top bits are >= b0, with their indices, into LDS
+  if (!kMulti) {
+    const uint32_t lo = prefix;
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) m |= (uint32_t)(u[e] >= lo) << e;
+    m &= valid_mask(0);
+    uint32_t total = 0;
+    // (its barriers also order every staging read before the list overwrites the staging area)
+    const uint32_t o = block_exclusive_scan(__builtin_popcount(m), wave_tot, &total);
+    if (total <= (uint32_t)kListCap) {
+      uint32_t* lkey = stage;
+      int32_t* lidx = reinterpret_cast<int32_t*>(stage + kListCap);
+      // element e goes to slot o + (number of kept elements before e): no data-dependent loop
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        if ((m >> e) & 1u) {
+          const uint32_t slot = o + __builtin_popcount(m & ((1u << e) - 1u));
+          lkey[slot] = u[e];
+          lidx[slot] = tid * kPer + e;
         }
       }
-      __syncthreads();
-      if (private_hist) {
-        for (int j = tid; j < kHistBins; j += kTopkThreads) {
-          uint32_t t = 0;
-#pragma unroll
-          for (int w = 0; w < kTopkWaves; ++w) t += stage[w * kHistBins + j];
-          hist[j] = t;
+#pragma unroll 1
+      for (int shift = kBits12; shift >= 0; shift -= kBits12) {
+        for (int j = tid; j < kHistWords; j += kTopkThreads) hist[j] = 0;
+        __syncthreads();   // list written (first time), histogram cleared
+        for (int j = tid; j < (int)total; j += kTopkThreads) {
+          const uint32_t key = lkey[j];
+          if ((key & pmask) == prefix) atomicAdd(&hist[hp((key >> shift) & 2047u)], 1u);
         }
         __syncthreads();
+        uint32_t b, ab;
+        select_bin(hist, 2048, remaining, sel_res, &b, &ab);
+        prefix |= b << shift;
+        pmask |= 2047u << shift;
+        remaining -= ab;
       }
-    }
-    // Wave 0 finds the bin holding the remaining-th largest key: lane l sums 32 bins (in
-    // descending order), one wave scan, then the owning lane walks its 32 bins in registers.
-    if (wave == 0) {
-      uint32_t hb[32];
-      const u32x4* hv = reinterpret_cast<const u32x4*>(hist + kHistBins - 32 * (lane + 1));
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const u32x4 v = hv[q];
-        hb[31 - 4 * q] = v[0];
-        hb[30 - 4 * q] = v[1];
-        hb[29 - 4 * q] = v[2];
-        hb[28 - 4 * q] = v[3];
+      const uint32_t T = prefix;   // the k-th largest key; `remaining` keys equal to it are taken
+      // thread t owns list positions [j0, j1), in index order
+      const int C = ((int)total + kTopkThreads - 1) / kTopkThreads;
+      const int j0 = min((int)total, tid * C), j1 = min((int)total, j0 + C);
+      uint32_t gt = 0, tie = 0;
+      for (int j = j0; j < j1; ++j) {
+        gt += lkey[j] > T;
+        tie += lkey[j] == T;
       }
-      uint32_t sum = 0;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) sum += hb[e];
-      const uint32_t incl = wave_inclusive_scan(sum);
-      const uint32_t excl = incl - sum;
-      if (excl < remaining && incl >= remaining) {
-        uint32_t above = excl;
-        int found = 31;
-        uint32_t found_above = 0;
-        bool done = false;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          const bool hit = !done && above + hb[e] >= remaining;
-          found = hit ? e : found;
-          found_above = hit ? above : found_above;
-          done = done || hit;
-          above += hb[e];
+      // counts <= kListCap < 2^16: both fit 16 bits of one word
+      const uint32_t pre = block_exclusive_scan((tie << 16) | gt, wave_tot, nullptr);
+      // signed clamps (ties still to take when this thread's keys begin may be negative)
+      const int32_t left = (int32_t)remaining - (int32_t)(pre >> 16);
+      uint32_t pos = (pre & 0xffffu) + (uint32_t)((int32_t)remaining - max(left, 0));
+      int32_t tseen = 0;
+      for (int j = j0; j < j1; ++j) {
+        const uint32_t key = lkey[j];
+        bool take = key > T;
+        if (key == T) {
+          take = tseen < left;
+          ++tseen;
         }
-        s_bin = (uint32_t)(kHistBins - 1 - 32 * lane - found);
-        s_above = found_above;
+        if (take) {
+          if (pos < (uint32_t)k) out[pos] = lidx[j];
+          ++pos;
+        }
+      }
+      return;
+    }
+  }
+
+  // ---- general form: the other two passes over every key of the row
+#pragma unroll 1
+  for (int shift = kBits12; shift >= 0; shift -= kBits12) {
+    for (int j = tid; j < kHistWords; j += kTopkThreads) hist[j] = 0;
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 0; c < n_chunks; ++c) {
+      if (kMulti && n_chunks > 1) load_chunk(c);
+      uint32_t m = match_mask(valid_mask(c), pmask, prefix);
+      // later passes see few matching keys: visit only those
+      while (m) {
+        const int e = __builtin_ctz(m);
+        m &= m - 1;
+        uint32_t ue = 0;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) ue = q == e ? u[q] : ue;
+        atomicAdd(&hist[hp((ue >> shift) & 2047u)], 1u);
       }
     }
     __syncthreads();
-    prefix |= s_bin << shift;
-    pmask |= bmask << shift;
-    remaining -= s_above;
+    uint32_t b, ab;
+    select_bin(hist, 2048, remaining, sel_res, &b, &ab);
+    prefix |= b << shift;
+    pmask |= 2047u << shift;
+    remaining -= ab;
   }
   const uint32_t T = prefix;  // key of the k-th largest score; `remaining` ties of it are taken
 

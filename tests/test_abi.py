@@ -147,8 +147,9 @@ def test_index_validation(lib):
     assert call(p=pool(ratio=4, dim=100, dtype=hyb.FP4_E2M1)) == hyb.HYB_EINVAL
     assert call(p=pool(ratio=4, dim=128, dtype=hyb.FP8_E4M3)) == hyb.HYB_ENOTSUP
     assert call(heads=128, p=pool(ratio=4, dim=128, dtype=hyb.F32)) == hyb.HYB_ENOTSUP
-    # scores [16][32768] float + first-pass histograms [16][2048] uint32
-    assert lib.hyb_index_topk_workspace_bytes(16, 131071, 128, 4) == 16 * 32768 * 4 + 16 * 2048 * 4
+    # order keys [16][32768] uint32, then the indexer's partial histograms [16][32][1024] uint16
+    assert lib.hyb_index_topk_workspace_bytes(16, 131071, 128, 4) == \
+        16 * 32768 * 4 + 16 * 32 * 1024 * 2
     assert lib.hyb_topk(FAKE, 10, FAKE, 4, 20, 8, FAKE, None) == hyb.HYB_EINVAL   # ld < max_len
     assert lib.hyb_topk(FAKE, 20, FAKE, 4, 20, 0, FAKE, None) == hyb.HYB_EINVAL   # k = 0
     assert lib.hyb_topk(None, 20, FAKE, 4, 20, 8, FAKE, None) == hyb.HYB_EINVAL
