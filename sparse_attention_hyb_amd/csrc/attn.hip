@@ -185,7 +185,6 @@ __device__ __attribute__((aligned(16))) uint8_t kZeroRow[1024];   // zero-initia
 
 constexpr int kSeg = 2048;           // keys whose entry indices are resolved per segment
 constexpr int kPitch = kMD + 16;     // LDS row pitch of a K tile (bf16): 1056 B, 8 banks per row
-constexpr int kQPitch = kMD + 8;     // LDS row pitch of the query (bf16): 1040 B, 4 banks per row
 
 // LDS address (in bf16 elements) of dims [d, d + 8) of key row `row` of a K tile. Rows are 1056 B
 // apart (8 banks), and the 16-byte chunk index is XORed with bit 3 of the row: sixteen
@@ -224,20 +223,39 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const uint16_t* p0, const uint16_t
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// The hardware hands consecutive workgroup ids to the 8 XCDs in turn. This maps a workgroup id to
+// a logical index so that consecutive logical indices - the splits of one query - run on one XCD
+// and share its L2 (the query, and for sparse decode the sequence's entries).
+__device__ __forceinline__ int xcd_logical(int L, int total) {
+  constexpr int X = 8;
+  const int per = total / X, rem = total % X;
+  const int x = L % X, s = L / X;
+  return x < rem ? x * (per + 1) + s : rem * (per + 1) + (x - rem) * per + s;
+}
+
 // MFMA attention. Work of one workgroup: query i, keys [split*chunk, (split+1)*chunk) of its list.
-// Waves form a 2 x 2 grid: hh = head half (32 heads), dh = dim half (256 dims). Wave (hh, dh)
-// loads only dim quarter qd = 2*dh + hh of every key (each key byte is fetched once per
-// workgroup), three tiles deep in registers; the quarter is written to the LDS tile, where the
-// partner wave of the same dim half picks it up for its QK and all waves read it transposed for PV.
+// Waves form a 2 x 2 grid: hh = head half (32 heads), dh = dim half (256 dims). Each wave keeps
+// its query slice (32 heads x 256 dims) in registers and loads only dim quarter qd = 2*dh + hh of
+// every key (each key byte is fetched once per workgroup), one iteration ahead of its publication
+// (one staged tile in registers keeps the kernel free of spills). Tiles pass through three LDS
+// buffers, and each loop iteration needs a single barrier:
+//   iteration t: S(t) = own QK partial + the partner's (exchanged through double-buffered LDS),
+//                publish this wave's quarter of tile t+2, issue the loads of tile t+3,
+//                QK partial of tile t+1 (MFMA, independent of the softmax below),
+//                softmax of tile t, PV of tile t (K tile read back transposed), barrier.
+// At the barrier ending iteration t every wave has finished reading the buffer of tile t, which
+// iteration t+1 refills with tile t+3, and the score buffer read in iteration t, which iteration
+// t+1 refills with the partials of tile t+2.
 template <bool kFp8>
 __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ktile[2 * kKT * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t qlds[kMH * kQPitch];   // the query, [head][dim]
-  __shared__ __attribute__((aligned(16))) float sx[4][4 * 64 * 4];   // [wave][quad][lane][4]
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[3 * kKT * kPitch];
+  __shared__ __attribute__((aligned(16))) float sx[2][4][4 * 64 * 4];   // [buf][wave][quad][lane][4]
   __shared__ int32_t kidx[kSeg];
-  __shared__ __attribute__((aligned(16))) float kscale[2 * kKT];
+  __shared__ __attribute__((aligned(16))) float kscale[3 * kKT];
+  __shared__ uint32_t kvalid[3];   // per tile buffer: bit j = key j of the tile is valid
 
-  const int i = blockIdx.y, sp = blockIdx.x;
+  const int logical = xcd_logical(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
+  const int sp = logical % a.n_split, i = logical / a.n_split;
   const QueryKeys qk = query_keys(a, i);
   const int j_begin = sp * a.chunk, j_end = min(qk.n_keys, j_begin + a.chunk);
   const int tid = threadIdx.x;
@@ -245,22 +263,17 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
   const int col = lane & 31, hf = lane >> 5;
   const int hh = wave >> 1, dh = wave & 1;
   const int qd = 2 * dh + hh;          // the dim quarter this wave loads
-  const int oq = 2 * dh + (1 - hh);    // the partner's quarter
 
-  // The query stays in LDS (registers go to the O accumulators and the staged K tiles). Q^T is
-  // the QK B operand (column = head 32*hh + col); K-step s covers quarter 2*dh + s/8, dims
+  // Q^T is the QK B operand (column = head 32*hh + col); K-step s covers quarter 2*dh + s/8, dims
   // 128*quarter + 64*hf + 8*(s%8) + [0, 8): the same split the K operand uses.
+  bf16x8 qreg[16];
   {
-    const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)i * kMH * kMD;
-    for (int e = tid; e < kMH * kMD / 8; e += 256) {
-      const int h = e / (kMD / 8), d = (e % (kMD / 8)) * 8;
-      *reinterpret_cast<bf16x8*>(qlds + h * kQPitch + d) = *reinterpret_cast<const bf16x8*>(qsrc + h * kMD + d);
-    }
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)i * kMH + 32 * hh + col) * kMD + 64 * hf;
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      qreg[s] = *reinterpret_cast<const bf16x8*>(qrow + 128 * (2 * dh + (s >> 3)) + 8 * (s & 7));
   }
-  const uint16_t* qrow = qlds + (32 * hh + col) * kQPitch + 64 * hf;
-  auto qb = [&](int s) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(qrow + 128 * (2 * dh + (s >> 3)) + 8 * (s & 7));
-  };
   f32x16 o[8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) o[mb] = f32x16{};
@@ -268,9 +281,26 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
   const float sl2 = a.scale * kLog2e;
   const int lane_off = 128 * qd + 64 * hf;   // first dim of this lane's staged run
 
+  // LDS addresses in a tile buffer (bf16 elements), tile_off() written out as a per-lane base plus
+  // a compile-time offset, so that few address registers stay live. Row col's 16-byte chunk c sits
+  // at chunk c ^ x (x = bit 3 of the row): +8 elements for even c, -8 for odd c when x = 1.
+  const int x8 = 8 * ((col >> 3) & 1);
+  const int qk_even = col * kPitch + 256 * dh + 64 * hf + x8;   // + 128*(s/8) + 8*(s%8), s even
+  const int qk_odd = col * kPitch + 256 * dh + 64 * hf - x8;    // ... s odd
+  const int pub_even = col * kPitch + lane_off + x8;            // + 8c, c even
+  const int pub_odd = col * kPitch + lane_off - x8;             // ... c odd
+  // transposed PV reads: rows trow + 16*t2 (bit 3 clear) and trow + 16*t2 + 8 (bit 3 set), dims
+  // tdim + 32*mb; in the second row the chunk index is flipped: +8 elements if its bit 0 (bit 3 of
+  // tdim) is clear, -8 if set
+  const int i16 = lane & 15;
+  const int trow = 4 * hf + (i16 >> 2);
+  const int tdim = 256 * dh + (col >> 4) * 16 + 4 * (i16 & 3);
+  const int pv_lo = trow * kPitch + tdim;
+  const int pv_hi = (trow + 8) * kPitch + tdim + (((tdim >> 3) & 1) ? -8 : 8);
+
   for (int seg = j_begin; seg < j_end; seg += kSeg) {
     const int nseg = min(kSeg, j_end - seg);
-    __syncthreads();   // readers of the previous segment's index table are done
+    __syncthreads();   // readers of the previous segment's index table and tiles are done
     for (int jj = tid; jj < nseg; jj += 256) {
       KeyRef r = resolve_key(a, i, qk.seq, qk.ws, qk.n_win, qk.nv, seg + jj);
       kidx[jj] = (int32_t)r.idx;
@@ -280,7 +310,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
 
     // Loads are issued without any branch (masked lanes read the zero row): a branch between a
     // prefetch and the use of an older tile would make the compiler wait for every outstanding
-    // load, prefetch included.
+    // load, prefetch included. Tiles past the end load masked rows.
     auto load = [&](Stage<kFp8>& st, int tt) {
       const int jraw = tt * kKT + col;
       const int jl = min(jraw, nseg - 1);
@@ -303,7 +333,6 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
         st.sc = reinterpret_cast<const float*>(win ? a.swa.scale : a.comp.scale)[ok ? idx : 0];
       }
     };
-
     auto own = [&](const Stage<kFp8>& st, int c) -> bf16x8 {
       if constexpr (!kFp8) {
         return st.v[c];
@@ -312,64 +341,68 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
         return (c & 1) ? fp8x8_to_bf16x8(q[2], q[3]) : fp8x8_to_bf16x8(q[0], q[1]);
       }
     };
-
-    auto process = [&](const Stage<kFp8>& st, int tt) {
-      const int kb = tt & 1;
-      uint16_t* kt = ktile + kb * kKT * kPitch;
-      // ---- publish this wave's quarter of the tile (natural [key][dim] layout)
+    // This wave's quarter of tile tt into its buffer (natural [key][dim] layout), with the
+    // validity of the tile's 32 keys (bit j = key j; every wave resolved the same keys).
+    auto publish = [&](const Stage<kFp8>& st, int tt) {
+      uint16_t* kt = ktile + (tt % 3) * (kKT * kPitch);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        *reinterpret_cast<bf16x8*>(kt + tile_off(col, lane_off + 8 * c)) = own(st, c);
-      if constexpr (kFp8) {
-        if (wave == 0 && hf == 0) kscale[kb * kKT + col] = st.valid ? st.sc : 0.f;
+        *reinterpret_cast<bf16x8*>(kt + ((c & 1) ? pub_odd : pub_even) + 8 * c) = own(st, c);
+      const uint32_t vm = (uint32_t)__ballot(st.valid);
+      if (wave == 0) {
+        if constexpr (kFp8) {
+          if (hf == 0) kscale[(tt % 3) * kKT + col] = st.valid ? st.sc : 0.f;
+        }
+        if (lane == 0) kvalid[tt % 3] = vm;
       }
-      // validity of the tile's 32 keys (every wave resolved the same keys): bit j = key j
-      const uint32_t vmask = (uint32_t)__ballot(st.valid);
-      __syncthreads();
-      // ---- QK over this wave's dim half: own quarter from registers, partner's from LDS
-      bf16x8 oth[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        oth[c] = *reinterpret_cast<const bf16x8*>(kt + tile_off(col, 128 * oq + 64 * hf + 8 * c));
-      // two independent accumulation chains (even / odd K-steps) keep the MFMA pipe busy
-      f32x16 sacc = {}, sacc1 = {};
+    };
+    // QK over this wave's dim half, both quarters read from the tile's buffer; two independent
+    // accumulation chains (even / odd K-steps) keep the MFMA pipe busy.
+    auto qk_partial = [&](int tt) -> f32x16 {
+      const uint16_t* kt = ktile + (tt % 3) * (kKT * kPitch);
+      f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
       for (int s = 0; s < 16; s += 2) {
-        const bf16x8 ka0 = ((s >> 3) == hh) ? own(st, s & 7) : oth[s & 7];
-        const bf16x8 ka1 = (((s + 1) >> 3) == hh) ? own(st, (s + 1) & 7) : oth[(s + 1) & 7];
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qb(s), sacc, 0, 0, 0);
-        sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qb(s + 1), sacc1, 0, 0, 0);
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kt + qk_even + 128 * (s >> 3) + 8 * (s & 7));
+        const bf16x8 k1 =
+            *reinterpret_cast<const bf16x8*>(kt + qk_odd + 128 * ((s + 1) >> 3) + 8 * ((s + 1) & 7));
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[s + 1], acc1, 0, 0, 0);
       }
+      return acc0 + acc1;
+    };
+    // [buf][wave][quad][lane][4]: a wave's 16-byte accesses are lane-contiguous (no conflicts)
+    auto write_sx = [&](int tt, const f32x16& v) {
+      f32x4* mine = reinterpret_cast<f32x4*>(&sx[tt & 1][wave][0]) + lane;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] += sacc1[r];
-      {
-        // [wave][quad][lane][4]: a wave's 16-byte accesses are lane-contiguous (no conflicts)
-        f32x4* mine = reinterpret_cast<f32x4*>(&sx[wave][0]) + lane;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 w;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = sacc[4 * q4 + e];
-          mine[64 * q4] = v;
-        }
+        for (int e = 0; e < 4; ++e) w[e] = v[4 * q4 + e];
+        mine[64 * q4] = w;
       }
-      __syncthreads();
-      {
-        const f32x4* theirs = reinterpret_cast<const f32x4*>(&sx[wave ^ 1][0]) + lane;
-        f32x4 t[4];
+    };
+    auto read_sx = [&](int tt) -> f32x16 {
+      const f32x4* theirs = reinterpret_cast<const f32x4*>(&sx[tt & 1][wave ^ 1][0]) + lane;
+      f32x16 v;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) t[q4] = theirs[64 * q4];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 w = theirs[64 * q4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sacc[4 * q4 + e] += t[q4][e];
+        for (int e = 0; e < 4; ++e) v[4 * q4 + e] = w[e];
       }
-      // ---- online softmax for head 32*hh + col; this lane's keys are 8*(r/4) + 4*hf + r%4
+      return v;
+    };
+    // Online softmax of tile tt for head 32*hh + col (this lane's keys are 8*(r/4) + 4*hf + r%4),
+    // then PV over the tile.
+    auto soft_pv = [&](const f32x16& S, int tt) {
+      const uint16_t* kt = ktile + (tt % 3) * (kKT * kPitch);
+      const uint32_t vmask = kvalid[tt % 3];
       float ksc[16];
       if constexpr (kFp8) {
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(kscale + kb * kKT + 8 * j4 + 4 * hf);
+          const f32x4 v = *reinterpret_cast<const f32x4*>(kscale + (tt % 3) * kKT + 8 * j4 + 4 * hf);
 #pragma unroll
           for (int e = 0; e < 4; ++e) ksc[4 * j4 + e] = v[e];
         }
@@ -379,7 +412,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
-        float v = sacc[r] * sl2;
+        float v = S[r] * sl2;
         if constexpr (kFp8) v *= ksc[r];
         z[r] = ((vmask >> key) & 1u) ? v : -INFINITY;
         mx = fmaxf(mx, z[r]);
@@ -413,9 +446,9 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
       }
       psum += __shfl_xor(psum, 32, 64);
       l_run += psum;
-      // ---- PV: B = probabilities (element e of K-step t <-> key 16t + 8(e/4) + 4hf + e%4),
-      //      A = K^T read transposed from LDS: lane j of each 16-lane group points at key
-      //      k0 + j/4, dims d0 + 4*(j%4), and receives keys k0..k0+3 of dim d0 + j.
+      // PV: B = probabilities (element e of K-step t2 <-> key 16*t2 + 8(e/4) + 4hf + e%4),
+      //     A = K^T read transposed from LDS: lane j of each 16-lane group points at key
+      //     k0 + j/4, dims d0 + 4*(j%4), and receives keys k0..k0+3 of dim d0 + j.
       bf16x8 pb[2];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
@@ -424,12 +457,9 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(pr[8 * t2 + 2 * e], pr[8 * t2 + 2 * e + 1]);
         pb[t2] = __builtin_bit_cast(bf16x8, w);
       }
-      const int i16 = lane & 15;
-      const int trow = 4 * hf + (i16 >> 2);                       // + 16*t2 (+ 8 for the 2nd half)
-      const int tdim = 256 * dh + (col >> 4) * 16 + 4 * (i16 & 3);  // + 32*mb
       auto trf = [&](int mb, int t2) {
-        return lds_tr_pair(kt + tile_off(trow + 16 * t2, tdim + 32 * mb),
-                           kt + tile_off(trow + 16 * t2 + 8, tdim + 32 * mb));
+        return lds_tr_pair(kt + pv_lo + 16 * t2 * kPitch + 32 * mb,
+                           kt + pv_hi + 16 * t2 * kPitch + 32 * mb);
       };
       // fragments for block mb + 1 are read while block mb multiplies
       bf16x8 af[2][2];
@@ -447,25 +477,32 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
       }
     };
 
-    // Global loads run two tiles ahead of the tile being processed (three staged tiles fit
-    // beside the O accumulators; the query lives in LDS).
-    // (tiles past the end are loaded masked: harmless, and it keeps the loop free of branches
-    // between a prefetch and the use of the tile before it)
-    {
-      Stage<kFp8> s0, s1, s2;
-      load(s0, 0);
-      load(s1, 1);
-      for (int t = 0; t < n_tiles; t += 3) {
-        load(s2, t + 2);
-        process(s0, t);
-        if (t + 1 >= n_tiles) break;
-        load(s0, t + 3);
-        process(s1, t + 1);
-        if (t + 2 >= n_tiles) break;
-        load(s1, t + 4);
-        process(s2, t + 2);
+    // One tile is in flight in registers; the tile after it is already in its LDS buffer.
+    Stage<kFp8> s0;
+    load(s0, 0);
+    publish(s0, 0);
+    load(s0, 1);
+    __syncthreads();
+    f32x16 sown = qk_partial(0);
+    write_sx(0, sown);
+    publish(s0, 1);
+    load(s0, 2);
+    __syncthreads();
+    // iteration t; X holds tile t+2, whose buffer was last read in iteration t-1
+    auto iter = [&](int t, Stage<kFp8>& X) {
+      const f32x16 S = sown + read_sx(t);
+      publish(X, t + 2);
+      load(X, t + 3);
+      f32x16 snext = {};
+      if (t + 1 < n_tiles) {
+        snext = qk_partial(t + 1);
+        write_sx(t + 1, snext);
       }
-    }
+      soft_pv(S, t);
+      sown = snext;
+      __syncthreads();
+    };
+    for (int t = 0; t < n_tiles; ++t) iter(t, s0);
   }
   // ---- partials: O^T rows d = 256*dh + 32*mb + 8*(r/4) + 4*hf + r%4, column h = 32*hh + col
   float* po = a.part_o + ((int64_t)i * a.n_split + sp) * kMD * kMH;
@@ -487,63 +524,106 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // Combine: merge split partials, inverse RoPE at the query position, cast.
-// Grid (dim slice of 64, query): each workgroup reads its 64 dims x all heads of every split.
+// Workgroup (dim slice of 32, query), mapped to the XCD that ran the query's splits so that their
+// partials are read from its L2. Thread t owns dims d0 + 2(t/16) + {0, 1} of heads 4(t%16) + [0, 4):
+// per split two 16-byte loads (the partials are [dim][head], heads contiguous), all issued before
+// any is used.
 // ------------------------------------------------------------------------------------------
 constexpr int kCombineDims = 32;
+constexpr int kCombineHeads = 64;   // heads of either attention kernel
 
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
-  const int i = blockIdx.y;
-  const int d0 = blockIdx.x * kCombineDims;
+  const int logical = xcd_logical(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
+  const int i = logical / gridDim.x;
+  const int d0 = (logical % gridDim.x) * kCombineDims;
   const int H = a.n_heads, D = a.dim, ns = a.n_split;
   int seq, p;
   query_at(a.qd, i, &seq, &p);
-  __shared__ float wsplit[kMaxSplit * 128];
+  __shared__ __attribute__((aligned(16))) float wsplit[kMaxSplit * kCombineHeads];   // [split][head]
+  __shared__ float ml[kMaxSplit * 2 * kCombineHeads];   // (m, l) staged as [split][2][head]
   __shared__ float rc[kCombineDims / 2], rs[kCombineDims / 2];
-  const float* pml = a.part_ml + (int64_t)i * ns * 2 * H;
-  for (int h = threadIdx.x; h < H; h += 256) {
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, pml[s * 2 * H + h]);
-    float den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = pml[s * 2 * H + h];
-      den += ms == -INFINITY ? 0.f : expf(ms - M) * pml[s * 2 * H + H + h];
-    }
-    const float inv = den > 0.f ? 1.0f / den : 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = pml[s * 2 * H + h];
-      wsplit[s * H + h] = ms == -INFINITY ? 0.f : expf(ms - M) * inv;
-    }
+  const int tid = threadIdx.x;
+  {
+    const float* pml = a.part_ml + (int64_t)i * ns * 2 * H;
+    for (int e = tid; e < ns * 2 * H; e += 256) ml[e] = pml[e];
   }
   const int rope_lo = D - a.rope_dim;
   const int dend = min(D, d0 + kCombineDims);
-  for (int t = threadIdx.x; t < kCombineDims / 2; t += 256) {
+  for (int t = tid; t < kCombineDims / 2; t += 256) {
     const int d = d0 + 2 * t;
     if (d >= rope_lo && d < dend)
       rope_cs(-(double)p, (d - rope_lo) >> 1, a.rope_dim, a.rope_base, &rc[t], &rs[t]);
   }
   __syncthreads();
-  const float* po = a.part_o + (int64_t)i * ns * D * H;
-  const int npair = (dend - d0) / 2;
-  for (int e = threadIdx.x; e < npair * H; e += 256) {
-    const int h = e % H, t = e / H, d = d0 + 2 * t;
-    float v0 = 0.f, v1 = 0.f;
-#pragma unroll 8
+  for (int h = tid; h < H; h += 256) {
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s * 2 * H + h]);
+    float den = 0.f;
     for (int s = 0; s < ns; ++s) {
-      const float wgt = wsplit[s * H + h];
-      v0 = fmaf(wgt, po[((int64_t)s * D + d) * H + h], v0);
-      v1 = fmaf(wgt, po[((int64_t)s * D + d + 1) * H + h], v1);
+      const float ms = ml[s * 2 * H + h];
+      den += ms == -INFINITY ? 0.f : expf(ms - M) * ml[s * 2 * H + H + h];
     }
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float ms = ml[s * 2 * H + h];
+      wsplit[s * H + h] = ms == -INFINITY ? 0.f : expf(ms - M) * inv;
+    }
+  }
+  __syncthreads();
+  const float* po = a.part_o + (int64_t)i * ns * D * H;
+  auto store = [&](int h, int d, float x0, float x1, int pr) {
     if (d >= rope_lo) {
-      const float z0 = v0 * rc[t] - v1 * rs[t];
-      const float z1 = v0 * rs[t] + v1 * rc[t];
-      v0 = z0;
-      v1 = z1;
+      const float z0 = x0 * rc[pr] - x1 * rs[pr];
+      const float z1 = x0 * rs[pr] + x1 * rc[pr];
+      x0 = z0;
+      x1 = z1;
     }
     const int64_t off = ((int64_t)i * H + h) * D + d;
     if (a.out_dtype == F32) {
-      *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + off) = make_float2(v0, v1);
+      *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + off) = make_float2(x0, x1);
     } else {
-      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + off) = pack_bf16x2(v0, v1);
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + off) = pack_bf16x2(x0, x1);
+    }
+  };
+  if ((H & 3) == 0) {
+    // thread t: dim pair d0 + 2(t/16), heads 4(t%16) + [0, 4)
+    const int pr = tid >> 4, h4 = 4 * (tid & 15);
+    const int d = d0 + 2 * pr;
+    if (h4 >= H || d >= dend) return;
+    f32x4 v0 = {}, v1 = {};
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+      f32x4 x0[8], x1[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int s = min(s0 + q, ns - 1);
+        x0[q] = *reinterpret_cast<const f32x4*>(po + ((int64_t)s * D + d) * H + h4);
+        x1[q] = *reinterpret_cast<const f32x4*>(po + ((int64_t)s * D + d + 1) * H + h4);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x4 wq = s0 + q < ns ? *reinterpret_cast<const f32x4*>(wsplit + (s0 + q) * H + h4)
+                                     : f32x4{};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v0[e] = fmaf(wq[e], x0[q][e], v0[e]);
+          v1[e] = fmaf(wq[e], x1[q][e], v1[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store(h4 + e, d, v0[e], v1[e], pr);
+  } else {
+    // any head count: one (head, dim pair) per thread and step
+    const int npair = (dend - d0) / 2;
+    for (int e = tid; e < npair * H; e += 256) {
+      const int h = e % H, pr = e / H, d = d0 + 2 * pr;
+      float x0 = 0.f, x1 = 0.f;
+      for (int s = 0; s < ns; ++s) {
+        const float wgt = wsplit[s * H + h];
+        x0 = fmaf(wgt, po[((int64_t)s * D + d) * H + h], x0);
+        x1 = fmaf(wgt, po[((int64_t)s * D + d + 1) * H + h], x1);
+      }
+      store(h, d, x0, x1, pr);
     }
   }
 }
