@@ -87,16 +87,15 @@ def c4_sparse(torch, hyb, W, BM, args):
     B, L, R = 16, 131072, max(1, args.replicas)
     dev = "cuda"
     reps = []
+    kshape, hshape = hyb.index_keys_shapes(B, L - 1)
     for r in range(R):
         wl = W.sparse_decode(dev, seed=r)
         g = W.generator(2, r, 99, dev)
-        p = L - 1
-        nv = BM.n_visible(p, 4, wl.window)
         reps.append(dict(
             wl=wl,
             qpos=(wl.seq_lens - 1).contiguous(),
-            lengths=torch.full((B,), nv, dtype=torch.int32, device=dev),   # request metadata
-            scores=torch.empty(B, (nv + 63) // 64 * 64, dtype=torch.float32, device=dev),
+            keys=torch.empty(kshape, dtype=torch.int32, device=dev),
+            hist=torch.empty(hshape, dtype=torch.int16, device=dev),
             topk=torch.empty(B, wl.k, dtype=torch.int32, device=dev),
             out=torch.empty_like(wl.q),
             ws=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, L, 4, wl.k), dtype=torch.uint8, device=dev),
@@ -105,18 +104,18 @@ def c4_sparse(torch, hyb, W, BM, args):
             start=torch.full((B,), L - 1, dtype=torch.int32, device=dev),
             state=W.randn((B, 4, 512), g, dev),
         ))
-    nv = BM.n_visible(L - 1, 4, 128)
 
     def step(r, ev):
         d = reps[r]
         wl = d["wl"]
         hyb.hyb_compress(d["x_new"], d["cu"], d["start"], 1, d["state"], wl.comp, 64)
+        # hyb_index_topk in its two halves, so that the indexer kernel can be timed on its own
         if ev:
             ev[0].record()
-        hyb.hyb_index_score(wl.idx_q, wl.idx_w, d["qpos"], L - 1, wl.idx_pool, d["scores"])
+        hyb.hyb_index_score_keys(wl.idx_q, wl.idx_w, d["qpos"], L - 1, wl.idx_pool, d["keys"], d["hist"])
         if ev:
             ev[1].record()
-        hyb.hyb_topk(d["scores"], d["lengths"], nv, wl.k, d["topk"])
+        hyb.hyb_topk_keys(d["keys"], d["hist"], d["qpos"], L - 1, wl.k, d["topk"])
         hyb.hyb_attn_decode(wl.q, wl.seq_lens, L, wl.swa, wl.comp, d["out"], topk_idx=d["topk"],
                             k=wl.k, workspace=d["ws"])
 

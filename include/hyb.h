@@ -167,6 +167,27 @@ int32_t hyb_topk(const float* scores, int64_t scores_ld, const int32_t* lengths,
                  int32_t max_len, int32_t k, int32_t* out_idx, void* stream);
 
 /* --------------------------------------------------------------------------------------------
+ * hyb_index_score_keys / hyb_topk_keys - the two halves of hyb_index_topk, for callers that want
+ * to place them (or time them) separately. Same selection as hyb_index_score + hyb_topk.
+ * hyb_index_score_keys writes each score as its order key, a uint32 that sorts like the float
+ * (non-negative: bits | 0x80000000; negative: ~bits; -0.0 stored as +0.0), and, for every block
+ * of 1024 entries of a row, a histogram of the keys' top 10 bits:
+ *   keys       uint32 [n_q][keys_ld], keys_ld >= n_vis(max_pos)
+ *   part_hist  uint16 [n_q][part_ld][1024], part_ld >= ceil(n_vis(max_pos) / 1024)
+ * Other arguments as in hyb_index_score. hyb_topk_keys selects from them with the same q_pos,
+ * max_pos, window and the pool's ratio (row i holds n_vis(q_pos[i]) entries), as hyb_topk does:
+ *   out_idx int32 [n_q][k];  1 <= k <= HYB_KMAX.
+ * ------------------------------------------------------------------------------------------ */
+int32_t hyb_index_score_keys(const void* q_idx, int32_t q_dtype, const float* w,
+                             const int32_t* q_seq, const int32_t* q_pos, int32_t n_q,
+                             int32_t n_heads, int32_t max_pos, int32_t window,
+                             const hyb_paged* idx_pool, uint32_t* keys, int64_t keys_ld,
+                             uint16_t* part_hist, int64_t part_ld, void* stream);
+int32_t hyb_topk_keys(const uint32_t* keys, int64_t keys_ld, const uint16_t* part_hist,
+                      int64_t part_ld, const int32_t* q_pos, int32_t n_q, int32_t max_pos,
+                      int32_t window, int32_t ratio, int32_t k, int32_t* out_idx, void* stream);
+
+/* --------------------------------------------------------------------------------------------
  * hyb_index_topk - hyb_index_score followed by hyb_topk over n_vis(q_pos[i]) entries; the
  * scores live in the workspace (size from hyb_index_topk_workspace_bytes with the same n_q,
  * max_pos, window and ratio) as order keys, next to per-block histograms that the indexer

@@ -28,7 +28,8 @@ DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp4": FP4_E2M1}
 
 EXPORTS = (
     "hyb_abi_version", "hyb_status_str", "hyb_last_error", "hyb_compress", "hyb_swa_insert",
-    "hyb_index_score", "hyb_topk", "hyb_index_topk_workspace_bytes", "hyb_index_topk",
+    "hyb_index_score", "hyb_topk", "hyb_index_score_keys", "hyb_topk_keys",
+    "hyb_index_topk_workspace_bytes", "hyb_index_topk",
     "hyb_attn_decode_workspace_bytes", "hyb_attn_decode", "hyb_attn_prefill_workspace_bytes",
     "hyb_attn_prefill",
 )
@@ -67,6 +68,9 @@ _SIGS = {
     "hyb_swa_insert": (_I32, [_P, _I32, _P, _P, _I32, _I32, _PP, _I32, _D, _P]),
     "hyb_index_score": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _PP, _P, _I64, _P]),
     "hyb_topk": (_I32, [_P, _I64, _P, _I32, _I32, _I32, _P, _P]),
+    "hyb_index_score_keys": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _PP, _P, _I64, _P,
+                                    _I64, _P]),
+    "hyb_topk_keys": (_I32, [_P, _I64, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]),
     "hyb_index_topk_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "hyb_index_topk": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _PP, _I32, _P, _P, _SZ, _P]),
     "hyb_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
@@ -173,6 +177,32 @@ def hyb_topk(scores, lengths, max_len: int, k: int, out_idx, stream=None) -> Non
     _check(load().hyb_topk(_ptr(scores), int(scores.stride(0)), _ptr(lengths),
                            int(scores.shape[0]), int(max_len), int(k), _ptr(out_idx),
                            _stream(stream)))
+
+
+def index_keys_shapes(n_q: int, max_pos: int, window: int = 128, ratio: int = 4):
+    """Shapes of the `keys` (uint32 as int32) and `part_hist` (uint16 as int16) buffers of
+    hyb_index_score_keys / hyb_topk_keys: ([n_q, ld], [n_q, part_ld, 1024])."""
+    ws = max(0, max_pos - window + 1)                  # window start of the last position
+    nv = max(1, (ws + ratio - 1) // ratio)             # compressed entries visible to it
+    ld = (nv + 63) // 64 * 64
+    return (n_q, ld), (n_q, (nv + 1023) // 1024, 1024)
+
+
+def hyb_index_score_keys(q_idx, w, q_pos, max_pos: int, idx_pool, keys, part_hist, window: int = 128,
+                         q_seq=None, stream=None) -> None:
+    d = paged(idx_pool)
+    _check(load().hyb_index_score_keys(_ptr(q_idx), _tdtype(q_idx), _ptr(w), _ptr(q_seq), _ptr(q_pos),
+                                       int(q_idx.shape[0]), int(q_idx.shape[1]), int(max_pos),
+                                       int(window), ctypes.byref(d), _ptr(keys), int(keys.stride(0)),
+                                       _ptr(part_hist), int(part_hist.shape[1]), _stream(stream)))
+
+
+def hyb_topk_keys(keys, part_hist, q_pos, max_pos: int, k: int, out_idx, window: int = 128,
+                  ratio: int = 4, stream=None) -> None:
+    _check(load().hyb_topk_keys(_ptr(keys), int(keys.stride(0)), _ptr(part_hist),
+                                int(part_hist.shape[1]), _ptr(q_pos), int(keys.shape[0]),
+                                int(max_pos), int(window), int(ratio), int(k), _ptr(out_idx),
+                                _stream(stream)))
 
 
 def hyb_index_topk_workspace_bytes(n_q: int, max_pos: int, window: int, ratio: int) -> int:

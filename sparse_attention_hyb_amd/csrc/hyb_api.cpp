@@ -325,6 +325,59 @@ int32_t hyb_topk(const float* scores, int64_t scores_ld, const int32_t* lengths,
   return launch_status(hyb::launch_topk(a, static_cast<hipStream_t>(stream)), op);
 }
 
+static int64_t part_blocks(int64_t nv) { return (nv + hyb::kScorePartKeys - 1) / hyb::kScorePartKeys; }
+
+int32_t hyb_index_score_keys(const void* q_idx, int32_t q_dtype, const float* w, const int32_t* q_seq,
+                             const int32_t* q_pos, int32_t n_q, int32_t n_heads, int32_t max_pos,
+                             int32_t window, const hyb_paged* idx_pool, uint32_t* keys,
+                             int64_t keys_ld, uint16_t* part_hist, int64_t part_ld, void* stream) {
+  const char* op = "hyb_index_score_keys";
+  hyb::ScoreArgs a;
+  HYB_TRY(check_score(op, q_idx, q_dtype, w, q_pos, n_q, n_heads, max_pos, window, idx_pool, &a));
+  if (!keys || !part_hist) return fail(HYB_EINVAL, "%s: keys and part_hist must be non-NULL", op);
+  const int64_t nv = visible(max_pos, a.pool.ratio, window);
+  if (keys_ld < nv) return fail(HYB_EINVAL, "%s: keys_ld %lld < visible entries %lld", op, (long long)keys_ld, (long long)nv);
+  if (part_ld < part_blocks(nv) || part_ld > INT32_MAX)
+    return fail(HYB_EINVAL, "%s: part_ld %lld outside [%lld, 2^31)", op, (long long)part_ld, (long long)part_blocks(nv));
+  a.qd = hyb::QueryDev{nullptr, q_seq, q_pos};
+  a.scores = reinterpret_cast<float*>(keys);
+  a.ld = keys_ld;
+  a.part_hist = part_hist;
+  a.part_ld = (int32_t)part_ld;
+  return launch_status(hyb::launch_index_score(a, static_cast<hipStream_t>(stream)), op);
+}
+
+int32_t hyb_topk_keys(const uint32_t* keys, int64_t keys_ld, const uint16_t* part_hist,
+                      int64_t part_ld, const int32_t* q_pos, int32_t n_q, int32_t max_pos,
+                      int32_t window, int32_t ratio, int32_t k, int32_t* out_idx, void* stream) {
+  const char* op = "hyb_topk_keys";
+  if (!keys || !part_hist || !q_pos || !out_idx)
+    return fail(HYB_EINVAL, "%s: keys, part_hist, q_pos and out_idx must be non-NULL", op);
+  if (n_q < 0 || max_pos < 0) return fail(HYB_EINVAL, "%s: n_q and max_pos must be >= 0", op);
+  if (window <= 0) return fail(HYB_EINVAL, "%s: window %d must be positive", op, window);
+  if (ratio != 4 && ratio != 128) return fail(HYB_EINVAL, "%s: ratio %d must be 4 or 128", op, ratio);
+  if (k < 1 || k > HYB_KMAX) return fail(HYB_EINVAL, "%s: k %d outside [1, %d]", op, k, HYB_KMAX);
+  const int64_t nv = visible(max_pos, ratio, window);
+  if (keys_ld < nv) return fail(HYB_EINVAL, "%s: keys_ld %lld < visible entries %lld", op, (long long)keys_ld, (long long)nv);
+  if (part_ld < part_blocks(nv) || part_ld > INT32_MAX)
+    return fail(HYB_EINVAL, "%s: part_ld %lld outside [%lld, 2^31)", op, (long long)part_ld, (long long)part_blocks(nv));
+  if (n_q == 0) return HYB_OK;
+  hyb::TopkArgs t{};
+  t.scores = reinterpret_cast<const float*>(keys);
+  t.ld = keys_ld;
+  t.lengths = nullptr;
+  t.qd = hyb::QueryDev{nullptr, nullptr, q_pos};
+  t.ratio = ratio;
+  t.window = window;
+  t.n_q = n_q;
+  t.max_len = (int32_t)nv;
+  t.k = k;
+  t.out = out_idx;
+  t.part_hist = part_hist;
+  t.part_ld = (int32_t)part_ld;
+  return launch_status(hyb::launch_topk(t, static_cast<hipStream_t>(stream)), op);
+}
+
 // Workspace of hyb_index_topk: order keys [n_q][ld] (uint32), then the indexer's partial
 // histograms [n_q][part_ld][kTopBins] (uint16), part_ld = ld / kScorePartKeys rounded up.
 static size_t topk_part_ld(int64_t ld) {

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(hyb.EXPORTS) == names
@@ -155,3 +155,29 @@ def test_index_validation(lib):
     assert lib.hyb_topk(None, 20, FAKE, 4, 20, 8, FAKE, None) == hyb.HYB_EINVAL
     assert lib.hyb_index_score(FAKE, hyb.BF16, FAKE, None, FAKE, 16, 64, 131071, 128,
                                ctypes.byref(ip), FAKE, 100, None) == hyb.HYB_EINVAL  # ld too small
+
+
+def test_index_keys_validation(lib):
+    ip = pool(ratio=4, dim=128)
+
+    def score(keys=FAKE, ld=32768, hist=FAKE, pld=32, p=ip):
+        return lib.hyb_index_score_keys(FAKE, hyb.BF16, FAKE, None, FAKE, 16, 64, 131071, 128,
+                                        ctypes.byref(p), keys, ld, hist, pld, None)
+
+    def topk(keys=FAKE, ld=32768, hist=FAKE, pld=32, ratio=4, k=512, q_pos=FAKE):
+        return lib.hyb_topk_keys(keys, ld, hist, pld, q_pos, 16, 131071, 128, ratio, k, FAKE, None)
+
+    # 131071 - 127 = 130944 -> 32736 visible C4 entries -> 32 blocks of 1024
+    assert score(keys=None) == hyb.HYB_EINVAL
+    assert score(hist=None) == hyb.HYB_EINVAL
+    assert score(ld=32735) == hyb.HYB_EINVAL
+    assert score(pld=31) == hyb.HYB_EINVAL
+    assert score(p=pool(ratio=1, dim=128)) == hyb.HYB_EINVAL
+    assert topk(keys=None) == hyb.HYB_EINVAL
+    assert topk(q_pos=None) == hyb.HYB_EINVAL
+    assert topk(ld=100) == hyb.HYB_EINVAL
+    assert topk(pld=31) == hyb.HYB_EINVAL
+    assert topk(ratio=8) == hyb.HYB_EINVAL
+    assert topk(k=0) == hyb.HYB_EINVAL
+    assert lib.hyb_last_error().decode().startswith("hyb_topk_keys")
+    assert hyb.index_keys_shapes(16, 131071) == ((16, 32768), (16, 32, 1024))

@@ -243,6 +243,39 @@ def test_exact_arithmetic_topk_is_bit_exact(gpu_lib):
         assert len(np.unique(sc)) < len(sc)        # ties are present
 
 
+def test_index_keys_halves_match_fused(gpu_lib):
+    """hyb_index_score_keys + hyb_topk_keys select exactly what hyb_index_topk selects; the stored
+    keys are the order keys of hyb_index_score's floats and the per-block histograms count the top
+    10 bits of every entry once (bit-exact)."""
+    hyb = gpu_lib
+    wl = W.sparse_decode(DEV, seed=5, batch=4, ctx=[3000, 20000, 70001, 131072])
+    qpos = wl.seq_lens - 1
+    mp = wl.max_seq_len - 1
+    kshape, hshape = hyb.index_keys_shapes(wl.batch, mp)
+    keys = torch.empty(kshape, dtype=torch.int32, device=DEV)
+    hist = torch.empty(hshape, dtype=torch.int16, device=DEV)
+    hyb.hyb_index_score_keys(wl.idx_q, wl.idx_w, qpos, mp, wl.idx_pool, keys, hist)
+    out = torch.full((wl.batch, wl.k), -7, dtype=I32, device=DEV)
+    hyb.hyb_topk_keys(keys, hist, qpos, mp, wl.k, out)
+    fused = gpu_topk(hyb, wl)
+    scores = torch.zeros(kshape, device=DEV)
+    hyb.hyb_index_score(wl.idx_q, wl.idx_w, qpos, mp, wl.idx_pool, scores)
+    sync()
+    assert torch.equal(out, fused)
+    for b, L in enumerate(wl.seq_lens_host):
+        nv = O.n_visible(L - 1, 4, wl.window)
+        f = scores[b, :nv].cpu().numpy().view(np.uint32).astype(np.uint64)
+        f = np.where(f == 0x80000000, 0, f)
+        want = np.where(f & 0x80000000, (~f) & 0xFFFFFFFF, f | 0x80000000).astype(np.uint32)
+        got = keys[b, :nv].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, want)
+        nb = (nv + 1023) // 1024
+        h = hist[b, :nb].cpu().numpy().view(np.uint16).astype(np.int64)
+        for blk in range(nb):
+            part = got[blk * 1024:(blk + 1) * 1024] >> 22
+            assert np.array_equal(np.bincount(part.astype(np.int64), minlength=1024), h[blk])
+
+
 # ========================================================================= C128 dense decode
 def test_c128_dense_decode_small(gpu_lib):
     wl = W.dense_decode(DEV, seed=1, batch=6, ctx=[1, 128, 129, 300, 20000, 70001])
