@@ -21,7 +21,8 @@
 
 namespace hyb {
 
-constexpr int kScoreKeysPerBlock = kScorePartKeys;  // keys per workgroup
+constexpr int kScoreKeysPerBlock = 2 * kScorePartKeys;  // keys per workgroup (MFMA kernel)
+constexpr int kScoreParts = kScoreKeysPerBlock / kScorePartKeys;
 constexpr int kMfmaHeads = 64;
 constexpr int kMfmaDim = 128;
 
@@ -55,7 +56,9 @@ __device__ __forceinline__ void store_part_hist(const ScoreArgs& a, const uint32
 
 template <bool kFp4>
 __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
-  __shared__ uint32_t lhist[kTopBins];
+  __shared__ uint32_t lhist[kScoreParts * kTopBins];   // one histogram per kScorePartKeys keys
+  // physical blocks of this workgroup's keys (at least 2 entries per block: ratio <= 128)
+  __shared__ int32_t tbl[kScoreKeysPerBlock / 2 + 2];
   const int i = blockIdx.y;
   int seq, p;
   query_at(a.qd, i, &seq, &p);
@@ -68,10 +71,21 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
   const int wave = threadIdx.x >> 6;
   const int col = lane & 31;
   const int hf = lane >> 5;
-  if (a.part_hist) {
-    for (int j = threadIdx.x; j < kTopBins; j += 256) lhist[j] = 0;
-    __syncthreads();
+  if (a.part_hist)
+    for (int j = threadIdx.x; j < kScoreParts * kTopBins; j += 256) lhist[j] = 0;
+  // The block table entries of the workgroup's key range are read once: a table lookup inside the
+  // tile loop would be a load that the data loads depend on, and waiting for it would also wait
+  // for the prefetched tile.
+  const int per_block = a.pool.per_block;           // 256 / ratio: a power of two
+  const int pb_shift = __builtin_ctz(per_block);
+  const int lb0 = base >> pb_shift;
+  const int n_lb = ((end - 1) >> pb_shift) - lb0 + 1;
+  for (int j = threadIdx.x; j < n_lb; j += 256) {
+    const int lb = lb0 + j;
+    const int phys = lb < a.pool.max_blocks ? a.pool.block_table[(int64_t)seq * a.pool.max_blocks + lb] : -1;
+    tbl[j] = (phys >= 0 && phys < a.pool.num_blocks) ? phys : -1;
   }
+  __syncthreads();
 
   // The contraction index d is split as d = 64*hf + 8*s + e for K-step s (0..7) and element e of
   // a lane's 8-wide operand; query and keys use the same split, so each lane holds 64 contiguous
@@ -92,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
       wv[mb][r] = a.w[(int64_t)i * kMfmaHeads + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3)];
 
   float* out = a.scores + (int64_t)i * a.ld;
-  // Each wave walks 32-key tiles with stride 128; the next tile's keys are loaded while the
+  // Each wave walks 32-key tiles with stride 128; the next two tiles' keys are loaded while the
   // current one is multiplied. fp4 tiles stay packed (32 B + 2 scale bytes per lane) until used.
   struct KeysBf16 {
     bf16x8 v[8];
@@ -106,11 +120,16 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
   using Keys = std::conditional_t<kFp4, KeysFp4, KeysBf16>;
   // Branch-free loads (out-of-range or absent keys read entry 0 of the pool; their scores are
   // written as -inf or not at all), so the prefetch never forces a wait on itself.
+  // pool entry of key g (entry 0 when its block is absent; such keys score -inf)
+  auto entry_of = [&](int g) -> int64_t {
+    g = min(g, end - 1);
+    const int phys = tbl[(g >> pb_shift) - lb0];
+    return phys >= 0 ? ((int64_t)phys << pb_shift) + (g & (per_block - 1)) : 0;
+  };
+  auto key_valid = [&](int g) { return tbl[(min(g, end - 1) >> pb_shift) - lb0] >= 0; };
   auto load = [&](Keys& kb, int t0) {
-    const int g = min(t0 + col, end - 1);
-    const int64_t idx = entry_index(a.pool, seq, g);
-    const int64_t e = idx >= 0 ? idx : 0;
-    kb.valid = idx >= 0;
+    const int64_t e = entry_of(t0 + col);
+    kb.valid = key_valid(t0 + col);
     if constexpr (!kFp4) {
       const uint16_t* row =
           reinterpret_cast<const uint16_t*>(a.pool.data + e * a.pool.entry_bytes) + 64 * hf;
@@ -153,25 +172,35 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
       if (a.part_hist) {
         const uint32_t key = order_key(v);
         reinterpret_cast<uint32_t*>(out)[g] = key;
-        atomicAdd(&lhist[key >> (32 - kTopBits)], 1u);
+        atomicAdd(&lhist[((g - base) / kScorePartKeys) * kTopBins + (key >> (32 - kTopBits))], 1u);
       } else {
         out[g] = v;
       }
     }
   };
-  Keys ka, kc;
+  // three tiles per wave in flight: two loading while one is multiplied
+  Keys k0, k1, k2;
   int t0 = base + wave * 32;
   if (t0 < end) {
-    load(ka, t0);
-    for (; t0 < end; t0 += 256) {
-      load(kc, t0 + 128);
-      score(ka, t0);
+    load(k0, t0);
+    load(k1, t0 + 128);
+    for (; t0 < end; t0 += 384) {
+      load(k2, t0 + 256);
+      score(k0, t0);
       if (t0 + 128 >= end) break;
-      load(ka, t0 + 256);
-      score(kc, t0 + 128);
+      load(k0, t0 + 384);
+      score(k1, t0 + 128);
+      if (t0 + 256 >= end) break;
+      load(k1, t0 + 512);
+      score(k2, t0 + 256);
     }
   }
-  if (a.part_hist) store_part_hist(a, lhist, i, blockIdx.x);
+  if (a.part_hist) {
+#pragma unroll
+    for (int q = 0; q < kScoreParts; ++q)
+      if (base + q * kScorePartKeys < end)   // uniform
+        store_part_hist(a, lhist + q * kTopBins, i, blockIdx.x * kScoreParts + q);
+  }
 }
 
 // One thread per key (workgroups of kScorePartKeys keys, four per thread); query rows and weights
