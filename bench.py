@@ -12,7 +12,7 @@ A step is one pass of the whole decode path over one batch:
 Inputs are resident in HBM; R replicas of every cache are cycled so the 256 MiB Infinity Cache
 cannot hold a step's working set. Prints one JSON line (rank 0) with the headline metric, the
 roofline of the dominant kernel (indexer scores, timed with HIP events on its stream inside the
-timed region) and the float64 oracle timed on the host on a bounded sample.
+timed region, on every tenth step) and the float64 oracle timed on the host on a bounded sample.
 """
 
 from __future__ import annotations
@@ -72,15 +72,27 @@ def parse():
 
 
 # ------------------------------------------------------------------------------------------
+EVENT_EVERY = 10   # steps between two event-timed launches of the dominant kernel
+
+
 def time_loop(torch, step, n_steps, warmup, n_rep, events=None):
+    """Runs warm-up steps, then times n_steps steps. Every EVENT_EVERY-th step brackets the
+    dominant kernel with a pair from `events` (recording events around every launch would add
+    several microseconds of queue work to every step)."""
     for i in range(warmup):
         step(i % n_rep, None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(n_steps):
-        step(i % n_rep, events[i] if events else None)
+        ev = events[i // EVENT_EVERY] if events and i % EVENT_EVERY == 0 else None
+        step(i % n_rep, ev)
     torch.cuda.synchronize()
     return time.perf_counter() - t0
+
+
+def timing_events(torch, n_steps):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range((n_steps + EVENT_EVERY - 1) // EVENT_EVERY)]
 
 
 def c4_sparse(torch, hyb, W, BM, args):
@@ -119,8 +131,7 @@ def c4_sparse(torch, hyb, W, BM, args):
         hyb.hyb_attn_decode(wl.q, wl.seq_lens, L, wl.swa, wl.comp, d["out"], topk_idx=d["topk"],
                             k=wl.k, workspace=d["ws"])
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    events = timing_events(torch, args.steps)
     secs = time_loop(torch, step, args.steps, args.warmup, R, events)
     score_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
     per_tok = BM.decode_query_bytes(L, ratio=4, sparse=True)
@@ -183,8 +194,7 @@ def c128_dense(torch, hyb, W, BM, args):
             ev[1].record()
 
     n = max(args.steps // 2, 20)
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
+    events = timing_events(torch, n)
     secs = time_loop(torch, step, n, max(args.warmup // 2, 5), R, events)
     attn_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
     per_tok = BM.decode_query_bytes(L, ratio=128, sparse=False)
