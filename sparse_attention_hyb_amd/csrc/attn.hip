@@ -211,15 +211,13 @@ struct Stage<true> {
   int valid;
 };
 
+// Two transposed 8-byte LDS reads (ds_read_b64_tr_b16) forming one 8 x bf16 MFMA operand.
 __device__ __forceinline__ bf16x8 lds_tr_pair(const uint16_t* p0, const uint16_t* p1) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
-  u32x4 w;
-  w[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-  w[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-  w[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-  w[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+  const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0)));
+  const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1)));
+  const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
   return __builtin_bit_cast(bf16x8, w);
 }
 
