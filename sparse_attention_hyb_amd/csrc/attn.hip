@@ -178,47 +178,68 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 }
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
 // Masked keys (past the end of a split, absent blocks, unused top-k slots) load this row instead
 // of a pool entry, so their operands are zero without any per-use select. Never written.
 __device__ __attribute__((aligned(16))) uint8_t kZeroRow[1024];   // zero-initialised device memory
 
 constexpr int kSeg = 2048;           // keys whose entry indices are resolved per segment
-constexpr int kPitch = kMD + 16;     // LDS row pitch of a K tile (bf16): 1056 B, 8 banks per row
+constexpr int kRow = kMD;            // LDS row of a K tile: 512 bf16 = 1024 B, no padding
+constexpr int kTileElems = kKT * kRow;
+constexpr int kPPitch = 40;          // bf16 per head row of a probability tile (80 B)
 
-// LDS address (in bf16 elements) of dims [d, d + 8) of key row `row` of a K tile. Rows are 1056 B
-// apart (8 banks), and the 16-byte chunk index is XORed with bit 3 of the row: sixteen
-// consecutive rows written or read 16 bytes each then cover all 64 banks once, while the
-// transposed reads (4 consecutive rows, which share bit 3) keep their conflict-free pattern.
-__device__ __forceinline__ int tile_off(int row, int d) {
-  return row * kPitch + ((((d >> 3) ^ ((row >> 3) & 1)) << 3) | (d & 7));
-}
-
-// One wave's quarter (64 of the 512 dims per lane-half) of one 32-key tile, held in registers
-// between its global load and its use.
-template <bool kFp8>
-struct Stage;
-template <>
-struct Stage<false> {
-  bf16x8 v[8];
-  float sc;
-  int valid;
-};
-template <>
-struct Stage<true> {
-  u32x4 v[4];
-  float sc;
-  int valid;
-};
+// K tiles sit in LDS as [key][dim] rows of 1024 B (64 chunks of 16 B, 4 chunks per bank sweep).
+// Chunk c of row r is stored at chunk c ^ swz(r), swz(r) = 4*(r%4) + (r/4)%4, which keeps both
+// access patterns free of bank conflicts: 16 consecutive rows reading one chunk (score operands
+// and stores) hit 16 different 4-bank groups, and 4 consecutive rows reading 4 consecutive
+// chunks (transposed reads for the value operand) hit 16 different groups as well.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // Two transposed 8-byte LDS reads (ds_read_b64_tr_b16) forming one 8 x bf16 MFMA operand.
 __device__ __forceinline__ bf16x8 lds_tr_pair(const uint16_t* p0, const uint16_t* p1) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
   const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0)));
   const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1)));
   const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
   return __builtin_bit_cast(bf16x8, w);
+}
+
+// Reductions over the four 16-lane rows of a wave (lanes with equal lane % 16), without LDS.
+// v_permlane16_swap / v_permlane32_swap exchange rows between their two operands; with both
+// operands holding x, the two results are rows {0,0,2,2} and {1,1,3,3} (resp. {lo,lo}, {hi,hi}).
+// Compiler pitfalls avoided here: the returned pair is read into two scalars (built into a
+// two-element vector, or bit-cast to one, the optimiser reads its first element twice), and the
+// second operand is an opaque copy so that the two results are never taken to be equal.
+template <bool kRow32>
+__device__ __forceinline__ void swap_rows(float x, float& r0, float& r1) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, x);
+  uint32_t b = a;
+  asm volatile("" : "+v"(b));
+  uint32_t u0, u1;
+  if constexpr (kRow32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    u0 = r[0];
+    u1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    u0 = r[0];
+    u1 = r[1];
+  }
+  r0 = __builtin_bit_cast(float, u0);
+  r1 = __builtin_bit_cast(float, u1);
+}
+__device__ __forceinline__ float rows_max(float x) {
+  float a, b;
+  swap_rows<false>(x, a, b);
+  swap_rows<true>(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  float a, b;
+  swap_rows<false>(x, a, b);
+  swap_rows<true>(a + b, a, b);
+  return a + b;
 }
 
 // The hardware hands consecutive workgroup ids to the 8 XCDs in turn. This maps a workgroup id to
@@ -231,86 +252,110 @@ __device__ __forceinline__ int xcd_logical(int L, int total) {
   return x < rem ? x * (per + 1) + s : rem * (per + 1) + (x - rem) * per + s;
 }
 
-// MFMA attention. Work of one workgroup: query i, keys [split*chunk, (split+1)*chunk) of its list.
-// Waves form a 2 x 2 grid: hh = head half (32 heads), dh = dim half (256 dims). Each wave keeps
-// its query slice (32 heads x 256 dims) in registers and loads only dim quarter qd = 2*dh + hh of
-// every key (each key byte is fetched once per workgroup), one iteration ahead of its publication
-// (one staged tile in registers keeps the kernel free of spills). Tiles pass through three LDS
-// buffers, and each loop iteration needs a single barrier:
-//   iteration t: S(t) = own QK partial + the partner's (exchanged through double-buffered LDS),
-//                publish this wave's quarter of tile t+2, issue the loads of tile t+3,
-//                QK partial of tile t+1 (MFMA, independent of the softmax below),
-//                softmax of tile t, PV of tile t (K tile read back transposed), barrier.
-// At the barrier ending iteration t every wave has finished reading the buffer of tile t, which
-// iteration t+1 refills with tile t+3, and the score buffer read in iteration t, which iteration
-// t+1 refills with the partials of tile t+2.
+// One thread's share of one 32-key tile between its global load and its LDS store: key t/16,
+// chunks t%16 + 16c (c < 4) of the row (bf16: 16 B each; fp8: 8 codes each).
 template <bool kFp8>
-__global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ktile[3 * kKT * kPitch];
-  __shared__ __attribute__((aligned(16))) float sx[2][4][4 * 64 * 4];   // [buf][wave][quad][lane][4]
+struct Stage;
+template <>
+struct Stage<false> {
+  bf16x8 v[4];
+  float sc;
+};
+template <>
+struct Stage<true> {
+  u32x2 v[4];
+  float sc;
+};
+
+// MFMA attention. Work of one workgroup: query i, keys [split*chunk, (split+1)*chunk) of its list.
+// Eight waves, two per SIMD, in two roles:
+//   score waves 0..3: wave q owns heads 16q..16q+15. S^T[key][h] = sum_d K[key][d] Q[h][d] on
+//        v_mfma_f32_16x16x32_bf16 (two 16-key blocks x 16 steps of 32 dims, query in registers,
+//        keys from the LDS tile), then the online softmax of those heads; the probabilities go to
+//        LDS as bf16 [head][key], with the factor that rescales the running output.
+//   value waves 4..7: wave (hh, dh) owns O^T for dims 256dh..+256 x heads 32hh..+32.
+//        O^T[d][h] += sum_key K^T[d][key] P^T[key][h] on v_mfma_f32_32x32x16_bf16, the K tile (the
+//        same bytes as the values) read back transposed.
+// All eight waves load the tiles: each thread carries its share of three tiles in registers
+// (loads are issued three tiles ahead of their store to LDS). Tiles rotate through three LDS
+// buffers and probabilities through two, with one barrier per tile:
+//   iteration t: store tile t+2 and issue the loads of tile t+5; score waves: scores and softmax
+//                of tile t+1; value waves: PV of tile t; barrier.
+// The buffer stored in iteration t held tile t-1, last read by PV in iteration t-1; the
+// probability buffer written in iteration t was last read in iteration t-1.
+// fp8 pools: codes are widened to bf16 exactly; the per-entry scale multiplies the score before
+// the softmax and the probability before PV (so no rounding of scaled values).
+template <bool kFp8>
+__global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[3 * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t ptile[2 * kMH * kPPitch];
+  __shared__ __attribute__((aligned(16))) float alpha_s[2 * kMH];
+  __shared__ uint32_t rflag[2 * 4];
   __shared__ int32_t kidx[kSeg];
+  __shared__ uint32_t tmask[kSeg / kKT];   // per tile of the segment: bit j = key j is valid
   __shared__ __attribute__((aligned(16))) float kscale[3 * kKT];
-  __shared__ uint32_t kvalid[3];   // per tile buffer: bit j = key j of the tile is valid
 
   const int logical = xcd_logical(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
   const int sp = logical % a.n_split, i = logical / a.n_split;
   const QueryKeys qk = query_keys(a, i);
   const int j_begin = sp * a.chunk, j_end = min(qk.n_keys, j_begin + a.chunk);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 31, hf = lane >> 5;
-  const int hh = wave >> 1, dh = wave & 1;
-  const int qd = 2 * dh + hh;          // the dim quarter this wave loads
-
-  // Q^T is the QK B operand (column = head 32*hh + col); K-step s covers quarter 2*dh + s/8, dims
-  // 128*quarter + 64*hf + 8*(s%8) + [0, 8): the same split the K operand uses.
-  bf16x8 qreg[16];
-  {
-    const uint16_t* qrow =
-        reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)i * kMH + 32 * hh + col) * kMD + 64 * hf;
-#pragma unroll
-    for (int s = 0; s < 16; ++s)
-      qreg[s] = *reinterpret_cast<const bf16x8*>(qrow + 128 * (2 * dh + (s >> 3)) + 8 * (s & 7));
-  }
-  f32x16 o[8];
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb) o[mb] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool scorer = wave < 4;
   const float sl2 = a.scale * kLog2e;
-  const int lane_off = 128 * qd + 64 * hf;   // first dim of this lane's staged run
 
-  // LDS addresses in a tile buffer (bf16 elements), tile_off() written out as a per-lane base plus
-  // a compile-time offset, so that few address registers stay live. Row col's 16-byte chunk c sits
-  // at chunk c ^ x (x = bit 3 of the row): +8 elements for even c, -8 for odd c when x = 1.
-  const int x8 = 8 * ((col >> 3) & 1);
-  const int qk_even = col * kPitch + 256 * dh + 64 * hf + x8;   // + 128*(s/8) + 8*(s%8), s even
-  const int qk_odd = col * kPitch + 256 * dh + 64 * hf - x8;    // ... s odd
-  const int pub_even = col * kPitch + lane_off + x8;            // + 8c, c even
-  const int pub_odd = col * kPitch + lane_off - x8;             // ... c odd
-  // transposed PV reads: rows trow + 16*t2 (bit 3 clear) and trow + 16*t2 + 8 (bit 3 set), dims
-  // tdim + 32*mb; in the second row the chunk index is flipped: +8 elements if its bit 0 (bit 3 of
-  // tdim) is clear, -8 if set
-  const int i16 = lane & 15;
-  const int trow = 4 * hf + (i16 >> 2);
-  const int tdim = 256 * dh + (col >> 4) * 16 + 4 * (i16 & 3);
-  const int pv_lo = trow * kPitch + tdim;
-  const int pv_hi = (trow + 8) * kPitch + tdim + (((tdim >> 3) & 1) ? -8 : 8);
+  // loader: key lk of a tile, chunks lp + 16c
+  const int lk = tid >> 4, lp = tid & 15;
+  const int st_base = lk * kRow + 8 * (lp ^ swz(lk));   // + 128*c elements
+
+  // score waves: head 16*wave + sh, keys 16b + 4*sg + r of the tile
+  const int sh = lane & 15, sg = lane >> 4;
+  // value waves
+  const int vw = wave - 4;
+  const int hh = (vw >> 1) & 1, dh = vw & 1;
+  const int col = lane & 31, hf = lane >> 5, i16 = lane & 15;
+
+  // The two roles run separate copies of the tile loop (same loads, stores and barriers), so that
+  // neither keeps the other's state (query registers, output accumulators) live.
+  auto role = [&](auto score_role) {
+  constexpr bool kScore = decltype(score_role)::value;
+  bf16x8 qreg[16];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[8];
+  if constexpr (kScore) {
+    // Q^T is the B operand: column = head, k-step ks covers dims 32ks + 8*sg + [0, 8)
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)i * kMH + 16 * wave + sh) * kMD + 8 * sg;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) o[mb] = f32x16{};
+  }
 
   for (int seg = j_begin; seg < j_end; seg += kSeg) {
     const int nseg = min(kSeg, j_end - seg);
-    __syncthreads();   // readers of the previous segment's index table and tiles are done
-    for (int jj = tid; jj < nseg; jj += 256) {
-      KeyRef r = resolve_key(a, i, qk.seq, qk.ws, qk.n_win, qk.nv, seg + jj);
-      kidx[jj] = (int32_t)r.idx;
+    const int n_tiles = (nseg + kKT - 1) / kKT;
+    __syncthreads();   // every reader of the previous segment's tables and tiles is done
+    for (int j0 = 0; j0 < n_tiles * kKT; j0 += 512) {
+      const int jj = j0 + tid;
+      int idx = -1;
+      if (jj < nseg) idx = (int32_t)resolve_key(a, i, qk.seq, qk.ws, qk.n_win, qk.nv, seg + jj).idx;
+      if (jj < kSeg) kidx[jj] = idx;
+      const uint64_t vb = __ballot(idx >= 0);   // keys 64*wave + j0 + [0, 64): two tiles
+      if (lane == 0 && jj < kSeg) {
+        tmask[jj / kKT] = (uint32_t)vb;
+        tmask[jj / kKT + 1] = (uint32_t)(vb >> 32);
+      }
     }
     __syncthreads();
-    const int n_tiles = (nseg + kKT - 1) / kKT;
 
-    // Loads are issued without any branch (masked lanes read the zero row): a branch between a
+    // Loads are issued without any branch (masked keys read the zero row): a branch between a
     // prefetch and the use of an older tile would make the compiler wait for every outstanding
     // load, prefetch included. Tiles past the end load masked rows.
     auto load = [&](Stage<kFp8>& st, int tt) {
-      const int jraw = tt * kKT + col;
+      const int jraw = tt * kKT + lk;
       const int jl = min(jraw, nseg - 1);
       const int idx = kidx[jl];
       const bool ok = jraw < nseg && idx >= 0;
@@ -318,208 +363,217 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
       const uint8_t* base = win ? a.swa.data : a.comp.data;
       const int64_t eb = win ? a.swa.entry_bytes : a.comp.entry_bytes;
       const uint8_t* entry = ok ? base + (int64_t)idx * eb : kZeroRow;
-      st.valid = ok;
       if constexpr (!kFp8) {
-        const uint16_t* row = reinterpret_cast<const uint16_t*>(entry) + lane_off;
+        const uint16_t* row = reinterpret_cast<const uint16_t*>(entry) + 8 * lp;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) st.v[c] = *reinterpret_cast<const bf16x8*>(row + 8 * c);
+        for (int c = 0; c < 4; ++c) st.v[c] = *reinterpret_cast<const bf16x8*>(row + 128 * c);
         st.sc = 1.f;
       } else {
-        const uint8_t* row = entry + lane_off;
+        const uint8_t* row = entry + 8 * lp;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) st.v[c] = *reinterpret_cast<const u32x4*>(row + 16 * c);
-        st.sc = reinterpret_cast<const float*>(win ? a.swa.scale : a.comp.scale)[ok ? idx : 0];
+        for (int c = 0; c < 4; ++c) st.v[c] = *reinterpret_cast<const u32x2*>(row + 128 * c);
+        const float s = reinterpret_cast<const float*>(win ? a.swa.scale : a.comp.scale)[ok ? idx : 0];
+        st.sc = ok ? s : 0.f;
       }
     };
-    auto own = [&](const Stage<kFp8>& st, int c) -> bf16x8 {
-      if constexpr (!kFp8) {
-        return st.v[c];
-      } else {
-        const u32x4 q = st.v[c >> 1];
-        return (c & 1) ? fp8x8_to_bf16x8(q[2], q[3]) : fp8x8_to_bf16x8(q[0], q[1]);
-      }
-    };
-    // This wave's quarter of tile tt into its buffer (natural [key][dim] layout), with the
-    // validity of the tile's 32 keys (bit j = key j; every wave resolved the same keys).
     auto publish = [&](const Stage<kFp8>& st, int tt) {
-      uint16_t* kt = ktile + (tt % 3) * (kKT * kPitch);
+      uint16_t* kt = ktile + (tt % 3) * kTileElems + st_base;
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        *reinterpret_cast<bf16x8*>(kt + ((c & 1) ? pub_odd : pub_even) + 8 * c) = own(st, c);
-      const uint32_t vm = (uint32_t)__ballot(st.valid);
-      if (wave == 0) {
-        if constexpr (kFp8) {
-          if (hf == 0) kscale[(tt % 3) * kKT + col] = st.valid ? st.sc : 0.f;
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (!kFp8) {
+          *reinterpret_cast<bf16x8*>(kt + 128 * c) = st.v[c];
+        } else {
+          *reinterpret_cast<bf16x8*>(kt + 128 * c) = fp8x8_to_bf16x8(st.v[c][0], st.v[c][1]);
         }
-        if (lane == 0) kvalid[tt % 3] = vm;
+      }
+      if constexpr (kFp8) {
+        if (lp == 0) kscale[(tt % 3) * kKT + lk] = st.sc;
       }
     };
-    // QK over this wave's dim half, both quarters read from the tile's buffer; two independent
-    // accumulation chains (even / odd K-steps) keep the MFMA pipe busy.
-    auto qk_partial = [&](int tt) -> f32x16 {
-      const uint16_t* kt = ktile + (tt % 3) * (kKT * kPitch);
-      f32x16 acc0 = {}, acc1 = {};
+
+    // ---- score waves: scores and softmax of tile tt into probability buffer tt % 2
+    auto score_tile = [&](int tt) {
+      // A operand (16 keys x 32 dims): row 16b + sh, logical chunk 4ks + sg, stored at
+      // 16(ks/4) + 4((ks%4) ^ (sh%4)) + (sg ^ (sh/4)%4). The four per-lane bases (one per ks%4)
+      // are made opaque to the optimiser so that it uses the reads' immediate offsets.
+      int qb[4];
 #pragma unroll
-      for (int s = 0; s < 16; s += 2) {
-        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kt + qk_even + 128 * (s >> 3) + 8 * (s & 7));
-        const bf16x8 k1 =
-            *reinterpret_cast<const bf16x8*>(kt + qk_odd + 128 * ((s + 1) >> 3) + 8 * ((s + 1) & 7));
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[s + 1], acc1, 0, 0, 0);
-      }
-      return acc0 + acc1;
-    };
-    // [buf][wave][quad][lane][4]: a wave's 16-byte accesses are lane-contiguous (no conflicts)
-    auto write_sx = [&](int tt, const f32x16& v) {
-      f32x4* mine = reinterpret_cast<f32x4*>(&sx[tt & 1][wave][0]) + lane;
+      for (int m = 0; m < 4; ++m)
+        qb[m] = (tt % 3) * kTileElems + sh * kRow + 8 * (4 * (m ^ (sh & 3)) + (sg ^ ((sh >> 2) & 3)));
+      asm volatile("" : "+v"(qb[0]), "+v"(qb[1]), "+v"(qb[2]), "+v"(qb[3]));
+      f32x4 acc[2][2] = {};
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 w;
+      for (int ks = 0; ks < 16; ++ks)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = v[4 * q4 + e];
-        mine[64 * q4] = w;
-      }
-    };
-    auto read_sx = [&](int tt) -> f32x16 {
-      const f32x4* theirs = reinterpret_cast<const f32x4*>(&sx[tt & 1][wave ^ 1][0]) + lane;
-      f32x16 v;
+        for (int b = 0; b < 2; ++b) {
+          const bf16x8 kf =
+              *reinterpret_cast<const bf16x8*>(ktile + qb[ks & 3] + 16 * b * kRow + 128 * (ks >> 2));
+          acc[b][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qreg[ks], acc[b][ks & 1], 0, 0, 0);
+        }
+      // this lane: head 16*wave + sh, key 16b + 4sg + r <-> z[4b + r]
+      float z[8];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 w = theirs[64 * q4];
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * q4 + e] = w[e];
-      }
-      return v;
-    };
-    // Online softmax of tile tt for head 32*hh + col (this lane's keys are 8*(r/4) + 4*hf + r%4),
-    // then PV over the tile.
-    auto soft_pv = [&](const f32x16& S, int tt) {
-      const uint16_t* kt = ktile + (tt % 3) * (kKT * kPitch);
-      const uint32_t vmask = kvalid[tt % 3];
-      float ksc[16];
+        for (int r = 0; r < 4; ++r) z[4 * b + r] = acc[b][0][r] + acc[b][1][r];
+      float ksc[8];
       if constexpr (kFp8) {
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(kscale + (tt % 3) * kKT + 8 * j4 + 4 * hf);
+        for (int b = 0; b < 2; ++b) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(kscale + (tt % 3) * kKT + 16 * b + 4 * sg);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ksc[4 * j4 + e] = v[e];
+          for (int r = 0; r < 4; ++r) ksc[4 * b + r] = v[r];
         }
-      }
-      float z[16];
-      float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
-        float v = S[r] * sl2;
-        if constexpr (kFp8) v *= ksc[r];
-        z[r] = ((vmask >> key) & 1u) ? v : -INFINITY;
-        mx = fmaxf(mx, z[r]);
+        for (int e = 0; e < 8; ++e) z[e] *= ksc[e];
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const uint32_t vm = __builtin_amdgcn_readfirstlane(tmask[tt]);
+      if (vm != 0xffffffffu) {   // only tiles with masked keys pay for the mask
+        const uint32_t lm = vm >> (4 * sg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = ((lm >> (16 * (e >> 2) + (e & 3))) & 1u) ? z[e] : -INFINITY;
+      }
+      // The scores stay unscaled: max(z) * sl2 = max(z * sl2) for sl2 > 0, and the exponent takes
+      // sl2 in a fused multiply-add.
+      float mx = z[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
+      mx = rows_max(mx) * sl2;
       // The reference maximum only moves when a score exceeds it by more than 2^8 (or on the
-      // first keys): probabilities then stay <= 256, and the O rescale is skipped for the wave
-      // unless one of its heads moved. Exact: l and O share the same reference.
-      if (__ballot(mx > m_run + 8.f) != 0) {
+      // first keys): probabilities then stay <= 256, and the value waves rescale O only for
+      // tiles where one of the wave's heads moved. Exact: l and O share the same reference.
+      float alpha = 1.f;
+      const bool moved = __ballot(mx > m_run + 8.f) != 0;
+      if (moved) {
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
+        m_run = m_new;
+      }
+      const int pb = tt & 1;
+      if (sg == 0) alpha_s[pb * kMH + 16 * wave + sh] = alpha;
+      if (lane == 0) rflag[pb * 4 + wave] = moved ? 1u : 0u;
+      const float nref = m_run == -INFINITY ? 0.f : -m_run;
+      float p[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[e], sl2, nref));
+        psum += p[e];
+      }
+      l_run += rows_sum(psum);
+      if constexpr (kFp8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] *= ksc[e];
+      }
+      // [head][key] rows; key 16b + 4sg + r sits at 16b + 8(sg%2) + 4(sg/2) + r, the order of the
+      // value waves' B operand (element e of step t2 <-> key 16t2 + 8(e/4) + 4hf + e%4)
+      uint16_t* prow = ptile + pb * kMH * kPPitch + (16 * wave + sh) * kPPitch + 8 * (sg & 1) + 4 * (sg >> 1);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const u32x2 w = {pack_bf16x2(p[4 * b], p[4 * b + 1]), pack_bf16x2(p[4 * b + 2], p[4 * b + 3])};
+        *reinterpret_cast<u32x2*>(prow + 16 * b) = w;
+      }
+    };
+
+    // ---- value waves: rescale and PV of tile tt
+    auto value_tile = [&](int tt) {
+      const int pb = tt & 1;
+      const uint32_t fl = __builtin_amdgcn_readfirstlane(rflag[pb * 4 + 2 * hh] | rflag[pb * 4 + 2 * hh + 1]);
+      if (fl) {
+        const float al = alpha_s[pb * kMH + 32 * hh + col];
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
-        m_run = m_new;
+          for (int r = 0; r < 16; ++r) o[mb][r] *= al;
       }
-      const float ref = m_run == -INFINITY ? 0.f : m_run;
-      float psum = 0.f;
-      float pr[16];
+      // B = P^T: 8 keys of step t2 for head 32hh + col
+      const uint16_t* prow = ptile + pb * kMH * kPPitch + (32 * hh + col) * kPPitch + 8 * hf;
+      bf16x8 pbf[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(z[r] - ref);
-        psum += e;
-        if constexpr (kFp8) {
-          pr[r] = e * ksc[r];
-        } else {
-          pr[r] = e;
-        }
-      }
-      psum += __shfl_xor(psum, 32, 64);
-      l_run += psum;
-      // PV: B = probabilities (element e of K-step t2 <-> key 16*t2 + 8(e/4) + 4hf + e%4),
-      //     A = K^T read transposed from LDS: lane j of each 16-lane group points at key
-      //     k0 + j/4, dims d0 + 4*(j%4), and receives keys k0..k0+3 of dim d0 + j.
-      bf16x8 pb[2];
+      for (int t2 = 0; t2 < 2; ++t2) pbf[t2] = *reinterpret_cast<const bf16x8*>(prow + 16 * t2);
+      // A = K^T (32 dims x 16 keys) read transposed: lane j of each 16-lane group points at row
+      // k0 + j/4 (+8 for the second read), dims d0 + 4(j%4), and receives 4 keys of dim d0 + j.
+      // Rows 16t2 + 4hf + i16/4 (+8x), dims 256dh + 32mb + 16(col/16) + 4(i16%4); stored chunk
+      // = logical chunk ^ swz(row), with swz(row) = 4(i16/4) + hf + 2x. One base per (x, mb%4).
+      int vb[2][4];
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        u32x4 w;
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(pr[8 * t2 + 2 * e], pr[8 * t2 + 2 * e + 1]);
-        pb[t2] = __builtin_bit_cast(bf16x8, w);
-      }
+        for (int m = 0; m < 4; ++m)
+          vb[x][m] = (tt % 3) * kTileElems + (4 * hf + (i16 >> 2) + 8 * x) * kRow +
+                     8 * (32 * dh + 4 * (m ^ (i16 >> 2)) +
+                          ((2 * (col >> 4) + ((i16 & 3) >> 1)) ^ (hf + 2 * x))) +
+                     4 * (i16 & 1);
+      asm volatile("" : "+v"(vb[0][0]), "+v"(vb[0][1]), "+v"(vb[0][2]), "+v"(vb[0][3]));
+      asm volatile("" : "+v"(vb[1][0]), "+v"(vb[1][1]), "+v"(vb[1][2]), "+v"(vb[1][3]));
       auto trf = [&](int mb, int t2) {
-        return lds_tr_pair(kt + pv_lo + 16 * t2 * kPitch + 32 * mb,
-                           kt + pv_hi + 16 * t2 * kPitch + 32 * mb);
+        const int off = 16 * t2 * kRow + 128 * (mb >> 2);
+        return lds_tr_pair(ktile + vb[0][mb & 3] + off, ktile + vb[1][mb & 3] + off);
       };
-      // fragments for block mb + 1 are read while block mb multiplies
-      bf16x8 af[2][2];
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) af[0][t2] = trf(0, t2);
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        if (mb + 1 < 8) {
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) af[(mb + 1) & 1][t2] = trf(mb + 1, t2);
-        }
+      for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
-          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb & 1][t2], pb[t2], o[mb], 0, 0, 0);
-      }
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf(mb, t2), pbf[t2], o[mb], 0, 0, 0);
     };
 
-    // One tile is in flight in registers; the tile after it is already in its LDS buffer.
-    Stage<kFp8> s0;
+    Stage<kFp8> s0, s1, s2;
     load(s0, 0);
+    load(s1, 1);
+    load(s2, 2);
     publish(s0, 0);
-    load(s0, 1);
+    load(s0, 3);
     __syncthreads();
-    f32x16 sown = qk_partial(0);
-    write_sx(0, sown);
-    publish(s0, 1);
-    load(s0, 2);
+    if constexpr (kScore) score_tile(0);
+    publish(s1, 1);
+    load(s1, 4);
     __syncthreads();
-    // iteration t; X holds tile t+2, whose buffer was last read in iteration t-1
+    // iteration t: X holds tile t+2 (stored now, then reloaded with tile t+5)
     auto iter = [&](int t, Stage<kFp8>& X) {
-      const f32x16 S = sown + read_sx(t);
       publish(X, t + 2);
-      load(X, t + 3);
-      f32x16 snext = {};
-      if (t + 1 < n_tiles) {
-        snext = qk_partial(t + 1);
-        write_sx(t + 1, snext);
+      load(X, t + 5);
+      if constexpr (kScore) {
+        if (t + 1 < n_tiles) score_tile(t + 1);
+      } else {
+        value_tile(t);
       }
-      soft_pv(S, t);
-      sown = snext;
       __syncthreads();
     };
-    for (int t = 0; t < n_tiles; ++t) iter(t, s0);
-  }
-  // ---- partials: O^T rows d = 256*dh + 32*mb + 8*(r/4) + 4*hf + r%4, column h = 32*hh + col
-  float* po = a.part_o + ((int64_t)i * a.n_split + sp) * kMD * kMH;
-  const int h = 32 * hh + col;
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int d = 256 * dh + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3);
-      po[d * kMH + h] = o[mb][r];
+    for (int t = 0; t < n_tiles; t += 3) {
+      iter(t, s2);
+      if (t + 1 >= n_tiles) break;
+      iter(t + 1, s0);
+      if (t + 2 >= n_tiles) break;
+      iter(t + 2, s1);
     }
-  if (dh == 0 && hf == 0) {
-    float* pml = a.part_ml + ((int64_t)i * a.n_split + sp) * 2 * kMH;
-    // m is kept in log2 units inside the kernel; store natural-log units for the combine
-    pml[h] = m_run == -INFINITY ? -INFINITY : m_run / kLog2e;
-    pml[kMH + h] = l_run;
   }
+  if constexpr (kScore) {
+    if (sg == 0) {
+      float* pml = a.part_ml + ((int64_t)i * a.n_split + sp) * 2 * kMH;
+      const int h = 16 * wave + sh;
+      // m is kept in log2 units inside the kernel; store natural-log units for the combine
+      pml[h] = m_run == -INFINITY ? -INFINITY : m_run / kLog2e;
+      pml[kMH + h] = l_run;
+    }
+  } else {
+    // O^T rows d = 256*dh + 32*mb + 8*(r/4) + 4*hf + r%4, column h = 32*hh + col
+    float* po = a.part_o + ((int64_t)i * a.n_split + sp) * kMD * kMH;
+    const int h = 32 * hh + col;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 256 * dh + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3);
+        po[d * kMH + h] = o[mb][r];
+      }
+  }
+  };
+  if (scorer)
+    role(std::true_type{});
+  else
+    role(std::false_type{});
 }
-
 // ------------------------------------------------------------------------------------------
 // Combine: merge split partials, inverse RoPE at the query position, cast.
 // Workgroup (dim slice of 32, query), mapped to the XCD that ran the query's splits so that their
@@ -663,9 +717,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.n_q);
   if (a.use_mfma) {
     if (a.swa.dtype == FP8)
-      hipLaunchKernelGGL(attn_mfma<true>, grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(attn_mfma<true>, grid, dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL(attn_mfma<false>, grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(attn_mfma<false>, grid, dim3(512), 0, s, a);
   } else {
     size_t lds = sizeof(float) * ((size_t)2 * a.n_heads * a.dim + (size_t)a.n_heads * kGenTile +
                                   3 * (size_t)a.n_heads);
