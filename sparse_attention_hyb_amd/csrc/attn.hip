@@ -23,6 +23,7 @@
 //        back transposed.
 // fp8 pools: codes are widened to bf16 exactly; the per-entry scale multiplies the score before
 // the softmax and the probability before PV (so no rounding of scaled values).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -152,11 +153,11 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a) {
     }
     __syncthreads();
   }
-  // partials: o as [dim][head], then m and l per head
-  float* po = a.part_o + ((int64_t)i * a.n_split + sp) * D * H;
+  // partials: o / l as [head][dim] (zero for a split without keys), then m and l per head
+  float* po = reinterpret_cast<float*>(a.part_o) + ((int64_t)i * a.n_split + sp) * D * H;
   for (int e = threadIdx.x; e < H * D; e += 256) {
-    const int d = e / H, h = e % H;
-    po[e] = os[h * D + d];
+    const float l = lrow[e / D];
+    po[e] = l > 0.f ? os[e] / l : 0.f;
   }
   float* pml = a.part_ml + ((int64_t)i * a.n_split + sp) * 2 * H;
   for (int h = threadIdx.x; h < H; h += 256) {
@@ -294,6 +295,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
   __shared__ int32_t kidx[kSeg];
   __shared__ uint32_t tmask[kSeg / kKT];   // per tile of the segment: bit j = key j is valid
   __shared__ __attribute__((aligned(16))) float kscale[3 * kKT];
+  __shared__ float lfin[kMH];
 
   const int logical = xcd_logical(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
   const int sp = logical % a.n_split, i = logical / a.n_split;
@@ -323,13 +325,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
   bf16x8 qreg[16];
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[8];
-  if constexpr (kScore) {
-    // Q^T is the B operand: column = head, k-step ks covers dims 32ks + 8*sg + [0, 8)
-    const uint16_t* qrow =
-        reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)i * kMH + 16 * wave + sh) * kMD + 8 * sg;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-  } else {
+  if constexpr (!kScore) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) o[mb] = f32x16{};
   }
@@ -338,15 +334,64 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
     const int nseg = min(kSeg, j_end - seg);
     const int n_tiles = (nseg + kKT - 1) / kKT;
     __syncthreads();   // every reader of the previous segment's tables and tiles is done
-    for (int j0 = 0; j0 < n_tiles * kKT; j0 += 512) {
-      const int jj = j0 + tid;
-      int idx = -1;
-      if (jj < nseg) idx = (int32_t)resolve_key(a, i, qk.seq, qk.ws, qk.n_win, qk.nv, seg + jj).idx;
-      if (jj < kSeg) kidx[jj] = idx;
-      const uint64_t vb = __ballot(idx >= 0);   // keys 64*wave + j0 + [0, 64): two tiles
-      if (lane == 0 && jj < kSeg) {
-        tmask[jj / kKT] = (uint32_t)vb;
-        tmask[jj / kKT + 1] = (uint32_t)(vb >> 32);
+    {
+      // Entry index of every key of the segment (-1 = masked), with its loads batched: each
+      // thread issues the top-k reads of its (up to four) keys, then their block-table reads, so
+      // the whole table costs two dependent global round trips. Every load is in bounds
+      // (clamped indices); masked keys discard the value read.
+      constexpr int kR = kSeg / 512;
+      const int nres = n_tiles * kKT;
+      int g[kR];
+      bool win[kR];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const int j = seg + r * 512 + tid;
+        win[r] = j < qk.n_win;
+        g[r] = win[r] ? qk.ws + j : j - qk.n_win;   // window position or compressed slot
+      }
+      if (a.topk != nullptr) {
+        int tv[kR];
+#pragma unroll
+        for (int r = 0; r < kR; ++r) tv[r] = a.topk[(int64_t)i * a.k + min(max(g[r], 0), a.k - 1)];
+#pragma unroll
+        for (int r = 0; r < kR; ++r)
+          if (!win[r]) g[r] = tv[r];
+      }
+      int lb[kR], phys[kR];
+      bool lok[kR];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const bool w = win[r];
+        const int per = w ? a.swa.per_block : a.comp.per_block;
+        const bool gok = r * 512 + tid < nseg && g[r] >= 0 && (w || g[r] < qk.nv);
+        lb[r] = gok ? g[r] / per : 0;
+        lok[r] = gok && lb[r] < (w ? a.swa.max_blocks : a.comp.max_blocks);
+      }
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const bool w = win[r];
+        const int32_t* bt = w ? a.swa.block_table : a.comp.block_table;
+        const int mbk = w ? a.swa.max_blocks : a.comp.max_blocks;
+        phys[r] = bt[(int64_t)qk.seq * mbk + (lok[r] ? lb[r] : 0)];
+      }
+      int idxr[kR];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const bool w = win[r];
+        const int per = w ? a.swa.per_block : a.comp.per_block;
+        const int nbk = w ? a.swa.num_blocks : a.comp.num_blocks;
+        idxr[r] = (lok[r] && phys[r] >= 0 && phys[r] < nbk) ? phys[r] * per + (g[r] - lb[r] * per) : -1;
+      }
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        if (r * 512 >= nres) continue;
+        const int jj = r * 512 + tid;
+        kidx[jj] = idxr[r];
+        const uint64_t vb = __ballot(idxr[r] >= 0);   // keys r*512 + 64*wave + [0, 64): two tiles
+        if (lane == 0) {
+          tmask[jj / kKT] = (uint32_t)vb;
+          tmask[jj / kKT + 1] = (uint32_t)(vb >> 32);
+        }
       }
     }
     __syncthreads();
@@ -518,6 +563,15 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
           o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf(mb, t2), pbf[t2], o[mb], 0, 0, 0);
     };
 
+    if constexpr (kScore) {
+      // Q^T is the B operand: column = head, k-step ks covers dims 32ks + 8*sg + [0, 8). Read
+      // here (again for a later segment) so that its latency overlaps the first tile loads
+      // rather than the key resolution.
+      const uint16_t* qrow =
+          reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)i * kMH + 16 * wave + sh) * kMD + 8 * sg;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    }
     Stage<kFp8> s0, s1, s2;
     load(s0, 0);
     load(s1, 1);
@@ -548,6 +602,11 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
       iter(t + 2, s1);
     }
   }
+  // ---- partials: m and l per head from the score waves; O / l as bf16 [head][dim] (zero for a
+  // split without keys), staged through LDS by the value waves so that every global store writes
+  // one contiguous 1 KB row
+  constexpr int kOPitch = kMD + 8;   // staged row (bf16): 1040 B, rows 4 banks apart
+  uint16_t* ost = ktile;             // the tile buffers are free after the last barrier
   if constexpr (kScore) {
     if (sg == 0) {
       float* pml = a.part_ml + ((int64_t)i * a.n_split + sp) * 2 * kMH;
@@ -555,18 +614,38 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
       // m is kept in log2 units inside the kernel; store natural-log units for the combine
       pml[h] = m_run == -INFINITY ? -INFINITY : m_run / kLog2e;
       pml[kMH + h] = l_run;
+      lfin[h] = l_run;
     }
+    __syncthreads();
+    __syncthreads();
   } else {
-    // O^T rows d = 256*dh + 32*mb + 8*(r/4) + 4*hf + r%4, column h = 32*hh + col
-    float* po = a.part_o + ((int64_t)i * a.n_split + sp) * kMD * kMH;
+    __syncthreads();
+    // O^T rows d = 256*dh + 32*mb + 8*(r/4) + 4*hf + r%4, column h = 32*hh + col: four
+    // consecutive dims per (mb, r/4), 8 bytes each
     const int h = 32 * hh + col;
+    const float l = lfin[h];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* orow = ost + h * kOPitch + 256 * dh + 4 * hf;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 256 * dh + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3);
-        po[d * kMH + h] = o[mb][r];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x16& v = o[mb];
+        const u32x2 w = {pack_bf16x2(v[4 * q4] * inv, v[4 * q4 + 1] * inv),
+                         pack_bf16x2(v[4 * q4 + 2] * inv, v[4 * q4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + 32 * mb + 8 * q4) = w;
       }
+    __syncthreads();
+  }
+  // wave w stores rows 8w..8w+7, one row (64 lanes x 16 B) per instruction
+  {
+    uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + ((int64_t)i * a.n_split + sp) * kMH * kMD;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int row = 8 * wave + c;
+      *reinterpret_cast<u32x4*>(po + row * kMD + 8 * lane) =
+          *reinterpret_cast<const u32x4*>(ost + row * kOPitch + 8 * lane);
+    }
   }
   };
   if (scorer)
@@ -575,110 +654,194 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
     role(std::false_type{});
 }
 // ------------------------------------------------------------------------------------------
-// Combine: merge split partials, inverse RoPE at the query position, cast.
-// Workgroup (dim slice of 32, query), mapped to the XCD that ran the query's splits so that their
-// partials are read from its L2. Thread t owns dims d0 + 2(t/16) + {0, 1} of heads 4(t%16) + [0, 4):
-// per split two 16-byte loads (the partials are [dim][head], heads contiguous), all issued before
-// any is used.
+// Combine: merge the split partials, inverse RoPE at the query position, cast.
+// Split s of a query holds O_s / l_s with its (m_s, l_s); the output is sum_s w_s O_s / l_s with
+// w_s = l_s exp(m_s - M) / sum_s' l_s' exp(m_s' - M), M = max_s m_s.
+// Workgroup (group of hpw heads, query), mapped to the XCD that ran the query's splits so that the
+// partials come from its L2; thread = 8 consecutive dims of one head (one 16- or 32-byte load per
+// split, eight splits in flight), or single dims when dim % 8 != 0.
 // ------------------------------------------------------------------------------------------
-constexpr int kCombineDims = 32;
-constexpr int kCombineHeads = 64;   // heads of either attention kernel
+constexpr int kCombineHeads = 64;     // heads per combine workgroup at most
+constexpr int kCombineElems = 2048;   // elements per combine workgroup (hpw = 2048 / dim, >= 1)
+constexpr int kMaxRopePairs = 64;      // rope_dim <= 128
 
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
-  const int logical = xcd_logical(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
-  const int i = logical / gridDim.x;
-  const int d0 = (logical % gridDim.x) * kCombineDims;
-  const int H = a.n_heads, D = a.dim, ns = a.n_split;
-  int seq, p;
-  query_at(a.qd, i, &seq, &p);
-  __shared__ __attribute__((aligned(16))) float wsplit[kMaxSplit * kCombineHeads];   // [split][head]
-  __shared__ float ml[kMaxSplit * 2 * kCombineHeads];   // (m, l) staged as [split][2][head]
-  __shared__ float rc[kCombineDims / 2], rs[kCombineDims / 2];
-  const int tid = threadIdx.x;
-  {
-    const float* pml = a.part_ml + (int64_t)i * ns * 2 * H;
-    for (int e = tid; e < ns * 2 * H; e += 256) ml[e] = pml[e];
-  }
-  const int rope_lo = D - a.rope_dim;
-  const int dend = min(D, d0 + kCombineDims);
-  for (int t = tid; t < kCombineDims / 2; t += 256) {
-    const int d = d0 + 2 * t;
-    if (d >= rope_lo && d < dend)
-      rope_cs(-(double)p, (d - rope_lo) >> 1, a.rope_dim, a.rope_base, &rc[t], &rs[t]);
-  }
-  __syncthreads();
-  for (int h = tid; h < H; h += 256) {
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s * 2 * H + h]);
-    float den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = ml[s * 2 * H + h];
-      den += ms == -INFINITY ? 0.f : expf(ms - M) * ml[s * 2 * H + H + h];
-    }
-    const float inv = den > 0.f ? 1.0f / den : 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = ml[s * 2 * H + h];
-      wsplit[s * H + h] = ms == -INFINITY ? 0.f : expf(ms - M) * inv;
-    }
-  }
-  __syncthreads();
-  const float* po = a.part_o + (int64_t)i * ns * D * H;
-  auto store = [&](int h, int d, float x0, float x1, int pr) {
-    if (d >= rope_lo) {
-      const float z0 = x0 * rc[pr] - x1 * rs[pr];
-      const float z1 = x0 * rs[pr] + x1 * rc[pr];
-      x0 = z0;
-      x1 = z1;
-    }
-    const int64_t off = ((int64_t)i * H + h) * D + d;
-    if (a.out_dtype == F32) {
-      *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + off) = make_float2(x0, x1);
-    } else {
-      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + off) = pack_bf16x2(x0, x1);
-    }
-  };
-  if ((H & 3) == 0) {
-    // thread t: dim pair d0 + 2(t/16), heads 4(t%16) + [0, 4)
-    const int pr = tid >> 4, h4 = 4 * (tid & 15);
-    const int d = d0 + 2 * pr;
-    if (h4 >= H || d >= dend) return;
-    f32x4 v0 = {}, v1 = {};
-    for (int s0 = 0; s0 < ns; s0 += 8) {
-      f32x4 x0[8], x1[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int s = min(s0 + q, ns - 1);
-        x0[q] = *reinterpret_cast<const f32x4*>(po + ((int64_t)s * D + d) * H + h4);
-        x1[q] = *reinterpret_cast<const f32x4*>(po + ((int64_t)s * D + d + 1) * H + h4);
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const f32x4 wq = s0 + q < ns ? *reinterpret_cast<const f32x4*>(wsplit + (s0 + q) * H + h4)
-                                     : f32x4{};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v0[e] = fmaf(wq[e], x0[q][e], v0[e]);
-          v1[e] = fmaf(wq[e], x1[q][e], v1[e]);
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) store(h4 + e, d, v0[e], v1[e], pr);
+// Raw 8-element load of a partial (16 bytes of bf16 or 32 bytes of fp32), widened later.
+template <typename PT>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+  u32x4 w;
+};
+template <>
+struct Raw8<float> {
+  f32x4 a, b;
+};
+template <typename PT>
+__device__ __forceinline__ Raw8<PT> load8(const PT* p) {
+  Raw8<PT> r;
+  if constexpr (sizeof(PT) == 2) {
+    r.w = *reinterpret_cast<const u32x4*>(p);
   } else {
-    // any head count: one (head, dim pair) per thread and step
-    const int npair = (dend - d0) / 2;
-    for (int e = tid; e < npair * H; e += 256) {
-      const int h = e % H, pr = e / H, d = d0 + 2 * pr;
-      float x0 = 0.f, x1 = 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const float wgt = wsplit[s * H + h];
-        x0 = fmaf(wgt, po[((int64_t)s * D + d) * H + h], x0);
-        x1 = fmaf(wgt, po[((int64_t)s * D + d + 1) * H + h], x1);
-      }
-      store(h, d, x0, x1, pr);
+    r.a = *reinterpret_cast<const f32x4*>(p);
+    r.b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  return r;
+}
+template <typename PT>
+__device__ __forceinline__ void widen8(const Raw8<PT>& r, float* x) {
+  if constexpr (sizeof(PT) == 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __builtin_bit_cast(float, r.w[e] << 16);
+      x[2 * e + 1] = __builtin_bit_cast(float, r.w[e] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = r.a[e];
+      x[4 + e] = r.b[e];
     }
   }
 }
+
+template <typename PT>
+__device__ __forceinline__ float load1(const PT* p) {
+  if constexpr (sizeof(PT) == 2) {
+    return bf16_to_f32(*p);
+  } else {
+    return *p;
+  }
+}
+
+template <typename PT>
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int hpw) {
+  const int logical = xcd_logical(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
+  const int i = logical / gridDim.x;
+  const int h0 = (logical % gridDim.x) * hpw;
+  const int H = a.n_heads, D = a.dim, ns = a.n_split;
+  const int nh = min(hpw, H - h0);
+  __shared__ float wsp[kMaxSplit * kCombineHeads];       // [split][head of the group]
+  __shared__ float mls[kMaxSplit * 2 * kCombineHeads];   // [split][m, l][head of the group]
+  __shared__ float rc[kMaxRopePairs], rs[kMaxRopePairs];
+  const int tid = threadIdx.x;
+  const int64_t sstride = (int64_t)H * D;
+  const PT* po = reinterpret_cast<const PT*>(a.part_o) + (int64_t)i * ns * sstride;
+  // the first eight splits' partials are requested before the weights are formed
+  const bool oct = (D & 7) == 0;
+  const int n8 = oct ? nh * (D / 8) : 0;
+  Raw8<PT> pre[8];
+  if (oct && tid < n8) {
+    const PT* base = po + (int64_t)(h0 + tid / (D / 8)) * D + 8 * (tid % (D / 8));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) pre[q] = load8<PT>(base + min(q, ns - 1) * sstride);
+  }
+  int seq, p;
+  query_at(a.qd, i, &seq, &p);
+  const float* pml = a.part_ml + (int64_t)i * ns * 2 * H;
+  for (int e = tid; e < ns * 2 * nh; e += 256) {
+    const int s2 = e / nh, hl = e % nh;   // s2 = 2 * split + (0: m, 1: l)
+    mls[e] = pml[s2 * H + h0 + hl];
+  }
+  const int rope_lo = D - a.rope_dim;
+  for (int t = tid; t < a.rope_dim / 2; t += 256)
+    rope_cs(-(double)p, t, a.rope_dim, a.rope_base, &rc[t], &rs[t]);
+  __syncthreads();
+  for (int hl = tid; hl < nh; hl += 256) {
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, mls[(2 * s) * nh + hl]);
+    float den = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float ms = mls[(2 * s) * nh + hl];
+      den += ms == -INFINITY ? 0.f : expf(ms - M) * mls[(2 * s + 1) * nh + hl];
+    }
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float ms = mls[(2 * s) * nh + hl];
+      wsp[s * kCombineHeads + hl] = ms == -INFINITY ? 0.f : expf(ms - M) * mls[(2 * s + 1) * nh + hl] * inv;
+    }
+  }
+  __syncthreads();
+  auto finish = [&](int h, int d, float* x, int n) {   // n = 8 or 1 values at dims d..d+n-1
+    if (n == 8 && d + 8 > rope_lo) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        if (d + e >= rope_lo) {
+          const int pr = (d + e - rope_lo) >> 1;
+          const float z0 = x[e] * rc[pr] - x[e + 1] * rs[pr];
+          const float z1 = x[e] * rs[pr] + x[e + 1] * rc[pr];
+          x[e] = z0;
+          x[e + 1] = z1;
+        }
+      }
+    }
+    const int64_t off = ((int64_t)i * H + h) * D + d;
+    if (n == 8) {
+      if (a.out_dtype == F32) {
+        float* o = reinterpret_cast<float*>(a.out) + off;
+        *reinterpret_cast<f32x4*>(o) = f32x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{x[4], x[5], x[6], x[7]};
+      } else {
+        const u32x4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                         pack_bf16x2(x[6], x[7])};
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + off) = w;
+      }
+    } else {
+      if (a.out_dtype == F32)
+        reinterpret_cast<float*>(a.out)[off] = x[0];
+      else
+        reinterpret_cast<uint16_t*>(a.out)[off] = (uint16_t)(pack_bf16x2(x[0], 0.f) & 0xffffu);
+    }
+  };
+  if (oct) {
+    for (int e8 = tid; e8 < n8; e8 += 256) {
+      const int hl = e8 / (D / 8), d = 8 * (e8 % (D / 8));
+      const int h = h0 + hl;
+      const PT* base = po + (int64_t)h * D + d;
+      float acc[8] = {};
+      for (int s0 = 0; s0 < ns; s0 += 8) {
+        Raw8<PT> raw[8];
+        if (e8 == tid && s0 == 0) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) raw[q] = pre[q];
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) raw[q] = load8<PT>(base + min(s0 + q, ns - 1) * sstride);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          float x[8];
+          widen8<PT>(raw[q], x);
+          const float w = s0 + q < ns ? wsp[(s0 + q) * kCombineHeads + hl] : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+        }
+      }
+      finish(h, d, acc, 8);
+    }
+  } else {
+    // any dim: one element per thread and step; RoPE pairs are formed from both elements
+    for (int e = tid; e < nh * D; e += 256) {
+      const int hl = e / D, d = e % D, h = h0 + hl;
+      const int dp = d >= rope_lo ? rope_lo + ((d - rope_lo) & ~1) : d;   // first of the pair
+      float x0 = 0.f, x1 = 0.f;
+      for (int s = 0; s < ns; ++s) {
+        const float w = wsp[s * kCombineHeads + hl];
+        x0 = fmaf(w, load1<PT>(po + s * sstride + (int64_t)h * D + dp), x0);
+        if (d >= rope_lo) x1 = fmaf(w, load1<PT>(po + s * sstride + (int64_t)h * D + dp + 1), x1);
+      }
+      float y = x0;
+      if (d >= rope_lo) {
+        const int pr = (dp - rope_lo) >> 1;
+        y = d == dp ? x0 * rc[pr] - x1 * rs[pr] : x0 * rs[pr] + x1 * rc[pr];
+      }
+      finish(h, d, &y, 1);
+    }
+  }
+}
+
+// Fewest keys per split of the MFMA kernel: below this the fixed cost of a workgroup (key
+// resolution, pipeline fill, writing its partial) outweighs the parallelism gained.
+constexpr int kMfmaMinChunk = 128;
 
 AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_keys,
                         int32_t q_dtype, int32_t pool_dtype) {
@@ -687,7 +850,7 @@ AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_k
                 (pool_dtype == BF16 || pool_dtype == FP8);
   const int tile = pl.use_mfma ? kKT : kGenTile;
   const int target_blocks = pl.use_mfma ? 256 : 512;
-  const int min_chunk = 64;
+  const int min_chunk = pl.use_mfma ? kMfmaMinChunk : 64;
   int max_split = (max_keys + min_chunk - 1) / min_chunk;
   int ns = n_q > 0 ? (target_blocks + n_q - 1) / n_q : 1;
   ns = ns < 1 ? 1 : ns;
@@ -708,7 +871,9 @@ AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_k
   if (ns < 1) ns = 1;
   pl.n_split = ns;
   pl.chunk = chunk;
-  pl.ws_bytes = (size_t)n_q * ns * ((size_t)dim * n_heads + 2 * (size_t)n_heads) * sizeof(float);
+  const size_t elem = pl.use_mfma ? sizeof(uint16_t) : sizeof(float);
+  pl.o_bytes = ((size_t)n_q * ns * dim * n_heads * elem + 255) / 256 * 256;
+  pl.ws_bytes = pl.o_bytes + (size_t)n_q * ns * 2 * n_heads * sizeof(float);
   return pl;
 }
 
@@ -727,7 +892,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine, dim3((a.dim + kCombineDims - 1) / kCombineDims, a.n_q), dim3(256), 0, s, a);
+  const int hpw = std::max(1, std::min(kCombineHeads, std::min(a.n_heads, kCombineElems / a.dim)));
+  const dim3 cgrid((a.n_heads + hpw - 1) / hpw, a.n_q);
+  if (a.use_mfma)
+    hipLaunchKernelGGL(attn_combine<uint16_t>, cgrid, dim3(256), 0, s, a, hpw);
+  else
+    hipLaunchKernelGGL(attn_combine<float>, cgrid, dim3(256), 0, s, a, hpw);
   return hipGetLastError();
 }
 

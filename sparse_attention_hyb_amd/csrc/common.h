@@ -76,12 +76,23 @@ __device__ __forceinline__ int n_visible(int p, int ratio, int window) {
   return (window_start(p, window) + ratio - 1) / ratio;
 }
 
-// cos / sin of pos * base^(-2i / rope_dim), formed and reduced in double precision.
+// cos / sin of pos * base^(-2i / rope_dim), formed and reduced in double precision. The angle is
+// first brought to [-pi, pi] by subtracting k * 2pi with 2pi split in three parts (24 + 24 + 53
+// bits): for |angle| < 2^31, k < 2^29, so the first two products are exact and the residue keeps
+// full double precision; sincos then stays on its short path instead of a large-argument
+// reduction.
 __device__ __forceinline__ void rope_cs(double pos, int i, int rope_dim, double base, float* c,
                                         float* s) {
-  double theta = exp(-2.0 * (double)i / (double)rope_dim * log(base));
+  const double theta = exp(-2.0 * (double)i / (double)rope_dim * log(base));
+  const double ang = pos * theta;
+  constexpr double kInv2Pi = 0.15915494309189535;
+  constexpr double kP1 = 6.2831854820251465;        // 2pi rounded to 24 bits
+  constexpr double kP2 = -1.7484555314695172e-07;   // next 24 bits
+  constexpr double kP3 = -6.8604979977715316e-15;   // the rest, to double precision
+  const double k = rint(ang * kInv2Pi);
+  const double r = ((ang - k * kP1) - k * kP2) - k * kP3;
   double sn, cs;
-  sincos(pos * theta, &sn, &cs);
+  sincos(r, &sn, &cs);
   *c = (float)cs;
   *s = (float)sn;
 }

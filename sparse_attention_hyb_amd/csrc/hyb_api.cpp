@@ -187,9 +187,8 @@ int attach_workspace(const char* op, AttnCommon* c, void* ws, size_t ws_bytes) {
   if (c->plan.ws_bytes > 0 && (!ws || ws_bytes < c->plan.ws_bytes))
     return fail(HYB_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", op, c->plan.ws_bytes,
                 ws ? ws_bytes : (size_t)0);
-  const size_t n_o = (size_t)c->args.n_q * c->plan.n_split * c->args.dim * c->args.n_heads;
-  c->args.part_o = static_cast<float*>(ws);
-  c->args.part_ml = static_cast<float*>(ws) + n_o;
+  c->args.part_o = ws;
+  c->args.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + c->plan.o_bytes);
   return HYB_OK;
 }
 

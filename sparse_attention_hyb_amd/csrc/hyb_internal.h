@@ -120,8 +120,11 @@ struct AttnArgs {
   int32_t n_split;
   int32_t chunk;      // keys per split
   int32_t use_mfma;
-  float* part_o;      // [n_q][n_split][dim][n_heads]
-  float* part_ml;     // [n_q][n_split][2][n_heads]
+  // Split partials: each split's output normalised by its own softmax sum, [n_q][n_split][n_heads]
+  // [dim], fp32 from the generic kernel and bf16 from the MFMA kernel (whose probabilities are
+  // bf16 already); m (natural-log units) and l per split and head in part_ml [n_q][n_split][2][n_heads].
+  void* part_o;
+  float* part_ml;
 };
 
 // Split plan and workspace size for an attention call; identical for sizing and for launching.
@@ -129,6 +132,7 @@ struct AttnPlan {
   int32_t use_mfma;
   int32_t n_split;
   int32_t chunk;
+  size_t o_bytes;    // part_o bytes, rounded up to 256; part_ml follows
   size_t ws_bytes;
 };
 AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_keys,
