@@ -203,6 +203,177 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
   }
 }
 
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane i's bytes land
+// at LDS byte address lds + 16i. Issued through inline asm: with the compiler builtin every LDS
+// read waits for all outstanding loads (the compiler cannot tell which LDS bytes a load writes),
+// which would serialise the prefetch; here the caller waits with wait_vmcnt for exactly the tiles
+// it reads. Younger loads or stores issued by the compiler only make such a wait stricter.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// bf16 keys: the same contraction as score_mfma, with the keys streamed into LDS by coalesced
+// direct loads (each load instruction moves 1 KB = four whole key rows) instead of row-wise loads
+// into operand registers; row-wise loads reach only about 5 TB/s on this access pattern.
+// Each wave owns four 8 KB stages (32 keys x 256 B) and keeps three tiles in flight. In a stage,
+// 16-byte chunk c of key n sits at chunk c ^ (n % 16) of its row, so the operand reads (32 keys,
+// one logical chunk) hit 16 different bank groups per 16 lanes; the loads pick their source
+// chunks to match.
+constexpr int kDmaStages = 4;
+
+__global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[kDmaStages][4][8192];
+  __shared__ uint32_t lhist[kScoreParts * kTopBins];
+  __shared__ int32_t tbl[kScoreKeysPerBlock / 2 + 2];
+  const int i = blockIdx.y;
+  const int base = blockIdx.x * kScoreKeysPerBlock;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31;
+  const int hf = lane >> 5;
+  // In decode form the sequence is the query index itself, so the block table of the
+  // workgroup's whole key range is read in parallel with the sequence length (which only bounds
+  // the range); in prefill form the sequence comes from q_seq first.
+  const int seq = (a.qd.seq_lens || !a.qd.q_seq) ? i : a.qd.q_seq[i];
+  const int per_block = a.pool.per_block;   // 256 / ratio: a power of two
+  const int pb_shift = __builtin_ctz(per_block);
+  const int lb0 = base >> pb_shift;
+  const int n_lb_max = ((base + kScoreKeysPerBlock - 1) >> pb_shift) - lb0 + 1;
+  for (int j = threadIdx.x; j < n_lb_max; j += 256) {
+    const int lb = lb0 + j;
+    const int phys = lb < a.pool.max_blocks ? a.pool.block_table[(int64_t)seq * a.pool.max_blocks + lb] : -1;
+    tbl[j] = (phys >= 0 && phys < a.pool.num_blocks) ? phys : -1;
+  }
+  const int p = a.qd.seq_lens ? a.qd.seq_lens[i] - 1 : a.qd.q_pos[i];
+  const int nv = min(n_visible(p, a.pool.ratio, a.window), n_visible(a.max_pos, a.pool.ratio, a.window));
+  if (base >= nv) return;   // uniform, before any barrier
+  const int end = min(nv, base + kScoreKeysPerBlock);
+  if (a.part_hist)
+    for (int j = threadIdx.x; j < kScoreParts * kTopBins; j += 256) lhist[j] = 0;
+  __syncthreads();
+
+  // operands as in score_mfma: d = 64*hf + 8*s + e, i.e. lane (key col, hf) takes logical chunk
+  // 8*hf + s of its key at K-step s
+  bf16x8 qa[2][8];
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)i * kMfmaHeads * kMfmaDim;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qa[mb][s] = *reinterpret_cast<const bf16x8*>(q + (32 * mb + col) * kMfmaDim + 64 * hf + 8 * s);
+  float wv[2][16];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      wv[mb][r] = a.w[(int64_t)i * kMfmaHeads + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3)];
+  float* out = a.scores + (int64_t)i * a.ld;
+
+  auto entry_of = [&](int g) -> int64_t {   // entry 0 when the block is absent (scored -inf)
+    g = min(g, end - 1);
+    const int phys = tbl[(g >> pb_shift) - lb0];
+    return phys >= 0 ? ((int64_t)phys << pb_shift) + (g & (per_block - 1)) : 0;
+  };
+  const uint32_t st0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&stage[0][wave][0]);
+  constexpr uint32_t kStageBytes = 4 * 8192;
+  // tile m of this wave: keys base + 32*wave + 128*m + [0, 32)
+  const int first = base + 32 * wave;
+  const int n_mine = first < end ? (end - first + 127) / 128 : 0;
+  // load instruction j: LDS bytes 1024j + 16*lane <- key n = 4j + lane/16, chunk (lane%16) ^ (n%16)
+  auto issue = [&](int s, int m) {
+    const int tb = first + 128 * m;
+    int64_t e[8];
+    if (per_block >= 32) {
+      // uniform: the 32-key tile lies in one block; tiles past the end re-read the last tile's
+      // block (in bounds, unused)
+      const int gb = min(tb, (end - 1) & ~31);
+      const int phys = tbl[(gb >> pb_shift) - lb0];
+      const int64_t e0 = (phys >= 0 ? ((int64_t)phys << pb_shift) : 0) + (gb & (per_block - 1));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = e0 + 4 * j + (lane >> 4);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = entry_of(tb + 4 * j + (lane >> 4));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // earlier reads of this stage are done
+    const uint32_t lds = st0 + s * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = 4 * j + (lane >> 4);
+      const int c = (lane & 15) ^ (n & 15);
+      lds_dma16(a.pool.data + e[j] * a.pool.entry_bytes + 16 * c, lds + 1024 * j);
+    }
+  };
+  // operand read offsets (bytes within a stage): key col, chunk (8hf + s) ^ (col % 16)
+  uint32_t roff[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) roff[s] = wave * 8192 + col * 256 + 16 * ((8 * hf + s) ^ (col & 15));
+  auto score = [&](int st, int m) {
+    const uint8_t* sb = &stage[st][0][0];
+    f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(sb + roff[s]);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], b, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], b, acc1, 0, 0, 0);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      part = fmaf(wv[0][r], fmaxf(acc0[r], 0.f), part);
+      part = fmaf(wv[1][r], fmaxf(acc1[r], 0.f), part);
+    }
+    part += __shfl_xor(part, 32, 64);
+    const int g = first + 128 * m + col;
+    if (hf == 0 && g < end) {
+      const bool valid = tbl[(g >> pb_shift) - lb0] >= 0;
+      const float v = valid ? canonical_zero(part) : -INFINITY;
+      if (a.part_hist) {
+        const uint32_t key = order_key(v);
+        reinterpret_cast<uint32_t*>(out)[g] = key;
+        atomicAdd(&lhist[((g - base) / kScorePartKeys) * kTopBins + (key >> (32 - kTopBits))], 1u);
+      } else {
+        out[g] = v;
+      }
+    }
+  };
+  if (n_mine > 0) {
+    // three tiles in flight; tiles past the wave's last one load clamped (real) rows, unused
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    for (int m = 0; m < n_mine; m += 4) {
+      issue(3, m + 3);
+      wait_vmcnt<24>();
+      score(0, m);
+      if (m + 1 >= n_mine) break;
+      issue(0, m + 4);
+      wait_vmcnt<24>();
+      score(1, m + 1);
+      if (m + 2 >= n_mine) break;
+      issue(1, m + 5);
+      wait_vmcnt<24>();
+      score(2, m + 2);
+      if (m + 3 >= n_mine) break;
+      issue(2, m + 6);
+      wait_vmcnt<24>();
+      score(3, m + 3);
+    }
+  }
+  wait_vmcnt<0>();   // no load may still be writing this workgroup's LDS when it exits
+  if (a.part_hist) {
+#pragma unroll
+    for (int q = 0; q < kScoreParts; ++q)
+      if (base + q * kScorePartKeys < end)   // uniform
+        store_part_hist(a, lhist + q * kTopBins, i, blockIdx.x * kScoreParts + q);
+  }
+}
+
 // One thread per key (workgroups of kScorePartKeys keys, four per thread); query rows and weights
 // staged in LDS as float.
 __global__ __launch_bounds__(256) void score_generic(ScoreArgs a) {
@@ -275,7 +446,7 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s) {
   if (mfma) {
     dim3 grid((max_nv + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock, a.n_q);
     if (a.pool.dtype == BF16)
-      hipLaunchKernelGGL(score_mfma<false>, grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(score_mfma_dma, grid, dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL(score_mfma<true>, grid, dim3(256), 0, s, a);
   } else {
