@@ -169,12 +169,16 @@ int32_t hyb_topk(const float* scores, int64_t scores_ld, const int32_t* lengths,
 /* --------------------------------------------------------------------------------------------
  * hyb_index_score_keys / hyb_topk_keys - the two halves of hyb_index_topk, for callers that want
  * to place them (or time them) separately. Same selection as hyb_index_score + hyb_topk.
- * hyb_index_score_keys writes each score as its order key, a uint32 that sorts like the float
- * (non-negative: bits | 0x80000000; negative: ~bits; -0.0 stored as +0.0), and, for every block
- * of 1024 entries of a row, a histogram of the keys' top 10 bits:
- *   keys       uint32 [n_q][keys_ld], keys_ld >= n_vis(max_pos)
- *   part_hist  uint16 [n_q][part_ld][1024], part_ld >= ceil(n_vis(max_pos) / 1024)
- * Other arguments as in hyb_index_score. hyb_topk_keys selects from them with the same q_pos,
+ * hyb_index_score_keys turns each score into its order key, a uint32 that sorts like the float
+ * (non-negative: bits | 0x80000000; negative: ~bits; -0.0 stored as +0.0), and hands each block
+ * p of 1024 entries of a row over as
+ *   part_hist[p][b]  the number of the block's keys whose top 10 bits are >= b (b < 1024), and
+ *   keys[2048 p ..]  the block's (key, entry index) pairs as uint32 pairs, ordered by the keys'
+ *                    top 10 bits from high to low (order within equal bits unspecified);
+ *   keys       uint32 [n_q][keys_ld], keys_ld >= 2048 * part_ld
+ *   part_hist  uint16 [n_q][part_ld][1024], ceil(n_vis(max_pos) / 1024) <= part_ld <= 4096
+ * so the selector reads only the pairs that can be chosen. Other arguments as in
+ * hyb_index_score. hyb_topk_keys selects from them with the same q_pos,
  * max_pos, window and the pool's ratio (row i holds n_vis(q_pos[i]) entries), as hyb_topk does:
  *   out_idx int32 [n_q][k];  1 <= k <= HYB_KMAX.
  * ------------------------------------------------------------------------------------------ */
@@ -190,9 +194,9 @@ int32_t hyb_topk_keys(const uint32_t* keys, int64_t keys_ld, const uint16_t* par
 /* --------------------------------------------------------------------------------------------
  * hyb_index_topk - hyb_index_score followed by hyb_topk over n_vis(q_pos[i]) entries; the
  * scores live in the workspace (size from hyb_index_topk_workspace_bytes with the same n_q,
- * max_pos, window and ratio) as order keys, next to per-block histograms that the indexer
- * counts for the selector's first radix pass. The workspace needs no initialisation; its
- * contents are undefined after the call.
+ * max_pos, window and ratio) in the hand-off form of hyb_index_score_keys. At most 4096 * 1024
+ * visible entries (HYB_ENOTSUP beyond). The workspace needs no initialisation; its contents are
+ * undefined after the call.
  * ------------------------------------------------------------------------------------------ */
 size_t hyb_index_topk_workspace_bytes(int32_t n_q, int32_t max_pos, int32_t window,
                                       int32_t ratio);

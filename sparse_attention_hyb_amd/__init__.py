@@ -181,11 +181,11 @@ def hyb_topk(scores, lengths, max_len: int, k: int, out_idx, stream=None) -> Non
 
 def index_keys_shapes(n_q: int, max_pos: int, window: int = 128, ratio: int = 4):
     """Shapes of the `keys` (uint32 as int32) and `part_hist` (uint16 as int16) buffers of
-    hyb_index_score_keys / hyb_topk_keys: ([n_q, ld], [n_q, part_ld, 1024])."""
+    hyb_index_score_keys / hyb_topk_keys: ([n_q, 2048 * parts], [n_q, parts, 1024])."""
     ws = max(0, max_pos - window + 1)                  # window start of the last position
     nv = max(1, (ws + ratio - 1) // ratio)             # compressed entries visible to it
-    ld = (nv + 63) // 64 * 64
-    return (n_q, ld), (n_q, (nv + 1023) // 1024, 1024)
+    parts = (nv + 1023) // 1024
+    return (n_q, 2048 * parts), (n_q, parts, 1024)
 
 
 def hyb_index_score_keys(q_idx, w, q_pos, max_pos: int, idx_pool, keys, part_hist, window: int = 128,

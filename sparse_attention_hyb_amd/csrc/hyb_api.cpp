@@ -325,6 +325,8 @@ int32_t hyb_topk(const float* scores, int64_t scores_ld, const int32_t* lengths,
 }
 
 static int64_t part_blocks(int64_t nv) { return (nv + hyb::kScorePartKeys - 1) / hyb::kScorePartKeys; }
+// uint32 words of one row of the selector hand-off: a (key, index) pair per entry, per part
+static int64_t pair_words(int64_t parts) { return 2 * hyb::kScorePartKeys * parts; }
 
 int32_t hyb_index_score_keys(const void* q_idx, int32_t q_dtype, const float* w, const int32_t* q_seq,
                              const int32_t* q_pos, int32_t n_q, int32_t n_heads, int32_t max_pos,
@@ -335,9 +337,12 @@ int32_t hyb_index_score_keys(const void* q_idx, int32_t q_dtype, const float* w,
   HYB_TRY(check_score(op, q_idx, q_dtype, w, q_pos, n_q, n_heads, max_pos, window, idx_pool, &a));
   if (!keys || !part_hist) return fail(HYB_EINVAL, "%s: keys and part_hist must be non-NULL", op);
   const int64_t nv = visible(max_pos, a.pool.ratio, window);
-  if (keys_ld < nv) return fail(HYB_EINVAL, "%s: keys_ld %lld < visible entries %lld", op, (long long)keys_ld, (long long)nv);
-  if (part_ld < part_blocks(nv) || part_ld > INT32_MAX)
-    return fail(HYB_EINVAL, "%s: part_ld %lld outside [%lld, 2^31)", op, (long long)part_ld, (long long)part_blocks(nv));
+  if (part_ld < part_blocks(nv) || part_ld > hyb::kTopkMaxParts)
+    return fail(HYB_EINVAL, "%s: part_ld %lld outside [%lld, %d]", op, (long long)part_ld,
+                (long long)part_blocks(nv), hyb::kTopkMaxParts);
+  if (keys_ld < pair_words(part_ld) || (keys_ld & 1) || (reinterpret_cast<uintptr_t>(keys) & 7))
+    return fail(HYB_EINVAL, "%s: keys needs 8-byte alignment and an even keys_ld >= 2048 * part_ld = %lld (got %lld)",
+                op, (long long)pair_words(part_ld), (long long)keys_ld);
   a.qd = hyb::QueryDev{nullptr, q_seq, q_pos};
   a.scores = reinterpret_cast<float*>(keys);
   a.ld = keys_ld;
@@ -357,9 +362,12 @@ int32_t hyb_topk_keys(const uint32_t* keys, int64_t keys_ld, const uint16_t* par
   if (ratio != 4 && ratio != 128) return fail(HYB_EINVAL, "%s: ratio %d must be 4 or 128", op, ratio);
   if (k < 1 || k > HYB_KMAX) return fail(HYB_EINVAL, "%s: k %d outside [1, %d]", op, k, HYB_KMAX);
   const int64_t nv = visible(max_pos, ratio, window);
-  if (keys_ld < nv) return fail(HYB_EINVAL, "%s: keys_ld %lld < visible entries %lld", op, (long long)keys_ld, (long long)nv);
-  if (part_ld < part_blocks(nv) || part_ld > INT32_MAX)
-    return fail(HYB_EINVAL, "%s: part_ld %lld outside [%lld, 2^31)", op, (long long)part_ld, (long long)part_blocks(nv));
+  if (part_ld < part_blocks(nv) || part_ld > hyb::kTopkMaxParts)
+    return fail(HYB_EINVAL, "%s: part_ld %lld outside [%lld, %d]", op, (long long)part_ld,
+                (long long)part_blocks(nv), hyb::kTopkMaxParts);
+  if (keys_ld < pair_words(part_ld) || (keys_ld & 1) || (reinterpret_cast<uintptr_t>(keys) & 7))
+    return fail(HYB_EINVAL, "%s: keys needs 8-byte alignment and an even keys_ld >= 2048 * part_ld = %lld (got %lld)",
+                op, (long long)pair_words(part_ld), (long long)keys_ld);
   if (n_q == 0) return HYB_OK;
   hyb::TopkArgs t{};
   t.scores = reinterpret_cast<const float*>(keys);
@@ -377,13 +385,14 @@ int32_t hyb_topk_keys(const uint32_t* keys, int64_t keys_ld, const uint16_t* par
   return launch_status(hyb::launch_topk(t, static_cast<hipStream_t>(stream)), op);
 }
 
-// Workspace of hyb_index_topk: order keys [n_q][ld] (uint32), then the indexer's partial
-// histograms [n_q][part_ld][kTopBins] (uint16), part_ld = ld / kScorePartKeys rounded up.
+// Workspace of hyb_index_topk: the selector hand-off, (key, index) pairs [n_q][part_ld *
+// kScorePartKeys] (uint2), then the cumulative histograms [n_q][part_ld][kTopBins] (uint16),
+// part_ld = ld / kScorePartKeys rounded up.
 static size_t topk_part_ld(int64_t ld) {
   return (size_t)((ld + hyb::kScorePartKeys - 1) / hyb::kScorePartKeys);
 }
 static size_t topk_ws_bytes(int32_t n_q, int64_t ld) {
-  return (size_t)n_q * ld * sizeof(uint32_t) +
+  return (size_t)n_q * pair_words((int64_t)topk_part_ld(ld)) * sizeof(uint32_t) +
          (size_t)n_q * topk_part_ld(ld) * hyb::kTopBins * sizeof(uint16_t);
 }
 
@@ -407,16 +416,20 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
                 workspace ? workspace_bytes : (size_t)0);
   if (n_q == 0) return HYB_OK;
   const int64_t ld = (int64_t)score_ld(max_pos, window, a.pool.ratio);
+  if ((int64_t)topk_part_ld(ld) > hyb::kTopkMaxParts)
+    return fail(HYB_ENOTSUP, "%s: %lld visible entries exceed the selector (%d x 1024)", op,
+                (long long)ld, hyb::kTopkMaxParts);
+  const int64_t pld = pair_words((int64_t)topk_part_ld(ld));
   a.qd = hyb::QueryDev{nullptr, q_seq, q_pos};
   a.scores = static_cast<float*>(workspace);
-  a.ld = ld;
-  a.part_hist = reinterpret_cast<uint16_t*>(static_cast<uint32_t*>(workspace) + (size_t)n_q * ld);
+  a.ld = pld;
+  a.part_hist = reinterpret_cast<uint16_t*>(static_cast<uint32_t*>(workspace) + (size_t)n_q * pld);
   a.part_ld = (int32_t)topk_part_ld(ld);
   hipStream_t s = static_cast<hipStream_t>(stream);
   HYB_TRY(launch_status(hyb::launch_index_score(a, s), op));
   hyb::TopkArgs t{};
   t.scores = a.scores;
-  t.ld = ld;
+  t.ld = pld;
   t.lengths = nullptr;
   t.qd = a.qd;
   t.ratio = a.pool.ratio;

@@ -66,9 +66,11 @@ struct ScoreArgs {
   PoolDev pool;
   float* scores;
   int64_t ld;
-  // Optional, for the selector that follows: each workgroup's histogram of the top kTopBits
-  // bits of the order keys of its kScorePartKeys keys, [n_q][part_ld][kTopBins] uint16; the rows
-  // then hold the order keys (uint32 bits) instead of the float scores.
+  // Optional, for the selector that follows (the hand-off): per part of kScorePartKeys keys, the
+  // cumulative histogram of the top kTopBits bits of the order keys, [n_q][part_ld][kTopBins]
+  // uint16 (entry b = the part's keys whose top bits are >= b); `scores` then holds, per row of
+  // ld uint32 words, each part's (order key, index) pairs bucketed by those bits, highest first,
+  // as uint2 at kScorePartKeys * part.
   uint16_t* part_hist;
   int32_t part_ld;
 };
@@ -76,6 +78,7 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s);
 constexpr int kTopBits = 10;                  // the selector's first radix pass (then 11 + 11)
 constexpr int kTopBins = 1 << kTopBits;
 constexpr int kScorePartKeys = 1024;          // keys per partial histogram (one indexer workgroup)
+constexpr int kTopkMaxParts = 4096;           // parts per row the hand-off selector takes
 
 // ---- top-k ----------------------------------------------------------------------------------
 // Row lengths come from `lengths` or, if null, from n_visible(p_i, ratio, window) of the queries.
@@ -90,8 +93,8 @@ struct TopkArgs {
   int32_t max_len;
   int32_t k;
   int32_t* out;
-  // Optional (after the indexer, see ScoreArgs::part_hist): the rows hold order keys and these
-  // partial histograms give the first radix pass.
+  // Optional (after the indexer, see ScoreArgs::part_hist): `scores` is the hand-off of (key,
+  // index) pairs and these cumulative histograms give the first radix pass.
   const uint16_t* part_hist;
   int32_t part_ld;
 };

@@ -12,9 +12,10 @@
 //    keys as N; each lane then owns one key column and 32 of its heads, so the ReLU-weighted head
 //    sum is 32 in-lane FMAs plus one cross-half add.
 //  * score_generic: any (heads x dim) <= 8192, fp32 / bf16 / fp4 - one thread per key.
-// Both can also count, per workgroup of kScorePartKeys keys, a histogram of the top kTopBits bits of
-// the scores' order keys for the selector that follows (then the rows hold the order keys): the first
-// radix pass of the top-k rides along with the score stream.
+// For the selector that follows, all can instead hand over each part of kScorePartKeys keys as a
+// cumulative histogram of the top kTopBits bits of the scores' order keys plus the part's
+// (order key, index) pairs bucketed by those bits (see finish_parts): the first radix pass of the
+// top-k, and the gathering of its candidates, ride along with the score stream.
 #include <type_traits>
 
 #include "common.h"
@@ -41,22 +42,74 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float sc) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Writes a workgroup's LDS histogram (counts <= kScorePartKeys) as its uint16 partial histogram:
-// 256 threads, kTopBins / 256 bins each.
-__device__ __forceinline__ void store_part_hist(const ScoreArgs& a, const uint32_t* lhist, int i,
-                                                int blk) {
+// Selector hand-off (part_hist set). For each part of kScorePartKeys keys a workgroup writes
+//  * its cumulative histogram over the top kTopBits bits of the order keys: part_hist[b] = number
+//    of the part's keys whose top bits are >= b (uint16, <= kScorePartKeys), and
+//  * the part's (order key, row index) pairs bucketed by those bits, highest bin first (order
+//    within a bin unspecified), as uint2 at pairs + kScorePartKeys * part,
+// so that the selector, once it knows the bin b0 of the k-th largest key, reads only the leading
+// part_hist[b0] pairs of every part. The workgroup's keys are in lkeys[0, P * kScorePartKeys)
+// (index g - base) and its per-part counts in lhist[P][kTopBins], which become bucket cursors;
+// lsorted (P * kScorePartKeys uint2) is scratch. 256 threads.
+template <int P>
+__device__ __forceinline__ void finish_parts(const ScoreArgs& a, int i, int part0, int base, int end,
+                                             const uint32_t* lkeys, uint32_t* lhist, uint2* lsorted,
+                                             uint32_t* wtot) {
   static_assert(kTopBins == 4 * 256, "four bins per thread");
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  __syncthreads();   // keys and counts complete
+#pragma unroll
+  for (int q = 0; q < P; ++q) {
+    if (base + q * kScorePartKeys >= end) break;   // uniform
+    uint32_t* h = lhist + q * kTopBins;
+    // thread t owns bins 1023 - 4t - e (e < 4), i.e. bins in descending order across threads
+    uint32_t c[4], tot = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c[e] = h[kTopBins - 1 - 4 * t - e];
+      tot += c[e];
+    }
+    const uint32_t incl = wave_inclusive_scan(tot);
+    if (lane == 63) wtot[q * 4 + w] = incl;
+    __syncthreads();
+    uint32_t before = incl - tot;
+    for (int v = 0; v < w; ++v) before += wtot[q * 4 + v];
+    // cum[b] = keys with top bits >= b; bucket b starts at cum[b] - count[b]
+    uint32_t run = before;
+    uint32_t cum[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[kTopBins - 1 - 4 * t - e] = run;   // cursor: start of the bucket
+      run += c[e];
+      cum[e] = run;
+    }
+    // bins 1020 - 4t .. 1023 - 4t, ascending in memory
+    uint2 wv;
+    wv.x = cum[3] | (cum[2] << 16);
+    wv.y = cum[1] | (cum[0] << 16);
+    *reinterpret_cast<uint2*>(a.part_hist + ((int64_t)i * a.part_ld + part0 + q) * kTopBins +
+                              (kTopBins - 4 - 4 * t)) = wv;
+  }
   __syncthreads();
-  const int t = threadIdx.x;
-  uint2 w;
-  w.x = lhist[4 * t] | (lhist[4 * t + 1] << 16);
-  w.y = lhist[4 * t + 2] | (lhist[4 * t + 3] << 16);
-  *reinterpret_cast<uint2*>(a.part_hist + ((int64_t)i * a.part_ld + blk) * kTopBins + 4 * t) = w;
+  const int nk = min(P * kScorePartKeys, end - base);
+  for (int j = t; j < nk; j += 256) {
+    const uint32_t key = lkeys[j];
+    const int q = j / kScorePartKeys;
+    const uint32_t slot = atomicAdd(&lhist[q * kTopBins + (key >> (32 - kTopBits))], 1u);
+    lsorted[q * kScorePartKeys + slot] = make_uint2(key, (uint32_t)(base + j));
+  }
+  __syncthreads();
+  uint2* pairs = reinterpret_cast<uint2*>(a.scores) + (int64_t)i * (a.ld / 2) +
+                 (int64_t)part0 * kScorePartKeys;
+  for (int j = t; j < nk; j += 256) pairs[j] = lsorted[j];
 }
 
 template <bool kFp4>
 __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
   __shared__ uint32_t lhist[kScoreParts * kTopBins];   // one histogram per kScorePartKeys keys
+  __shared__ uint32_t lkeys[kScoreKeysPerBlock];
+  __shared__ uint2 lsorted[kScoreKeysPerBlock];
+  __shared__ uint32_t wtot[kScoreParts * 4];
   // physical blocks of this workgroup's keys (at least 2 entries per block: ratio <= 128)
   __shared__ int32_t tbl[kScoreKeysPerBlock / 2 + 2];
   const int i = blockIdx.y;
@@ -171,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
       const float v = kb.valid ? canonical_zero(part) : -INFINITY;
       if (a.part_hist) {
         const uint32_t key = order_key(v);
-        reinterpret_cast<uint32_t*>(out)[g] = key;
+        lkeys[g - base] = key;
         atomicAdd(&lhist[((g - base) / kScorePartKeys) * kTopBins + (key >> (32 - kTopBits))], 1u);
       } else {
         out[g] = v;
@@ -195,12 +248,8 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
       score(k2, t0 + 256);
     }
   }
-  if (a.part_hist) {
-#pragma unroll
-    for (int q = 0; q < kScoreParts; ++q)
-      if (base + q * kScorePartKeys < end)   // uniform
-        store_part_hist(a, lhist + q * kTopBins, i, blockIdx.x * kScoreParts + q);
-  }
+  if (a.part_hist)
+    finish_parts<kScoreParts>(a, i, blockIdx.x * kScoreParts, base, end, lkeys, lhist, lsorted, wtot);
 }
 
 // Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane i's bytes land
@@ -230,6 +279,8 @@ __global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage[kDmaStages][4][8192];
   __shared__ uint32_t lhist[kScoreParts * kTopBins];
   __shared__ int32_t tbl[kScoreKeysPerBlock / 2 + 2];
+  __shared__ uint32_t lkeys[kScoreKeysPerBlock];
+  __shared__ uint32_t wtot[kScoreParts * 4];
   const int i = blockIdx.y;
   const int base = blockIdx.x * kScoreKeysPerBlock;
   const int lane = threadIdx.x & 63;
@@ -335,7 +386,7 @@ __global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
       const float v = valid ? canonical_zero(part) : -INFINITY;
       if (a.part_hist) {
         const uint32_t key = order_key(v);
-        reinterpret_cast<uint32_t*>(out)[g] = key;
+        lkeys[g - base] = key;
         atomicAdd(&lhist[((g - base) / kScorePartKeys) * kTopBins + (key >> (32 - kTopBits))], 1u);
       } else {
         out[g] = v;
@@ -366,12 +417,9 @@ __global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
     }
   }
   wait_vmcnt<0>();   // no load may still be writing this workgroup's LDS when it exits
-  if (a.part_hist) {
-#pragma unroll
-    for (int q = 0; q < kScoreParts; ++q)
-      if (base + q * kScorePartKeys < end)   // uniform
-        store_part_hist(a, lhist + q * kTopBins, i, blockIdx.x * kScoreParts + q);
-  }
+  if (a.part_hist)   // the stages are free now: the sorted pairs use them
+    finish_parts<kScoreParts>(a, i, blockIdx.x * kScoreParts, base, end, lkeys, lhist,
+                              reinterpret_cast<uint2*>(&stage[0][0][0]), wtot);
 }
 
 // One thread per key (workgroups of kScorePartKeys keys, four per thread); query rows and weights
@@ -379,6 +427,9 @@ __global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
 __global__ __launch_bounds__(256) void score_generic(ScoreArgs a) {
   extern __shared__ float sm[];
   __shared__ uint32_t lhist[kTopBins];
+  __shared__ uint32_t lkeys[kScorePartKeys];
+  __shared__ uint2 lsorted[kScorePartKeys];
+  __shared__ uint32_t wtot[4];
   const int i = blockIdx.y;
   int seq, p;
   query_at(a.qd, i, &seq, &p);
@@ -427,13 +478,14 @@ __global__ __launch_bounds__(256) void score_generic(ScoreArgs a) {
     }
     if (a.part_hist) {
       const uint32_t key = order_key(v);
-      reinterpret_cast<uint32_t*>(a.scores)[(int64_t)i * a.ld + g] = key;
+      lkeys[g - base] = key;
       atomicAdd(&lhist[key >> (32 - kTopBits)], 1u);
     } else {
       a.scores[(int64_t)i * a.ld + g] = v;
     }
   }
-  if (a.part_hist) store_part_hist(a, lhist, i, blockIdx.x);
+  if (a.part_hist)
+    finish_parts<1>(a, i, blockIdx.x, base, min(nv, base + kScorePartKeys), lkeys, lhist, lsorted, wtot);
 }
 
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s) {

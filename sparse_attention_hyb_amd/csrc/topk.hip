@@ -20,6 +20,8 @@
 
 namespace hyb {
 
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 
@@ -420,19 +422,452 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Single-chunk rows (n <= kChunk): thread t owns the elements 4t + 4096q + e (q < 8, e < 4), i.e.
+// the row is read with one coalesced 16-byte load per q and never redistributed. The row and the
+// first-pass partials are requested before the row length is known (addresses are clamped into
+// the row's ld and the partials' part_ld; the length only masks). The other two passes visit
+// each thread's few elements that match the prefix so far. The output order comes from two
+// 32768-bit maps (keys > T, keys == T): thread t takes word t of both, and one workgroup scan of
+// the packed counts gives every chosen index its slot, lowest-index ties first.
+// ------------------------------------------------------------------------------------------
+constexpr int kShortUnion = kTopkWaves * kTopWords;   // per-wave first-pass histograms
+constexpr int kMapWords = kChunk / 32;
+constexpr size_t kShortLds = sizeof(uint32_t) * ((size_t)kShortUnion + kHistWords + 2 * kMapWords);
+
+__global__ __launch_bounds__(kTopkThreads) void topk_short(TopkArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t ts_lds[];
+  uint32_t* uni = ts_lds;                 // per-wave first-pass histograms
+  uint32_t* hist = ts_lds + kShortUnion;
+  uint32_t* gtmap = hist + kHistWords;
+  uint32_t* tiemap = gtmap + kMapWords;
+  __shared__ uint32_t wave_tot[kTopkWaves];
+  __shared__ uint32_t sel_res[2];
+
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int k = a.k;
+  const float* sc = a.scores + (int64_t)i * a.ld;
+  const bool keys_in = a.part_hist != nullptr;
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(sc) & 15u) == 0) && (a.ld & 3) == 0 && a.ld >= 4;
+  const int64_t ld_last = a.ld - 1;
+
+  // ---- loads, before the row length arrives
+  f32x4 raw[kPer / 4];
+  if (vec_ok) {
+    const int vec_last = (int)min<int64_t>(a.ld - 4, INT32_MAX - 4);
+#pragma unroll
+    for (int q = 0; q < kPer / 4; ++q)
+      raw[q] = *reinterpret_cast<const f32x4*>(sc + min(4 * tid + kTopkThreads * 4 * q, vec_last));
+  } else {
+#pragma unroll
+    for (int q = 0; q < kPer / 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        raw[q][e] = sc[min<int64_t>(4 * tid + kTopkThreads * 4 * q + e, ld_last)];
+  }
+  constexpr int kPartWords = kTopBins / 2;
+  constexpr int kPartGroups = kTopkThreads / kPartWords;            // 2
+  constexpr int kPartLoads = (kChunk / kScorePartKeys) / kPartGroups;   // 16 per thread
+  const int pwd = tid % kPartWords, pg = tid / kPartWords;
+  uint32_t pw[kPartLoads];
+  if (keys_in) {
+    const uint32_t* ph = reinterpret_cast<const uint32_t*>(a.part_hist + (int64_t)i * a.part_ld * kTopBins) + pwd;
+#pragma unroll
+    for (int q = 0; q < kPartLoads; ++q)
+      pw[q] = ph[(int64_t)min(pg + kPartGroups * q, a.part_ld - 1) * kPartWords];
+  }
+  for (int j = tid; j < kHistWords; j += kTopkThreads) hist[j] = 0;
+
+  const int n = topk_row_len(a, i);
+  int* out = a.out + (int64_t)i * k;
+  if (n <= k) {   // uniform
+    for (int j = tid; j < k; j += kTopkThreads) out[j] = j < n ? j : -1;
+    return;
+  }
+  // element 4q + e of this thread is row index 4 tid + 4096 q + e
+  uint32_t u[kPer];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int q = 0; q < kPer / 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * tid + kTopkThreads * 4 * q + e;
+      const uint32_t key = keys_in ? __float_as_uint(raw[q][e]) : order_key(raw[q][e]);
+      u[4 * q + e] = j < n ? key : 0u;
+      valid |= (uint32_t)(j < n) << (4 * q + e);
+    }
+  auto index_of = [&](int e) { return 4 * tid + kTopkThreads * 4 * (e >> 2) + (e & 3); };
+
+  // ---- first pass (top kTopBits bits)
+  if (keys_in) {
+    const int nb = (n + kScorePartKeys - 1) / kScorePartKeys;
+    uint32_t h0 = 0, h1 = 0;
+#pragma unroll
+    for (int q = 0; q < kPartLoads; ++q) {
+      const uint32_t on = pg + kPartGroups * q < nb ? 0xffffffffu : 0u;
+      h0 += pw[q] & 0xffffu & on;
+      h1 += (pw[q] >> 16) & on;
+    }
+    __syncthreads();   // histogram cleared
+    atomicAdd(&hist[hp(2 * pwd)], h0);
+    atomicAdd(&hist[hp(2 * pwd + 1)], h1);
+    __syncthreads();
+  } else {
+    // per-wave histograms (the busiest bins would otherwise serialise the atomics of all waves)
+    uint32_t* h = uni + wave * kTopWords;
+    for (int j = lane; j < kTopWords; j += 64) h[j] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if ((valid >> e) & 1u) atomicAdd(&h[hp(u[e] >> kShift0)], 1u);
+    __syncthreads();
+    const int j = hp(tid);   // kTopBins == kTopkThreads: one bin per thread
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) t += uni[w * kTopWords + j];
+    hist[j] = t;
+    __syncthreads();   // also: every read of the per-wave histograms precedes the short list
+  }
+  uint32_t b0, above0;
+  select_bin(hist, kTopBins, (uint32_t)k, sel_res, &b0, &above0);
+  uint32_t prefix = b0 << kShift0, pmask = ~0u << kShift0;
+  uint32_t remaining = (uint32_t)k - above0;
+
+  // ---- second and third passes (11 bits each) over the keys matching the prefix; after the
+  // first pass they are few, so each thread visits only its matching elements
+#pragma unroll 1
+  for (int shift = kBits12; shift >= 0; shift -= kBits12) {
+    for (int j = tid; j < kHistWords; j += kTopkThreads) hist[j] = 0;
+    __syncthreads();
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) m |= (uint32_t)((u[e] & pmask) == prefix) << e;
+    m &= valid;
+    while (m) {
+      const int e = __builtin_ctz(m);
+      m &= m - 1;
+      uint32_t ue = 0;
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) ue = q == e ? u[q] : ue;
+      atomicAdd(&hist[hp((ue >> shift) & 2047u)], 1u);
+    }
+    __syncthreads();
+    uint32_t b, ab;
+    select_bin(hist, 2048, remaining, sel_res, &b, &ab);
+    prefix |= b << shift;
+    pmask |= 2047u << shift;
+    remaining -= ab;
+  }
+  const uint32_t T = prefix;   // the k-th largest key; `remaining` keys equal to it are taken
+
+  // ---- index maps of the keys > T and == T. Element 4q + e of thread t is index
+  // 4t + 4096q + e: map word t/8 + 128q, bits 4(t%8) + e. The eight threads of a word (consecutive
+  // lanes) OR their nibbles together with row shifts, and the first of them stores the word.
+  {
+    uint32_t gtm = 0, tiem = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      gtm |= (uint32_t)(u[e] > T) << e;
+      tiem |= (uint32_t)(u[e] == T) << e;
+    }
+    gtm &= valid;
+    tiem &= valid;
+    const int sh = 4 * (tid & 7);
+#pragma unroll
+    for (int q = 0; q < kPer / 4; ++q) {
+      uint32_t g = ((gtm >> (4 * q)) & 15u) << sh;
+      uint32_t t = ((tiem >> (4 * q)) & 15u) << sh;
+      // OR over lanes l..l+7 into lane l (l % 8 == 0): row_shl 1, 2, 4 (lanes past the row end
+      // contribute 0; only the group's first lane is used)
+      g |= __builtin_amdgcn_update_dpp(0u, g, 0x101, 0xf, 0xf, false);
+      t |= __builtin_amdgcn_update_dpp(0u, t, 0x101, 0xf, 0xf, false);
+      g |= __builtin_amdgcn_update_dpp(0u, g, 0x102, 0xf, 0xf, false);
+      t |= __builtin_amdgcn_update_dpp(0u, t, 0x102, 0xf, 0xf, false);
+      g |= __builtin_amdgcn_update_dpp(0u, g, 0x104, 0xf, 0xf, false);
+      t |= __builtin_amdgcn_update_dpp(0u, t, 0x104, 0xf, 0xf, false);
+      if ((tid & 7) == 0) {
+        gtmap[(tid >> 3) + 128 * q] = g;
+        tiemap[(tid >> 3) + 128 * q] = t;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t gtw = gtmap[tid], tiew = tiemap[tid];
+  const uint32_t gt = __builtin_popcount(gtw), tie = __builtin_popcount(tiew);
+  // counts <= 32768 in total: both fit 16 bits of one word
+  const uint32_t pre = block_exclusive_scan((tie << 16) | gt, wave_tot, nullptr);
+  // signed clamps (ties still to take when this word begins may be negative)
+  const int32_t left = (int32_t)remaining - (int32_t)(pre >> 16);
+  const int32_t take = max(0, min(left, (int32_t)tie));
+  uint32_t keep = 0, tm = tiew;
+  for (int32_t t = 0; t < take; ++t) {
+    keep |= tm & (0u - tm);
+    tm &= tm - 1;
+  }
+  uint32_t sel = gtw | keep;
+  uint32_t pos = (pre & 0xffffu) + (uint32_t)((int32_t)remaining - max(left, 0));
+  while (sel) {
+    const int b = __builtin_ctz(sel);
+    sel &= sel - 1;
+    if (pos < (uint32_t)k) out[pos] = 32 * tid + b;
+    ++pos;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Selection from the indexer's hand-off (TopkArgs::part_hist set): per part of kScorePartKeys
+// keys, a cumulative histogram of the top kTopBits key bits (cum_p[b] = keys with top bits >= b)
+// and the part's (key, index) pairs bucketed by those bits, highest bin first. One workgroup per
+// row:
+//   1. C[b] = sum_p cum_p[b]; the first-pass bin b0 is the one with C[b0] >= k > C[b0 + 1].
+//   2. The candidates are the keys with top bits >= b0: the leading cum_p[b0] pairs of every
+//      part. They are gathered into LDS (a few per thread); the first 64 pairs of the first 32
+//      parts are requested together with the counts, before b0 is known, so the usual row costs
+//      one global round trip.
+//   3. Two 11-bit passes over the candidates whose top bits equal b0 find the k-th largest key T
+//      and how many keys equal to T are taken (the lowest-indexed ones).
+//   4. Output in ascending index order, 32768 indices at a time: bit maps of the chosen keys > T
+//      and of the keys == T (word w = indices 32w..32w+31, one word per thread), one workgroup
+//      scan of the packed counts, ties taken lowest index first.
+// When the candidates exceed the LDS list (degenerate score distributions) they are read from
+// the hand-off buffer in every step instead.
+// ------------------------------------------------------------------------------------------
+constexpr int kPairCap = 8192;         // candidates held in LDS
+constexpr int kPairMaxParts = kTopkMaxParts;   // parts per row (rows of up to 4M entries)
+constexpr int kPairLdsWords = kTopBins + kHistWords + 2 * (kPairMaxParts + 1) + 2 * kPairCap +
+                              2 * kMapWords;
+constexpr size_t kPairLds = sizeof(uint32_t) * (size_t)kPairLdsWords;
+
+__global__ __launch_bounds__(kTopkThreads) void topk_pairs(TopkArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t tp_lds[];
+  uint32_t* C = tp_lds;                         // [kTopBins] global cumulative counts
+  uint32_t* hist = C + kTopBins;                // [kHistWords] padded 2048-bin histogram
+  uint32_t* cnt = hist + kHistWords;            // [kPairMaxParts + 1] candidates per part
+  uint32_t* off = cnt + kPairMaxParts + 1;      // [kPairMaxParts + 1] their offsets
+  uint32_t* lkey = off + kPairMaxParts + 1;     // [kPairCap]
+  uint32_t* lidx = lkey + kPairCap;             // [kPairCap]
+  uint32_t* gtmap = lidx + kPairCap;            // [kMapWords]
+  uint32_t* tiemap = gtmap + kMapWords;         // [kMapWords]
+  __shared__ uint32_t wave_tot[kTopkWaves];
+  __shared__ uint32_t sel_res[2];
+
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int k = a.k;
+  // first 32 parts' cumulative counts, before the row length is known (clamped to part_ld)
+  constexpr int kPartWords = kTopBins / 2;
+  constexpr int kPartGroups = kTopkThreads / kPartWords;            // 2
+  constexpr int kPartLoads = 16;                                     // parts pg + 2q, q < 16
+  const int pwd = tid % kPartWords, pg = tid / kPartWords;
+  const uint32_t* ph = reinterpret_cast<const uint32_t*>(a.part_hist + (int64_t)i * a.part_ld * kTopBins);
+  uint32_t pw[kPartLoads];
+#pragma unroll
+  for (int q = 0; q < kPartLoads; ++q)
+    pw[q] = ph[(int64_t)min(pg + kPartGroups * q, a.part_ld - 1) * kPartWords + pwd];
+  const uint2* pairs = reinterpret_cast<const uint2*>(a.scores) + (int64_t)i * (a.ld / 2);
+  // (ext-vector pairs: a register array of HIP's union-based uint2 would stay in scratch)
+  const int ep = tid >> 5, el = tid & 31;   // early part, lane: pairs el and el + 32
+  u32x2 pre[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    pre[j] = *reinterpret_cast<const u32x2*>(pairs + (int64_t)min(ep, a.part_ld - 1) * kScorePartKeys + el + 32 * j);
+  C[tid] = 0;
+  const int n = topk_row_len(a, i);
+  int* out = a.out + (int64_t)i * k;
+  if (n <= k) {   // uniform
+    for (int j = tid; j < k; j += kTopkThreads) out[j] = j < n ? j : -1;
+    return;
+  }
+  const int nb = (n + kScorePartKeys - 1) / kScorePartKeys;   // <= kPairMaxParts (host check)
+
+  // ---- 1. global cumulative histogram and b0
+  uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+  for (int q = 0; q < kPartLoads; ++q) {
+    const uint32_t on = pg + kPartGroups * q < nb ? 0xffffffffu : 0u;
+    c0 += pw[q] & 0xffffu & on;
+    c1 += (pw[q] >> 16) & on;
+  }
+  for (int p = pg + kPartGroups * kPartLoads; p < nb; p += kPartGroups) {   // rows past 32 parts
+    const uint32_t w = ph[(int64_t)p * kPartWords + pwd];
+    c0 += w & 0xffffu;
+    c1 += w >> 16;
+  }
+  __syncthreads();   // C cleared
+  atomicAdd(&C[2 * pwd], c0);
+  atomicAdd(&C[2 * pwd + 1], c1);
+  __syncthreads();
+  {
+    // C is non-increasing in b and C[0] = n > k: exactly one bin satisfies this
+    const uint32_t here = C[tid], next = tid + 1 < kTopBins ? C[tid + 1] : 0u;
+    if (here >= (uint32_t)k && next < (uint32_t)k) {
+      sel_res[0] = (uint32_t)tid;
+      sel_res[1] = next;
+    }
+  }
+  __syncthreads();
+  const uint32_t b0 = sel_res[0], above0 = sel_res[1];
+
+  // ---- 2. candidates per part: cum_p[b0]
+  if (pwd == (int)(b0 >> 1)) {
+#pragma unroll
+    for (int q = 0; q < kPartLoads; ++q) {
+      const int p = pg + kPartGroups * q;
+      if (p < nb) cnt[p] = (b0 & 1u) ? (pw[q] >> 16) : (pw[q] & 0xffffu);
+    }
+  }
+  for (int p = kPartGroups * kPartLoads + tid; p < nb; p += kTopkThreads)
+    cnt[p] = a.part_hist[((int64_t)i * a.part_ld + p) * kTopBins + b0];
+  for (int j = tid; j < 2 * kMapWords; j += kTopkThreads) gtmap[j] = 0;
+  __syncthreads();
+  // exclusive scan of the counts over parts (four parts per thread)
+  {
+    uint32_t v[4], s = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p = 4 * tid + e;
+      v[e] = p < nb ? cnt[p] : 0u;
+      s += v[e];
+    }
+    uint32_t total = 0;
+    uint32_t run = block_exclusive_scan(s, wave_tot, &total);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p = 4 * tid + e;
+      if (p < nb) off[p] = run;
+      run += v[e];
+    }
+    if (tid == 0) off[nb] = total;
+  }
+  __syncthreads();
+  const uint32_t M = off[nb];
+  const bool in_lds = M <= (uint32_t)kPairCap;   // uniform
+  // candidate m: part p with off[p] <= m < off[p + 1], position m - off[p]
+  auto fetch = [&](uint32_t m) -> uint2 {
+    int lo = 0, hi = nb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= m) lo = mid; else hi = mid - 1;
+    }
+    return pairs[(int64_t)lo * kScorePartKeys + (m - off[lo])];
+  };
+  if (in_lds) {
+    if (ep < nb) {
+      const uint32_t cp = cnt[ep], op = off[ep];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t pos = el + 32 * j;
+        if (pos < cp) {
+          lkey[op + pos] = pre[j][0];
+          lidx[op + pos] = pre[j][1];
+        }
+      }
+      for (uint32_t pos = 64 + el; pos < cp; pos += 32) {   // long early parts
+        const uint2 pr = pairs[(int64_t)ep * kScorePartKeys + pos];
+        lkey[op + pos] = pr.x;
+        lidx[op + pos] = pr.y;
+      }
+    }
+    if (nb > 32) {
+      for (uint32_t m = off[32] + tid; m < M; m += kTopkThreads) {
+        const uint2 pr = fetch(m);
+        lkey[m] = pr.x;
+        lidx[m] = pr.y;
+      }
+    }
+    __syncthreads();
+  }
+  auto cand = [&](uint32_t m) -> uint2 { return in_lds ? make_uint2(lkey[m], lidx[m]) : fetch(m); };
+
+  // ---- 3. passes over the candidates of bin b0
+  uint32_t prefix = b0 << kShift0, pmask = ~0u << kShift0;
+  uint32_t remaining = (uint32_t)k - above0;
+#pragma unroll 1
+  for (int shift = kBits12; shift >= 0; shift -= kBits12) {
+    for (int j = tid; j < kHistWords; j += kTopkThreads) hist[j] = 0;
+    __syncthreads();
+    for (uint32_t m = tid; m < M; m += kTopkThreads) {
+      const uint32_t key = cand(m).x;
+      if ((key & pmask) == prefix) atomicAdd(&hist[hp((key >> shift) & 2047u)], 1u);
+    }
+    __syncthreads();
+    uint32_t b, ab;
+    select_bin(hist, 2048, remaining, sel_res, &b, &ab);
+    prefix |= b << shift;
+    pmask |= 2047u << shift;
+    remaining -= ab;
+  }
+  const uint32_t T = prefix;   // the k-th largest key; `remaining` keys equal to it are taken
+
+  // ---- 4. output, 32768 indices at a time
+  uint32_t gt_base = 0, tie_base = 0;
+  const int n_chunks = (n + kChunk - 1) / kChunk;
+#pragma unroll 1
+  for (int c = 0; c < n_chunks; ++c) {
+    const uint32_t lo = (uint32_t)c * kChunk;
+    if (c > 0) {
+      __syncthreads();   // the previous chunk's maps are read
+      for (int j = tid; j < 2 * kMapWords; j += kTopkThreads) gtmap[j] = 0;
+      __syncthreads();
+    }
+    for (uint32_t m = tid; m < M; m += kTopkThreads) {
+      const uint2 pr = cand(m);
+      const uint32_t j = pr.y - lo;
+      if (j < (uint32_t)kChunk) {
+        if (pr.x > T) atomicOr(&gtmap[j >> 5], 1u << (j & 31));
+        else if (pr.x == T) atomicOr(&tiemap[j >> 5], 1u << (j & 31));
+      }
+    }
+    __syncthreads();
+    const uint32_t gtw = gtmap[tid], tiew = tiemap[tid];
+    const uint32_t gt = __builtin_popcount(gtw), tie = __builtin_popcount(tiew);
+    uint32_t tot = 0;
+    // per-chunk counts <= 32768: both fit 16 bits of one word
+    const uint32_t pre = block_exclusive_scan((tie << 16) | gt, wave_tot, &tot);
+    const uint32_t gt_pre = gt_base + (pre & 0xffffu);
+    const uint32_t tie_pre = tie_base + (pre >> 16);
+    // signed clamps (ties still to take when this word begins may be negative)
+    const int32_t left = (int32_t)remaining - (int32_t)tie_pre;
+    const int32_t take = max(0, min(left, (int32_t)tie));
+    uint32_t keep = 0, tm = tiew;
+    for (int32_t t = 0; t < take; ++t) {
+      keep |= tm & (0u - tm);
+      tm &= tm - 1;
+    }
+    uint32_t sel = gtw | keep;
+    uint32_t pos = gt_pre + (uint32_t)((int32_t)remaining - max(left, 0));
+    while (sel) {
+      const int b = __builtin_ctz(sel);
+      sel &= sel - 1;
+      if (pos < (uint32_t)k) out[pos] = (int)(lo + 32 * tid + b);
+      ++pos;
+    }
+    gt_base += tot & 0xffffu;
+    tie_base += tot >> 16;
+  }
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.n_q == 0) return hipSuccess;
   static bool attr_set = false;   // the dynamic LDS above 64 KiB must be enabled once per kernel
   if (!attr_set) {
-    for (const void* f : {reinterpret_cast<const void*>(topk_kernel<false>),
-                          reinterpret_cast<const void*>(topk_kernel<true>)}) {
-      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTopkLds);
-      if (e != hipSuccess) return e;
-    }
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTopkLds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_short),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kShortLds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_pairs),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPairLds);
+    if (e != hipSuccess) return e;
     attr_set = true;
   }
-  if (a.max_len <= kChunk)
-    hipLaunchKernelGGL(topk_kernel<false>, dim3(a.n_q), dim3(kTopkThreads), kTopkLds, s, a);
+  if (a.part_hist)
+    hipLaunchKernelGGL(topk_pairs, dim3(a.n_q), dim3(kTopkThreads), kPairLds, s, a);
+  else if (a.max_len <= kChunk)
+    hipLaunchKernelGGL(topk_short, dim3(a.n_q), dim3(kTopkThreads), kShortLds, s, a);
   else
     hipLaunchKernelGGL(topk_kernel<true>, dim3(a.n_q), dim3(kTopkThreads), kTopkLds, s, a);
   return hipGetLastError();

@@ -147,9 +147,9 @@ def test_index_validation(lib):
     assert call(p=pool(ratio=4, dim=100, dtype=hyb.FP4_E2M1)) == hyb.HYB_EINVAL
     assert call(p=pool(ratio=4, dim=128, dtype=hyb.FP8_E4M3)) == hyb.HYB_ENOTSUP
     assert call(heads=128, p=pool(ratio=4, dim=128, dtype=hyb.F32)) == hyb.HYB_ENOTSUP
-    # order keys [16][32768] uint32, then the indexer's partial histograms [16][32][1024] uint16
+    # hand-off pairs [16][32 x 1024] uint2, then the cumulative histograms [16][32][1024] uint16
     assert lib.hyb_index_topk_workspace_bytes(16, 131071, 128, 4) == \
-        16 * 32768 * 4 + 16 * 32 * 1024 * 2
+        16 * 32 * 1024 * 8 + 16 * 32 * 1024 * 2
     assert lib.hyb_topk(FAKE, 10, FAKE, 4, 20, 8, FAKE, None) == hyb.HYB_EINVAL   # ld < max_len
     assert lib.hyb_topk(FAKE, 20, FAKE, 4, 20, 0, FAKE, None) == hyb.HYB_EINVAL   # k = 0
     assert lib.hyb_topk(None, 20, FAKE, 4, 20, 8, FAKE, None) == hyb.HYB_EINVAL
@@ -160,18 +160,20 @@ def test_index_validation(lib):
 def test_index_keys_validation(lib):
     ip = pool(ratio=4, dim=128)
 
-    def score(keys=FAKE, ld=32768, hist=FAKE, pld=32, p=ip):
+    def score(keys=FAKE, ld=65536, hist=FAKE, pld=32, p=ip):
         return lib.hyb_index_score_keys(FAKE, hyb.BF16, FAKE, None, FAKE, 16, 64, 131071, 128,
                                         ctypes.byref(p), keys, ld, hist, pld, None)
 
-    def topk(keys=FAKE, ld=32768, hist=FAKE, pld=32, ratio=4, k=512, q_pos=FAKE):
+    def topk(keys=FAKE, ld=65536, hist=FAKE, pld=32, ratio=4, k=512, q_pos=FAKE):
         return lib.hyb_topk_keys(keys, ld, hist, pld, q_pos, 16, 131071, 128, ratio, k, FAKE, None)
 
     # 131071 - 127 = 130944 -> 32736 visible C4 entries -> 32 blocks of 1024
     assert score(keys=None) == hyb.HYB_EINVAL
     assert score(hist=None) == hyb.HYB_EINVAL
-    assert score(ld=32735) == hyb.HYB_EINVAL
+    assert score(ld=65535) == hyb.HYB_EINVAL   # below 2048 x part_ld
+    assert score(ld=65537 + 2048) == hyb.HYB_EINVAL   # odd
     assert score(pld=31) == hyb.HYB_EINVAL
+    assert score(pld=4097, ld=2048 * 4097) == hyb.HYB_EINVAL   # beyond the selector's parts
     assert score(p=pool(ratio=1, dim=128)) == hyb.HYB_EINVAL
     assert topk(keys=None) == hyb.HYB_EINVAL
     assert topk(q_pos=None) == hyb.HYB_EINVAL
@@ -180,4 +182,4 @@ def test_index_keys_validation(lib):
     assert topk(ratio=8) == hyb.HYB_EINVAL
     assert topk(k=0) == hyb.HYB_EINVAL
     assert lib.hyb_last_error().decode().startswith("hyb_topk_keys")
-    assert hyb.index_keys_shapes(16, 131071) == ((16, 32768), (16, 32, 1024))
+    assert hyb.index_keys_shapes(16, 131071) == ((16, 65536), (16, 32, 1024))

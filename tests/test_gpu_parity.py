@@ -244,9 +244,10 @@ def test_exact_arithmetic_topk_is_bit_exact(gpu_lib):
 
 
 def test_index_keys_halves_match_fused(gpu_lib):
-    """hyb_index_score_keys + hyb_topk_keys select exactly what hyb_index_topk selects; the stored
-    keys are the order keys of hyb_index_score's floats and the per-block histograms count the top
-    10 bits of every entry once (bit-exact)."""
+    """hyb_index_score_keys + hyb_topk_keys select exactly what hyb_index_topk selects. The hand-off
+    holds, per block of 1024 entries, every entry once as (order key of hyb_index_score's float,
+    index), ordered by the keys' top 10 bits from high to low, and a cumulative count of those
+    bits (bit-exact)."""
     hyb = gpu_lib
     wl = W.sparse_decode(DEV, seed=5, batch=4, ctx=[3000, 20000, 70001, 131072])
     qpos = wl.seq_lens - 1
@@ -258,7 +259,7 @@ def test_index_keys_halves_match_fused(gpu_lib):
     out = torch.full((wl.batch, wl.k), -7, dtype=I32, device=DEV)
     hyb.hyb_topk_keys(keys, hist, qpos, mp, wl.k, out)
     fused = gpu_topk(hyb, wl)
-    scores = torch.zeros(kshape, device=DEV)
+    scores = torch.zeros((wl.batch, kshape[1] // 2), device=DEV)
     hyb.hyb_index_score(wl.idx_q, wl.idx_w, qpos, mp, wl.idx_pool, scores)
     sync()
     assert torch.equal(out, fused)
@@ -267,13 +268,19 @@ def test_index_keys_halves_match_fused(gpu_lib):
         f = scores[b, :nv].cpu().numpy().view(np.uint32).astype(np.uint64)
         f = np.where(f == 0x80000000, 0, f)
         want = np.where(f & 0x80000000, (~f) & 0xFFFFFFFF, f | 0x80000000).astype(np.uint32)
-        got = keys[b, :nv].cpu().numpy().view(np.uint32)
-        assert np.array_equal(got, want)
+        row = keys[b].cpu().numpy().view(np.uint32)
         nb = (nv + 1023) // 1024
         h = hist[b, :nb].cpu().numpy().view(np.uint16).astype(np.int64)
         for blk in range(nb):
-            part = got[blk * 1024:(blk + 1) * 1024] >> 22
-            assert np.array_equal(np.bincount(part.astype(np.int64), minlength=1024), h[blk])
+            cnt = min(1024, nv - 1024 * blk)
+            pr = row[2048 * blk: 2048 * blk + 2 * cnt].reshape(cnt, 2)
+            idx = pr[:, 1].astype(np.int64)
+            assert np.array_equal(np.sort(idx), np.arange(1024 * blk, 1024 * blk + cnt))
+            assert np.array_equal(pr[:, 0], want[idx])
+            top = (pr[:, 0] >> 22).astype(np.int64)
+            assert np.all(np.diff(top) <= 0), "pairs not ordered by their top bits"
+            cum = np.cumsum(np.bincount(top, minlength=1024)[::-1])[::-1]
+            assert np.array_equal(cum, h[blk])
 
 
 # ========================================================================= C128 dense decode
