@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_mfma_c4_128k_hbm_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_mfma_dma_c4_128k_hbm_traffic.md")
 
 
 def measured_traffic():
@@ -137,7 +137,7 @@ def c4_sparse(torch, hyb, W, BM, args):
     per_tok = BM.decode_query_bytes(L, ratio=4, sparse=True)
     comp_b = BM.compress_decode_bytes(4)
     step_bytes = B * (per_tok.total + comp_b)
-    score_bytes = B * BM.index_score_bytes(L)
+    score_bytes = B * BM.index_score_bytes(L, handoff=True)
     ms = secs * 1e3 / args.steps
     res = dict(
         value=B * args.steps / secs, ms_per_step=ms, step_bytes=step_bytes,
@@ -410,7 +410,7 @@ def main():
                    "step": "compress new token + indexer scores + top-512 + sparse attention + combine/inverse RoPE"},
         "hbm_frac_step": res["hbm_frac_step"],
         "step_bytes": res["step_bytes"],
-        "roofline": {"kernel": "score_mfma (indexer scores)", "bound": "hbm",
+        "roofline": {"kernel": "score_mfma_dma (indexer scores + top-k hand-off)", "bound": "hbm",
                      "achieved": res["score_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": res["score_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "traffic_unit": "bytes per launch (FETCH_SIZE x 2 + WRITE_SIZE, copy-calibrated)",

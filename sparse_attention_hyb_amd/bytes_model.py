@@ -72,12 +72,15 @@ def compress_decode_bytes(ratio: int, dim: int = 512, x_bytes: int = 2, out_dtyp
 
 
 def index_score_bytes(L: int, *, ratio: int = 4, idx_heads: int = 64, idx_dim: int = 128,
-                      idx_dtype: str = "bf16", q_bytes: int = 2, window: int = 128) -> int:
+                      idx_dtype: str = "bf16", q_bytes: int = 2, window: int = 128,
+                      handoff: bool = False) -> int:
     """The indexer-score kernel's own mandatory traffic for one query: visible keys + its query
-    and weights + the fp32 scores it writes."""
+    and weights + what it writes: fp32 scores, or (handoff) the selector hand-off of an 8-byte
+    (key, index) pair per entry plus a 1024-bin uint16 cumulative histogram per 1024 entries."""
     nv = n_visible(L - 1, ratio, window)
+    written = nv * 8 + (nv + 1023) // 1024 * 1024 * 2 if handoff else nv * 4
     return (nv * entry_bytes(idx_dtype, idx_dim) + idx_heads * idx_dim * q_bytes + idx_heads * 4
-            + nv * 4)
+            + written)
 
 
 def attention_flops(n_keys: int, n_heads: int = 64, dim: int = 512) -> int:
