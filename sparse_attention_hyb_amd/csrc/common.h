@@ -76,25 +76,34 @@ __device__ __forceinline__ int n_visible(int p, int ratio, int window) {
   return (window_start(p, window) + ratio - 1) / ratio;
 }
 
-// cos / sin of pos * base^(-2i / rope_dim), formed and reduced in double precision. The angle is
-// first brought to [-pi, pi] by subtracting k * 2pi with 2pi split in three parts (24 + 24 + 53
-// bits): for |angle| < 2^31, k < 2^29, so the first two products are exact and the residue keeps
-// full double precision; sincos then stays on its short path instead of a large-argument
-// reduction.
-__device__ __forceinline__ void rope_cs(double pos, int i, int rope_dim, double base, float* c,
-                                        float* s) {
-  const double theta = exp(-2.0 * (double)i / (double)rope_dim * log(base));
-  const double ang = pos * theta;
+// RoPE angle brought to [-pi, pi] in double precision: k * 2pi is subtracted with 2pi split in
+// three parts (24 + 24 + 53 bits). For |angle| < 2^31, k < 2^29, so the first two products are
+// exact and the residue keeps full double precision.
+__device__ __forceinline__ double rope_reduce(double ang) {
   constexpr double kInv2Pi = 0.15915494309189535;
   constexpr double kP1 = 6.2831854820251465;        // 2pi rounded to 24 bits
   constexpr double kP2 = -1.7484555314695172e-07;   // next 24 bits
   constexpr double kP3 = -6.8604979977715316e-15;   // the rest, to double precision
   const double k = rint(ang * kInv2Pi);
-  const double r = ((ang - k * kP1) - k * kP2) - k * kP3;
+  return ((ang - k * kP1) - k * kP2) - k * kP3;
+}
+
+// cos / sin of pos * base^(-2i / rope_dim), formed and reduced in double precision (sincos then
+// stays on its short path instead of a large-argument reduction).
+__device__ __forceinline__ void rope_cs(double pos, int i, int rope_dim, double base, float* c,
+                                        float* s) {
+  const double theta = exp(-2.0 * (double)i / (double)rope_dim * log(base));
   double sn, cs;
-  sincos(r, &sn, &cs);
+  sincos(rope_reduce(pos * theta), &sn, &cs);
   *c = (float)cs;
   *s = (float)sn;
+}
+
+// cos / sin of pos * theta for a frequency theta formed on the host: the angle is formed and
+// reduced in double precision, the reduced angle's cos / sin are taken in float (a few float
+// ulps; the double path above costs far more registers and time).
+__device__ __forceinline__ void rope_cs_theta(double pos, double theta, float* c, float* s) {
+  sincosf((float)rope_reduce(pos * theta), s, c);
 }
 
 // Query i -> (sequence, position).

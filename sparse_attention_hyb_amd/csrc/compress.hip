@@ -7,19 +7,16 @@
 // state in a state pool).
 //
 // Layout of the work: one workgroup per (group touched, sequence). A group's r raw tokens are
-// read once, row by row (each row is read by the whole workgroup: coalesced), pooled in float32
-// registers, normalised with a workgroup reduction, rotated and stored once. Only the workgroup of
-// the first group touched reads the state ring (it is the only group that can hold positions
-// from earlier calls), and the same workgroup writes the trailing incomplete group into the ring
-// after its reads, so no two workgroups touch the ring.
+// read once (each row by one wave: coalesced), pooled in float32 registers, normalised, rotated
+// and stored once. Only the workgroup of the first group touched reads the state ring (it is the
+// only group that can hold positions from earlier calls), and the same workgroup writes the
+// trailing incomplete group into the ring after its reads, so no two workgroups touch the ring.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 
 namespace hyb {
-
-constexpr int kCompressThreads = 1024;
-constexpr int kRowGroups = 4;                                  // token rows split 4 ways
-constexpr int kPairThreads = kCompressThreads / kRowGroups;    // 256 threads per row group
-constexpr int kMaxPairsPerThread = 4;                          // dim <= 2048
 
 template <typename T>
 __device__ __forceinline__ float2 load_pair(const T* row, int d);
@@ -46,20 +43,83 @@ __device__ __forceinline__ void store_pair(const PoolDev& p, int64_t idx, int d,
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs a) {
+// kVec consecutive dims d .. d + kVec - 1 of a row, widened to float (kVec = 4 needs the row
+// 16-byte aligned for float, 8-byte aligned for bf16; kVec = 2 needs 8 / 4 bytes).
+template <typename T, int kVec>
+__device__ __forceinline__ void load_vec(const T* row, int d, float (&v)[kVec]) {
+  if constexpr (kVec == 4) {
+    if constexpr (sizeof(T) == 4) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(row + d);
+      v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+    } else {
+      const uint2 q = *reinterpret_cast<const uint2*>(row + d);
+      v[0] = bf16_to_f32(q.x & 0xffffu); v[1] = bf16_to_f32(q.x >> 16);
+      v[2] = bf16_to_f32(q.y & 0xffffu); v[3] = bf16_to_f32(q.y >> 16);
+    }
+  } else {
+    const float2 q = load_pair<T>(row, d);
+    v[0] = q.x; v[1] = q.y;
+  }
+}
+
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+template <int kVec>
+__device__ __forceinline__ void store_f32_vec(float* row, int d, const float (&v)[kVec]) {
+  if constexpr (kVec == 4)
+    *reinterpret_cast<f32x4*>(row + d) = f32x4{v[0], v[1], v[2], v[3]};
+  else
+    *reinterpret_cast<float2*>(row + d) = make_float2(v[0], v[1]);
+}
+
+template <int kVec>
+__device__ __forceinline__ void load_f32_vec(const float* row, int d, float (&v)[kVec]) {
+  if constexpr (kVec == 4) {
+    const f32x4 q = *reinterpret_cast<const f32x4*>(row + d);
+    v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+  } else {
+    const float2 q = *reinterpret_cast<const float2*>(row + d);
+    v[0] = q.x; v[1] = q.y;
+  }
+}
+
+template <int kVec>
+__device__ __forceinline__ void store_vec(const PoolDev& p, int64_t idx, int d,
+                                          const float (&y)[kVec]) {
+  if (p.dtype == F32) {
+    store_f32_vec<kVec>(reinterpret_cast<float*>(p.data + idx * p.entry_bytes), d, y);
+  } else {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(p.data + idx * p.entry_bytes);
+    if constexpr (kVec == 4)
+      *reinterpret_cast<uint2*>(dst + d) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+    else
+      *reinterpret_cast<uint32_t*>(dst + d) = pack_bf16x2(y[0], y[1]);
+  }
+}
+
+// Compressor: one workgroup per (group touched, sequence). Wave w of the workgroup pools the
+// group's tokens t = w, w + nw, ... (ascending), each lane holding kJ chunks of kVec dims of the
+// row (chunk c = lane + 64 j, so every row load is a coalesced sweep). All of a wave's row loads
+// of a batch are issued before the first is used. The waves' partial sums meet in LDS behind the
+// one barrier of the kernel; wave 0 then adds them in wave order, normalises with a wave-only
+// reduction, rotates and stores. The RoPE cos / sin of the entry's position (one pair per lane of
+// the last wave) are formed while the row loads are in flight.
+template <typename T, int kVec, int kJ, int kRB>
+__global__ __launch_bounds__(1024) void compress_kernel(CompressArgs a) {
+  extern __shared__ float lds[];                       // [nw - 1][D] partials, then cs pairs
   const int b = blockIdx.y;
   const int gi = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int pt = tid % kPairThreads;   // which dim pairs
-  const int rg = tid / kPairThreads;   // which token rows (t = rg mod 4)
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;   // <= ratio (the launch sees to it)
   const int r = a.out.ratio;
   const int D = a.out.dim;
-  const int npairs = D / 2;
+  const int nchunks = D / kVec;
   const int c0 = a.cu_seqlens[b];
-  const int n_new = a.cu_seqlens[b + 1] - c0;
+  const int c1 = a.cu_seqlens[b + 1];
+  const int s0 = a.start_pos[b];   // loaded with the offsets: one round trip, not two
+  const int n_new = c1 - c0;
   if (n_new <= 0) return;
-  const int s0 = a.start_pos[b];
   const int t_end = s0 + n_new;
   const int g0 = s0 / r;
   const int g_last = (t_end - 1) / r;
@@ -67,138 +127,207 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
   if (g > g_last) return;
   const int gstart = g * r;
   const T* x = reinterpret_cast<const T*>(a.x);
-
-  __shared__ float wts[128];
-  __shared__ float red[kPairThreads / 64];
-  __shared__ float2 part[kRowGroups - 1][kMaxPairsPerThread * kPairThreads];
+  float2* cs = reinterpret_cast<float2*>(lds + (nw - 1) * D);
 
   if (gstart + r <= t_end) {  // group complete: emit entry g
-    if (tid < 64) {
-      // pooling weights: 1/r for the mean, softmax of the logits for the gate
-      float l0 = -INFINITY, l1 = -INFINITY;
-      if (a.mode == 1) {
-        int t = gstart + tid;
-        if (tid < r) l0 = t < s0 ? a.state_logits[(int64_t)b * r + tid] : a.gate[c0 + t - s0];
-        t = gstart + tid + 64;
-        if (tid + 64 < r) l1 = t < s0 ? a.state_logits[(int64_t)b * r + tid + 64] : a.gate[c0 + t - s0];
-        float m = wave_max(fmaxf(l0, l1));
-        float e0 = tid < r ? expf(l0 - m) : 0.f;
-        float e1 = tid + 64 < r ? expf(l1 - m) : 0.f;
-        float inv = 1.0f / wave_sum(e0 + e1);
-        if (tid < r) wts[tid] = e0 * inv;
-        if (tid + 64 < r) wts[tid + 64] = e1 * inv;
-      } else {
-        if (tid < r) wts[tid] = 1.0f;
-        if (tid + 64 < r) wts[tid + 64] = 1.0f;
-      }
+    // block-table entry of the output, loaded now and checked after the barrier
+    const int lb = g / a.out.per_block;
+    const int phys = lb < a.out.max_blocks ? a.out.block_table[(int64_t)b * a.out.max_blocks + lb] : -1;
+    // pooling weights: 1 for the mean (scaled by 1/r at the end), softmax of the logits for the
+    // gate; every wave forms the softmax itself (r <= 128: two logits per lane), behind its first
+    // batch of row loads
+    float e0 = 1.f, e1 = 1.f;
+    float l0 = -INFINITY, l1 = -INFINITY;
+    if (a.mode == 1) {
+      int t = gstart + lane;
+      if (lane < r) l0 = t < s0 ? a.state_logits[(int64_t)b * r + lane] : a.gate[c0 + t - s0];
+      t += 64;
+      if (lane + 64 < r) l1 = t < s0 ? a.state_logits[(int64_t)b * r + lane + 64] : a.gate[c0 + t - s0];
     }
-    __syncthreads();
 
-    float acc[kMaxPairsPerThread][2];
+    float acc[kJ][kVec];
 #pragma unroll
-    for (int j = 0; j < kMaxPairsPerThread; ++j) acc[j][0] = acc[j][1] = 0.f;
-    // Row group rg sums the group's tokens t = rg, rg + 4, ... in ascending order: those that
-    // arrived in earlier calls from the state ring, the rest from x. The split depends only on
-    // t, so a chunked compression adds exactly the same numbers in the same order as a one-shot
-    // one. Loops are unrolled so each thread keeps several row loads in flight.
+    for (int j = 0; j < kJ; ++j)
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) acc[j][e] = 0.f;
+    // Tokens before s0 come from the state ring, the rest from x. Which wave adds which token,
+    // and in what order, depends only on t, so a chunked compression adds the same numbers in
+    // the same order as a one-shot one.
     const int n_state = max(0, min(s0, gstart + r) - gstart);
-#pragma unroll 8
-    for (int t = rg; t < n_state; t += kRowGroups) {
-      const float wt = wts[t];
-      const float* row = a.state + ((int64_t)b * r + t) * D;
+    // chunk offsets of this lane; lanes past the row's end load its last chunk again (so no load
+    // is predicated) and drop it at the end
+    int coff[kJ];
 #pragma unroll
-      for (int j = 0; j < kMaxPairsPerThread; ++j) {
-        int pi = pt + j * kPairThreads;
-        if (pi < npairs) {
-          float2 v = load_pair<float>(row, 2 * pi);
-          acc[j][0] = fmaf(wt, v.x, acc[j][0]);
-          acc[j][1] = fmaf(wt, v.y, acc[j][1]);
+    for (int j = 0; j < kJ; ++j) coff[j] = min(lane + 64 * j, nchunks - 1) * kVec;
+    const float* ring = a.state + (int64_t)b * r * D;
+    const T* xs = x + (int64_t)(c0 - s0 + gstart) * D;   // row of token t of the group: xs + t * D
+    // Raw words per chunk. With four-dim chunks a bf16 row is read 16 bytes at a time too: the
+    // lane loads the 8-dim block holding its 4 dims and keeps the half it owns, so that ring rows
+    // and rows of x take the same load and a batch of rows needs no branch between a load and
+    // its use (where branches met, the compiler would wait for every load in flight).
+    using Raw = std::conditional_t<kVec == 4, u32x4, u32x2>;
+    // the RoPE frequency of this lane's pair (last wave), read before the rows
+    const double theta = a.theta[min(lane, 63)];
+    for (int t0 = w; t0 < r; t0 += kRB * nw) {
+      Raw v[kRB][kJ];
+#pragma unroll
+      for (int i = 0; i < kRB; ++i) {
+        const int t = t0 + i * nw;
+        const bool from_ring = t < n_state;
+        if constexpr (sizeof(T) == 4) {
+          const float* row = from_ring ? ring + (int64_t)t * D
+                                       : reinterpret_cast<const float*>(xs) + (int64_t)t * D;
+#pragma unroll
+          for (int j = 0; j < kJ; ++j) v[i][j] = *reinterpret_cast<const Raw*>(row + coff[j]);
+        } else if constexpr (kVec == 4) {
+          const char* row = from_ring ? reinterpret_cast<const char*>(ring + (int64_t)t * D)
+                                      : reinterpret_cast<const char*>(xs + (int64_t)t * D);
+#pragma unroll
+          for (int j = 0; j < kJ; ++j) {
+            const int off = from_ring ? coff[j] * 4 : (coff[j] & ~7) * 2;
+            v[i][j] = *reinterpret_cast<const Raw*>(row + off);
+          }
+        } else {   // pairs of bf16 (kRB == 1)
+          if (from_ring) {
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) v[i][j] = *reinterpret_cast<const Raw*>(ring + (int64_t)t * D + coff[j]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < kJ; ++j)
+              v[i][j] = Raw{*reinterpret_cast<const uint32_t*>(xs + (int64_t)t * D + coff[j]), 0u};
+          }
+        }
+      }
+      if (t0 == w && a.mode == 1) {
+        float m0 = l0, m1 = l1;
+        asm volatile("" : "+v"(m0), "+v"(m1));   // keeps the softmax (and its wait) here
+        const float m = wave_max(fmaxf(m0, m1));
+        e0 = lane < r ? expf(m0 - m) : 0.f;
+        e1 = lane + 64 < r ? expf(m1 - m) : 0.f;
+        const float inv = 1.0f / wave_sum(e0 + e1);
+        e0 *= inv;
+        e1 *= inv;
+      }
+      if (t0 == w && w == nw - 1 && lane < (a.rope_dim >> 1)) {
+        // here, behind the batch's loads (the empty asm keeps the compiler from hoisting the
+        // math, and the wait for theta, in front of them)
+        double th = theta;
+        asm volatile("" : "+v"(th));
+        float c, s;
+        rope_cs_theta((double)(gstart + r - 1), th, &c, &s);
+        cs[lane] = make_float2(c, s);
+      }
+#pragma unroll
+      for (int i = 0; i < kRB; ++i) {
+        const int t = t0 + i * nw;
+        const bool from_ring = t < n_state;
+        // weight of token t: lane t mod 64 holds it (t is the same on every lane)
+        const float wt = __int_as_float(t < 64 ? __builtin_amdgcn_readlane(__float_as_int(e0), t & 63)
+                                               : __builtin_amdgcn_readlane(__float_as_int(e1), t & 63));
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+          const Raw q = v[i][j];
+          float val[kVec];
+          if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) val[e] = __uint_as_float(q[e]);
+          } else if constexpr (kVec == 4) {
+            // the words of x holding this lane's dims: the low or high half of the 16 bytes read
+            const bool hi = coff[j] & 4;
+            const uint32_t x0 = hi ? q[2] : q[0];
+            const uint32_t x1 = hi ? q[3] : q[1];
+            val[0] = from_ring ? __uint_as_float(q[0]) : bf16_to_f32(x0 & 0xffffu);
+            val[1] = from_ring ? __uint_as_float(q[1]) : bf16_to_f32(x0 >> 16);
+            val[2] = from_ring ? __uint_as_float(q[2]) : bf16_to_f32(x1 & 0xffffu);
+            val[3] = from_ring ? __uint_as_float(q[3]) : bf16_to_f32(x1 >> 16);
+          } else {
+            val[0] = from_ring ? __uint_as_float(q[0]) : bf16_to_f32(q[0] & 0xffffu);
+            val[1] = from_ring ? __uint_as_float(q[1]) : bf16_to_f32(q[0] >> 16);
+          }
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) acc[j][e] = fmaf(wt, val[e], acc[j][e]);
         }
       }
     }
-    const int t_x0 = n_state + ((rg - n_state) % kRowGroups + kRowGroups) % kRowGroups;
-#pragma unroll 8
-    for (int t = t_x0; t < r; t += kRowGroups) {
-      const float wt = wts[t];
-      const T* row = x + (int64_t)(c0 + gstart + t - s0) * D;
+    if (w > 0) {
+      float* part = lds + (w - 1) * D;
 #pragma unroll
-      for (int j = 0; j < kMaxPairsPerThread; ++j) {
-        int pi = pt + j * kPairThreads;
-        if (pi < npairs) {
-          float2 v = load_pair<T>(row, 2 * pi);
-          acc[j][0] = fmaf(wt, v.x, acc[j][0]);
-          acc[j][1] = fmaf(wt, v.y, acc[j][1]);
-        }
+      for (int j = 0; j < kJ; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nchunks) store_f32_vec<kVec>(part, c * kVec, acc[j]);
       }
-    }
-    if (rg > 0) {
-#pragma unroll
-      for (int j = 0; j < kMaxPairsPerThread; ++j)
-        part[rg - 1][pt + j * kPairThreads] = make_float2(acc[j][0], acc[j][1]);
     }
     __syncthreads();
-    const float post = a.mode == 1 ? 1.0f : 1.0f / (float)r;
-    float ss = 0.f;
-    if (rg == 0) {
+    if (w == 0) {
+      const float post = a.mode == 1 ? 1.0f : 1.0f / (float)r;
+      float ss = 0.f;
 #pragma unroll
-      for (int j = 0; j < kMaxPairsPerThread; ++j) {
+      for (int j = 0; j < kJ; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nchunks) {
+          for (int q = 1; q < nw; ++q) {
+            float p[kVec];
+            load_f32_vec<kVec>(lds + (q - 1) * D, c * kVec, p);
 #pragma unroll
-        for (int q = 0; q < kRowGroups - 1; ++q) {
-          const float2 v = part[q][pt + j * kPairThreads];
-          acc[j][0] += v.x;
-          acc[j][1] += v.y;
+            for (int e = 0; e < kVec; ++e) acc[j][e] += p[e];
+          }
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            acc[j][e] *= post;
+            ss = fmaf(acc[j][e], acc[j][e], ss);
+          }
         }
-        acc[j][0] *= post;
-        acc[j][1] *= post;
-        ss = fmaf(acc[j][0], acc[j][0], fmaf(acc[j][1], acc[j][1], ss));
       }
       ss = wave_sum(ss);
-      if ((tid & 63) == 0) red[tid >> 6] = ss;
-    }
-    __syncthreads();
-    if (rg == 0) {
-      float tot = 0.f;
+      const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+      if (phys >= 0 && phys < a.out.num_blocks) {
+        const int64_t idx = (int64_t)phys * a.out.per_block + (g - lb * a.out.per_block);
+        const int rope_lo = D - a.rope_dim;
 #pragma unroll
-      for (int w = 0; w < kPairThreads / 64; ++w) tot += red[w];
-      const float inv = 1.0f / sqrtf(tot / (float)D + a.eps);
-      const int64_t idx = entry_index(a.out, b, g);
-      const int rope_lo = D - a.rope_dim;
-      const double pos = (double)(gstart + r - 1);
+        for (int j = 0; j < kJ; ++j) {
+          const int c = lane + 64 * j;
+          if (c < nchunks) {
+            float y[kVec];
 #pragma unroll
-      for (int j = 0; j < kMaxPairsPerThread; ++j) {
-        int pi = pt + j * kPairThreads;
-        if (pi < npairs && idx >= 0) {
-          float y0 = acc[j][0] * inv, y1 = acc[j][1] * inv;
-          int d = 2 * pi;
-          if (d >= rope_lo) {
-            float c, s;
-            rope_cs(pos, (d - rope_lo) >> 1, a.rope_dim, a.rope_base, &c, &s);
-            float z0 = y0 * c - y1 * s;
-            float z1 = y0 * s + y1 * c;
-            y0 = z0;
-            y1 = z1;
+            for (int e = 0; e < kVec; e += 2) {
+              float y0 = acc[j][e] * inv, y1 = acc[j][e + 1] * inv;
+              const int d = c * kVec + e;
+              if (d >= rope_lo) {
+                const float2 q = cs[(d - rope_lo) >> 1];
+                const float z0 = y0 * q.x - y1 * q.y;
+                const float z1 = y0 * q.y + y1 * q.x;
+                y0 = z0;
+                y1 = z1;
+              }
+              y[e] = y0;
+              y[e + 1] = y1;
+            }
+            store_vec<kVec>(a.out, idx, c * kVec, y);
           }
-          store_pair(a.out, idx, d, y0, y1);
         }
       }
     }
   }
 
   if (gi == 0) {
-    // trailing incomplete group -> state ring (this workgroup's ring reads are finished)
+    // trailing incomplete group -> state ring
     const int tail_start = g_last * r;
     if (tail_start + r > t_end) {
-      __syncthreads();
       const int lo = tail_start > s0 ? tail_start : s0;
-      for (int t = lo + rg; t < t_end; t += kRowGroups) {
+      for (int t = lo + w; t < t_end; t += nw) {
         const int slot = t - tail_start;
         const T* row = x + (int64_t)(c0 + t - s0) * D;
         float* dst = a.state + ((int64_t)b * r + slot) * D;
-        for (int pi = pt; pi < npairs; pi += kPairThreads) {
-          float2 v = load_pair<T>(row, 2 * pi);
-          *reinterpret_cast<float2*>(dst + 2 * pi) = v;
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+          const int c = lane + 64 * j;
+          if (c < nchunks) {
+            float v[kVec];
+            load_vec<T, kVec>(row, c * kVec, v);
+            store_f32_vec<kVec>(dst, c * kVec, v);
+          }
         }
-        if (a.mode == 1 && pt == 0) a.state_logits[(int64_t)b * r + slot] = a.gate[c0 + t - s0];
+        if (a.mode == 1 && lane == 0) a.state_logits[(int64_t)b * r + slot] = a.gate[c0 + t - s0];
       }
     }
   }
@@ -227,7 +356,7 @@ __global__ __launch_bounds__(256) void swa_insert_kernel(CompressArgs a) {
       int d = 2 * pi;
       if (d >= rope_lo) {
         float c, s;
-        rope_cs((double)t, (d - rope_lo) >> 1, a.rope_dim, a.rope_base, &c, &s);
+        rope_cs_theta((double)t, a.theta[(d - rope_lo) >> 1], &c, &s);
         float z0 = v.x * c - v.y * s;
         float z1 = v.x * s + v.y * c;
         v.x = z0;
@@ -238,14 +367,47 @@ __global__ __launch_bounds__(256) void swa_insert_kernel(CompressArgs a) {
   }
 }
 
+namespace {
+template <typename T, int kVec, int kJ>
+hipError_t launch_compress_t(const CompressArgs& a, int rows_per_wave, dim3 grid, dim3 block,
+                             size_t lds, hipStream_t s) {
+  // rows per batch and wave: 64 words of loads in flight per lane; one row above dim 512, and
+  // for bf16 pairs (whose ring and x rows take different loads)
+  constexpr int kRB = (kJ * kVec >= 32 || (sizeof(T) == 2 && kVec == 2)) ? 1 : 64 / (kJ * kVec);
+  if (rows_per_wave % kRB == 0)
+    hipLaunchKernelGGL((compress_kernel<T, kVec, kJ, kRB>), grid, block, lds, s, a);
+  else
+    hipLaunchKernelGGL((compress_kernel<T, kVec, kJ, 1>), grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_compress_x(const CompressArgs& a, bool v4, int rows_per_wave, dim3 grid,
+                             dim3 block, size_t lds, hipStream_t s) {
+  const int D = a.out.dim;
+  if (v4) return D <= 512 ? launch_compress_t<T, 4, 2>(a, rows_per_wave, grid, block, lds, s)
+                          : launch_compress_t<T, 4, 8>(a, rows_per_wave, grid, block, lds, s);
+  return D <= 512 ? launch_compress_t<T, 2, 4>(a, rows_per_wave, grid, block, lds, s)
+                  : launch_compress_t<T, 2, 16>(a, rows_per_wave, grid, block, lds, s);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+}  // namespace
+
+// dim <= 2048, ratio 4 or 128. Waves per workgroup: min(ratio, 16), 8 above dim 1024, so the
+// partials fit in 60 KB of LDS. Four-dim chunks when x, the state ring and the pool are 16-byte
+// aligned and dim % 4 == 0 (float x) or dim % 8 == 0 (bf16 x), else pairs.
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   const int r = a.out.ratio;
-  dim3 grid((a.max_new_tokens + r - 1) / r + 1, a.batch);
-  if (a.x_dtype == F32)
-    hipLaunchKernelGGL(compress_kernel<float>, grid, dim3(kCompressThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(compress_kernel<uint16_t>, grid, dim3(kCompressThreads), 0, s, a);
-  return hipGetLastError();
+  const int D = a.out.dim;
+  const int nw = std::min(r, D <= 1024 ? 16 : 8);
+  const bool v4 = D % (a.x_dtype == F32 ? 4 : 8) == 0 && aligned16(a.x) && aligned16(a.state) &&
+                  aligned16(a.out.data);
+  const dim3 grid((a.max_new_tokens + r - 1) / r + 1, a.batch);
+  const dim3 block(64 * nw);
+  const size_t lds = ((size_t)(nw - 1) * D + 128) * sizeof(float);
+  return a.x_dtype == F32 ? launch_compress_x<float>(a, v4, r / nw, grid, block, lds, s)
+                          : launch_compress_x<uint16_t>(a, v4, r / nw, grid, block, lds, s);
 }
 
 hipError_t launch_swa_insert(const CompressArgs& a, hipStream_t s) {

@@ -95,6 +95,12 @@ int check_rope(const char* op, int32_t rope_dim, double base, int32_t dim) {
   return HYB_OK;
 }
 
+// RoPE frequencies base^(-2i / rope_dim) for the compressor kernels (rope_dim <= 128).
+void fill_theta(hyb::CompressArgs* a, int32_t rope_dim, double base) {
+  for (int i = 0; i < rope_dim / 2; ++i)
+    a->theta[i] = std::exp(-2.0 * (double)i / (double)rope_dim * std::log(base));
+}
+
 int64_t visible(int64_t p, int64_t ratio, int64_t window) {
   int64_t ws = p - window + 1;
   if (ws < 0) ws = 0;
@@ -243,7 +249,8 @@ int32_t hyb_compress(const void* x, int32_t x_dtype, const float* gate_logits,
   HYB_TRY(check_rope(op, rope_dim, rope_base, po.dim));
   if (batch == 0 || max_new_tokens == 0) return HYB_OK;
   hyb::CompressArgs a{x, x_dtype, gate_logits, cu_seqlens, start_pos, batch, max_new_tokens,
-                      state, state_logits, mode, po, rope_dim, rope_base, eps};
+                      state, state_logits, mode, po, rope_dim, rope_base, eps, {}};
+  fill_theta(&a, rope_dim, rope_base);
   return launch_status(hyb::launch_compress(a, static_cast<hipStream_t>(stream)), op);
 }
 
@@ -257,7 +264,8 @@ int32_t hyb_swa_insert(const void* x, int32_t x_dtype, const int32_t* cu_seqlens
   HYB_TRY(check_rope(op, rope_dim, rope_base, ps.dim));
   if (batch == 0 || max_new_tokens == 0) return HYB_OK;
   hyb::CompressArgs a{x, x_dtype, nullptr, cu_seqlens, start_pos, batch, max_new_tokens,
-                      nullptr, nullptr, 0, ps, rope_dim, rope_base, 0.f};
+                      nullptr, nullptr, 0, ps, rope_dim, rope_base, 0.f, {}};
+  fill_theta(&a, rope_dim, rope_base);
   return launch_status(hyb::launch_swa_insert(a, static_cast<hipStream_t>(stream)), op);
 }
 

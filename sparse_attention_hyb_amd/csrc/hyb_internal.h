@@ -49,6 +49,7 @@ struct CompressArgs {
   int32_t rope_dim;
   double rope_base;
   float eps;
+  double theta[64];   // RoPE frequencies base^(-2i / rope_dim), i < rope_dim / 2 (host-formed)
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 hipError_t launch_swa_insert(const CompressArgs& a, hipStream_t s);
