@@ -130,6 +130,25 @@ int32_t hyb_compress(const void* x, int32_t x_dtype, const float* gate_logits,
                      const hyb_paged* out, int32_t rope_dim, double rope_base, float eps,
                      void* stream);
 
+/* The arguments of one hyb_compress call, as one struct (same meaning, layout and rules; the
+ * stream is the caller's of the entry point that takes the struct). */
+typedef struct hyb_compress_call {
+  const void* x;
+  int32_t x_dtype;
+  const float* gate_logits;
+  const int32_t* cu_seqlens;
+  const int32_t* start_pos;
+  int32_t batch;
+  int32_t max_new_tokens;
+  float* state;
+  float* state_logits;
+  int32_t mode;
+  const hyb_paged* out;
+  int32_t rope_dim;
+  double rope_base;
+  float eps;
+} hyb_compress_call;
+
 /* --------------------------------------------------------------------------------------------
  * hyb_swa_insert - raw sliding-window entries s_t = RoPE(x_t, t) (no norm) written to the raw
  * pool (ratio 1) at position t. The "KV RoPE + K insert" step of [vLLM]'s fused-kernel list.
@@ -230,6 +249,28 @@ int32_t hyb_attn_decode(const void* q, int32_t q_dtype, const int32_t* seq_lens,
                         const hyb_paged* comp, const int32_t* topk_idx, int32_t k, int32_t window,
                         float softmax_scale, int32_t rope_dim, double rope_base, void* out,
                         int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------------
+ * hyb_attn_decode_compress - hyb_attn_decode, then hyb_compress(*compress), on one stream.
+ * [vLLM] "vLLM side" (multi-stream overlap of the step's kernels): with the 64 x 512 bf16
+ * attention kernel and a compressor call that four waves run in four-dim chunks (dim <= 512,
+ * dim % 4 == 0 for F32 x and % 8 for BF16 x, x / state / pool data 16-byte aligned), the
+ * compressor's workgroups are launched together with the attention's split combine, so its
+ * memory latency hides behind the combine; otherwise the compressor is launched after it.
+ * The result is exactly that of the two calls in that order: the attention reads the pools as
+ * they were before the call. In a decode step this equals compressing the new token first, as
+ * an entry that a group completes at position p is not yet visible to the query at p
+ * (n_vis(p) <= floor(p / ratio) for window >= ratio). compress's buffers must not overlap `out`
+ * or the workspace. Arguments: those of hyb_attn_decode, then compress (non-NULL), then stream.
+ * ------------------------------------------------------------------------------------------ */
+int32_t hyb_attn_decode_compress(const void* q, int32_t q_dtype, const int32_t* seq_lens,
+                                 int32_t batch, int32_t n_heads, int32_t max_seq_len,
+                                 const hyb_paged* swa, const hyb_paged* comp,
+                                 const int32_t* topk_idx, int32_t k, int32_t window,
+                                 float softmax_scale, int32_t rope_dim, double rope_base,
+                                 void* out, int32_t out_dtype, void* workspace,
+                                 size_t workspace_bytes, const hyb_compress_call* compress,
+                                 void* stream);
 
 /* --------------------------------------------------------------------------------------------
  * hyb_attn_prefill - causal attention for a chunk of query tokens: query i of sequence q_seq[i]

@@ -30,8 +30,8 @@ EXPORTS = (
     "hyb_abi_version", "hyb_status_str", "hyb_last_error", "hyb_compress", "hyb_swa_insert",
     "hyb_index_score", "hyb_topk", "hyb_index_score_keys", "hyb_topk_keys",
     "hyb_index_topk_workspace_bytes", "hyb_index_topk",
-    "hyb_attn_decode_workspace_bytes", "hyb_attn_decode", "hyb_attn_prefill_workspace_bytes",
-    "hyb_attn_prefill",
+    "hyb_attn_decode_workspace_bytes", "hyb_attn_decode", "hyb_attn_decode_compress",
+    "hyb_attn_prefill_workspace_bytes", "hyb_attn_prefill",
 )
 
 
@@ -52,6 +52,25 @@ class hyb_paged(ctypes.Structure):
         ("num_blocks", ctypes.c_int32),
         ("max_blocks", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
+    ]
+
+
+class hyb_compress_call(ctypes.Structure):
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("x_dtype", ctypes.c_int32),
+        ("gate_logits", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("start_pos", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("max_new_tokens", ctypes.c_int32),
+        ("state", ctypes.c_void_p),
+        ("state_logits", ctypes.c_void_p),
+        ("mode", ctypes.c_int32),
+        ("out", ctypes.POINTER(hyb_paged)),
+        ("rope_dim", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+        ("eps", ctypes.c_float),
     ]
 
 
@@ -76,6 +95,9 @@ _SIGS = {
     "hyb_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "hyb_attn_decode": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F, _I32,
                                _D, _P, _I32, _P, _SZ, _P]),
+    "hyb_attn_decode_compress": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F,
+                                        _I32, _D, _P, _I32, _P, _SZ,
+                                        ctypes.POINTER(hyb_compress_call), _P]),
     "hyb_attn_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "hyb_attn_prefill": (_I32, [_P, _I32, _P, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F,
                                 _I32, _D, _P, _I32, _P, _SZ, _P]),
@@ -247,6 +269,36 @@ def hyb_attn_decode(q, seq_lens, max_seq_len: int, swa_pool, comp_pool, out, top
                                   int(window), scale, int(rope_dim), float(rope_base), _ptr(out),
                                   _tdtype(out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def hyb_attn_decode_compress(q, seq_lens, max_seq_len: int, swa_pool, comp_pool, out, x,
+                             cu_seqlens, start_pos, max_new_tokens: int, state, out_pool,
+                             topk_idx=None, k: int = 0, window: int = 128,
+                             softmax_scale: Optional[float] = None, rope_dim: int = 64,
+                             rope_base: float = 10000.0, eps: float = 1e-6, gate_logits=None,
+                             state_logits=None, workspace=None, stream=None) -> None:
+    """hyb_attn_decode(q, ...) then hyb_compress(x, ...) in one call (see include/hyb.h); both
+    use rope_dim and rope_base."""
+    b, h, dim = (int(s) for s in q.shape)
+    if topk_idx is not None and not k:
+        k = int(topk_idx.shape[1])
+    scale = float(softmax_scale) if softmax_scale is not None else dim ** -0.5
+    if workspace is None:
+        need = hyb_attn_decode_workspace_bytes(b, h, dim, max_seq_len, comp_pool.ratio,
+                                               k if topk_idx is not None else 0, window)
+        workspace = _empty_workspace(need, q.device)
+    ds, dc, do = paged(swa_pool), paged(comp_pool), paged(out_pool)
+    call = hyb_compress_call(
+        x=_ptr(x), x_dtype=_tdtype(x), gate_logits=_ptr(gate_logits), cu_seqlens=_ptr(cu_seqlens),
+        start_pos=_ptr(start_pos), batch=int(start_pos.shape[0]), max_new_tokens=int(max_new_tokens),
+        state=_ptr(state), state_logits=_ptr(state_logits),
+        mode=POOL_SOFTMAX_GATE if gate_logits is not None else POOL_MEAN,
+        out=ctypes.pointer(do), rope_dim=int(rope_dim), rope_base=float(rope_base), eps=float(eps))
+    _check(load().hyb_attn_decode_compress(
+        _ptr(q), _tdtype(q), _ptr(seq_lens), b, h, int(max_seq_len), ctypes.byref(ds),
+        ctypes.byref(dc), _ptr(topk_idx), int(k), int(window), scale, int(rope_dim),
+        float(rope_base), _ptr(out), _tdtype(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), ctypes.byref(call), _stream(stream)))
 
 
 def hyb_attn_prefill_workspace_bytes(n_q: int, n_heads: int, dim: int, max_pos: int,

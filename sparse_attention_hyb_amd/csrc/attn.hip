@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "compress_dev.h"
 
 namespace hyb {
 
@@ -179,7 +180,6 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 }
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
 // Masked keys (past the end of a split, absent blocks, unused top-k slots) load this row instead
 // of a pool entry, so their operands are zero without any per-use select. Never written.
@@ -713,15 +713,23 @@ __device__ __forceinline__ float load1(const PT* p) {
   }
 }
 
+// LDS of one combine workgroup: split weights [split][head of the group] and the splits' (m, l)
+// [split][m, l][head of the group], sized by the split count.
+__host__ __device__ inline size_t combine_lds_bytes(int n_split) {
+  return (size_t)n_split * 3 * kCombineHeads * sizeof(float);
+}
+
+// Workgroup `logical` of the combine: head group logical % gx (gx groups of hpw heads), query
+// logical / gx. sm: combine_lds_bytes(n_split) of LDS.
 template <typename PT>
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int hpw) {
-  const int logical = xcd_logical(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
-  const int i = logical / gridDim.x;
-  const int h0 = (logical % gridDim.x) * hpw;
+__device__ __forceinline__ void combine_group(const AttnArgs& a, int hpw, int logical, int gx,
+                                              float* sm) {
+  const int i = logical / gx;
+  const int h0 = (logical % gx) * hpw;
   const int H = a.n_heads, D = a.dim, ns = a.n_split;
   const int nh = min(hpw, H - h0);
-  __shared__ float wsp[kMaxSplit * kCombineHeads];       // [split][head of the group]
-  __shared__ float mls[kMaxSplit * 2 * kCombineHeads];   // [split][m, l][head of the group]
+  float* wsp = sm;                              // [split][head of the group]
+  float* mls = sm + ns * kCombineHeads;         // [split][m, l][head of the group]
   __shared__ float rc[kMaxRopePairs], rs[kMaxRopePairs];
   const int tid = threadIdx.x;
   const int64_t sstride = (int64_t)H * D;
@@ -839,6 +847,33 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int hpw) {
   }
 }
 
+template <typename PT>
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int hpw) {
+  extern __shared__ __attribute__((aligned(16))) float csm[];
+  combine_group<PT>(a, hpw, xcd_logical(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y),
+                    gridDim.x, csm);
+}
+
+// The combine of the MFMA kernel's splits with a compressor call riding along: workgroups
+// [0, n_comb) combine (mapped as attn_combine's), the rest each pool one compressor group with
+// four waves (float or bf16 x, dim <= 512 in four-dim chunks). The compressor's latency then hides
+// behind the combine instead of taking a launch of its own. Nothing here orders the two: the
+// caller guarantees that neither reads what the other writes.
+template <typename T, int kRB, int kV>
+__global__ __launch_bounds__(256, 4) void attn_combine_compress(AttnArgs a, int hpw, int gx,
+                                                             int n_comb, CompressArgs c,
+                                                             int comp_gx) {
+  // dynamic LDS: the combine's (combine_lds_bytes) or the compressor's ((3 dim + 128) floats)
+  extern __shared__ __attribute__((aligned(16))) float csm[];
+  const int bid = blockIdx.x;
+  if (bid < n_comb) {
+    combine_group<uint16_t>(a, hpw, xcd_logical(bid, n_comb), gx, csm);
+  } else {
+    const int k = bid - n_comb;
+    compress_group<T, 4, 2, kRB, kV>(c, k % comp_gx, k / comp_gx, csm);
+  }
+}
+
 // Fewest keys per split of the MFMA kernel: below this the fixed cost of a workgroup (key
 // resolution, pipeline fill, writing its partial) outweighs the parallelism gained.
 constexpr int kMfmaMinChunk = 128;
@@ -877,8 +912,8 @@ AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_k
   return pl;
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  if (a.n_q == 0) return hipSuccess;
+namespace {
+hipError_t launch_attention_kernel(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.n_q);
   if (a.use_mfma) {
     if (a.swa.dtype == FP8)
@@ -890,14 +925,65 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
                                   3 * (size_t)a.n_heads);
     hipLaunchKernelGGL(attn_generic, grid, dim3(256), lds, s, a);
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+int combine_heads_per_wg(const AttnArgs& a) {
+  return std::max(1, std::min(kCombineHeads, std::min(a.n_heads, kCombineElems / a.dim)));
+}
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.n_q == 0) return hipSuccess;
+  hipError_t e = launch_attention_kernel(a, s);
   if (e != hipSuccess) return e;
-  const int hpw = std::max(1, std::min(kCombineHeads, std::min(a.n_heads, kCombineElems / a.dim)));
+  const int hpw = combine_heads_per_wg(a);
   const dim3 cgrid((a.n_heads + hpw - 1) / hpw, a.n_q);
+  const size_t lds = combine_lds_bytes(a.n_split);
   if (a.use_mfma)
-    hipLaunchKernelGGL(attn_combine<uint16_t>, cgrid, dim3(256), 0, s, a, hpw);
+    hipLaunchKernelGGL(attn_combine<uint16_t>, cgrid, dim3(256), lds, s, a, hpw);
   else
-    hipLaunchKernelGGL(attn_combine<float>, cgrid, dim3(256), 0, s, a, hpw);
+    hipLaunchKernelGGL(attn_combine<float>, cgrid, dim3(256), lds, s, a, hpw);
+  return hipGetLastError();
+}
+
+// Attention, then the compressor call c. With the MFMA kernel and a compressor call that four
+// waves can run in four-dim chunks (dim <= 512, dim % 4 == 0 for float x and % 8 for bf16 x,
+// x / state / pool 16-byte aligned), the compressor's workgroups join the combine's launch;
+// otherwise the compressor gets its own launch after the combine.
+hipError_t launch_attention_compress(const AttnArgs& a, const CompressArgs& c, hipStream_t s) {
+  const int r = c.out.ratio, D = c.out.dim;
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  const bool fuse = a.n_q > 0 && a.use_mfma && c.batch > 0 && c.max_new_tokens > 0 && D <= 512 &&
+                    D % (c.x_dtype == F32 ? 4 : 8) == 0 && al16(c.x) && al16(c.state) &&
+                    al16(c.out.data) && (r == 4 || r == 128);
+  if (!fuse) {
+    hipError_t e = launch_attention(a, s);
+    if (e != hipSuccess) return e;
+    return c.batch > 0 && c.max_new_tokens > 0 ? launch_compress(c, s) : hipSuccess;
+  }
+  hipError_t e = launch_attention_kernel(a, s);
+  if (e != hipSuccess) return e;
+  const int hpw = combine_heads_per_wg(a);
+  const int gx = (a.n_heads + hpw - 1) / hpw;
+  const int n_comb = gx * a.n_q;
+  const int comp_gx = (c.max_new_tokens + r - 1) / r + 1;
+  const dim3 grid(n_comb + comp_gx * c.batch);
+  const size_t lds = std::max(combine_lds_bytes(a.n_split), (size_t)(3 * D + 128) * sizeof(float));
+  // four waves run pooled_waves(r, D) virtual waves: 4 (r = 4) or 16 (r = 128, D <= 512); at
+  // r = 128 a batch holds two rows of each of a wave's four virtual waves (the kernel keeps to
+  // 128 registers, so that four of its workgroups fit on a compute unit)
+  if (c.x_dtype == F32) {
+    if (r == 4)
+      hipLaunchKernelGGL((attn_combine_compress<float, 1, 1>), grid, dim3(256), lds, s, a, hpw, gx, n_comb, c, comp_gx);
+    else
+      hipLaunchKernelGGL((attn_combine_compress<float, 2, 4>), grid, dim3(256), lds, s, a, hpw, gx, n_comb, c, comp_gx);
+  } else {
+    if (r == 4)
+      hipLaunchKernelGGL((attn_combine_compress<uint16_t, 1, 1>), grid, dim3(256), lds, s, a, hpw, gx, n_comb, c, comp_gx);
+    else
+      hipLaunchKernelGGL((attn_combine_compress<uint16_t, 2, 4>), grid, dim3(256), lds, s, a, hpw, gx, n_comb, c, comp_gx);
+  }
   return hipGetLastError();
 }
 

@@ -1,0 +1,378 @@
+// Device side of the KV compressor (pool -> RMSNorm -> RoPE -> paged insert, with an in-progress
+// state ring), shared by the compressor's own kernel and the kernel that runs it beside the
+// attention combine.
+//
+// Method: vLLM DeepSeek-V4 day-0 post, "four moves" (c4a / c128a KV compression) and "vLLM side"
+// (fused compressor + RMSNorm + RoPE + cache insert); SGLang DeepSeek-V4 day-0 blog, section
+// "Shadow Radix" (each compression layer keeps its in-progress compression state in a state pool).
+//
+// Layout of the work: one workgroup per (group touched, sequence). A group's r raw tokens are
+// read once (each row by one wave: coalesced), pooled in float32 registers, normalised, rotated
+// and stored once. Only the workgroup of the first group touched reads the state ring (it is the
+// only group that can hold positions from earlier calls), and the same workgroup writes the
+// trailing incomplete group into the ring after its reads, so no two workgroups touch the ring.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+
+namespace hyb {
+
+template <typename T>
+__device__ __forceinline__ float2 load_pair(const T* row, int d);
+
+template <>
+__device__ __forceinline__ float2 load_pair<float>(const float* row, int d) {
+  return *reinterpret_cast<const float2*>(row + d);
+}
+
+template <>
+__device__ __forceinline__ float2 load_pair<uint16_t>(const uint16_t* row, int d) {
+  uint32_t v = *reinterpret_cast<const uint32_t*>(row + d);
+  return make_float2(bf16_to_f32(v & 0xffffu), bf16_to_f32(v >> 16));
+}
+
+__device__ __forceinline__ void store_pair(const PoolDev& p, int64_t idx, int d, float a,
+                                           float b) {
+  if (p.dtype == F32) {
+    float* dst = reinterpret_cast<float*>(p.data + idx * p.entry_bytes);
+    *reinterpret_cast<float2*>(dst + d) = make_float2(a, b);
+  } else {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(p.data + idx * p.entry_bytes);
+    *reinterpret_cast<uint32_t*>(dst + d) = pack_bf16x2(a, b);
+  }
+}
+
+// kVec consecutive dims d .. d + kVec - 1 of a row, widened to float (kVec = 4 needs the row
+// 16-byte aligned for float, 8-byte aligned for bf16; kVec = 2 needs 8 / 4 bytes).
+template <typename T, int kVec>
+__device__ __forceinline__ void load_vec(const T* row, int d, float (&v)[kVec]) {
+  if constexpr (kVec == 4) {
+    if constexpr (sizeof(T) == 4) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(row + d);
+      v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+    } else {
+      const uint2 q = *reinterpret_cast<const uint2*>(row + d);
+      v[0] = bf16_to_f32(q.x & 0xffffu); v[1] = bf16_to_f32(q.x >> 16);
+      v[2] = bf16_to_f32(q.y & 0xffffu); v[3] = bf16_to_f32(q.y >> 16);
+    }
+  } else {
+    const float2 q = load_pair<T>(row, d);
+    v[0] = q.x; v[1] = q.y;
+  }
+}
+
+template <int kVec>
+__device__ __forceinline__ void store_f32_vec(float* row, int d, const float (&v)[kVec]) {
+  if constexpr (kVec == 4)
+    *reinterpret_cast<f32x4*>(row + d) = f32x4{v[0], v[1], v[2], v[3]};
+  else
+    *reinterpret_cast<float2*>(row + d) = make_float2(v[0], v[1]);
+}
+
+template <int kVec>
+__device__ __forceinline__ void load_f32_vec(const float* row, int d, float (&v)[kVec]) {
+  if constexpr (kVec == 4) {
+    const f32x4 q = *reinterpret_cast<const f32x4*>(row + d);
+    v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+  } else {
+    const float2 q = *reinterpret_cast<const float2*>(row + d);
+    v[0] = q.x; v[1] = q.y;
+  }
+}
+
+template <int kVec>
+__device__ __forceinline__ void store_vec(const PoolDev& p, int64_t idx, int d,
+                                          const float (&y)[kVec]) {
+  if (p.dtype == F32) {
+    store_f32_vec<kVec>(reinterpret_cast<float*>(p.data + idx * p.entry_bytes), d, y);
+  } else {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(p.data + idx * p.entry_bytes);
+    if constexpr (kVec == 4)
+      *reinterpret_cast<uint2*>(dst + d) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+    else
+      *reinterpret_cast<uint32_t*>(dst + d) = pack_bf16x2(y[0], y[1]);
+  }
+}
+
+// Virtual waves pooling one group: min(ratio, 16), 8 above dim 1024. The rows and the order in
+// which they are added depend only on this count, not on how many waves run them.
+__host__ __device__ inline int pooled_waves(int ratio, int dim) {
+  const int v = dim <= 1024 ? 16 : 8;
+  return ratio < v ? ratio : v;
+}
+
+// One group, pooled by V = pooled_waves(ratio, dim) virtual waves: virtual wave v adds the
+// group's tokens t = v, v + V, ... in ascending order, each lane holding kJ chunks of kVec dims of
+// the row (chunk c = lane + 64 j, so every row load is a coalesced sweep). The calling
+// workgroup's nw = blockDim.x / 64 waves run kV = V / nw virtual waves each (v = w + nw u). All row
+// loads of a batch are issued before the first is used. The partial sums p_v are then added as
+// ((q_0 + q_1) + q_2) + q_3 with q_k = ((p_k + p_{k+4}) + p_{k+8}) + ...: a fixed order whatever
+// nw is (with kV > 1, nw = 4 and wave w forms q_w itself). They meet in LDS behind the one
+// barrier of the group, after which wave 0 normalises with a wave-only reduction, rotates and
+// stores. The RoPE cos / sin of the entry's position (one pair per lane of the last wave) are
+// formed while the row loads are in flight.
+// The group is group gi (counted from the first group the call touches) of sequence b; the rows
+// per virtual wave, ratio / V, are a multiple of kRB, the rows per virtual wave and batch (the
+// launches see to it); lds holds (nw - 1) * dim + 128 floats.
+template <typename T, int kVec, int kJ, int kRB, int kV>
+__device__ __forceinline__ void compress_group(const CompressArgs& a, int gi, int b, float* lds) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int V = nw * kV;
+  const int r = a.out.ratio;
+  const int D = a.out.dim;
+  const int nchunks = D / kVec;
+  const int c0 = a.cu_seqlens[b];
+  const int c1 = a.cu_seqlens[b + 1];
+  const int s0 = a.start_pos[b];   // loaded with the offsets: one round trip, not two
+  const int n_new = c1 - c0;
+  if (n_new <= 0) return;
+  const int t_end = s0 + n_new;
+  const int g0 = s0 / r;
+  const int g_last = (t_end - 1) / r;
+  const int g = g0 + gi;
+  if (g > g_last) return;
+  const int gstart = g * r;
+  const T* x = reinterpret_cast<const T*>(a.x);
+  float2* cs = reinterpret_cast<float2*>(lds + (nw - 1) * D);
+
+  if (gstart + r <= t_end) {  // group complete: emit entry g
+    // block-table entry of the output, loaded now and checked after the barrier
+    const int lb = g / a.out.per_block;
+    const int phys = lb < a.out.max_blocks ? a.out.block_table[(int64_t)b * a.out.max_blocks + lb] : -1;
+    // pooling weights: 1 for the mean (scaled by 1/r at the end), softmax of the logits for the
+    // gate; every wave forms the softmax itself (r <= 128: two logits per lane), behind its first
+    // batch of row loads
+    float e0 = 1.f, e1 = 1.f;
+    float l0 = -INFINITY, l1 = -INFINITY;
+    if (a.mode == 1) {
+      int t = gstart + lane;
+      if (lane < r) l0 = t < s0 ? a.state_logits[(int64_t)b * r + lane] : a.gate[c0 + t - s0];
+      t += 64;
+      if (lane + 64 < r) l1 = t < s0 ? a.state_logits[(int64_t)b * r + lane + 64] : a.gate[c0 + t - s0];
+    }
+
+    float acc[kV][kJ][kVec];
+#pragma unroll
+    for (int u = 0; u < kV; ++u)
+#pragma unroll
+      for (int j = 0; j < kJ; ++j)
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) acc[u][j][e] = 0.f;
+    // Tokens before s0 come from the state ring, the rest from x. Which virtual wave adds which
+    // token, and in what order, depends only on t, so a chunked compression adds the same numbers
+    // in the same order as a one-shot one.
+    const int n_state = max(0, min(s0, gstart + r) - gstart);
+    // chunk offsets of this lane; lanes past the row's end load its last chunk again (so no load
+    // is predicated) and drop it at the end
+    int coff[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) coff[j] = min(lane + 64 * j, nchunks - 1) * kVec;
+    const float* ring = a.state + (int64_t)b * r * D;
+    const T* xs = x + (int64_t)(c0 - s0 + gstart) * D;   // row of token t of the group: xs + t * D
+    // Raw words per chunk. With four-dim chunks a bf16 row is read 16 bytes at a time too: the
+    // lane loads the 8-dim block holding its 4 dims and keeps the half it owns, so that ring rows
+    // and rows of x take the same load and a batch of rows needs no branch between a load and
+    // its use (where branches met, the compiler would wait for every load in flight).
+    using Raw = std::conditional_t<kVec == 4, u32x4, u32x2>;
+    // the RoPE frequency of this lane's pair (last wave), read before the rows
+    const double theta = a.theta[min(lane, 63)];
+    // batch: rows i0 .. i0 + kRB - 1 of each of this wave's virtual waves (row i of virtual wave
+    // v is token v + V i), all loaded before any is added
+    const int rows = r / V;
+    for (int i0 = 0; i0 < rows; i0 += kRB) {
+      Raw rv[kV][kRB][kJ];
+#pragma unroll
+      for (int u = 0; u < kV; ++u)
+#pragma unroll
+        for (int i = 0; i < kRB; ++i) {
+          const int t = w + nw * u + V * (i0 + i);
+          const bool from_ring = t < n_state;
+          if constexpr (sizeof(T) == 4) {
+            const float* row = from_ring ? ring + (int64_t)t * D
+                                         : reinterpret_cast<const float*>(xs) + (int64_t)t * D;
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) rv[u][i][j] = *reinterpret_cast<const Raw*>(row + coff[j]);
+          } else if constexpr (kVec == 4) {
+            const char* row = from_ring ? reinterpret_cast<const char*>(ring + (int64_t)t * D)
+                                        : reinterpret_cast<const char*>(xs + (int64_t)t * D);
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+              const int off = from_ring ? coff[j] * 4 : (coff[j] & ~7) * 2;
+              rv[u][i][j] = *reinterpret_cast<const Raw*>(row + off);
+            }
+          } else {   // pairs of bf16 (kRB == 1, kV == 1)
+            if (from_ring) {
+#pragma unroll
+              for (int j = 0; j < kJ; ++j) rv[u][i][j] = *reinterpret_cast<const Raw*>(ring + (int64_t)t * D + coff[j]);
+            } else {
+#pragma unroll
+              for (int j = 0; j < kJ; ++j)
+                rv[u][i][j] = Raw{*reinterpret_cast<const uint32_t*>(xs + (int64_t)t * D + coff[j]), 0u};
+            }
+          }
+        }
+      if (i0 == 0 && a.mode == 1) {
+        float m0 = l0, m1 = l1;
+        asm volatile("" : "+v"(m0), "+v"(m1));   // keeps the softmax (and its wait) here
+        const float m = wave_max(fmaxf(m0, m1));
+        e0 = lane < r ? expf(m0 - m) : 0.f;
+        e1 = lane + 64 < r ? expf(m1 - m) : 0.f;
+        const float inv = 1.0f / wave_sum(e0 + e1);
+        e0 *= inv;
+        e1 *= inv;
+      }
+      if (i0 == 0 && w == nw - 1 && lane < (a.rope_dim >> 1)) {
+        // here, behind the batch's loads (the empty asm keeps the compiler from hoisting the
+        // math, and the wait for theta, in front of them)
+        double th = theta;
+        asm volatile("" : "+v"(th));
+        float c, s;
+        rope_cs_theta((double)(gstart + r - 1), th, &c, &s);
+        cs[lane] = make_float2(c, s);
+      }
+#pragma unroll
+      for (int u = 0; u < kV; ++u)
+#pragma unroll
+        for (int i = 0; i < kRB; ++i) {
+          const int t = w + nw * u + V * (i0 + i);
+          const bool from_ring = t < n_state;
+          // weight of token t: lane t mod 64 holds it (t is the same on every lane)
+          const float wt = __int_as_float(t < 64 ? __builtin_amdgcn_readlane(__float_as_int(e0), t & 63)
+                                                 : __builtin_amdgcn_readlane(__float_as_int(e1), t & 63));
+#pragma unroll
+          for (int j = 0; j < kJ; ++j) {
+            const Raw q = rv[u][i][j];
+            float val[kVec];
+            if constexpr (sizeof(T) == 4) {
+#pragma unroll
+              for (int e = 0; e < kVec; ++e) val[e] = __uint_as_float(q[e]);
+            } else if constexpr (kVec == 4) {
+              // the words of x holding this lane's dims: the low or high half of the 16 bytes
+              const bool hi = coff[j] & 4;
+              const uint32_t x0 = hi ? q[2] : q[0];
+              const uint32_t x1 = hi ? q[3] : q[1];
+              val[0] = from_ring ? __uint_as_float(q[0]) : bf16_to_f32(x0 & 0xffffu);
+              val[1] = from_ring ? __uint_as_float(q[1]) : bf16_to_f32(x0 >> 16);
+              val[2] = from_ring ? __uint_as_float(q[2]) : bf16_to_f32(x1 & 0xffffu);
+              val[3] = from_ring ? __uint_as_float(q[3]) : bf16_to_f32(x1 >> 16);
+            } else {
+              val[0] = from_ring ? __uint_as_float(q[0]) : bf16_to_f32(q[0] & 0xffffu);
+              val[1] = from_ring ? __uint_as_float(q[1]) : bf16_to_f32(q[0] >> 16);
+            }
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) acc[u][j][e] = fmaf(wt, val[e], acc[u][j][e]);
+          }
+        }
+    }
+    // with several virtual waves per wave (nw = 4), wave w holds p_w, p_{w+4}, ...: its q_w
+#pragma unroll
+    for (int u = 1; u < kV; ++u)
+#pragma unroll
+      for (int j = 0; j < kJ; ++j)
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) acc[0][j][e] += acc[u][j][e];
+    if (w > 0) {
+      float* part = lds + (w - 1) * D;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nchunks) store_f32_vec<kVec>(part, c * kVec, acc[0][j]);
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      const float post = a.mode == 1 ? 1.0f : 1.0f / (float)r;
+      float ss = 0.f;
+      float (&tot)[kJ][kVec] = acc[0];
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nchunks) {
+          // q_k = p_k + p_{k+4} + ... (slot v - 1 holds p_v; with kV > 1 slot k - 1 holds q_k)
+          float qk[4][kVec];
+          const int per = kV > 1 ? 1 : V / 4;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) qk[k][e] = 0.f;
+            for (int m = 0; m < per; ++m) {
+              const int v = k + 4 * m;
+              float p[kVec];
+              if (v == 0) {
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) p[e] = tot[j][e];
+              } else {
+                load_f32_vec<kVec>(lds + (v - 1) * D, c * kVec, p);
+              }
+#pragma unroll
+              for (int e = 0; e < kVec; ++e) qk[k][e] = m == 0 ? p[e] : qk[k][e] + p[e];
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            tot[j][e] = ((qk[0][e] + qk[1][e]) + qk[2][e]) + qk[3][e];
+            tot[j][e] *= post;
+            ss = fmaf(tot[j][e], tot[j][e], ss);
+          }
+        }
+      }
+      ss = wave_sum(ss);
+      const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+      if (phys >= 0 && phys < a.out.num_blocks) {
+        const int64_t idx = (int64_t)phys * a.out.per_block + (g - lb * a.out.per_block);
+        const int rope_lo = D - a.rope_dim;
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+          const int c = lane + 64 * j;
+          if (c < nchunks) {
+            float y[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; e += 2) {
+              float y0 = tot[j][e] * inv, y1 = tot[j][e + 1] * inv;
+              const int d = c * kVec + e;
+              if (d >= rope_lo) {
+                const float2 q = cs[(d - rope_lo) >> 1];
+                const float z0 = y0 * q.x - y1 * q.y;
+                const float z1 = y0 * q.y + y1 * q.x;
+                y0 = z0;
+                y1 = z1;
+              }
+              y[e] = y0;
+              y[e + 1] = y1;
+            }
+            store_vec<kVec>(a.out, idx, c * kVec, y);
+          }
+        }
+      }
+    }
+  }
+
+  if (gi == 0) {
+    // trailing incomplete group -> state ring
+    const int tail_start = g_last * r;
+    if (tail_start + r > t_end) {
+      const int lo = tail_start > s0 ? tail_start : s0;
+      for (int t = lo + w; t < t_end; t += nw) {
+        const int slot = t - tail_start;
+        const T* row = x + (int64_t)(c0 + t - s0) * D;
+        float* dst = a.state + ((int64_t)b * r + slot) * D;
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+          const int c = lane + 64 * j;
+          if (c < nchunks) {
+            float v[kVec];
+            load_vec<T, kVec>(row, c * kVec, v);
+            store_f32_vec<kVec>(dst, c * kVec, v);
+          }
+        }
+        if (a.mode == 1 && lane == 0) a.state_logits[(int64_t)b * r + slot] = a.gate[c0 + t - s0];
+      }
+    }
+  }
+}
+
+}  // namespace hyb

@@ -129,6 +129,26 @@ int check_compress_common(const char* op, const void* x, int32_t x_dtype,
   return HYB_OK;
 }
 
+int check_compress(const char* op, const hyb_compress_call& c, hyb::CompressArgs* a) {
+  HYB_TRY(check_compress_common(op, c.x, c.x_dtype, c.cu_seqlens, c.start_pos, c.batch,
+                                c.max_new_tokens));
+  if (!c.state) return fail(HYB_EINVAL, "%s: state is NULL", op);
+  if (c.mode != HYB_POOL_MEAN && c.mode != HYB_POOL_SOFTMAX_GATE)
+    return fail(HYB_EINVAL, "%s: mode %d unknown", op, c.mode);
+  if (c.mode == HYB_POOL_SOFTMAX_GATE && (!c.gate_logits || !c.state_logits))
+    return fail(HYB_EINVAL, "%s: softmax-gate pooling needs gate_logits and state_logits", op);
+  if (!(c.eps >= 0.f) || !std::isfinite(c.eps)) return fail(HYB_EINVAL, "%s: eps must be >= 0", op);
+  hyb::PoolDev po{};
+  HYB_TRY(check_pool(c.out, op, "out", false, false, 2 | 4, &po));
+  if (po.dim > 2048) return fail(HYB_ENOTSUP, "%s: dim %d > 2048", op, po.dim);
+  HYB_TRY(check_rope(op, c.rope_dim, c.rope_base, po.dim));
+  *a = hyb::CompressArgs{c.x, c.x_dtype, c.gate_logits, c.cu_seqlens, c.start_pos, c.batch,
+                         c.max_new_tokens, c.state, c.state_logits, c.mode, po, c.rope_dim,
+                         c.rope_base, c.eps, {}};
+  fill_theta(a, c.rope_dim, c.rope_base);
+  return HYB_OK;
+}
+
 struct AttnCommon {
   hyb::AttnArgs args;
   hyb::AttnPlan plan;
@@ -237,20 +257,12 @@ int32_t hyb_compress(const void* x, int32_t x_dtype, const float* gate_logits,
                      const hyb_paged* out, int32_t rope_dim, double rope_base, float eps,
                      void* stream) {
   const char* op = "hyb_compress";
-  HYB_TRY(check_compress_common(op, x, x_dtype, cu_seqlens, start_pos, batch, max_new_tokens));
-  if (!state) return fail(HYB_EINVAL, "%s: state is NULL", op);
-  if (mode != HYB_POOL_MEAN && mode != HYB_POOL_SOFTMAX_GATE) return fail(HYB_EINVAL, "%s: mode %d unknown", op, mode);
-  if (mode == HYB_POOL_SOFTMAX_GATE && (!gate_logits || !state_logits))
-    return fail(HYB_EINVAL, "%s: softmax-gate pooling needs gate_logits and state_logits", op);
-  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(HYB_EINVAL, "%s: eps must be >= 0", op);
-  hyb::PoolDev po{};
-  HYB_TRY(check_pool(out, op, "out", false, false, 2 | 4, &po));
-  if (po.dim > 2048) return fail(HYB_ENOTSUP, "%s: dim %d > 2048", op, po.dim);
-  HYB_TRY(check_rope(op, rope_dim, rope_base, po.dim));
+  const hyb_compress_call call{x, x_dtype, gate_logits, cu_seqlens, start_pos, batch,
+                               max_new_tokens, state, state_logits, mode, out, rope_dim,
+                               rope_base, eps};
+  hyb::CompressArgs a;
+  HYB_TRY(check_compress(op, call, &a));
   if (batch == 0 || max_new_tokens == 0) return HYB_OK;
-  hyb::CompressArgs a{x, x_dtype, gate_logits, cu_seqlens, start_pos, batch, max_new_tokens,
-                      state, state_logits, mode, po, rope_dim, rope_base, eps, {}};
-  fill_theta(&a, rope_dim, rope_base);
   return launch_status(hyb::launch_compress(a, static_cast<hipStream_t>(stream)), op);
 }
 
@@ -473,6 +485,29 @@ int32_t hyb_attn_decode(const void* q, int32_t q_dtype, const int32_t* seq_lens,
   if (batch == 0) return HYB_OK;
   c.args.qd = hyb::QueryDev{seq_lens, nullptr, nullptr};
   return launch_status(hyb::launch_attention(c.args, static_cast<hipStream_t>(stream)), op);
+}
+
+int32_t hyb_attn_decode_compress(const void* q, int32_t q_dtype, const int32_t* seq_lens,
+                                 int32_t batch, int32_t n_heads, int32_t max_seq_len,
+                                 const hyb_paged* swa, const hyb_paged* comp,
+                                 const int32_t* topk_idx, int32_t k, int32_t window,
+                                 float softmax_scale, int32_t rope_dim, double rope_base,
+                                 void* out, int32_t out_dtype, void* workspace,
+                                 size_t workspace_bytes, const hyb_compress_call* compress,
+                                 void* stream) {
+  const char* op = "hyb_attn_decode_compress";
+  if (!seq_lens) return fail(HYB_EINVAL, "%s: seq_lens is NULL", op);
+  if (max_seq_len < 1) return fail(HYB_EINVAL, "%s: max_seq_len %d < 1", op, max_seq_len);
+  if (!compress) return fail(HYB_EINVAL, "%s: compress is NULL", op);
+  AttnCommon c;
+  HYB_TRY(check_attention(op, q, q_dtype, batch, n_heads, swa, comp, topk_idx, k, window,
+                          softmax_scale, rope_dim, rope_base, out, out_dtype,
+                          (int64_t)max_seq_len - 1, &c));
+  HYB_TRY(attach_workspace(op, &c, workspace, workspace_bytes));
+  hyb::CompressArgs ca;
+  HYB_TRY(check_compress(op, *compress, &ca));
+  c.args.qd = hyb::QueryDev{seq_lens, nullptr, nullptr};
+  return launch_status(hyb::launch_attention_compress(c.args, ca, static_cast<hipStream_t>(stream)), op);
 }
 
 size_t hyb_attn_prefill_workspace_bytes(int32_t n_q, int32_t n_heads, int32_t dim,

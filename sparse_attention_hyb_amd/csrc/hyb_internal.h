@@ -142,5 +142,6 @@ struct AttnPlan {
 AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_keys,
                         int32_t q_dtype, int32_t pool_dtype);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_compress(const AttnArgs& a, const CompressArgs& c, hipStream_t s);
 
 }  // namespace hyb

@@ -20,8 +20,6 @@
 
 namespace hyb {
 
-typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
-
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 

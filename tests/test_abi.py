@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(hyb.EXPORTS) == names
@@ -81,6 +81,36 @@ def decode(lib, swa=None, comp=None, q_dtype=hyb.BF16, topk=None, k=0, window=12
 def test_attn_decode_validation(lib, kw, code):
     assert decode(lib, **kw) == code
     assert lib.hyb_last_error().decode().startswith("hyb_attn_decode")
+
+
+def test_attn_decode_compress_validation(lib):
+    """The fused entry point checks the attention arguments, then the compressor's, before any
+    launch (every case here fails in host code)."""
+    out = pool(ratio=128)
+
+    def call(swa=None, comp=None, ccall=True, mode=hyb.POOL_MEAN, o=out, rope=64, ws=1 << 40,
+             eps=1e-6, state=FAKE):
+        swa = swa or pool(ratio=1)
+        comp = comp or pool(ratio=128)
+        cc = hyb.hyb_compress_call(x=FAKE, x_dtype=hyb.BF16, gate_logits=None, cu_seqlens=FAKE,
+                                   start_pos=FAKE, batch=4, max_new_tokens=1, state=state,
+                                   state_logits=None, mode=mode, out=ctypes.pointer(o),
+                                   rope_dim=rope, rope_base=1e4, eps=eps)
+        return lib.hyb_attn_decode_compress(FAKE, hyb.BF16, FAKE, 4, 64, 1000, ctypes.byref(swa),
+                                            ctypes.byref(comp), None, 0, 128, 0.04, 64, 1e4,
+                                            FAKE, hyb.BF16, FAKE, ws,
+                                            ctypes.byref(cc) if ccall else None, None)
+
+    assert call(ccall=False) == hyb.HYB_EINVAL                        # compressor call required
+    assert call(swa=pool(ratio=4)) == hyb.HYB_EINVAL                  # attention checked first
+    assert call(ws=16) == hyb.HYB_EWORKSPACE
+    assert call(state=None) == hyb.HYB_EINVAL
+    assert call(mode=hyb.POOL_SOFTMAX_GATE) == hyb.HYB_EINVAL         # logits missing
+    assert call(o=pool(ratio=1)) == hyb.HYB_EINVAL
+    assert call(o=pool(ratio=128, dtype=hyb.FP8_E4M3)) == hyb.HYB_ENOTSUP
+    assert call(rope=3) == hyb.HYB_EINVAL
+    assert call(eps=-1.0) == hyb.HYB_EINVAL
+    assert lib.hyb_last_error().decode().startswith("hyb_attn_decode_compress")
 
 
 def test_attn_workspace_sizes(lib):

@@ -544,3 +544,72 @@ def test_block_placement_and_determinism(gpu_lib):
     sync()
     assert torch.equal(t1, t1b) and torch.equal(o1, o1b)
     assert torch.equal(t1, t2) and torch.equal(o1, o2)
+
+
+# ====================================================== attention with the compressor alongside
+def _clone_pool(p):
+    return W.PagedTensors(p.data.clone(), None if p.scale is None else p.scale.clone(),
+                          p.block_table, p.dtype, p.dim, p.ratio)
+
+
+@pytest.mark.parametrize("case", ["c4_bf16", "c128_gate_bf16", "c4_f32x", "c4_unaligned_x"])
+def test_attn_decode_compress_equals_two_calls(gpu_lib, case):
+    """hyb_attn_decode_compress leaves exactly what hyb_attn_decode then hyb_compress leave: the
+    attention output, every pool byte, the state ring and its logits. The compressor runs beside
+    the combine (bf16 / f32 x) or after it (x not 16-byte aligned); sequences complete a group or
+    only extend the ring."""
+    hyb = gpu_lib
+    g = W.generator(91, ["c4_bf16", "c128_gate_bf16", "c4_f32x", "c4_unaligned_x"].index(case), 0, DEV)
+    if case.startswith("c4"):
+        lens = [4096, 4097, 4098, 4099, 131072, 9000]
+        wl = W.sparse_decode(DEV, seed=5, batch=len(lens), ctx=lens)
+        topk = gpu_topk(hyb, wl)
+        r, gate = 4, False
+    else:
+        lens = [2048, 5000, 65536, 131072]
+        wl = W.dense_decode(DEV, seed=5, batch=len(lens), ctx=lens)
+        topk, r, gate = None, 128, True
+    B, D = wl.batch, wl.dim
+    x = W.randn((B, D), g, DEV)
+    if case == "c4_unaligned_x":
+        buf = torch.zeros(B * D + 16, dtype=torch.bfloat16, device=DEV)
+        x_use = buf[4:4 + B * D].view(B, D)          # 8-byte but not 16-byte aligned
+        x_use.copy_(x.to(torch.bfloat16))
+        assert x_use.data_ptr() % 16 != 0
+    else:
+        x_use = x if case == "c4_f32x" else W.to_storage(x, "bf16")
+    cu = torch.arange(0, B + 1, dtype=I32, device=DEV)
+    start = (wl.seq_lens - 1).contiguous()
+    state = W.randn((B, r, D), g, DEV)
+    st_l = W.randn((B, r), g, DEV) if gate else None
+    gl = W.randn((B,), g, DEV) if gate else None
+    runs = []
+    for fused in (False, True):
+        comp, swa = _clone_pool(wl.comp), wl.swa
+        stt, stl = state.clone(), None if st_l is None else st_l.clone()
+        out = torch.empty_like(wl.q)
+        kw = dict(topk_idx=topk, k=wl.k if topk is not None else 0, window=wl.window,
+                  rope_dim=wl.rope_dim, rope_base=wl.rope_base)
+        if fused:
+            hyb.hyb_attn_decode_compress(wl.q, wl.seq_lens, wl.max_seq_len, swa, comp, out, x_use,
+                                         cu, start, 1, stt, comp, eps=1e-6, gate_logits=gl,
+                                         state_logits=stl, **kw)
+        else:
+            hyb.hyb_attn_decode(wl.q, wl.seq_lens, wl.max_seq_len, swa, comp, out, **kw)
+            hyb.hyb_compress(x_use, cu, start, 1, stt, comp, wl.rope_dim, wl.rope_base, eps=1e-6,
+                             gate_logits=gl, state_logits=stl)
+        runs.append((out, comp.data, stt, stl))
+    sync()
+    (o0, c0, s0, l0), (o1, c1, s1, l1) = runs
+    assert torch.equal(o0, o1)
+    assert torch.equal(c0, c1)
+    assert torch.equal(s0, s1)
+    if gate:
+        assert torch.equal(l0, l1)
+    # the call did write: every completed group's entry differs from the pool it started from
+    for b, L in enumerate(lens):
+        if L % r == 0:
+            gidx = (L - 1) // r
+            lb, slot = gidx // (256 // r), gidx % (256 // r)
+            phys = int(wl.comp.block_table[b, lb])
+            assert not torch.equal(c1[phys, slot], wl.comp.data[phys, slot])
