@@ -116,7 +116,7 @@ def c4_sparse(torch, hyb, W, BM, args):
             x_new=W.to_storage(W.randn((B, 512), g, dev), "bf16"),
             cu=torch.arange(0, B + 1, dtype=torch.int32, device=dev),
             start=torch.full((B,), L - 1, dtype=torch.int32, device=dev),
-            state=W.randn((B, 4, 512), g, dev),
+            state=W.to_storage(W.randn((B, 4, 512), g, dev), "bf16"),   # ring in x's dtype
         ))
 
     def step(r, ev):
@@ -155,7 +155,7 @@ def c128_dense(torch, hyb, W, BM, args):
     R = 4
     dev = "cuda"
     wl0 = W.dense_decode(dev, seed=0, fill_comp=False)
-    state = torch.zeros(B, 128, D, device=dev)
+    state = torch.zeros(B, 128, D, dtype=torch.bfloat16, device=dev)   # ring in x's dtype
     st_l = torch.zeros(B, 128, device=dev)
     cu = torch.arange(0, (B + 1) * W.RAW_CHUNK, W.RAW_CHUNK, dtype=torch.int32, device=dev)
     comp_secs = 0.0
@@ -181,7 +181,7 @@ def c128_dense(torch, hyb, W, BM, args):
                   ws=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, D, L, 128, 0), dtype=torch.uint8, device=dev),
                   x_new=W.to_storage(W.randn((B, D), g, dev), "bf16"),
                   lg_new=W.randn((B,), g, dev),
-                  state=W.randn((B, 128, D), g, dev), st_l=W.randn((B, 128), g, dev),
+                  state=W.to_storage(W.randn((B, 128, D), g, dev), "bf16"), st_l=W.randn((B, 128), g, dev),
                   cu=torch.arange(0, B + 1, dtype=torch.int32, device=dev),
                   start=torch.full((B,), L - 1, dtype=torch.int32, device=dev)) for w in reps]
 
@@ -220,8 +220,9 @@ def prefill(torch, hyb, W, BM, args):
     wl = W.chunked_prefill(dev, seed=0)
     D, n = wl.q.shape[2], wl.n_new
     cu, st = torch.tensor([0, n], dtype=torch.int32, device=dev), torch.tensor([wl.prior], dtype=torch.int32, device=dev)
-    s4 = torch.zeros(1, 4, D, device=dev)
-    s128, l128 = torch.zeros(1, 128, D, device=dev), torch.zeros(1, 128, device=dev)
+    s4 = torch.zeros(1, 4, D, dtype=wl.x_new.dtype, device=dev)   # rings in x's dtype
+    s128 = torch.zeros(1, 128, D, dtype=wl.x_new.dtype, device=dev)
+    l128 = torch.zeros(1, 128, device=dev)
     max_pos = wl.prior + n - 1
     topk = torch.empty(n, wl.k, dtype=torch.int32, device=dev)
     out = torch.empty_like(wl.q)
@@ -323,7 +324,7 @@ def cpu_baseline(torch, W, BM, rep, budget):
     q = wl.q.cpu().double().numpy()
     iq, iw = wl.idx_q.cpu().double().numpy(), wl.idx_w.cpu().double().numpy()
     x_new = rep["x_new"].cpu().double().numpy()
-    state = rep["state"].cpu().double().numpy()
+    state = rep["state"].float().cpu().double().numpy()
     scale = 1.0 / math.sqrt(wl.dim)
     done = 0
     t0 = time.perf_counter()

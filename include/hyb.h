@@ -119,14 +119,14 @@ const char* hyb_last_error(void);
  *   cu_seqlens    int32 [batch + 1], non-decreasing, cu_seqlens[0] = 0
  *   start_pos     int32 [batch], position of each sequence's first new token
  *   max_new_tokens host bound on cu_seqlens[b+1] - cu_seqlens[b] (sizes the grid)
- *   state         float [batch][ratio][dim] raw tokens of the in-progress group
+ *   state         [batch][ratio][dim] in x_dtype: raw tokens of the in-progress group
  *   state_logits  float [batch][ratio] (gate mode), NULL for mean
  *   out           host descriptor of the C4 / C128 pool (ratio 4 or 128, dtype F32 or BF16,
  *                 dim = x's dim, block_table rows indexed by b)
  * ------------------------------------------------------------------------------------------ */
 int32_t hyb_compress(const void* x, int32_t x_dtype, const float* gate_logits,
                      const int32_t* cu_seqlens, const int32_t* start_pos, int32_t batch,
-                     int32_t max_new_tokens, float* state, float* state_logits, int32_t mode,
+                     int32_t max_new_tokens, void* state, float* state_logits, int32_t mode,
                      const hyb_paged* out, int32_t rope_dim, double rope_base, float eps,
                      void* stream);
 
@@ -140,7 +140,7 @@ typedef struct hyb_compress_call {
   const int32_t* start_pos;
   int32_t batch;
   int32_t max_new_tokens;
-  float* state;
+  void* state;
   float* state_logits;
   int32_t mode;
   const hyb_paged* out;

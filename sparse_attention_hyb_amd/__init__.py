@@ -156,6 +156,11 @@ def paged(pool) -> hyb_paged:
         num_blocks=int(pool.data.shape[0]), max_blocks=int(pool.block_table.shape[1]), reserved=0)
 
 
+def _check_state(x, state) -> None:
+    if state.dtype != x.dtype:
+        raise TypeError(f"state ring dtype {state.dtype} must be x's dtype {x.dtype}")
+
+
 def _empty_workspace(nbytes: int, device):
     import torch
     return torch.empty(max(1, int(nbytes)), dtype=torch.uint8, device=device)
@@ -169,7 +174,9 @@ def hyb_abi_version() -> int:
 def hyb_compress(x, cu_seqlens, start_pos, max_new_tokens: int, state, out_pool, rope_dim: int,
                  rope_base: float = 10000.0, eps: float = 1e-6, gate_logits=None,
                  state_logits=None, stream=None) -> None:
-    """Compressor: see hyb_compress in include/hyb.h. Mean pooling unless gate_logits is given."""
+    """Compressor: see hyb_compress in include/hyb.h. Mean pooling unless gate_logits is given.
+    The state ring holds raw tokens in x's dtype."""
+    _check_state(x, state)
     mode = POOL_SOFTMAX_GATE if gate_logits is not None else POOL_MEAN
     d = paged(out_pool)
     _check(load().hyb_compress(_ptr(x), _tdtype(x), _ptr(gate_logits), _ptr(cu_seqlens),
@@ -279,6 +286,7 @@ def hyb_attn_decode_compress(q, seq_lens, max_seq_len: int, swa_pool, comp_pool,
                              state_logits=None, workspace=None, stream=None) -> None:
     """hyb_attn_decode(q, ...) then hyb_compress(x, ...) in one call (see include/hyb.h); both
     use rope_dim and rope_base."""
+    _check_state(x, state)
     b, h, dim = (int(s) for s in q.shape)
     if topk_idx is not None and not k:
         k = int(topk_idx.shape[1])

@@ -856,7 +856,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int hpw) {
 
 // The combine of the MFMA kernel's splits with a compressor call riding along: workgroups
 // [0, n_comb) combine (mapped as attn_combine's), the rest each pool one compressor group with
-// four waves (float or bf16 x, dim <= 512 in four-dim chunks). The compressor's latency then hides
+// four waves (float or bf16 x, dim <= 512 in 16-byte chunks). The compressor's latency then hides
 // behind the combine instead of taking a launch of its own. Nothing here orders the two: the
 // caller guarantees that neither reads what the other writes.
 template <typename T, int kRB, int kV>
@@ -870,7 +870,8 @@ __global__ __launch_bounds__(256, 4) void attn_combine_compress(AttnArgs a, int 
     combine_group<uint16_t>(a, hpw, xcd_logical(bid, n_comb), gx, csm);
   } else {
     const int k = bid - n_comb;
-    compress_group<T, 4, 2, kRB, kV>(c, k % comp_gx, k / comp_gx, csm);
+    constexpr int kVec = 16 / (int)sizeof(T);   // 16-byte chunks: dim <= 512 is one or two per lane
+    compress_group<T, kVec, 512 / kVec / 64, kRB, kV>(c, k % comp_gx, k / comp_gx, csm);
   }
 }
 
@@ -971,8 +972,8 @@ hipError_t launch_attention_compress(const AttnArgs& a, const CompressArgs& c, h
   const dim3 grid(n_comb + comp_gx * c.batch);
   const size_t lds = std::max(combine_lds_bytes(a.n_split), (size_t)(3 * D + 128) * sizeof(float));
   // four waves run pooled_waves(r, D) virtual waves: 4 (r = 4) or 16 (r = 128, D <= 512); at
-  // r = 128 a batch holds two rows of each of a wave's four virtual waves (the kernel keeps to
-  // 128 registers, so that four of its workgroups fit on a compute unit)
+  // r = 128 a batch holds two (float) or four (bf16) rows of each of a wave's four virtual waves
+  // (the kernel keeps to 128 registers, so that four of its workgroups fit on a compute unit)
   if (c.x_dtype == F32) {
     if (r == 4)
       hipLaunchKernelGGL((attn_combine_compress<float, 1, 1>), grid, dim3(256), lds, s, a, hpw, gx, n_comb, c, comp_gx);
@@ -982,7 +983,7 @@ hipError_t launch_attention_compress(const AttnArgs& a, const CompressArgs& c, h
     if (r == 4)
       hipLaunchKernelGGL((attn_combine_compress<uint16_t, 1, 1>), grid, dim3(256), lds, s, a, hpw, gx, n_comb, c, comp_gx);
     else
-      hipLaunchKernelGGL((attn_combine_compress<uint16_t, 2, 4>), grid, dim3(256), lds, s, a, hpw, gx, n_comb, c, comp_gx);
+      hipLaunchKernelGGL((attn_combine_compress<uint16_t, 4, 4>), grid, dim3(256), lds, s, a, hpw, gx, n_comb, c, comp_gx);
   }
   return hipGetLastError();
 }

@@ -54,9 +54,10 @@ namespace {
 template <typename T, int kVec, int kJ>
 hipError_t launch_compress_t(const CompressArgs& a, int rows_per_wave, dim3 grid, dim3 block,
                              size_t lds, hipStream_t s) {
-  // rows per batch and wave: 64 words of loads in flight per lane; one row above dim 512, and
-  // for bf16 pairs (whose ring and x rows take different loads)
-  constexpr int kRB = (kJ * kVec >= 32 || (sizeof(T) == 2 && kVec == 2)) ? 1 : 64 / (kJ * kVec);
+  // rows per batch and virtual wave: up to 64 words of loads in flight per lane and 8 rows for
+  // rows of up to 8 words, fewer for wider rows (whose accumulators take registers too)
+  constexpr int kWords = kJ * chunk_words<T, kVec>();
+  constexpr int kRB = kWords >= 32 ? 1 : (kWords >= 16 ? 2 : (64 / kWords > 8 ? 8 : 64 / kWords));
   if (rows_per_wave % kRB == 0)
     hipLaunchKernelGGL((compress_kernel<T, kVec, kJ, kRB>), grid, block, lds, s, a);
   else
@@ -65,32 +66,34 @@ hipError_t launch_compress_t(const CompressArgs& a, int rows_per_wave, dim3 grid
 }
 
 template <typename T>
-hipError_t launch_compress_x(const CompressArgs& a, bool v4, int rows_per_wave, dim3 grid,
+hipError_t launch_compress_x(const CompressArgs& a, bool wide, int rows_per_wave, dim3 grid,
                              dim3 block, size_t lds, hipStream_t s) {
-  const int D = a.out.dim;
-  if (v4) return D <= 512 ? launch_compress_t<T, 4, 2>(a, rows_per_wave, grid, block, lds, s)
-                          : launch_compress_t<T, 4, 8>(a, rows_per_wave, grid, block, lds, s);
-  return D <= 512 ? launch_compress_t<T, 2, 4>(a, rows_per_wave, grid, block, lds, s)
-                  : launch_compress_t<T, 2, 16>(a, rows_per_wave, grid, block, lds, s);
+  constexpr int kWide = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+  const bool small = a.out.dim <= 512;
+  if (wide) return small ? launch_compress_t<T, kWide, 512 / kWide / 64>(a, rows_per_wave, grid, block, lds, s)
+                         : launch_compress_t<T, kWide, 2048 / kWide / 64>(a, rows_per_wave, grid, block, lds, s);
+  return small ? launch_compress_t<T, 2, 4>(a, rows_per_wave, grid, block, lds, s)
+               : launch_compress_t<T, 2, 16>(a, rows_per_wave, grid, block, lds, s);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 }  // namespace
 
 // dim <= 2048, ratio 4 or 128. One wave per virtual wave of the group (min(ratio, 16), 8 above
-// dim 1024, so the partials fit in 60 KB of LDS). Four-dim chunks when x, the state ring and the pool are 16-byte
-// aligned and dim % 4 == 0 (float x) or dim % 8 == 0 (bf16 x), else pairs.
+// dim 1024, so the partials fit in 60 KB of LDS). 16-byte chunks (four floats or eight bf16)
+// when x, the state ring and the pool are 16-byte aligned and a row is a whole number of
+// chunks, else element pairs.
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   const int r = a.out.ratio;
   const int D = a.out.dim;
   const int nw = pooled_waves(r, D);
-  const bool v4 = D % (a.x_dtype == F32 ? 4 : 8) == 0 && aligned16(a.x) && aligned16(a.state) &&
-                  aligned16(a.out.data);
+  const bool wide = D % (a.x_dtype == F32 ? 4 : 8) == 0 && aligned16(a.x) && aligned16(a.state) &&
+                    aligned16(a.out.data);
   const dim3 grid((a.max_new_tokens + r - 1) / r + 1, a.batch);
   const dim3 block(64 * nw);
   const size_t lds = ((size_t)(nw - 1) * D + 128) * sizeof(float);
-  return a.x_dtype == F32 ? launch_compress_x<float>(a, v4, r / nw, grid, block, lds, s)
-                          : launch_compress_x<uint16_t>(a, v4, r / nw, grid, block, lds, s);
+  return a.x_dtype == F32 ? launch_compress_x<float>(a, wide, r / nw, grid, block, lds, s)
+                          : launch_compress_x<uint16_t>(a, wide, r / nw, grid, block, lds, s);
 }
 
 hipError_t launch_swa_insert(const CompressArgs& a, hipStream_t s) {

@@ -8,9 +8,11 @@
 //
 // Layout of the work: one workgroup per (group touched, sequence). A group's r raw tokens are
 // read once (each row by one wave: coalesced), pooled in float32 registers, normalised, rotated
-// and stored once. Only the workgroup of the first group touched reads the state ring (it is the
-// only group that can hold positions from earlier calls), and the same workgroup writes the
-// trailing incomplete group into the ring after its reads, so no two workgroups touch the ring.
+// and stored once. The state ring holds the raw tokens of the group in progress in x's own
+// storage type (they are copies of x). Only the workgroup of the first group touched reads the
+// ring (it is the only group that can hold positions from earlier calls), and the same workgroup
+// writes the trailing incomplete group into the ring after its reads, so no two workgroups touch
+// the ring.
 #pragma once
 
 #include <type_traits>
@@ -44,55 +46,88 @@ __device__ __forceinline__ void store_pair(const PoolDev& p, int64_t idx, int d,
   }
 }
 
-// kVec consecutive dims d .. d + kVec - 1 of a row, widened to float (kVec = 4 needs the row
-// 16-byte aligned for float, 8-byte aligned for bf16; kVec = 2 needs 8 / 4 bytes).
+// A chunk of kVec consecutive elements of a row of T, as raw 32-bit words: 16 bytes in the
+// four-word form (four floats or eight bf16), else two or one words (element pairs).
 template <typename T, int kVec>
-__device__ __forceinline__ void load_vec(const T* row, int d, float (&v)[kVec]) {
-  if constexpr (kVec == 4) {
-    if constexpr (sizeof(T) == 4) {
-      const f32x4 q = *reinterpret_cast<const f32x4*>(row + d);
-      v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
-    } else {
-      const uint2 q = *reinterpret_cast<const uint2*>(row + d);
-      v[0] = bf16_to_f32(q.x & 0xffffu); v[1] = bf16_to_f32(q.x >> 16);
-      v[2] = bf16_to_f32(q.y & 0xffffu); v[3] = bf16_to_f32(q.y >> 16);
-    }
+constexpr int chunk_words() {
+  return kVec * (int)sizeof(T) / 4;
+}
+
+template <typename T, int kVec>
+__device__ __forceinline__ void load_words(const T* row, int d,
+                                           uint32_t (&w)[chunk_words<T, kVec>()]) {
+  constexpr int kW = chunk_words<T, kVec>();
+  if constexpr (kW == 4) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(row + d);
+    w[0] = q[0]; w[1] = q[1]; w[2] = q[2]; w[3] = q[3];
+  } else if constexpr (kW == 2) {
+    const u32x2 q = *reinterpret_cast<const u32x2*>(row + d);
+    w[0] = q[0]; w[1] = q[1];
   } else {
-    const float2 q = load_pair<T>(row, d);
-    v[0] = q.x; v[1] = q.y;
+    w[0] = *reinterpret_cast<const uint32_t*>(row + d);
   }
 }
 
+template <typename T, int kVec>
+__device__ __forceinline__ void store_words(T* row, int d,
+                                            const uint32_t (&w)[chunk_words<T, kVec>()]) {
+  constexpr int kW = chunk_words<T, kVec>();
+  if constexpr (kW == 4)
+    *reinterpret_cast<u32x4*>(row + d) = u32x4{w[0], w[1], w[2], w[3]};
+  else if constexpr (kW == 2)
+    *reinterpret_cast<u32x2*>(row + d) = u32x2{w[0], w[1]};
+  else
+    *reinterpret_cast<uint32_t*>(row + d) = w[0];
+}
+
+// element e of a chunk held as raw words
+template <typename T>
+__device__ __forceinline__ float word_elem(const uint32_t* w, int e) {
+  if constexpr (sizeof(T) == 4) return __uint_as_float(w[e]);
+  else return bf16_to_f32((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+}
+
+// kVec floats at d (LDS partials)
 template <int kVec>
 __device__ __forceinline__ void store_f32_vec(float* row, int d, const float (&v)[kVec]) {
-  if constexpr (kVec == 4)
-    *reinterpret_cast<f32x4*>(row + d) = f32x4{v[0], v[1], v[2], v[3]};
-  else
-    *reinterpret_cast<float2*>(row + d) = make_float2(v[0], v[1]);
+#pragma unroll
+  for (int e = 0; e < kVec; e += (kVec >= 4 ? 4 : 2)) {
+    if constexpr (kVec >= 4)
+      *reinterpret_cast<f32x4*>(row + d + e) = f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
+    else
+      *reinterpret_cast<float2*>(row + d + e) = make_float2(v[e], v[e + 1]);
+  }
 }
 
 template <int kVec>
 __device__ __forceinline__ void load_f32_vec(const float* row, int d, float (&v)[kVec]) {
-  if constexpr (kVec == 4) {
-    const f32x4 q = *reinterpret_cast<const f32x4*>(row + d);
-    v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
-  } else {
-    const float2 q = *reinterpret_cast<const float2*>(row + d);
-    v[0] = q.x; v[1] = q.y;
+#pragma unroll
+  for (int e = 0; e < kVec; e += (kVec >= 4 ? 4 : 2)) {
+    if constexpr (kVec >= 4) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(row + d + e);
+      v[e] = q[0]; v[e + 1] = q[1]; v[e + 2] = q[2]; v[e + 3] = q[3];
+    } else {
+      const float2 q = *reinterpret_cast<const float2*>(row + d + e);
+      v[e] = q.x; v[e + 1] = q.y;
+    }
   }
 }
 
+// kVec outputs at dim d of pool entry idx
 template <int kVec>
 __device__ __forceinline__ void store_vec(const PoolDev& p, int64_t idx, int d,
                                           const float (&y)[kVec]) {
   if (p.dtype == F32) {
     store_f32_vec<kVec>(reinterpret_cast<float*>(p.data + idx * p.entry_bytes), d, y);
   } else {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(p.data + idx * p.entry_bytes);
-    if constexpr (kVec == 4)
-      *reinterpret_cast<uint2*>(dst + d) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+    uint16_t* dst = reinterpret_cast<uint16_t*>(p.data + idx * p.entry_bytes) + d;
+    if constexpr (kVec == 8)
+      *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                             pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+    else if constexpr (kVec == 4)
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
     else
-      *reinterpret_cast<uint32_t*>(dst + d) = pack_bf16x2(y[0], y[1]);
+      *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(y[0], y[1]);
   }
 }
 
@@ -106,8 +141,9 @@ __host__ __device__ inline int pooled_waves(int ratio, int dim) {
 // One group, pooled by V = pooled_waves(ratio, dim) virtual waves: virtual wave v adds the
 // group's tokens t = v, v + V, ... in ascending order, each lane holding kJ chunks of kVec dims of
 // the row (chunk c = lane + 64 j, so every row load is a coalesced sweep). The calling
-// workgroup's nw = blockDim.x / 64 waves run kV = V / nw virtual waves each (v = w + nw u). All row
-// loads of a batch are issued before the first is used. The partial sums p_v are then added as
+// workgroup's nw = blockDim.x / 64 waves run kV = V / nw virtual waves each (v = w + nw u). Rows
+// of the ring and of x have the same storage type and take the same load; all row loads of a
+// batch are issued before the first is used. The partial sums p_v are then added as
 // ((q_0 + q_1) + q_2) + q_3 with q_k = ((p_k + p_{k+4}) + p_{k+8}) + ...: a fixed order whatever
 // nw is (with kV > 1, nw = 4 and wave w forms q_w itself). They meet in LDS behind the one
 // barrier of the group, after which wave 0 normalises with a wave-only reduction, rotates and
@@ -118,6 +154,7 @@ __host__ __device__ inline int pooled_waves(int ratio, int dim) {
 // launches see to it); lds holds (nw - 1) * dim + 128 floats.
 template <typename T, int kVec, int kJ, int kRB, int kV>
 __device__ __forceinline__ void compress_group(const CompressArgs& a, int gi, int b, float* lds) {
+  constexpr int kW = chunk_words<T, kVec>();
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
@@ -137,6 +174,7 @@ __device__ __forceinline__ void compress_group(const CompressArgs& a, int gi, in
   if (g > g_last) return;
   const int gstart = g * r;
   const T* x = reinterpret_cast<const T*>(a.x);
+  T* ring = reinterpret_cast<T*>(a.state) + (int64_t)b * r * D;
   float2* cs = reinterpret_cast<float2*>(lds + (nw - 1) * D);
 
   if (gstart + r <= t_end) {  // group complete: emit entry g
@@ -171,49 +209,22 @@ __device__ __forceinline__ void compress_group(const CompressArgs& a, int gi, in
     int coff[kJ];
 #pragma unroll
     for (int j = 0; j < kJ; ++j) coff[j] = min(lane + 64 * j, nchunks - 1) * kVec;
-    const float* ring = a.state + (int64_t)b * r * D;
     const T* xs = x + (int64_t)(c0 - s0 + gstart) * D;   // row of token t of the group: xs + t * D
-    // Raw words per chunk. With four-dim chunks a bf16 row is read 16 bytes at a time too: the
-    // lane loads the 8-dim block holding its 4 dims and keeps the half it owns, so that ring rows
-    // and rows of x take the same load and a batch of rows needs no branch between a load and
-    // its use (where branches met, the compiler would wait for every load in flight).
-    using Raw = std::conditional_t<kVec == 4, u32x4, u32x2>;
     // the RoPE frequency of this lane's pair (last wave), read before the rows
     const double theta = a.theta[min(lane, 63)];
     // batch: rows i0 .. i0 + kRB - 1 of each of this wave's virtual waves (row i of virtual wave
     // v is token v + V i), all loaded before any is added
     const int rows = r / V;
     for (int i0 = 0; i0 < rows; i0 += kRB) {
-      Raw rv[kV][kRB][kJ];
+      uint32_t rv[kV][kRB][kJ][kW];
 #pragma unroll
       for (int u = 0; u < kV; ++u)
 #pragma unroll
         for (int i = 0; i < kRB; ++i) {
           const int t = w + nw * u + V * (i0 + i);
-          const bool from_ring = t < n_state;
-          if constexpr (sizeof(T) == 4) {
-            const float* row = from_ring ? ring + (int64_t)t * D
-                                         : reinterpret_cast<const float*>(xs) + (int64_t)t * D;
+          const T* row = (t < n_state ? ring : xs) + (int64_t)t * D;
 #pragma unroll
-            for (int j = 0; j < kJ; ++j) rv[u][i][j] = *reinterpret_cast<const Raw*>(row + coff[j]);
-          } else if constexpr (kVec == 4) {
-            const char* row = from_ring ? reinterpret_cast<const char*>(ring + (int64_t)t * D)
-                                        : reinterpret_cast<const char*>(xs + (int64_t)t * D);
-#pragma unroll
-            for (int j = 0; j < kJ; ++j) {
-              const int off = from_ring ? coff[j] * 4 : (coff[j] & ~7) * 2;
-              rv[u][i][j] = *reinterpret_cast<const Raw*>(row + off);
-            }
-          } else {   // pairs of bf16 (kRB == 1, kV == 1)
-            if (from_ring) {
-#pragma unroll
-              for (int j = 0; j < kJ; ++j) rv[u][i][j] = *reinterpret_cast<const Raw*>(ring + (int64_t)t * D + coff[j]);
-            } else {
-#pragma unroll
-              for (int j = 0; j < kJ; ++j)
-                rv[u][i][j] = Raw{*reinterpret_cast<const uint32_t*>(xs + (int64_t)t * D + coff[j]), 0u};
-            }
-          }
+          for (int j = 0; j < kJ; ++j) load_words<T, kVec>(row, coff[j], rv[u][i][j]);
         }
       if (i0 == 0 && a.mode == 1) {
         float m0 = l0, m1 = l1;
@@ -239,33 +250,14 @@ __device__ __forceinline__ void compress_group(const CompressArgs& a, int gi, in
 #pragma unroll
         for (int i = 0; i < kRB; ++i) {
           const int t = w + nw * u + V * (i0 + i);
-          const bool from_ring = t < n_state;
           // weight of token t: lane t mod 64 holds it (t is the same on every lane)
           const float wt = __int_as_float(t < 64 ? __builtin_amdgcn_readlane(__float_as_int(e0), t & 63)
                                                  : __builtin_amdgcn_readlane(__float_as_int(e1), t & 63));
 #pragma unroll
-          for (int j = 0; j < kJ; ++j) {
-            const Raw q = rv[u][i][j];
-            float val[kVec];
-            if constexpr (sizeof(T) == 4) {
+          for (int j = 0; j < kJ; ++j)
 #pragma unroll
-              for (int e = 0; e < kVec; ++e) val[e] = __uint_as_float(q[e]);
-            } else if constexpr (kVec == 4) {
-              // the words of x holding this lane's dims: the low or high half of the 16 bytes
-              const bool hi = coff[j] & 4;
-              const uint32_t x0 = hi ? q[2] : q[0];
-              const uint32_t x1 = hi ? q[3] : q[1];
-              val[0] = from_ring ? __uint_as_float(q[0]) : bf16_to_f32(x0 & 0xffffu);
-              val[1] = from_ring ? __uint_as_float(q[1]) : bf16_to_f32(x0 >> 16);
-              val[2] = from_ring ? __uint_as_float(q[2]) : bf16_to_f32(x1 & 0xffffu);
-              val[3] = from_ring ? __uint_as_float(q[3]) : bf16_to_f32(x1 >> 16);
-            } else {
-              val[0] = from_ring ? __uint_as_float(q[0]) : bf16_to_f32(q[0] & 0xffffu);
-              val[1] = from_ring ? __uint_as_float(q[1]) : bf16_to_f32(q[0] >> 16);
-            }
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) acc[u][j][e] = fmaf(wt, val[e], acc[u][j][e]);
-          }
+            for (int e = 0; e < kVec; ++e)
+              acc[u][j][e] = fmaf(wt, word_elem<T>(rv[u][i][j], e), acc[u][j][e]);
         }
     }
     // with several virtual waves per wave (nw = 4), wave w holds p_w, p_{w+4}, ...: its q_w
@@ -352,21 +344,21 @@ __device__ __forceinline__ void compress_group(const CompressArgs& a, int gi, in
   }
 
   if (gi == 0) {
-    // trailing incomplete group -> state ring
+    // trailing incomplete group -> state ring (raw copies of x's rows)
     const int tail_start = g_last * r;
     if (tail_start + r > t_end) {
       const int lo = tail_start > s0 ? tail_start : s0;
       for (int t = lo + w; t < t_end; t += nw) {
         const int slot = t - tail_start;
         const T* row = x + (int64_t)(c0 + t - s0) * D;
-        float* dst = a.state + ((int64_t)b * r + slot) * D;
+        T* dst = ring + (int64_t)slot * D;
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
           const int c = lane + 64 * j;
           if (c < nchunks) {
-            float v[kVec];
-            load_vec<T, kVec>(row, c * kVec, v);
-            store_f32_vec<kVec>(dst, c * kVec, v);
+            uint32_t v[kW];
+            load_words<T, kVec>(row, c * kVec, v);
+            store_words<T, kVec>(dst, c * kVec, v);
           }
         }
         if (a.mode == 1 && lane == 0) a.state_logits[(int64_t)b * r + slot] = a.gate[c0 + t - s0];

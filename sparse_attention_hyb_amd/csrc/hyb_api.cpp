@@ -253,7 +253,7 @@ const char* hyb_last_error(void) { return g_last_error.c_str(); }
 
 int32_t hyb_compress(const void* x, int32_t x_dtype, const float* gate_logits,
                      const int32_t* cu_seqlens, const int32_t* start_pos, int32_t batch,
-                     int32_t max_new_tokens, float* state, float* state_logits, int32_t mode,
+                     int32_t max_new_tokens, void* state, float* state_logits, int32_t mode,
                      const hyb_paged* out, int32_t rope_dim, double rope_base, float eps,
                      void* stream) {
   const char* op = "hyb_compress";

@@ -42,7 +42,7 @@ struct CompressArgs {
   const int32_t* start_pos;
   int32_t batch;
   int32_t max_new_tokens;
-  float* state;
+  void* state;          // [batch][ratio][dim] in x_dtype
   float* state_logits;
   int32_t mode;
   PoolDev out;

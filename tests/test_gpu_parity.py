@@ -104,7 +104,7 @@ def test_tiny_c4_decode_fp32_from_raw_tokens(gpu_lib):
     wl = W.tiny_decode(DEV, seed=0)
     T, D = wl.x.shape
     cu, st = ints([0, T]), ints([0])
-    state = torch.zeros(1, 4, D, device=DEV)
+    state = torch.zeros(1, 4, D, dtype=wl.x.dtype, device=DEV)   # ring in x's dtype
     hyb.hyb_swa_insert(wl.x, cu, st, T, wl.swa, wl.rope_dim)
     hyb.hyb_compress(wl.x, cu, st, T, state, wl.comp, wl.rope_dim, eps=1e-6)
     qpos = wl.seq_lens - 1
@@ -144,15 +144,20 @@ def test_tiny_c4_decode_fp32_from_raw_tokens(gpu_lib):
 
 
 # ============================================================================== compressor
-@pytest.mark.parametrize("ratio,mode,dtype", [(4, "mean", "f32"), (128, "gate", "f32"),
-                                              (4, "gate", "bf16"), (128, "mean", "bf16")])
-def test_compress_chunked_matches_oracle_and_state(gpu_lib, ratio, mode, dtype):
+@pytest.mark.parametrize("ratio,mode,dtype,D,rd,T", [
+    (4, "mean", "f32", 64, 16, 1000), (128, "gate", "f32", 64, 16, 1500),
+    (4, "gate", "bf16", 512, 64, 1000), (128, "mean", "bf16", 512, 64, 1500),
+    # wider rows and other load shapes: 16-byte chunks with several per lane (1024, 2048, 520),
+    # eight virtual waves above dim 1024 (1536), element pairs when a row is not a whole number
+    # of 16-byte chunks (514)
+    (128, "gate", "bf16", 1024, 64, 600), (4, "mean", "f32", 2048, 128, 300),
+    (128, "mean", "f32", 1536, 64, 600), (4, "gate", "bf16", 514, 64, 300),
+    (128, "mean", "bf16", 520, 32, 600)])
+def test_compress_chunked_matches_oracle_and_state(gpu_lib, ratio, mode, dtype, D, rd, T):
     """Three sequences with different chunkings (token by token, ragged chunks, one shot):
     entries equal the oracle's; chunked output is bitwise equal to one-shot; the state ring holds
     exactly the in-progress group's raw tokens."""
     hyb = gpu_lib
-    D, rd = 512 if dtype == "bf16" else 64, 64 if dtype == "bf16" else 16
-    T = 1000 if ratio == 4 else 1500
     g = W.generator(90, ratio, 0, DEV)
     xs = [W.to_storage(W.randn((T, D), g, DEV), dtype) for _ in range(3)]
     lg = [W.randn((T,), g, DEV) for _ in range(3)]
@@ -161,11 +166,11 @@ def test_compress_chunked_matches_oracle_and_state(gpu_lib, ratio, mode, dtype):
                                g, DEV, fill=False)
     pool_once = W.PagedTensors(torch.zeros_like(pool_chunked.data), None,
                                pool_chunked.block_table.clone(), dtype, D, ratio)
-    state = torch.zeros(3, ratio, D, device=DEV)
+    state = torch.zeros(3, ratio, D, dtype=xs[0].dtype, device=DEV)   # ring in x's dtype
     st_l = torch.zeros(3, ratio, device=DEV)
     gate = (lambda c: torch.cat([lg[b][c[b][0]:c[b][1]] for b in range(3)])) if mode == "gate" else None
     cuts = [list(range(0, T + 1)),                              # token by token
-            [0, 1, 3, 130, 131, 517, 900, T],                    # ragged
+            sorted({0, 1, 3, 130, 131, 517 % T, 900 % T, T}),    # ragged
             [0, T]]                                              # one shot
     n_steps = max(len(c) for c in cuts) - 1
     for s in range(n_steps):
@@ -315,7 +320,7 @@ def test_c128_dense_from_raw_tokens_full_size_sampled(gpu_lib):
     hyb = gpu_lib
     wl = W.dense_decode(DEV, seed=0, fill_comp=False)
     B, L, D = wl.batch, wl.seq_lens_host[0], wl.dim
-    state = torch.zeros(B, 128, D, device=DEV)
+    state = torch.zeros(B, 128, D, dtype=torch.bfloat16, device=DEV)   # ring in x's dtype
     st_l = torch.zeros(B, 128, device=DEV)
     n_chunks = L // W.RAW_CHUNK
     for c in range(n_chunks):
@@ -368,8 +373,8 @@ def test_prefill_from_raw_small(gpu_lib):
     c4 = W.make_pool("bf16", D, 4, [W.blocks_for_entries(T // 4, 4)], mb, g, DEV, fill=False)
     c128 = W.make_pool("bf16", D, 128, [W.blocks_for_entries(T // 128, 128)], mb, g, DEV, fill=False)
     ip = W.make_pool("bf16", 128, 4, [W.blocks_for_entries(T // 4, 4)], mb, g, DEV)
-    s4, s128, l128 = (torch.zeros(1, 4, D, device=DEV), torch.zeros(1, 128, D, device=DEV),
-                      torch.zeros(1, 128, device=DEV))
+    s4, s128, l128 = (torch.zeros(1, 4, D, dtype=x.dtype, device=DEV),
+                      torch.zeros(1, 128, D, dtype=x.dtype, device=DEV), torch.zeros(1, 128, device=DEV))
     for a, e in ((0, T0), (T0, T)):
         cu, st = ints([0, e - a]), ints([a])
         hyb.hyb_swa_insert(x[a:e], cu, st, e - a, swa, rd)
@@ -420,8 +425,9 @@ def test_prefill_full_size_sampled(gpu_lib):
     D, rd, n = wl.q.shape[2], wl.rope_dim, wl.n_new
     cu, st = ints([0, n]), ints([wl.prior])
     hyb.hyb_swa_insert(wl.x_new, cu, st, n, wl.swa, rd)
-    s4 = torch.zeros(1, 4, D, device=DEV)
-    s128, l128 = torch.zeros(1, 128, D, device=DEV), torch.zeros(1, 128, device=DEV)
+    s4 = torch.zeros(1, 4, D, dtype=wl.x_new.dtype, device=DEV)
+    s128 = torch.zeros(1, 128, D, dtype=wl.x_new.dtype, device=DEV)
+    l128 = torch.zeros(1, 128, device=DEV)
     hyb.hyb_compress(wl.x_new, cu, st, n, s4, wl.c4, rd, eps=1e-6)
     hyb.hyb_compress(wl.x_new, cu, st, n, s128, wl.c128, rd, eps=1e-6, gate_logits=wl.gate_new,
                      state_logits=l128)
@@ -580,7 +586,7 @@ def test_attn_decode_compress_equals_two_calls(gpu_lib, case):
         x_use = x if case == "c4_f32x" else W.to_storage(x, "bf16")
     cu = torch.arange(0, B + 1, dtype=I32, device=DEV)
     start = (wl.seq_lens - 1).contiguous()
-    state = W.randn((B, r, D), g, DEV)
+    state = W.randn((B, r, D), g, DEV).to(x_use.dtype)   # ring in x's dtype
     st_l = W.randn((B, r), g, DEV) if gate else None
     gl = W.randn((B,), g, DEV) if gate else None
     runs = []
