@@ -411,7 +411,7 @@ def main():
         "config": {"workload": "c4_sparse_decode", "batch": 16, "context": 131072, "heads": 64,
                    "dim": 512, "rope_dims": 64, "indexer": "64 heads x 128, bf16", "topk": 512,
                    "window": 128, "replicas": args.replicas,
-                   "step": "compress new token + indexer scores + top-512 + sparse attention + combine/inverse RoPE"},
+                   "step": "indexer scores + top-512 + sparse attention + combine/inverse RoPE, new token compressed beside the combine"},
         "hbm_frac_step": res["hbm_frac_step"],
         "step_bytes": res["step_bytes"],
         "roofline": {"kernel": "score_mfma_dma (indexer scores + top-k hand-off)", "bound": "hbm",
