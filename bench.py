@@ -136,6 +136,22 @@ def c4_sparse(torch, hyb, W, BM, args):
     events = timing_events(torch, args.steps)
     secs = time_loop(torch, step, args.steps, args.warmup, R, events)
     score_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
+    graph = None
+    if args.all:
+        # the same step captured once per replica in a HIP graph and replayed (no call allocates,
+        # clears memory or synchronises, so the captured step is the eager one)
+        graphs = []
+        for r in range(R):
+            gr = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(gr):
+                step(r, None)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        gsecs = time_loop(torch, lambda r, ev: graphs[r].replay(), args.steps, args.warmup, R)
+        graph = dict(value=B * args.steps / gsecs, unit="query-tokens/s",
+                     ms_per_step=gsecs * 1e3 / args.steps, steps=args.steps,
+                     config={"workload": "c4_sparse_decode", "replay": "one HIP graph per step"})
     per_tok = BM.decode_query_bytes(L, ratio=4, sparse=True)
     comp_b = BM.compress_decode_bytes(4)
     step_bytes = B * (per_tok.total + comp_b)
@@ -145,7 +161,7 @@ def c4_sparse(torch, hyb, W, BM, args):
         value=B * args.steps / secs, ms_per_step=ms, step_bytes=step_bytes,
         hbm_frac_step=step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         score_kernel_ms=score_ms, score_bytes=score_bytes,
-        score_gbs=score_bytes / (score_ms * 1e-3) / 1e9,
+        score_gbs=score_bytes / (score_ms * 1e-3) / 1e9, graph=graph,
     )
     return res, reps[0]
 
@@ -258,6 +274,45 @@ def prefill(torch, hyb, W, BM, args):
         mfma_frac=(fi + fa) / ((t[1] + t[2]) * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         query_tokens_per_s=n / (sum(t) * 1e-3),
         config={"workload": "chunked_prefill", "prior": wl.prior, "chunk": n, "heads": 64, "dim": D, "topk": wl.k},
+    )
+
+
+def multi_decode(torch, hyb, W, BM, args):
+    """Multi-query C4 decode (speculative-decoding verify pass): 16 sequences x 131072 tokens, two
+    query tokens each, through the prefill-form entry points; the two new tokens compressed too."""
+    dev = "cuda"
+    R, B, L, T = 4, 16, 131072, 2
+    reps = []
+    for r in range(R):
+        wl = W.multi_decode(dev, seed=r, batch=B, ctx=L, n_tok=T)
+        n = wl.n_q
+        reps.append(dict(
+            wl=wl, topk=torch.empty(n, wl.k, dtype=torch.int32, device=dev), out=torch.empty_like(wl.q),
+            ws_i=torch.empty(hyb.hyb_index_topk_workspace_bytes(n, L - 1, 128, 4), dtype=torch.uint8, device=dev),
+            ws_a=torch.empty(hyb.hyb_attn_prefill_workspace_bytes(n, 64, 512, L - 1, 4, wl.k), dtype=torch.uint8, device=dev),
+            cu=torch.arange(0, (B + 1) * T, T, dtype=torch.int32, device=dev),
+            start=torch.full((B,), L - T, dtype=torch.int32, device=dev),
+            state=torch.zeros(B, 4, 512, dtype=wl.x_new.dtype, device=dev)))
+
+    def step(r, ev):
+        d = reps[r]
+        wl = d["wl"]
+        hyb.hyb_index_topk(wl.idx_q, wl.idx_w, wl.q_pos, L - 1, wl.idx_pool, wl.k, d["topk"],
+                           q_seq=wl.q_seq, workspace=d["ws_i"])
+        hyb.hyb_attn_prefill(wl.q, wl.q_pos, L - 1, wl.swa, wl.comp, d["out"], topk_idx=d["topk"],
+                             k=wl.k, q_seq=wl.q_seq, workspace=d["ws_a"])
+        hyb.hyb_compress(wl.x_new, d["cu"], d["start"], T, d["state"], wl.comp, 64)
+
+    n = max(args.steps // 2, 20)
+    secs = time_loop(torch, step, n, max(args.warmup // 2, 5), R, None)
+    ms = secs * 1e3 / n
+    per_tok = BM.decode_query_bytes(L, ratio=4, sparse=True)
+    return dict(
+        value=B * T * n / secs, unit="query-tokens/s", ms_per_step=ms, steps=n,
+        hbm_frac_step=B * T * per_tok.total / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        config={"workload": "c4_multi_query_decode", "batch": B, "query_tokens_per_sequence": T,
+                "context": L, "heads": 64, "dim": 512, "topk": 512, "window": 128, "replicas": R,
+                "step": "indexer scores + top-512 per query token + attention (prefill form) + compression of the new tokens"},
     )
 
 
@@ -382,6 +437,8 @@ def main():
     log(f"C4 sparse decode: {res['value']:.0f} q-tok/s, {res['ms_per_step'] * 1e3:.1f} us/step, "
         f"score kernel {res['score_kernel_ms'] * 1e3:.1f} us = {res['score_gbs']:.0f} GB/s")
     extra = {}
+    if res.get("graph"):
+        extra["c4_sparse_decode_graph"] = res["graph"]
     if not args.no_c128:
         log("C128 dense decode: compressing 32 x 2^20 raw tokens, then timing")
         extra["c128_dense_decode_1M"] = c128_dense(torch, hyb, W, BM, args)
@@ -391,6 +448,8 @@ def main():
         extra["chunked_prefill"] = prefill(torch, hyb, W, BM, args)
         log("quantised mixed decode")
         extra["quantized_mixed_decode"] = quant_mixed(torch, hyb, W, BM, args)
+        log("multi-query decode")
+        extra["multi_query_decode"] = multi_decode(torch, hyb, W, BM, args)
     cpu = None
     if not args.no_cpu_baseline:
         log("oracle CPU baseline")

@@ -435,3 +435,54 @@ def quantized_mixed(device, seed: int = 0, batch: int = 64, n_heads: int = 64, d
                         dtype="fp8", workload_id=workload_id * 10 + 2)
     c4.name, c128.name = "quant_c4_decode", "quant_c128_decode"
     return c4, c128
+
+
+@dataclass
+class MultiDecode:
+    """Multi-query decode (the verify pass of speculative decoding): n_tok query tokens per
+    sequence at the last n_tok positions of its context, in the prefill form (q_seq, q_pos). The
+    pools already hold every position (the new tokens' raw window entries included); x_new holds
+    the new tokens' raw values for the compressor."""
+
+    q: torch.Tensor          # [B * n_tok, H, D], sequence-major
+    q_seq: torch.Tensor      # [B * n_tok] int32
+    q_pos: torch.Tensor      # [B * n_tok] int32
+    q_pos_host: List[int]
+    lens: List[int]
+    n_tok: int
+    swa: PagedTensors
+    comp: PagedTensors
+    idx_q: torch.Tensor      # [B * n_tok, H_I, D_I]
+    idx_w: torch.Tensor      # [B * n_tok, H_I]
+    idx_pool: PagedTensors
+    x_new: torch.Tensor      # [B * n_tok, D] raw tokens at the query positions
+    k: int = 512
+    window: int = 128
+    rope_dim: int = 64
+    rope_base: float = 10000.0
+
+    @property
+    def n_q(self) -> int:
+        return int(self.q.shape[0])
+
+
+def multi_decode(device, seed: int = 0, batch: int = 16, ctx=131072, n_tok: int = 2,
+                 n_heads: int = 64, dim: int = 512, rope_dim: int = 64, idx_heads: int = 64,
+                 idx_dim: int = 128, k: int = 512, window: int = 128, dtype: str = "bf16",
+                 workload_id: int = 6) -> MultiDecode:
+    """C4 multi-query decode: the pools of a C4 sparse decode batch, n_tok queries per sequence."""
+    base = sparse_decode(device, seed, batch, ctx, n_heads, dim, rope_dim, idx_heads, idx_dim, k,
+                         window, dtype=dtype, workload_id=workload_id)
+    lens = base.seq_lens_host
+    g = generator(workload_id, seed, 5, device)
+    n_q = batch * n_tok
+    qdt = "bf16" if dtype in ("bf16", "fp8") else dtype
+    q = to_storage(randn((n_q, n_heads, dim), g, device), qdt)
+    idx_q = to_storage(randn((n_q, idx_heads, idx_dim), g, device), qdt)
+    idx_w = randn((n_q, idx_heads), g, device) / math.sqrt(128.0)
+    x_new = to_storage(randn((n_q, dim), g, device), qdt)
+    seqs = [b for b in range(batch) for _ in range(n_tok)]
+    pos = [lens[b] - n_tok + t for b in range(batch) for t in range(n_tok)]
+    return MultiDecode(q, _ints(seqs, device), _ints(pos, device), pos, lens, n_tok, base.swa,
+                       base.comp, idx_q, idx_w, base.idx_pool, x_new, k=k, window=window,
+                       rope_dim=rope_dim)

@@ -619,3 +619,110 @@ def test_attn_decode_compress_equals_two_calls(gpu_lib, case):
             lb, slot = gidx // (256 // r), gidx % (256 // r)
             phys = int(wl.comp.block_table[b, lb])
             assert not torch.equal(c1[phys, slot], wl.comp.data[phys, slot])
+
+
+# ============================================================ multi-query (speculative) decode
+def _check_multi(hyb, wl, rows):
+    """Indexer + top-k + attention of a multi-query decode batch through the prefill-form entry
+    points; the oracle recomputes the sampled rows, fed its own selection and chained after the
+    GPU's where the two agree."""
+    max_pos = max(wl.q_pos_host)
+    topk = torch.full((wl.n_q, wl.k), -7, dtype=I32, device=DEV)
+    hyb.hyb_index_topk(wl.idx_q, wl.idx_w, wl.q_pos, max_pos, wl.idx_pool, wl.k, topk, q_seq=wl.q_seq)
+    ipo, swa, comp = to_oracle_pool(wl.idx_pool), to_oracle_pool(wl.swa), to_oracle_pool(wl.comp)
+    iq64, iw64 = to_f64(wl.idx_q), wl.idx_w.cpu().double().numpy()
+    seqs = wl.q_seq.cpu().numpy()
+    sel = {}
+    for i in rows:
+        p, b = wl.q_pos_host[i], int(seqs[i])
+        keys = O.pool_entries(ipo, b, range(O.n_visible(p, 4, wl.window)))
+        sc = O.indexer_scores(iq64[i], iw64[i], keys)
+        sel[i] = (sc, O.topk_select(sc, wl.k), topk_delta(iq64[i], iw64[i], keys))
+    feed = torch.full((wl.n_q, wl.k), -1, dtype=I32)
+    for i in rows:
+        feed[i] = torch.from_numpy(sel[i][1].astype(np.int32))
+    feed = feed.to(DEV)
+    out_fed, out_chain = torch.empty_like(wl.q), torch.empty_like(wl.q)
+    for o, t in ((out_fed, feed), (out_chain, topk)):
+        hyb.hyb_attn_prefill(wl.q, wl.q_pos, max_pos, wl.swa, wl.comp, o, topk_idx=t, k=wl.k,
+                             q_seq=wl.q_seq, window=wl.window, rope_dim=wl.rope_dim,
+                             rope_base=wl.rope_base)
+    sync()
+    gt = topk.cpu().numpy()
+    q64 = to_f64(wl.q)
+    scale = 1.0 / math.sqrt(wl.q.shape[2])
+    for i in rows:
+        check_topk_set(gt[i], sel[i][1], sel[i][0], sel[i][2], wl.k)
+        want = O.hybrid_query(q64[i], wl.q_pos_host[i], int(seqs[i]), swa, comp, wl.window, scale,
+                              wl.rope_dim, wl.rope_base, sel[i][1])
+        assert_abs_close(to_f64(out_fed)[i], want)
+        if list(gt[i]) == list(sel[i][1]):
+            assert_abs_close(to_f64(out_chain)[i], want)
+
+
+def test_multi_decode_small(gpu_lib):
+    """Three sequences (3000, 9001, 20002 tokens), three query tokens each at the last three
+    positions: every row against the oracle."""
+    wl = W.multi_decode(DEV, seed=0, batch=3, ctx=[3000, 9001, 20002], n_tok=3)
+    _check_multi(gpu_lib, wl, range(wl.n_q))
+
+
+def test_multi_decode_full_size_sampled(gpu_lib):
+    """16 sequences x 131072 tokens, two query tokens each (the C4 decode batch with one draft
+    token): rows 0, 1, 17 and 31 against the oracle."""
+    wl = W.multi_decode(DEV, seed=1, batch=16, ctx=131072, n_tok=2)
+    _check_multi(gpu_lib, wl, (0, 1, 17, 31))
+
+
+# ============================================================== graph capture of the decode step
+def test_c4_decode_step_graph_replay(gpu_lib):
+    """The C4 decode step (indexer halves, top-k, attention with the compressor beside the
+    combine) captured in one HIP graph: no call allocates or clears memory, so every replay
+    (outputs cleared eagerly in between) reproduces the eager step exactly."""
+    hyb = gpu_lib
+    lens = [4096, 8192, 20000, 65536]
+    wl = W.sparse_decode(DEV, seed=3, batch=len(lens), ctx=lens)
+    B, D, L = wl.batch, wl.dim, wl.max_seq_len
+    g = W.generator(92, 0, 0, DEV)
+    kshape, hshape = hyb.index_keys_shapes(B, L - 1)
+    keys = torch.empty(kshape, dtype=I32, device=DEV)
+    hist = torch.empty(hshape, dtype=torch.int16, device=DEV)
+    topk = torch.empty(B, wl.k, dtype=I32, device=DEV)
+    out = torch.empty_like(wl.q)
+    ws = torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, D, L, 4, wl.k), dtype=torch.uint8,
+                     device=DEV)
+    x_new = W.to_storage(W.randn((B, D), g, DEV), "bf16")
+    cu = torch.arange(0, B + 1, dtype=I32, device=DEV)
+    qpos = (wl.seq_lens - 1).contiguous()
+    state = W.to_storage(W.randn((B, 4, D), g, DEV), "bf16")
+    pool0, state0 = wl.comp.data.clone(), state.clone()
+
+    def step():
+        hyb.hyb_index_score_keys(wl.idx_q, wl.idx_w, qpos, L - 1, wl.idx_pool, keys, hist)
+        hyb.hyb_topk_keys(keys, hist, qpos, L - 1, wl.k, topk)
+        hyb.hyb_attn_decode_compress(wl.q, wl.seq_lens, L, wl.swa, wl.comp, out, x_new, cu, qpos, 1,
+                                     state, wl.comp, topk_idx=topk, k=wl.k, workspace=ws)
+
+    step()
+    sync()
+    want = (topk.clone(), out.clone(), wl.comp.data.clone(), state.clone())
+    assert not torch.equal(want[2], pool0)   # the step completed groups (4096 % 4 == 0, ...)
+    wl.comp.data.copy_(pool0)
+    state.copy_(state0)
+    graph = torch.cuda.CUDAGraph()
+    sync()
+    with torch.cuda.graph(graph):
+        step()
+    sync()
+    for rep in range(3):
+        topk.fill_(-7)
+        out.zero_()
+        wl.comp.data.copy_(pool0)
+        state.copy_(state0)
+        sync()
+        graph.replay()
+        sync()
+        assert torch.equal(topk, want[0]), rep
+        assert torch.equal(out, want[1]), rep
+        assert torch.equal(wl.comp.data, want[2]), rep
+        assert torch.equal(state, want[3]), rep
