@@ -36,6 +36,7 @@ constexpr int kMD = 512;        // dims in the MFMA kernel
 constexpr int kKT = 32;         // keys per tile in the MFMA kernel
 constexpr int kGenTile = 64;    // keys per tile in the generic kernel
 constexpr int kMaxSplit = 64;
+constexpr int kMaxRopePairs = 64;   // rope_dim <= 128
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Where key j of a query lives: a pool and the flattened entry index (-1 = masked).
@@ -296,6 +297,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
   __shared__ uint32_t tmask[kSeg / kKT];   // per tile of the segment: bit j = key j is valid
   __shared__ __attribute__((aligned(16))) float kscale[3 * kKT];
   __shared__ float lfin[kMH];
+  __shared__ float2 orope[kMaxRopePairs];   // RoPE(-p) table of the one-split output
 
   const int logical = xcd_logical(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
   const int sp = logical % a.n_split, i = logical / a.n_split;
@@ -604,16 +606,30 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
   }
   // ---- partials: m and l per head from the score waves; O / l as bf16 [head][dim] (zero for a
   // split without keys), staged through LDS by the value waves so that every global store writes
-  // one contiguous 1 KB row
+  // one contiguous 1 KB row. With one split and a bf16 output the partial is the output: the
+  // value waves rotate it by RoPE(-p) before staging and the rows go straight to `out` (the
+  // launch then skips the combine).
   constexpr int kOPitch = kMD + 8;   // staged row (bf16): 1040 B, rows 4 banks apart
   uint16_t* ost = ktile;             // the tile buffers are free after the last barrier
+  const bool direct = a.n_split == 1 && a.out_dtype == BF16;
+  const int rope_lo = kMD - a.rope_dim;
   if constexpr (kScore) {
+    if (direct) {
+      // cos / sin of -p * theta_t for the value waves (the score waves are idle here)
+      for (int t = tid; t < (a.rope_dim >> 1); t += 256) {
+        float c, sn;
+        rope_cs(-(double)qk.p, t, a.rope_dim, a.rope_base, &c, &sn);
+        orope[t] = make_float2(c, sn);
+      }
+    }
     if (sg == 0) {
-      float* pml = a.part_ml + ((int64_t)i * a.n_split + sp) * 2 * kMH;
       const int h = 16 * wave + sh;
-      // m is kept in log2 units inside the kernel; store natural-log units for the combine
-      pml[h] = m_run == -INFINITY ? -INFINITY : m_run / kLog2e;
-      pml[kMH + h] = l_run;
+      if (!direct) {
+        float* pml = a.part_ml + ((int64_t)i * a.n_split + sp) * 2 * kMH;
+        // m is kept in log2 units inside the kernel; store natural-log units for the combine
+        pml[h] = m_run == -INFINITY ? -INFINITY : m_run / kLog2e;
+        pml[kMH + h] = l_run;
+      }
       lfin[h] = l_run;
     }
     __syncthreads();
@@ -631,15 +647,27 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x16& v = o[mb];
-        const u32x2 w = {pack_bf16x2(v[4 * q4] * inv, v[4 * q4 + 1] * inv),
-                         pack_bf16x2(v[4 * q4 + 2] * inv, v[4 * q4 + 3] * inv)};
+        float y[4] = {v[4 * q4] * inv, v[4 * q4 + 1] * inv, v[4 * q4 + 2] * inv, v[4 * q4 + 3] * inv};
+        const int d = 256 * dh + 32 * mb + 8 * q4 + 4 * hf;   // first of the four dims
+        if (direct && d >= rope_lo) {
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const float2 cs = orope[(d + e - rope_lo) >> 1];
+            const float y0 = y[e] * cs.x - y[e + 1] * cs.y;
+            const float y1 = y[e] * cs.y + y[e + 1] * cs.x;
+            y[e] = y0;
+            y[e + 1] = y1;
+          }
+        }
+        const u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
         *reinterpret_cast<u32x2*>(orow + 32 * mb + 8 * q4) = w;
       }
     __syncthreads();
   }
   // wave w stores rows 8w..8w+7, one row (64 lanes x 16 B) per instruction
   {
-    uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + ((int64_t)i * a.n_split + sp) * kMH * kMD;
+    uint16_t* po = direct ? reinterpret_cast<uint16_t*>(a.out) + (int64_t)i * kMH * kMD
+                          : reinterpret_cast<uint16_t*>(a.part_o) + ((int64_t)i * a.n_split + sp) * kMH * kMD;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int row = 8 * wave + c;
@@ -663,7 +691,6 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
 // ------------------------------------------------------------------------------------------
 constexpr int kCombineHeads = 64;     // heads per combine workgroup at most
 constexpr int kCombineElems = 2048;   // elements per combine workgroup (hpw = 2048 / dim, >= 1)
-constexpr int kMaxRopePairs = 64;      // rope_dim <= 128
 
 // Raw 8-element load of a partial (16 bytes of bf16 or 32 bytes of fp32), widened later.
 template <typename PT>
@@ -934,10 +961,13 @@ int combine_heads_per_wg(const AttnArgs& a) {
 }
 }  // namespace
 
+// The MFMA kernel writes the output itself when there is one split and the output is bf16.
+static bool writes_output(const AttnArgs& a) { return a.use_mfma && a.n_split == 1 && a.out_dtype == BF16; }
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.n_q == 0) return hipSuccess;
   hipError_t e = launch_attention_kernel(a, s);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || writes_output(a)) return e;
   const int hpw = combine_heads_per_wg(a);
   const dim3 cgrid((a.n_heads + hpw - 1) / hpw, a.n_q);
   const size_t lds = combine_lds_bytes(a.n_split);
@@ -955,7 +985,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_attention_compress(const AttnArgs& a, const CompressArgs& c, hipStream_t s) {
   const int r = c.out.ratio, D = c.out.dim;
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  const bool fuse = a.n_q > 0 && a.use_mfma && c.batch > 0 && c.max_new_tokens > 0 && D <= 512 &&
+  const bool fuse = a.n_q > 0 && a.use_mfma && !writes_output(a) && c.batch > 0 && c.max_new_tokens > 0 && D <= 512 &&
                     D % (c.x_dtype == F32 ? 4 : 8) == 0 && al16(c.x) && al16(c.state) &&
                     al16(c.out.data) && (r == 4 || r == 128);
   if (!fuse) {
