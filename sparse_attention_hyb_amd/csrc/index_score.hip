@@ -30,15 +30,15 @@ constexpr int kMfmaDim = 128;
 __device__ __forceinline__ float canonical_zero(float v) { return v == 0.0f ? 0.0f : v; }
 
 // Eight E2M1 nibbles (one 32-bit word, element 0 in the low nibble) times a power-of-two block
-// scale -> eight bf16 values, exactly.
+// scale -> eight bf16 values, exactly, with gfx950's scaled conversion (two elements of one byte
+// per instruction, low nibble first; it matches the arithmetic conversion bit for bit for every
+// code and scales from 2^-100 to 2^60).
 __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float sc) {
   u32x4 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float lo = fp4_to_f32((w >> (8 * j)) & 0xfu) * sc;
-    float hi = fp4_to_f32((w >> (8 * j + 4)) & 0xfu) * sc;
-    r[j] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-  }
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -190,11 +190,13 @@ __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
       for (int s = 0; s < 8; ++s) kb.v[s] = *reinterpret_cast<const bf16x8*>(row + 8 * s);
     } else {
       const uint8_t* row = a.pool.data + e * a.pool.entry_bytes + 32 * hf;
-      const uint8_t* scl = reinterpret_cast<const uint8_t*>(a.pool.scale) + e * 4 + 2 * hf;
+      // the two E8M0 scale bytes of this lane's 64 dims, one 2-byte read
+      const uint16_t scl = *reinterpret_cast<const uint16_t*>(
+          reinterpret_cast<const uint8_t*>(a.pool.scale) + e * 4 + 2 * hf);
       kb.w0 = *reinterpret_cast<const u32x4*>(row);
       kb.w1 = *reinterpret_cast<const u32x4*>(row + 16);
-      kb.s0 = e8m0_to_f32(scl[0]);
-      kb.s1 = e8m0_to_f32(scl[1]);
+      kb.s0 = e8m0_to_f32(scl & 0xffu);
+      kb.s1 = e8m0_to_f32(scl >> 8);
     }
   };
   auto operand = [&](const Keys& kb, int s) -> bf16x8 {
