@@ -171,12 +171,15 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a) {
 // ------------------------------------------------------------------------------------------
 // MFMA kernel: 64 heads x 512 dims.
 // ------------------------------------------------------------------------------------------
+// Eight E4M3 codes (two words, element 0 in the low byte) -> eight bf16 values, exactly: gfx950's
+// scaled conversion with scale 1, two codes of one 16-bit half per instruction (it matches the
+// arithmetic widening for every non-NaN code; E4M3 NaN is never stored).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   u32x4 r;
-  r[0] = fp8_to_bf16(w0 & 0xffu) | (fp8_to_bf16((w0 >> 8) & 0xffu) << 16);
-  r[1] = fp8_to_bf16((w0 >> 16) & 0xffu) | (fp8_to_bf16(w0 >> 24) << 16);
-  r[2] = fp8_to_bf16(w1 & 0xffu) | (fp8_to_bf16((w1 >> 8) & 0xffu) << 16);
-  r[3] = fp8_to_bf16((w1 >> 16) & 0xffu) | (fp8_to_bf16(w1 >> 24) << 16);
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
   return __builtin_bit_cast(bf16x8, r);
 }
 
