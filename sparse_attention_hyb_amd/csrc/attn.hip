@@ -290,7 +290,7 @@ struct Stage<true> {
 // probability buffer written in iteration t was last read in iteration t-1.
 // fp8 pools: codes are widened to bf16 exactly; the per-entry scale multiplies the score before
 // the softmax and the probability before PV (so no rounding of scaled values).
-template <bool kFp8>
+template <bool kFp8, bool kDirect>
 __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ktile[3 * kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t ptile[2 * kMH * kPPitch];
@@ -614,10 +614,10 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
   // launch then skips the combine).
   constexpr int kOPitch = kMD + 8;   // staged row (bf16): 1040 B, rows 4 banks apart
   uint16_t* ost = ktile;             // the tile buffers are free after the last barrier
-  const bool direct = a.n_split == 1 && a.out_dtype == BF16;
+  constexpr bool direct = kDirect;   // one split and a bf16 output (the launch decides)
   const int rope_lo = kMD - a.rope_dim;
   if constexpr (kScore) {
-    if (direct) {
+    if constexpr (direct) {
       // cos / sin of -p * theta_t for the value waves (the score waves are idle here)
       for (int t = tid; t < (a.rope_dim >> 1); t += 256) {
         float c, sn;
@@ -627,7 +627,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
     }
     if (sg == 0) {
       const int h = 16 * wave + sh;
-      if (!direct) {
+      if constexpr (!direct) {
         float* pml = a.part_ml + ((int64_t)i * a.n_split + sp) * 2 * kMH;
         // m is kept in log2 units inside the kernel; store natural-log units for the combine
         pml[h] = m_run == -INFINITY ? -INFINITY : m_run / kLog2e;
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
         const f32x16& v = o[mb];
         float y[4] = {v[4 * q4] * inv, v[4 * q4 + 1] * inv, v[4 * q4 + 2] * inv, v[4 * q4 + 3] * inv};
         const int d = 256 * dh + 32 * mb + 8 * q4 + 4 * hf;   // first of the four dims
-        if (direct && d >= rope_lo) {
+        if (kDirect && d >= rope_lo) {
 #pragma unroll
           for (int e = 0; e < 4; e += 2) {
             const float2 cs = orope[(d + e - rope_lo) >> 1];
@@ -947,10 +947,18 @@ namespace {
 hipError_t launch_attention_kernel(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.n_q);
   if (a.use_mfma) {
-    if (a.swa.dtype == FP8)
-      hipLaunchKernelGGL(attn_mfma<true>, grid, dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL(attn_mfma<false>, grid, dim3(512), 0, s, a);
+    const bool direct = a.n_split == 1 && a.out_dtype == BF16;   // writes_output(a)
+    if (a.swa.dtype == FP8) {
+      if (direct)
+        hipLaunchKernelGGL((attn_mfma<true, true>), grid, dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_mfma<true, false>), grid, dim3(512), 0, s, a);
+    } else {
+      if (direct)
+        hipLaunchKernelGGL((attn_mfma<false, true>), grid, dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_mfma<false, false>), grid, dim3(512), 0, s, a);
+    }
   } else {
     size_t lds = sizeof(float) * ((size_t)2 * a.n_heads * a.dim + (size_t)a.n_heads * kGenTile +
                                   3 * (size_t)a.n_heads);
