@@ -424,6 +424,161 @@ __global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
                               reinterpret_cast<uint2*>(&stage[0][0][0]), wtot);
 }
 
+// Prefill form, bf16 keys: four query tokens per workgroup, one per wave, share every key tile.
+// Queries of one sequence see the same keys, so a tile streamed once into LDS serves all of them:
+// the key traffic of a prefill chunk drops fourfold and the kernel becomes MFMA-bound. The waves'
+// queries are grouped by sequence (consecutive queries of a chunk usually share one): each group
+// streams the keys up to its longest visible range, the four waves loading a quarter of each
+// tile (two direct loads of four keys each) into a ring of kMStages shared tiles; after a barrier
+// every wave whose query is in the group scores the tile. Each query's keys and histograms then go
+// through the same hand-off (or plain scores) as in the one-query kernels.
+constexpr int kMQ = 4;        // queries per workgroup (one per wave)
+constexpr int kMStages = 6;   // shared 8 KB tiles in the ring (five in flight)
+// Launches with explicit sequence ids and at least this many queries take the shared-tile kernel.
+// A workgroup whose four queries belong to different sequences streams each sequence's keys in
+// turn, which is only cheap when most workgroups hold one sequence and the grid is large; a decode
+// batch (one or a few queries per sequence) keeps the one-query kernel.
+constexpr int kMultiMinQueries = 256;
+
+__global__ __launch_bounds__(256, 1) void score_mfma_multi(ScoreArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[kMStages][8192];
+  __shared__ uint32_t lhist[kMQ][kScoreParts * kTopBins];
+  __shared__ uint32_t lkeys[kMQ][kScoreKeysPerBlock];
+  __shared__ int32_t tbl[kScoreKeysPerBlock / 2 + 2];
+  __shared__ uint32_t wtot[kScoreParts * 4];
+  __shared__ int32_t gseq[kMQ], gnv[kMQ];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int hf = lane >> 5;
+  const int base = blockIdx.x * kScoreKeysPerBlock;
+  const int i = blockIdx.y * kMQ + wave;   // this wave's query
+  const bool has_q = i < a.n_q;
+  const int iq = min(i, a.n_q - 1);        // in-bounds row for the loads of an absent query
+  const int seq = a.qd.q_seq ? a.qd.q_seq[iq] : iq;
+  const int p = a.qd.q_pos[iq];
+  const int nv = has_q ? min(n_visible(p, a.pool.ratio, a.window),
+                             n_visible(a.max_pos, a.pool.ratio, a.window)) : 0;
+  const int end_w = min(nv, base + kScoreKeysPerBlock);   // this wave's keys: [base, end_w)
+  if (lane == 0) {
+    gseq[wave] = has_q ? seq : -1;
+    gnv[wave] = nv;
+  }
+  if (a.part_hist)
+    for (int j = tid; j < kMQ * kScoreParts * kTopBins; j += 256) (&lhist[0][0])[j] = 0;
+
+  // this wave's query and head weights (as in score_mfma_dma)
+  bf16x8 qa[2][8];
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)iq * kMfmaHeads * kMfmaDim;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qa[mb][s] = *reinterpret_cast<const bf16x8*>(q + (32 * mb + col) * kMfmaDim + 64 * hf + 8 * s);
+  float wv[2][16];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      wv[mb][r] = a.w[(int64_t)iq * kMfmaHeads + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3)];
+  __syncthreads();   // gseq / gnv / histograms ready
+
+  const int per_block = a.pool.per_block;   // 256 / ratio: a power of two
+  const int pb_shift = __builtin_ctz(per_block);
+  const int lb0 = base >> pb_shift;
+  const uint32_t st0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&stage[0][0]);
+  uint32_t roff[8];   // operand read offsets within a tile: key col, chunk (8hf + s) ^ (col % 16)
+#pragma unroll
+  for (int s = 0; s < 8; ++s) roff[s] = col * 256 + 16 * ((8 * hf + s) ^ (col & 15));
+
+  for (int w0 = 0; w0 < kMQ; ++w0) {
+    const int sq = gseq[w0];
+    bool lead = sq >= 0;   // w0 is the first wave of its sequence
+    int nv_s = 0;
+    for (int w1 = 0; w1 < kMQ; ++w1) {
+      if (gseq[w1] != sq) continue;
+      if (w1 < w0) lead = false;
+      nv_s = max(nv_s, gnv[w1]);
+    }
+    const int end_s = min(nv_s, base + kScoreKeysPerBlock);
+    if (!lead || base >= end_s) continue;   // uniform
+    const bool mine = has_q && seq == sq;   // uniform per wave
+    __syncthreads();   // the previous group's readers of tbl and of the tiles are done
+    const int n_lb = ((end_s - 1) >> pb_shift) - lb0 + 1;
+    for (int j = tid; j < n_lb; j += 256) {
+      const int lb = lb0 + j;
+      const int phys = lb < a.pool.max_blocks ? a.pool.block_table[(int64_t)sq * a.pool.max_blocks + lb] : -1;
+      tbl[j] = (phys >= 0 && phys < a.pool.num_blocks) ? phys : -1;
+    }
+    __syncthreads();
+    const int n_tiles = (end_s - base + 31) / 32;
+    // tile t into stage t % kMStages: this wave moves keys 8 wave .. 8 wave + 7 (two loads of
+    // four keys); keys past the group's range re-read its last key (in bounds, unused)
+    auto issue = [&](int t) {
+      const int tb = base + 32 * t;
+      const uint32_t lds = st0 + (t % kMStages) * 8192;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = 8 * wave + 4 * j + (lane >> 4);
+        const int g = min(tb + n, end_s - 1);
+        const int phys = tbl[(g >> pb_shift) - lb0];
+        const int64_t e = phys >= 0 ? ((int64_t)phys << pb_shift) + (g & (per_block - 1)) : 0;
+        const int c = (lane & 15) ^ (n & 15);
+        lds_dma16(a.pool.data + e * a.pool.entry_bytes + 16 * c, lds + 1024 * (2 * wave + j));
+      }
+    };
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // tbl reads of the address math above
+#pragma unroll
+    for (int t = 0; t < kMStages - 1; ++t) issue(t);
+    for (int t = 0; t < n_tiles; ++t) {
+      wait_vmcnt<2 * (kMStages - 2)>();   // this wave's loads of tile t are done
+      __syncthreads();                    // everyone's are, and tile t - 1 has been read
+      issue(t + kMStages - 1);
+      if (mine) {
+        const uint8_t* sb = &stage[t % kMStages][0];
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(sb + roff[s]);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], b, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], b, acc1, 0, 0, 0);
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          part = fmaf(wv[0][r], fmaxf(acc0[r], 0.f), part);
+          part = fmaf(wv[1][r], fmaxf(acc1[r], 0.f), part);
+        }
+        part += __shfl_xor(part, 32, 64);
+        const int g = base + 32 * t + col;
+        if (hf == 0 && g < end_w) {
+          const bool valid = tbl[(g >> pb_shift) - lb0] >= 0;
+          const float v = valid ? canonical_zero(part) : -INFINITY;
+          if (a.part_hist) {
+            const uint32_t key = order_key(v);
+            lkeys[wave][g - base] = key;
+            atomicAdd(&lhist[wave][((g - base) / kScorePartKeys) * kTopBins + (key >> (32 - kTopBits))], 1u);
+          } else {
+            a.scores[(int64_t)i * a.ld + g] = v;
+          }
+        }
+      }
+    }
+    wait_vmcnt<0>();   // no load may still be writing a tile when the ring is reused
+  }
+  if (a.part_hist) {
+    // the tiles are free now: the sorted pairs use them
+    for (int w = 0; w < kMQ; ++w) {
+      const int qi = blockIdx.y * kMQ + w;
+      const int e = min(gnv[w], base + kScoreKeysPerBlock);
+      if (gseq[w] < 0 || base >= e) continue;   // uniform
+      finish_parts<kScoreParts>(a, qi, blockIdx.x * kScoreParts, base, e, lkeys[w], lhist[w],
+                                reinterpret_cast<uint2*>(&stage[0][0]), wtot);
+    }
+  }
+}
+
 // One thread per key (workgroups of kScorePartKeys keys, four per thread); query rows and weights
 // staged in LDS as float.
 __global__ __launch_bounds__(256) void score_generic(ScoreArgs a) {
@@ -499,10 +654,15 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s) {
                     (a.pool.dtype == BF16 || a.pool.dtype == FP4);
   if (mfma) {
     dim3 grid((max_nv + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock, a.n_q);
-    if (a.pool.dtype == BF16)
+    if (a.pool.dtype == BF16 && a.qd.q_seq && a.n_q >= kMultiMinQueries) {
+      // a prefill chunk: runs of queries of one sequence share the key stream, kMQ per workgroup
+      grid.y = (a.n_q + kMQ - 1) / kMQ;
+      hipLaunchKernelGGL(score_mfma_multi, grid, dim3(256), 0, s, a);
+    } else if (a.pool.dtype == BF16) {
       hipLaunchKernelGGL(score_mfma_dma, grid, dim3(256), 0, s, a);
-    else
+    } else {
       hipLaunchKernelGGL(score_mfma<true>, grid, dim3(256), 0, s, a);
+    }
   } else {
     dim3 grid((max_nv + kScorePartKeys - 1) / kScorePartKeys, a.n_q);
     size_t lds = sizeof(float) * ((size_t)a.n_heads * a.pool.dim + a.n_heads);

@@ -464,6 +464,48 @@ def test_prefill_full_size_sampled(gpu_lib):
             assert_abs_close(to_f64(out)[i], want)
 
 
+def test_prefill_indexer_mixed_sequences(gpu_lib):
+    """Prefill queries of three sequences in one indexer launch of 283 queries (the last group of
+    four is ragged): 37 of sequence 0, then 20 of sequences 1 and 2 interleaved query by query,
+    then the rest of each. Groups of four then hold one, two or three sequences. Each sampled
+    query's top-64 must equal that of a launch holding the query alone (the one-query kernel), and
+    agree with the oracle's selection."""
+    hyb = gpu_lib
+    g = W.generator(92, 0, 0, DEV)
+    lens, counts = [2003, 701, 4999], [37, 101, 145]
+    rows = [(0, p) for p in range(lens[0] - counts[0], lens[0])]
+    tail = [[(s, p) for p in range(lens[s] - counts[s], lens[s])] for s in (1, 2)]
+    for j in range(20):
+        rows += [tail[0][j], tail[1][j]]
+    rows += tail[0][20:] + tail[1][20:]
+    n = len(rows)
+    assert n == 283
+    mb = -(-max(lens) // 256)
+    ip = W.make_pool("bf16", 128, 4, [W.blocks_for_entries(L // 4, 4) for L in lens], mb, g, DEV)
+    iq = W.to_storage(W.randn((n, 64, 128), g, DEV), "bf16")
+    iw = W.randn((n, 64), g, DEV) / math.sqrt(128.0)
+    qseq, pos = ints([s for s, _ in rows]), ints([p for _, p in rows])
+    max_pos, k = max(lens) - 1, 64
+    topk = torch.empty(n, k, dtype=I32, device=DEV)
+    hyb.hyb_index_topk(iq, iw, pos, max_pos, ip, k, topk, q_seq=qseq)
+    sample = [0, 1, 35, 36, 37, 38, 39, 40, 76, 77, 78, 79, 120, 157, 158, 200, 279, 280, 281, 282]
+    alone = torch.empty(len(sample), k, dtype=I32, device=DEV)
+    for j, i in enumerate(sample):
+        hyb.hyb_index_topk(iq[i:i + 1], iw[i:i + 1], pos[i:i + 1], max_pos, ip, k, alone[j:j + 1],
+                           q_seq=qseq[i:i + 1])
+    sync()
+    tk, al = topk.cpu().numpy(), alone.cpu().numpy()
+    for j, i in enumerate(sample):
+        assert list(tk[i]) == list(al[j]), f"query {i} (sequence {rows[i][0]})"
+    ipo = to_oracle_pool(ip)
+    iq64, iw64 = to_f64(iq), iw.cpu().double().numpy()
+    for i in (0, 36, 37, 38, 282):
+        s, p = rows[i]
+        keys = O.pool_entries(ipo, s, range(O.n_visible(p, 4, 128)))
+        sc = O.indexer_scores(iq64[i], iw64[i], keys)
+        check_topk_set(tk[i], O.topk_select(sc, k), sc, topk_delta(iq64[i], iw64[i], keys), k)
+
+
 # ================================================================ quantised mixed-length decode
 def _quant_check(hyb, c4, c128, seqs4, seqs128):
     check_sparse(hyb, c4, seqs4)
