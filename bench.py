@@ -363,7 +363,8 @@ def quant_mixed(torch, hyb, W, BM, args):
 # ------------------------------------------------------------------------------------------
 def cpu_baseline(torch, W, BM, rep, budget):
     """The float64 oracle, as it stands, on the same C4 decode step (compress the new token,
-    indexer, top-k, attention), sequence by sequence until the time budget is spent."""
+    indexer, top-k, attention), sequence by sequence, cycling over the batch until the time budget
+    is spent."""
     import numpy as np
     import oracle as O
 
@@ -383,7 +384,8 @@ def cpu_baseline(torch, W, BM, rep, budget):
     scale = 1.0 / math.sqrt(wl.dim)
     done = 0
     t0 = time.perf_counter()
-    for b in range(wl.batch):
+    while time.perf_counter() - t0 < budget:   # passes over the batch until the budget is spent
+        b = done % wl.batch
         L = wl.seq_lens_host[b]
         p = L - 1
         toks = np.concatenate([state[b, :3], x_new[b][None]])
@@ -393,8 +395,6 @@ def cpu_baseline(torch, W, BM, rep, budget):
         sel = O.topk_select(sc, wl.k)
         O.hybrid_query(q[b], p, b, swa, comp, 128, scale, 64, 1e4, sel)
         done += 1
-        if time.perf_counter() - t0 > budget:
-            break
     secs = time.perf_counter() - t0
     threads = os.cpu_count() or 1
     try:
@@ -405,8 +405,8 @@ def cpu_baseline(torch, W, BM, rep, budget):
     except Exception:
         pass
     return {"value": done / secs, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of 16 sequences of the C4 decode step (131072-token contexts), "
-                      f"one at a time, {secs:.1f} s, numpy float64"}
+            "sample": f"{done} query tokens of the C4 decode step (the batch's 16 sequences of "
+                      f"131072 tokens in turn, one at a time), {secs:.1f} s, numpy float64"}
 
 
 def main():

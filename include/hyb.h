@@ -62,7 +62,8 @@ typedef enum hyb_status {
 
 /* Element storage types. FP8_E4M3 = OCP E4M3 ("fn": no inf, max 448) with one float32 scale per
  * entry; FP4_E2M1 = OCP MX E2M1 with one E8M0 scale byte per 32 elements (value =
- * e2m1 * 2^(scale - 127)). [vLLM]: "fp8 attention cache + fp4 indexer cache". */
+ * e2m1 * 2^(scale - 127); scale bytes 27..187, i.e. 2^-100 .. 2^60, for which every value is
+ * widened to bf16 exactly). [vLLM]: "fp8 attention cache + fp4 indexer cache". */
 typedef enum hyb_dtype {
   HYB_F32 = 0,
   HYB_BF16 = 1,
