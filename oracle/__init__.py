@@ -27,5 +27,6 @@ pin are marked "parity unpinned" in their docstrings.
 """
 
 from .formats import (bf16_bits_to_f64, e2m1_to_f64, e4m3fn_to_f64, e8m0_to_f64,  # noqa: F401
-                      round_to_bf16_bits)
+                      encode_e2m1, encode_e4m3fn, f32_quotient, mx_exponent, quantize_fp4_row,
+                      quantize_fp8_row, round_to_bf16_bits)
 from .hyb_oracle import *  # noqa: F401,F403

@@ -14,6 +14,8 @@ Each decoder is written from the bit-field definition (not a table) so that the 
 pins in ``tests/test_oracle_formats.py`` compare two independent descriptions.
 """
 
+import math
+
 import numpy as np
 
 
@@ -76,3 +78,86 @@ def unpack_fp4_row(packed_row: np.ndarray, scales_row: np.ndarray, dim: int) -> 
     vals = e2m1_to_f64(codes)
     sc = e8m0_to_f64(np.asarray(scales_row))
     return vals * np.repeat(sc, 32)[:dim]
+
+
+# --------------------------------------------------------------------------------------------
+# Encoders (quantise-on-insert and the fp8 attention output). The pages name the fp8 / fp4
+# caches but not how values are quantised; readings taken here:
+#   * fp8 row (one attention-cache entry, or one head's output row): scale = amax / 448 in
+#     float32 (1 when the row is all zero), code = E4M3 nearest to x / scale (float32 quotient),
+#     ties to the even code, magnitudes beyond 448 saturating to 448.
+#   * fp4 block of 32 (indexer keys, OCP MX rule): shared exponent e = floor(log2 amax) - 2,
+#     clamped to [-100, 60] (an all-zero block takes -100), stored as the E8M0 byte e + 127;
+#     code = E2M1 nearest to x / 2**e, ties to the even code, saturating at 6.
+# The encoders search the decoders' code tables for the nearest value (independent of how a
+# kernel rounds). Float32 steps are taken as float64 operations rounded once to float32, which
+# equals the float32 operation for a quotient of float32 operands (53 >= 2 * 24 + 2).
+# --------------------------------------------------------------------------------------------
+_E4M3_POS = e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))      # codes 0..126: 0 .. 448
+_E2M1_POS = e2m1_to_f64(np.arange(8))                             # codes 0..7: 0 .. 6
+
+
+def _nearest_even_code(mag: np.ndarray, table: np.ndarray) -> np.ndarray:
+    """Index of the table value nearest to each magnitude; equal distances go to the even index
+    (the code whose mantissa LSB is 0). Magnitudes beyond the last value take the last index."""
+    mag = np.asarray(mag, dtype=np.float64)
+    d = np.abs(mag[..., None] - table)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    idx = np.arange(table.size)
+    even = cand & (idx % 2 == 0)
+    pick = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    return np.where(mag >= table[-1], table.size - 1, pick)
+
+
+def f32_quotient(x, s) -> np.ndarray:
+    """float32(x / s) for float32 x and s (the float32 division, correctly rounded)."""
+    return (np.asarray(x, np.float32).astype(np.float64) /
+            np.asarray(s, np.float32).astype(np.float64)).astype(np.float32)
+
+
+def encode_e4m3fn(v) -> np.ndarray:
+    """float values -> E4M3 codes (uint8): nearest, ties to even, saturating at +-448.
+    Negative values (and -0) keep the sign bit."""
+    v = np.asarray(v, dtype=np.float64)
+    code = _nearest_even_code(np.abs(v), _E4M3_POS).astype(np.uint8)
+    return np.where(np.signbit(v), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def encode_e2m1(v) -> np.ndarray:
+    """float values -> E2M1 codes (low 4 bits): nearest, ties to even, saturating at +-6."""
+    v = np.asarray(v, dtype=np.float64)
+    code = _nearest_even_code(np.abs(v), _E2M1_POS).astype(np.uint8)
+    return np.where(np.signbit(v), code | np.uint8(0x8), code).astype(np.uint8)
+
+
+def quantize_fp8_row(x):
+    """One row (float32 values) -> (E4M3 codes uint8[D], float32 scale)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    scale = np.float32(np.float64(amax) / 448.0) if amax > 0 else np.float32(1.0)
+    return encode_e4m3fn(f32_quotient(x, scale)), scale
+
+
+def mx_exponent(amax: float) -> int:
+    """Shared exponent of one fp4 block: floor(log2 amax) - 2 clamped to [-100, 60]."""
+    if not amax > 0:
+        return -100
+    m, e = math.frexp(amax)          # amax = m * 2**e, 0.5 <= m < 1: floor(log2 amax) = e - 1
+    return int(min(60, max(-100, (e - 1) - 2)))
+
+
+def quantize_fp4_row(x):
+    """One row (float32 values, D % 32 == 0) -> (packed uint8[D/2], E8M0 uint8[D/32]).
+    Element 2j in the low nibble of byte j."""
+    x = np.asarray(x, dtype=np.float32)
+    d = x.size
+    codes = np.empty(d, dtype=np.uint8)
+    sc = np.empty(d // 32, dtype=np.uint8)
+    for blk in range(d // 32):
+        xb = x[32 * blk:32 * blk + 32].astype(np.float64)
+        e = mx_exponent(float(np.abs(xb).max()))
+        sc[blk] = e + 127
+        codes[32 * blk:32 * blk + 32] = encode_e2m1(xb / 2.0 ** e)   # exact: power-of-two scale
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    return packed, sc

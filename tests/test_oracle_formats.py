@@ -126,3 +126,98 @@ def test_round_to_bf16_matches_torch_on_float32_values():
     ours = round_to_bf16_bits(x.numpy().astype(np.float64))
     ref = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(ours, ref)
+
+
+# ------------------------------------------------------------------ encoders (quantise-on-insert)
+from oracle.formats import (encode_e2m1, encode_e4m3fn, mx_exponent, quantize_fp4_row,  # noqa: E402
+                            quantize_fp8_row)
+
+
+def _e4m3_test_values():
+    pos = e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))            # every finite magnitude
+    mids = (pos[:-1] + pos[1:]) / 2                                   # every tie
+    rng = np.random.default_rng(5)
+    rand = np.exp2(rng.uniform(-12, np.log2(448.0), 20000)) * rng.choice([-1, 1], 20000)
+    near = np.concatenate([np.nextafter(mids, 0), np.nextafter(mids, 1)])
+    v = np.concatenate([pos, -pos, mids, -mids, near, rand]).astype(np.float32)
+    return v[np.abs(v) <= 448.0]
+
+
+def test_e4m3_encoder_matches_torch_cast():
+    """Round to nearest even inside the finite range: torch's float32 -> float8_e4m3fn cast is an
+    independent implementation of the same rounding."""
+    v = _e4m3_test_values()
+    ours = encode_e4m3fn(v)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (ours == ref).all()
+
+
+def test_e4m3_encoder_saturates_and_keeps_sign():
+    assert list(encode_e4m3fn([448.0, 449.0, 1e9, -500.0])) == [0x7E, 0x7E, 0x7E, 0xFE]
+    assert encode_e4m3fn([-0.0])[0] == 0x80 and encode_e4m3fn([0.0])[0] == 0
+    # the smallest subnormal is 2^-9; half of it is a tie that goes to zero, just above goes up
+    assert list(encode_e4m3fn([2.0 ** -10, 2.0 ** -10 * 1.0001, 2.0 ** -9])) == [0, 1, 1]
+
+
+def test_e2m1_encoder_hand_values():
+    """OCP MX E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 (codes 0..7): each tie goes to the code
+    with mantissa bit 0, values above 6 saturate."""
+    v = [0.0, 0.25, 0.26, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 5.01, 6.0, 100.0]
+    want = [0, 0, 1, 1, 2, 2, 2, 3, 4, 4, 4, 5, 6, 6, 6, 7, 7, 7]
+    assert list(encode_e2m1(v)) == want
+    assert list(encode_e2m1([-0.75, -6.5])) == [0x8 | 2, 0x8 | 7]
+
+
+def test_encoders_round_trip_every_code():
+    c8 = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert (encode_e4m3fn(e4m3fn_to_f64(c8)) == c8).all()
+    c4 = np.arange(16, dtype=np.uint8)
+    assert (encode_e2m1(e2m1_to_f64(c4)) == c4).all()
+
+
+def test_mx_exponent_hand_values():
+    assert mx_exponent(6.0) == 0 and mx_exponent(4.0) == 0 and mx_exponent(7.99) == 0
+    assert mx_exponent(8.0) == 1 and mx_exponent(1.0) == -2 and mx_exponent(0.75) == -3
+    assert mx_exponent(0.0) == -100 and mx_exponent(2.0 ** -300) == -100
+    assert mx_exponent(2.0 ** 100) == 60
+
+
+def test_quantize_fp8_row_error_bound_and_exact_rows():
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        x = (rng.standard_normal(512) * np.exp2(rng.uniform(-20, 20))).astype(np.float32)
+        codes, s = quantize_fp8_row(x)
+        assert s == np.float32(np.float64(np.abs(x).max()) / 448.0)
+        y = e4m3fn_to_f64(codes) * np.float64(s)
+        v = x.astype(np.float64) / np.float64(s)
+        # half an E4M3 step at v's binade (subnormal step 2^-9), plus the float32 quotient's rounding
+        step = np.exp2(np.maximum(np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -6))), -6) - 3)
+        assert (np.abs(y - x) <= (0.5 * step + 2.0 ** -23 * np.abs(v)) * np.float64(s)).all()
+    # a row whose maximum is 448 has scale 1 and is its own code image
+    x = e4m3fn_to_f64(np.arange(0, 0x7F, dtype=np.uint8)).astype(np.float32)
+    codes, s = quantize_fp8_row(x)
+    assert s == 1.0 and (codes == np.arange(0, 0x7F)).all()
+    codes, s = quantize_fp8_row(np.zeros(64, np.float32))
+    assert s == 1.0 and (codes == 0).all()
+
+
+def test_quantize_fp4_row_layout_and_error_bound():
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(128) * np.repeat(np.exp2(rng.uniform(-8, 8, 4)), 32)).astype(np.float32)
+    packed, sc = quantize_fp4_row(x)
+    assert packed.shape == (64,) and sc.shape == (4,)
+    y = unpack_fp4_row(packed, sc, 128)
+    for blk in range(4):
+        xb = x[32 * blk:32 * blk + 32].astype(np.float64)
+        e = mx_exponent(np.abs(xb).max())
+        assert sc[blk] == e + 127
+        v = np.abs(xb) / 2.0 ** e
+        # grid steps: 0.5 below 2, 1 in [2, 4), 2 from 4; saturation at 6 beyond
+        step = np.where(v < 2, 0.5, np.where(v < 4, 1.0, 2.0))
+        err = np.abs(y[32 * blk:32 * blk + 32] - xb) / 2.0 ** e
+        assert (err <= np.maximum(0.5 * step, v - 6.0) + 1e-12).all()
+    # element 2j in the low nibble of byte j
+    x = np.zeros(32, np.float32)
+    x[0], x[1], x[31] = 4.0, -1.0, 0.5
+    packed, sc = quantize_fp4_row(x)
+    assert sc[0] == 127 and packed[0] == (0x6 | (0xA << 4)) and packed[15] == (0x1 << 4)
