@@ -122,8 +122,15 @@ const char* hyb_last_error(void);
  *   max_new_tokens host bound on cu_seqlens[b+1] - cu_seqlens[b] (sizes the grid)
  *   state         [batch][ratio][dim] in x_dtype: raw tokens of the in-progress group
  *   state_logits  float [batch][ratio] (gate mode), NULL for mean
- *   out           host descriptor of the C4 / C128 pool (ratio 4 or 128, dtype F32 or BF16,
- *                 dim = x's dim, block_table rows indexed by b)
+ *   out           host descriptor of the C4 / C128 pool (ratio 4 or 128, dim = x's dim,
+ *                 block_table rows indexed by b); dtype F32 or BF16, or quantised as stored
+ *                 (quantise-on-insert, [vLLM] "fp8 attention cache + fp4 indexer cache"):
+ *                 FP8_E4M3 - one float32 scale per entry, scale = amax / 448 (1 for an all-zero
+ *                   entry), code = E4M3 nearest to value / scale (float32 quotient), ties to
+ *                   the even code, saturating at 448;
+ *                 FP4_E2M1 (dim % 32 == 0; compressed indexer keys) - per 32 values the E8M0
+ *                   byte e + 127 with e = floor(log2 amax) - 2 clamped to [-100, 60], code =
+ *                   E2M1 nearest to value * 2^-e, ties to the even code, saturating at 6.
  * ------------------------------------------------------------------------------------------ */
 int32_t hyb_compress(const void* x, int32_t x_dtype, const float* gate_logits,
                      const int32_t* cu_seqlens, const int32_t* start_pos, int32_t batch,
@@ -153,7 +160,8 @@ typedef struct hyb_compress_call {
 /* --------------------------------------------------------------------------------------------
  * hyb_swa_insert - raw sliding-window entries s_t = RoPE(x_t, t) (no norm) written to the raw
  * pool (ratio 1) at position t. The "KV RoPE + K insert" step of [vLLM]'s fused-kernel list.
- * Arguments as in hyb_compress; swa->dtype F32 or BF16.
+ * Arguments as in hyb_compress; swa->dtype F32, BF16 or FP8_E4M3 (dim <= 2048; each entry
+ * quantised as stored, with the FP8_E4M3 rule of hyb_compress).
  * ------------------------------------------------------------------------------------------ */
 int32_t hyb_swa_insert(const void* x, int32_t x_dtype, const int32_t* cu_seqlens,
                        const int32_t* start_pos, int32_t batch, int32_t max_new_tokens,

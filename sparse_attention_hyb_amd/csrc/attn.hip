@@ -998,7 +998,7 @@ hipError_t launch_attention_compress(const AttnArgs& a, const CompressArgs& c, h
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   const bool fuse = a.n_q > 0 && a.use_mfma && !writes_output(a) && c.batch > 0 && c.max_new_tokens > 0 && D <= 512 &&
                     D % (c.x_dtype == F32 ? 4 : 8) == 0 && al16(c.x) && al16(c.state) &&
-                    al16(c.out.data) && (r == 4 || r == 128);
+                    al16(c.out.data) && (r == 4 || r == 128) && (c.out.dtype == F32 || c.out.dtype == BF16);
   if (!fuse) {
     hipError_t e = launch_attention(a, s);
     if (e != hipSuccess) return e;

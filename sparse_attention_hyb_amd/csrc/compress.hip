@@ -10,10 +10,10 @@
 
 namespace hyb {
 
-template <typename T, int kVec, int kJ, int kRB>
+template <typename T, int kVec, int kJ, int kRB, bool kQuant>
 __global__ __launch_bounds__(1024) void compress_kernel(CompressArgs a) {
   extern __shared__ float lds[];   // [nw - 1][D] partials, then cs pairs
-  compress_group<T, kVec, kJ, kRB, 1>(a, blockIdx.x, blockIdx.y, lds);
+  compress_group<T, kVec, kJ, kRB, 1, kQuant>(a, blockIdx.x, blockIdx.y, lds);
 }
 
 // Raw window entries: s_t = RoPE(x_t, t), stored at position t of the ratio-1 pool.
@@ -50,6 +50,47 @@ __global__ __launch_bounds__(256) void swa_insert_kernel(CompressArgs a) {
   }
 }
 
+// Window entries into an FP8_E4M3 pool (quantise-on-insert): one wave per token (dim <= 2048:
+// up to 16 element pairs per lane), the rotated row quantised with one scale per entry.
+constexpr int kInsertWaves = 4;
+
+template <typename T>
+__global__ __launch_bounds__(64 * kInsertWaves) void swa_insert_fp8_kernel(CompressArgs a) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * kInsertWaves + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int c0 = a.cu_seqlens[b];
+  if (i >= a.cu_seqlens[b + 1] - c0) return;   // whole waves
+  const int t = a.start_pos[b] + i;
+  const int64_t idx = entry_index(a.out, b, t);
+  if (idx < 0) return;
+  const int D = a.out.dim;
+  const int npairs = D / 2;
+  const int rope_lo = D - a.rope_dim;
+  const T* row = reinterpret_cast<const T*>(a.x) + (int64_t)(c0 + i) * D;
+  float y[16][2];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int pi = lane + 64 * j;
+    float2 v = make_float2(0.f, 0.f);
+    if (pi < npairs) {
+      v = load_pair<T>(row, 2 * pi);
+      const int d = 2 * pi;
+      if (d >= rope_lo) {
+        float c, s;
+        rope_cs_theta((double)t, a.theta[(d - rope_lo) >> 1], &c, &s);
+        const float z0 = v.x * c - v.y * s;
+        const float z1 = v.x * s + v.y * c;
+        v.x = z0;
+        v.y = z1;
+      }
+    }
+    y[j][0] = v.x;
+    y[j][1] = v.y;
+  }
+  store_quantized<2, 16>(a.out, idx, lane, npairs, y);
+}
+
 namespace {
 template <typename T, int kVec, int kJ>
 hipError_t launch_compress_t(const CompressArgs& a, int rows_per_wave, dim3 grid, dim3 block,
@@ -58,10 +99,17 @@ hipError_t launch_compress_t(const CompressArgs& a, int rows_per_wave, dim3 grid
   // rows of up to 8 words, fewer for wider rows (whose accumulators take registers too)
   constexpr int kWords = kJ * chunk_words<T, kVec>();
   constexpr int kRB = kWords >= 32 ? 1 : (kWords >= 16 ? 2 : (64 / kWords > 8 ? 8 : 64 / kWords));
-  if (rows_per_wave % kRB == 0)
-    hipLaunchKernelGGL((compress_kernel<T, kVec, kJ, kRB>), grid, block, lds, s, a);
-  else
-    hipLaunchKernelGGL((compress_kernel<T, kVec, kJ, 1>), grid, block, lds, s, a);
+  const bool quant = a.out.dtype == FP8 || a.out.dtype == FP4;
+  if (quant) {
+    if (rows_per_wave % kRB == 0)
+      hipLaunchKernelGGL((compress_kernel<T, kVec, kJ, kRB, true>), grid, block, lds, s, a);
+    else
+      hipLaunchKernelGGL((compress_kernel<T, kVec, kJ, 1, true>), grid, block, lds, s, a);
+  } else if (rows_per_wave % kRB == 0) {
+    hipLaunchKernelGGL((compress_kernel<T, kVec, kJ, kRB, false>), grid, block, lds, s, a);
+  } else {
+    hipLaunchKernelGGL((compress_kernel<T, kVec, kJ, 1, false>), grid, block, lds, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -97,6 +145,14 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_swa_insert(const CompressArgs& a, hipStream_t s) {
+  if (a.out.dtype == FP8) {
+    dim3 grid((a.max_new_tokens + kInsertWaves - 1) / kInsertWaves, a.batch);
+    if (a.x_dtype == F32)
+      hipLaunchKernelGGL(swa_insert_fp8_kernel<float>, grid, dim3(64 * kInsertWaves), 0, s, a);
+    else
+      hipLaunchKernelGGL(swa_insert_fp8_kernel<uint16_t>, grid, dim3(64 * kInsertWaves), 0, s, a);
+    return hipGetLastError();
+  }
   dim3 grid((a.max_new_tokens + kInsertTokens - 1) / kInsertTokens, a.batch);
   if (a.x_dtype == F32)
     hipLaunchKernelGGL(swa_insert_kernel<float>, grid, dim3(256), 0, s, a);

@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "quant_dev.h"
 
 namespace hyb {
 
@@ -151,8 +152,9 @@ __host__ __device__ inline int pooled_waves(int ratio, int dim) {
 // formed while the row loads are in flight.
 // The group is group gi (counted from the first group the call touches) of sequence b; the rows
 // per virtual wave, ratio / V, are a multiple of kRB, the rows per virtual wave and batch (the
-// launches see to it); lds holds (nw - 1) * dim + 128 floats.
-template <typename T, int kVec, int kJ, int kRB, int kV>
+// launches see to it); lds holds (nw - 1) * dim + 128 floats. kQuant: the pool is FP8_E4M3 or
+// FP4_E2M1 and the entry is quantised as it is stored (float32 pools and bf16 pools otherwise).
+template <typename T, int kVec, int kJ, int kRB, int kV, bool kQuant = false>
 __device__ __forceinline__ void compress_group(const CompressArgs& a, int gi, int b, float* lds) {
   constexpr int kW = chunk_words<T, kVec>();
   const int lane = threadIdx.x & 63;
@@ -336,9 +338,15 @@ __device__ __forceinline__ void compress_group(const CompressArgs& a, int gi, in
               y[e] = y0;
               y[e + 1] = y1;
             }
-            store_vec<kVec>(a.out, idx, c * kVec, y);
+            if constexpr (kQuant) {
+#pragma unroll
+              for (int e = 0; e < kVec; ++e) tot[j][e] = y[e];
+            } else {
+              store_vec<kVec>(a.out, idx, c * kVec, y);
+            }
           }
         }
+        if constexpr (kQuant) store_quantized<kVec, kJ>(a.out, idx, lane, nchunks, tot);
       }
     }
   }

@@ -139,7 +139,7 @@ int check_compress(const char* op, const hyb_compress_call& c, hyb::CompressArgs
     return fail(HYB_EINVAL, "%s: softmax-gate pooling needs gate_logits and state_logits", op);
   if (!(c.eps >= 0.f) || !std::isfinite(c.eps)) return fail(HYB_EINVAL, "%s: eps must be >= 0", op);
   hyb::PoolDev po{};
-  HYB_TRY(check_pool(c.out, op, "out", false, false, 2 | 4, &po));
+  HYB_TRY(check_pool(c.out, op, "out", true, true, 2 | 4, &po));
   if (po.dim > 2048) return fail(HYB_ENOTSUP, "%s: dim %d > 2048", op, po.dim);
   HYB_TRY(check_rope(op, c.rope_dim, c.rope_base, po.dim));
   *a = hyb::CompressArgs{c.x, c.x_dtype, c.gate_logits, c.cu_seqlens, c.start_pos, c.batch,
@@ -272,7 +272,9 @@ int32_t hyb_swa_insert(const void* x, int32_t x_dtype, const int32_t* cu_seqlens
   const char* op = "hyb_swa_insert";
   HYB_TRY(check_compress_common(op, x, x_dtype, cu_seqlens, start_pos, batch, max_new_tokens));
   hyb::PoolDev ps{};
-  HYB_TRY(check_pool(swa, op, "swa", false, false, 1, &ps));
+  HYB_TRY(check_pool(swa, op, "swa", true, false, 1, &ps));
+  if (ps.dtype == HYB_FP8_E4M3 && ps.dim > 2048)
+    return fail(HYB_ENOTSUP, "%s: FP8_E4M3 window pool dim %d > 2048", op, ps.dim);
   HYB_TRY(check_rope(op, rope_dim, rope_base, ps.dim));
   if (batch == 0 || max_new_tokens == 0) return HYB_OK;
   hyb::CompressArgs a{x, x_dtype, nullptr, cu_seqlens, start_pos, batch, max_new_tokens,

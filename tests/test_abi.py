@@ -107,7 +107,7 @@ def test_attn_decode_compress_validation(lib):
     assert call(state=None) == hyb.HYB_EINVAL
     assert call(mode=hyb.POOL_SOFTMAX_GATE) == hyb.HYB_EINVAL         # logits missing
     assert call(o=pool(ratio=1)) == hyb.HYB_EINVAL
-    assert call(o=pool(ratio=128, dtype=hyb.FP8_E4M3)) == hyb.HYB_ENOTSUP
+    assert call(o=pool(ratio=128, dtype=hyb.FP8_E4M3, scale=False)) == hyb.HYB_EINVAL
     assert call(rope=3) == hyb.HYB_EINVAL
     assert call(eps=-1.0) == hyb.HYB_EINVAL
     assert lib.hyb_last_error().decode().startswith("hyb_attn_decode_compress")
@@ -147,7 +147,10 @@ def test_compress_validation(lib):
     assert call(mode=7) == hyb.HYB_EINVAL
     assert call(mode=hyb.POOL_SOFTMAX_GATE) == hyb.HYB_EINVAL         # logits missing
     assert call(o=pool(ratio=1)) == hyb.HYB_EINVAL
-    assert call(o=pool(ratio=4, dtype=hyb.FP8_E4M3)) == hyb.HYB_ENOTSUP
+    # quantised pools (fp8 entries, fp4 keys) need their scale arrays; fp4 rows whole blocks of 32
+    assert call(o=pool(ratio=4, dtype=hyb.FP8_E4M3, scale=False)) == hyb.HYB_EINVAL
+    assert call(o=pool(ratio=4, dtype=hyb.FP4_E2M1, scale=False)) == hyb.HYB_EINVAL
+    assert call(o=pool(ratio=4, dim=80, dtype=hyb.FP4_E2M1)) == hyb.HYB_EINVAL
     assert call(o=pool(ratio=4, dim=4096)) == hyb.HYB_ENOTSUP
     assert call(rope=3) == hyb.HYB_EINVAL
     assert call(eps=-1.0) == hyb.HYB_EINVAL
@@ -158,6 +161,11 @@ def test_compress_validation(lib):
     s = pool(ratio=1)
     assert lib.hyb_swa_insert(FAKE, hyb.BF16, FAKE, FAKE, 2, 4, ctypes.byref(pool(ratio=4)), 64,
                               1e4, None) == hyb.HYB_EINVAL
+    for bad, code in ((pool(ratio=1, dtype=hyb.FP4_E2M1), hyb.HYB_ENOTSUP),   # fp4 is for keys
+                      (pool(ratio=1, dtype=hyb.FP8_E4M3, scale=False), hyb.HYB_EINVAL),
+                      (pool(ratio=1, dtype=hyb.FP8_E4M3, dim=4096), hyb.HYB_ENOTSUP)):
+        assert lib.hyb_swa_insert(FAKE, hyb.BF16, FAKE, FAKE, 2, 4, ctypes.byref(bad), 64, 1e4,
+                                  None) == code
     assert lib.hyb_swa_insert(FAKE, hyb.BF16, FAKE, FAKE, 0, 4, ctypes.byref(s), 64, 1e4,
                               None) == hyb.HYB_OK
 

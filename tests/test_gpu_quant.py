@@ -1,0 +1,193 @@
+"""GPU parity of quantise-on-insert: window entries into an fp8 pool and compressed entries into
+fp8 (attention cache) and fp4 (indexer keys) pools, through the C ABI, against the oracle's
+encoders and entries.
+
+Where the stored row is exactly the input (window insert without rotation) the codes and scales
+must equal the oracle's encoder bit for bit. Where the row is computed (rotation, pooling and
+normalisation in float32 against the oracle's float64), a code may differ from the oracle's
+encoding of its own row only where that row lies within the float32 error of a rounding
+boundary: the decoded values are checked against the oracle's entries to half a code step plus
+that error, and the scales / shared exponents against the oracle's row maxima.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_hyb_amd import workloads as W
+from tests.conftest import to_f64, to_oracle_pool
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+I32 = torch.int32
+
+
+def ints(v):
+    return torch.tensor([int(a) for a in v], dtype=I32, device=DEV)
+
+
+def stored(pt):
+    """(data, scale, block table) of a pool on the host, as stored."""
+    return pt.data.cpu().numpy(), pt.scale.cpu().numpy(), pt.block_table.cpu().numpy()
+
+
+def raw_entry(host, ratio, seq, g):
+    data, scale, table = host
+    per = 256 // ratio
+    phys = table[seq, g // per]
+    return data[phys, g % per], scale[phys, g % per]
+
+
+def e4m3_step(v):
+    """Spacing of E4M3 values at magnitude |v| (subnormal spacing 2^-9 below 2^-6)."""
+    return np.exp2(np.maximum(np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -6))), -6) - 3)
+
+
+def check_fp8_rows(codes, scales, ref, err):
+    """Rows stored as fp8 (codes [n, D], scales [n]) against the oracle's float64 rows `ref`,
+    whose float32 computation may be off by `err` per element."""
+    ref = np.asarray(ref, np.float64)
+    amax = np.abs(ref).max(axis=1)
+    s = scales.astype(np.float64)
+    assert np.all(np.abs(s - amax / 448.0) <= (err + 1e-12) / 448.0 + 2.0 ** -23 * s)
+    dec = O.e4m3fn_to_f64(codes) * s[:, None]
+    bound = 0.5 * e4m3_step(ref / s[:, None]) * s[:, None] + 2 * err + 2.0 ** -23 * np.abs(ref)
+    assert np.all(np.abs(dec - ref) <= bound)
+    # codes differ from the oracle's own encoding only at near-ties
+    want = np.stack([O.quantize_fp8_row(r.astype(np.float32))[0] for r in ref])
+    assert np.mean(codes != want) < 0.01
+
+
+# =================================================================== window insert, fp8 pool
+@pytest.mark.parametrize("xdt,D", [("f32", 512), ("bf16", 512), ("f32", 96), ("bf16", 2048)])
+def test_swa_insert_fp8_bit_exact(gpu_lib, xdt, D):
+    """Without rotation (rope_dim 0) a window entry is the token itself, so the stored codes and
+    scale must equal the oracle's fp8 row encoder bit for bit. Three sequences take 300 / 1 / 77
+    new tokens from positions 0 / 1000 / 250 (crossing block boundaries); rows are N(0,1) values
+    times 2^N(0, 13^2); one row is all zero and one holds exact E4M3 ties (its maximum is 448, so
+    its scale is 1 and every quotient is the value itself)."""
+    hyb = gpu_lib
+    g = W.generator(93, D, 0, DEV)
+    n_new, starts = [300, 1, 77], [0, 1000, 250]
+    T = sum(n_new)
+    x = W.randn((T, D), g, DEV) * torch.exp2(W.randn((T, 1), g, DEV) * 13.0)
+    x[5] = 0.0
+    pos = O.e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))
+    ties = ((pos[:-1] + pos[1:]) / 2)[:D - 1]
+    ties = ties * np.where(np.arange(ties.size) % 2, -1.0, 1.0)
+    x[7] = torch.tensor(np.concatenate([[448.0], ties, np.zeros(max(0, D - 1 - ties.size))])[:D],
+                        dtype=torch.float32, device=DEV)
+    x = W.to_storage(x, xdt)
+    mb = (max(s + n for s, n in zip(starts, n_new)) + 255) // 256
+    swa = W.make_pool("fp8", D, 1, [W.blocks_for_positions(s, s + n) for s, n in zip(starts, n_new)],
+                      mb, g, DEV, fill=False)
+    cu = np.cumsum([0] + n_new)
+    hyb.hyb_swa_insert(x, ints(cu), ints(starts), max(n_new), swa, 0)
+    torch.cuda.synchronize()
+    xs = x.float().cpu().numpy()   # exact widening of the stored tokens
+    host = stored(swa)
+    for b in range(3):
+        for i in range(n_new[b]):
+            codes, sc = raw_entry(host, 1, b, starts[b] + i)
+            want_c, want_s = O.quantize_fp8_row(xs[cu[b] + i])
+            assert sc == want_s, (b, i)
+            assert np.array_equal(codes, want_c), (b, i)
+
+
+def test_swa_insert_fp8_rotated(gpu_lib):
+    """With RoPE on the last 64 dims (bf16 tokens, dim 512, positions up to 2^20): decoded entries
+    against the oracle's rotated entries."""
+    hyb = gpu_lib
+    g = W.generator(94, 0, 0, DEV)
+    n_new, starts = [130, 64], [5, (1 << 20) - 64]
+    T, D, rd = sum(n_new), 512, 64
+    x = W.to_storage(W.randn((T, D), g, DEV), "bf16")
+    mb = (max(s + n for s, n in zip(starts, n_new)) + 255) // 256
+    swa = W.make_pool("fp8", D, 1, [W.blocks_for_positions(s, s + n) for s, n in zip(starts, n_new)],
+                      mb, g, DEV, fill=False)
+    cu = np.cumsum([0] + n_new)
+    hyb.hyb_swa_insert(x, ints(cu), ints(starts), max(n_new), swa, rd)
+    torch.cuda.synchronize()
+    x64 = to_f64(x)
+    host = stored(swa)
+    for b in range(2):
+        p = np.arange(starts[b], starts[b] + n_new[b])
+        ref = O.swa_entries(x64[cu[b]:cu[b + 1]], p, rd, 1e4)
+        rows = [raw_entry(host, 1, b, int(t)) for t in p]
+        check_fp8_rows(np.stack([r[0] for r in rows]), np.array([r[1] for r in rows]), ref, 2e-5)
+
+
+# ============================================================= compressor, fp8 and fp4 pools
+def _compress_chunked_and_once(hyb, dtype, ratio, mode, xdt, D, rd, T, seed):
+    """Three sequences compressed in ragged chunks and in one shot into two pools of `dtype`."""
+    g = W.generator(95, seed, 0, DEV)
+    xs = [W.to_storage(W.randn((T, D), g, DEV), xdt) for _ in range(3)]
+    lg = [W.randn((T,), g, DEV) for _ in range(3)]
+    mb = -(-T // 256)
+    need = [W.blocks_for_entries(T // ratio, ratio)] * 3
+    pc = W.make_pool(dtype, D, ratio, need, mb, g, DEV, fill=False)
+    po = W.PagedTensors(pc.data.clone(), pc.scale.clone(), pc.block_table.clone(), dtype, D, ratio)
+    gate = mode == "gate"
+    state = torch.zeros(3, ratio, D, dtype=xs[0].dtype, device=DEV)
+    st_l = torch.zeros(3, ratio, device=DEV)
+    cuts = [sorted({0, 1, 3, 130, 131, 517 % T, 900 % T, T}), [0, 1, T], [0, T]]
+    for s in range(max(len(c) for c in cuts) - 1):
+        rng = [(c[s], c[s + 1]) if s + 1 < len(c) else (T, T) for c in cuts]
+        x = torch.cat([xs[b][a:e] for b, (a, e) in enumerate(rng)])
+        cu = ints([0] + list(np.cumsum([e - a for a, e in rng])))
+        hyb.hyb_compress(x, cu, ints([a for a, _ in rng]), max(e - a for a, e in rng), state, pc, rd,
+                         eps=1e-6, gate_logits=torch.cat([lg[b][a:e] for b, (a, e) in enumerate(rng)])
+                         if gate else None, state_logits=st_l if gate else None)
+    st2, stl2 = torch.zeros_like(state), torch.zeros_like(st_l)
+    hyb.hyb_compress(torch.cat(xs), ints([0, T, 2 * T, 3 * T]), ints([0, 0, 0]), T, st2, po, rd,
+                     eps=1e-6, gate_logits=torch.cat(lg) if gate else None,
+                     state_logits=stl2 if gate else None)
+    torch.cuda.synchronize()
+    refs = [O.compress_stream(to_f64(xs[b]), lg[b].cpu().double().numpy() if gate else None,
+                              ratio, mode, rd, 1e4, 1e-6) for b in range(3)]
+    return pc, po, refs
+
+
+@pytest.mark.parametrize("ratio,mode,xdt,D,rd,T", [
+    (4, "mean", "bf16", 512, 64, 1000), (128, "gate", "bf16", 512, 64, 1500),
+    (4, "gate", "f32", 256, 64, 600), (4, "mean", "bf16", 514, 64, 300)])
+def test_compress_into_fp8_pool(gpu_lib, ratio, mode, xdt, D, rd, T):
+    """Compressed entries quantised as they are stored (fp8 attention cache): chunked equals one
+    shot byte for byte (codes and scales), and decoded entries match the oracle's."""
+    pc, po, refs = _compress_chunked_and_once(gpu_lib, "fp8", ratio, mode, xdt, D, rd, T, ratio)
+    assert torch.equal(pc.data, po.data) and torch.equal(pc.scale, po.scale)
+    host = stored(pc)
+    for b in range(3):
+        n = T // ratio
+        rows = [raw_entry(host, ratio, b, g) for g in range(n)]
+        check_fp8_rows(np.stack([r[0] for r in rows]), np.array([r[1] for r in rows]), refs[b], 1e-5)
+
+
+@pytest.mark.parametrize("ratio,mode,xdt,D,rd,T", [
+    (4, "mean", "bf16", 128, 64, 1000), (4, "gate", "f32", 128, 64, 700),
+    (128, "mean", "bf16", 256, 64, 600)])
+def test_compress_into_fp4_pool(gpu_lib, ratio, mode, xdt, D, rd, T):
+    """Compressed entries quantised to OCP MX fp4 as they are stored (indexer-key compression):
+    chunked equals one shot byte for byte; each 32-value block's shared exponent is the oracle's
+    (unless the block maximum lies within float32 error of a power of two) and decoded values lie
+    within half an E2M1 step (or the saturation error above 6) of the oracle's entries."""
+    pc, po, refs = _compress_chunked_and_once(gpu_lib, "fp4", ratio, mode, xdt, D, rd, T, 7 + ratio)
+    assert torch.equal(pc.data, po.data) and torch.equal(pc.scale, po.scale)
+    host = stored(pc)
+    opool = to_oracle_pool(pc)
+    err = 1e-5
+    for b in range(3):
+        n = T // ratio
+        dec = O.pool_entries(opool, b, range(n))
+        ref = refs[b]
+        ex = np.stack([raw_entry(host, ratio, b, g)[1] for g in range(n)]).astype(np.int64) - 127
+        amax = np.abs(ref).reshape(n, D // 32, 32).max(axis=2)
+        want = np.vectorize(O.mx_exponent)(amax)
+        near = np.abs(np.log2(amax) - np.round(np.log2(amax))) < 1e-5
+        assert np.all((ex == want) | near)
+        sc = np.repeat(np.exp2(ex.astype(np.float64)), 32, axis=1)
+        v = np.abs(ref) / sc
+        step = np.where(v < 2, 0.5, np.where(v < 4, 1.0, 2.0))
+        bound = (0.5 * step + np.maximum(v - 6.0, 0.0)) * sc + 2 * err
+        assert np.all(np.abs(dec - ref) <= bound)
