@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define HYB_ABI_VERSION 1
+#define HYB_ABI_VERSION 2
 
 /* [vLLM] "vLLM side": one logical block = 256 native (raw) positions for every compression
  * rate, i.e. 256 raw entries, 64 C4 entries or 2 C128 entries. */
@@ -246,7 +246,12 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
  *   swa      raw pool (ratio 1);  comp compressed pool (ratio 4 or 128); same dtype, dim as q;
  *            pool dtype F32 (q F32), BF16 or FP8_E4M3 (q BF16)
  *   topk_idx int32 [batch][k] entries of comp (negative = unused), or NULL
- *   out      [batch][n_heads][dim], out_dtype F32 or BF16
+ *   out      [batch][n_heads][dim], out_dtype F32, BF16 or FP8_E4M3. FP8_E4M3 (dim % 8 == 0,
+ *            dim <= 2048) quantises each (query, head) row after the inverse RoPE ([vLLM] fused
+ *            "inverse RoPE + fp8 quant"): uint8 E4M3 codes in out, the row's float32 scale in
+ *            out_scale [batch][n_heads], with the FP8_E4M3 rule of hyb_compress (scale = amax /
+ *            448, nearest code to value / scale, ties to even, saturating)
+ *   out_scale float [batch][n_heads] for an FP8_E4M3 output, NULL otherwise
  *   workspace size from hyb_attn_decode_workspace_bytes with the same batch, n_heads, dim,
  *            max_seq_len, comp ratio, k (0 when topk_idx is NULL) and window.
  * ------------------------------------------------------------------------------------------ */
@@ -257,7 +262,8 @@ int32_t hyb_attn_decode(const void* q, int32_t q_dtype, const int32_t* seq_lens,
                         int32_t n_heads, int32_t max_seq_len, const hyb_paged* swa,
                         const hyb_paged* comp, const int32_t* topk_idx, int32_t k, int32_t window,
                         float softmax_scale, int32_t rope_dim, double rope_base, void* out,
-                        int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+                        int32_t out_dtype, float* out_scale, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------------
  * hyb_attn_decode_compress - hyb_attn_decode, then hyb_compress(*compress), on one stream.
@@ -277,7 +283,7 @@ int32_t hyb_attn_decode_compress(const void* q, int32_t q_dtype, const int32_t* 
                                  const hyb_paged* swa, const hyb_paged* comp,
                                  const int32_t* topk_idx, int32_t k, int32_t window,
                                  float softmax_scale, int32_t rope_dim, double rope_base,
-                                 void* out, int32_t out_dtype, void* workspace,
+                                 void* out, int32_t out_dtype, float* out_scale, void* workspace,
                                  size_t workspace_bytes, const hyb_compress_call* compress,
                                  void* stream);
 
@@ -287,6 +293,7 @@ int32_t hyb_attn_decode_compress(const void* q, int32_t q_dtype, const int32_t* 
  * to every compressed entry visible at q_pos[i]). Same arithmetic and pools as hyb_attn_decode.
  *   q [n_q][n_heads][dim] rotated at q_pos;  q_seq int32 [n_q] (NULL = identity);  q_pos int32 [n_q]
  *   max_pos host bound on q_pos;  topk_idx int32 [n_q][k] or NULL;  out [n_q][n_heads][dim]
+ *   (out_dtype and out_scale [n_q][n_heads] as in hyb_attn_decode)
  * ------------------------------------------------------------------------------------------ */
 size_t hyb_attn_prefill_workspace_bytes(int32_t n_q, int32_t n_heads, int32_t dim,
                                         int32_t max_pos, int32_t comp_ratio, int32_t k,
@@ -295,8 +302,8 @@ int32_t hyb_attn_prefill(const void* q, int32_t q_dtype, const int32_t* q_seq,
                          const int32_t* q_pos, int32_t n_q, int32_t n_heads, int32_t max_pos,
                          const hyb_paged* swa, const hyb_paged* comp, const int32_t* topk_idx,
                          int32_t k, int32_t window, float softmax_scale, int32_t rope_dim,
-                         double rope_base, void* out, int32_t out_dtype, void* workspace,
-                         size_t workspace_bytes, void* stream);
+                         double rope_base, void* out, int32_t out_dtype, float* out_scale,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyb.so")
 
 HYB_OK, HYB_EINVAL, HYB_ENOTSUP, HYB_EWORKSPACE, HYB_ELAUNCH = 0, 1, 2, 3, 4
 F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
+ABI_VERSION = 2   # HYB_ABI_VERSION of include/hyb.h that these signatures follow
 POOL_MEAN, POOL_SOFTMAX_GATE = 0, 1
 BLOCK_POSITIONS = 256
 KMAX = 2048
@@ -94,13 +95,13 @@ _SIGS = {
     "hyb_index_topk": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _PP, _I32, _P, _P, _SZ, _P]),
     "hyb_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "hyb_attn_decode": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F, _I32,
-                               _D, _P, _I32, _P, _SZ, _P]),
+                               _D, _P, _I32, _P, _P, _SZ, _P]),
     "hyb_attn_decode_compress": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F,
-                                        _I32, _D, _P, _I32, _P, _SZ,
+                                        _I32, _D, _P, _I32, _P, _P, _SZ,
                                         ctypes.POINTER(hyb_compress_call), _P]),
     "hyb_attn_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "hyb_attn_prefill": (_I32, [_P, _I32, _P, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F,
-                                _I32, _D, _P, _I32, _P, _SZ, _P]),
+                                _I32, _D, _P, _I32, _P, _P, _SZ, _P]),
 }
 
 
@@ -117,6 +118,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.hyb_abi_version() != ABI_VERSION:
+        raise ImportError(f"{p} has ABI version {lib.hyb_abi_version()}, the binding expects {ABI_VERSION}")
     if path is None:
         _lib = lib
     return lib
@@ -146,6 +149,17 @@ def _tdtype(t) -> int:
     if t.dtype == torch.bfloat16:
         return BF16
     raise TypeError(f"tensor dtype {t.dtype} is not float32 or bfloat16")
+
+
+def _odtype(out, out_scale) -> int:
+    """Output dtype: FP8_E4M3 when a scale tensor is given (out holds the codes as uint8 or
+    float8_e4m3fn), else that of `out`."""
+    import torch
+    if out_scale is None:
+        return _tdtype(out)
+    if out.dtype not in (torch.uint8, torch.float8_e4m3fn) or out_scale.dtype != torch.float32:
+        raise TypeError("an fp8 output takes uint8 / float8_e4m3fn codes and float32 scales")
+    return FP8_E4M3
 
 
 def paged(pool) -> hyb_paged:
@@ -261,7 +275,7 @@ def hyb_attn_decode_workspace_bytes(batch: int, n_heads: int, dim: int, max_seq_
 def hyb_attn_decode(q, seq_lens, max_seq_len: int, swa_pool, comp_pool, out, topk_idx=None,
                     k: int = 0, window: int = 128, softmax_scale: Optional[float] = None,
                     rope_dim: int = 64, rope_base: float = 10000.0, workspace=None,
-                    stream=None) -> None:
+                    out_scale=None, stream=None) -> None:
     b, h, dim = (int(s) for s in q.shape)
     if topk_idx is not None and not k:
         k = int(topk_idx.shape[1])
@@ -274,7 +288,7 @@ def hyb_attn_decode(q, seq_lens, max_seq_len: int, swa_pool, comp_pool, out, top
     _check(load().hyb_attn_decode(_ptr(q), _tdtype(q), _ptr(seq_lens), b, h, int(max_seq_len),
                                   ctypes.byref(ds), ctypes.byref(dc), _ptr(topk_idx), int(k),
                                   int(window), scale, int(rope_dim), float(rope_base), _ptr(out),
-                                  _tdtype(out), _ptr(workspace),
+                                  _odtype(out, out_scale), _ptr(out_scale), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
@@ -283,7 +297,7 @@ def hyb_attn_decode_compress(q, seq_lens, max_seq_len: int, swa_pool, comp_pool,
                              topk_idx=None, k: int = 0, window: int = 128,
                              softmax_scale: Optional[float] = None, rope_dim: int = 64,
                              rope_base: float = 10000.0, eps: float = 1e-6, gate_logits=None,
-                             state_logits=None, workspace=None, stream=None) -> None:
+                             state_logits=None, workspace=None, out_scale=None, stream=None) -> None:
     """hyb_attn_decode(q, ...) then hyb_compress(x, ...) in one call (see include/hyb.h); both
     use rope_dim and rope_base."""
     _check_state(x, state)
@@ -305,7 +319,7 @@ def hyb_attn_decode_compress(q, seq_lens, max_seq_len: int, swa_pool, comp_pool,
     _check(load().hyb_attn_decode_compress(
         _ptr(q), _tdtype(q), _ptr(seq_lens), b, h, int(max_seq_len), ctypes.byref(ds),
         ctypes.byref(dc), _ptr(topk_idx), int(k), int(window), scale, int(rope_dim),
-        float(rope_base), _ptr(out), _tdtype(out), _ptr(workspace),
+        float(rope_base), _ptr(out), _odtype(out, out_scale), _ptr(out_scale), _ptr(workspace),
         workspace.numel() * workspace.element_size(), ctypes.byref(call), _stream(stream)))
 
 
@@ -319,7 +333,7 @@ def hyb_attn_prefill_workspace_bytes(n_q: int, n_heads: int, dim: int, max_pos: 
 def hyb_attn_prefill(q, q_pos, max_pos: int, swa_pool, comp_pool, out, topk_idx=None, k: int = 0,
                      q_seq=None, window: int = 128, softmax_scale: Optional[float] = None,
                      rope_dim: int = 64, rope_base: float = 10000.0, workspace=None,
-                     stream=None) -> None:
+                     out_scale=None, stream=None) -> None:
     n_q, h, dim = (int(s) for s in q.shape)
     if topk_idx is not None and not k:
         k = int(topk_idx.shape[1])
@@ -332,5 +346,5 @@ def hyb_attn_prefill(q, q_pos, max_pos: int, swa_pool, comp_pool, out, topk_idx=
     _check(load().hyb_attn_prefill(_ptr(q), _tdtype(q), _ptr(q_seq), _ptr(q_pos), n_q, h,
                                    int(max_pos), ctypes.byref(ds), ctypes.byref(dc),
                                    _ptr(topk_idx), int(k), int(window), scale, int(rope_dim),
-                                   float(rope_base), _ptr(out), _tdtype(out), _ptr(workspace),
+                                   float(rope_base), _ptr(out), _odtype(out, out_scale), _ptr(out_scale), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -761,6 +761,7 @@ __device__ __forceinline__ void combine_group(const AttnArgs& a, int hpw, int lo
   float* wsp = sm;                              // [split][head of the group]
   float* mls = sm + ns * kCombineHeads;         // [split][m, l][head of the group]
   __shared__ float rc[kMaxRopePairs], rs[kMaxRopePairs];
+  __shared__ uint32_t lamax[kCombineHeads];   // FP8 output: bits of each head's largest |value|
   const int tid = threadIdx.x;
   const int64_t sstride = (int64_t)H * D;
   const PT* po = reinterpret_cast<const PT*>(a.part_o) + (int64_t)i * ns * sstride;
@@ -780,6 +781,7 @@ __device__ __forceinline__ void combine_group(const AttnArgs& a, int hpw, int lo
     const int s2 = e / nh, hl = e % nh;   // s2 = 2 * split + (0: m, 1: l)
     mls[e] = pml[s2 * H + h0 + hl];
   }
+  if (tid < kCombineHeads) lamax[tid] = 0u;
   const int rope_lo = D - a.rope_dim;
   for (int t = tid; t < a.rope_dim / 2; t += 256)
     rope_cs(-(double)p, t, a.rope_dim, a.rope_base, &rc[t], &rs[t]);
@@ -799,8 +801,8 @@ __device__ __forceinline__ void combine_group(const AttnArgs& a, int hpw, int lo
     }
   }
   __syncthreads();
-  auto finish = [&](int h, int d, float* x, int n) {   // n = 8 or 1 values at dims d..d+n-1
-    if (n == 8 && d + 8 > rope_lo) {
+  auto rope8 = [&](int d, float* x) {   // RoPE(-p) of dims d..d+7
+    if (d + 8 > rope_lo) {
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         if (d + e >= rope_lo) {
@@ -812,6 +814,9 @@ __device__ __forceinline__ void combine_group(const AttnArgs& a, int hpw, int lo
         }
       }
     }
+  };
+  auto finish = [&](int h, int d, float* x, int n) {   // n = 8 or 1 values at dims d..d+n-1
+    if (n == 8) rope8(d, x);
     const int64_t off = ((int64_t)i * H + h) * D + d;
     if (n == 8) {
       if (a.out_dtype == F32) {
@@ -830,7 +835,55 @@ __device__ __forceinline__ void combine_group(const AttnArgs& a, int hpw, int lo
         reinterpret_cast<uint16_t*>(a.out)[off] = (uint16_t)(pack_bf16x2(x[0], 0.f) & 0xffffu);
     }
   };
-  if (oct) {
+  // weighted sum of the splits' partials at chunk e8 (head e8 / (D/8), dims 8 (e8 % (D/8)) + [0, 8))
+  auto accumulate = [&](int e8, float* acc) __attribute__((always_inline)) {
+      const int hl = e8 / (D / 8), d = 8 * (e8 % (D / 8));
+      const PT* base = po + (int64_t)(h0 + hl) * D + d;
+      for (int s0 = 0; s0 < ns; s0 += 8) {
+        Raw8<PT> raw[8];
+        if (e8 == tid && s0 == 0) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) raw[q] = pre[q];
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) raw[q] = load8<PT>(base + min(s0 + q, ns - 1) * sstride);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          float x[8];
+          widen8<PT>(raw[q], x);
+          const float w = s0 + q < ns ? wsp[(s0 + q) * kCombineHeads + hl] : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+        }
+      }
+  };
+  if (oct && a.out_dtype == FP8) {
+    // Inverse RoPE + fp8 output ([vLLM] fused "inverse RoPE + fp8 quant"): each thread holds one
+    // chunk (n8 <= 256 for dim <= 2048); the head's largest magnitude gathers in LDS, then every
+    // row is encoded with scale = amax / 448 and written with its scale.
+    const bool have = tid < n8;
+    const int hl = have ? tid / (D / 8) : 0, d = 8 * (tid % (D / 8)), h = h0 + hl;
+    float acc[8] = {};
+    if (have) {
+      accumulate(tid, acc);
+      rope8(d, acc);
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(acc[e]));
+      atomicMax(&lamax[hl], __float_as_uint(m));
+    }
+    __syncthreads();
+    if (have) {
+      const float amax = __uint_as_float(lamax[hl]);
+      const float scale = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = f32_to_e4m3(__fdiv_rn(acc[e], scale));
+      store_bytes<8>(reinterpret_cast<uint8_t*>(a.out) + ((int64_t)i * H + h) * D + d, b);
+      if (d == 0) a.out_scale[(int64_t)i * H + h] = scale;
+    }
+  } else if (oct) {
     for (int e8 = tid; e8 < n8; e8 += 256) {
       const int hl = e8 / (D / 8), d = 8 * (e8 % (D / 8));
       const int h = h0 + hl;

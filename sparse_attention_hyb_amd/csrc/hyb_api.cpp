@@ -157,13 +157,17 @@ struct AttnCommon {
 int check_attention(const char* op, const void* q, int32_t q_dtype, int32_t n_q, int32_t n_heads,
                     const hyb_paged* swa, const hyb_paged* comp, const int32_t* topk_idx,
                     int32_t k, int32_t window, float softmax_scale, int32_t rope_dim,
-                    double rope_base, void* out, int32_t out_dtype, int64_t max_pos,
-                    AttnCommon* c) {
+                    double rope_base, void* out, int32_t out_dtype, float* out_scale,
+                    int64_t max_pos, AttnCommon* c) {
   if (!q || !out) return fail(HYB_EINVAL, "%s: q and out must be non-NULL", op);
   if (n_q < 0) return fail(HYB_EINVAL, "%s: query count %d < 0", op, n_q);
   if (n_heads <= 0 || n_heads > 128) return fail(HYB_EINVAL, "%s: n_heads %d outside [1, 128]", op, n_heads);
-  if (!is_plain(q_dtype) || !is_plain(out_dtype))
-    return fail(HYB_ENOTSUP, "%s: q_dtype and out_dtype must be F32 or BF16", op);
+  const bool fp8_out = out_dtype == HYB_FP8_E4M3;
+  if (!is_plain(q_dtype) || !(is_plain(out_dtype) || fp8_out))
+    return fail(HYB_ENOTSUP, "%s: q_dtype must be F32 or BF16, out_dtype F32, BF16 or FP8_E4M3", op);
+  if (fp8_out != (out_scale != nullptr))
+    return fail(HYB_EINVAL, "%s: out_scale is required with an FP8_E4M3 output and must be NULL "
+                "otherwise", op);
   if (window <= 0) return fail(HYB_EINVAL, "%s: window %d must be positive", op, window);
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
     return fail(HYB_EINVAL, "%s: softmax_scale must be positive and finite", op);
@@ -177,6 +181,8 @@ int check_attention(const char* op, const void* q, int32_t q_dtype, int32_t n_q,
   if (topk_idx && (k < 1 || k > HYB_KMAX)) return fail(HYB_EINVAL, "%s: k %d outside [1, %d]", op, k, HYB_KMAX);
   HYB_TRY(check_rope(op, rope_dim, rope_base, ps.dim));
   const int dim = ps.dim;
+  if (fp8_out && (dim % 8 || dim > 2048))
+    return fail(HYB_ENOTSUP, "%s: an FP8_E4M3 output needs dim %% 8 == 0 and dim <= 2048", op);
   const int64_t n_win = max_pos + 1 < window ? max_pos + 1 : window;
   const int64_t n_comp = topk_idx ? k : visible(max_pos, pc.ratio, window);
   const int64_t max_keys = n_win + n_comp;
@@ -202,6 +208,7 @@ int check_attention(const char* op, const void* q, int32_t q_dtype, int32_t n_q,
   a.rope_base = rope_base;
   a.out = out;
   a.out_dtype = out_dtype;
+  a.out_scale = out_scale;
   a.max_keys = (int32_t)max_keys;
   a.n_split = c->plan.n_split;
   a.chunk = c->plan.chunk;
@@ -475,13 +482,14 @@ int32_t hyb_attn_decode(const void* q, int32_t q_dtype, const int32_t* seq_lens,
                         int32_t n_heads, int32_t max_seq_len, const hyb_paged* swa,
                         const hyb_paged* comp, const int32_t* topk_idx, int32_t k, int32_t window,
                         float softmax_scale, int32_t rope_dim, double rope_base, void* out,
-                        int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                        int32_t out_dtype, float* out_scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   const char* op = "hyb_attn_decode";
   if (!seq_lens) return fail(HYB_EINVAL, "%s: seq_lens is NULL", op);
   if (max_seq_len < 1) return fail(HYB_EINVAL, "%s: max_seq_len %d < 1", op, max_seq_len);
   AttnCommon c;
   HYB_TRY(check_attention(op, q, q_dtype, batch, n_heads, swa, comp, topk_idx, k, window,
-                          softmax_scale, rope_dim, rope_base, out, out_dtype,
+                          softmax_scale, rope_dim, rope_base, out, out_dtype, out_scale,
                           (int64_t)max_seq_len - 1, &c));
   HYB_TRY(attach_workspace(op, &c, workspace, workspace_bytes));
   if (batch == 0) return HYB_OK;
@@ -494,7 +502,7 @@ int32_t hyb_attn_decode_compress(const void* q, int32_t q_dtype, const int32_t* 
                                  const hyb_paged* swa, const hyb_paged* comp,
                                  const int32_t* topk_idx, int32_t k, int32_t window,
                                  float softmax_scale, int32_t rope_dim, double rope_base,
-                                 void* out, int32_t out_dtype, void* workspace,
+                                 void* out, int32_t out_dtype, float* out_scale, void* workspace,
                                  size_t workspace_bytes, const hyb_compress_call* compress,
                                  void* stream) {
   const char* op = "hyb_attn_decode_compress";
@@ -503,7 +511,7 @@ int32_t hyb_attn_decode_compress(const void* q, int32_t q_dtype, const int32_t* 
   if (!compress) return fail(HYB_EINVAL, "%s: compress is NULL", op);
   AttnCommon c;
   HYB_TRY(check_attention(op, q, q_dtype, batch, n_heads, swa, comp, topk_idx, k, window,
-                          softmax_scale, rope_dim, rope_base, out, out_dtype,
+                          softmax_scale, rope_dim, rope_base, out, out_dtype, out_scale,
                           (int64_t)max_seq_len - 1, &c));
   HYB_TRY(attach_workspace(op, &c, workspace, workspace_bytes));
   hyb::CompressArgs ca;
@@ -522,14 +530,15 @@ int32_t hyb_attn_prefill(const void* q, int32_t q_dtype, const int32_t* q_seq,
                          const int32_t* q_pos, int32_t n_q, int32_t n_heads, int32_t max_pos,
                          const hyb_paged* swa, const hyb_paged* comp, const int32_t* topk_idx,
                          int32_t k, int32_t window, float softmax_scale, int32_t rope_dim,
-                         double rope_base, void* out, int32_t out_dtype, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         double rope_base, void* out, int32_t out_dtype, float* out_scale,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   const char* op = "hyb_attn_prefill";
   if (!q_pos) return fail(HYB_EINVAL, "%s: q_pos is NULL", op);
   if (max_pos < 0) return fail(HYB_EINVAL, "%s: max_pos %d < 0", op, max_pos);
   AttnCommon c;
   HYB_TRY(check_attention(op, q, q_dtype, n_q, n_heads, swa, comp, topk_idx, k, window,
-                          softmax_scale, rope_dim, rope_base, out, out_dtype, max_pos, &c));
+                          softmax_scale, rope_dim, rope_base, out, out_dtype, out_scale, max_pos,
+                          &c));
   HYB_TRY(attach_workspace(op, &c, workspace, workspace_bytes));
   if (n_q == 0) return HYB_OK;
   c.args.qd = hyb::QueryDev{nullptr, q_seq, q_pos};

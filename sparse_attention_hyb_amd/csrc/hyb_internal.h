@@ -119,6 +119,7 @@ struct AttnArgs {
   double rope_base;
   void* out;
   int32_t out_dtype;
+  float* out_scale;   // FP8 output: one scale per (query, head) row
   int32_t max_keys;   // host bound on keys per query (window + compressed)
   // split-K plan (filled by plan_attention)
   int32_t n_split;

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hyb_abi_version() == 1
+    assert lib.hyb_abi_version() == hyb.ABI_VERSION == 2
     assert [lib.hyb_status_str(i).decode() for i in range(5)] == [
         "HYB_OK", "HYB_EINVAL", "HYB_ENOTSUP", "HYB_EWORKSPACE", "HYB_ELAUNCH"]
 
@@ -46,15 +46,21 @@ def pool(dtype=hyb.BF16, dim=512, ratio=4, scale=True, data=FAKE, reserved=0):
 
 
 def decode(lib, swa=None, comp=None, q_dtype=hyb.BF16, topk=None, k=0, window=128, ws=1 << 40,
-           heads=64, scale=0.04, max_len=1000, rope_dim=64, q=FAKE):
+           heads=64, scale=0.04, max_len=1000, rope_dim=64, q=FAKE, out_dtype=hyb.BF16,
+           out_scale=None):
     swa = swa or pool(ratio=1)
     comp = comp or pool(ratio=128)
     return lib.hyb_attn_decode(q, q_dtype, FAKE, 4, heads, max_len, ctypes.byref(swa),
                                ctypes.byref(comp), topk, k, window, scale, rope_dim, 10000.0,
-                               FAKE, hyb.BF16, FAKE, ws, None)
+                               FAKE, out_dtype, out_scale, FAKE, ws, None)
 
 
 @pytest.mark.parametrize("kw,code", [
+    (dict(out_dtype=hyb.FP8_E4M3), hyb.HYB_EINVAL),                # fp8 output needs out_scale
+    (dict(out_scale=FAKE), hyb.HYB_EINVAL),                        # out_scale only with fp8 output
+    (dict(out_dtype=hyb.FP4_E2M1), hyb.HYB_ENOTSUP),
+    (dict(out_dtype=hyb.FP8_E4M3, out_scale=FAKE, swa=pool(ratio=1, dim=4096),
+          comp=pool(ratio=128, dim=4096)), hyb.HYB_ENOTSUP),      # fp8 output: dim <= 2048
     (dict(q=None), hyb.HYB_EINVAL),
     (dict(swa=pool(ratio=4)), hyb.HYB_EINVAL),                       # raw pool must be ratio 1
     (dict(comp=pool(ratio=1)), hyb.HYB_EINVAL),                      # compressed: 4 or 128
@@ -98,7 +104,7 @@ def test_attn_decode_compress_validation(lib):
                                    rope_dim=rope, rope_base=1e4, eps=eps)
         return lib.hyb_attn_decode_compress(FAKE, hyb.BF16, FAKE, 4, 64, 1000, ctypes.byref(swa),
                                             ctypes.byref(comp), None, 0, 128, 0.04, 64, 1e4,
-                                            FAKE, hyb.BF16, FAKE, ws,
+                                            FAKE, hyb.BF16, None, FAKE, ws,
                                             ctypes.byref(cc) if ccall else None, None)
 
     assert call(ccall=False) == hyb.HYB_EINVAL                        # compressor call required
@@ -126,11 +132,11 @@ def test_prefill_validation(lib):
     s, c = pool(ratio=1), pool(ratio=4)
     st = lib.hyb_attn_prefill(FAKE, hyb.BF16, None, None, 4, 64, 100, ctypes.byref(s),
                               ctypes.byref(c), None, 0, 128, 0.04, 64, 1e4, FAKE, hyb.BF16,
-                              FAKE, 1 << 40, None)
+                              None, FAKE, 1 << 40, None)
     assert st == hyb.HYB_EINVAL  # q_pos is required
     st = lib.hyb_attn_prefill(FAKE, hyb.BF16, None, FAKE, 0, 64, 100, ctypes.byref(s),
                               ctypes.byref(c), None, 0, 128, 0.04, 64, 1e4, FAKE, hyb.BF16,
-                              None, 0, None)
+                              None, None, 0, None)
     assert st == hyb.HYB_OK      # zero queries: nothing to do, nothing launched
 
 

@@ -191,3 +191,53 @@ def test_compress_into_fp4_pool(gpu_lib, ratio, mode, xdt, D, rd, T):
         step = np.where(v < 2, 0.5, np.where(v < 4, 1.0, 2.0))
         bound = (0.5 * step + np.maximum(v - 6.0, 0.0)) * sc + 2 * err
         assert np.all(np.abs(dec - ref) <= bound)
+
+
+# ================================================== attention output: inverse RoPE + fp8 rows
+def _check_fp8_output(codes, scales, out_bf16, want, tol):
+    """fp8 output rows (codes [n, H, D], scales [n, H]) against (1) the same call's bf16 output:
+    both come from one float32 row v, which bf16 rounds to within 2^-9 |v|, and (2) the oracle's
+    output within the attention tolerance `tol`, each plus half an E4M3 step of the row's scale."""
+    c = codes.cpu().numpy().reshape(-1, codes.shape[-1])
+    s = scales.cpu().numpy().astype(np.float64).reshape(-1)
+    b16 = to_f64(out_bf16).reshape(c.shape)
+    amax = np.abs(b16).max(axis=1)
+    assert np.all(np.abs(s * 448.0 - amax) <= 2.0 ** -8 * amax + 1e-30)
+    dec = O.e4m3fn_to_f64(c) * s[:, None]
+    half = 0.5 * e4m3_step(b16 / s[:, None]) * s[:, None]
+    assert np.all(np.abs(dec - b16) <= half * 1.0001 + 2.0 ** -8 * np.abs(b16) + 1e-30)
+    w = np.asarray(want, np.float64).reshape(-1, c.shape[1])
+    assert np.all(np.abs(dec - w) <= 2 * half + tol)
+
+
+def test_attention_fp8_output(gpu_lib):
+    """C4 sparse decode (L = 1 .. 33333, top-512), C128 dense decode and the same C128 queries in
+    the prefill form, each with a bf16 output and with an fp8 output (one scale per query and
+    head) from otherwise identical calls."""
+    hyb = gpu_lib
+    from tests.test_gpu_parity import gpu_decode, gpu_topk, oracle_out
+    from tests.parity_util import BF16_ABS
+    c4 = W.sparse_decode(DEV, seed=1, batch=5, ctx=[1, 100, 700, 5000, 33333])
+    c128 = W.dense_decode(DEV, seed=1, batch=6, ctx=[1, 128, 129, 300, 20000, 70001])
+    for wl, sparse in ((c4, True), (c128, False)):
+        topk = gpu_topk(hyb, wl) if sparse else None
+        out = gpu_decode(hyb, wl, topk)
+        codes = torch.empty(wl.q.shape, dtype=torch.uint8, device=DEV)
+        sc = torch.empty(wl.q.shape[:2], dtype=torch.float32, device=DEV)
+        hyb.hyb_attn_decode(wl.q, wl.seq_lens, wl.max_seq_len, wl.swa, wl.comp, codes,
+                            topk_idx=topk, k=wl.k if sparse else 0, window=wl.window,
+                            rope_dim=wl.rope_dim, rope_base=wl.rope_base, out_scale=sc)
+        torch.cuda.synchronize()
+        seqs = range(wl.batch)
+        sel = {b: topk[b].cpu().numpy() for b in seqs} if sparse else None
+        want = oracle_out(wl, to_oracle_pool(wl.swa), to_oracle_pool(wl.comp), seqs, sel)
+        _check_fp8_output(codes, sc, out, want, BF16_ABS)
+        if not sparse:
+            # the prefill entry point, same queries (position seq_len - 1 of each sequence)
+            pos = (wl.seq_lens - 1).contiguous()
+            codes2, sc2 = torch.empty_like(codes), torch.empty_like(sc)
+            hyb.hyb_attn_prefill(wl.q, pos, wl.max_seq_len - 1, wl.swa, wl.comp, codes2,
+                                 window=wl.window, rope_dim=wl.rope_dim, rope_base=wl.rope_base,
+                                 q_seq=torch.arange(wl.batch, dtype=I32, device=DEV), out_scale=sc2)
+            torch.cuda.synchronize()
+            assert torch.equal(codes2, codes) and torch.equal(sc2, sc)
