@@ -44,6 +44,7 @@ __all__ = [
     "compress_stream",
     "pending_group",
     "swa_entries",
+    "q_norm_rope",
     "window_start",
     "n_visible",
     "indexer_scores",
@@ -218,6 +219,16 @@ def pending_group(x, logits, r: int):
 def swa_entries(x, positions, rope_dim: int, base: float) -> np.ndarray:
     """Raw sliding-window entries s_t = RoPE(x_t, t), no norm (the "KV RoPE + K insert" step)."""
     return rope(np.asarray(x, np.float64), np.asarray(positions, np.float64), rope_dim, base)
+
+
+def q_norm_rope(q, positions, rope_dim: int, base: float, eps: float) -> np.ndarray:
+    """Query preparation of the fused "Q-norm + KV RoPE + K insert" step (vLLM post, "vLLM side"
+    list). Reading: each query head's row is RMS-normalised over its dim with unit gain (as the
+    compressor's RMSNorm, reading R3), then rotated at its token's position (reading R4), which
+    gives the rotated query the attention takes. q [T][H][D], positions [T]."""
+    q = np.asarray(q, np.float64)
+    pos = np.asarray(positions, np.float64)[:, None]
+    return rope(rmsnorm(q, eps), pos, rope_dim, base)
 
 
 # --------------------------------------------------------------------------------------------

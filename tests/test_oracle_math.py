@@ -110,6 +110,32 @@ def test_swa_entries_are_rotated_tokens():
     assert np.allclose(np.linalg.norm(s, axis=1), np.linalg.norm(x, axis=1))
 
 
+def test_q_norm_rope_hand_example_and_invariants():
+    """Hand example: head rows (3, 4) and (0, 2) with no rotated dims normalise to (3, 4) / 3.5355..
+    and (0, 1.4142..); with both dims rotated at position 1 (theta_0 = 1) the second row turns by
+    one radian. Invariants at D = 512, r_d = 64: every head's norm is sqrt(D * ms / (ms + eps)) (the
+    rotation keeps it), the unrotated dims equal the RMS-normalised row, and undoing the rotation
+    gives the RMS-normalised row back."""
+    q = np.array([[[3.0, 4.0], [0.0, 2.0]]])
+    got = O.q_norm_rope(q, [0], 0, 1e4, 0.0)
+    assert np.allclose(got[0, 0], [3 / math.sqrt(12.5), 4 / math.sqrt(12.5)], rtol=0, atol=1e-15)
+    assert np.allclose(got[0, 1], [0.0, math.sqrt(2.0)], rtol=0, atol=1e-15)
+    got = O.q_norm_rope(q, [1], 2, 1e4, 0.0)
+    r2 = math.sqrt(2.0)
+    assert np.allclose(got[0, 1], [-r2 * math.sin(1.0), r2 * math.cos(1.0)], rtol=0, atol=1e-15)
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((3, 5, 512)) * 7.0
+    pos = [0, 77, 1_000_000]
+    eps = 1e-6
+    got = O.q_norm_rope(q, pos, 64, 1e4, eps)
+    ms = np.mean(q * q, axis=-1)
+    assert np.allclose(np.linalg.norm(got, axis=-1), np.sqrt(512 * ms / (ms + eps)), rtol=1e-12)
+    normed = q / np.sqrt(ms + eps)[..., None]
+    assert np.allclose(got[..., :448], normed[..., :448], rtol=1e-14)
+    back = O.rope(got, -np.asarray(pos, np.float64)[:, None], 64, 1e4)
+    assert np.allclose(back, normed, rtol=0, atol=1e-9)
+
+
 # ----------------------------------------------------------------------------- visibility
 @pytest.mark.parametrize("p,r,want", [
     (0, 4, 0), (127, 4, 0), (128, 4, 1), (131, 4, 1), (132, 4, 2), (131071, 4, 32736),
