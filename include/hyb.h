@@ -168,6 +168,25 @@ int32_t hyb_swa_insert(const void* x, int32_t x_dtype, const int32_t* cu_seqlens
                        const hyb_paged* swa, int32_t rope_dim, double rope_base, void* stream);
 
 /* --------------------------------------------------------------------------------------------
+ * hyb_q_norm_kv_insert - the step before the attention for new tokens, in one launch ([vLLM]
+ * "vLLM side": fused "Q-norm + KV RoPE + K insert"). For token i of sequence b (position
+ * pos = start_pos[b] + i, tokens ordered as in hyb_compress):
+ *   q_out[tok][h] = RoPE(RMSNorm(q[tok][h]), pos)   for every head h (RMSNorm over dim, eps,
+ *                                                    unit gain; RoPE on the last rope_dim dims)
+ *   window entry pos of sequence b = RoPE(kv[tok], pos)   (exactly hyb_swa_insert of kv)
+ *   q      [T][n_heads][dim], q_dtype F32 or BF16;  q_out the same shape and dtype (may be q)
+ *   kv     [T][dim], kv_dtype F32 or BF16 (T = cu_seqlens[batch]);  1 <= n_heads <= 128
+ *   swa    raw pool (ratio 1) of dim `dim` <= 2048, dtype F32, BF16 or FP8_E4M3 (quantised as
+ *          in hyb_swa_insert)
+ * The query rows it writes are what hyb_attn_decode / hyb_attn_prefill take at these positions.
+ * ------------------------------------------------------------------------------------------ */
+int32_t hyb_q_norm_kv_insert(const void* q, int32_t q_dtype, int32_t n_heads, const void* kv,
+                             int32_t kv_dtype, const int32_t* cu_seqlens, const int32_t* start_pos,
+                             int32_t batch, int32_t max_new_tokens, void* q_out,
+                             const hyb_paged* swa, int32_t rope_dim, double rope_base, float eps,
+                             void* stream);
+
+/* --------------------------------------------------------------------------------------------
  * hyb_index_score - indexer scores over the visible compressed entries.
  * [vLLM] "DeepSeek Sparse Attention over compressed tokens"; [SGLang] "indexer top-k".
  *   score[i][g] = sum_h w[i][h] * max(0, q_idx[i][h] . key_g), g = 0 .. n_vis(q_pos[i]) - 1,

@@ -29,6 +29,7 @@ DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp4": FP4_E2M1}
 
 EXPORTS = (
     "hyb_abi_version", "hyb_status_str", "hyb_last_error", "hyb_compress", "hyb_swa_insert",
+    "hyb_q_norm_kv_insert",
     "hyb_index_score", "hyb_topk", "hyb_index_score_keys", "hyb_topk_keys",
     "hyb_index_topk_workspace_bytes", "hyb_index_topk",
     "hyb_attn_decode_workspace_bytes", "hyb_attn_decode", "hyb_attn_decode_compress",
@@ -93,6 +94,8 @@ _SIGS = {
     "hyb_topk_keys": (_I32, [_P, _I64, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]),
     "hyb_index_topk_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "hyb_index_topk": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _PP, _I32, _P, _P, _SZ, _P]),
+    "hyb_q_norm_kv_insert": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P, _PP, _I32, _D,
+                                    _F, _P]),
     "hyb_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "hyb_attn_decode": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F, _I32,
                                _D, _P, _I32, _P, _P, _SZ, _P]),
@@ -205,6 +208,22 @@ def hyb_swa_insert(x, cu_seqlens, start_pos, max_new_tokens: int, swa_pool, rope
     _check(load().hyb_swa_insert(_ptr(x), _tdtype(x), _ptr(cu_seqlens), _ptr(start_pos),
                                  int(start_pos.shape[0]), int(max_new_tokens), ctypes.byref(d),
                                  int(rope_dim), float(rope_base), _stream(stream)))
+
+
+def hyb_q_norm_kv_insert(q, kv, cu_seqlens, start_pos, max_new_tokens: int, swa_pool, q_out=None,
+                         rope_dim: int = 64, rope_base: float = 10000.0, eps: float = 1e-6,
+                         stream=None):
+    """Query RMSNorm + RoPE and the window insert of the new tokens (see include/hyb.h). q_out
+    defaults to q (in place). Returns q_out."""
+    q_out = q if q_out is None else q_out
+    if q_out.dtype != q.dtype or q_out.shape != q.shape:
+        raise TypeError("q_out must have q's shape and dtype")
+    d = paged(swa_pool)
+    _check(load().hyb_q_norm_kv_insert(_ptr(q), _tdtype(q), int(q.shape[1]), _ptr(kv), _tdtype(kv),
+                                       _ptr(cu_seqlens), _ptr(start_pos), int(start_pos.shape[0]),
+                                       int(max_new_tokens), _ptr(q_out), ctypes.byref(d),
+                                       int(rope_dim), float(rope_base), float(eps), _stream(stream)))
+    return q_out
 
 
 def hyb_index_score(q_idx, w, q_pos, max_pos: int, idx_pool, scores, window: int = 128,

@@ -290,6 +290,34 @@ int32_t hyb_swa_insert(const void* x, int32_t x_dtype, const int32_t* cu_seqlens
   return launch_status(hyb::launch_swa_insert(a, static_cast<hipStream_t>(stream)), op);
 }
 
+int32_t hyb_q_norm_kv_insert(const void* q, int32_t q_dtype, int32_t n_heads, const void* kv,
+                             int32_t kv_dtype, const int32_t* cu_seqlens, const int32_t* start_pos,
+                             int32_t batch, int32_t max_new_tokens, void* q_out,
+                             const hyb_paged* swa, int32_t rope_dim, double rope_base, float eps,
+                             void* stream) {
+  const char* op = "hyb_q_norm_kv_insert";
+  HYB_TRY(check_compress_common(op, kv, kv_dtype, cu_seqlens, start_pos, batch, max_new_tokens));
+  if (!q || !q_out) return fail(HYB_EINVAL, "%s: q and q_out must be non-NULL", op);
+  if (!is_plain(q_dtype)) return fail(HYB_ENOTSUP, "%s: q_dtype must be F32 or BF16", op);
+  if (n_heads <= 0 || n_heads > 128) return fail(HYB_EINVAL, "%s: n_heads %d outside [1, 128]", op, n_heads);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(HYB_EINVAL, "%s: eps must be >= 0", op);
+  hyb::PoolDev ps{};
+  HYB_TRY(check_pool(swa, op, "swa", true, false, 1, &ps));
+  if (ps.dim > 2048) return fail(HYB_ENOTSUP, "%s: dim %d > 2048", op, ps.dim);
+  HYB_TRY(check_rope(op, rope_dim, rope_base, ps.dim));
+  if (batch == 0 || max_new_tokens == 0) return HYB_OK;
+  hyb::QNormArgs a{};
+  a.kv = hyb::CompressArgs{kv, kv_dtype, nullptr, cu_seqlens, start_pos, batch, max_new_tokens,
+                           nullptr, nullptr, 0, ps, rope_dim, rope_base, 0.f, {}};
+  fill_theta(&a.kv, rope_dim, rope_base);
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.q_out = q_out;
+  a.n_heads = n_heads;
+  a.eps = eps;
+  return launch_status(hyb::launch_q_norm_kv_insert(a, static_cast<hipStream_t>(stream)), op);
+}
+
 static int check_score(const char* op, const void* q_idx, int32_t q_dtype, const float* w,
                        const int32_t* q_pos, int32_t n_q, int32_t n_heads, int32_t max_pos,
                        int32_t window, const hyb_paged* idx_pool, hyb::ScoreArgs* a) {

@@ -54,6 +54,18 @@ struct CompressArgs {
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 hipError_t launch_swa_insert(const CompressArgs& a, hipStream_t s);
 
+// Query RMSNorm + RoPE of new tokens, with their window entries (kv: the tokens' K=V rows in x,
+// their window pool in out, positions and RoPE as in the insert).
+struct QNormArgs {
+  CompressArgs kv;
+  const void* q;       // [T][n_heads][dim]
+  int32_t q_dtype;
+  void* q_out;         // same shape and dtype (may be q)
+  int32_t n_heads;
+  float eps;
+};
+hipError_t launch_q_norm_kv_insert(const QNormArgs& a, hipStream_t s);
+
 // ---- indexer scores -------------------------------------------------------------------------
 struct ScoreArgs {
   const void* q;

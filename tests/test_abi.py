@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(hyb.EXPORTS) == names
@@ -227,3 +227,27 @@ def test_index_keys_validation(lib):
     assert topk(k=0) == hyb.HYB_EINVAL
     assert lib.hyb_last_error().decode().startswith("hyb_topk_keys")
     assert hyb.index_keys_shapes(16, 131071) == ((16, 65536), (16, 32, 1024))
+
+
+def test_q_norm_kv_insert_validation(lib):
+    def call(q=FAKE, q_dtype=hyb.BF16, heads=64, kv=FAKE, kv_dtype=hyb.BF16, batch=2, maxnew=4,
+             q_out=FAKE, swa=None, rope=64, eps=1e-6):
+        swa = swa or pool(ratio=1)
+        return lib.hyb_q_norm_kv_insert(q, q_dtype, heads, kv, kv_dtype, FAKE, FAKE, batch, maxnew,
+                                        q_out, ctypes.byref(swa), rope, 1e4, eps, None)
+
+    assert call(q=None) == hyb.HYB_EINVAL
+    assert call(q_out=None) == hyb.HYB_EINVAL
+    assert call(kv=None) == hyb.HYB_EINVAL
+    assert call(q_dtype=hyb.FP8_E4M3) == hyb.HYB_ENOTSUP
+    assert call(kv_dtype=hyb.FP4_E2M1) == hyb.HYB_ENOTSUP
+    assert call(heads=0) == hyb.HYB_EINVAL and call(heads=129) == hyb.HYB_EINVAL
+    assert call(swa=pool(ratio=4)) == hyb.HYB_EINVAL                  # window pool: ratio 1
+    assert call(swa=pool(ratio=1, dtype=hyb.FP4_E2M1)) == hyb.HYB_ENOTSUP
+    assert call(swa=pool(ratio=1, dim=4096)) == hyb.HYB_ENOTSUP
+    assert call(rope=3) == hyb.HYB_EINVAL
+    assert call(eps=-1.0) == hyb.HYB_EINVAL
+    assert call(batch=-1) == hyb.HYB_EINVAL
+    assert call(eps=-1.0) == hyb.HYB_EINVAL
+    assert lib.hyb_last_error().decode().startswith("hyb_q_norm_kv_insert")
+    assert call(batch=0) == hyb.HYB_OK and call(maxnew=0) == hyb.HYB_OK

@@ -241,3 +241,42 @@ def test_attention_fp8_output(gpu_lib):
                                  q_seq=torch.arange(wl.batch, dtype=I32, device=DEV), out_scale=sc2)
             torch.cuda.synchronize()
             assert torch.equal(codes2, codes) and torch.equal(sc2, sc)
+
+
+# ====================================== fused step before the attention: Q-norm + KV RoPE + insert
+@pytest.mark.parametrize("qdt,kvdt,pdt,D,H,rd", [
+    ("bf16", "bf16", "bf16", 512, 64, 64), ("f32", "f32", "f32", 64, 8, 16),
+    ("bf16", "f32", "fp8", 512, 64, 64), ("f32", "bf16", "bf16", 514, 3, 32)])
+def test_q_norm_kv_insert(gpu_lib, qdt, kvdt, pdt, D, H, rd):
+    """Three sequences (300 / 1 / 77 new tokens at positions 0 / 999_999 / 250): query rows
+    against the oracle's RMSNorm + RoPE per head; the window entries equal hyb_swa_insert's bytes
+    for the same tokens; the in-place form (q_out = q) writes the same rows."""
+    hyb = gpu_lib
+    g = W.generator(96, D, H, DEV)
+    n_new, starts = [300, 1, 77], [0, 999_999, 250]
+    T = sum(n_new)
+    q = W.to_storage(W.randn((T, H, D), g, DEV) * torch.exp2(W.randn((T, H, 1), g, DEV) * 3), qdt)
+    kv = W.to_storage(W.randn((T, D), g, DEV), kvdt)
+    mb = (max(s + n for s, n in zip(starts, n_new)) + 255) // 256
+    need = [W.blocks_for_positions(s, s + n) for s, n in zip(starts, n_new)]
+    swa1 = W.make_pool(pdt, D, 1, need, mb, g, DEV, fill=False)
+    swa2 = W.PagedTensors(swa1.data.clone(), None if swa1.scale is None else swa1.scale.clone(),
+                          swa1.block_table.clone(), pdt, D, 1)
+    cu, st = ints(np.cumsum([0] + n_new)), ints(starts)
+    q_out = torch.empty_like(q)
+    hyb.hyb_q_norm_kv_insert(q, kv, cu, st, max(n_new), swa1, q_out=q_out, rope_dim=rd, eps=1e-6)
+    hyb.hyb_swa_insert(kv, cu, st, max(n_new), swa2, rd)
+    q2 = q.clone()
+    hyb.hyb_q_norm_kv_insert(q2, kv, cu, st, max(n_new), swa1, rope_dim=rd, eps=1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(swa1.data, swa2.data)
+    if swa1.scale is not None:
+        assert torch.equal(swa1.scale, swa2.scale)
+    assert torch.equal(q2, q_out)
+    pos = np.concatenate([np.arange(s, s + n) for s, n in zip(starts, n_new)])
+    want = O.q_norm_rope(to_f64(q), pos, rd, 1e4, 1e-6)
+    got = to_f64(q_out)
+    if qdt == "f32":
+        assert np.all(np.abs(got - want) <= 4e-6 * (1.0 + np.abs(want)))
+    else:
+        assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-5)
