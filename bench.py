@@ -316,6 +316,53 @@ def multi_decode(torch, hyb, W, BM, args):
     )
 
 
+def neighbour_steps(torch, hyb, W, BM, args, rep):
+    """The fused steps around the C4 decode step's attention, on one replica of its workload
+    (16 sequences, 64 heads x 512): the query RMSNorm + RoPE with the window insert before it,
+    and the attention (+ combine with the new token's compression) writing bf16 or fp8 rows."""
+    dev = "cuda"
+    wl = rep["wl"]
+    B, L = wl.batch, wl.max_seq_len
+    g = W.generator(7, 0, 99, dev)
+    q_raw = W.to_storage(W.randn((B, 64, 512), g, dev), "bf16")
+    q_out = torch.empty_like(q_raw)
+    kv = W.to_storage(W.randn((B, 512), g, dev), "bf16")
+    cu = torch.arange(0, B + 1, dtype=torch.int32, device=dev)
+    start = (wl.seq_lens - 1).contiguous()
+    n = max(args.steps, 50)
+
+    # the prep kernel is far shorter than a Python call: time it from a HIP graph of 20 launches
+    # (nothing in the call allocates, clears memory or synchronises)
+    per_graph = 20
+    gr = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gr):
+        for _ in range(per_graph):
+            hyb.hyb_q_norm_kv_insert(q_raw, kv, cu, start, 1, wl.swa, q_out=q_out)
+    prep_s = time_loop(torch, lambda r, ev: gr.replay(), n // per_graph + 1, 3, 1)
+    prep_s /= per_graph * (n // per_graph + 1) / n
+    codes = torch.empty(wl.q.shape, dtype=torch.uint8, device=dev)
+    scales = torch.empty(wl.q.shape[:2], dtype=torch.float32, device=dev)
+
+    def attn(fp8):
+        def step(r, ev):
+            hyb.hyb_attn_decode_compress(wl.q, wl.seq_lens, L, wl.swa, wl.comp,
+                                         codes if fp8 else rep["out"], rep["x_new"], rep["cu"],
+                                         rep["start"], 1, rep["state"], wl.comp,
+                                         topk_idx=rep["topk"], k=wl.k, workspace=rep["ws"],
+                                         out_scale=scales if fp8 else None)
+        return step
+
+    bf16_s = time_loop(torch, attn(False), n, 10, 1)
+    fp8_s = time_loop(torch, attn(True), n, 10, 1)
+    prep_bytes = 2 * B * 64 * 512 * 2 + 2 * B * 512 * 2
+    return dict(
+        q_norm_kv_insert_us=prep_s * 1e6 / n, q_norm_kv_insert_gbs=prep_bytes * n / prep_s / 1e9,
+        attn_combine_bf16_out_us=bf16_s * 1e6 / n, attn_combine_fp8_out_us=fp8_s * 1e6 / n,
+        steps=n, config={"workload": "c4_sparse_decode, one replica", "batch": B, "heads": 64,
+                         "dim": 512, "note": "attention + combine with compression; cache-warm"})
+
+
 def quant_mixed(torch, hyb, W, BM, args):
     dev = "cuda"
     c4, c128 = W.quantized_mixed(dev, seed=0)
@@ -450,6 +497,8 @@ def main():
         extra["quantized_mixed_decode"] = quant_mixed(torch, hyb, W, BM, args)
         log("multi-query decode")
         extra["multi_query_decode"] = multi_decode(torch, hyb, W, BM, args)
+        log("fused steps around the decode attention")
+        extra["decode_neighbour_steps"] = neighbour_steps(torch, hyb, W, BM, args, rep0)
     cpu = None
     if not args.no_cpu_baseline:
         log("oracle CPU baseline")
