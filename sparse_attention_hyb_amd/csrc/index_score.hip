@@ -432,27 +432,32 @@ __global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
 // tile (two direct loads of four keys each) into a ring of kMStages shared tiles; after a barrier
 // every wave whose query is in the group scores the tile. Each query's keys and histograms then go
 // through the same hand-off (or plain scores) as in the one-query kernels.
-constexpr int kMQ = 4;        // queries per workgroup (one per wave)
-constexpr int kMStages = 6;   // shared 8 KB tiles in the ring (five in flight)
+constexpr int kMQ = 4;                       // queries per workgroup (one per wave)
+constexpr int kMKeys = kScorePartKeys;       // keys per workgroup: one hand-off part
+constexpr int kMParts = kMKeys / kScorePartKeys;
+constexpr int kMStages = 4;                  // shared 8 KB tiles in the ring (three in flight)
+// LDS: ring 32 KB + per query 1024 keys and 1024 bins (16 KB each for four queries) + block
+// table: about 66 KB, so that two workgroups (two waves per SIMD) share a compute unit and one's
+// barriers, operand reads and hand-off overlap the other's MFMA work.
 // Launches with explicit sequence ids and at least this many queries take the shared-tile kernel.
 // A workgroup whose four queries belong to different sequences streams each sequence's keys in
 // turn, which is only cheap when most workgroups hold one sequence and the grid is large; a decode
 // batch (one or a few queries per sequence) keeps the one-query kernel.
 constexpr int kMultiMinQueries = 256;
 
-__global__ __launch_bounds__(256, 1) void score_mfma_multi(ScoreArgs a) {
+__global__ __launch_bounds__(256, 2) void score_mfma_multi(ScoreArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage[kMStages][8192];
-  __shared__ uint32_t lhist[kMQ][kScoreParts * kTopBins];
-  __shared__ uint32_t lkeys[kMQ][kScoreKeysPerBlock];
-  __shared__ int32_t tbl[kScoreKeysPerBlock / 2 + 2];
-  __shared__ uint32_t wtot[kScoreParts * 4];
+  __shared__ uint32_t lhist[kMQ][kMParts * kTopBins];
+  __shared__ uint32_t lkeys[kMQ][kMKeys];
+  __shared__ int32_t tbl[kMKeys / 2 + 2];
+  __shared__ uint32_t wtot[kMParts * 4];
   __shared__ int32_t gseq[kMQ], gnv[kMQ];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int hf = lane >> 5;
-  const int base = blockIdx.x * kScoreKeysPerBlock;
+  const int base = blockIdx.x * kMKeys;
   const int i = blockIdx.y * kMQ + wave;   // this wave's query
   const bool has_q = i < a.n_q;
   const int iq = min(i, a.n_q - 1);        // in-bounds row for the loads of an absent query
@@ -460,13 +465,13 @@ __global__ __launch_bounds__(256, 1) void score_mfma_multi(ScoreArgs a) {
   const int p = a.qd.q_pos[iq];
   const int nv = has_q ? min(n_visible(p, a.pool.ratio, a.window),
                              n_visible(a.max_pos, a.pool.ratio, a.window)) : 0;
-  const int end_w = min(nv, base + kScoreKeysPerBlock);   // this wave's keys: [base, end_w)
+  const int end_w = min(nv, base + kMKeys);   // this wave's keys: [base, end_w)
   if (lane == 0) {
     gseq[wave] = has_q ? seq : -1;
     gnv[wave] = nv;
   }
   if (a.part_hist)
-    for (int j = tid; j < kMQ * kScoreParts * kTopBins; j += 256) (&lhist[0][0])[j] = 0;
+    for (int j = tid; j < kMQ * kMParts * kTopBins; j += 256) (&lhist[0][0])[j] = 0;
 
   // this wave's query and head weights (as in score_mfma_dma)
   bf16x8 qa[2][8];
@@ -501,7 +506,7 @@ __global__ __launch_bounds__(256, 1) void score_mfma_multi(ScoreArgs a) {
       if (w1 < w0) lead = false;
       nv_s = max(nv_s, gnv[w1]);
     }
-    const int end_s = min(nv_s, base + kScoreKeysPerBlock);
+    const int end_s = min(nv_s, base + kMKeys);
     if (!lead || base >= end_s) continue;   // uniform
     const bool mine = has_q && seq == sq;   // uniform per wave
     __syncthreads();   // the previous group's readers of tbl and of the tiles are done
@@ -571,10 +576,10 @@ __global__ __launch_bounds__(256, 1) void score_mfma_multi(ScoreArgs a) {
     // the tiles are free now: the sorted pairs use them
     for (int w = 0; w < kMQ; ++w) {
       const int qi = blockIdx.y * kMQ + w;
-      const int e = min(gnv[w], base + kScoreKeysPerBlock);
+      const int e = min(gnv[w], base + kMKeys);
       if (gseq[w] < 0 || base >= e) continue;   // uniform
-      finish_parts<kScoreParts>(a, qi, blockIdx.x * kScoreParts, base, e, lkeys[w], lhist[w],
-                                reinterpret_cast<uint2*>(&stage[0][0]), wtot);
+      finish_parts<kMParts>(a, qi, blockIdx.x * kMParts, base, e, lkeys[w], lhist[w],
+                            reinterpret_cast<uint2*>(&stage[0][0]), wtot);
     }
   }
 }
@@ -656,6 +661,7 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s) {
     dim3 grid((max_nv + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock, a.n_q);
     if (a.pool.dtype == BF16 && a.qd.q_seq && a.n_q >= kMultiMinQueries) {
       // a prefill chunk: runs of queries of one sequence share the key stream, kMQ per workgroup
+      grid.x = (max_nv + kMKeys - 1) / kMKeys;
       grid.y = (a.n_q + kMQ - 1) / kMQ;
       hipLaunchKernelGGL(score_mfma_multi, grid, dim3(256), 0, s, a);
     } else if (a.pool.dtype == BF16) {
