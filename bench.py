@@ -363,6 +363,44 @@ def neighbour_steps(torch, hyb, W, BM, args, rep):
                          "dim": 512, "note": "attention + combine with compression; cache-warm"})
 
 
+def full_step(torch, hyb, W, BM, args):
+    """The whole C4 decode step with the query prep and window insert (hyb_q_norm_kv_insert)
+    in front: serial on one stream, prep on a side stream beside the indexer, and the two-stream
+    step replayed from one HIP graph per replica."""
+    from sparse_attention_hyb_amd.decode_step import DecodeStep, DecodeStepBuffers
+    dev = "cuda"
+    B, L, R = 16, 131072, max(1, args.replicas)
+    kshape, hshape = hyb.index_keys_shapes(B, L - 1)
+    steps, side = [], torch.cuda.Stream()
+    for r in range(R):
+        wl = W.sparse_decode(dev, seed=r)
+        g = W.generator(8, r, 99, dev)
+        buf = DecodeStepBuffers(
+            q_raw=W.to_storage(W.randn((B, 64, 512), g, dev), "bf16"),
+            kv_new=W.to_storage(W.randn((B, 512), g, dev), "bf16"), q=wl.q,
+            seq_lens=wl.seq_lens, cu=torch.arange(0, B + 1, dtype=torch.int32, device=dev),
+            start=(wl.seq_lens - 1).contiguous(), swa=wl.swa, comp=wl.comp,
+            state=W.to_storage(W.randn((B, 4, 512), g, dev), "bf16"), out=torch.empty_like(wl.q),
+            workspace=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, L, 4, wl.k),
+                                  dtype=torch.uint8, device=dev),
+            max_seq_len=L, idx_q=wl.idx_q, idx_w=wl.idx_w, idx_pool=wl.idx_pool,
+            keys=torch.empty(kshape, dtype=torch.int32, device=dev),
+            hist=torch.empty(hshape, dtype=torch.int16, device=dev),
+            topk=torch.empty(B, wl.k, dtype=torch.int32, device=dev), k=wl.k)
+        steps.append(DecodeStep(buf, side))
+    n = args.steps
+    serial = time_loop(torch, lambda r, ev: steps[r].run_serial(), n, args.warmup, R)
+    two = time_loop(torch, lambda r, ev: steps[r].run(), n, args.warmup, R)
+    graphs = [s.capture() for s in steps]
+    gr = time_loop(torch, lambda r, ev: graphs[r].replay(), n, args.warmup, R)
+    us = lambda t: t * 1e6 / n
+    return dict(value=B * n / two, unit="query-tokens/s", serial_us=us(serial),
+                two_stream_us=us(two), two_stream_graph_us=us(gr), steps=n,
+                config={"workload": "c4_sparse_decode + query prep", "batch": B, "context": L,
+                        "replicas": R, "step": "q RMSNorm+RoPE and window insert (side stream) | "
+                        "indexer + top-512 (main), then attention + combine with compression"})
+
+
 def quant_mixed(torch, hyb, W, BM, args):
     dev = "cuda"
     c4, c128 = W.quantized_mixed(dev, seed=0)
@@ -497,6 +535,8 @@ def main():
         extra["quantized_mixed_decode"] = quant_mixed(torch, hyb, W, BM, args)
         log("multi-query decode")
         extra["multi_query_decode"] = multi_decode(torch, hyb, W, BM, args)
+        log("full decode step with the query prep, one and two streams, graph")
+        extra["c4_full_decode_step"] = full_step(torch, hyb, W, BM, args)
         log("fused steps around the decode attention")
         extra["decode_neighbour_steps"] = neighbour_steps(torch, hyb, W, BM, args, rep0)
     cpu = None
