@@ -600,14 +600,19 @@ def _clone_pool(p):
                           p.block_table, p.dtype, p.dim, p.ratio)
 
 
-@pytest.mark.parametrize("case", ["c4_bf16", "c128_gate_bf16", "c4_f32x", "c4_unaligned_x"])
+_FUSED_CASES = ["c4_bf16", "c128_gate_bf16", "c4_f32x", "c4_unaligned_x", "c4_fp8out",
+                "c128_gate_fp8out"]
+
+
+@pytest.mark.parametrize("case", _FUSED_CASES)
 def test_attn_decode_compress_equals_two_calls(gpu_lib, case):
     """hyb_attn_decode_compress leaves exactly what hyb_attn_decode then hyb_compress leave: the
-    attention output, every pool byte, the state ring and its logits. The compressor runs beside
-    the combine (bf16 / f32 x) or after it (x not 16-byte aligned); sequences complete a group or
-    only extend the ring."""
+    attention output (bf16 rows, or fp8 rows and their scales), every pool byte, the state ring
+    and its logits. The compressor runs beside the combine (bf16 / f32 x) or after it (x not
+    16-byte aligned); sequences complete a group or only extend the ring."""
     hyb = gpu_lib
-    g = W.generator(91, ["c4_bf16", "c128_gate_bf16", "c4_f32x", "c4_unaligned_x"].index(case), 0, DEV)
+    g = W.generator(91, _FUSED_CASES.index(case), 0, DEV)
+    fp8 = case.endswith("fp8out")
     if case.startswith("c4"):
         lens = [4096, 4097, 4098, 4099, 131072, 9000]
         wl = W.sparse_decode(DEV, seed=5, batch=len(lens), ctx=lens)
@@ -635,9 +640,10 @@ def test_attn_decode_compress_equals_two_calls(gpu_lib, case):
     for fused in (False, True):
         comp, swa = _clone_pool(wl.comp), wl.swa
         stt, stl = state.clone(), None if st_l is None else st_l.clone()
-        out = torch.empty_like(wl.q)
+        out = torch.empty(wl.q.shape, dtype=torch.uint8 if fp8 else wl.q.dtype, device=DEV)
+        sc = torch.empty(wl.q.shape[:2], dtype=torch.float32, device=DEV) if fp8 else None
         kw = dict(topk_idx=topk, k=wl.k if topk is not None else 0, window=wl.window,
-                  rope_dim=wl.rope_dim, rope_base=wl.rope_base)
+                  rope_dim=wl.rope_dim, rope_base=wl.rope_base, out_scale=sc)
         if fused:
             hyb.hyb_attn_decode_compress(wl.q, wl.seq_lens, wl.max_seq_len, swa, comp, out, x_use,
                                          cu, start, 1, stt, comp, eps=1e-6, gate_logits=gl,
@@ -646,10 +652,12 @@ def test_attn_decode_compress_equals_two_calls(gpu_lib, case):
             hyb.hyb_attn_decode(wl.q, wl.seq_lens, wl.max_seq_len, swa, comp, out, **kw)
             hyb.hyb_compress(x_use, cu, start, 1, stt, comp, wl.rope_dim, wl.rope_base, eps=1e-6,
                              gate_logits=gl, state_logits=stl)
-        runs.append((out, comp.data, stt, stl))
+        runs.append((out, comp.data, stt, stl, sc))
     sync()
-    (o0, c0, s0, l0), (o1, c1, s1, l1) = runs
+    (o0, c0, s0, l0, q0), (o1, c1, s1, l1, q1) = runs
     assert torch.equal(o0, o1)
+    if fp8:
+        assert torch.equal(q0, q1)
     assert torch.equal(c0, c1)
     assert torch.equal(s0, s1)
     if gate:
