@@ -51,7 +51,7 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float sc) {
 // part_hist[b0] pairs of every part. The workgroup's keys are in lkeys[0, P * kScorePartKeys)
 // (index g - base) and its per-part counts in lhist[P][kTopBins], which become bucket cursors;
 // lsorted (P * kScorePartKeys uint2) is scratch. 256 threads.
-template <int P>
+template <int P, bool kPacked = false>
 __device__ __forceinline__ void finish_parts(const ScoreArgs& a, int i, int part0, int base, int end,
                                              const uint32_t* lkeys, uint32_t* lhist, uint2* lsorted,
                                              uint32_t* wtot) {
@@ -61,12 +61,14 @@ __device__ __forceinline__ void finish_parts(const ScoreArgs& a, int i, int part
 #pragma unroll
   for (int q = 0; q < P; ++q) {
     if (base + q * kScorePartKeys >= end) break;   // uniform
-    uint32_t* h = lhist + q * kTopBins;
+    uint32_t* h = lhist + q * (kPacked ? kTopBins / 2 : kTopBins);
     // thread t owns bins 1023 - 4t - e (e < 4), i.e. bins in descending order across threads
+    // (packed: two 16-bit counts per word, bin b in half b % 2 of word b / 2)
     uint32_t c[4], tot = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      c[e] = h[kTopBins - 1 - 4 * t - e];
+      const int bin = kTopBins - 1 - 4 * t - e;
+      c[e] = kPacked ? (h[bin >> 1] >> (16 * (bin & 1))) & 0xffffu : h[bin];
       tot += c[e];
     }
     const uint32_t incl = wave_inclusive_scan(tot);
@@ -76,12 +78,19 @@ __device__ __forceinline__ void finish_parts(const ScoreArgs& a, int i, int part
     for (int v = 0; v < w; ++v) before += wtot[q * 4 + v];
     // cum[b] = keys with top bits >= b; bucket b starts at cum[b] - count[b]
     uint32_t run = before;
-    uint32_t cum[4];
+    uint32_t cum[4], cur[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      h[kTopBins - 1 - 4 * t - e] = run;   // cursor: start of the bucket
+      cur[e] = run;   // cursor: start of the bucket
       run += c[e];
       cum[e] = run;
+    }
+    if constexpr (kPacked) {   // bins 1020 - 4t .. 1023 - 4t: words 510 - 2t, 511 - 2t
+      h[kTopBins / 2 - 2 - 2 * t] = cur[3] | (cur[2] << 16);
+      h[kTopBins / 2 - 1 - 2 * t] = cur[1] | (cur[0] << 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[kTopBins - 1 - 4 * t - e] = cur[e];
     }
     // bins 1020 - 4t .. 1023 - 4t, ascending in memory
     uint2 wv;
@@ -95,7 +104,14 @@ __device__ __forceinline__ void finish_parts(const ScoreArgs& a, int i, int part
   for (int j = t; j < nk; j += 256) {
     const uint32_t key = lkeys[j];
     const int q = j / kScorePartKeys;
-    const uint32_t slot = atomicAdd(&lhist[q * kTopBins + (key >> (32 - kTopBits))], 1u);
+    const uint32_t bin = key >> (32 - kTopBits);
+    uint32_t slot;
+    if constexpr (kPacked) {
+      const uint32_t sh = 16 * (bin & 1u);
+      slot = (atomicAdd(&lhist[q * (kTopBins / 2) + (bin >> 1)], 1u << sh) >> sh) & 0xffffu;
+    } else {
+      slot = atomicAdd(&lhist[q * kTopBins + bin], 1u);
+    }
     lsorted[q * kScorePartKeys + slot] = make_uint2(key, (uint32_t)(base + j));
   }
   __syncthreads();
@@ -435,19 +451,20 @@ __global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
 constexpr int kMQ = 4;                       // queries per workgroup (one per wave)
 constexpr int kMKeys = kScorePartKeys;       // keys per workgroup: one hand-off part
 constexpr int kMParts = kMKeys / kScorePartKeys;
-constexpr int kMStages = 4;                  // shared 8 KB tiles in the ring (three in flight)
-// LDS: ring 32 KB + per query 1024 keys and 1024 bins (16 KB each for four queries) + block
-// table: about 66 KB, so that two workgroups (two waves per SIMD) share a compute unit and one's
-// barriers, operand reads and hand-off overlap the other's MFMA work.
+constexpr int kMStages = 3;                  // shared 8 KB tiles in the ring (two in flight)
+// LDS: ring 24 KB + per query 1024 keys (16 KB for four queries) and 1024 16-bit bin counts
+// packed two to a word (8 KB) + block table: about 50 KB, so that three workgroups (three waves
+// per SIMD) share a compute unit and one's barriers, operand reads and hand-off overlap the
+// others' MFMA work.
 // Launches with explicit sequence ids and at least this many queries take the shared-tile kernel.
 // A workgroup whose four queries belong to different sequences streams each sequence's keys in
 // turn, which is only cheap when most workgroups hold one sequence and the grid is large; a decode
 // batch (one or a few queries per sequence) keeps the one-query kernel.
 constexpr int kMultiMinQueries = 256;
 
-__global__ __launch_bounds__(256, 2) void score_mfma_multi(ScoreArgs a) {
+__global__ __launch_bounds__(256, 3) void score_mfma_multi(ScoreArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage[kMStages][8192];
-  __shared__ uint32_t lhist[kMQ][kMParts * kTopBins];
+  __shared__ uint32_t lhist[kMQ][kMParts * kTopBins / 2];   // counts <= 1024: 16 bits each
   __shared__ uint32_t lkeys[kMQ][kMKeys];
   __shared__ int32_t tbl[kMKeys / 2 + 2];
   __shared__ uint32_t wtot[kMParts * 4];
@@ -471,7 +488,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_multi(ScoreArgs a) {
     gnv[wave] = nv;
   }
   if (a.part_hist)
-    for (int j = tid; j < kMQ * kMParts * kTopBins; j += 256) (&lhist[0][0])[j] = 0;
+    for (int j = tid; j < kMQ * kMParts * kTopBins / 2; j += 256) (&lhist[0][0])[j] = 0;
 
   // this wave's query and head weights (as in score_mfma_dma)
   bf16x8 qa[2][8];
@@ -563,7 +580,8 @@ __global__ __launch_bounds__(256, 2) void score_mfma_multi(ScoreArgs a) {
           if (a.part_hist) {
             const uint32_t key = order_key(v);
             lkeys[wave][g - base] = key;
-            atomicAdd(&lhist[wave][((g - base) / kScorePartKeys) * kTopBins + (key >> (32 - kTopBits))], 1u);
+            const uint32_t bin = key >> (32 - kTopBits);   // one part per workgroup
+            atomicAdd(&lhist[wave][bin >> 1], 1u << (16 * (bin & 1u)));
           } else {
             a.scores[(int64_t)i * a.ld + g] = v;
           }
@@ -578,8 +596,8 @@ __global__ __launch_bounds__(256, 2) void score_mfma_multi(ScoreArgs a) {
       const int qi = blockIdx.y * kMQ + w;
       const int e = min(gnv[w], base + kMKeys);
       if (gseq[w] < 0 || base >= e) continue;   // uniform
-      finish_parts<kMParts>(a, qi, blockIdx.x * kMParts, base, e, lkeys[w], lhist[w],
-                            reinterpret_cast<uint2*>(&stage[0][0]), wtot);
+      finish_parts<kMParts, true>(a, qi, blockIdx.x * kMParts, base, e, lkeys[w], lhist[w],
+                                  reinterpret_cast<uint2*>(&stage[0][0]), wtot);
     }
   }
 }
