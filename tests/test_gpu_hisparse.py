@@ -1,0 +1,41 @@
+"""C4 offload (pinned host mirror + device working set): the attention over the working set equals
+the attention over the device-resident pool bit for bit, step after step, while pages are
+evicted and brought back."""
+
+import pytest
+import torch
+
+from sparse_attention_hyb_amd import workloads as W
+from sparse_attention_hyb_amd.hisparse import C4Offload
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def test_c4_offload_equals_device_pool(gpu_lib):
+    """Four sequences (20000, 50000, 131072 and 7000 tokens: 815 pages of 64 entries in all), a
+    working set of 700 pages, and three decode steps whose indexer queries are drawn afresh, so
+    each step selects about 600 pages, some of them evicted by the step before."""
+    hyb = gpu_lib
+    from tests.test_gpu_parity import gpu_decode, gpu_topk
+    lens = [20000, 50000, 131072, 7000]
+    wl = W.sparse_decode(DEV, seed=6, batch=len(lens), ctx=lens)
+    mirror = W.PagedTensors(wl.comp.data.cpu().pin_memory(), None, wl.comp.block_table.cpu(),
+                            wl.comp.dtype, wl.dim, 4)
+    off = C4Offload(mirror, slots=700)
+    g = W.generator(98, 0, 0, DEV)
+    hits = 0
+    for step in range(3):
+        wl.idx_q = W.to_storage(W.randn(tuple(wl.idx_q.shape), g, DEV), "bf16")
+        topk = gpu_topk(hyb, wl)
+        st = off.admit(topk.cpu().numpy())
+        assert st.pages <= 700
+        hits += st.pages - st.misses
+        want = gpu_decode(hyb, wl, topk)
+        comp = wl.comp
+        wl.comp = off.pool()
+        got = gpu_decode(hyb, wl, topk)
+        wl.comp = comp
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), step
+    assert hits > 0   # later steps reuse resident pages
