@@ -401,6 +401,62 @@ def full_step(torch, hyb, W, BM, args):
                         "indexer + top-512 (main), then attention + combine with compression"})
 
 
+def offload_decode(torch, hyb, W, BM, args):
+    """C4 decode (16 x 131072) with the C4 pool offloaded to a pinned host mirror and a device
+    working set of three quarters of its pages. With independent random keys a query's top-512
+    falls on about 63 % of its sequence's 512 pages, so a step needs about 5200 of the 8192 pages
+    and a smaller working set cannot hold one step. Synthetic step-to-step locality: each step's
+    indexer queries are the first step's plus a fresh N(0, 0.3^2) perturbation, so consecutive
+    top-k sets overlap. A step: indexer + top-512, top-k read back, admission of the missing
+    pages, attention."""
+    from sparse_attention_hyb_amd.hisparse import C4Offload
+    dev = "cuda"
+    wl = W.sparse_decode(dev, seed=0)
+    B, L = wl.batch, wl.max_seq_len
+    mirror = W.PagedTensors(wl.comp.data.cpu().pin_memory(), None, wl.comp.block_table.cpu(),
+                            wl.comp.dtype, wl.dim, 4)
+    total_pages = int((wl.comp.block_table >= 0).sum())
+    off = C4Offload(mirror, slots=3 * total_pages // 4)
+    g = W.generator(9, 0, 99, dev)
+    q0 = wl.idx_q.float()
+    kshape, hshape = hyb.index_keys_shapes(B, L - 1)
+    keys = torch.empty(kshape, dtype=torch.int32, device=dev)
+    hist = torch.empty(hshape, dtype=torch.int16, device=dev)
+    topk = torch.empty(B, wl.k, dtype=torch.int32, device=dev)
+    out = torch.empty_like(wl.q)
+    ws = torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, L, 4, wl.k), dtype=torch.uint8, device=dev)
+    qpos = (wl.seq_lens - 1).contiguous()
+    pool = off.pool()
+    n_steps = 20
+    queries = [W.to_storage(q0 + 0.3 * W.randn(tuple(q0.shape), g, dev), "bf16") for _ in range(n_steps + 2)]
+    stats, t_step, t_admit = [], 0.0, 0.0
+    for s in range(n_steps + 2):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        hyb.hyb_index_score_keys(queries[s], wl.idx_w, qpos, L - 1, wl.idx_pool, keys, hist)
+        hyb.hyb_topk_keys(keys, hist, qpos, L - 1, wl.k, topk)
+        rows = topk.cpu().numpy()
+        t1 = time.perf_counter()
+        st = off.admit(rows)
+        hyb.hyb_attn_decode(wl.q, wl.seq_lens, L, wl.swa, pool, out, topk_idx=topk, k=wl.k, workspace=ws)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        if s >= 2:   # the first steps fill the working set
+            stats.append(st)
+            t_step += t2 - t0
+            t_admit += t2 - t1
+    n = len(stats)
+    miss = sum(x.misses for x in stats) / n
+    pages = sum(x.pages for x in stats) / n
+    nbytes = sum(x.bytes for x in stats) / n
+    return dict(value=B * n / t_step, unit="query-tokens/s", ms_per_step=t_step * 1e3 / n,
+                ms_admit_and_attention=t_admit * 1e3 / n, pages_per_step=pages, misses_per_step=miss,
+                mb_copied_per_step=nbytes / 1e6, working_set_pages=off.slots, pool_pages=total_pages,
+                steps=n, config={"workload": "c4_sparse_decode with the C4 pool offloaded", "batch": B,
+                                 "context": L, "working_set": "3/4 of the pool's pages",
+                                 "locality": "indexer queries = first step's + N(0, 0.3^2)"})
+
+
 def quant_mixed(torch, hyb, W, BM, args):
     dev = "cuda"
     c4, c128 = W.quantized_mixed(dev, seed=0)
@@ -537,6 +593,8 @@ def main():
         extra["multi_query_decode"] = multi_decode(torch, hyb, W, BM, args)
         log("full decode step with the query prep, one and two streams, graph")
         extra["c4_full_decode_step"] = full_step(torch, hyb, W, BM, args)
+        log("C4 decode with the C4 pool offloaded to host memory")
+        extra["c4_offload_decode"] = offload_decode(torch, hyb, W, BM, args)
         log("fused steps around the decode attention")
         extra["decode_neighbour_steps"] = neighbour_steps(torch, hyb, W, BM, args, rep0)
     cpu = None

@@ -180,6 +180,19 @@ int32_t hyb_swa_insert(const void* x, int32_t x_dtype, const int32_t* cu_seqlens
  *          in hyb_swa_insert)
  * The query rows it writes are what hyb_attn_decode / hyb_attn_prefill take at these positions.
  * ------------------------------------------------------------------------------------------ */
+/* --------------------------------------------------------------------------------------------
+ * hyb_gather_pages - fill pages of a device working set from a pinned host mirror in one launch
+ * (the offload of [SGLang] "HiSparse": the C4 pool lives in CPU memory, missing pages are brought
+ * to a device buffer every step). For j < n:
+ *   dst + dst_page[j] * page_bytes  <-  src_host + src_page[j] * page_bytes   (page_bytes bytes)
+ *   src_host  pinned host memory (hipHostMalloc, or a pinned torch tensor); the kernel reads it
+ *             through the device alias hipHostGetDevicePointer gives; HYB_EINVAL if it has none
+ *   dst       device memory;  src_page, dst_page int32 [n] in device memory;  page_bytes % 16 == 0,
+ *             src_host and dst 16-byte aligned. Destination pages must not repeat.
+ * ------------------------------------------------------------------------------------------ */
+int32_t hyb_gather_pages(const void* src_host, void* dst, const int32_t* src_page,
+                         const int32_t* dst_page, int32_t n, int64_t page_bytes, void* stream);
+
 int32_t hyb_q_norm_kv_insert(const void* q, int32_t q_dtype, int32_t n_heads, const void* kv,
                              int32_t kv_dtype, const int32_t* cu_seqlens, const int32_t* start_pos,
                              int32_t batch, int32_t max_new_tokens, void* q_out,

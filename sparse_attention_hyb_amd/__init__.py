@@ -29,7 +29,7 @@ DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp4": FP4_E2M1}
 
 EXPORTS = (
     "hyb_abi_version", "hyb_status_str", "hyb_last_error", "hyb_compress", "hyb_swa_insert",
-    "hyb_q_norm_kv_insert",
+    "hyb_q_norm_kv_insert", "hyb_gather_pages",
     "hyb_index_score", "hyb_topk", "hyb_index_score_keys", "hyb_topk_keys",
     "hyb_index_topk_workspace_bytes", "hyb_index_topk",
     "hyb_attn_decode_workspace_bytes", "hyb_attn_decode", "hyb_attn_decode_compress",
@@ -96,6 +96,7 @@ _SIGS = {
     "hyb_index_topk": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _PP, _I32, _P, _P, _SZ, _P]),
     "hyb_q_norm_kv_insert": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P, _PP, _I32, _D,
                                     _F, _P]),
+    "hyb_gather_pages": (_I32, [_P, _P, _P, _P, _I32, _I64, _P]),
     "hyb_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "hyb_attn_decode": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F, _I32,
                                _D, _P, _I32, _P, _P, _SZ, _P]),
@@ -224,6 +225,17 @@ def hyb_q_norm_kv_insert(q, kv, cu_seqlens, start_pos, max_new_tokens: int, swa_
                                        int(max_new_tokens), _ptr(q_out), ctypes.byref(d),
                                        int(rope_dim), float(rope_base), float(eps), _stream(stream)))
     return q_out
+
+
+def hyb_gather_pages(src_host, dst, src_page, dst_page, stream=None) -> None:
+    """Copy pages src_host[src_page[j]] -> dst[dst_page[j]] in one launch (see include/hyb.h).
+    src_host: a pinned CPU tensor [pages, ...]; dst: a device tensor of the same page shape;
+    src_page, dst_page: int32 device tensors of one length."""
+    page = src_host[0].numel() * src_host.element_size()
+    if dst[0].numel() * dst.element_size() != page:
+        raise TypeError("src_host and dst pages differ in size")
+    _check(load().hyb_gather_pages(_ptr(src_host), _ptr(dst), _ptr(src_page), _ptr(dst_page),
+                                   int(src_page.numel()), int(page), _stream(stream)))
 
 
 def hyb_index_score(q_idx, w, q_pos, max_pos: int, idx_pool, scores, window: int = 128,

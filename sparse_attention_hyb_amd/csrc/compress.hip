@@ -267,4 +267,36 @@ hipError_t launch_q_norm_kv_insert(const QNormArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Working-set fill of an offloaded pool: workgroup j copies page src_page[j] of the host mirror
+// (through its device alias) to page dst_page[j] of the device pool, 16 bytes per thread and
+// load, every load of a thread issued before its stores.
+__global__ __launch_bounds__(256) void gather_pages_kernel(const uint8_t* src, uint8_t* dst,
+                                                           const int32_t* src_page,
+                                                           const int32_t* dst_page,
+                                                           int64_t page_bytes) {
+  const int j = blockIdx.x;
+  const u32x4* s = reinterpret_cast<const u32x4*>(src + (int64_t)src_page[j] * page_bytes);
+  u32x4* d = reinterpret_cast<u32x4*>(dst + (int64_t)dst_page[j] * page_bytes);
+  const int64_t n16 = page_bytes / 16;
+  constexpr int kU = 8;
+  for (int64_t o = threadIdx.x; o < n16; o += 256 * kU) {
+    u32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (o + 256 * u < n16) v[u] = s[o + 256 * u];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (o + 256 * u < n16) d[o + 256 * u] = v[u];
+  }
+}
+
+hipError_t launch_gather_pages(const void* src_dev, void* dst, const int32_t* src_page,
+                               const int32_t* dst_page, int32_t n, int64_t page_bytes,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(gather_pages_kernel, dim3(n), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(src_dev), static_cast<uint8_t*>(dst), src_page,
+                     dst_page, page_bytes);
+  return hipGetLastError();
+}
+
 }  // namespace hyb

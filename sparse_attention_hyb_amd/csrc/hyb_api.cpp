@@ -318,6 +318,27 @@ int32_t hyb_q_norm_kv_insert(const void* q, int32_t q_dtype, int32_t n_heads, co
   return launch_status(hyb::launch_q_norm_kv_insert(a, static_cast<hipStream_t>(stream)), op);
 }
 
+int32_t hyb_gather_pages(const void* src_host, void* dst, const int32_t* src_page,
+                         const int32_t* dst_page, int32_t n, int64_t page_bytes, void* stream) {
+  const char* op = "hyb_gather_pages";
+  if (!src_host || !dst || !src_page || !dst_page)
+    return fail(HYB_EINVAL, "%s: src_host, dst, src_page and dst_page must be non-NULL", op);
+  if (n < 0) return fail(HYB_EINVAL, "%s: n %d < 0", op, n);
+  if (page_bytes <= 0 || page_bytes % 16)
+    return fail(HYB_EINVAL, "%s: page_bytes %lld must be a positive multiple of 16", op,
+                (long long)page_bytes);
+  if ((reinterpret_cast<uintptr_t>(src_host) | reinterpret_cast<uintptr_t>(dst)) & 15u)
+    return fail(HYB_EINVAL, "%s: src_host and dst must be 16-byte aligned", op);
+  if (n == 0) return HYB_OK;
+  void* src_dev = nullptr;
+  if (hipHostGetDevicePointer(&src_dev, const_cast<void*>(src_host), 0) != hipSuccess || !src_dev) {
+    (void)hipGetLastError();
+    return fail(HYB_EINVAL, "%s: src_host is not pinned host memory with a device alias", op);
+  }
+  return launch_status(hyb::launch_gather_pages(src_dev, dst, src_page, dst_page, n, page_bytes,
+                                                static_cast<hipStream_t>(stream)), op);
+}
+
 static int check_score(const char* op, const void* q_idx, int32_t q_dtype, const float* w,
                        const int32_t* q_pos, int32_t n_q, int32_t n_heads, int32_t max_pos,
                        int32_t window, const hyb_paged* idx_pool, hyb::ScoreArgs* a) {

@@ -18,7 +18,7 @@ the step changed (the one that receives a new entry) back to the mirror.
 """
 
 from dataclasses import dataclass
-from typing import Iterable, List, Optional, Tuple
+from typing import Iterable, Optional, Tuple
 
 import numpy as np
 import torch
@@ -52,66 +52,89 @@ class C4Offload:
         pin = self.device.type == "cuda"
         self._table_stage = torch.empty(self.table.shape, dtype=torch.int32, pin_memory=pin)
         self.dev_table = torch.full(self.table.shape, -1, dtype=torch.int32, device=self.device)
-        self.owner: List[Optional[Tuple[int, int]]] = [None] * self.slots   # slot -> (seq, block)
-        self.where = {}                                                       # (seq, block) -> slot
-        self.stamp = np.zeros(self.slots, dtype=np.int64)
+        # pages copied by one gather launch (hyb_gather_pages) when the mirror is pinned and the
+        # working set is on the GPU; page lists staged through pinned memory
+        self.one_launch = pin and mirror.data.is_pinned() and mirror.data.is_contiguous()
+        if self.one_launch:
+            self._idx_stage = torch.empty((2, self.slots), dtype=torch.int32, pin_memory=True)
+            self._idx_dev = torch.empty((2, self.slots), dtype=torch.int32, device=self.device)
+        self.owner = np.full(self.slots, -1, dtype=np.int64)   # slot -> page key seq * max_blocks + block
+        self.stamp = np.zeros(self.slots, dtype=np.int64)       # last step that needed the slot's page
         self.clock = 0
+
+    @property
+    def where(self) -> dict:
+        """Resident pages: (sequence, logical block) -> slot."""
+        mb = self.table.shape[1]
+        return {(int(k // mb), int(k % mb)): int(s) for s, k in enumerate(self.owner) if k >= 0}
 
     def pool(self) -> PagedTensors:
         """The working set as a pool for the attention entry points."""
         return PagedTensors(self.data, None, self.dev_table, self.mirror.dtype, self.mirror.dim, 4)
 
-    def pages_of(self, topk_rows: np.ndarray) -> List[Tuple[int, int]]:
-        """Distinct (sequence, logical block) pages that top-k rows [B, k] select (-1 ignored)."""
-        need = set()
-        for b, row in enumerate(np.asarray(topk_rows)):
-            for lb in np.unique(row[row >= 0] // self.per):
-                need.add((b, int(lb)))
-        return sorted(need)
+    def page_keys(self, topk_rows: np.ndarray) -> np.ndarray:
+        """Sorted distinct page keys (sequence * max_blocks + logical block) that top-k rows
+        [B, k] select (-1 entries ignored)."""
+        rows = np.asarray(topk_rows, dtype=np.int64)
+        seq = np.broadcast_to(np.arange(rows.shape[0])[:, None], rows.shape)
+        sel = rows >= 0
+        return np.unique(seq[sel] * self.table.shape[1] + rows[sel] // self.per)
 
     def admit(self, topk_rows: np.ndarray, extra: Iterable[Tuple[int, int]] = (),
               stream: Optional[torch.cuda.Stream] = None) -> AdmitStats:
         """Make every page the rows select (and `extra` pages) resident; evict least recently used
         pages that this step does not need. Copies run on `stream` (the current one by default)
-        before the block table update, so work queued after this call on that stream sees them."""
-        need = sorted(set(self.pages_of(topk_rows)) | {(int(b), int(lb)) for b, lb in extra})
-        if len(need) > self.slots:
-            raise RuntimeError(f"step needs {len(need)} pages, working set holds {self.slots}")
+        before the block table update, so work queued after this call on that stream sees them.
+        Calls are ordered by the caller's read-back of each step's top-k rows (a host sync)."""
+        mb = self.table.shape[1]
+        need = self.page_keys(topk_rows)
+        ext = [int(b) * mb + int(lb) for b, lb in extra]
+        if ext:
+            need = np.union1d(need, np.asarray(ext, dtype=np.int64))
+        if need.size > self.slots:
+            raise RuntimeError(f"step needs {need.size} pages, working set holds {self.slots}")
         self.clock += 1
-        needed = set(need)
-        misses = [pg for pg in need if pg not in self.where]
-        for pg in need:
-            if pg in self.where:
-                self.stamp[self.where[pg]] = self.clock
-        free = [s for s in range(self.slots) if self.owner[s] is None]
-        # eviction order: least recently used first, among pages this step does not need
-        victims = sorted((s for s in range(self.slots)
-                          if self.owner[s] is not None and self.owner[s] not in needed),
-                         key=lambda s: self.stamp[s])
-        nbytes = 0
+        flat = self.dev_table_host.reshape(-1)
+        cur = flat[need]
+        hit = cur >= 0
+        self.stamp[cur[hit]] = self.clock
+        miss = need[~hit]
+        free = np.flatnonzero(self.owner < 0)
+        if miss.size > free.size:
+            # least recently used first, among resident pages this step does not need
+            keep = np.zeros(self.slots, dtype=bool)
+            keep[cur[hit]] = True
+            cand = np.flatnonzero((self.owner >= 0) & ~keep)
+            victims = cand[np.argsort(self.stamp[cand], kind="stable")[:miss.size - free.size]]
+            flat[self.owner[victims]] = -1
+            self.owner[victims] = -1
+            slots = np.concatenate([free, victims])
+        else:
+            slots = free[:miss.size]
+        src = self.table.reshape(-1)[miss]
+        if (src < 0).any():
+            raise RuntimeError("a selected page is not in the mirror")
+        page = self.data[0].numel() * self.data.element_size()
+        nbytes = page * int(miss.size)
         ctx = torch.cuda.stream(stream) if stream is not None else _nullctx()
         with ctx:
-            for pg in misses:
-                if free:
-                    s = free.pop()
-                else:
-                    s = victims.pop(0)
-                    old = self.owner[s]
-                    del self.where[old]
-                    self.dev_table_host[old] = -1
-                b, lb = pg
-                src = int(self.table[b, lb])
-                if src < 0:
-                    raise RuntimeError(f"page {pg} is not in the mirror")
-                self.data[s].copy_(self.mirror.data[src], non_blocking=True)
-                nbytes += self.data[s].numel() * self.data[s].element_size()
-                self.owner[s] = pg
-                self.where[pg] = s
-                self.stamp[s] = self.clock
-                self.dev_table_host[pg] = s
+            if self.one_launch and miss.size:
+                from . import hyb_gather_pages
+                m = int(miss.size)
+                self._idx_stage[0, :m].copy_(torch.from_numpy(src.astype(np.int32)))
+                self._idx_stage[1, :m].copy_(torch.from_numpy(slots.astype(np.int32)))
+                self._idx_dev[:, :m].copy_(self._idx_stage[:, :m], non_blocking=True)
+                hyb_gather_pages(self.mirror.data, self.data, self._idx_dev[0, :m], self._idx_dev[1, :m],
+                                 stream=stream)
+            else:
+                for sl, sb in zip(slots.tolist(), src.tolist()):
+                    self.data[sl].copy_(self.mirror.data[sb], non_blocking=True)
+            self.owner[slots] = miss
+            self.stamp[slots] = self.clock
+            flat[miss] = slots
             self._table_stage.copy_(torch.from_numpy(self.dev_table_host))
             self.dev_table.copy_(self._table_stage, non_blocking=True)
-        return AdmitStats(len(need), len(misses), nbytes)
+        return AdmitStats(int(need.size), int(miss.size), nbytes)
 
     def write_back(self, pages: Iterable[Tuple[int, int]],
                    stream: Optional[torch.cuda.Stream] = None) -> None:
@@ -119,9 +142,11 @@ class C4Offload:
         asynchronously on `stream`."""
         ctx = torch.cuda.stream(stream) if stream is not None else _nullctx()
         with ctx:
-            for pg in pages:
-                s = self.where[(int(pg[0]), int(pg[1]))]
-                self.mirror.data[int(self.table[pg])].copy_(self.data[s], non_blocking=True)
+            for b, lb in pages:
+                s = int(self.dev_table_host[int(b), int(lb)])
+                if s < 0:
+                    raise RuntimeError(f"page {(b, lb)} is not resident")
+                self.mirror.data[int(self.table[int(b), int(lb)])].copy_(self.data[s], non_blocking=True)
 
 
 class _nullctx:

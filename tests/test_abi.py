@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(hyb.EXPORTS) == names
@@ -251,3 +251,15 @@ def test_q_norm_kv_insert_validation(lib):
     assert call(eps=-1.0) == hyb.HYB_EINVAL
     assert lib.hyb_last_error().decode().startswith("hyb_q_norm_kv_insert")
     assert call(batch=0) == hyb.HYB_OK and call(maxnew=0) == hyb.HYB_OK
+
+
+def test_gather_pages_validation(lib):
+    def call(src=FAKE, dst=FAKE, sp=FAKE, dp=FAKE, n=4, page=65536):
+        return lib.hyb_gather_pages(src, dst, sp, dp, n, page, None)
+
+    assert call(src=None) == hyb.HYB_EINVAL and call(dp=None) == hyb.HYB_EINVAL
+    assert call(n=-1) == hyb.HYB_EINVAL
+    assert call(page=0) == hyb.HYB_EINVAL and call(page=100) == hyb.HYB_EINVAL
+    assert call(src=FAKE + 8) == hyb.HYB_EINVAL                      # not 16-byte aligned
+    assert lib.hyb_last_error().decode().startswith("hyb_gather_pages")
+    assert call(n=0) == hyb.HYB_OK

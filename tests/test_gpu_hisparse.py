@@ -38,4 +38,9 @@ def test_c4_offload_equals_device_pool(gpu_lib):
         wl.comp = comp
         torch.cuda.synchronize()
         assert torch.equal(got, want), step
+        # resident pages hold their mirror pages byte for byte (sampled)
+        res = sorted(off.where.items())
+        for (b, lb), s in res[::max(1, len(res) // 64)]:
+            assert torch.equal(off.data[s].cpu(), mirror.data[int(mirror.block_table[b, lb])]), (b, lb)
+    assert off.one_launch   # the pinned mirror took the one-launch gather
     assert hits > 0   # later steps reuse resident pages
