@@ -39,8 +39,8 @@ class C4Offload:
     def __init__(self, mirror: PagedTensors, slots: int, device="cuda"):
         if mirror.ratio != 4:
             raise ValueError("the offload takes a C4 pool (ratio 4)")
-        if mirror.scale is not None:
-            raise ValueError("fp8 mirrors: not supported by this coordinator")
+        if mirror.dtype not in ("bf16", "f32", "fp8"):
+            raise ValueError(f"{mirror.dtype} C4 mirrors are not supported")
         self.mirror = mirror                              # data on the host (pinned), table on the host
         self.table = mirror.block_table.cpu().numpy()     # logical block -> mirror block
         self.per = BLOCK_POSITIONS // 4
@@ -48,13 +48,17 @@ class C4Offload:
         self.device = torch.device(device)
         shape = (self.slots,) + tuple(mirror.data.shape[1:])
         self.data = torch.zeros(shape, dtype=mirror.data.dtype, device=self.device)
+        # fp8 pools: each page's per-entry scales travel with its codes
+        self.scale = None if mirror.scale is None else torch.ones(
+            (self.slots,) + tuple(mirror.scale.shape[1:]), dtype=mirror.scale.dtype, device=self.device)
         self.dev_table_host = np.full(self.table.shape, -1, dtype=np.int32)
         pin = self.device.type == "cuda"
         self._table_stage = torch.empty(self.table.shape, dtype=torch.int32, pin_memory=pin)
         self.dev_table = torch.full(self.table.shape, -1, dtype=torch.int32, device=self.device)
         # pages copied by one gather launch (hyb_gather_pages) when the mirror is pinned and the
         # working set is on the GPU; page lists staged through pinned memory
-        self.one_launch = pin and mirror.data.is_pinned() and mirror.data.is_contiguous()
+        self.one_launch = (pin and mirror.data.is_pinned() and mirror.data.is_contiguous() and
+                           (mirror.scale is None or (mirror.scale.is_pinned() and mirror.scale.is_contiguous())))
         if self.one_launch:
             self._idx_stage = torch.empty((2, self.slots), dtype=torch.int32, pin_memory=True)
             self._idx_dev = torch.empty((2, self.slots), dtype=torch.int32, device=self.device)
@@ -70,7 +74,7 @@ class C4Offload:
 
     def pool(self) -> PagedTensors:
         """The working set as a pool for the attention entry points."""
-        return PagedTensors(self.data, None, self.dev_table, self.mirror.dtype, self.mirror.dim, 4)
+        return PagedTensors(self.data, self.scale, self.dev_table, self.mirror.dtype, self.mirror.dim, 4)
 
     def page_keys(self, topk_rows: np.ndarray) -> np.ndarray:
         """Sorted distinct page keys (sequence * max_blocks + logical block) that top-k rows
@@ -115,6 +119,8 @@ class C4Offload:
         if (src < 0).any():
             raise RuntimeError("a selected page is not in the mirror")
         page = self.data[0].numel() * self.data.element_size()
+        if self.scale is not None:
+            page += self.scale[0].numel() * self.scale.element_size()
         nbytes = page * int(miss.size)
         ctx = torch.cuda.stream(stream) if stream is not None else _nullctx()
         with ctx:
@@ -126,9 +132,14 @@ class C4Offload:
                 self._idx_dev[:, :m].copy_(self._idx_stage[:, :m], non_blocking=True)
                 hyb_gather_pages(self.mirror.data, self.data, self._idx_dev[0, :m], self._idx_dev[1, :m],
                                  stream=stream)
+                if self.scale is not None:
+                    hyb_gather_pages(self.mirror.scale, self.scale, self._idx_dev[0, :m],
+                                     self._idx_dev[1, :m], stream=stream)
             else:
                 for sl, sb in zip(slots.tolist(), src.tolist()):
                     self.data[sl].copy_(self.mirror.data[sb], non_blocking=True)
+                    if self.scale is not None:
+                        self.scale[sl].copy_(self.mirror.scale[sb], non_blocking=True)
             self.owner[slots] = miss
             self.stamp[slots] = self.clock
             flat[miss] = slots
@@ -146,7 +157,10 @@ class C4Offload:
                 s = int(self.dev_table_host[int(b), int(lb)])
                 if s < 0:
                     raise RuntimeError(f"page {(b, lb)} is not resident")
-                self.mirror.data[int(self.table[int(b), int(lb)])].copy_(self.data[s], non_blocking=True)
+                dst = int(self.table[int(b), int(lb)])
+                self.mirror.data[dst].copy_(self.data[s], non_blocking=True)
+                if self.scale is not None:
+                    self.mirror.scale[dst].copy_(self.scale[s], non_blocking=True)
 
 
 class _nullctx:

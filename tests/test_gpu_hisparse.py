@@ -12,16 +12,19 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def test_c4_offload_equals_device_pool(gpu_lib):
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_c4_offload_equals_device_pool(gpu_lib, dtype):
     """Four sequences (20000, 50000, 131072 and 7000 tokens: 815 pages of 64 entries in all), a
     working set of 700 pages, and three decode steps whose indexer queries are drawn afresh, so
-    each step selects about 600 pages, some of them evicted by the step before."""
+    each step selects about 600 pages, some of them evicted by the step before. fp8 pools bring
+    each page's per-entry scales along."""
     hyb = gpu_lib
     from tests.test_gpu_parity import gpu_decode, gpu_topk
     lens = [20000, 50000, 131072, 7000]
-    wl = W.sparse_decode(DEV, seed=6, batch=len(lens), ctx=lens)
-    mirror = W.PagedTensors(wl.comp.data.cpu().pin_memory(), None, wl.comp.block_table.cpu(),
-                            wl.comp.dtype, wl.dim, 4)
+    wl = W.sparse_decode(DEV, seed=6, batch=len(lens), ctx=lens, dtype=dtype)
+    mirror = W.PagedTensors(wl.comp.data.cpu().pin_memory(),
+                            None if wl.comp.scale is None else wl.comp.scale.cpu().pin_memory(),
+                            wl.comp.block_table.cpu(), wl.comp.dtype, wl.dim, 4)
     off = C4Offload(mirror, slots=700)
     g = W.generator(98, 0, 0, DEV)
     hits = 0
@@ -41,6 +44,23 @@ def test_c4_offload_equals_device_pool(gpu_lib):
         # resident pages hold their mirror pages byte for byte (sampled)
         res = sorted(off.where.items())
         for (b, lb), s in res[::max(1, len(res) // 64)]:
-            assert torch.equal(off.data[s].cpu(), mirror.data[int(mirror.block_table[b, lb])]), (b, lb)
+            src = int(mirror.block_table[b, lb])
+            assert torch.equal(off.data[s].cpu(), mirror.data[src]), (b, lb)
+            if mirror.scale is not None:
+                assert torch.equal(off.scale[s].cpu(), mirror.scale[src]), (b, lb)
     assert off.one_launch   # the pinned mirror took the one-launch gather
     assert hits > 0   # later steps reuse resident pages
+
+
+def test_gather_pages_refuses_pageable_memory(gpu_lib):
+    """A host buffer that is not pinned has no device alias: the call fails on the host with
+    HYB_EINVAL and launches nothing."""
+    hyb = gpu_lib
+    src = torch.zeros(4, 64, 16)                       # pageable
+    dst = torch.zeros(4, 64, 16, device=DEV)
+    idx = torch.arange(4, dtype=torch.int32, device=DEV)
+    with pytest.raises(hyb.HybError) as e:
+        hyb.hyb_gather_pages(src, dst, idx, idx)
+    assert e.value.status == hyb.HYB_EINVAL
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dst) == 0
