@@ -188,7 +188,10 @@ int32_t hyb_swa_insert(const void* x, int32_t x_dtype, const int32_t* cu_seqlens
  *   src_host  pinned host memory (hipHostMalloc, or a pinned torch tensor); the kernel reads it
  *             through the device alias hipHostGetDevicePointer gives; HYB_EINVAL if it has none
  *   dst       device memory;  src_page, dst_page int32 [n] in device memory;  page_bytes % 16 == 0,
- *             src_host and dst 16-byte aligned. Destination pages must not repeat.
+ *             src_host and dst 16-byte aligned. Destination pages must not repeat. The indices
+ *             are device data the host cannot see: every src_page[j] must address a page inside
+ *             the pinned allocation and every dst_page[j] one inside dst (as with block tables,
+ *             the caller owns their validity).
  * ------------------------------------------------------------------------------------------ */
 int32_t hyb_gather_pages(const void* src_host, void* dst, const int32_t* src_page,
                          const int32_t* dst_page, int32_t n, int64_t page_bytes, void* stream);
