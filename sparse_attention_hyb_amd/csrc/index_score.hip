@@ -120,6 +120,57 @@ __device__ __forceinline__ void finish_parts(const ScoreArgs& a, int i, int part
   for (int j = t; j < nk; j += 256) pairs[j] = lsorted[j];
 }
 
+// The hand-off of one part for one query by one wave (no workgroup barrier): the wave's 16-bit
+// packed histogram of the part's keys becomes the cumulative histogram (written out) and bucket
+// cursors (written back), then every key is scattered to its bucket in the output pairs. Lane l
+// owns bins 1023 - 16 l - e (e < 16), i.e. bins in descending order across lanes.
+__device__ __forceinline__ void finish_part_wave(const ScoreArgs& a, int i, int part, int base,
+                                                 int end, const uint32_t* lkeys, uint32_t* lhist,
+                                                 int lane) {
+  uint32_t c[16], tot = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int bin = kTopBins - 1 - 16 * lane - e;
+    c[e] = (lhist[bin >> 1] >> (16 * (bin & 1))) & 0xffffu;
+    tot += c[e];
+  }
+  const uint32_t incl = wave_inclusive_scan(tot);
+  uint32_t run = incl - tot;
+  uint32_t cur[16], cum[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    cur[e] = run;
+    run += c[e];
+    cum[e] = run;
+  }
+  // bins 1008 - 16l .. 1023 - 16l: ascending in memory, bin 1023 - 16l - e holds cum[e]
+  u32x4 w0, w1;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    w0[m] = cum[15 - 2 * m] | (cum[14 - 2 * m] << 16);
+    w1[m] = cum[7 - 2 * m] | (cum[6 - 2 * m] << 16);
+  }
+  uint16_t* ph = a.part_hist + ((int64_t)i * a.part_ld + part) * kTopBins + (kTopBins - 16 - 16 * lane);
+  *reinterpret_cast<u32x4*>(ph) = w0;
+  *reinterpret_cast<u32x4*>(ph + 8) = w1;
+#pragma unroll
+  for (int m = 0; m < 8; ++m)   // word 504 - 8l + m: bins 1008 - 16l + 2m (low), + 1 (high)
+    lhist[kTopBins / 2 - 8 - 8 * lane + m] = cur[15 - 2 * m] | (cur[14 - 2 * m] << 16);
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the cursors before any lane's atomics
+  __builtin_amdgcn_wave_barrier();
+  uint2* pairs = reinterpret_cast<uint2*>(a.scores) + (int64_t)i * (a.ld / 2) +
+                 (int64_t)part * kScorePartKeys;
+  const int nk = min(kScorePartKeys, end - base);
+  for (int j = lane; j < nk; j += 64) {
+    const uint32_t key = lkeys[j];
+    const uint32_t bin = key >> (32 - kTopBits);
+    const uint32_t sh = 16 * (bin & 1u);
+    const uint32_t slot = (atomicAdd(&lhist[bin >> 1], 1u << sh) >> sh) & 0xffffu;
+    pairs[slot] = make_uint2(key, (uint32_t)(base + j));
+  }
+}
+
 template <bool kFp4>
 __global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
   __shared__ uint32_t lhist[kScoreParts * kTopBins];   // one histogram per kScorePartKeys keys
@@ -590,15 +641,9 @@ __global__ __launch_bounds__(256, 3) void score_mfma_multi(ScoreArgs a) {
     }
     wait_vmcnt<0>();   // no load may still be writing a tile when the ring is reused
   }
-  if (a.part_hist) {
-    // the tiles are free now: the sorted pairs use them
-    for (int w = 0; w < kMQ; ++w) {
-      const int qi = blockIdx.y * kMQ + w;
-      const int e = min(gnv[w], base + kMKeys);
-      if (gseq[w] < 0 || base >= e) continue;   // uniform
-      finish_parts<kMParts, true>(a, qi, blockIdx.x * kMParts, base, e, lkeys[w], lhist[w],
-                                  reinterpret_cast<uint2*>(&stage[0][0]), wtot);
-    }
+  if (a.part_hist && has_q && base < end_w) {
+    // each wave hands off its own query's part (its keys and counts are its own LDS writes)
+    finish_part_wave(a, i, blockIdx.x, base, end_w, lkeys[wave], lhist[wave], lane);
   }
 }
 
