@@ -222,6 +222,16 @@ def test_c4_sparse_decode_full_size_sampled(gpu_lib):
     assert swaps <= 1
 
 
+@pytest.mark.parametrize("k", [1024, 2048])
+def test_c4_sparse_decode_large_k(gpu_lib, k):
+    """Top-1024 and top-2048 (the largest k) through the indexer, the selector and the sparse
+    attention (up to 2176 keys per query with the window), over L = 3000 (fewer visible entries
+    than k), 40000 and 131072."""
+    wl = W.sparse_decode(DEV, seed=8, batch=3, ctx=[3000, 40000, 131072], k=k)
+    swaps = check_sparse(gpu_lib, wl, range(3))
+    assert swaps <= 2
+
+
 def test_exact_arithmetic_topk_is_bit_exact(gpu_lib):
     """Dyadic indexer inputs make every fp32 partial sum exact in any order, so the GPU scores
     equal the oracle's exactly and the top-k sets (with their many ties) must be identical."""
@@ -294,6 +304,18 @@ def test_c128_dense_decode_small(gpu_lib):
     out = gpu_decode(gpu_lib, wl)
     sync()
     want = oracle_out(wl, to_oracle_pool(wl.swa), to_oracle_pool(wl.comp), range(6))
+    assert_abs_close(to_f64(out), want)
+
+
+def test_c128_dense_decode_two_resolution_segments(gpu_lib):
+    """One sequence of 2^24 + 2^17 tokens: 132096 visible C128 entries + the window are more keys
+    than 64 splits of one 2048-key resolution segment hold, so every workgroup resolves and
+    streams its keys in two segments (the online softmax carried across them)."""
+    L = (1 << 24) + (1 << 17)
+    wl = W.dense_decode(DEV, seed=9, batch=1, ctx=[L])
+    out = gpu_decode(gpu_lib, wl)
+    sync()
+    want = oracle_out(wl, to_oracle_pool(wl.swa), to_oracle_pool(wl.comp), range(1))
     assert_abs_close(to_f64(out), want)
 
 
