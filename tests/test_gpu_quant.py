@@ -280,3 +280,56 @@ def test_q_norm_kv_insert(gpu_lib, qdt, kvdt, pdt, D, H, rd):
         assert np.all(np.abs(got - want) <= 4e-6 * (1.0 + np.abs(want)))
     else:
         assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-5)
+
+
+# ================================== prefill over fp8 caches built by quantise-on-insert
+def test_prefill_over_fp8_pools_built_from_raw_tokens(gpu_lib):
+    """One sequence: 1000 prior raw tokens then a 300-token chunk, its window, C4 and C128 entries
+    written into fp8 pools by the window insert and the compressors (quantised as stored), then C4
+    top-64 and C128 dense prefill attention over those pools. The oracle attends over exactly the
+    stored entries (decoded codes times scales) with the same selections."""
+    hyb = gpu_lib
+    from tests.parity_util import BF16_ABS
+    D, rd, H, T0, T1, k = 512, 64, 64, 1000, 300, 64
+    T = T0 + T1
+    g = W.generator(99, 0, 0, DEV)
+    x = W.to_storage(W.randn((T, D), g, DEV), "bf16")
+    lg = W.randn((T,), g, DEV)
+    q = W.to_storage(W.randn((T1, H, D), g, DEV), "bf16")
+    iq = W.to_storage(W.randn((T1, 64, 128), g, DEV), "bf16")
+    iw = W.randn((T1, 64), g, DEV) / 128 ** 0.5
+    mb = -(-T // 256)
+    swa = W.make_pool("fp8", D, 1, [W.blocks_for_positions(0, T)], mb, g, DEV, fill=False)
+    c4 = W.make_pool("fp8", D, 4, [W.blocks_for_entries(T // 4, 4)], mb, g, DEV, fill=False)
+    c128 = W.make_pool("fp8", D, 128, [W.blocks_for_entries(T // 128, 128)], mb, g, DEV, fill=False)
+    ip = W.make_pool("bf16", 128, 4, [W.blocks_for_entries(T // 4, 4)], mb, g, DEV)
+    s4 = torch.zeros(1, 4, D, dtype=x.dtype, device=DEV)
+    s128 = torch.zeros(1, 128, D, dtype=x.dtype, device=DEV)
+    l128 = torch.zeros(1, 128, device=DEV)
+    for a, e in ((0, T0), (T0, T)):
+        cu, st = ints([0, e - a]), ints([a])
+        hyb.hyb_swa_insert(x[a:e], cu, st, e - a, swa, rd)
+        hyb.hyb_compress(x[a:e], cu, st, e - a, s4, c4, rd, eps=1e-6)
+        hyb.hyb_compress(x[a:e], cu, st, e - a, s128, c128, rd, eps=1e-6, gate_logits=lg[a:e],
+                         state_logits=l128)
+    pos = torch.arange(T0, T, dtype=I32, device=DEV)
+    qseq = torch.zeros(T1, dtype=I32, device=DEV)
+    topk = torch.empty(T1, k, dtype=I32, device=DEV)
+    hyb.hyb_index_topk(iq, iw, pos, T - 1, ip, k, topk, q_seq=qseq)
+    out4, out128 = torch.empty_like(q), torch.empty_like(q)
+    hyb.hyb_attn_prefill(q, pos, T - 1, swa, c4, out4, topk_idx=topk, k=k, q_seq=qseq)
+    hyb.hyb_attn_prefill(q, pos, T - 1, swa, c128, out128, q_seq=qseq)
+    torch.cuda.synchronize()
+    sw, p4, p128 = to_oracle_pool(swa), to_oracle_pool(c4), to_oracle_pool(c128)
+    # the stored entries are the quantised oracle entries (checked against the float64 entries)
+    ref4 = O.compress_stream(to_f64(x), None, 4, "mean", rd, 1e4, 1e-6)
+    got4 = O.pool_entries(p4, 0, range(T // 4))
+    assert np.all(np.abs(got4 - ref4) <= 0.5 * e4m3_step(ref4 / (np.abs(ref4).max(1, keepdims=True) / 448))
+                  * (np.abs(ref4).max(1, keepdims=True) / 448) * 1.001 + 2e-5)
+    qq, tk = to_f64(q), topk.cpu().numpy()
+    for i in (0, 1, 57, 128, 200, 299):
+        p = T0 + i
+        want4 = O.hybrid_query(qq[i], p, 0, sw, p4, 128, D ** -0.5, rd, 1e4, tk[i])
+        want128 = O.hybrid_query(qq[i], p, 0, sw, p128, 128, D ** -0.5, rd, 1e4, None)
+        assert np.abs(to_f64(out4)[i] - want4).max() <= BF16_ABS, i
+        assert np.abs(to_f64(out128)[i] - want128).max() <= BF16_ABS, i
