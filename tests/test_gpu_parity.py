@@ -623,7 +623,7 @@ def _clone_pool(p):
 
 
 _FUSED_CASES = ["c4_bf16", "c128_gate_bf16", "c4_f32x", "c4_unaligned_x", "c4_fp8out",
-                "c128_gate_fp8out"]
+                "c128_gate_fp8out", "c4_fp8pool", "c128_gate_fp8pool"]
 
 
 @pytest.mark.parametrize("case", _FUSED_CASES)
@@ -631,18 +631,21 @@ def test_attn_decode_compress_equals_two_calls(gpu_lib, case):
     """hyb_attn_decode_compress leaves exactly what hyb_attn_decode then hyb_compress leave: the
     attention output (bf16 rows, or fp8 rows and their scales), every pool byte, the state ring
     and its logits. The compressor runs beside the combine (bf16 / f32 x) or after it (x not
-    16-byte aligned); sequences complete a group or only extend the ring."""
+    16-byte aligned, or the pools are fp8 and the compressor quantises as it stores); sequences
+    complete a group or only extend the ring."""
     hyb = gpu_lib
     g = W.generator(91, _FUSED_CASES.index(case), 0, DEV)
     fp8 = case.endswith("fp8out")
     if case.startswith("c4"):
         lens = [4096, 4097, 4098, 4099, 131072, 9000]
-        wl = W.sparse_decode(DEV, seed=5, batch=len(lens), ctx=lens)
+        wl = W.sparse_decode(DEV, seed=5, batch=len(lens), ctx=lens,
+                             dtype="fp8" if case.endswith("fp8pool") else "bf16")
         topk = gpu_topk(hyb, wl)
         r, gate = 4, False
     else:
         lens = [2048, 5000, 65536, 131072]
-        wl = W.dense_decode(DEV, seed=5, batch=len(lens), ctx=lens)
+        wl = W.dense_decode(DEV, seed=5, batch=len(lens), ctx=lens,
+                            dtype="fp8" if case.endswith("fp8pool") else "bf16")
         topk, r, gate = None, 128, True
     B, D = wl.batch, wl.dim
     x = W.randn((B, D), g, DEV)
@@ -674,10 +677,12 @@ def test_attn_decode_compress_equals_two_calls(gpu_lib, case):
             hyb.hyb_attn_decode(wl.q, wl.seq_lens, wl.max_seq_len, swa, comp, out, **kw)
             hyb.hyb_compress(x_use, cu, start, 1, stt, comp, wl.rope_dim, wl.rope_base, eps=1e-6,
                              gate_logits=gl, state_logits=stl)
-        runs.append((out, comp.data, stt, stl, sc))
+        runs.append((out, comp.data, stt, stl, sc, comp.scale))
     sync()
-    (o0, c0, s0, l0, q0), (o1, c1, s1, l1, q1) = runs
+    (o0, c0, s0, l0, q0, e0), (o1, c1, s1, l1, q1, e1) = runs
     assert torch.equal(o0, o1)
+    if e0 is not None:
+        assert torch.equal(e0, e1)
     if fp8:
         assert torch.equal(q0, q1)
     assert torch.equal(c0, c1)
