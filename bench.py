@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8, help="cache replicas cycled per step (C4)")
     ap.add_argument("--no-c128", action="store_true", help="skip the 1M-context C128 layer")
     ap.add_argument("--all", action="store_true", help="also time chunked prefill and the quantised mixed batch")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the chunked-prefill step and print its figures (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -573,6 +575,10 @@ def main():
         del src, dst
         log("copy calibration: 3 x 1 GiB device copies done")
 
+    if args.prefill_only:
+        r = prefill(torch, hyb, W, BM, args)
+        print(json.dumps({"workload": "chunked_prefill", **r}), flush=True)
+        return
     log("C4 sparse decode: building 8 replicas")
     res, rep0 = c4_sparse(torch, hyb, W, BM, args)
     log(f"C4 sparse decode: {res['value']:.0f} q-tok/s, {res['ms_per_step'] * 1e3:.1f} us/step, "
