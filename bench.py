@@ -1,20 +1,24 @@
 #!/usr/bin/env python3
 """Decode benchmark of the hybrid C4/C128 + sliding-window attention step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--only c4|c128|prefill|quant|probe]
 
 A step is one pass of the whole decode path over one batch:
   C4 layer (headline, 16 sequences x 131072 tokens): indexer scores over every visible C4 entry,
   top-512, sparse attention over the 128-token window plus the selected entries, combine +
   inverse RoPE, and the compression of the new token into the C4 pool (its workgroups run beside
-  the combine: the entry it completes is not visible to the step's own query).
-  C128 layer (32 sequences x 2^20 tokens, pool built by compressing raw tokens with softmax gates):
-  dense attention over the window plus every visible C128 entry, and the new token's compression
-  (beside the combine, as above).
-Inputs are resident in HBM; R replicas of every cache are cycled so the 256 MiB Infinity Cache
-cannot hold a step's working set. Prints one JSON line (rank 0) with the headline metric, the
-roofline of the dominant kernel (indexer scores, timed with HIP events on its stream inside the
-timed region, on every tenth step) and the float64 oracle timed on the host on a bounded sample.
+  the combine: the entry it completes is not visible to the step's own query) and of its
+  indexer-key row into the indexer-key pool.
+Also on every run, each with its own roofline: the C128 layer (32 sequences x 2^20 tokens, pool
+built by compressing raw tokens with softmax gates: dense attention over the window plus every
+visible C128 entry, and the new token's compression), the chunked prefill (65536 + 4096 tokens,
+MFMA roofline) and the quantised mixed-length batch (fp8 caches, fp4 indexer keys), and the HBM
+probe's best streaming read (the measured peak beside the published 8 TB/s).
+Inputs are resident in HBM; replicas of every cache are cycled so the 256 MiB Infinity Cache
+cannot hold a step's working set. Each kernel on the roofline is timed in its own loop of at
+least 50 back-to-back launches with HIP events on its stream. Prints one JSON line with the
+headline metric, the roofline of the dominant kernel (indexer scores) and the float64 oracle
+timed on the host on a bounded sample.
 """
 
 from __future__ import annotations
@@ -64,10 +68,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=8, help="cache replicas cycled per step (C4)")
-    ap.add_argument("--no-c128", action="store_true", help="skip the 1M-context C128 layer")
-    ap.add_argument("--all", action="store_true", help="also time chunked prefill and the quantised mixed batch")
-    ap.add_argument("--prefill-only", action="store_true",
-                    help="time only the chunked-prefill step and print its figures (for profiling)")
+    ap.add_argument("--kernel-launches", type=int, default=64,
+                    help="back-to-back launches per kernel timing loop (at least 50)")
+    ap.add_argument("--only", choices=["c4", "c128", "prefill", "quant", "probe"], default=None,
+                    help="time one workload only and print its figures (for profiling runs)")
+    ap.add_argument("--all", action="store_true",
+                    help="also the graph replay, multi-query decode, two-stream step, offload and fused neighbour steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -76,30 +82,71 @@ def parse():
 
 
 # ------------------------------------------------------------------------------------------
-EVENT_EVERY = 10   # steps between two event-timed launches of the dominant kernel
-
-
-def time_loop(torch, step, n_steps, warmup, n_rep, events=None):
-    """Runs warm-up steps, then times n_steps steps. Every EVENT_EVERY-th step brackets the
-    dominant kernel with a pair from `events` (recording events around every launch would add
-    several microseconds of queue work to every step)."""
+def time_loop(torch, step, n_steps, warmup, n_rep):
+    """Runs warm-up steps, then times n_steps steps (cycling n_rep replicas) between two device
+    synchronisations. Returns seconds."""
     for i in range(warmup):
-        step(i % n_rep, None)
+        step(i % n_rep)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(n_steps):
-        ev = events[i // EVENT_EVERY] if events and i % EVENT_EVERY == 0 else None
-        step(i % n_rep, ev)
+        step(i % n_rep)
     torch.cuda.synchronize()
     return time.perf_counter() - t0
 
 
-def timing_events(torch, n_steps):
-    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range((n_steps + EVENT_EVERY - 1) // EVENT_EVERY)]
+def kernel_loop(torch, launch, n, n_rep):
+    """Average duration in microseconds of one call, from HIP events on the current stream around
+    n back-to-back calls cycling n_rep replicas (three untimed calls first). Back-to-back calls
+    include the short gap between two launches, so this errs high against a kernel trace."""
+    n = max(50, n)
+    for i in range(3):
+        launch(i % n_rep)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        launch(i % n_rep)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
 
 
-def c4_sparse(torch, hyb, W, BM, args):
+def roofline_hbm(kernel, nbytes, us, peak_meas, traffic=None, **more):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    d = {"kernel": kernel, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "avg_launch_us": us,
+         "bytes_per_launch": nbytes}
+    if peak_meas:
+        d["measured_peak"] = peak_meas
+        d["frac_of_measured_peak"] = gbs / peak_meas
+    d.update(more)
+    return d
+
+
+def hbm_probe(torch, hyb):
+    """The best streaming-read rate of plain HIP kernels (include/hyb_probe.h) over a 2 GiB buffer
+    (eight times the Infinity Cache), ten launches per shape: the measured peak beside 8 TB/s."""
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    buf.view(torch.int32).fill_(7)
+    best, rates = 0.0, {}
+    for unroll, nwg in ((16, 256), (8, 512), (8, 1024), (16, 1024)):
+        us = kernel_loop(torch, lambda r: hyb.hyb_probe(hyb.PROBE_READ, buf, nwg, unroll=unroll), 10, 1)
+        gbs = (2 << 30) / (us * 1e-6) / 1e9
+        rates[f"read_u{unroll}_wg{nwg}"] = gbs
+        best = max(best, gbs)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    us = kernel_loop(torch, lambda r: hyb.hyb_probe(hyb.PROBE_COPY, buf[:1 << 30], 1024, unroll=8, dst=dst), 10, 1)
+    rates["copy_u8_wg1024 (read + write)"] = (2 << 30) / (us * 1e-6) / 1e9
+    del buf, dst
+    torch.cuda.empty_cache()
+    return best, rates
+
+
+def c4_sparse(torch, hyb, W, BM, args, peak_meas):
+    """The headline step: indexer scores + top-512 + sparse attention + combine/inverse RoPE, and
+    the new token compressed into the C4 pool (beside the combine) and its indexer-key row into
+    the indexer-key pool."""
     B, L, R = 16, 131072, max(1, args.replicas)
     dev = "cuda"
     reps = []
@@ -119,26 +166,55 @@ def c4_sparse(torch, hyb, W, BM, args):
             cu=torch.arange(0, B + 1, dtype=torch.int32, device=dev),
             start=torch.full((B,), L - 1, dtype=torch.int32, device=dev),
             state=W.to_storage(W.randn((B, 4, 512), g, dev), "bf16"),   # ring in x's dtype
+            ix_new=W.to_storage(W.randn((B, 128), g, dev), "bf16"),
+            istate=W.to_storage(W.randn((B, 4, 128), g, dev), "bf16"),
         ))
 
-    def step(r, ev):
+    def score(r):
         d = reps[r]
         wl = d["wl"]
-        # hyb_index_topk in its two halves, so that the indexer kernel can be timed on its own
-        if ev:
-            ev[0].record()
         hyb.hyb_index_score_keys(wl.idx_q, wl.idx_w, d["qpos"], L - 1, wl.idx_pool, d["keys"], d["hist"])
-        if ev:
-            ev[1].record()
-        hyb.hyb_topk_keys(d["keys"], d["hist"], d["qpos"], L - 1, wl.k, d["topk"])
+
+    def select(r):
+        d = reps[r]
+        hyb.hyb_topk_keys(d["keys"], d["hist"], d["qpos"], L - 1, d["wl"].k, d["topk"])
+
+    def attend(r):
+        d = reps[r]
+        wl = d["wl"]
         hyb.hyb_attn_decode_compress(wl.q, wl.seq_lens, L, wl.swa, wl.comp, d["out"], d["x_new"],
                                      d["cu"], d["start"], 1, d["state"], wl.comp,
                                      topk_idx=d["topk"], k=wl.k, workspace=d["ws"])
 
-    events = timing_events(torch, args.steps)
-    secs = time_loop(torch, step, args.steps, args.warmup, R, events)
-    score_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
-    graph = None
+    def idx_compress(r):
+        d = reps[r]
+        hyb.hyb_compress(d["ix_new"], d["cu"], d["start"], 1, d["istate"], d["wl"].idx_pool, 64)
+
+    def step(r):
+        score(r)
+        select(r)
+        attend(r)
+        idx_compress(r)
+
+    secs = time_loop(torch, step, args.steps, args.warmup, R)
+    n = args.kernel_launches
+    parts_us = {"index_score": kernel_loop(torch, score, n, R), "topk": kernel_loop(torch, select, n, R),
+                "attention_combine_compress": kernel_loop(torch, attend, n, R),
+                "indexer_key_compress": kernel_loop(torch, idx_compress, n, R)}
+    per_tok = BM.decode_query_bytes(L, ratio=4, sparse=True)
+    comp_b = BM.compress_decode_bytes(4) + BM.compress_decode_bytes(4, dim=128)
+    step_bytes = B * (per_tok.total + comp_b)
+    ms = secs * 1e3 / args.steps
+    score_bytes = B * BM.index_score_bytes(L)
+    res = dict(
+        value=B * args.steps / secs, ms_per_step=ms, step_bytes=step_bytes,
+        hbm_frac_step=step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        kernel_us=parts_us,
+        roofline=roofline_hbm("score_mfma_dma (indexer scores + top-k hand-off)", score_bytes,
+                              parts_us["index_score"], peak_meas, measured_traffic(),
+                              handoff_bytes_per_launch=B * BM.handoff_bytes(L),
+                              launches_timed=max(50, n)),
+    )
     if args.all:
         # the same step captured once per replica in a HIP graph and replayed (no call allocates,
         # clears memory or synchronises, so the captured step is the eager one)
@@ -147,28 +223,17 @@ def c4_sparse(torch, hyb, W, BM, args):
             gr = torch.cuda.CUDAGraph()
             torch.cuda.synchronize()
             with torch.cuda.graph(gr):
-                step(r, None)
+                step(r)
             graphs.append(gr)
         torch.cuda.synchronize()
-        gsecs = time_loop(torch, lambda r, ev: graphs[r].replay(), args.steps, args.warmup, R)
-        graph = dict(value=B * args.steps / gsecs, unit="query-tokens/s",
-                     ms_per_step=gsecs * 1e3 / args.steps, steps=args.steps,
-                     config={"workload": "c4_sparse_decode", "replay": "one HIP graph per step"})
-    per_tok = BM.decode_query_bytes(L, ratio=4, sparse=True)
-    comp_b = BM.compress_decode_bytes(4)
-    step_bytes = B * (per_tok.total + comp_b)
-    score_bytes = B * BM.index_score_bytes(L, handoff=True)
-    ms = secs * 1e3 / args.steps
-    res = dict(
-        value=B * args.steps / secs, ms_per_step=ms, step_bytes=step_bytes,
-        hbm_frac_step=step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-        score_kernel_ms=score_ms, score_bytes=score_bytes,
-        score_gbs=score_bytes / (score_ms * 1e-3) / 1e9, graph=graph,
-    )
+        gsecs = time_loop(torch, lambda r: graphs[r].replay(), args.steps, args.warmup, R)
+        res["graph"] = dict(value=B * args.steps / gsecs, unit="query-tokens/s",
+                            ms_per_step=gsecs * 1e3 / args.steps, steps=args.steps,
+                            config={"workload": "c4_sparse_decode", "replay": "one HIP graph per step"})
     return res, reps[0]
 
 
-def c128_dense(torch, hyb, W, BM, args):
+def c128_dense(torch, hyb, W, BM, args, peak_meas):
     B, L, D = 32, 1 << 20, 512
     R = 4
     dev = "cuda"
@@ -203,30 +268,25 @@ def c128_dense(torch, hyb, W, BM, args):
                   cu=torch.arange(0, B + 1, dtype=torch.int32, device=dev),
                   start=torch.full((B,), L - 1, dtype=torch.int32, device=dev)) for w in reps]
 
-    def step(r, ev):
+    def step(r):
         w, e = reps[r], extra[r]
-        if ev:
-            ev[0].record()
         hyb.hyb_attn_decode_compress(w.q, w.seq_lens, L, w.swa, w.comp, e["out"], e["x_new"],
                                      e["cu"], e["start"], 1, e["state"], w.comp,
                                      gate_logits=e["lg_new"], state_logits=e["st_l"],
                                      workspace=e["ws"])
-        if ev:
-            ev[1].record()
 
     n = max(args.steps // 2, 20)
-    events = timing_events(torch, n)
-    secs = time_loop(torch, step, n, max(args.warmup // 2, 5), R, events)
-    attn_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
+    secs = time_loop(torch, step, n, max(args.warmup // 2, 5), R)
+    call_us = kernel_loop(torch, step, args.kernel_launches, R)
     per_tok = BM.decode_query_bytes(L, ratio=128, sparse=False)
-    step_bytes = B * (per_tok.total + BM.compress_decode_bytes(128))
+    step_bytes = B * (per_tok.total + BM.compress_decode_bytes(128, gate=True))
     ms = secs * 1e3 / n
     return dict(
         value=B * n / secs, unit="query-tokens/s", ms_per_step=ms, steps=n,
         hbm_frac_step=step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-        # the attention call carries the compressor: its time and bytes include it
-        attn_compress_ms=attn_ms, attn_compress_gbs=step_bytes / (attn_ms * 1e-3) / 1e9,
-        attn_tflops=B * BM.attention_flops(8191 + 128) / (attn_ms * 1e-3) / 1e12,
+        roofline=roofline_hbm("attention call (attn_mfma, then the combine with the compressor)",
+                              step_bytes, call_us, peak_meas, None,
+                              attn_tflops=B * BM.attention_flops(8191 + 128) / (call_us * 1e-6) / 1e12),
         compress_raw_gbs=raw_bytes / comp_secs / 1e9,
         config={"workload": "c128_dense_decode", "batch": B, "context": L, "heads": 64, "dim": D,
                 "window": 128, "replicas": R, "pool": "bf16, built by softmax-gate compression of raw tokens"},
@@ -270,11 +330,15 @@ def prefill(torch, hyb, W, BM, args):
         for j in range(3):
             t[j] += ev[j].elapsed_time(ev[j + 1]) / reps
     fi, fa = BM.prefill_flops(range(wl.prior, wl.prior + n))
+    tflops = (fi + fa) / ((t[1] + t[2]) * 1e-3) / 1e12
     return dict(
-        ms_total=sum(t), ms_compress_insert=t[0], ms_index_topk=t[1], ms_attention=t[2],
+        value=n / (sum(t) * 1e-3), unit="query-tokens/s", ms_per_step=sum(t),
+        ms_compress_insert=t[0], ms_index_topk=t[1], ms_attention=t[2],
         indexer_tflops=fi / (t[1] * 1e-3) / 1e12, attention_tflops=fa / (t[2] * 1e-3) / 1e12,
-        mfma_frac=(fi + fa) / ((t[1] + t[2]) * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
-        query_tokens_per_s=n / (sum(t) * 1e-3),
+        roofline={"kernel": "indexer + top-512, then attention (MFMA)", "bound": "mfma",
+                  "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                  "flops_per_step": fi + fa, "avg_launch_us": (t[1] + t[2]) * 1e3},
         config={"workload": "chunked_prefill", "prior": wl.prior, "chunk": n, "heads": 64, "dim": D, "topk": wl.k},
     )
 
@@ -296,7 +360,7 @@ def multi_decode(torch, hyb, W, BM, args):
             start=torch.full((B,), L - T, dtype=torch.int32, device=dev),
             state=torch.zeros(B, 4, 512, dtype=wl.x_new.dtype, device=dev)))
 
-    def step(r, ev):
+    def step(r):
         d = reps[r]
         wl = d["wl"]
         hyb.hyb_index_topk(wl.idx_q, wl.idx_w, wl.q_pos, L - 1, wl.idx_pool, wl.k, d["topk"],
@@ -306,7 +370,7 @@ def multi_decode(torch, hyb, W, BM, args):
         hyb.hyb_compress(wl.x_new, d["cu"], d["start"], T, d["state"], wl.comp, 64)
 
     n = max(args.steps // 2, 20)
-    secs = time_loop(torch, step, n, max(args.warmup // 2, 5), R, None)
+    secs = time_loop(torch, step, n, max(args.warmup // 2, 5), R)
     ms = secs * 1e3 / n
     per_tok = BM.decode_query_bytes(L, ratio=4, sparse=True)
     return dict(
@@ -341,13 +405,13 @@ def neighbour_steps(torch, hyb, W, BM, args, rep):
     with torch.cuda.graph(gr):
         for _ in range(per_graph):
             hyb.hyb_q_norm_kv_insert(q_raw, kv, cu, start, 1, wl.swa, q_out=q_out)
-    prep_s = time_loop(torch, lambda r, ev: gr.replay(), n // per_graph + 1, 3, 1)
+    prep_s = time_loop(torch, lambda r: gr.replay(), n // per_graph + 1, 3, 1)
     prep_s /= per_graph * (n // per_graph + 1) / n
     codes = torch.empty(wl.q.shape, dtype=torch.uint8, device=dev)
     scales = torch.empty(wl.q.shape[:2], dtype=torch.float32, device=dev)
 
     def attn(fp8):
-        def step(r, ev):
+        def step(r):
             hyb.hyb_attn_decode_compress(wl.q, wl.seq_lens, L, wl.swa, wl.comp,
                                          codes if fp8 else rep["out"], rep["x_new"], rep["cu"],
                                          rep["start"], 1, rep["state"], wl.comp,
@@ -388,18 +452,20 @@ def full_step(torch, hyb, W, BM, args):
             max_seq_len=L, idx_q=wl.idx_q, idx_w=wl.idx_w, idx_pool=wl.idx_pool,
             keys=torch.empty(kshape, dtype=torch.int32, device=dev),
             hist=torch.empty(hshape, dtype=torch.int16, device=dev),
-            topk=torch.empty(B, wl.k, dtype=torch.int32, device=dev), k=wl.k)
+            topk=torch.empty(B, wl.k, dtype=torch.int32, device=dev), k=wl.k,
+            idx_kv_new=W.to_storage(W.randn((B, 128), g, dev), "bf16"),
+            idx_state=W.to_storage(W.randn((B, 4, 128), g, dev), "bf16"))
         steps.append(DecodeStep(buf, side))
     n = args.steps
-    serial = time_loop(torch, lambda r, ev: steps[r].run_serial(), n, args.warmup, R)
-    two = time_loop(torch, lambda r, ev: steps[r].run(), n, args.warmup, R)
+    serial = time_loop(torch, lambda r: steps[r].run_serial(), n, args.warmup, R)
+    two = time_loop(torch, lambda r: steps[r].run(), n, args.warmup, R)
     graphs = [s.capture() for s in steps]
-    gr = time_loop(torch, lambda r, ev: graphs[r].replay(), n, args.warmup, R)
+    gr = time_loop(torch, lambda r: graphs[r].replay(), n, args.warmup, R)
     us = lambda t: t * 1e6 / n
     return dict(value=B * n / two, unit="query-tokens/s", serial_us=us(serial),
                 two_stream_us=us(two), two_stream_graph_us=us(gr), steps=n,
                 config={"workload": "c4_sparse_decode + query prep", "batch": B, "context": L,
-                        "replicas": R, "step": "q RMSNorm+RoPE and window insert (side stream) | "
+                        "replicas": R, "step": "q RMSNorm+RoPE, window insert and indexer-key compression (side stream) | "
                         "indexer + top-512 (main), then attention + combine with compression"})
 
 
@@ -459,55 +525,58 @@ def offload_decode(torch, hyb, W, BM, args):
                                  "locality": "indexer queries = first step's + N(0, 0.3^2)"})
 
 
-def quant_mixed(torch, hyb, W, BM, args):
+def quant_mixed(torch, hyb, W, BM, args, peak_meas):
+    """64 sequences of log-uniform lengths (one draw, seed 0), fp8 attention caches and fp4
+    indexer keys; a C4-layer step (indexer + top-512 + attention) and a C128-layer step
+    (attention), each timed over 3 replicas of every cache (same lengths, other draws and
+    addresses), so that the Infinity Cache does not hold a step's working set."""
     dev = "cuda"
-    c4, c128 = W.quantized_mixed(dev, seed=0)
-    B = c4.batch
-    lens = c4.seq_lens_host
-    max_len = max(lens)
-    topk = torch.empty(B, c4.k, dtype=torch.int32, device=dev)
-    o4, o128 = torch.empty_like(c4.q), torch.empty_like(c128.q)
-    qpos = (c4.seq_lens - 1).contiguous()
-    ws_i = torch.empty(hyb.hyb_index_topk_workspace_bytes(B, max_len - 1, 128, 4), dtype=torch.uint8, device=dev)
-    ws4 = torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, max_len, 4, c4.k), dtype=torch.uint8, device=dev)
-    ws128 = torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, max_len, 128, 0), dtype=torch.uint8, device=dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    R = 3
+    c4_0, c128_0 = W.quantized_mixed(dev, seed=0)
+    lens = c4_0.seq_lens_host
+    B, max_len = c4_0.batch, max(lens)
+    reps = [(c4_0, c128_0)] + [W.quantized_mixed(dev, seed=r, lens=lens) for r in range(1, R)]
+    bufs = []
+    for c4, c128 in reps:
+        bufs.append(dict(
+            topk=torch.empty(B, c4.k, dtype=torch.int32, device=dev),
+            o4=torch.empty_like(c4.q), o128=torch.empty_like(c128.q),
+            qpos=(c4.seq_lens - 1).contiguous(),
+            ws_i=torch.empty(hyb.hyb_index_topk_workspace_bytes(B, max_len - 1, 128, 4), dtype=torch.uint8, device=dev),
+            ws4=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, max_len, 4, c4.k), dtype=torch.uint8, device=dev),
+            ws128=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, max_len, 128, 0), dtype=torch.uint8, device=dev)))
 
-    def step():
-        ev[0].record()
-        hyb.hyb_index_topk(c4.idx_q, c4.idx_w, qpos, max_len - 1, c4.idx_pool, c4.k, topk, workspace=ws_i)
-        hyb.hyb_attn_decode(c4.q, c4.seq_lens, max_len, c4.swa, c4.comp, o4, topk_idx=topk, k=c4.k, workspace=ws4)
-        ev[1].record()
-        hyb.hyb_attn_decode(c128.q, c128.seq_lens, max_len, c128.swa, c128.comp, o128, workspace=ws128)
-        ev[2].record()
+    def step4(r):
+        (c4, _), d = reps[r], bufs[r]
+        hyb.hyb_index_topk(c4.idx_q, c4.idx_w, d["qpos"], max_len - 1, c4.idx_pool, c4.k, d["topk"], workspace=d["ws_i"])
+        hyb.hyb_attn_decode(c4.q, c4.seq_lens, max_len, c4.swa, c4.comp, d["o4"], topk_idx=d["topk"], k=c4.k, workspace=d["ws4"])
 
-    for _ in range(3):
-        step()
-    torch.cuda.synchronize()
-    reps = 10
-    t4 = t128 = 0.0
-    for _ in range(reps):
-        step()
-        torch.cuda.synchronize()
-        t4 += ev[0].elapsed_time(ev[1]) / reps
-        t128 += ev[1].elapsed_time(ev[2]) / reps
+    def step128(r):
+        (_, c128), d = reps[r], bufs[r]
+        hyb.hyb_attn_decode(c128.q, c128.seq_lens, max_len, c128.swa, c128.comp, d["o128"], workspace=d["ws128"])
+
+    n = max(args.steps // 4, 30)
+    t4 = time_loop(torch, step4, n, 6, R) * 1e3 / n
+    t128 = time_loop(torch, step128, n, 6, R) * 1e3 / n
     b4 = sum(BM.decode_query_bytes(L, ratio=4, sparse=True, dtype="fp8", idx_dtype="fp4").total for L in lens)
     b128 = sum(BM.decode_query_bytes(L, ratio=128, sparse=False, dtype="fp8").total for L in lens)
     return dict(
-        c4_ms=t4, c4_query_tokens_per_s=B / (t4 * 1e-3), c4_hbm_frac=b4 / (t4 * 1e-3) / (HBM_PEAK_GBS * 1e9),
-        c128_ms=t128, c128_query_tokens_per_s=B / (t128 * 1e-3),
-        c128_hbm_frac=b128 / (t128 * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        value=B / (t4 * 1e-3), unit="query-tokens/s (C4 layer)", ms_per_step=t4,
+        c128_value=B / (t128 * 1e-3), c128_ms_per_step=t128,
+        roofline=roofline_hbm("C4 layer step (indexer + top-512 + attention)", b4, t4 * 1e3, peak_meas),
+        c128_roofline=roofline_hbm("C128 layer step (attention)", b128, t128 * 1e3, peak_meas),
         config={"workload": "quantized_mixed_decode", "batch": B, "lengths": "log-uniform 4096..2^20 (seed 0)",
                 "mean_len": sum(lens) / B, "attn_cache": "fp8 e4m3 + fp32 scale per entry",
-                "indexer_cache": "fp4 e2m1 + e8m0 per 32"},
+                "indexer_cache": "fp4 e2m1 + e8m0 per 32", "replicas": R},
     )
 
 
 # ------------------------------------------------------------------------------------------
 def cpu_baseline(torch, W, BM, rep, budget):
     """The float64 oracle, as it stands, on the same C4 decode step (compress the new token,
-    indexer, top-k, attention), sequence by sequence, cycling over the batch until the time budget
-    is spent."""
+    indexer, top-k, attention), sequence by sequence, cycling over the batch. Three runs with the
+    host's BLAS threads (the best is the value) and one with a single thread, each a quarter of
+    the time budget."""
     import numpy as np
     import oracle as O
 
@@ -525,31 +594,53 @@ def cpu_baseline(torch, W, BM, rep, budget):
     x_new = rep["x_new"].cpu().double().numpy()
     state = rep["state"].float().cpu().double().numpy()
     scale = 1.0 / math.sqrt(wl.dim)
-    done = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget:   # passes over the batch until the budget is spent
-        b = done % wl.batch
-        L = wl.seq_lens_host[b]
-        p = L - 1
-        toks = np.concatenate([state[b, :3], x_new[b][None]])
-        O.compressed_entry(toks, None, p // 4, 4, "mean", 64, 1e4, 1e-6)
-        nv = O.n_visible(p, 4, 128)
-        sc = O.indexer_scores(iq[b], iw[b], O.pool_entries(ip, b, range(nv)))
-        sel = O.topk_select(sc, wl.k)
-        O.hybrid_query(q[b], p, b, swa, comp, 128, scale, 64, 1e4, sel)
-        done += 1
-    secs = time.perf_counter() - t0
+
+    def run(secs_budget):
+        done = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < secs_budget:   # passes over the batch until the budget is spent
+            b = done % wl.batch
+            L = wl.seq_lens_host[b]
+            p = L - 1
+            toks = np.concatenate([state[b, :3], x_new[b][None]])
+            O.compressed_entry(toks, None, p // 4, 4, "mean", 64, 1e4, 1e-6)
+            nv = O.n_visible(p, 4, 128)
+            sc = O.indexer_scores(iq[b], iw[b], O.pool_entries(ip, b, range(nv)))
+            sel = O.topk_select(sc, wl.k)
+            O.hybrid_query(q[b], p, b, swa, comp, 128, scale, 64, 1e4, sel)
+            done += 1
+        return done, time.perf_counter() - t0
+
     threads = os.cpu_count() or 1
+    limits = None
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         blas = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
         if blas:
             threads = max(blas)
+        limits = threadpool_limits
     except Exception:
         pass
-    return {"value": done / secs, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} query tokens of the C4 decode step (the batch's 16 sequences of "
-                      f"131072 tokens in turn, one at a time), {secs:.1f} s, numpy float64"}
+    model = "unknown"
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except Exception:
+        pass
+    runs = [run(budget / 4) for _ in range(3)]
+    best = max(d / t for d, t in runs)
+    one = None
+    if limits is not None:
+        with limits(limits=1, user_api="blas"):
+            d1, t1 = run(budget / 4)
+        one = d1 / t1
+    done = sum(d for d, _ in runs)
+    return {"value": best, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "one_thread_value": one, "cpu_model": model, "host_cpus": os.cpu_count(),
+            "runs": [d / t for d, t in runs],
+            "sample": f"best of 3 runs of {budget / 4:.0f} s ({done} query tokens of the C4 decode "
+                      f"step in all: the batch's 16 sequences of 131072 tokens in turn, one at a "
+                      f"time), numpy float64 with {threads} BLAS threads; one more run with one "
+                      f"thread"}
 
 
 def main():
@@ -575,26 +666,42 @@ def main():
         del src, dst
         log("copy calibration: 3 x 1 GiB device copies done")
 
-    if args.prefill_only:
-        r = prefill(torch, hyb, W, BM, args)
-        print(json.dumps({"workload": "chunked_prefill", **r}), flush=True)
+    only = args.only
+    peak = None
+    probe_rates = None
+    if only in (None, "probe"):
+        log("HBM probe")
+        peak, probe_rates = hbm_probe(torch, hyb)
+        log(f"HBM probe: best streaming read {peak:.0f} GB/s")
+        if only == "probe":
+            print(json.dumps({"workload": "hbm_probe", "measured_peak": peak, **probe_rates}), flush=True)
+            return
+    one_line = {"prefill": lambda: prefill(torch, hyb, W, BM, args),
+                "c128": lambda: c128_dense(torch, hyb, W, BM, args, peak),
+                "quant": lambda: quant_mixed(torch, hyb, W, BM, args, peak),
+                "c4": lambda: c4_sparse(torch, hyb, W, BM, args, peak)[0]}
+    if only is not None:
+        r = one_line[only]()
+        r.pop("graph", None)
+        print(json.dumps({"workload": only, **r}), flush=True)
         return
-    log("C4 sparse decode: building 8 replicas")
-    res, rep0 = c4_sparse(torch, hyb, W, BM, args)
+    log(f"C4 sparse decode: building {args.replicas} replicas")
+    res, rep0 = c4_sparse(torch, hyb, W, BM, args, peak)
     log(f"C4 sparse decode: {res['value']:.0f} q-tok/s, {res['ms_per_step'] * 1e3:.1f} us/step, "
-        f"score kernel {res['score_kernel_ms'] * 1e3:.1f} us = {res['score_gbs']:.0f} GB/s")
-    extra = {}
+        f"kernels (us) {json.dumps({k: round(v, 1) for k, v in res['kernel_us'].items()})}")
+    extra = {"hbm_probe": {"measured_peak": peak, "unit": "GB/s", **probe_rates}}
     if res.get("graph"):
-        extra["c4_sparse_decode_graph"] = res["graph"]
-    if not args.no_c128:
-        log("C128 dense decode: compressing 32 x 2^20 raw tokens, then timing")
-        extra["c128_dense_decode_1M"] = c128_dense(torch, hyb, W, BM, args)
-        log(f"C128: {extra['c128_dense_decode_1M']['value']:.0f} q-tok/s")
+        extra["c4_sparse_decode_graph"] = res.pop("graph")
+    log("C128 dense decode: compressing 32 x 2^20 raw tokens, then timing")
+    extra["c128_dense_decode_1M"] = c128_dense(torch, hyb, W, BM, args, peak)
+    log(f"C128: {extra['c128_dense_decode_1M']['value']:.0f} q-tok/s")
+    log("chunked prefill")
+    extra["chunked_prefill"] = prefill(torch, hyb, W, BM, args)
+    log(f"prefill: {extra['chunked_prefill']['ms_per_step']:.2f} ms per chunk")
+    log("quantised mixed decode")
+    extra["quantized_mixed_decode"] = quant_mixed(torch, hyb, W, BM, args, peak)
+    log(f"quantised mixed: C4 {extra['quantized_mixed_decode']['value']:.0f} q-tok/s")
     if args.all:
-        log("chunked prefill")
-        extra["chunked_prefill"] = prefill(torch, hyb, W, BM, args)
-        log("quantised mixed decode")
-        extra["quantized_mixed_decode"] = quant_mixed(torch, hyb, W, BM, args)
         log("multi-query decode")
         extra["multi_query_decode"] = multi_decode(torch, hyb, W, BM, args)
         log("full decode step with the query prep, one and two streams, graph")
@@ -623,15 +730,13 @@ def main():
         "config": {"workload": "c4_sparse_decode", "batch": 16, "context": 131072, "heads": 64,
                    "dim": 512, "rope_dims": 64, "indexer": "64 heads x 128, bf16", "topk": 512,
                    "window": 128, "replicas": args.replicas,
-                   "step": "indexer scores + top-512 + sparse attention + combine/inverse RoPE, new token compressed beside the combine"},
+                   "step": "indexer scores + top-512 + sparse attention + combine/inverse RoPE; the new "
+                           "token compressed into the C4 pool and its indexer-key row into the indexer-key pool"},
         "hbm_frac_step": res["hbm_frac_step"],
         "step_bytes": res["step_bytes"],
-        "roofline": {"kernel": "score_mfma_dma (indexer scores + top-k hand-off)", "bound": "hbm",
-                     "achieved": res["score_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": res["score_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "traffic_unit": "bytes per launch (FETCH_SIZE x 2 + WRITE_SIZE, copy-calibrated)",
-                     "avg_launch_us": res["score_kernel_ms"] * 1e3,
-                     "bytes_per_launch": res["score_bytes"]},
+        "kernel_us": res["kernel_us"],
+        "roofline": dict(res["roofline"], traffic_unit="bytes per launch (FETCH_SIZE x 2 + WRITE_SIZE, "
+                                                       "copy-calibrated); null when the kernel changed since"),
         "cpu_baseline": cpu,
         "extra": extra,
     }

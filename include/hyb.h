@@ -29,7 +29,9 @@
  *   - Positions are absolute, 0-based raw-token positions. A query at position p sees the
  *     raw window [max(0, p - window + 1), p] and the compressed entries 0 .. n_vis(p) - 1 with
  *     n_vis(p) = ceil(max(0, p - window + 1) / ratio) (every complete group that holds at least
- *     one position older than the window).
+ *     one position older than the window). Every entry point that takes a window and a ratio
+ *     requires window >= ratio (HYB_EINVAL otherwise): then every visible group is complete,
+ *     and the group a token at p completes is not yet visible at p.
  *   - RoPE rotates the last rope_dim dims in adjacent pairs: pair i = (D - rope_dim + 2i,
  *     D - rope_dim + 2i + 1) turns by pos * rope_base^(-2i / rope_dim). Angles are formed and
  *     reduced in double precision.
@@ -44,7 +46,7 @@
 extern "C" {
 #endif
 
-#define HYB_ABI_VERSION 2
+#define HYB_ABI_VERSION 3
 
 /* [vLLM] "vLLM side": one logical block = 256 native (raw) positions for every compression
  * rate, i.e. 256 raw entries, 64 C4 entries or 2 C128 entries. */
@@ -180,27 +182,30 @@ int32_t hyb_swa_insert(const void* x, int32_t x_dtype, const int32_t* cu_seqlens
  *          in hyb_swa_insert)
  * The query rows it writes are what hyb_attn_decode / hyb_attn_prefill take at these positions.
  * ------------------------------------------------------------------------------------------ */
-/* --------------------------------------------------------------------------------------------
- * hyb_gather_pages - fill pages of a device working set from a pinned host mirror in one launch
- * (the offload of [SGLang] "HiSparse": the C4 pool lives in CPU memory, missing pages are brought
- * to a device buffer every step). For j < n:
- *   dst + dst_page[j] * page_bytes  <-  src_host + src_page[j] * page_bytes   (page_bytes bytes)
- *   src_host  pinned host memory (hipHostMalloc, or a pinned torch tensor); the kernel reads it
- *             through the device alias hipHostGetDevicePointer gives; HYB_EINVAL if it has none
- *   dst       device memory;  src_page, dst_page int32 [n] in device memory;  page_bytes % 16 == 0,
- *             src_host and dst 16-byte aligned. Destination pages must not repeat. The indices
- *             are device data the host cannot see: every src_page[j] must address a page inside
- *             the pinned allocation and every dst_page[j] one inside dst (as with block tables,
- *             the caller owns their validity).
- * ------------------------------------------------------------------------------------------ */
-int32_t hyb_gather_pages(const void* src_host, void* dst, const int32_t* src_page,
-                         const int32_t* dst_page, int32_t n, int64_t page_bytes, void* stream);
-
 int32_t hyb_q_norm_kv_insert(const void* q, int32_t q_dtype, int32_t n_heads, const void* kv,
                              int32_t kv_dtype, const int32_t* cu_seqlens, const int32_t* start_pos,
                              int32_t batch, int32_t max_new_tokens, void* q_out,
                              const hyb_paged* swa, int32_t rope_dim, double rope_base, float eps,
                              void* stream);
+
+/* --------------------------------------------------------------------------------------------
+ * hyb_gather_pages - fill pages of a device working set from a pinned host mirror in one launch
+ * (the offload of [SGLang] "HiSparse": the C4 pool lives in CPU memory, missing pages are brought
+ * to a device buffer every step). For j < n:
+ *   dst + dst_page[j] * page_bytes  <-  src_host + src_page[j] * page_bytes   (page_bytes bytes)
+ *   src_host     pinned host memory of n_src_pages pages (hipHostMalloc, or a pinned torch tensor);
+ *                the kernel reads it through the device alias hipHostGetDevicePointer gives;
+ *                HYB_EINVAL if it has none
+ *   dst          device memory of n_dst_pages pages
+ *   src_page, dst_page  int32 [n] in device memory. The indices are device data the host cannot
+ *                see: a j whose src_page[j] is outside [0, n_src_pages) or dst_page[j] outside
+ *                [0, n_dst_pages) is skipped (nothing read, nothing written). Destination pages
+ *                must not repeat.
+ *   page_bytes % 16 == 0; src_host and dst 16-byte aligned; n_src_pages, n_dst_pages >= 1.
+ * ------------------------------------------------------------------------------------------ */
+int32_t hyb_gather_pages(const void* src_host, int32_t n_src_pages, void* dst, int32_t n_dst_pages,
+                         const int32_t* src_page, const int32_t* dst_page, int32_t n,
+                         int64_t page_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------------
  * hyb_index_score - indexer scores over the visible compressed entries.

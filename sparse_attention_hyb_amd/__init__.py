@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyb.so")
 
 HYB_OK, HYB_EINVAL, HYB_ENOTSUP, HYB_EWORKSPACE, HYB_ELAUNCH = 0, 1, 2, 3, 4
 F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
-ABI_VERSION = 2   # HYB_ABI_VERSION of include/hyb.h that these signatures follow
+ABI_VERSION = 3   # HYB_ABI_VERSION of include/hyb.h that these signatures follow
 POOL_MEAN, POOL_SOFTMAX_GATE = 0, 1
 BLOCK_POSITIONS = 256
 KMAX = 2048
@@ -34,6 +34,7 @@ EXPORTS = (
     "hyb_index_topk_workspace_bytes", "hyb_index_topk",
     "hyb_attn_decode_workspace_bytes", "hyb_attn_decode", "hyb_attn_decode_compress",
     "hyb_attn_prefill_workspace_bytes", "hyb_attn_prefill",
+    "hyb_probe_granule", "hyb_probe",
 )
 
 
@@ -96,7 +97,7 @@ _SIGS = {
     "hyb_index_topk": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _PP, _I32, _P, _P, _SZ, _P]),
     "hyb_q_norm_kv_insert": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P, _PP, _I32, _D,
                                     _F, _P]),
-    "hyb_gather_pages": (_I32, [_P, _P, _P, _P, _I32, _I64, _P]),
+    "hyb_gather_pages": (_I32, [_P, _I32, _P, _I32, _P, _P, _I32, _I64, _P]),
     "hyb_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "hyb_attn_decode": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F, _I32,
                                _D, _P, _I32, _P, _P, _SZ, _P]),
@@ -106,6 +107,8 @@ _SIGS = {
     "hyb_attn_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "hyb_attn_prefill": (_I32, [_P, _I32, _P, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F,
                                 _I32, _D, _P, _I32, _P, _P, _SZ, _P]),
+    "hyb_probe_granule": (ctypes.c_uint64, [_I32, _I32]),
+    "hyb_probe": (_I32, [_I32, _I32, _I32, _P, _P, ctypes.c_uint64, _P, _P, _I32, _I64, _P, _P]),
 }
 
 
@@ -229,12 +232,22 @@ def hyb_q_norm_kv_insert(q, kv, cu_seqlens, start_pos, max_new_tokens: int, swa_
 
 def hyb_gather_pages(src_host, dst, src_page, dst_page, stream=None) -> None:
     """Copy pages src_host[src_page[j]] -> dst[dst_page[j]] in one launch (see include/hyb.h).
-    src_host: a pinned CPU tensor [pages, ...]; dst: a device tensor of the same page shape;
-    src_page, dst_page: int32 device tensors of one length."""
+    src_host: a contiguous pinned CPU tensor [pages, ...]; dst: a contiguous device tensor of the
+    same page shape; src_page, dst_page: int32 device tensors of one length (indices outside the
+    two tensors' page counts are skipped by the kernel)."""
+    import torch
+    if not (src_host.is_contiguous() and dst.is_contiguous()):
+        raise TypeError("src_host and dst must be contiguous")
+    for t in (src_page, dst_page):
+        if t.dtype != torch.int32 or t.device.type != "cuda" or t.dim() != 1 or not t.is_contiguous():
+            raise TypeError("src_page and dst_page must be contiguous 1-d int32 device tensors")
+    if src_page.numel() != dst_page.numel():
+        raise TypeError("src_page and dst_page differ in length")
     page = src_host[0].numel() * src_host.element_size()
     if dst[0].numel() * dst.element_size() != page:
         raise TypeError("src_host and dst pages differ in size")
-    _check(load().hyb_gather_pages(_ptr(src_host), _ptr(dst), _ptr(src_page), _ptr(dst_page),
+    _check(load().hyb_gather_pages(_ptr(src_host), int(src_host.shape[0]), _ptr(dst),
+                                   int(dst.shape[0]), _ptr(src_page), _ptr(dst_page),
                                    int(src_page.numel()), int(page), _stream(stream)))
 
 
@@ -379,3 +392,22 @@ def hyb_attn_prefill(q, q_pos, max_pos: int, swa_pool, comp_pool, out, topk_idx=
                                    _ptr(topk_idx), int(k), int(window), scale, int(rope_dim),
                                    float(rope_base), _ptr(out), _odtype(out, out_scale), _ptr(out_scale), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------------------------
+# HBM bandwidth probe (include/hyb_probe.h): a measurement aid beside the attention step.
+PROBE_READ, PROBE_READ_DYN, PROBE_READ_LDS, PROBE_READ_PAGES, PROBE_COPY = 0, 1, 2, 3, 4
+
+
+def hyb_probe_granule(variant: int, unroll: int = 8) -> int:
+    return int(load().hyb_probe_granule(int(variant), int(unroll)))
+
+
+def hyb_probe(variant: int, src, n_workgroups: int, unroll: int = 8, dst=None, nbytes: int = 0,
+              counter=None, pages=None, page_bytes: int = 0, trace=None, stream=None) -> None:
+    """One probe launch (see include/hyb_probe.h). nbytes defaults to src's size."""
+    nbytes = int(nbytes) or src.numel() * src.element_size()
+    _check(load().hyb_probe(int(variant), int(unroll), int(n_workgroups), _ptr(src), _ptr(dst),
+                            nbytes, _ptr(counter), _ptr(pages),
+                            int(pages.numel()) if pages is not None else 0, int(page_bytes),
+                            _ptr(trace), _stream(stream)))

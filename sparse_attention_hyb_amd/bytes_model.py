@@ -63,24 +63,32 @@ def decode_query_bytes(L: int, *, ratio: int, sparse: bool, n_heads: int = 64, d
 
 
 def compress_decode_bytes(ratio: int, dim: int = 512, x_bytes: int = 2, out_dtype: str = "bf16",
-                          completes: bool = True) -> int:
-    """One new token per sequence: read the r-1 earlier group tokens from the fp32 state ring and
-    the new token, write the entry (when the group completes)."""
+                          completes: bool = True, gate: bool = False) -> int:
+    """One new token per sequence. The state ring holds the raw tokens of the group in x's own
+    storage type (x_bytes per element) and, with softmax-gate pooling, one float32 logit each.
+    A completing group reads its r-1 earlier tokens from the ring and the new token and writes
+    the entry; otherwise the new token is read and written to the ring."""
+    lg = 4 if gate else 0
     if not completes:
-        return dim * x_bytes + dim * 4
-    return (ratio - 1) * dim * 4 + dim * x_bytes + entry_bytes(out_dtype, dim)
+        return 2 * (dim * x_bytes + lg)
+    return (ratio - 1) * (dim * x_bytes + lg) + dim * x_bytes + lg + entry_bytes(out_dtype, dim)
 
 
 def index_score_bytes(L: int, *, ratio: int = 4, idx_heads: int = 64, idx_dim: int = 128,
-                      idx_dtype: str = "bf16", q_bytes: int = 2, window: int = 128,
-                      handoff: bool = False) -> int:
-    """The indexer-score kernel's own mandatory traffic for one query: visible keys + its query
-    and weights + what it writes: fp32 scores, or (handoff) the selector hand-off of an 8-byte
-    (key, index) pair per entry plus a 1024-bin uint16 cumulative histogram per 1024 entries."""
+                      idx_dtype: str = "bf16", q_bytes: int = 2, window: int = 128) -> int:
+    """The indexer's algorithmic traffic for one query: every visible key, its query and its head
+    weights. The scores are an intermediate of the selection (a fused scorer and selector never
+    writes them), so nothing written is counted; see handoff_bytes for what this library's
+    scorer hands to its selector."""
     nv = n_visible(L - 1, ratio, window)
-    written = nv * 8 + (nv + 1023) // 1024 * 1024 * 2 if handoff else nv * 4
-    return (nv * entry_bytes(idx_dtype, idx_dim) + idx_heads * idx_dim * q_bytes + idx_heads * 4
-            + written)
+    return nv * entry_bytes(idx_dtype, idx_dim) + idx_heads * idx_dim * q_bytes + idx_heads * 4
+
+
+def handoff_bytes(L: int, *, ratio: int = 4, window: int = 128) -> int:
+    """What the scorer writes for the selector per query (not algorithmic): an 8-byte (key,
+    index) pair per visible entry and a 1024-bin uint16 cumulative histogram per 1024 entries."""
+    nv = n_visible(L - 1, ratio, window)
+    return nv * 8 + (nv + 1023) // 1024 * 1024 * 2
 
 
 def attention_flops(n_keys: int, n_heads: int = 64, dim: int = 512) -> int:

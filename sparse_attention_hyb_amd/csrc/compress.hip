@@ -270,13 +270,16 @@ hipError_t launch_q_norm_kv_insert(const QNormArgs& a, hipStream_t s) {
 // Working-set fill of an offloaded pool: workgroup j copies page src_page[j] of the host mirror
 // (through its device alias) to page dst_page[j] of the device pool, 16 bytes per thread and
 // load, every load of a thread issued before its stores.
-__global__ __launch_bounds__(256) void gather_pages_kernel(const uint8_t* src, uint8_t* dst,
+__global__ __launch_bounds__(256) void gather_pages_kernel(const uint8_t* src, int32_t n_src,
+                                                           uint8_t* dst, int32_t n_dst,
                                                            const int32_t* src_page,
                                                            const int32_t* dst_page,
                                                            int64_t page_bytes) {
   const int j = blockIdx.x;
-  const u32x4* s = reinterpret_cast<const u32x4*>(src + (int64_t)src_page[j] * page_bytes);
-  u32x4* d = reinterpret_cast<u32x4*>(dst + (int64_t)dst_page[j] * page_bytes);
+  const int sp = src_page[j], dp = dst_page[j];
+  if (sp < 0 || sp >= n_src || dp < 0 || dp >= n_dst) return;   // out of range: skipped
+  const u32x4* s = reinterpret_cast<const u32x4*>(src + (int64_t)sp * page_bytes);
+  u32x4* d = reinterpret_cast<u32x4*>(dst + (int64_t)dp * page_bytes);
   const int64_t n16 = page_bytes / 16;
   constexpr int kU = 8;
   for (int64_t o = threadIdx.x; o < n16; o += 256 * kU) {
@@ -290,12 +293,12 @@ __global__ __launch_bounds__(256) void gather_pages_kernel(const uint8_t* src, u
   }
 }
 
-hipError_t launch_gather_pages(const void* src_dev, void* dst, const int32_t* src_page,
-                               const int32_t* dst_page, int32_t n, int64_t page_bytes,
-                               hipStream_t s) {
+hipError_t launch_gather_pages(const void* src_dev, int32_t n_src, void* dst, int32_t n_dst,
+                               const int32_t* src_page, const int32_t* dst_page, int32_t n,
+                               int64_t page_bytes, hipStream_t s) {
   hipLaunchKernelGGL(gather_pages_kernel, dim3(n), dim3(256), 0, s,
-                     static_cast<const uint8_t*>(src_dev), static_cast<uint8_t*>(dst), src_page,
-                     dst_page, page_bytes);
+                     static_cast<const uint8_t*>(src_dev), n_src, static_cast<uint8_t*>(dst), n_dst,
+                     src_page, dst_page, page_bytes);
   return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // dispatch to the kernel launchers. Declarations, argument meaning and error behaviour are in
 // include/hyb.h.
 #include "hyb.h"
+#include "hyb_probe.h"
 
 #include <hip/hip_runtime.h>
 
@@ -11,6 +12,7 @@
 #include <string>
 
 #include "hyb_internal.h"
+#include "hyb_probe_internal.h"
 
 namespace {
 
@@ -174,6 +176,9 @@ int check_attention(const char* op, const void* q, int32_t q_dtype, int32_t n_q,
   hyb::PoolDev ps{}, pc{};
   HYB_TRY(check_pool(swa, op, "swa", true, false, 1, &ps));
   HYB_TRY(check_pool(comp, op, "comp", true, false, 2 | 4, &pc));
+  if (window < pc.ratio)
+    return fail(HYB_EINVAL, "%s: window %d < comp ratio %d (the group being filled would be visible)",
+                op, window, pc.ratio);
   if (ps.dim != pc.dim) return fail(HYB_EINVAL, "%s: swa.dim %d != comp.dim %d", op, ps.dim, pc.dim);
   if (ps.dtype != pc.dtype) return fail(HYB_EINVAL, "%s: swa and comp must share one dtype", op);
   if (ps.dtype == HYB_FP8_E4M3 && q_dtype != HYB_BF16)
@@ -318,12 +323,16 @@ int32_t hyb_q_norm_kv_insert(const void* q, int32_t q_dtype, int32_t n_heads, co
   return launch_status(hyb::launch_q_norm_kv_insert(a, static_cast<hipStream_t>(stream)), op);
 }
 
-int32_t hyb_gather_pages(const void* src_host, void* dst, const int32_t* src_page,
-                         const int32_t* dst_page, int32_t n, int64_t page_bytes, void* stream) {
+int32_t hyb_gather_pages(const void* src_host, int32_t n_src_pages, void* dst, int32_t n_dst_pages,
+                         const int32_t* src_page, const int32_t* dst_page, int32_t n,
+                         int64_t page_bytes, void* stream) {
   const char* op = "hyb_gather_pages";
   if (!src_host || !dst || !src_page || !dst_page)
     return fail(HYB_EINVAL, "%s: src_host, dst, src_page and dst_page must be non-NULL", op);
   if (n < 0) return fail(HYB_EINVAL, "%s: n %d < 0", op, n);
+  if (n_src_pages < 1 || n_dst_pages < 1)
+    return fail(HYB_EINVAL, "%s: n_src_pages %d and n_dst_pages %d must be positive", op,
+                n_src_pages, n_dst_pages);
   if (page_bytes <= 0 || page_bytes % 16)
     return fail(HYB_EINVAL, "%s: page_bytes %lld must be a positive multiple of 16", op,
                 (long long)page_bytes);
@@ -335,7 +344,8 @@ int32_t hyb_gather_pages(const void* src_host, void* dst, const int32_t* src_pag
     (void)hipGetLastError();
     return fail(HYB_EINVAL, "%s: src_host is not pinned host memory with a device alias", op);
   }
-  return launch_status(hyb::launch_gather_pages(src_dev, dst, src_page, dst_page, n, page_bytes,
+  return launch_status(hyb::launch_gather_pages(src_dev, n_src_pages, dst, n_dst_pages, src_page,
+                                                dst_page, n, page_bytes,
                                                 static_cast<hipStream_t>(stream)), op);
 }
 
@@ -350,6 +360,9 @@ static int check_score(const char* op, const void* q_idx, int32_t q_dtype, const
   if (!is_plain(q_dtype)) return fail(HYB_ENOTSUP, "%s: q_dtype must be F32 or BF16", op);
   hyb::PoolDev pp{};
   HYB_TRY(check_pool(idx_pool, op, "idx_pool", false, true, 2 | 4, &pp));
+  if (window < pp.ratio)
+    return fail(HYB_EINVAL, "%s: window %d < idx_pool ratio %d (the group being filled would be visible)",
+                op, window, pp.ratio);
   const bool mfma = n_heads == 64 && pp.dim == 128 && q_dtype == HYB_BF16 &&
                     (pp.dtype == HYB_BF16 || pp.dtype == HYB_FP4_E2M1);
   if (!mfma && (int64_t)n_heads * pp.dim > 8192)
@@ -438,6 +451,9 @@ int32_t hyb_topk_keys(const uint32_t* keys, int64_t keys_ld, const uint16_t* par
   if (n_q < 0 || max_pos < 0) return fail(HYB_EINVAL, "%s: n_q and max_pos must be >= 0", op);
   if (window <= 0) return fail(HYB_EINVAL, "%s: window %d must be positive", op, window);
   if (ratio != 4 && ratio != 128) return fail(HYB_EINVAL, "%s: ratio %d must be 4 or 128", op, ratio);
+  if (window < ratio)
+    return fail(HYB_EINVAL, "%s: window %d < ratio %d (the group being filled would be visible)",
+                op, window, ratio);
   if (k < 1 || k > HYB_KMAX) return fail(HYB_EINVAL, "%s: k %d outside [1, %d]", op, k, HYB_KMAX);
   const int64_t nv = visible(max_pos, ratio, window);
   if (part_ld < part_blocks(nv) || part_ld > hyb::kTopkMaxParts)
@@ -592,6 +608,49 @@ int32_t hyb_attn_prefill(const void* q, int32_t q_dtype, const int32_t* q_seq,
   if (n_q == 0) return HYB_OK;
   c.args.qd = hyb::QueryDev{nullptr, q_seq, q_pos};
   return launch_status(hyb::launch_attention(c.args, static_cast<hipStream_t>(stream)), op);
+}
+
+uint64_t hyb_probe_granule(int32_t variant, int32_t unroll) {
+  if (variant < HYB_PROBE_READ || variant > HYB_PROBE_COPY) return 0;
+  if (variant != HYB_PROBE_READ_LDS && unroll != 4 && unroll != 8 && unroll != 16) return 0;
+  return hyb::probe_granule(variant, unroll);
+}
+
+int32_t hyb_probe(int32_t variant, int32_t unroll, int32_t n_workgroups, const void* src,
+                  void* dst, uint64_t bytes, uint32_t* counter, const int32_t* pages,
+                  int32_t n_pages, int64_t page_bytes, uint64_t* trace, void* stream) {
+  const char* op = "hyb_probe";
+  const uint64_t gran = hyb_probe_granule(variant, unroll);
+  if (gran == 0) return fail(HYB_EINVAL, "%s: variant %d / unroll %d unknown", op, variant, unroll);
+  if (n_workgroups < 1 || n_workgroups > 65536)
+    return fail(HYB_EINVAL, "%s: n_workgroups %d outside [1, 65536]", op, n_workgroups);
+  if (!src || (reinterpret_cast<uintptr_t>(src) & 15u))
+    return fail(HYB_EINVAL, "%s: src must be non-NULL and 16-byte aligned", op);
+  if (variant == HYB_PROBE_READ_PAGES) {
+    if (!pages || n_pages < 1) return fail(HYB_EINVAL, "%s: READ_PAGES needs pages and n_pages >= 1", op);
+    if (page_bytes <= 0 || (uint64_t)page_bytes % gran)
+      return fail(HYB_EINVAL, "%s: page_bytes %lld must be a positive multiple of %llu", op,
+                  (long long)page_bytes, (unsigned long long)gran);
+  } else {
+    if (bytes == 0 || bytes % gran)
+      return fail(HYB_EINVAL, "%s: bytes %llu must be a positive multiple of %llu", op,
+                  (unsigned long long)bytes, (unsigned long long)gran);
+  }
+  if (variant == HYB_PROBE_READ_DYN && (!counter || page_bytes <= 0))
+    return fail(HYB_EINVAL, "%s: READ_DYN needs a counter and page_bytes > 0", op);
+  if (variant == HYB_PROBE_COPY && (!dst || (reinterpret_cast<uintptr_t>(dst) & 15u)))
+    return fail(HYB_EINVAL, "%s: COPY needs a 16-byte aligned dst", op);
+  hyb::ProbeArgs a{};
+  a.src = static_cast<const uint8_t*>(src);
+  a.dst = static_cast<uint8_t*>(dst);
+  a.bytes = bytes;
+  a.counter = counter;
+  a.pages = pages;
+  a.n_pages = n_pages;
+  a.chunk_bytes = page_bytes;
+  a.trace = trace;
+  a.sink = variant == HYB_PROBE_COPY ? nullptr : static_cast<uint32_t*>(dst);
+  return launch_status(hyb::launch_probe(variant, unroll, n_workgroups, a, static_cast<hipStream_t>(stream)), op);
 }
 
 }  // extern "C"

@@ -65,10 +65,11 @@ struct QNormArgs {
   float eps;
 };
 hipError_t launch_q_norm_kv_insert(const QNormArgs& a, hipStream_t s);
-// n pages of page_bytes: dst + dst_page[j] * page_bytes <- src_dev + src_page[j] * page_bytes
-hipError_t launch_gather_pages(const void* src_dev, void* dst, const int32_t* src_page,
-                               const int32_t* dst_page, int32_t n, int64_t page_bytes,
-                               hipStream_t s);
+// n pages of page_bytes: dst + dst_page[j] * page_bytes <- src_dev + src_page[j] * page_bytes,
+// skipping every j whose source page is outside [0, n_src) or destination page outside [0, n_dst)
+hipError_t launch_gather_pages(const void* src_dev, int32_t n_src, void* dst, int32_t n_dst,
+                               const int32_t* src_page, const int32_t* dst_page, int32_t n,
+                               int64_t page_bytes, hipStream_t s);
 
 // ---- indexer scores -------------------------------------------------------------------------
 struct ScoreArgs {

@@ -2,7 +2,9 @@
 
 The step's work and what each part reads and writes:
   prep      hyb_q_norm_kv_insert: query RMSNorm + RoPE of the new tokens (writes q) and their
-            window entries (writes the window pool at each sequence's position p);
+            window entries (writes the window pool at each sequence's position p); on C4 layers
+            also hyb_compress of the new tokens' indexer-key rows into the indexer-key pool (an
+            entry that a token completes at p is not visible at p, so the indexer never reads it);
   indexer   C4 layers: hyb_index_score_keys + hyb_topk_keys (reads the indexer keys, writes
             top-k) - independent of prep;
   attention hyb_attn_decode_compress: reads q, the window (entry p included) and the compressed
@@ -21,7 +23,8 @@ from typing import Optional
 
 import torch
 
-from . import hyb_attn_decode_compress, hyb_index_score_keys, hyb_q_norm_kv_insert, hyb_topk_keys
+from . import (hyb_attn_decode_compress, hyb_compress, hyb_index_score_keys, hyb_q_norm_kv_insert,
+               hyb_topk_keys)
 
 
 @dataclass
@@ -48,6 +51,8 @@ class DecodeStepBuffers:
     hist: Optional[torch.Tensor] = None
     topk: Optional[torch.Tensor] = None
     k: int = 512
+    idx_kv_new: Optional[torch.Tensor] = None   # [B, D_I] the new tokens' indexer-key rows
+    idx_state: Optional[torch.Tensor] = None    # indexer-key compressor ring [B, 4, D_I]
     gate_logits: Optional[torch.Tensor] = None    # C128 softmax-gate pooling
     state_logits: Optional[torch.Tensor] = None
     rope_dim: int = 64
@@ -68,6 +73,9 @@ class DecodeStep:
         b = self.b
         hyb_q_norm_kv_insert(b.q_raw, b.kv_new, b.cu, b.start, 1, b.swa, q_out=b.q,
                              rope_dim=b.rope_dim, rope_base=b.rope_base, eps=b.eps, stream=stream)
+        if b.idx_kv_new is not None:
+            hyb_compress(b.idx_kv_new, b.cu, b.start, 1, b.idx_state, b.idx_pool, b.rope_dim,
+                         rope_base=b.rope_base, eps=b.eps, stream=stream)
 
     def _indexer(self, stream):
         b = self.b

@@ -263,10 +263,12 @@ def _ints(x, device) -> torch.Tensor:
 def sparse_decode(device, seed: int = 0, batch: int = 16, ctx=131072, n_heads: int = 64,
                   dim: int = 512, rope_dim: int = 64, idx_heads: int = 64, idx_dim: int = 128,
                   k: int = 512, window: int = 128, dtype: str = "bf16", idx_dtype: str = "bf16",
-                  workload_id: int = 2, shuffle: bool = True) -> Decode:
+                  workload_id: int = 2, shuffle: bool = True, grow: int = 0) -> Decode:
     """C4 sparse decode: SWA window + indexer top-k over C4 entries (entries drawn directly).
 
-    ``ctx`` is one context length for every sequence or a per-sequence list.
+    ``ctx`` is one context length for every sequence or a per-sequence list. ``grow`` > 0 sizes
+    the pools (and block tables) for that many more tokens per sequence, for runs of several
+    decode steps; the blocks the extra tokens reach hold drawn values until written.
     """
     lens = list(ctx) if isinstance(ctx, (list, tuple)) else [int(ctx)] * batch
     assert len(lens) == batch
@@ -276,11 +278,11 @@ def sparse_decode(device, seed: int = 0, batch: int = 16, ctx=131072, n_heads: i
     q = to_storage(randn((batch, n_heads, dim), g, device), qdt)
     idx_q = to_storage(randn((batch, idx_heads, idx_dim), g, device), qdt)
     idx_w = randn((batch, idx_heads), g, device) / math.sqrt(128.0)
-    swa_need = [blocks_for_positions(max(0, L - window), L) for L in lens]
-    swa = make_pool(dtype, dim, 1, swa_need, -(-max_len // BLOCK_POSITIONS),
+    swa_need = [blocks_for_positions(max(0, L - window), L + grow) for L in lens]
+    swa = make_pool(dtype, dim, 1, swa_need, -(-(max_len + grow) // BLOCK_POSITIONS),
                     generator(workload_id, seed, 1, device), device, shuffle=shuffle)
-    c_need = [blocks_for_entries(L // 4, 4) for L in lens]
-    mb = -(-max_len // BLOCK_POSITIONS)
+    c_need = [blocks_for_entries((L + grow) // 4, 4) for L in lens]
+    mb = -(-(max_len + grow) // BLOCK_POSITIONS)
     comp = make_pool(dtype, dim, 4, c_need, mb, generator(workload_id, seed, 2, device), device,
                      shuffle=shuffle)
     idx_pool = make_pool(idx_dtype, idx_dim, 4, c_need, mb,

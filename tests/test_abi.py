@@ -22,20 +22,24 @@ def lib():
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "hyb.h")).read()
-    return sorted(set(re.findall(r"^(?:int32_t|size_t|const char\*)\s+(hyb_\w+)\(", src, re.M)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"^(?:int32_t|size_t|uint64_t|const char\*)\s+(hyb_\w+)\(", src, re.M))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(hyb.EXPORTS) == names
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hyb_abi_version() == hyb.ABI_VERSION == 2
+    assert lib.hyb_abi_version() == hyb.ABI_VERSION == 3
     assert [lib.hyb_status_str(i).decode() for i in range(5)] == [
         "HYB_OK", "HYB_EINVAL", "HYB_ENOTSUP", "HYB_EWORKSPACE", "HYB_ELAUNCH"]
 
@@ -254,12 +258,43 @@ def test_q_norm_kv_insert_validation(lib):
 
 
 def test_gather_pages_validation(lib):
-    def call(src=FAKE, dst=FAKE, sp=FAKE, dp=FAKE, n=4, page=65536):
-        return lib.hyb_gather_pages(src, dst, sp, dp, n, page, None)
+    def call(src=FAKE, dst=FAKE, sp=FAKE, dp=FAKE, n=4, page=65536, n_src=16, n_dst=8):
+        return lib.hyb_gather_pages(src, n_src, dst, n_dst, sp, dp, n, page, None)
 
     assert call(src=None) == hyb.HYB_EINVAL and call(dp=None) == hyb.HYB_EINVAL
     assert call(n=-1) == hyb.HYB_EINVAL
+    assert call(n_src=0) == hyb.HYB_EINVAL and call(n_dst=-3) == hyb.HYB_EINVAL
     assert call(page=0) == hyb.HYB_EINVAL and call(page=100) == hyb.HYB_EINVAL
     assert call(src=FAKE + 8) == hyb.HYB_EINVAL                      # not 16-byte aligned
     assert lib.hyb_last_error().decode().startswith("hyb_gather_pages")
     assert call(n=0) == hyb.HYB_OK
+
+
+def test_gather_pages_binding_checks():
+    """The binding refuses index tensors that are not 1-d int32 device tensors of one length and
+    buffers that are not contiguous, before any library call (CPU tensors stand in here)."""
+    import torch
+    src = torch.zeros(4, 64, 16)
+    dst = torch.zeros(4, 64, 16)
+    i32 = torch.arange(4, dtype=torch.int32)
+    with pytest.raises(TypeError, match="int32 device"):
+        hyb.hyb_gather_pages(src, dst, i32, i32)               # host index tensors
+    with pytest.raises(TypeError, match="int32 device"):
+        hyb.hyb_gather_pages(src, dst, i32.long(), i32)
+    with pytest.raises(TypeError, match="contiguous"):
+        hyb.hyb_gather_pages(src.transpose(1, 2), dst, i32, i32)
+
+
+@pytest.mark.parametrize("op", ["decode", "score", "topk"])
+def test_window_smaller_than_ratio_is_refused(lib, op):
+    """A window shorter than the compression ratio would make the group being filled visible."""
+    if op == "decode":
+        st = decode(lib, comp=pool(ratio=128), window=64)
+    elif op == "score":
+        ip = pool(dim=128, ratio=4)
+        st = lib.hyb_index_score(FAKE, hyb.BF16, FAKE, None, FAKE, 2, 64, 1000, 2, ctypes.byref(ip),
+                                 FAKE, 1024, None)
+    else:
+        st = lib.hyb_topk_keys(FAKE, 4096, FAKE, 2, FAKE, 2, 10000, 100, 128, 64, FAKE, None)
+    assert st == hyb.HYB_EINVAL
+    assert "window" in lib.hyb_last_error().decode()

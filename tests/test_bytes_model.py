@@ -57,3 +57,17 @@ def test_page_constants_fixture():
     assert O.BLOCK_POSITIONS == hyb.BLOCK_POSITIONS == c["block_native_positions"]
     assert c["window_raw_tokens"] == 128 and c["topk"] == 512
     assert (c["c4_ratio"], c["c128_ratio"]) == (4, 128)
+
+
+def test_compressor_and_indexer_bytes():
+    """The compressor's ring holds raw tokens in x's storage type: a completing C128 group of bf16
+    512-dim rows reads 127 ring rows and the new row (128 x 1 KiB) and writes one 1 KiB entry;
+    softmax gates add a 4-byte logit per token. The indexer's algorithmic bytes at 128K are the
+    32736 visible 256-byte keys, its 64 x 128 bf16 query and 64 float weights; the hand-off to the
+    selector (8 bytes per entry + 2 KiB per 1024 entries) is counted apart."""
+    assert BM.compress_decode_bytes(128) == 129 * 1024
+    assert BM.compress_decode_bytes(128, gate=True) == 129 * 1024 + 128 * 4
+    assert BM.compress_decode_bytes(4) == 5 * 1024
+    assert BM.compress_decode_bytes(4, completes=False) == 2 * 1024
+    assert BM.index_score_bytes(131072) == 32736 * 256 + 64 * 128 * 2 + 64 * 4
+    assert BM.handoff_bytes(131072) == 32736 * 8 + 32 * 2048

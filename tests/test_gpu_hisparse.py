@@ -1,12 +1,14 @@
 """C4 offload (pinned host mirror + device working set): the attention over the working set equals
 the attention over the device-resident pool bit for bit, step after step, while pages are
-evicted and brought back."""
+evicted and brought back, and sampled sequences match the float64 oracle (top-k and output)."""
 
 import pytest
 import torch
 
 from sparse_attention_hyb_amd import workloads as W
 from sparse_attention_hyb_amd.hisparse import C4Offload
+from tests.conftest import to_f64, to_oracle_pool
+from tests.parity_util import assert_abs_close, check_topk_set
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -19,9 +21,12 @@ def test_c4_offload_equals_device_pool(gpu_lib, dtype):
     each step selects about 600 pages, some of them evicted by the step before. fp8 pools bring
     each page's per-entry scales along."""
     hyb = gpu_lib
-    from tests.test_gpu_parity import gpu_decode, gpu_topk
+    from tests.test_gpu_parity import gpu_decode, gpu_topk, oracle_out, oracle_select
     lens = [20000, 50000, 131072, 7000]
     wl = W.sparse_decode(DEV, seed=6, batch=len(lens), ctx=lens, dtype=dtype)
+    swa_o, comp_o, idx_o = to_oracle_pool(wl.swa), to_oracle_pool(wl.comp), to_oracle_pool(wl.idx_pool)
+    seqs = (1, 2)
+    compared = 0
     mirror = W.PagedTensors(wl.comp.data.cpu().pin_memory(),
                             None if wl.comp.scale is None else wl.comp.scale.cpu().pin_memory(),
                             wl.comp.block_table.cpu(), wl.comp.dtype, wl.dim, 4)
@@ -41,6 +46,18 @@ def test_c4_offload_equals_device_pool(gpu_lib, dtype):
         wl.comp = comp
         torch.cuda.synchronize()
         assert torch.equal(got, want), step
+        # sampled sequences against the oracle: its own top-k and attention over its own pools
+        # (the working set holds the pages of the GPU's selection, so the output is compared
+        # where the two selections are equal; a near-tie swap is checked by the fp32 bound)
+        sel = oracle_select(wl, idx_o, seqs)
+        gt = topk.cpu().numpy()
+        for b in seqs:
+            check_topk_set(gt[b], sel[b][1], sel[b][0], sel[b][2], wl.k)
+        same = [b for b in seqs if list(gt[b]) == list(sel[b][1])]
+        if same:
+            want_o = oracle_out(wl, swa_o, comp_o, same, {b: sel[b][1] for b in same})
+            assert_abs_close(to_f64(got)[same], want_o)
+            compared += len(same)
         # resident pages hold their mirror pages byte for byte (sampled)
         res = sorted(off.where.items())
         for (b, lb), s in res[::max(1, len(res) // 64)]:
@@ -48,6 +65,7 @@ def test_c4_offload_equals_device_pool(gpu_lib, dtype):
             assert torch.equal(off.data[s].cpu(), mirror.data[src]), (b, lb)
             if mirror.scale is not None:
                 assert torch.equal(off.scale[s].cpu(), mirror.scale[src]), (b, lb)
+    assert compared >= 3   # outputs were checked against the oracle in most steps
     assert off.one_launch   # the pinned mirror took the one-launch gather
     assert hits > 0   # later steps reuse resident pages
 

@@ -101,6 +101,64 @@ def test_compress_stream_prefix_and_pending():
     assert np.array_equal(slots[2], x[26]) and lslots[0] == lg[24]
 
 
+def test_compress_stream_hand_groups():
+    """Three softmax-gate groups of ratio 2 built by hand, with a different logit pair in each
+    group, plus one trailing token of an incomplete group. With r_d = 2 and theta_0 = 1 the last
+    pair turns by the group-end position (1, 3, 5) in radians; eps = 0.
+      group 0: logits (0, ln 3) -> weights (1/4, 3/4): pooled (1, 0, 0, 3), RMS sqrt(2.5)
+      group 1: logits (ln 3, 0) -> weights (3/4, 1/4): pooled (0, 3, 1, 0), RMS sqrt(2.5)
+      group 2: logits (5, 5)    -> weights (1/2, 1/2): pooled (1, 1, 1, 1), RMS 1
+    A logits window taken at the wrong offset, a group rotated at the wrong position or a group
+    built from the wrong tokens changes at least one entry."""
+    x = np.array([[4.0, 0, 0, 0], [0, 0, 0, 4.0],
+                  [0, 4.0, 0, 0], [0, 0, 4.0, 0],
+                  [2.0, 2.0, 0, 0], [0, 0, 2.0, 2.0],
+                  [9.0, -9.0, 9.0, 9.0]])
+    lg = np.array([0.0, math.log(3.0), math.log(3.0), 0.0, 5.0, 5.0, -3.0])
+    got = O.compress_stream(x, lg, 2, "gate", 2, 10000.0, 0.0)
+    s25 = math.sqrt(2.5)
+    want = np.array([
+        [1 / s25, 0.0, -3 * math.sin(1.0) / s25, 3 * math.cos(1.0) / s25],
+        [0.0, 3 / s25, math.cos(3.0) / s25, math.sin(3.0) / s25],
+        [1.0, 1.0, math.cos(5.0) - math.sin(5.0), math.sin(5.0) + math.cos(5.0)],
+    ])
+    assert got.shape == (3, 4)
+    assert np.allclose(got, want, rtol=0, atol=1e-14)
+    # mean mode over the same tokens: group 1 pools to (0, 2, 2, 0), RMS sqrt(2)
+    got_m = O.compress_stream(x, None, 2, "mean", 2, 10000.0, 0.0)
+    r2 = math.sqrt(2.0)
+    assert np.allclose(got_m[1], [0.0, r2, r2 * math.cos(3.0), r2 * math.sin(3.0)], rtol=0, atol=1e-14)
+
+
+def test_logical_pool_layout_and_round_trip():
+    """Entries of several sequences laid out block by block in sequence order: with ratio 4 a
+    block holds 64 entries, so 150 entries take blocks 0, 1, 2 (the last one 22 entries, rest
+    zero) and the next sequence starts at block 3; the table pads with -1. Reading every entry
+    back through the paged address rule returns it unchanged (bf16: rounded to nearest even)."""
+    rng = np.random.default_rng(12)
+    e = [rng.standard_normal((150, 8)), rng.standard_normal((64, 8)), rng.standard_normal((1, 8))]
+    pool = O.logical_pool(e, 4)
+    assert pool.data.shape == (5, 64, 8)
+    assert pool.block_table.tolist() == [[0, 1, 2], [3, -1, -1], [4, -1, -1]]
+    assert np.array_equal(pool.data[1, 6], e[0][70])      # entry 70: block 1, slot 6
+    assert np.array_equal(pool.data[2, 21], e[0][149])
+    assert not pool.data[2, 22:].any() and not pool.data[4, 1:].any()
+    for b, ent in enumerate(e):
+        assert np.array_equal(O.pool_entries(pool, b, range(len(ent))), ent)
+    # ratio 128: two entries per block
+    p128 = O.logical_pool([e[0][:5]], 128)
+    assert p128.data.shape == (3, 2, 8) and p128.block_table.tolist() == [[0, 1, 2]]
+    assert np.array_equal(p128.data[2, 0], e[0][4])
+    assert np.array_equal(O.pool_entries(p128, 0, [4, 0, 3]), e[0][[4, 0, 3]])
+    # bf16 storage: the stored bit patterns are the nearest-even bf16 of each value
+    vals = np.array([[1.0, 1.00390625, 1.01171875, -3.0e-3, 65504.0, 0.0, -0.0, 1e-40]])
+    pb = O.logical_pool([vals], 1, dtype="bf16")
+    # 1 + 2^-8 ties to 1 (even); 1 + 3 * 2^-8 ties up to 1 + 2^-6
+    assert pb.data[0, 0, :3].tolist() == [0x3F80, 0x3F80, 0x3F82]
+    back = O.pool_entries(pb, 0, [0])[0]
+    assert back[0] == 1.0 and back[2] == 1.0 + 2 ** -6 and back[4] == 65536.0
+
+
 def test_swa_entries_are_rotated_tokens():
     rng = np.random.default_rng(6)
     x = rng.standard_normal((3, 8))
