@@ -274,6 +274,26 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------------
+ * hyb_index_topk_noalloc - hyb_index_topk for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments without the workspace, the same selection from the same kernels. Its scratch memory
+ * is a static device array of HYB_NOALLOC_SCRATCH_BYTES per GPU, which the library holds from
+ * the first call on that GPU until the process ends; the call allocates nothing. The scratch
+ * that hyb_index_topk_workspace_bytes gives for these arguments must not exceed the array
+ * (HYB_EINVAL otherwise; 64 MiB holds e.g. 16 queries at 2^20 positions or 64 at 2^18). Every
+ * call on one GPU shares that GPU's array and its contents persist between calls: calls that
+ * overlap on one GPU (other streams, other host threads) race, and the caller must order them.
+ * The first call on a device looks up the array's address with that device current
+ * (HYB_ELAUNCH if that fails).
+ * ------------------------------------------------------------------------------------------ */
+#define HYB_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int32_t hyb_index_topk_noalloc(const void* q_idx, int32_t q_dtype, const float* w,
+                               const int32_t* q_seq, const int32_t* q_pos, int32_t n_q,
+                               int32_t n_heads, int32_t max_pos, int32_t window,
+                               const hyb_paged* idx_pool, int32_t k, int32_t* out_idx,
+                               void* stream);
+
+/* --------------------------------------------------------------------------------------------
  * hyb_attn_decode - one query token per sequence, p = seq_lens[b] - 1.
  * [vLLM] "Shared K/V + inverse RoPE", "short sliding window"; [SGLang] "Shadow Radix": SWA over
  * the newest `window` raw tokens plus either the selected C4 entries (topk_idx != NULL, sparse)

@@ -31,7 +31,7 @@ EXPORTS = (
     "hyb_abi_version", "hyb_status_str", "hyb_last_error", "hyb_compress", "hyb_swa_insert",
     "hyb_q_norm_kv_insert", "hyb_gather_pages",
     "hyb_index_score", "hyb_topk", "hyb_index_score_keys", "hyb_topk_keys",
-    "hyb_index_topk_workspace_bytes", "hyb_index_topk",
+    "hyb_index_topk_workspace_bytes", "hyb_index_topk", "hyb_index_topk_noalloc",
     "hyb_attn_decode_workspace_bytes", "hyb_attn_decode", "hyb_attn_decode_compress",
     "hyb_attn_prefill_workspace_bytes", "hyb_attn_prefill",
     "hyb_probe_granule", "hyb_probe",
@@ -95,6 +95,7 @@ _SIGS = {
     "hyb_topk_keys": (_I32, [_P, _I64, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]),
     "hyb_index_topk_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "hyb_index_topk": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _PP, _I32, _P, _P, _SZ, _P]),
+    "hyb_index_topk_noalloc": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _PP, _I32, _P, _P]),
     "hyb_q_norm_kv_insert": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P, _PP, _I32, _D,
                                     _F, _P]),
     "hyb_gather_pages": (_I32, [_P, _I32, _P, _I32, _P, _P, _I32, _I64, _P]),
@@ -307,6 +308,20 @@ def hyb_index_topk(q_idx, w, q_pos, max_pos: int, idx_pool, k: int, out_idx, win
                                  n_q, int(q_idx.shape[1]), int(max_pos), int(window),
                                  ctypes.byref(d), int(k), _ptr(out_idx), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # HYB_NOALLOC_SCRATCH_BYTES
+
+
+def hyb_index_topk_noalloc(q_idx, w, q_pos, max_pos: int, idx_pool, k: int, out_idx,
+                           window: int = 128, q_seq=None, stream=None) -> None:
+    """hyb_index_topk with its scratch in the library's static per-GPU array (see include/hyb.h):
+    nothing is allocated; calls overlapping on one GPU race."""
+    d = paged(idx_pool)
+    _check(load().hyb_index_topk_noalloc(_ptr(q_idx), _tdtype(q_idx), _ptr(w), _ptr(q_seq),
+                                         _ptr(q_pos), int(q_idx.shape[0]), int(q_idx.shape[1]),
+                                         int(max_pos), int(window), ctypes.byref(d), int(k),
+                                         _ptr(out_idx), _stream(stream)))
 
 
 def hyb_attn_decode_workspace_bytes(batch: int, n_heads: int, dim: int, max_seq_len: int,

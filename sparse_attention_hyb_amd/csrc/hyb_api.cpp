@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "hyb_internal.h"
@@ -535,6 +536,65 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
   t.part_hist = a.part_hist;
   t.part_ld = a.part_ld;
   return launch_status(hyb::launch_topk(t, s), op);
+}
+
+}  // extern "C"
+
+// Scratch memory of hyb_index_topk_noalloc: one array per GPU, zero at load, held until the process
+// ends. Host code never passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol): the device address comes from hipGetSymbolAddress, looked up once per device with
+// that device current and kept per device.
+static __device__ __align__(256) uint8_t scratch[HYB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(const char* op, void** out) {
+  int dev = -1;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(HYB_ELAUNCH, "%s: no current device (%s)", op, hipGetErrorString(ge));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(HYB_ELAUNCH, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s",
+                  op, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HYB_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int32_t hyb_index_topk_noalloc(const void* q_idx, int32_t q_dtype, const float* w,
+                               const int32_t* q_seq, const int32_t* q_pos, int32_t n_q,
+                               int32_t n_heads, int32_t max_pos, int32_t window,
+                               const hyb_paged* idx_pool, int32_t k, int32_t* out_idx,
+                               void* stream) {
+  const char* op = "hyb_index_topk_noalloc";
+  if (!idx_pool) return fail(HYB_EINVAL, "%s: idx_pool descriptor is NULL", op);
+  const size_t need = hyb_index_topk_workspace_bytes(n_q, max_pos, window, idx_pool->ratio);
+  if (need > (size_t)HYB_NOALLOC_SCRATCH_BYTES)
+    return fail(HYB_EINVAL, "%s: %zu bytes of scratch needed, the static array holds %llu", op, need,
+                (unsigned long long)HYB_NOALLOC_SCRATCH_BYTES);
+  if (n_q <= 0 || need == 0)   // nothing to do, or arguments hyb_index_topk refuses: no lookup
+    return hyb_index_topk(q_idx, q_dtype, w, q_seq, q_pos, n_q, n_heads, max_pos, window, idx_pool,
+                          k, out_idx, nullptr, 0, stream);
+  void* ws = nullptr;
+  HYB_TRY(scratch_address(op, &ws));
+  const int32_t st = hyb_index_topk(q_idx, q_dtype, w, q_seq, q_pos, n_q, n_heads, max_pos, window,
+                                    idx_pool, k, out_idx, ws, (size_t)HYB_NOALLOC_SCRATCH_BYTES, stream);
+  if (st != HYB_OK) {   // name this entry point in the message
+    const std::string msg = g_last_error;
+    return fail(st, "%s: %s", op, msg.c_str());
+  }
+  return HYB_OK;
 }
 
 size_t hyb_attn_decode_workspace_bytes(int32_t batch, int32_t n_heads, int32_t dim,

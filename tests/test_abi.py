@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(hyb.EXPORTS) == names
@@ -298,3 +298,18 @@ def test_window_smaller_than_ratio_is_refused(lib, op):
         st = lib.hyb_topk_keys(FAKE, 4096, FAKE, 2, FAKE, 2, 10000, 100, 128, 64, FAKE, None)
     assert st == hyb.HYB_EINVAL
     assert "window" in lib.hyb_last_error().decode()
+
+
+def test_noalloc_index_topk_refuses_scratch_beyond_the_array(lib):
+    """The allocation-free selector checks its scratch need against the static array on the host,
+    before it looks up any device address: 100000 queries at 2^20 positions need far more."""
+    ip = pool(dim=128, ratio=4)
+    st = lib.hyb_index_topk_noalloc(FAKE, hyb.BF16, FAKE, None, FAKE, 100000, 64, 1 << 20, 128,
+                                    ctypes.byref(ip), 512, FAKE, None)
+    assert st == hyb.HYB_EINVAL
+    assert "scratch" in lib.hyb_last_error().decode()
+    need = lib.hyb_index_topk_workspace_bytes(16, (1 << 20) - 1, 128, 4)
+    assert 0 < need <= hyb.NOALLOC_SCRATCH_BYTES
+    # no queries: nothing to do, nothing looked up
+    assert lib.hyb_index_topk_noalloc(FAKE, hyb.BF16, FAKE, None, FAKE, 0, 64, 1000, 128,
+                                      ctypes.byref(ip), 512, FAKE, None) == hyb.HYB_OK
