@@ -170,6 +170,13 @@ def c4_sparse(torch, hyb, W, BM, args, peak_meas):
             istate=W.to_storage(W.randn((B, 4, 128), g, dev), "bf16"),
         ))
 
+    for d in reps:
+        wl = d["wl"]
+        d["calls"] = [hyb.compress_call(d["x_new"], d["cu"], d["start"], 1, d["state"], wl.comp, 64),
+                      hyb.compress_call(d["ix_new"], d["cu"], d["start"], 1, d["istate"], wl.idx_pool, 64)]
+        d["ws_step"] = torch.zeros(hyb.hyb_decode_step_workspace_bytes(B, 64, 512, L, 4, wl.k),
+                                   dtype=torch.uint8, device=dev)
+
     def score(r):
         d = reps[r]
         wl = d["wl"]
@@ -182,25 +189,21 @@ def c4_sparse(torch, hyb, W, BM, args, peak_meas):
     def attend(r):
         d = reps[r]
         wl = d["wl"]
-        hyb.hyb_attn_decode_compress(wl.q, wl.seq_lens, L, wl.swa, wl.comp, d["out"], d["x_new"],
-                                     d["cu"], d["start"], 1, d["state"], wl.comp,
-                                     topk_idx=d["topk"], k=wl.k, workspace=d["ws"])
-
-    def idx_compress(r):
-        d = reps[r]
-        hyb.hyb_compress(d["ix_new"], d["cu"], d["start"], 1, d["istate"], d["wl"].idx_pool, 64)
+        hyb.hyb_attn_decode(wl.q, wl.seq_lens, L, wl.swa, wl.comp, d["out"], topk_idx=d["topk"],
+                            k=wl.k, workspace=d["ws"])
 
     def step(r):
-        score(r)
-        select(r)
-        attend(r)
-        idx_compress(r)
+        d = reps[r]
+        wl = d["wl"]
+        hyb.hyb_decode_step(wl.q, wl.seq_lens, L, wl.swa, wl.comp, d["out"], idx_q=wl.idx_q,
+                            idx_w=wl.idx_w, idx_pool=wl.idx_pool, k=wl.k, topk_out=d["topk"],
+                            compress=d["calls"], workspace=d["ws_step"])
 
     secs = time_loop(torch, step, args.steps, args.warmup, R)
     n = args.kernel_launches
-    parts_us = {"index_score": kernel_loop(torch, score, n, R), "topk": kernel_loop(torch, select, n, R),
-                "attention_combine_compress": kernel_loop(torch, attend, n, R),
-                "indexer_key_compress": kernel_loop(torch, idx_compress, n, R)}
+    parts_us = {"step": kernel_loop(torch, step, n, R),
+                "index_score": kernel_loop(torch, score, n, R), "topk": kernel_loop(torch, select, n, R),
+                "attention_combine": kernel_loop(torch, attend, n, R)}
     per_tok = BM.decode_query_bytes(L, ratio=4, sparse=True)
     comp_b = BM.compress_decode_bytes(4) + BM.compress_decode_bytes(4, dim=128)
     step_bytes = B * (per_tok.total + comp_b)
@@ -210,7 +213,7 @@ def c4_sparse(torch, hyb, W, BM, args, peak_meas):
         value=B * args.steps / secs, ms_per_step=ms, step_bytes=step_bytes,
         hbm_frac_step=step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         kernel_us=parts_us,
-        roofline=roofline_hbm("score_mfma_dma (indexer scores + top-k hand-off)", score_bytes,
+        roofline=roofline_hbm("score_mfma_reg (indexer scores + top-k hand-off)", score_bytes,
                               parts_us["index_score"], peak_meas, measured_traffic(),
                               handoff_bytes_per_launch=B * BM.handoff_bytes(L),
                               launches_timed=max(50, n)),
@@ -261,19 +264,21 @@ def c128_dense(torch, hyb, W, BM, args, peak_meas):
         reps.append(wl)
     g = W.generator(3, 0, 99, dev)
     extra = [dict(out=torch.empty_like(w.q),
-                  ws=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, D, L, 128, 0), dtype=torch.uint8, device=dev),
+                  ws=torch.zeros(hyb.hyb_decode_step_workspace_bytes(B, 64, D, L, 128, 0), dtype=torch.uint8, device=dev),
                   x_new=W.to_storage(W.randn((B, D), g, dev), "bf16"),
                   lg_new=W.randn((B,), g, dev),
                   state=W.to_storage(W.randn((B, 128, D), g, dev), "bf16"), st_l=W.randn((B, 128), g, dev),
                   cu=torch.arange(0, B + 1, dtype=torch.int32, device=dev),
                   start=torch.full((B,), L - 1, dtype=torch.int32, device=dev)) for w in reps]
 
+    for w, e in zip(reps, extra):
+        e["calls"] = [hyb.compress_call(e["x_new"], e["cu"], e["start"], 1, e["state"], w.comp, 64,
+                                        gate_logits=e["lg_new"], state_logits=e["st_l"])]
+
     def step(r):
         w, e = reps[r], extra[r]
-        hyb.hyb_attn_decode_compress(w.q, w.seq_lens, L, w.swa, w.comp, e["out"], e["x_new"],
-                                     e["cu"], e["start"], 1, e["state"], w.comp,
-                                     gate_logits=e["lg_new"], state_logits=e["st_l"],
-                                     workspace=e["ws"])
+        hyb.hyb_decode_step(w.q, w.seq_lens, L, w.swa, w.comp, e["out"], compress=e["calls"],
+                            workspace=e["ws"])
 
     n = max(args.steps // 2, 20)
     secs = time_loop(torch, step, n, max(args.warmup // 2, 5), R)
@@ -284,7 +289,7 @@ def c128_dense(torch, hyb, W, BM, args, peak_meas):
     return dict(
         value=B * n / secs, unit="query-tokens/s", ms_per_step=ms, steps=n,
         hbm_frac_step=step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-        roofline=roofline_hbm("attention call (attn_mfma, then the combine with the compressor)",
+        roofline=roofline_hbm("C128 decode step (attn_mfma, then the combine with the compressor)",
                               step_bytes, call_us, peak_meas, None,
                               attn_tflops=B * BM.attention_flops(8191 + 128) / (call_us * 1e-6) / 1e12),
         compress_raw_gbs=raw_bytes / comp_secs / 1e9,

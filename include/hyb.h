@@ -348,6 +348,37 @@ int32_t hyb_attn_decode_compress(const void* q, int32_t q_dtype, const int32_t* 
                                  void* stream);
 
 /* --------------------------------------------------------------------------------------------
+ * hyb_decode_step - one whole decode step of a hybrid attention layer for a batch of sequences
+ * (one query token each, at p = seq_lens[b] - 1), with its kernels fused as far as the data flow
+ * allows. [SGLang] "Shadow Radix": each layer is the window plus C4 top-k (sparse) or C128
+ * (dense); [vLLM] "vLLM side": the compressor, indexer and window work of a step overlap.
+ *   C4 layer (comp->ratio 4; q_idx, w and idx_pool given): the results of hyb_index_topk over
+ *     n_vis(p) indexer keys (decode form: the query of sequence b is b at p), written to
+ *     topk_out [batch][k] when that is not NULL, then hyb_attn_decode over those rows;
+ *   C128 layer (comp->ratio 128; q_idx, w and idx_pool NULL): hyb_attn_decode, dense;
+ *   then the n_compress <= 2 compressor calls compress[0 .. n_compress), as hyb_compress (e.g.
+ *     the new tokens into the C4 pool and their indexer-key rows into the indexer-key pool).
+ * The result equals those calls made one after another. The compressor calls may run beside the
+ * indexer or the attention: that is exact because nothing else in the step reads what they write
+ * (the entry a token at p completes is not visible at p, for window >= ratio) or writes what they
+ * read. Their x, state and output pools must not overlap q, out, topk_out or the workspace.
+ * Arguments as in hyb_index_topk (q_idx [batch][idx_heads][idx_pool->dim], w [batch][idx_heads])
+ * and hyb_attn_decode; workspace sized by hyb_decode_step_workspace_bytes with the same batch,
+ * n_heads, dim, max_seq_len, comp ratio, k (ignored for C128) and window.
+ * ------------------------------------------------------------------------------------------ */
+size_t hyb_decode_step_workspace_bytes(int32_t batch, int32_t n_heads, int32_t dim,
+                                       int32_t max_seq_len, int32_t comp_ratio, int32_t k,
+                                       int32_t window);
+int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens, int32_t batch,
+                        int32_t n_heads, int32_t max_seq_len, const hyb_paged* swa,
+                        const hyb_paged* comp, const void* q_idx, int32_t q_idx_dtype,
+                        const float* w, int32_t idx_heads, const hyb_paged* idx_pool, int32_t k,
+                        int32_t* topk_out, int32_t window, float softmax_scale, int32_t rope_dim,
+                        double rope_base, void* out, int32_t out_dtype, float* out_scale,
+                        const hyb_compress_call* compress, int32_t n_compress, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------------
  * hyb_attn_prefill - causal attention for a chunk of query tokens: query i of sequence q_seq[i]
  * at position q_pos[i] attends to its own window and its own top-k row (or, with topk_idx NULL,
  * to every compressed entry visible at q_pos[i]). Same arithmetic and pools as hyb_attn_decode.

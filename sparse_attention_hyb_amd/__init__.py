@@ -34,6 +34,7 @@ EXPORTS = (
     "hyb_index_topk_workspace_bytes", "hyb_index_topk", "hyb_index_topk_noalloc",
     "hyb_attn_decode_workspace_bytes", "hyb_attn_decode", "hyb_attn_decode_compress",
     "hyb_attn_prefill_workspace_bytes", "hyb_attn_prefill",
+    "hyb_decode_step_workspace_bytes", "hyb_decode_step",
     "hyb_probe_granule", "hyb_probe",
 )
 
@@ -108,6 +109,10 @@ _SIGS = {
     "hyb_attn_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "hyb_attn_prefill": (_I32, [_P, _I32, _P, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _I32, _F,
                                 _I32, _D, _P, _I32, _P, _P, _SZ, _P]),
+    "hyb_decode_step_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "hyb_decode_step": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _P, _I32, _PP, _I32,
+                               _P, _I32, _F, _I32, _D, _P, _I32, _P,
+                               ctypes.POINTER(hyb_compress_call), _I32, _P, _SZ, _P]),
     "hyb_probe_granule": (ctypes.c_uint64, [_I32, _I32]),
     "hyb_probe": (_I32, [_I32, _I32, _I32, _P, _P, ctypes.c_uint64, _P, _P, _I32, _I64, _P, _P]),
 }
@@ -380,6 +385,55 @@ def hyb_attn_decode_compress(q, seq_lens, max_seq_len: int, swa_pool, comp_pool,
         ctypes.byref(dc), _ptr(topk_idx), int(k), int(window), scale, int(rope_dim),
         float(rope_base), _ptr(out), _odtype(out, out_scale), _ptr(out_scale), _ptr(workspace),
         workspace.numel() * workspace.element_size(), ctypes.byref(call), _stream(stream)))
+
+
+def compress_call(x, cu_seqlens, start_pos, max_new_tokens: int, state, out_pool, rope_dim: int = 64,
+                  rope_base: float = 10000.0, eps: float = 1e-6, gate_logits=None,
+                  state_logits=None):
+    """The arguments of one hyb_compress call as a hyb_compress_call struct (for the entry points
+    that take compressor calls). Keep the returned object alive until the call is enqueued: it
+    holds the pool descriptor."""
+    _check_state(x, state)
+    d = paged(out_pool)
+    call = hyb_compress_call(
+        x=_ptr(x), x_dtype=_tdtype(x), gate_logits=_ptr(gate_logits), cu_seqlens=_ptr(cu_seqlens),
+        start_pos=_ptr(start_pos), batch=int(start_pos.shape[0]), max_new_tokens=int(max_new_tokens),
+        state=_ptr(state), state_logits=_ptr(state_logits),
+        mode=POOL_SOFTMAX_GATE if gate_logits is not None else POOL_MEAN,
+        out=ctypes.pointer(d), rope_dim=int(rope_dim), rope_base=float(rope_base), eps=float(eps))
+    call._keep = d
+    return call
+
+
+def hyb_decode_step_workspace_bytes(batch: int, n_heads: int, dim: int, max_seq_len: int,
+                                    comp_ratio: int, k: int, window: int = 128) -> int:
+    return int(load().hyb_decode_step_workspace_bytes(int(batch), int(n_heads), int(dim),
+                                                      int(max_seq_len), int(comp_ratio), int(k),
+                                                      int(window)))
+
+
+def hyb_decode_step(q, seq_lens, max_seq_len: int, swa_pool, comp_pool, out, idx_q=None, idx_w=None,
+                    idx_pool=None, k: int = 512, topk_out=None, compress=(), window: int = 128,
+                    softmax_scale: Optional[float] = None, rope_dim: int = 64,
+                    rope_base: float = 10000.0, workspace=None, out_scale=None, stream=None) -> None:
+    """One decode step of a C4 layer (idx_q, idx_w, idx_pool given) or a C128 layer (none), with
+    up to two compressor calls (compress_call(...) structs); see include/hyb.h."""
+    b, h, dim = (int(s) for s in q.shape)
+    scale = float(softmax_scale) if softmax_scale is not None else dim ** -0.5
+    if workspace is None:
+        workspace = _empty_workspace(hyb_decode_step_workspace_bytes(b, h, dim, max_seq_len,
+                                                                     comp_pool.ratio, k, window), q.device)
+    calls = list(compress)
+    arr = (hyb_compress_call * max(1, len(calls)))(*calls) if calls else None
+    ds, dc = paged(swa_pool), paged(comp_pool)
+    di = paged(idx_pool) if idx_pool is not None else None
+    _check(load().hyb_decode_step(
+        _ptr(q), _tdtype(q), _ptr(seq_lens), b, h, int(max_seq_len), ctypes.byref(ds), ctypes.byref(dc),
+        _ptr(idx_q), _tdtype(idx_q) if idx_q is not None else BF16, _ptr(idx_w),
+        int(idx_q.shape[1]) if idx_q is not None else 0, ctypes.byref(di) if di is not None else None,
+        int(k), _ptr(topk_out), int(window), scale, int(rope_dim), float(rope_base), _ptr(out),
+        _odtype(out, out_scale), _ptr(out_scale), arr, len(calls), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def hyb_attn_prefill_workspace_bytes(n_q: int, n_heads: int, dim: int, max_pos: int,

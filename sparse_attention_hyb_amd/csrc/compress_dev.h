@@ -154,12 +154,14 @@ __host__ __device__ inline int pooled_waves(int ratio, int dim) {
 // per virtual wave, ratio / V, are a multiple of kRB, the rows per virtual wave and batch (the
 // launches see to it); lds holds (nw - 1) * dim + 128 floats. kQuant: the pool is FP8_E4M3 or
 // FP4_E2M1 and the entry is quantised as it is stored (float32 pools and bf16 pools otherwise).
-template <typename T, int kVec, int kJ, int kRB, int kV, bool kQuant = false>
+// kNW > 0: only the first kNW waves of the workgroup pool (nw = kNW); the others take part in
+// the group's barrier and nothing else (for workgroups larger than the pooling needs).
+template <typename T, int kVec, int kJ, int kRB, int kV, bool kQuant = false, int kNW = 0>
 __device__ __forceinline__ void compress_group(const CompressArgs& a, int gi, int b, float* lds) {
   constexpr int kW = chunk_words<T, kVec>();
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = blockDim.x >> 6;
+  const int nw = kNW > 0 ? kNW : (blockDim.x >> 6);
   const int V = nw * kV;
   const int r = a.out.ratio;
   const int D = a.out.dim;
@@ -175,6 +177,10 @@ __device__ __forceinline__ void compress_group(const CompressArgs& a, int gi, in
   const int g = g0 + gi;
   if (g > g_last) return;
   const int gstart = g * r;
+  if (kNW > 0 && w >= kNW) {   // not a pooling wave: only the complete group's barrier
+    if (gstart + r <= t_end) __syncthreads();
+    return;
+  }
   const T* x = reinterpret_cast<const T*>(a.x);
   T* ring = reinterpret_cast<T*>(a.state) + (int64_t)b * r * D;
   float2* cs = reinterpret_cast<float2*>(lds + (nw - 1) * D);
@@ -371,6 +377,55 @@ __device__ __forceinline__ void compress_group(const CompressArgs& a, int gi, in
         }
         if (a.mode == 1 && lane == 0) a.state_logits[(int64_t)b * r + slot] = a.gate[c0 + t - s0];
       }
+    }
+  }
+}
+
+}  // namespace hyb
+
+namespace hyb {
+
+// A compressor call that can run as extra workgroups of another launch: four waves pool each
+// group in 16-byte chunks (dim <= 512, a whole number of chunks; x, the ring and the pool 16-byte
+// aligned), ratio 4 or 128. Host side: the launchers decide with this.
+inline bool compress_fusable(const CompressArgs& c) {
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  const int r = c.out.ratio, D = c.out.dim;
+  return c.batch > 0 && c.max_new_tokens > 0 && D <= 512 && D % (c.x_dtype == F32 ? 4 : 8) == 0 &&
+         al16(c.x) && al16(c.state) && al16(c.out.data) && (r == 4 || r == 128) &&
+         (c.out.dtype != FP4 || D % 32 == 0);
+}
+
+// Workgroups one fusable call takes: one per (group touched, sequence).
+inline int compress_fused_groups(const CompressArgs& c) {
+  return ((c.max_new_tokens + c.out.ratio - 1) / c.out.ratio + 1) * c.batch;
+}
+
+// LDS (bytes) of one fused compressor workgroup: three waves' partial sums and the RoPE table.
+constexpr size_t kCompressFusedLds = (3 * 512 + 128) * sizeof(float);
+
+// Workgroup k of a fusable call, run by the first four waves of the calling workgroup (any other
+// waves only take part in the barrier); lds: kCompressFusedLds bytes.
+template <int kNW>
+__device__ __forceinline__ void compress_fused(const CompressArgs& c, int k, float* lds) {
+  const int gx = (c.max_new_tokens + c.out.ratio - 1) / c.out.ratio + 1;
+  const int gi = k % gx, b = k / gx;
+  const bool quant = c.out.dtype == FP8 || c.out.dtype == FP4;
+  if (c.x_dtype == F32) {
+    if (c.out.ratio == 4) {
+      if (quant) compress_group<float, 4, 2, 1, 1, true, kNW>(c, gi, b, lds);
+      else compress_group<float, 4, 2, 1, 1, false, kNW>(c, gi, b, lds);
+    } else {
+      if (quant) compress_group<float, 4, 2, 2, 4, true, kNW>(c, gi, b, lds);
+      else compress_group<float, 4, 2, 2, 4, false, kNW>(c, gi, b, lds);
+    }
+  } else {
+    if (c.out.ratio == 4) {
+      if (quant) compress_group<uint16_t, 8, 1, 1, 1, true, kNW>(c, gi, b, lds);
+      else compress_group<uint16_t, 8, 1, 1, 1, false, kNW>(c, gi, b, lds);
+    } else {
+      if (quant) compress_group<uint16_t, 8, 1, 4, 4, true, kNW>(c, gi, b, lds);
+      else compress_group<uint16_t, 8, 1, 4, 4, false, kNW>(c, gi, b, lds);
     }
   }
 }

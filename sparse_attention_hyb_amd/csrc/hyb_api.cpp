@@ -14,6 +14,7 @@
 
 #include "hyb_internal.h"
 #include "hyb_probe_internal.h"
+#include "compress_dev.h"
 
 namespace {
 
@@ -536,6 +537,129 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
   t.part_hist = a.part_hist;
   t.part_ld = a.part_ld;
   return launch_status(hyb::launch_topk(t, s), op);
+}
+
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of hyb_decode_step: [top-k rows (C4, when the caller keeps none)][indexer hand-off (C4)]
+// [attention partials], each part 256-byte aligned.
+static size_t step_ws_bytes(int32_t batch, int32_t n_heads, int32_t dim, int32_t max_seq_len,
+                            int32_t comp_ratio, int32_t k, int32_t window) {
+  if (batch <= 0 || max_seq_len < 1 || window <= 0 || (comp_ratio != 4 && comp_ratio != 128)) return 0;
+  const int64_t max_pos = (int64_t)max_seq_len - 1;
+  size_t n = 0;
+  if (comp_ratio == 4) {
+    if (k < 1 || k > HYB_KMAX) return 0;
+    n += align256((size_t)batch * k * sizeof(int32_t));
+    n += align256(topk_ws_bytes(batch, (int64_t)score_ld((int32_t)max_pos, window, comp_ratio)));
+  }
+  return n + attn_ws(batch, n_heads, dim, max_pos, comp_ratio, comp_ratio == 4 ? k : 0, window, 0);
+}
+
+size_t hyb_decode_step_workspace_bytes(int32_t batch, int32_t n_heads, int32_t dim,
+                                       int32_t max_seq_len, int32_t comp_ratio, int32_t k,
+                                       int32_t window) {
+  return step_ws_bytes(batch, n_heads, dim, max_seq_len, comp_ratio, k, window);
+}
+
+int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens, int32_t batch,
+                        int32_t n_heads, int32_t max_seq_len, const hyb_paged* swa,
+                        const hyb_paged* comp, const void* q_idx, int32_t q_idx_dtype,
+                        const float* w, int32_t idx_heads, const hyb_paged* idx_pool, int32_t k,
+                        int32_t* topk_out, int32_t window, float softmax_scale, int32_t rope_dim,
+                        double rope_base, void* out, int32_t out_dtype, float* out_scale,
+                        const hyb_compress_call* compress, int32_t n_compress, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const char* op = "hyb_decode_step";
+  if (!seq_lens) return fail(HYB_EINVAL, "%s: seq_lens is NULL", op);
+  if (max_seq_len < 1) return fail(HYB_EINVAL, "%s: max_seq_len %d < 1", op, max_seq_len);
+  if (n_compress < 0 || n_compress > 2) return fail(HYB_EINVAL, "%s: n_compress %d outside [0, 2]", op, n_compress);
+  if (n_compress > 0 && !compress) return fail(HYB_EINVAL, "%s: compress is NULL", op);
+  if (!comp) return fail(HYB_EINVAL, "%s: comp descriptor is NULL", op);
+  const bool sparse = comp->ratio == 4;
+  if (sparse != (q_idx != nullptr))
+    return fail(HYB_EINVAL, "%s: a C4 layer (comp ratio 4) needs the indexer query and a C128 layer none", op);
+  const int64_t max_pos = (int64_t)max_seq_len - 1;
+  hyb::ScoreArgs sa{};
+  if (sparse) {
+    HYB_TRY(check_score(op, q_idx, q_idx_dtype, w, seq_lens, batch, idx_heads, (int32_t)max_pos,
+                        window, idx_pool, &sa));
+    if (k < 1 || k > HYB_KMAX) return fail(HYB_EINVAL, "%s: k %d outside [1, %d]", op, k, HYB_KMAX);
+  }
+  AttnCommon c;
+  int32_t* topk = topk_out;
+  static const int32_t kSelected = 0;   // stands for the step's own top-k rows while checking
+  HYB_TRY(check_attention(op, q, q_dtype, batch, n_heads, swa, comp, sparse ? &kSelected : nullptr, k,
+                          window, softmax_scale, rope_dim, rope_base, out, out_dtype, out_scale,
+                          max_pos, &c));
+  hyb::CompressArgs ca[2];
+  for (int j = 0; j < n_compress; ++j) HYB_TRY(check_compress(op, compress[j], &ca[j]));
+  const size_t need = step_ws_bytes(batch, n_heads, c.args.dim, max_seq_len, comp->ratio, k, window);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(HYB_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", op, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (batch == 0) return HYB_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  hyb::SideWork side{};
+  int n_side = 0;
+  bool done[2] = {false, false};
+  if (sparse) {
+    if (!topk) topk = reinterpret_cast<int32_t*>(ws);
+    ws += align256((size_t)batch * k * sizeof(int32_t));
+    const int64_t ld = (int64_t)score_ld((int32_t)max_pos, window, sa.pool.ratio);
+    if ((int64_t)topk_part_ld(ld) > hyb::kTopkMaxParts)
+      return fail(HYB_ENOTSUP, "%s: %lld visible entries exceed the selector (%d x 1024)", op,
+                  (long long)ld, hyb::kTopkMaxParts);
+    const int64_t pld = pair_words((int64_t)topk_part_ld(ld));
+    sa.qd = hyb::QueryDev{seq_lens, nullptr, nullptr};
+    sa.scores = reinterpret_cast<float*>(ws);
+    sa.ld = pld;
+    sa.part_hist = reinterpret_cast<uint16_t*>(reinterpret_cast<uint32_t*>(ws) + (size_t)batch * pld);
+    sa.part_ld = (int32_t)topk_part_ld(ld);
+    ws += align256(topk_ws_bytes(batch, ld));
+    // compressor calls that four waves can run ride along with the indexer's one-query kernel
+    const bool one_query_kernel = sa.n_heads == 64 && sa.pool.dim == 128 && sa.q_dtype == HYB_BF16 &&
+                                  sa.pool.dtype == HYB_BF16;
+    for (int j = 0; j < n_compress && one_query_kernel; ++j) {
+      if (hyb::compress_fusable(ca[j])) {
+        side.c[n_side] = ca[j];
+        side.n[n_side] = hyb::compress_fused_groups(ca[j]);
+        ++n_side;
+        done[j] = true;
+      }
+    }
+    HYB_TRY(launch_status(hyb::launch_index_score(sa, st, n_side ? &side : nullptr), op));
+    hyb::TopkArgs t{};
+    t.scores = sa.scores;
+    t.ld = pld;
+    t.qd = sa.qd;
+    t.ratio = sa.pool.ratio;
+    t.window = window;
+    t.n_q = batch;
+    t.max_len = (int32_t)visible(max_pos, sa.pool.ratio, window);
+    t.k = k;
+    t.out = topk;
+    t.part_hist = sa.part_hist;
+    t.part_ld = sa.part_ld;
+    HYB_TRY(launch_status(hyb::launch_topk(t, st), op));
+    c.args.topk = topk;
+    c.args.k = k;
+  }
+  HYB_TRY(attach_workspace(op, &c, ws, workspace_bytes - (size_t)(ws - static_cast<char*>(workspace))));
+  c.args.qd = hyb::QueryDev{seq_lens, nullptr, nullptr};
+  int first = -1;   // a C128 layer's first pending call rides along with the combine
+  for (int j = 0; j < n_compress; ++j)
+    if (!done[j]) { first = j; break; }
+  if (!sparse && first >= 0) {
+    HYB_TRY(launch_status(hyb::launch_attention_compress(c.args, ca[first], st), op));
+    done[first] = true;
+  } else {
+    HYB_TRY(launch_status(hyb::launch_attention(c.args, st), op));
+  }
+  for (int j = 0; j < n_compress; ++j)
+    if (!done[j]) HYB_TRY(launch_status(hyb::launch_compress(ca[j], st), op));
+  return HYB_OK;
 }
 
 }  // extern "C"

@@ -52,6 +52,15 @@ struct CompressArgs {
   double theta[64];   // RoPE frequencies base^(-2i / rope_dim), i < rope_dim / 2 (host-formed)
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+
+// Up to two compressor calls riding along as extra workgroups of another launch (the indexer's or
+// the attention's): n[j] workgroups for call j, or 0. A call runs there only when nothing else in
+// that launch reads what it writes or writes what it reads. Kernels take the two calls as two
+// separate arguments (c0, c1): an array indexed at run time would be copied to scratch memory.
+struct SideWork {
+  CompressArgs c[2];
+  int32_t n[2];
+};
 hipError_t launch_swa_insert(const CompressArgs& a, hipStream_t s);
 
 // Query RMSNorm + RoPE of new tokens, with their window entries (kv: the tokens' K=V rows in x,
@@ -92,7 +101,7 @@ struct ScoreArgs {
   uint16_t* part_hist;
   int32_t part_ld;
 };
-hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s, const SideWork* side = nullptr);
 constexpr int kTopBits = 10;                  // the selector's first radix pass (then 11 + 11)
 constexpr int kTopBins = 1 << kTopBits;
 constexpr int kScorePartKeys = 1024;          // keys per partial histogram (one indexer workgroup)

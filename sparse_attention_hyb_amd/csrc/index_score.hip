@@ -19,6 +19,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "compress_dev.h"
 
 namespace hyb {
 
@@ -335,30 +336,48 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// bf16 keys: the same contraction as score_mfma, with the keys streamed into LDS by coalesced
-// direct loads (each load instruction moves 1 KB = four whole key rows) instead of row-wise loads
-// into operand registers; row-wise loads reach only about 5 TB/s on this access pattern.
-// Each wave owns four 8 KB stages (32 keys x 256 B) and keeps three tiles in flight. In a stage,
-// 16-byte chunk c of key n sits at chunk c ^ (n % 16) of its row, so the operand reads (32 keys,
-// one logical chunk) hit 16 different bank groups per 16 lanes; the loads pick their source
-// chunks to match.
-constexpr int kDmaStages = 4;
-
-__global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t stage[kDmaStages][4][8192];
+// bf16 keys, decode form: the contraction of score_mfma with every key tile fetched by fully
+// coalesced loads into registers (eight 16-byte loads per lane, each instruction one contiguous
+// 1 KB = four whole key rows) and passed through the wave's own LDS stage to the MFMA operand
+// layout. A plain streaming read of this GPU's memory reaches about 7.1 TB/s with such loads
+// against 6.0-6.3 TB/s through direct global -> LDS loads. Each wave keeps its next two tiles in
+// flight in registers; the stage holds one tile (chunk c of key n at c ^ (n % 16), conflict-free
+// for both the stores and the operand reads), and since a wave reads only its own stage, the tile
+// loop has no workgroup barrier.
+// kTile: a 32-key tile always lies in one block (256 / ratio >= 32, the C4 case); kHand: hand-off
+// to the selector instead of plain scores. Both are launch-uniform, so the tile loop has no branch.
+// Workgroups: first n_c0 + n_c1 compressor workgroups (the compressor calls c0, c1 riding
+// along, run by this launch's four waves), then one per (key block, query) in query-major order.
+template <bool kTile, bool kHand>
+__global__ __launch_bounds__(256, 1) void score_mfma_reg(ScoreArgs a, CompressArgs c0, CompressArgs c1,
+                                                          int n_c0, int n_c1) {
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[4][8192];
   __shared__ uint32_t lhist[kScoreParts * kTopBins];
   __shared__ int32_t tbl[kScoreKeysPerBlock / 2 + 2];
   __shared__ uint32_t lkeys[kScoreKeysPerBlock];
   __shared__ uint32_t wtot[kScoreParts * 4];
-  const int i = blockIdx.y;
-  const int base = blockIdx.x * kScoreKeysPerBlock;
+  static_assert(sizeof(stage) >= kCompressFusedLds, "a compressor workgroup fits the stages");
+  int bid = blockIdx.x;
+  if (bid < n_c0) {
+    compress_fused<4>(c0, bid, reinterpret_cast<float*>(&stage[0][0]));
+    return;
+  }
+  if (bid < n_c0 + n_c1) {
+    compress_fused<4>(c1, bid - n_c0, reinterpret_cast<float*>(&stage[0][0]));
+    return;
+  }
+  bid -= n_c0 + n_c1;
+  const int max_nv = n_visible(a.max_pos, a.pool.ratio, a.window);
+  const int gx = (max_nv + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock;
+  const int i = bid / gx;
+  const int base = (bid - i * gx) * kScoreKeysPerBlock;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31;
   const int hf = lane >> 5;
   // In decode form the sequence is the query index itself, so the block table of the
-  // workgroup's whole key range is read in parallel with the sequence length (which only bounds
-  // the range); in prefill form the sequence comes from q_seq first.
+  // workgroup's whole key range is read together with the sequence length, the query and the
+  // head weights (all independent loads); in prefill form the sequence comes from q_seq first.
   const int seq = (a.qd.seq_lens || !a.qd.q_seq) ? i : a.qd.q_seq[i];
   const int per_block = a.pool.per_block;   // 256 / ratio: a power of two
   const int pb_shift = __builtin_ctz(per_block);
@@ -370,13 +389,6 @@ __global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
     tbl[j] = (phys >= 0 && phys < a.pool.num_blocks) ? phys : -1;
   }
   const int p = a.qd.seq_lens ? a.qd.seq_lens[i] - 1 : a.qd.q_pos[i];
-  const int nv = min(n_visible(p, a.pool.ratio, a.window), n_visible(a.max_pos, a.pool.ratio, a.window));
-  if (base >= nv) return;   // uniform, before any barrier
-  const int end = min(nv, base + kScoreKeysPerBlock);
-  if (a.part_hist)
-    for (int j = threadIdx.x; j < kScoreParts * kTopBins; j += 256) lhist[j] = 0;
-  __syncthreads();
-
   // operands as in score_mfma: d = 64*hf + 8*s + e, i.e. lane (key col, hf) takes logical chunk
   // 8*hf + s of its key at K-step s
   bf16x8 qa[2][8];
@@ -392,6 +404,12 @@ __global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       wv[mb][r] = a.w[(int64_t)i * kMfmaHeads + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3)];
+  const int nv = min(n_visible(p, a.pool.ratio, a.window), n_visible(a.max_pos, a.pool.ratio, a.window));
+  if (base >= nv) return;   // uniform, before any barrier
+  const int end = min(nv, base + kScoreKeysPerBlock);
+  if (kHand)
+    for (int j = threadIdx.x; j < kScoreParts * kTopBins; j += 256) lhist[j] = 0;
+  __syncthreads();
   float* out = a.scores + (int64_t)i * a.ld;
 
   auto entry_of = [&](int g) -> int64_t {   // entry 0 when the block is absent (scored -inf)
@@ -399,46 +417,46 @@ __global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
     const int phys = tbl[(g >> pb_shift) - lb0];
     return phys >= 0 ? ((int64_t)phys << pb_shift) + (g & (per_block - 1)) : 0;
   };
-  const uint32_t st0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&stage[0][wave][0]);
-  constexpr uint32_t kStageBytes = 4 * 8192;
-  // tile m of this wave: keys base + 32*wave + 128*m + [0, 32)
+  // tile m of this wave: keys base + 32*wave + 128*m + [0, 32); load instruction j brings key
+  // n = 4j + lane/16, logical chunk lane % 16
   const int first = base + 32 * wave;
   const int n_mine = first < end ? (end - first + 127) / 128 : 0;
-  // load instruction j: LDS bytes 1024j + 16*lane <- key n = 4j + lane/16, chunk (lane%16) ^ (n%16)
-  auto issue = [&](int s, int m) {
+  const int nk = lane >> 4, ck = lane & 15;
+  auto load = [&](u32x4 (&r)[8], int m) {
     const int tb = first + 128 * m;
-    int64_t e[8];
-    if (per_block >= 32) {
-      // uniform: the 32-key tile lies in one block; tiles past the end re-read the last tile's
+    if constexpr (kTile) {
+      // the 32-key tile lies in one block; tiles past the end re-read the last tile's
       // block (in bounds, unused)
       const int gb = min(tb, (end - 1) & ~31);
       const int phys = tbl[(gb >> pb_shift) - lb0];
       const int64_t e0 = (phys >= 0 ? ((int64_t)phys << pb_shift) : 0) + (gb & (per_block - 1));
+      const uint8_t* src = a.pool.data + (e0 + nk) * a.pool.entry_bytes + 16 * ck;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = e0 + 4 * j + (lane >> 4);
+      for (int j = 0; j < 8; ++j)
+        r[j] = *reinterpret_cast<const u32x4*>(src + 4 * j * a.pool.entry_bytes);
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = entry_of(tb + 4 * j + (lane >> 4));
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // earlier reads of this stage are done
-    const uint32_t lds = st0 + s * kStageBytes;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = 4 * j + (lane >> 4);
-      const int c = (lane & 15) ^ (n & 15);
-      lds_dma16(a.pool.data + e[j] * a.pool.entry_bytes + 16 * c, lds + 1024 * j);
+      for (int j = 0; j < 8; ++j)
+        r[j] = *reinterpret_cast<const u32x4*>(a.pool.data + entry_of(tb + 4 * j + nk) * a.pool.entry_bytes + 16 * ck);
     }
   };
-  // operand read offsets (bytes within a stage): key col, chunk (8hf + s) ^ (col % 16)
+  uint8_t* st = &stage[wave][0];
+  auto publish = [&](const u32x4 (&r)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = 4 * j + nk;
+      *reinterpret_cast<u32x4*>(st + n * 256 + 16 * (ck ^ (n & 15))) = r[j];
+    }
+  };
+  // operand read offsets: key col, chunk (8hf + s) ^ (col % 16)
   uint32_t roff[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) roff[s] = wave * 8192 + col * 256 + 16 * ((8 * hf + s) ^ (col & 15));
-  auto score = [&](int st, int m) {
-    const uint8_t* sb = &stage[st][0][0];
+  for (int s = 0; s < 8; ++s) roff[s] = col * 256 + 16 * ((8 * hf + s) ^ (col & 15));
+  auto score = [&](int m) {
     f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(sb + roff[s]);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(st + roff[s]);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], b, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], b, acc1, 0, 0, 0);
     }
@@ -453,7 +471,7 @@ __global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
     if (hf == 0 && g < end) {
       const bool valid = tbl[(g >> pb_shift) - lb0] >= 0;
       const float v = valid ? canonical_zero(part) : -INFINITY;
-      if (a.part_hist) {
+      if constexpr (kHand) {
         const uint32_t key = order_key(v);
         lkeys[g - base] = key;
         atomicAdd(&lhist[((g - base) / kScorePartKeys) * kTopBins + (key >> (32 - kTopBits))], 1u);
@@ -463,32 +481,23 @@ __global__ __launch_bounds__(256, 1) void score_mfma_dma(ScoreArgs a) {
     }
   };
   if (n_mine > 0) {
-    // three tiles in flight; tiles past the wave's last one load clamped (real) rows, unused
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
-    for (int m = 0; m < n_mine; m += 4) {
-      issue(3, m + 3);
-      wait_vmcnt<24>();
-      score(0, m);
-      if (m + 1 >= n_mine) break;
-      issue(0, m + 4);
-      wait_vmcnt<24>();
-      score(1, m + 1);
-      if (m + 2 >= n_mine) break;
-      issue(1, m + 5);
-      wait_vmcnt<24>();
-      score(2, m + 2);
-      if (m + 3 >= n_mine) break;
-      issue(2, m + 6);
-      wait_vmcnt<24>();
-      score(3, m + 3);
+    // two tiles in flight in registers while one is staged and multiplied
+    // (an odd count runs one more tile of clamped rows, whose keys score() drops)
+    u32x4 ra[8], rb[8];
+    load(ra, 0);
+    load(rb, 1);
+    for (int m = 0; m < n_mine; m += 2) {
+      publish(ra);
+      load(ra, m + 2);
+      score(m);
+      publish(rb);
+      load(rb, m + 3);
+      score(m + 1);
     }
   }
-  wait_vmcnt<0>();   // no load may still be writing this workgroup's LDS when it exits
-  if (a.part_hist)   // the stages are free now: the sorted pairs use them
-    finish_parts<kScoreParts>(a, i, blockIdx.x * kScoreParts, base, end, lkeys, lhist,
-                              reinterpret_cast<uint2*>(&stage[0][0][0]), wtot);
+  if constexpr (kHand)   // the stages are free now: the sorted pairs use them
+    finish_parts<kScoreParts>(a, i, base / kScorePartKeys, base, end, lkeys, lhist,
+                              reinterpret_cast<uint2*>(&stage[0][0]), wtot);
 }
 
 // Prefill form, bf16 keys: four query tokens per workgroup, one per wave, share every key tile.
@@ -713,10 +722,16 @@ __global__ __launch_bounds__(256) void score_generic(ScoreArgs a) {
     finish_parts<1>(a, i, blockIdx.x, base, min(nv, base + kScorePartKeys), lkeys, lhist, lsorted, wtot);
 }
 
-hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s) {
+hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s, const SideWork* side) {
   const int max_nv = (a.max_pos - a.window + 1 > 0)
                          ? (a.max_pos - a.window + 1 + a.pool.ratio - 1) / a.pool.ratio
                          : 0;
+  SideWork none{};
+  const SideWork& sw = side ? *side : none;
+  const int n_side = sw.n[0] + sw.n[1];
+  if (n_side > 0 && (max_nv == 0 || a.n_q == 0 || a.pool.dtype != BF16 || a.n_heads != kMfmaHeads ||
+                     a.pool.dim != kMfmaDim || a.q_dtype != BF16 || (a.qd.q_seq && a.n_q >= kMultiMinQueries)))
+    return hipErrorInvalidValue;   // the caller offers side work only to the one-query bf16 kernel
   if (max_nv == 0 || a.n_q == 0) return hipSuccess;
   const bool mfma = a.n_heads == kMfmaHeads && a.pool.dim == kMfmaDim && a.q_dtype == BF16 &&
                     (a.pool.dtype == BF16 || a.pool.dtype == FP4);
@@ -728,7 +743,16 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s) {
       grid.y = (a.n_q + kMQ - 1) / kMQ;
       hipLaunchKernelGGL(score_mfma_multi, grid, dim3(256), 0, s, a);
     } else if (a.pool.dtype == BF16) {
-      hipLaunchKernelGGL(score_mfma_dma, grid, dim3(256), 0, s, a);
+      const bool tile = a.pool.per_block >= 32, hand = a.part_hist != nullptr;
+      const dim3 g1(n_side + grid.x * grid.y);
+      if (tile && hand)
+        hipLaunchKernelGGL((score_mfma_reg<true, true>), g1, dim3(256), 0, s, a, sw.c[0], sw.c[1], sw.n[0], sw.n[1]);
+      else if (tile)
+        hipLaunchKernelGGL((score_mfma_reg<true, false>), g1, dim3(256), 0, s, a, sw.c[0], sw.c[1], sw.n[0], sw.n[1]);
+      else if (hand)
+        hipLaunchKernelGGL((score_mfma_reg<false, true>), g1, dim3(256), 0, s, a, sw.c[0], sw.c[1], sw.n[0], sw.n[1]);
+      else
+        hipLaunchKernelGGL((score_mfma_reg<false, false>), g1, dim3(256), 0, s, a, sw.c[0], sw.c[1], sw.n[0], sw.n[1]);
     } else {
       hipLaunchKernelGGL(score_mfma<true>, grid, dim3(256), 0, s, a);
     }

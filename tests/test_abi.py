@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(hyb.EXPORTS) == names
@@ -313,3 +313,28 @@ def test_noalloc_index_topk_refuses_scratch_beyond_the_array(lib):
     # no queries: nothing to do, nothing looked up
     assert lib.hyb_index_topk_noalloc(FAKE, hyb.BF16, FAKE, None, FAKE, 0, 64, 1000, 128,
                                       ctypes.byref(ip), 512, FAKE, None) == hyb.HYB_OK
+
+
+def test_decode_step_validation(lib):
+    """hyb_decode_step checks on the host: a C4 layer needs the indexer query, a C128 layer none;
+    at most two compressor calls; the workspace covers the step (selector rows, hand-off and
+    attention partials)."""
+    swa, c4, c128, ip = pool(ratio=1), pool(ratio=4), pool(ratio=128), pool(dim=128, ratio=4)
+
+    def call(comp=c4, q_idx=FAKE, n_comp=0, ws=1 << 40, k=512, idx=ip):
+        return lib.hyb_decode_step(FAKE, hyb.BF16, FAKE, 4, 64, 100000, ctypes.byref(swa),
+                                   ctypes.byref(comp), q_idx, hyb.BF16, FAKE, 64,
+                                   ctypes.byref(idx) if idx is not None else None, k, None, 128,
+                                   0.04, 64, 1e4, FAKE, hyb.BF16, None, None, n_comp, FAKE, ws, None)
+
+    assert call(q_idx=None) == hyb.HYB_EINVAL                 # C4 without the indexer
+    assert call(comp=c128) == hyb.HYB_EINVAL                  # C128 with an indexer query
+    assert call(n_comp=3) == hyb.HYB_EINVAL
+    assert call(n_comp=1) == hyb.HYB_EINVAL                   # compress NULL
+    assert call(k=0) == hyb.HYB_EINVAL
+    need = lib.hyb_decode_step_workspace_bytes(4, 64, 512, 100000, 4, 512, 128)
+    assert need > lib.hyb_attn_decode_workspace_bytes(4, 64, 512, 100000, 4, 512, 128)
+    assert call(ws=need - 1) == hyb.HYB_EWORKSPACE
+    assert lib.hyb_last_error().decode().startswith("hyb_decode_step")
+    assert lib.hyb_decode_step_workspace_bytes(4, 64, 512, 100000, 128, 0, 128) == \
+        lib.hyb_attn_decode_workspace_bytes(4, 64, 512, 100000, 128, 0, 128)

@@ -1,0 +1,129 @@
+"""hyb_decode_step: a whole decode step of a C4 layer (indexer, top-k, attention, the new tokens
+compressed into the C4 pool and into the indexer-key pool) or of a C128 layer (attention, the new
+tokens compressed with softmax gates) in one call. Its results equal the separate calls made one
+after another, bit for bit (outputs, top-k rows, pools and compressor rings), and sampled
+sequences match the float64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_hyb_amd import workloads as W
+from tests.conftest import to_f64, to_oracle_pool
+from tests.parity_util import assert_abs_close, check_topk_set, topk_delta
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+I32 = torch.int32
+
+
+def _rings(B, D, r, dtype, g):
+    return W.to_storage(W.randn((B, r, D), g, DEV), "bf16" if dtype == torch.bfloat16 else "f32")
+
+
+def _clone_pool(p):
+    return W.PagedTensors(p.data.clone(), None if p.scale is None else p.scale.clone(),
+                          p.block_table, p.dtype, p.dim, p.ratio)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_c4_decode_step_equals_separate_calls(gpu_lib, dtype):
+    """Five sequences (two complete a group on this token), bf16 or fp8 attention pools (the
+    compressor quantises its new entries into the fp8 pool as it stores them), bf16 indexer keys."""
+    hyb = gpu_lib
+    lens = [4096, 8191, 20000, 65535, 131072]
+    wl = W.sparse_decode(DEV, seed=21, batch=len(lens), ctx=lens, dtype=dtype)
+    B, D, L = wl.batch, wl.dim, wl.max_seq_len
+    g = W.generator(95, 0, 0, DEV)
+    x = W.to_storage(W.randn((B, D), g, DEV), "bf16")
+    xi = W.to_storage(W.randn((B, 128), g, DEV), "bf16")
+    ring, iring = _rings(B, D, 4, torch.bfloat16, g), _rings(B, 128, 4, torch.bfloat16, g)
+    cu = torch.arange(0, B + 1, dtype=I32, device=DEV)
+    start = (wl.seq_lens - 1).contiguous()
+    comp0, idx0, ring0, iring0 = _clone_pool(wl.comp), _clone_pool(wl.idx_pool), ring.clone(), iring.clone()
+
+    # separate calls
+    topk_a = torch.full((B, wl.k), -7, dtype=I32, device=DEV)
+    out_a = torch.empty_like(wl.q)
+    hyb.hyb_index_topk(wl.idx_q, wl.idx_w, start, L - 1, wl.idx_pool, wl.k, topk_a)
+    hyb.hyb_attn_decode(wl.q, wl.seq_lens, L, wl.swa, wl.comp, out_a, topk_idx=topk_a, k=wl.k)
+    hyb.hyb_compress(x, cu, start, 1, ring, wl.comp, 64)
+    hyb.hyb_compress(xi, cu, start, 1, iring, wl.idx_pool, 64)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (out_a, topk_a, wl.comp.data, wl.idx_pool.data, ring, iring)]
+    want_scale = None if wl.comp.scale is None else wl.comp.scale.clone()
+
+    # one step, from the same starting pools and rings
+    wl.comp.data.copy_(comp0.data)
+    if wl.comp.scale is not None:
+        wl.comp.scale.copy_(comp0.scale)
+    wl.idx_pool.data.copy_(idx0.data)
+    ring.copy_(ring0)
+    iring.copy_(iring0)
+    topk_b = torch.full((B, wl.k), -9, dtype=I32, device=DEV)
+    out_b = torch.empty_like(wl.q)
+    calls = [hyb.compress_call(x, cu, start, 1, ring, wl.comp, 64),
+             hyb.compress_call(xi, cu, start, 1, iring, wl.idx_pool, 64)]
+    ws = torch.zeros(hyb.hyb_decode_step_workspace_bytes(B, 64, D, L, 4, wl.k), dtype=torch.uint8, device=DEV)
+    hyb.hyb_decode_step(wl.q, wl.seq_lens, L, wl.swa, wl.comp, out_b, idx_q=wl.idx_q, idx_w=wl.idx_w,
+                        idx_pool=wl.idx_pool, k=wl.k, topk_out=topk_b, compress=calls, workspace=ws)
+    torch.cuda.synchronize()
+    got = [out_b, topk_b, wl.comp.data, wl.idx_pool.data, ring, iring]
+    for n, (a, b) in enumerate(zip(want, got)):
+        assert torch.equal(a, b), n
+    if want_scale is not None:
+        assert torch.equal(want_scale, wl.comp.scale)
+    assert not torch.equal(want[2], comp0.data)   # groups were completed and stored
+
+    # sampled sequences against the oracle (selection and attention over the pools as drawn)
+    swa_o, comp_o, idx_o = to_oracle_pool(wl.swa), to_oracle_pool(comp0), to_oracle_pool(idx0)
+    iq, iw, q = to_f64(wl.idx_q), wl.idx_w.cpu().double().numpy(), to_f64(wl.q)
+    for s in (1, 4):
+        p = lens[s] - 1
+        keys = O.pool_entries(idx_o, s, range(O.n_visible(p, 4, 128)))
+        sc = O.indexer_scores(iq[s], iw[s], keys)
+        sel = O.topk_select(sc, wl.k)
+        check_topk_set(topk_b[s].cpu().numpy(), sel, sc, topk_delta(iq[s], iw[s], keys), wl.k)
+        if list(topk_b[s].cpu().numpy()) == list(sel):
+            o = O.hybrid_query(q[s], p, s, swa_o, comp_o, 128, 1 / math.sqrt(D), 64, 1e4, sel)
+            assert_abs_close(to_f64(out_b[s]), o)
+
+
+def test_c128_decode_step_equals_separate_calls(gpu_lib):
+    """Four sequences of C128 dense decode (entries drawn), a softmax-gate compression of the new
+    tokens (two of them complete a group)."""
+    hyb = gpu_lib
+    lens = [2048, 40959, 300000, 131072]
+    wl = W.dense_decode(DEV, seed=22, batch=len(lens), ctx=lens)
+    B, D, L = wl.batch, wl.dim, wl.max_seq_len
+    g = W.generator(94, 0, 0, DEV)
+    x = W.to_storage(W.randn((B, D), g, DEV), "bf16")
+    lg = W.randn((B,), g, DEV)
+    ring, rl = _rings(B, D, 128, torch.bfloat16, g), W.randn((B, 128), g, DEV)
+    cu = torch.arange(0, B + 1, dtype=I32, device=DEV)
+    start = (wl.seq_lens - 1).contiguous()
+    comp0, ring0, rl0 = wl.comp.data.clone(), ring.clone(), rl.clone()
+    out_a = torch.empty_like(wl.q)
+    hyb.hyb_attn_decode(wl.q, wl.seq_lens, L, wl.swa, wl.comp, out_a)
+    hyb.hyb_compress(x, cu, start, 1, ring, wl.comp, 64, gate_logits=lg, state_logits=rl)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (out_a, wl.comp.data, ring, rl)]
+    wl.comp.data.copy_(comp0)
+    ring.copy_(ring0)
+    rl.copy_(rl0)
+    out_b = torch.empty_like(wl.q)
+    calls = [hyb.compress_call(x, cu, start, 1, ring, wl.comp, 64, gate_logits=lg, state_logits=rl)]
+    hyb.hyb_decode_step(wl.q, wl.seq_lens, L, wl.swa, wl.comp, out_b, compress=calls)
+    torch.cuda.synchronize()
+    for n, (a, b) in enumerate(zip(want, [out_b, wl.comp.data, ring, rl])):
+        assert torch.equal(a, b), n
+    assert not torch.equal(want[1], comp0)
+    swa_o = to_oracle_pool(wl.swa)
+    comp_o = to_oracle_pool(W.PagedTensors(comp0, None, wl.comp.block_table, "bf16", D, 128))
+    q = to_f64(wl.q)
+    for s in (0, 2):
+        o = O.hybrid_query(q[s], lens[s] - 1, s, swa_o, comp_o, 128, 1 / math.sqrt(D), 64, 1e4, None)
+        assert_abs_close(to_f64(out_b[s]), o)
