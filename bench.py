@@ -161,7 +161,7 @@ def c4_sparse(torch, hyb, W, BM, args, peak_meas):
             hist=torch.empty(hshape, dtype=torch.int16, device=dev),
             topk=torch.empty(B, wl.k, dtype=torch.int32, device=dev),
             out=torch.empty_like(wl.q),
-            ws=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, L, 4, wl.k), dtype=torch.uint8, device=dev),
+            ws=torch.zeros(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, L, 4, wl.k), dtype=torch.uint8, device=dev),
             x_new=W.to_storage(W.randn((B, 512), g, dev), "bf16"),
             cu=torch.arange(0, B + 1, dtype=torch.int32, device=dev),
             start=torch.full((B,), L - 1, dtype=torch.int32, device=dev),
@@ -309,8 +309,8 @@ def prefill(torch, hyb, W, BM, args):
     max_pos = wl.prior + n - 1
     topk = torch.empty(n, wl.k, dtype=torch.int32, device=dev)
     out = torch.empty_like(wl.q)
-    ws_i = torch.empty(hyb.hyb_index_topk_workspace_bytes(n, max_pos, 128, 4), dtype=torch.uint8, device=dev)
-    ws_a = torch.empty(hyb.hyb_attn_prefill_workspace_bytes(n, 64, D, max_pos, 4, wl.k), dtype=torch.uint8, device=dev)
+    ws_i = torch.zeros(hyb.hyb_index_topk_workspace_bytes(n, max_pos, 128, 4), dtype=torch.uint8, device=dev)
+    ws_a = torch.zeros(hyb.hyb_attn_prefill_workspace_bytes(n, 64, D, max_pos, 4, wl.k), dtype=torch.uint8, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
     def step():
@@ -359,8 +359,8 @@ def multi_decode(torch, hyb, W, BM, args):
         n = wl.n_q
         reps.append(dict(
             wl=wl, topk=torch.empty(n, wl.k, dtype=torch.int32, device=dev), out=torch.empty_like(wl.q),
-            ws_i=torch.empty(hyb.hyb_index_topk_workspace_bytes(n, L - 1, 128, 4), dtype=torch.uint8, device=dev),
-            ws_a=torch.empty(hyb.hyb_attn_prefill_workspace_bytes(n, 64, 512, L - 1, 4, wl.k), dtype=torch.uint8, device=dev),
+            ws_i=torch.zeros(hyb.hyb_index_topk_workspace_bytes(n, L - 1, 128, 4), dtype=torch.uint8, device=dev),
+            ws_a=torch.zeros(hyb.hyb_attn_prefill_workspace_bytes(n, 64, 512, L - 1, 4, wl.k), dtype=torch.uint8, device=dev),
             cu=torch.arange(0, (B + 1) * T, T, dtype=torch.int32, device=dev),
             start=torch.full((B,), L - T, dtype=torch.int32, device=dev),
             state=torch.zeros(B, 4, 512, dtype=wl.x_new.dtype, device=dev)))
@@ -452,7 +452,7 @@ def full_step(torch, hyb, W, BM, args):
             seq_lens=wl.seq_lens, cu=torch.arange(0, B + 1, dtype=torch.int32, device=dev),
             start=(wl.seq_lens - 1).contiguous(), swa=wl.swa, comp=wl.comp,
             state=W.to_storage(W.randn((B, 4, 512), g, dev), "bf16"), out=torch.empty_like(wl.q),
-            workspace=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, L, 4, wl.k),
+            workspace=torch.zeros(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, L, 4, wl.k),
                                   dtype=torch.uint8, device=dev),
             max_seq_len=L, idx_q=wl.idx_q, idx_w=wl.idx_w, idx_pool=wl.idx_pool,
             keys=torch.empty(kshape, dtype=torch.int32, device=dev),
@@ -497,7 +497,7 @@ def offload_decode(torch, hyb, W, BM, args):
     hist = torch.empty(hshape, dtype=torch.int16, device=dev)
     topk = torch.empty(B, wl.k, dtype=torch.int32, device=dev)
     out = torch.empty_like(wl.q)
-    ws = torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, L, 4, wl.k), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, L, 4, wl.k), dtype=torch.uint8, device=dev)
     qpos = (wl.seq_lens - 1).contiguous()
     pool = off.pool()
     n_steps = 20
@@ -547,9 +547,9 @@ def quant_mixed(torch, hyb, W, BM, args, peak_meas):
             topk=torch.empty(B, c4.k, dtype=torch.int32, device=dev),
             o4=torch.empty_like(c4.q), o128=torch.empty_like(c128.q),
             qpos=(c4.seq_lens - 1).contiguous(),
-            ws_i=torch.empty(hyb.hyb_index_topk_workspace_bytes(B, max_len - 1, 128, 4), dtype=torch.uint8, device=dev),
-            ws4=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, max_len, 4, c4.k), dtype=torch.uint8, device=dev),
-            ws128=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, max_len, 128, 0), dtype=torch.uint8, device=dev)))
+            ws_i=torch.zeros(hyb.hyb_index_topk_workspace_bytes(B, max_len - 1, 128, 4), dtype=torch.uint8, device=dev),
+            ws4=torch.zeros(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, max_len, 4, c4.k), dtype=torch.uint8, device=dev),
+            ws128=torch.zeros(hyb.hyb_attn_decode_workspace_bytes(B, 64, 512, max_len, 128, 0), dtype=torch.uint8, device=dev)))
 
     def step4(r):
         (c4, _), d = reps[r], bufs[r]

@@ -262,9 +262,11 @@ int32_t hyb_topk_keys(const uint32_t* keys, int64_t keys_ld, const uint16_t* par
 /* --------------------------------------------------------------------------------------------
  * hyb_index_topk - hyb_index_score followed by hyb_topk over n_vis(q_pos[i]) entries; the
  * scores live in the workspace (size from hyb_index_topk_workspace_bytes with the same n_q,
- * max_pos, window and ratio) in the hand-off form of hyb_index_score_keys. At most 4096 * 1024
- * visible entries (HYB_ENOTSUP beyond). The workspace needs no initialisation; its contents are
- * undefined after the call.
+ * max_pos, window and ratio) in the hand-off form of hyb_index_score_keys, after a block of
+ * per-row counts (1 MiB at the workspace's start) that the indexer adds to and the selector reads:
+ * those bytes must be zero before the workspace's first use (allocate it zeroed once), and every
+ * call leaves them zero, so the workspace can be reused for calls of any size, on one stream at a
+ * time (also from a captured graph). At most 4096 * 1024 visible entries (HYB_ENOTSUP beyond).
  * ------------------------------------------------------------------------------------------ */
 size_t hyb_index_topk_workspace_bytes(int32_t n_q, int32_t max_pos, int32_t window,
                                       int32_t ratio);
@@ -283,6 +285,8 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
  * (HYB_EINVAL otherwise; 64 MiB holds e.g. 16 queries at 2^20 positions or 64 at 2^18). Every
  * call on one GPU shares that GPU's array and its contents persist between calls: calls that
  * overlap on one GPU (other streams, other host threads) race, and the caller must order them.
+ * The array starts at zero, and every call leaves the 1 MiB of per-row counts at its start zero
+ * again, as hyb_index_topk needs.
  * The first call on a device looks up the array's address with that device current
  * (HYB_ELAUNCH if that fails).
  * ------------------------------------------------------------------------------------------ */
@@ -364,7 +368,9 @@ int32_t hyb_attn_decode_compress(const void* q, int32_t q_dtype, const int32_t* 
  * read. Their x, state and output pools must not overlap q, out, topk_out or the workspace.
  * Arguments as in hyb_index_topk (q_idx [batch][idx_heads][idx_pool->dim], w [batch][idx_heads])
  * and hyb_attn_decode; workspace sized by hyb_decode_step_workspace_bytes with the same batch,
- * n_heads, dim, max_seq_len, comp ratio, k (ignored for C128) and window.
+ * n_heads, dim, max_seq_len, comp ratio, k (ignored for C128) and window. A C4 step's workspace,
+ * like hyb_index_topk's, starts with 1 MiB that must be zero before its first use (every call
+ * leaves it zero).
  * ------------------------------------------------------------------------------------------ */
 size_t hyb_decode_step_workspace_bytes(int32_t batch, int32_t n_heads, int32_t dim,
                                        int32_t max_seq_len, int32_t comp_ratio, int32_t k,

@@ -189,8 +189,10 @@ def _check_state(x, state) -> None:
 
 
 def _empty_workspace(nbytes: int, device):
+    """A workspace for one call: zeroed, as the attention entry points need their split counters
+    zero before a workspace's first use (include/hyb.h)."""
     import torch
-    return torch.empty(max(1, int(nbytes)), dtype=torch.uint8, device=device)
+    return torch.zeros(max(1, int(nbytes)), dtype=torch.uint8, device=device)
 
 
 # ---------------------------------------------------------------------------------------------

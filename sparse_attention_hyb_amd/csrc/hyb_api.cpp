@@ -492,9 +492,10 @@ static size_t topk_ws_bytes(int32_t n_q, int64_t ld) {
          (size_t)n_q * topk_part_ld(ld) * hyb::kTopBins * sizeof(uint16_t);
 }
 
+// Workspace of hyb_index_topk: [per-row bin counts, kRowHistBytes, zero between calls][hand-off].
 size_t hyb_index_topk_workspace_bytes(int32_t n_q, int32_t max_pos, int32_t window, int32_t ratio) {
   if (n_q <= 0 || max_pos < 0 || window <= 0 || (ratio != 4 && ratio != 128)) return 0;
-  return topk_ws_bytes(n_q, (int64_t)score_ld(max_pos, window, ratio));
+  return hyb::kRowHistBytes + topk_ws_bytes(n_q, (int64_t)score_ld(max_pos, window, ratio));
 }
 
 int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const int32_t* q_seq,
@@ -517,10 +518,12 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
                 (long long)ld, hyb::kTopkMaxParts);
   const int64_t pld = pair_words((int64_t)topk_part_ld(ld));
   a.qd = hyb::QueryDev{nullptr, q_seq, q_pos};
-  a.scores = static_cast<float*>(workspace);
+  uint32_t* hand = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + hyb::kRowHistBytes);
+  a.scores = reinterpret_cast<float*>(hand);
   a.ld = pld;
-  a.part_hist = reinterpret_cast<uint16_t*>(static_cast<uint32_t*>(workspace) + (size_t)n_q * pld);
+  a.part_hist = reinterpret_cast<uint16_t*>(hand + (size_t)n_q * pld);
   a.part_ld = (int32_t)topk_part_ld(ld);
+  a.row_hist = n_q <= hyb::kRowHistRows ? static_cast<uint32_t*>(workspace) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   HYB_TRY(launch_status(hyb::launch_index_score(a, s), op));
   hyb::TopkArgs t{};
@@ -536,13 +539,15 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
   t.out = out_idx;
   t.part_hist = a.part_hist;
   t.part_ld = a.part_ld;
+  t.row_hist = a.row_hist;
   return launch_status(hyb::launch_topk(t, s), op);
 }
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-// Workspace of hyb_decode_step: [top-k rows (C4, when the caller keeps none)][indexer hand-off (C4)]
-// [attention partials], each part 256-byte aligned.
+// Workspace of hyb_decode_step: [per-row bin counts of the selector (C4; zero between calls)]
+// [top-k rows (C4, when the caller keeps none)][indexer hand-off (C4)][attention partials], each
+// part 256-byte aligned.
 static size_t step_ws_bytes(int32_t batch, int32_t n_heads, int32_t dim, int32_t max_seq_len,
                             int32_t comp_ratio, int32_t k, int32_t window) {
   if (batch <= 0 || max_seq_len < 1 || window <= 0 || (comp_ratio != 4 && comp_ratio != 128)) return 0;
@@ -550,6 +555,7 @@ static size_t step_ws_bytes(int32_t batch, int32_t n_heads, int32_t dim, int32_t
   size_t n = 0;
   if (comp_ratio == 4) {
     if (k < 1 || k > HYB_KMAX) return 0;
+    n += hyb::kRowHistBytes;
     n += align256((size_t)batch * k * sizeof(int32_t));
     n += align256(topk_ws_bytes(batch, (int64_t)score_ld((int32_t)max_pos, window, comp_ratio)));
   }
@@ -605,6 +611,8 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
   int n_side = 0;
   bool done[2] = {false, false};
   if (sparse) {
+    uint32_t* row_hist = reinterpret_cast<uint32_t*>(ws);
+    ws += hyb::kRowHistBytes;
     if (!topk) topk = reinterpret_cast<int32_t*>(ws);
     ws += align256((size_t)batch * k * sizeof(int32_t));
     const int64_t ld = (int64_t)score_ld((int32_t)max_pos, window, sa.pool.ratio);
@@ -617,10 +625,11 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
     sa.ld = pld;
     sa.part_hist = reinterpret_cast<uint16_t*>(reinterpret_cast<uint32_t*>(ws) + (size_t)batch * pld);
     sa.part_ld = (int32_t)topk_part_ld(ld);
+    sa.row_hist = batch <= hyb::kRowHistRows ? row_hist : nullptr;
     ws += align256(topk_ws_bytes(batch, ld));
     // compressor calls that four waves can run ride along with the indexer's one-query kernel
     const bool one_query_kernel = sa.n_heads == 64 && sa.pool.dim == 128 && sa.q_dtype == HYB_BF16 &&
-                                  sa.pool.dtype == HYB_BF16;
+                                  (sa.pool.dtype == HYB_BF16 || sa.pool.dtype == HYB_FP4_E2M1);
     for (int j = 0; j < n_compress && one_query_kernel; ++j) {
       if (hyb::compress_fusable(ca[j])) {
         side.c[n_side] = ca[j];
@@ -642,6 +651,7 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
     t.out = topk;
     t.part_hist = sa.part_hist;
     t.part_ld = sa.part_ld;
+    t.row_hist = sa.row_hist;
     HYB_TRY(launch_status(hyb::launch_topk(t, st), op));
     c.args.topk = topk;
     c.args.k = k;

@@ -100,12 +100,18 @@ struct ScoreArgs {
   // as uint2 at kScorePartKeys * part.
   uint16_t* part_hist;
   int32_t part_ld;
+  // Optional, with part_hist: per-query bin counts of the top kTopBits key bits over the whole row,
+  // uint32 [n_q][kTopBins], zero before the call; the hand-off adds each part's counts (the
+  // selector reads the row's first-pass bin from it and zeroes it again).
+  uint32_t* row_hist;
 };
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s, const SideWork* side = nullptr);
 constexpr int kTopBits = 10;                  // the selector's first radix pass (then 11 + 11)
 constexpr int kTopBins = 1 << kTopBits;
 constexpr int kScorePartKeys = 1024;          // keys per partial histogram (one indexer workgroup)
 constexpr int kTopkMaxParts = 4096;           // parts per row the hand-off selector takes
+constexpr int kRowHistRows = 256;             // queries of one call with a per-row histogram
+constexpr size_t kRowHistBytes = (size_t)kRowHistRows * kTopBins * sizeof(uint32_t);
 
 // ---- top-k ----------------------------------------------------------------------------------
 // Row lengths come from `lengths` or, if null, from n_visible(p_i, ratio, window) of the queries.
@@ -124,6 +130,9 @@ struct TopkArgs {
   // index) pairs and these cumulative histograms give the first radix pass.
   const uint16_t* part_hist;
   int32_t part_ld;
+  // Optional, with part_hist: the indexer's per-row bin counts (ScoreArgs::row_hist); the selector
+  // zeroes each row after reading it.
+  uint32_t* row_hist;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 

@@ -4,13 +4,13 @@
 // indexer cache) and the SGLang DeepSeek-V4 day-0 blog ("Shadow Radix": C4 keeps the top-512 of
 // the indexer's scores).
 //
-// Two kernels:
-//  * score_mfma: 64 heads x 128 dims, bf16 query, bf16 or fp4 (E2M1 + E8M0 per 32) keys. The
-//    step streams every visible key once (the step's dominant HBM traffic), so each wave reads
-//    its 32-key tiles straight into MFMA operand registers: no LDS round trip. S = Q . K^T runs on
-//    v_mfma_f32_32x32x16_bf16 with the 64 heads as the M dimension (two 32-row blocks) and the 32
-//    keys as N; each lane then owns one key column and 32 of its heads, so the ReLU-weighted head
-//    sum is 32 in-lane FMAs plus one cross-half add.
+// Kernels:
+//  * score_mfma_reg: 64 heads x 128 dims, bf16 query, bf16 or fp4 (E2M1 + E8M0 per 32) keys, one
+//    query per work item. The step streams every visible key once (the step's dominant HBM
+//    traffic). S = Q . K^T runs on v_mfma_f32_32x32x16_bf16 with the 64 heads as the M dimension
+//    (two 32-row blocks) and 32 keys as N; each lane then owns one key column and 32 of its heads,
+//    so the ReLU-weighted head sum is 32 in-lane FMAs plus one cross-half add.
+//  * score_mfma_multi: the same contraction for prefill chunks, four queries sharing each tile.
 //  * score_generic: any (heads x dim) <= 8192, fp32 / bf16 / fp4 - one thread per key.
 // For the selector that follows, all can instead hand over each part of kScorePartKeys keys as a
 // cumulative histogram of the top kTopBits bits of the scores' order keys plus the part's
@@ -29,6 +29,15 @@ constexpr int kMfmaHeads = 64;
 constexpr int kMfmaDim = 128;
 
 __device__ __forceinline__ float canonical_zero(float v) { return v == 0.0f ? 0.0f : v; }
+// A workgroup-uniform read of data no kernel writes while this one runs, through the constant
+// address space: a scalar load, which the wait counters track apart from the vector loads, so
+// that it holds up none of them.
+__device__ __forceinline__ int32_t uniform_ld(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+// max(x, 0) for finite x as one integer max on the bit pattern: negative values (and -0) have a
+// negative pattern and become +0, non-negative ones stay.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Eight E2M1 nibbles (one 32-bit word, element 0 in the low nibble) times a power-of-two block
 // scale -> eight bf16 values, exactly, with gfx950's scaled conversion (two elements of one byte
@@ -71,6 +80,8 @@ __device__ __forceinline__ void finish_parts(const ScoreArgs& a, int i, int part
       const int bin = kTopBins - 1 - 4 * t - e;
       c[e] = kPacked ? (h[bin >> 1] >> (16 * (bin & 1))) & 0xffffu : h[bin];
       tot += c[e];
+      if (a.row_hist != nullptr && c[e] != 0u)   // the row's counts for the selector's first pass
+        atomicAdd(a.row_hist + (int64_t)i * kTopBins + bin, c[e]);
     }
     const uint32_t incl = wave_inclusive_scan(tot);
     if (lane == 63) wtot[q * 4 + w] = incl;
@@ -172,156 +183,6 @@ __device__ __forceinline__ void finish_part_wave(const ScoreArgs& a, int i, int 
   }
 }
 
-template <bool kFp4>
-__global__ __launch_bounds__(256, 2) void score_mfma(ScoreArgs a) {
-  __shared__ uint32_t lhist[kScoreParts * kTopBins];   // one histogram per kScorePartKeys keys
-  __shared__ uint32_t lkeys[kScoreKeysPerBlock];
-  __shared__ uint2 lsorted[kScoreKeysPerBlock];
-  __shared__ uint32_t wtot[kScoreParts * 4];
-  // physical blocks of this workgroup's keys (at least 2 entries per block: ratio <= 128)
-  __shared__ int32_t tbl[kScoreKeysPerBlock / 2 + 2];
-  const int i = blockIdx.y;
-  int seq, p;
-  query_at(a.qd, i, &seq, &p);
-  // rows hold n_visible(max_pos) scores; a query past max_pos is clamped to that width
-  const int nv = min(n_visible(p, a.pool.ratio, a.window), n_visible(a.max_pos, a.pool.ratio, a.window));
-  const int base = blockIdx.x * kScoreKeysPerBlock;
-  if (base >= nv) return;
-  const int end = min(nv, base + kScoreKeysPerBlock);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 31;
-  const int hf = lane >> 5;
-  if (a.part_hist)
-    for (int j = threadIdx.x; j < kScoreParts * kTopBins; j += 256) lhist[j] = 0;
-  // The block table entries of the workgroup's key range are read once: a table lookup inside the
-  // tile loop would be a load that the data loads depend on, and waiting for it would also wait
-  // for the prefetched tile.
-  const int per_block = a.pool.per_block;           // 256 / ratio: a power of two
-  const int pb_shift = __builtin_ctz(per_block);
-  const int lb0 = base >> pb_shift;
-  const int n_lb = ((end - 1) >> pb_shift) - lb0 + 1;
-  for (int j = threadIdx.x; j < n_lb; j += 256) {
-    const int lb = lb0 + j;
-    const int phys = lb < a.pool.max_blocks ? a.pool.block_table[(int64_t)seq * a.pool.max_blocks + lb] : -1;
-    tbl[j] = (phys >= 0 && phys < a.pool.num_blocks) ? phys : -1;
-  }
-  __syncthreads();
-
-  // The contraction index d is split as d = 64*hf + 8*s + e for K-step s (0..7) and element e of
-  // a lane's 8-wide operand; query and keys use the same split, so each lane holds 64 contiguous
-  // dims of its row.
-  bf16x8 qa[2][8];
-  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)i * kMfmaHeads * kMfmaDim;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qa[mb][s] = *reinterpret_cast<const bf16x8*>(q + (32 * mb + col) * kMfmaDim + 64 * hf + 8 * s);
-  // weights of the 32 (head) rows this lane accumulates: row = 32*mb + 8*(r/4) + 4*hf + r%4
-  float wv[2][16];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      wv[mb][r] = a.w[(int64_t)i * kMfmaHeads + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3)];
-
-  float* out = a.scores + (int64_t)i * a.ld;
-  // Each wave walks 32-key tiles with stride 128; the next two tiles' keys are loaded while the
-  // current one is multiplied. fp4 tiles stay packed (32 B + 2 scale bytes per lane) until used.
-  struct KeysBf16 {
-    bf16x8 v[8];
-    bool valid;
-  };
-  struct KeysFp4 {
-    u32x4 w0, w1;
-    float s0, s1;
-    bool valid;
-  };
-  using Keys = std::conditional_t<kFp4, KeysFp4, KeysBf16>;
-  // Branch-free loads (out-of-range or absent keys read entry 0 of the pool; their scores are
-  // written as -inf or not at all), so the prefetch never forces a wait on itself.
-  // pool entry of key g (entry 0 when its block is absent; such keys score -inf)
-  auto entry_of = [&](int g) -> int64_t {
-    g = min(g, end - 1);
-    const int phys = tbl[(g >> pb_shift) - lb0];
-    return phys >= 0 ? ((int64_t)phys << pb_shift) + (g & (per_block - 1)) : 0;
-  };
-  auto key_valid = [&](int g) { return tbl[(min(g, end - 1) >> pb_shift) - lb0] >= 0; };
-  auto load = [&](Keys& kb, int t0) {
-    const int64_t e = entry_of(t0 + col);
-    kb.valid = key_valid(t0 + col);
-    if constexpr (!kFp4) {
-      const uint16_t* row =
-          reinterpret_cast<const uint16_t*>(a.pool.data + e * a.pool.entry_bytes) + 64 * hf;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) kb.v[s] = *reinterpret_cast<const bf16x8*>(row + 8 * s);
-    } else {
-      const uint8_t* row = a.pool.data + e * a.pool.entry_bytes + 32 * hf;
-      // the two E8M0 scale bytes of this lane's 64 dims, one 2-byte read
-      const uint16_t scl = *reinterpret_cast<const uint16_t*>(
-          reinterpret_cast<const uint8_t*>(a.pool.scale) + e * 4 + 2 * hf);
-      kb.w0 = *reinterpret_cast<const u32x4*>(row);
-      kb.w1 = *reinterpret_cast<const u32x4*>(row + 16);
-      kb.s0 = e8m0_to_f32(scl & 0xffu);
-      kb.s1 = e8m0_to_f32(scl >> 8);
-    }
-  };
-  auto operand = [&](const Keys& kb, int s) -> bf16x8 {
-    if constexpr (!kFp4) {
-      return kb.v[s];
-    } else {
-      return s < 4 ? fp4x8_to_bf16x8(kb.w0[s], kb.s0) : fp4x8_to_bf16x8(kb.w1[s - 4], kb.s1);
-    }
-  };
-  auto score = [&](const Keys& kb, int t0) {
-    f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 b = operand(kb, s);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], b, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], b, acc1, 0, 0, 0);
-    }
-    float part = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      part = fmaf(wv[0][r], fmaxf(acc0[r], 0.f), part);
-      part = fmaf(wv[1][r], fmaxf(acc1[r], 0.f), part);
-    }
-    part += __shfl_xor(part, 32, 64);
-    const int g = t0 + col;
-    if (hf == 0 && g < end) {
-      const float v = kb.valid ? canonical_zero(part) : -INFINITY;
-      if (a.part_hist) {
-        const uint32_t key = order_key(v);
-        lkeys[g - base] = key;
-        atomicAdd(&lhist[((g - base) / kScorePartKeys) * kTopBins + (key >> (32 - kTopBits))], 1u);
-      } else {
-        out[g] = v;
-      }
-    }
-  };
-  // three tiles per wave in flight: two loading while one is multiplied
-  Keys k0, k1, k2;
-  int t0 = base + wave * 32;
-  if (t0 < end) {
-    load(k0, t0);
-    load(k1, t0 + 128);
-    for (; t0 < end; t0 += 384) {
-      load(k2, t0 + 256);
-      score(k0, t0);
-      if (t0 + 128 >= end) break;
-      load(k0, t0 + 384);
-      score(k1, t0 + 128);
-      if (t0 + 256 >= end) break;
-      load(k1, t0 + 512);
-      score(k2, t0 + 256);
-    }
-  }
-  if (a.part_hist)
-    finish_parts<kScoreParts>(a, i, blockIdx.x * kScoreParts, base, end, lkeys, lhist, lsorted, wtot);
-}
-
 // Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane i's bytes land
 // at LDS byte address lds + 16i. Issued through inline asm: with the compiler builtin every LDS
 // read waits for all outstanding loads (the compiler cannot tell which LDS bytes a load writes),
@@ -336,26 +197,58 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// bf16 keys, decode form: the contraction of score_mfma with every key tile fetched by fully
-// coalesced loads into registers (eight 16-byte loads per lane, each instruction one contiguous
-// 1 KB = four whole key rows) and passed through the wave's own LDS stage to the MFMA operand
-// layout. A plain streaming read of this GPU's memory reaches about 7.1 TB/s with such loads
-// against 6.0-6.3 TB/s through direct global -> LDS loads. Each wave keeps its next two tiles in
-// flight in registers; the stage holds one tile (chunk c of key n at c ^ (n % 16), conflict-free
-// for both the stores and the operand reads), and since a wave reads only its own stage, the tile
-// loop has no workgroup barrier.
+// Decode form (one query per workgroup item), bf16 or fp4 keys: the contraction of score_mfma
+// with every key tile fetched by fully coalesced loads into registers and passed through the
+// wave's own LDS stage to the MFMA operand layout. A plain streaming read of this GPU's memory
+// reaches about 7.1 TB/s with such loads against 6.0-6.3 TB/s through direct global -> LDS loads.
+// A tile is 32 keys:
+//   bf16: 32 x 256 B; load instruction j (< 8) brings key 4j + lane/16, 16-byte chunk lane % 16,
+//         stored in the stage at chunk c ^ (n % 16) of row n (conflict-free for the stores and
+//         for the operand reads: 32 keys, one logical chunk);
+//   fp4:  32 x 64 B of E2M1 pairs + 32 x 4 E8M0 bytes; instruction j (< 2) brings key
+//         16j + lane/4, chunk lane % 4, stored at chunk c ^ ((n / 2) % 4) of row n (eight lanes
+//         reading one logical chunk of eight keys then hit eight different bank groups); lanes
+//         below 32 bring key `lane`'s four scale bytes. Operands are widened exactly to bf16.
+// Each wave keeps its next kDepth tiles in flight in registers and reads only its own stage, so
+// the tile loop has no workgroup barrier.
+// Work: an item is one block of kScoreKeysPerBlock visible keys of one query. Every workgroup
+// derives the list of non-empty items from the queries' positions itself (one load per query and a
+// prefix sum in LDS; up to kItemQueries queries, else it walks every (query, block) pair and skips
+// the empty ones), and workgroup w takes items w, w + G, ...: the grid is a fixed size, whatever the
+// lengths, and short and long rows spread evenly.
 // kTile: a 32-key tile always lies in one block (256 / ratio >= 32, the C4 case); kHand: hand-off
-// to the selector instead of plain scores. Both are launch-uniform, so the tile loop has no branch.
-// Workgroups: first n_c0 + n_c1 compressor workgroups (the compressor calls c0, c1 riding
-// along, run by this launch's four waves), then one per (key block, query) in query-major order.
-template <bool kTile, bool kHand>
+// to the selector instead of plain scores. The first n_c0 + n_c1 workgroups run the compressor
+// calls c0, c1 riding along with this launch.
+constexpr int kItemQueries = 1024;
+constexpr int kIndexWorkgroups = 512;
+
+template <bool kFp4>
+struct KeyFormat {
+  static constexpr int kLoads = 8;          // 16-byte loads per lane per tile
+  static constexpr int kRowBytes = 256;
+  static constexpr int kStageBytes = 8192;
+  static constexpr int kDepth = 2;          // tiles in flight per wave
+};
+template <>
+struct KeyFormat<true> {
+  static constexpr int kLoads = 2;
+  static constexpr int kRowBytes = 64;
+  static constexpr int kStageBytes = 2048 + 128;
+  static constexpr int kDepth = 4;
+};
+
+template <bool kTile, bool kHand, bool kFp4>
 __global__ __launch_bounds__(256, 1) void score_mfma_reg(ScoreArgs a, CompressArgs c0, CompressArgs c1,
                                                           int n_c0, int n_c1) {
+  using KF = KeyFormat<kFp4>;
+  constexpr int kLoads = KF::kLoads, kDepth = KF::kDepth;
   __shared__ __attribute__((aligned(1024))) uint8_t stage[4][8192];
   __shared__ uint32_t lhist[kScoreParts * kTopBins];
   __shared__ int32_t tbl[kScoreKeysPerBlock / 2 + 2];
   __shared__ uint32_t lkeys[kScoreKeysPerBlock];
   __shared__ uint32_t wtot[kScoreParts * 4];
+  __shared__ int32_t istart[kItemQueries + 1];
+  __shared__ int32_t nvq[kItemQueries];
   static_assert(sizeof(stage) >= kCompressFusedLds, "a compressor workgroup fits the stages");
   int bid = blockIdx.x;
   if (bid < n_c0) {
@@ -367,137 +260,260 @@ __global__ __launch_bounds__(256, 1) void score_mfma_reg(ScoreArgs a, CompressAr
     return;
   }
   bid -= n_c0 + n_c1;
-  const int max_nv = n_visible(a.max_pos, a.pool.ratio, a.window);
-  const int gx = (max_nv + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock;
-  const int i = bid / gx;
-  const int base = (bid - i * gx) * kScoreKeysPerBlock;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_wg = gridDim.x - n_c0 - n_c1;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int hf = lane >> 5;
-  // In decode form the sequence is the query index itself, so the block table of the
-  // workgroup's whole key range is read together with the sequence length, the query and the
-  // head weights (all independent loads); in prefill form the sequence comes from q_seq first.
-  const int seq = (a.qd.seq_lens || !a.qd.q_seq) ? i : a.qd.q_seq[i];
+  const int max_nv = n_visible(a.max_pos, a.pool.ratio, a.window);
+  const int gx = (max_nv + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock;
+  // positions: seq_lens - 1 (decode) or q_pos; one source and offset chosen once, so that the
+  // loads carry no branch and go out together
+  const int32_t* pos_src = a.qd.seq_lens ? a.qd.seq_lens : a.qd.q_pos;
+  const int pos_adj = a.qd.seq_lens ? 1 : 0;
+  auto nv_of = [&](int q) {   // q uniform
+    return min(n_visible(uniform_ld(pos_src + q) - pos_adj, a.pool.ratio, a.window), max_nv);
+  };
+
   const int per_block = a.pool.per_block;   // 256 / ratio: a power of two
   const int pb_shift = __builtin_ctz(per_block);
-  const int lb0 = base >> pb_shift;
-  const int n_lb_max = ((base + kScoreKeysPerBlock - 1) >> pb_shift) - lb0 + 1;
-  for (int j = threadIdx.x; j < n_lb_max; j += 256) {
-    const int lb = lb0 + j;
-    const int phys = lb < a.pool.max_blocks ? a.pool.block_table[(int64_t)seq * a.pool.max_blocks + lb] : -1;
-    tbl[j] = (phys >= 0 && phys < a.pool.num_blocks) ? phys : -1;
-  }
-  const int p = a.qd.seq_lens ? a.qd.seq_lens[i] - 1 : a.qd.q_pos[i];
-  // operands as in score_mfma: d = 64*hf + 8*s + e, i.e. lane (key col, hf) takes logical chunk
-  // 8*hf + s of its key at K-step s
-  bf16x8 qa[2][8];
-  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)i * kMfmaHeads * kMfmaDim;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qa[mb][s] = *reinterpret_cast<const bf16x8*>(q + (32 * mb + col) * kMfmaDim + 64 * hf + 8 * s);
-  float wv[2][16];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      wv[mb][r] = a.w[(int64_t)i * kMfmaHeads + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3)];
-  const int nv = min(n_visible(p, a.pool.ratio, a.window), n_visible(a.max_pos, a.pool.ratio, a.window));
-  if (base >= nv) return;   // uniform, before any barrier
-  const int end = min(nv, base + kScoreKeysPerBlock);
-  if (kHand)
-    for (int j = threadIdx.x; j < kScoreParts * kTopBins; j += 256) lhist[j] = 0;
-  __syncthreads();
-  float* out = a.scores + (int64_t)i * a.ld;
+  const int nk = kFp4 ? lane >> 2 : lane >> 4;
+  const int ck = kFp4 ? lane & 3 : lane & 15;
+  // bytes per key row: the pool's entry size for 128 dimensions (bf16: 256; fp4: 64, scales apart)
+  constexpr int kRow = KF::kRowBytes;
+  const uint32_t lane_off = nk * kRow + 16 * ck;   // this lane's bytes of the first load
+  // Operand reads: lane (key col, hf) reads logical chunk 8hf + s (bf16) or 2hf + s (fp4) of its
+  // key, stored at that chunk XOR (col % 16) or XOR ((col / 2) % 4). As the logical chunk is a
+  // disjoint OR of the hf and s bits, its stored offset is the s = 0 offset XOR 16 s: one offset
+  // per lane, and an XOR per read instead of a register per K-step.
+  const uint32_t roff0 = kFp4 ? col * 64 + 16 * ((2 * hf) ^ ((col >> 1) & 3))
+                              : col * 256 + 16 * ((8 * hf) ^ (col & 15));
 
-  auto entry_of = [&](int g) -> int64_t {   // entry 0 when the block is absent (scored -inf)
-    g = min(g, end - 1);
-    const int phys = tbl[(g >> pb_shift) - lb0];
-    return phys >= 0 ? ((int64_t)phys << pb_shift) + (g & (per_block - 1)) : 0;
-  };
-  // tile m of this wave: keys base + 32*wave + 128*m + [0, 32); load instruction j brings key
-  // n = 4j + lane/16, logical chunk lane % 16
-  const int first = base + 32 * wave;
-  const int n_mine = first < end ? (end - first + 127) / 128 : 0;
-  const int nk = lane >> 4, ck = lane & 15;
-  auto load = [&](u32x4 (&r)[8], int m) {
-    const int tb = first + 128 * m;
-    if constexpr (kTile) {
-      // the 32-key tile lies in one block; tiles past the end re-read the last tile's
-      // block (in bounds, unused)
-      const int gb = min(tb, (end - 1) & ~31);
-      const int phys = tbl[(gb >> pb_shift) - lb0];
-      const int64_t e0 = (phys >= 0 ? ((int64_t)phys << pb_shift) : 0) + (gb & (per_block - 1));
-      const uint8_t* src = a.pool.data + (e0 + nk) * a.pool.entry_bytes + 16 * ck;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        r[j] = *reinterpret_cast<const u32x4*>(src + 4 * j * a.pool.entry_bytes);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        r[j] = *reinterpret_cast<const u32x4*>(a.pool.data + entry_of(tb + 4 * j + nk) * a.pool.entry_bytes + 16 * ck);
-    }
-  };
   uint8_t* st = &stage[wave][0];
-  auto publish = [&](const u32x4 (&r)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = 4 * j + nk;
-      *reinterpret_cast<u32x4*>(st + n * 256 + 16 * (ck ^ (n & 15))) = r[j];
-    }
+  auto rd16 = [&](int s) -> u32x4 {   // 16 bytes of K-step s's operand chunk
+    return *reinterpret_cast<const u32x4*>(st + (roff0 ^ (16u * s)));
   };
-  // operand read offsets: key col, chunk (8hf + s) ^ (col % 16)
-  uint32_t roff[8];
+
+  // ---- one item's prologue: the block-table entries of its key range (into tbl), the query's
+  // operands and its head weights (registers), as independent loads issued together. In decode
+  // form the sequence is the query itself. Operands as in score_mfma: d = 64*hf + 8*s + e, i.e.
+  // lane (key col, hf) takes logical chunk 8*hf + s of its key at K-step s.
+  bf16x8 qa[2][8];
+  float wv[2][16];
+  int lb0 = 0;
+  auto fetch = [&](int i, int base, int end) {
+    const int seq = (a.qd.seq_lens || !a.qd.q_seq) ? i : uniform_ld(a.qd.q_seq + i);
+    lb0 = base >> pb_shift;
+    const int n_lb = ((end - 1) >> pb_shift) - lb0 + 1;
+    const int32_t* bt = a.pool.block_table + (int64_t)seq * a.pool.max_blocks;
+    auto raw = [&](int j) {   // in bounds of the row; checked by phys_of
+      return bt[min(lb0 + j, a.pool.max_blocks - 1)];
+    };
+    auto phys_of = [&](int j, int v) {
+      return (lb0 + j < a.pool.max_blocks && v >= 0 && v < a.pool.num_blocks) ? v : -1;
+    };
+    const int v0 = raw(min(tid, n_lb - 1));   // first entries: the load goes out before q and w's
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)i * kMfmaHeads * kMfmaDim;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) roff[s] = col * 256 + 16 * ((8 * hf + s) ^ (col & 15));
-  auto score = [&](int m) {
-    f32x16 acc0 = {}, acc1 = {};
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(st + roff[s]);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], b, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], b, acc1, 0, 0, 0);
+      for (int s = 0; s < 8; ++s)
+        qa[mb][s] = *reinterpret_cast<const bf16x8*>(q + (32 * mb + col) * kMfmaDim + 64 * hf + 8 * s);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        wv[mb][r] = a.w[(int64_t)i * kMfmaHeads + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3)];
+    if (tid < n_lb) tbl[tid] = phys_of(tid, v0);
+    for (int j = tid + 256; j < n_lb; j += 256) tbl[j] = phys_of(j, raw(j));   // ratio 128 only
+  };
+
+  // ---- the item list: istart[q] = items of the queries before q (exclusive prefix sum), and
+  // each query's visible key count in nvq. The workgroup's first item is guessed in the order of
+  // the walk over every (query, block) pair, which is the list's own order whenever every query
+  // sees max_nv keys (the usual batch of equal lengths); its prologue loads go out together with
+  // the lengths', so that the list costs no extra round trip to memory in that case.
+  const bool compact = a.n_q <= kItemQueries;
+  const int g_i = bid / gx, g_base = (bid - g_i * gx) * kScoreKeysPerBlock;
+  const bool guessed = g_i < a.n_q;   // uniform
+  int total;
+  if (compact) {
+    // Every wave builds the whole list itself, writing the same values to the same LDS words, and
+    // reads only words it has written itself (or identical ones): no workgroup barrier. Query
+    // q = 64 g + lane for group g < n_grp.
+    constexpr int kGroups = kItemQueries / 64;
+    const int n_grp = (a.n_q + 63) >> 6;
+    int pq[kGroups];   // queries past n_q read the last one's (in bounds, unused); no branch
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) pq[g] = pos_src[min(64 * g + lane, a.n_q - 1)];
+    __builtin_amdgcn_sched_barrier(0);   // the lengths' loads before the guess's
+    if (guessed) fetch(g_i, g_base, min(max_nv, g_base + kScoreKeysPerBlock));
+    uint32_t run = 0;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      if (g >= n_grp) break;   // uniform
+      const int q = 64 * g + lane;
+      const int nv = q < a.n_q ? min(n_visible(pq[g] - pos_adj, a.pool.ratio, a.window), max_nv) : 0;
+      const uint32_t cnt = (uint32_t)((nv + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock);
+      const uint32_t incl = wave_inclusive_scan(cnt);
+      if (q < a.n_q) {
+        istart[q] = (int32_t)(run + incl - cnt);
+        nvq[q] = nv;
+      }
+      run += __builtin_amdgcn_readlane(incl, 63);
     }
-    float part = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      part = fmaf(wv[0][r], fmaxf(acc0[r], 0.f), part);
-      part = fmaf(wv[1][r], fmaxf(acc1[r], 0.f), part);
+    if (lane == 0) istart[a.n_q] = (int32_t)run;
+    total = (int)run;
+  } else {
+    if (guessed) fetch(g_i, g_base, min(max_nv, g_base + kScoreKeysPerBlock));
+    total = a.n_q * gx;
+  }
+
+  for (int item = bid; item < total; item += n_wg) {
+    int i, base, nv;
+    if (compact) {
+      int lo = 0, hi = a.n_q - 1;   // last query whose first item is <= item
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (istart[mid] <= item) lo = mid; else hi = mid - 1;
+      }
+      // uniform across the workgroup: scalar registers keep the tile loop's control and the
+      // item's addresses out of the vector registers
+      i = __builtin_amdgcn_readfirstlane(lo);
+      base = __builtin_amdgcn_readfirstlane((item - istart[i]) * kScoreKeysPerBlock);
+      nv = __builtin_amdgcn_readfirstlane(nvq[i]);
+    } else {
+      i = item / gx;
+      base = (item - i * gx) * kScoreKeysPerBlock;
+      nv = nv_of(i);
     }
-    part += __shfl_xor(part, 32, 64);
-    const int g = first + 128 * m + col;
-    if (hf == 0 && g < end) {
-      const bool valid = tbl[(g >> pb_shift) - lb0] >= 0;
-      const float v = valid ? canonical_zero(part) : -INFINITY;
-      if constexpr (kHand) {
-        const uint32_t key = order_key(v);
-        lkeys[g - base] = key;
-        atomicAdd(&lhist[((g - base) / kScorePartKeys) * kTopBins + (key >> (32 - kTopBits))], 1u);
+    if (base >= nv) continue;   // only in the walk over every pair; uniform
+    const int end = min(nv, base + kScoreKeysPerBlock);
+    if (item != bid) __syncthreads();   // the previous item's readers of the LDS are done
+    // The previous item's hand-off stores have been issued. Waiting for them here (vmcnt 0, the
+    // other counters free) leaves only loads outstanding in the tile loop, whose waits then count
+    // tiles; with stores still in flight the compiler cannot count and waits for every load.
+    if constexpr (kHand) __builtin_amdgcn_s_waitcnt(0x0F70);
+    // the guess's range [g_base, min(max_nv, g_base + block)) covers [base, end) when it holds
+    if (!(item == bid && guessed && i == g_i && base == g_base)) fetch(i, base, end);
+    if (kHand)
+      for (int j = tid; j < kScoreParts * kTopBins; j += 256) lhist[j] = 0;
+    __syncthreads();
+    float* out = a.scores + (int64_t)i * a.ld;
+
+    auto entry_of = [&](int g) -> int64_t {   // entry 0 when the block is absent (scored -inf)
+      g = min(g, end - 1);
+      const int phys = tbl[(g >> pb_shift) - lb0];
+      return phys >= 0 ? ((int64_t)phys << pb_shift) + (g & (per_block - 1)) : 0;
+    };
+    // tile m of this wave: keys base + 32*wave + 128*m + [0, 32)
+    const int first = base + 32 * wave;
+    const int n_mine = first < end ? (end - first + 127) / 128 : 0;
+    struct Regs {
+      u32x4 v[kLoads];
+      uint32_t sc;
+    };
+    auto load = [&](Regs& r, int m) {
+      const int tb = first + 128 * m;   // wave-uniform
+      if constexpr (kTile) {
+        // the 32-key tile lies in one block; tiles past the end re-read the last tile's block
+        // (in bounds, unused). The tile's base address is wave-uniform (scalar registers) and
+        // each lane adds its fixed offset, so the loads need no per-lane address arithmetic.
+        const int gb = min(tb, (end - 1) & ~31);
+        const int phys = __builtin_amdgcn_readfirstlane(tbl[(gb >> pb_shift) - lb0]);
+        const int64_t e0 = (phys >= 0 ? ((int64_t)phys << pb_shift) : 0) + (gb & (per_block - 1));
+        const uint8_t* kb = a.pool.data + e0 * kRow;
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j)
+          r.v[j] = *reinterpret_cast<const u32x4*>(kb + lane_off + j * (kFp4 ? 16 : 4) * kRow);
+        if constexpr (kFp4) r.sc = (reinterpret_cast<const uint32_t*>(a.pool.scale) + e0)[lane & 31];
       } else {
-        out[g] = v;
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+          const int n = (kFp4 ? 16 : 4) * j + nk;
+          r.v[j] = *reinterpret_cast<const u32x4*>(a.pool.data + entry_of(tb + n) * kRow + 16 * ck);
+        }
+        if constexpr (kFp4) r.sc = reinterpret_cast<const uint32_t*>(a.pool.scale)[entry_of(tb + (lane & 31))];
+      }
+    };
+    auto publish = [&](const Regs& r) {
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        const int n = (kFp4 ? 16 : 4) * j + nk;
+        const int c = kFp4 ? (ck ^ ((n >> 1) & 3)) : (ck ^ (n & 15));
+        *reinterpret_cast<u32x4*>(st + n * KF::kRowBytes + 16 * c) = r.v[j];
+      }
+      if constexpr (kFp4) {
+        if (lane < 32) *reinterpret_cast<uint32_t*>(st + 2048 + 4 * lane) = r.sc;
+      }
+    };
+    auto score = [&](int m) {
+      f32x16 acc0 = {}, acc1 = {};
+      if constexpr (!kFp4) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 b = __builtin_bit_cast(bf16x8, rd16(s));
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], b, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], b, acc1, 0, 0, 0);
+        }
+      } else {
+        const u32x4 w0 = rd16(0);
+        const u32x4 w1 = rd16(1);
+        const uint32_t scb = *reinterpret_cast<const uint32_t*>(st + 2048 + 4 * col) >> (16 * hf);
+        const float s0 = e8m0_to_f32(scb & 0xffu), s1 = e8m0_to_f32((scb >> 8) & 0xffu);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 b = s < 4 ? fp4x8_to_bf16x8(w0[s], s0) : fp4x8_to_bf16x8(w1[s - 4], s1);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], b, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], b, acc1, 0, 0, 0);
+        }
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        part = fmaf(wv[0][r], relu(acc0[r]), part);
+        part = fmaf(wv[1][r], relu(acc1[r]), part);
+      }
+      part += __shfl_xor(part, 32, 64);
+      const int g = first + 128 * m + col;
+      if (hf == 0 && g < end) {
+        const bool valid = tbl[(g >> pb_shift) - lb0] >= 0;
+        const float v = valid ? canonical_zero(part) : -INFINITY;
+        if constexpr (kHand) {
+          const uint32_t key = order_key(v);
+          lkeys[g - base] = key;
+          atomicAdd(&lhist[((g - base) / kScorePartKeys) * kTopBins + (key >> (32 - kTopBits))], 1u);
+        } else {
+          out[g] = v;
+        }
+      }
+    };
+    if (n_mine > 0) {
+      // kDepth tiles in flight in registers while one is staged and multiplied (a count that is
+      // not a multiple of kDepth runs tiles of clamped rows, whose keys score() drops)
+      Regs r[kDepth];
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        load(r[d], d);
+        // keep the tiles' loads in tile order: loads return in order, so the tile loop's waits
+        // count only the tiles behind the one it stages (reordered, it would wait for all)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int m = 0; m < n_mine; m += kDepth) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+          publish(r[d]);
+          load(r[d], m + d + kDepth);
+          score(m + d);
+        }
       }
     }
-  };
-  if (n_mine > 0) {
-    // two tiles in flight in registers while one is staged and multiplied
-    // (an odd count runs one more tile of clamped rows, whose keys score() drops)
-    u32x4 ra[8], rb[8];
-    load(ra, 0);
-    load(rb, 1);
-    for (int m = 0; m < n_mine; m += 2) {
-      publish(ra);
-      load(ra, m + 2);
-      score(m);
-      publish(rb);
-      load(rb, m + 3);
-      score(m + 1);
-    }
+    if constexpr (kHand)   // the stages are free now: the sorted pairs use them
+      finish_parts<kScoreParts>(a, i, base / kScorePartKeys, base, end, lkeys, lhist,
+                                reinterpret_cast<uint2*>(&stage[0][0]), wtot);
   }
-  if constexpr (kHand)   // the stages are free now: the sorted pairs use them
-    finish_parts<kScoreParts>(a, i, base / kScorePartKeys, base, end, lkeys, lhist,
-                              reinterpret_cast<uint2*>(&stage[0][0]), wtot);
 }
 
 // Prefill form, bf16 keys: four query tokens per workgroup, one per wave, share every key tile.
@@ -629,8 +645,8 @@ __global__ __launch_bounds__(256, 3) void score_mfma_multi(ScoreArgs a) {
         float part = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          part = fmaf(wv[0][r], fmaxf(acc0[r], 0.f), part);
-          part = fmaf(wv[1][r], fmaxf(acc1[r], 0.f), part);
+          part = fmaf(wv[0][r], relu(acc0[r]), part);
+          part = fmaf(wv[1][r], relu(acc1[r]), part);
         }
         part += __shfl_xor(part, 32, 64);
         const int g = base + 32 * t + col;
@@ -729,7 +745,7 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s, const SideWork*
   SideWork none{};
   const SideWork& sw = side ? *side : none;
   const int n_side = sw.n[0] + sw.n[1];
-  if (n_side > 0 && (max_nv == 0 || a.n_q == 0 || a.pool.dtype != BF16 || a.n_heads != kMfmaHeads ||
+  if (n_side > 0 && (max_nv == 0 || a.n_q == 0 || (a.pool.dtype != BF16 && a.pool.dtype != FP4) || a.n_heads != kMfmaHeads ||
                      a.pool.dim != kMfmaDim || a.q_dtype != BF16 || (a.qd.q_seq && a.n_q >= kMultiMinQueries)))
     return hipErrorInvalidValue;   // the caller offers side work only to the one-query bf16 kernel
   if (max_nv == 0 || a.n_q == 0) return hipSuccess;
@@ -742,19 +758,26 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s, const SideWork*
       grid.x = (max_nv + kMKeys - 1) / kMKeys;
       grid.y = (a.n_q + kMQ - 1) / kMQ;
       hipLaunchKernelGGL(score_mfma_multi, grid, dim3(256), 0, s, a);
-    } else if (a.pool.dtype == BF16) {
-      const bool tile = a.pool.per_block >= 32, hand = a.part_hist != nullptr;
-      const dim3 g1(n_side + grid.x * grid.y);
-      if (tile && hand)
-        hipLaunchKernelGGL((score_mfma_reg<true, true>), g1, dim3(256), 0, s, a, sw.c[0], sw.c[1], sw.n[0], sw.n[1]);
-      else if (tile)
-        hipLaunchKernelGGL((score_mfma_reg<true, false>), g1, dim3(256), 0, s, a, sw.c[0], sw.c[1], sw.n[0], sw.n[1]);
-      else if (hand)
-        hipLaunchKernelGGL((score_mfma_reg<false, true>), g1, dim3(256), 0, s, a, sw.c[0], sw.c[1], sw.n[0], sw.n[1]);
-      else
-        hipLaunchKernelGGL((score_mfma_reg<false, false>), g1, dim3(256), 0, s, a, sw.c[0], sw.c[1], sw.n[0], sw.n[1]);
     } else {
-      hipLaunchKernelGGL(score_mfma<true>, grid, dim3(256), 0, s, a);
+      // one-query kernel over the item list: two workgroups per compute unit (registers and LDS
+      // allow two), fewer when the items fit
+      const int items = grid.x * grid.y;
+      const dim3 g1(n_side + (items < kIndexWorkgroups ? items : kIndexWorkgroups));
+      const bool tile = a.pool.per_block >= 32, hand = a.part_hist != nullptr;
+#define HYB_SCORE_REG(T, H, F) \
+  hipLaunchKernelGGL((score_mfma_reg<T, H, F>), g1, dim3(256), 0, s, a, sw.c[0], sw.c[1], sw.n[0], sw.n[1])
+      if (a.pool.dtype == BF16) {
+        if (tile && hand) HYB_SCORE_REG(true, true, false);
+        else if (tile) HYB_SCORE_REG(true, false, false);
+        else if (hand) HYB_SCORE_REG(false, true, false);
+        else HYB_SCORE_REG(false, false, false);
+      } else {
+        if (tile && hand) HYB_SCORE_REG(true, true, true);
+        else if (tile) HYB_SCORE_REG(true, false, true);
+        else if (hand) HYB_SCORE_REG(false, true, true);
+        else HYB_SCORE_REG(false, false, true);
+      }
+#undef HYB_SCORE_REG
     }
   } else {
     dim3 grid((max_nv + kScorePartKeys - 1) / kScorePartKeys, a.n_q);

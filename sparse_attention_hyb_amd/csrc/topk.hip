@@ -654,16 +654,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pairs(TopkArgs a) {
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
   const int k = a.k;
-  // first 32 parts' cumulative counts, before the row length is known (clamped to part_ld)
+  const bool rowh = a.row_hist != nullptr;   // uniform
+  // first 32 parts' cumulative counts, before the row length is known (clamped to part_ld) - or,
+  // with the indexer's per-row counts, this thread's bin of the row
   constexpr int kPartWords = kTopBins / 2;
   constexpr int kPartGroups = kTopkThreads / kPartWords;            // 2
   constexpr int kPartLoads = 16;                                     // parts pg + 2q, q < 16
   const int pwd = tid % kPartWords, pg = tid / kPartWords;
   const uint32_t* ph = reinterpret_cast<const uint32_t*>(a.part_hist + (int64_t)i * a.part_ld * kTopBins);
   uint32_t pw[kPartLoads];
+  uint32_t rcount = 0;
+  if (rowh) {
+    rcount = a.row_hist[(int64_t)i * kTopBins + (kTopBins - 1 - tid)];   // bin 1023 - tid
+  } else {
 #pragma unroll
-  for (int q = 0; q < kPartLoads; ++q)
-    pw[q] = ph[(int64_t)min(pg + kPartGroups * q, a.part_ld - 1) * kPartWords + pwd];
+    for (int q = 0; q < kPartLoads; ++q)
+      pw[q] = ph[(int64_t)min(pg + kPartGroups * q, a.part_ld - 1) * kPartWords + pwd];
+  }
   const uint2* pairs = reinterpret_cast<const uint2*>(a.scores) + (int64_t)i * (a.ld / 2);
   // (ext-vector pairs: a register array of HIP's union-based uint2 would stay in scratch)
   const int ep = tid >> 5, el = tid & 31;   // early part, lane: pairs el and el + 32
@@ -674,6 +681,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pairs(TopkArgs a) {
   C[tid] = 0;
   const int n = topk_row_len(a, i);
   int* out = a.out + (int64_t)i * k;
+  if (rowh) a.row_hist[(int64_t)i * kTopBins + (kTopBins - 1 - tid)] = 0u;   // zero for the next call
   if (n <= k) {   // uniform
     for (int j = tid; j < k; j += kTopkThreads) out[j] = j < n ? j : -1;
     return;
@@ -681,22 +689,31 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pairs(TopkArgs a) {
   const int nb = (n + kScorePartKeys - 1) / kScorePartKeys;   // <= kPairMaxParts (host check)
 
   // ---- 1. global cumulative histogram and b0
-  uint32_t c0 = 0, c1 = 0;
+  if (rowh) {
+    // C[b] = the row's keys with top bits >= b: thread t holds bin 1023 - t, so the inclusive
+    // scan over threads is C of its bin
+    __syncthreads();   // C cleared
+    const uint32_t incl = block_exclusive_scan(rcount, wave_tot, nullptr) + rcount;
+    C[kTopBins - 1 - tid] = incl;
+    __syncthreads();
+  } else {
+    uint32_t c0 = 0, c1 = 0;
 #pragma unroll
-  for (int q = 0; q < kPartLoads; ++q) {
-    const uint32_t on = pg + kPartGroups * q < nb ? 0xffffffffu : 0u;
-    c0 += pw[q] & 0xffffu & on;
-    c1 += (pw[q] >> 16) & on;
+    for (int q = 0; q < kPartLoads; ++q) {
+      const uint32_t on = pg + kPartGroups * q < nb ? 0xffffffffu : 0u;
+      c0 += pw[q] & 0xffffu & on;
+      c1 += (pw[q] >> 16) & on;
+    }
+    for (int p = pg + kPartGroups * kPartLoads; p < nb; p += kPartGroups) {   // rows past 32 parts
+      const uint32_t w = ph[(int64_t)p * kPartWords + pwd];
+      c0 += w & 0xffffu;
+      c1 += w >> 16;
+    }
+    __syncthreads();   // C cleared
+    atomicAdd(&C[2 * pwd], c0);
+    atomicAdd(&C[2 * pwd + 1], c1);
+    __syncthreads();
   }
-  for (int p = pg + kPartGroups * kPartLoads; p < nb; p += kPartGroups) {   // rows past 32 parts
-    const uint32_t w = ph[(int64_t)p * kPartWords + pwd];
-    c0 += w & 0xffffu;
-    c1 += w >> 16;
-  }
-  __syncthreads();   // C cleared
-  atomicAdd(&C[2 * pwd], c0);
-  atomicAdd(&C[2 * pwd + 1], c1);
-  __syncthreads();
   {
     // C is non-increasing in b and C[0] = n > k: exactly one bin satisfies this
     const uint32_t here = C[tid], next = tid + 1 < kTopBins ? C[tid + 1] : 0u;
@@ -709,15 +726,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pairs(TopkArgs a) {
   const uint32_t b0 = sel_res[0], above0 = sel_res[1];
 
   // ---- 2. candidates per part: cum_p[b0]
-  if (pwd == (int)(b0 >> 1)) {
+  if (rowh) {
+    for (int p = tid; p < nb; p += kTopkThreads)
+      cnt[p] = a.part_hist[((int64_t)i * a.part_ld + p) * kTopBins + b0];
+  } else {
+    if (pwd == (int)(b0 >> 1)) {
 #pragma unroll
-    for (int q = 0; q < kPartLoads; ++q) {
-      const int p = pg + kPartGroups * q;
-      if (p < nb) cnt[p] = (b0 & 1u) ? (pw[q] >> 16) : (pw[q] & 0xffffu);
+      for (int q = 0; q < kPartLoads; ++q) {
+        const int p = pg + kPartGroups * q;
+        if (p < nb) cnt[p] = (b0 & 1u) ? (pw[q] >> 16) : (pw[q] & 0xffffu);
+      }
     }
+    for (int p = kPartGroups * kPartLoads + tid; p < nb; p += kTopkThreads)
+      cnt[p] = a.part_hist[((int64_t)i * a.part_ld + p) * kTopBins + b0];
   }
-  for (int p = kPartGroups * kPartLoads + tid; p < nb; p += kTopkThreads)
-    cnt[p] = a.part_hist[((int64_t)i * a.part_ld + p) * kTopBins + b0];
   for (int j = tid; j < 2 * kMapWords; j += kTopkThreads) gtmap[j] = 0;
   __syncthreads();
   // exclusive scan of the counts over parts (four parts per thread)

@@ -196,8 +196,10 @@ def test_index_validation(lib):
     assert call(p=pool(ratio=4, dim=128, dtype=hyb.FP8_E4M3)) == hyb.HYB_ENOTSUP
     assert call(heads=128, p=pool(ratio=4, dim=128, dtype=hyb.F32)) == hyb.HYB_ENOTSUP
     # hand-off pairs [16][32 x 1024] uint2, then the cumulative histograms [16][32][1024] uint16
+    # a 1 MiB per-row histogram block (256 rows x 1024 bins x 4 B, zero between calls), then
+    # per 1024-key part: bucketed (key, index) pairs and a cumulative uint16 histogram
     assert lib.hyb_index_topk_workspace_bytes(16, 131071, 128, 4) == \
-        16 * 32 * 1024 * 8 + 16 * 32 * 1024 * 2
+        (1 << 20) + 16 * 32 * 1024 * 8 + 16 * 32 * 1024 * 2
     assert lib.hyb_topk(FAKE, 10, FAKE, 4, 20, 8, FAKE, None) == hyb.HYB_EINVAL   # ld < max_len
     assert lib.hyb_topk(FAKE, 20, FAKE, 4, 20, 0, FAKE, None) == hyb.HYB_EINVAL   # k = 0
     assert lib.hyb_topk(None, 20, FAKE, 4, 20, 8, FAKE, None) == hyb.HYB_EINVAL

@@ -247,8 +247,7 @@ def test_exact_arithmetic_topk_is_bit_exact(gpu_lib):
     ipool = to_oracle_pool(wl.idx_pool)
     sel = oracle_select(wl, ipool, range(3))
     got = gpu_topk(hyb, wl).cpu().numpy()
-    ld = hyb.hyb_index_topk_workspace_bytes(3, wl.max_seq_len - 1, 128, 4) // 4 // 3
-    scores = torch.zeros(3, ld, device=DEV)
+    scores = torch.zeros(3, wl.max_seq_len // 4 + 1, device=DEV)   # >= the visible C4 entries
     hyb.hyb_index_score(wl.idx_q, wl.idx_w, wl.seq_lens - 1, wl.max_seq_len - 1, wl.idx_pool, scores)
     sync()
     for b in range(3):
@@ -766,7 +765,7 @@ def test_c4_decode_step_graph_replay(gpu_lib):
     hist = torch.empty(hshape, dtype=torch.int16, device=DEV)
     topk = torch.empty(B, wl.k, dtype=I32, device=DEV)
     out = torch.empty_like(wl.q)
-    ws = torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, D, L, 4, wl.k), dtype=torch.uint8,
+    ws = torch.zeros(hyb.hyb_attn_decode_workspace_bytes(B, 64, D, L, 4, wl.k), dtype=torch.uint8,
                      device=DEV)
     x_new = W.to_storage(W.randn((B, D), g, DEV), "bf16")
     cu = torch.arange(0, B + 1, dtype=I32, device=DEV)

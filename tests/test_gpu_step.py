@@ -37,7 +37,7 @@ def _buffers(hyb, lens, seed, grow=0, idx_compress=False):
         cu=torch.arange(0, B + 1, dtype=I32, device=DEV), start=(wl.seq_lens - 1).contiguous(),
         swa=wl.swa, comp=wl.comp, state=W.to_storage(W.randn((B, 4, D), g, DEV), "bf16"),
         out=torch.empty_like(wl.q),
-        workspace=torch.empty(hyb.hyb_attn_decode_workspace_bytes(B, 64, D, L, 4, wl.k),
+        workspace=torch.zeros(hyb.hyb_attn_decode_workspace_bytes(B, 64, D, L, 4, wl.k),
                               dtype=torch.uint8, device=DEV),
         max_seq_len=L, idx_q=wl.idx_q, idx_w=wl.idx_w, idx_pool=wl.idx_pool,
         keys=torch.empty(kshape, dtype=I32, device=DEV),
