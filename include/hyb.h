@@ -368,10 +368,13 @@ int32_t hyb_attn_decode_compress(const void* q, int32_t q_dtype, const int32_t* 
  * read. Their x, state and output pools must not overlap q, out, topk_out or the workspace.
  * Arguments as in hyb_index_topk (q_idx [batch][idx_heads][idx_pool->dim], w [batch][idx_heads])
  * and hyb_attn_decode; workspace sized by hyb_decode_step_workspace_bytes with the same batch,
- * n_heads, dim, max_seq_len, comp ratio, k (ignored for C128) and window. A C4 step's workspace,
- * like hyb_index_topk's, starts with 1 MiB that must be zero before its first use (every call
- * leaves it zero).
+ * n_heads, dim, max_seq_len, comp ratio, k (ignored for C128) and window. A C4 step's workspace
+ * starts with HYB_STEP_ZERO_BYTES that must be zero before its first use (per-row counts; every
+ * call leaves them zero). With the MFMA attention (64 heads x 512 dims, bf16 query) and batch
+ * <= 256 the attention workgroups select their rows' top k themselves from the indexer's
+ * hand-off (no separate selection kernel); the rows are the same.
  * ------------------------------------------------------------------------------------------ */
+#define HYB_STEP_ZERO_BYTES ((1ull << 20) + 1024ull)
 size_t hyb_decode_step_workspace_bytes(int32_t batch, int32_t n_heads, int32_t dim,
                                        int32_t max_seq_len, int32_t comp_ratio, int32_t k,
                                        int32_t window);

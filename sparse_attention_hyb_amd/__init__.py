@@ -318,6 +318,7 @@ def hyb_index_topk(q_idx, w, q_pos, max_pos: int, idx_pool, k: int, out_idx, win
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # HYB_NOALLOC_SCRATCH_BYTES
+STEP_ZERO_BYTES = (1 << 20) + 1024   # HYB_STEP_ZERO_BYTES: a C4 step workspace's leading zero block
 
 
 def hyb_index_topk_noalloc(q_idx, w, q_pos, max_pos: int, idx_pool, k: int, out_idx,

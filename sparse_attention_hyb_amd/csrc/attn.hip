@@ -28,6 +28,7 @@
 
 #include "common.h"
 #include "compress_dev.h"
+#include "select_dev.h"
 
 namespace hyb {
 
@@ -69,7 +70,7 @@ __device__ __forceinline__ QueryKeys query_keys(const AttnArgs& a, int i) {
   k.ws = window_start(k.p, a.window);
   k.n_win = k.p - k.ws + 1;
   k.nv = n_visible(k.p, a.comp.ratio, a.window);
-  k.n_keys = k.n_win + (a.topk ? a.k : k.nv);
+  k.n_keys = k.n_win + ((a.topk || a.sel.pairs) ? a.k : k.nv);
   return k;
 }
 
@@ -290,8 +291,13 @@ struct Stage<true> {
 // probability buffer written in iteration t was last read in iteration t-1.
 // fp8 pools: codes are widened to bf16 exactly; the per-entry scale multiplies the score before
 // the softmax and the probability before PV (so no rounding of scaled values).
-template <bool kFp8, bool kDirect>
-__global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
+// kSel: the decode step's form, which selects each query's top k itself from the indexer's
+// hand-off (every workgroup of the query, before its keys are resolved; see select_finish) and
+// clears the row's bin counts for the next call once all of the query's workgroups have read them.
+// Workgroups from n_split x n_q on run the compressor calls c0 (n_c0 of them), then c1.
+template <bool kFp8, bool kDirect, bool kSel>
+__global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0, CompressArgs c1,
+                                                    int n_c0, int n_c1) {
   __shared__ __attribute__((aligned(16))) uint16_t ktile[3 * kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t ptile[2 * kMH * kPPitch];
   __shared__ __attribute__((aligned(16))) float alpha_s[2 * kMH];
@@ -301,12 +307,36 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float kscale[3 * kKT];
   __shared__ float lfin[kMH];
   __shared__ float2 orope[kMaxRopePairs];   // RoPE(-p) table of the one-split output
+  __shared__ int32_t lsel[kSel ? kMaxTopK : 1];   // the query's selected compressed entries
+  __shared__ uint32_t last_reader;
+  static_assert(sizeof(ktile) >= kCompressFusedLds, "a compressor workgroup fits the tile buffers");
+  static_assert(!kSel || sizeof(ktile) >= kSelLdsWords * sizeof(uint32_t), "the selection fits the tile buffers");
 
-  const int logical = xcd_logical(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
+  const int n_attn = a.n_split * a.n_q;
+  const int bid = blockIdx.x + blockIdx.y * gridDim.x;
+  if (bid >= n_attn) {   // compressor workgroups riding along (first four waves; all take barriers)
+    const int k = bid - n_attn;
+    if (k < n_c0) compress_fused<4>(c0, k, reinterpret_cast<float*>(ktile));
+    else compress_fused<4>(c1, k - n_c0, reinterpret_cast<float*>(ktile));
+    return;
+  }
+  const int logical = xcd_logical(bid, n_attn);
   const int sp = logical % a.n_split, i = logical / a.n_split;
+  SelRegs sreg;
+  if constexpr (kSel) select_issue(a.sel, i, sreg);   // the hand-off loads go out first
   const QueryKeys qk = query_keys(a, i);
   const int j_begin = sp * a.chunk, j_end = min(qk.n_keys, j_begin + a.chunk);
   const int tid = threadIdx.x;
+  if constexpr (kSel) {
+    // Every workgroup of the query selects (the first one also writes the top-k row out); one with
+    // no keys of its own (j_begin >= n_keys, uniform) does not. Then each counts itself as done
+    // reading the row's bin counts - the selection's first scan has consumed them - and the last
+    // one clears them at the end.
+    if (j_begin < qk.n_keys)
+      select_finish(a.sel, i, qk.nv, a.k, reinterpret_cast<uint32_t*>(ktile), lsel,
+                    sp == 0 && a.sel.out != nullptr, sreg);
+    if (tid == 0) last_reader = atomicAdd(a.sel.row_done + i, 1u) == (uint32_t)(a.n_split - 1) ? 1u : 0u;
+  }
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool scorer = wave < 4;
@@ -354,10 +384,13 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
         win[r] = j < qk.n_win;
         g[r] = win[r] ? qk.ws + j : j - qk.n_win;   // window position or compressed slot
       }
-      if (a.topk != nullptr) {
+      if (kSel || a.topk != nullptr) {
         int tv[kR];
 #pragma unroll
-        for (int r = 0; r < kR; ++r) tv[r] = a.topk[(int64_t)i * a.k + min(max(g[r], 0), a.k - 1)];
+        for (int r = 0; r < kR; ++r) {
+          const int c = min(max(g[r], 0), a.k - 1);
+          tv[r] = kSel ? lsel[c] : a.topk[(int64_t)i * a.k + c];
+        }
 #pragma unroll
         for (int r = 0; r < kR; ++r)
           if (!win[r]) g[r] = tv[r];
@@ -683,6 +716,13 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a) {
     role(std::true_type{});
   else
     role(std::false_type{});
+  if constexpr (kSel) {
+    if (last_reader) {   // uniform: every workgroup of the query has read the row's bin counts
+      uint32_t* rh = a.sel.row_hist + (int64_t)i * kTopBins;
+      for (int j = tid; j < kTopBins; j += 512) rh[j] = 0u;
+      if (tid == 0) a.sel.row_done[i] = 0u;
+    }
+  }
 }
 // ------------------------------------------------------------------------------------------
 // Combine: merge the split partials, inverse RoPE at the query position, cast.
@@ -1001,17 +1041,17 @@ hipError_t launch_attention_kernel(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.n_q);
   if (a.use_mfma) {
     const bool direct = a.n_split == 1 && a.out_dtype == BF16;   // writes_output(a)
+    const CompressArgs none{};
+#define HYB_ATTN_MFMA(F, D) \
+  hipLaunchKernelGGL((attn_mfma<F, D, false>), grid, dim3(512), 0, s, a, none, none, 0, 0)
     if (a.swa.dtype == FP8) {
-      if (direct)
-        hipLaunchKernelGGL((attn_mfma<true, true>), grid, dim3(512), 0, s, a);
-      else
-        hipLaunchKernelGGL((attn_mfma<true, false>), grid, dim3(512), 0, s, a);
+      if (direct) HYB_ATTN_MFMA(true, true);
+      else HYB_ATTN_MFMA(true, false);
     } else {
-      if (direct)
-        hipLaunchKernelGGL((attn_mfma<false, true>), grid, dim3(512), 0, s, a);
-      else
-        hipLaunchKernelGGL((attn_mfma<false, false>), grid, dim3(512), 0, s, a);
+      if (direct) HYB_ATTN_MFMA(false, true);
+      else HYB_ATTN_MFMA(false, false);
     }
+#undef HYB_ATTN_MFMA
   } else {
     size_t lds = sizeof(float) * ((size_t)2 * a.n_heads * a.dim + (size_t)a.n_heads * kGenTile +
                                   3 * (size_t)a.n_heads);
@@ -1039,6 +1079,40 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(attn_combine<uint16_t>, cgrid, dim3(256), lds, s, a, hpw);
   else
     hipLaunchKernelGGL(attn_combine<float>, cgrid, dim3(256), lds, s, a, hpw);
+  return hipGetLastError();
+}
+
+// The fused selection pays off while every part's candidates usually lie among its prefetched
+// pairs: at most kSelFusedParts parts per row (contexts up to 256K tokens at ratio 4), 64 or more
+// pairs per part. Longer rows go through the selection kernel.
+constexpr int kSelFusedParts = kSelPrefetch / 64;
+bool attention_select_supported(const AttnArgs& a) {
+  return a.use_mfma && a.sel.pairs != nullptr && a.k <= kMaxTopK && a.n_q <= kRowHistRows &&
+         (a.sel.max_nv + kScorePartKeys - 1) / kScorePartKeys <= kSelFusedParts;
+}
+
+hipError_t launch_attention_select(const AttnArgs& a, const SideWork* side, hipStream_t s) {
+  if (a.n_q == 0) return hipSuccess;
+  if (!attention_select_supported(a)) return hipErrorInvalidValue;
+  SideWork none{};
+  const SideWork& sw = side ? *side : none;
+  const dim3 grid(a.n_split * a.n_q + sw.n[0] + sw.n[1]);
+  const bool direct = writes_output(a);
+#define HYB_ATTN_SEL(F, D) \
+  hipLaunchKernelGGL((attn_mfma<F, D, true>), grid, dim3(512), 0, s, a, sw.c[0], sw.c[1], sw.n[0], sw.n[1])
+  if (a.swa.dtype == FP8) {
+    if (direct) HYB_ATTN_SEL(true, true);
+    else HYB_ATTN_SEL(true, false);
+  } else {
+    if (direct) HYB_ATTN_SEL(false, true);
+    else HYB_ATTN_SEL(false, false);
+  }
+#undef HYB_ATTN_SEL
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || direct) return e;
+  const int hpw = combine_heads_per_wg(a);
+  const dim3 cgrid((a.n_heads + hpw - 1) / hpw, a.n_q);
+  hipLaunchKernelGGL(attn_combine<uint16_t>, cgrid, dim3(256), combine_lds_bytes(a.n_split), s, a, hpw);
   return hipGetLastError();
 }
 

@@ -14,6 +14,8 @@
 
 #include "hyb_internal.h"
 #include "hyb_probe_internal.h"
+static_assert(hyb::kMaxTopK == HYB_KMAX, "the kernels size their top-k buffers for HYB_KMAX");
+static_assert(hyb::kRowHistBytes + hyb::kRowDoneBytes == HYB_STEP_ZERO_BYTES, "the step's zero block");
 #include "compress_dev.h"
 
 namespace {
@@ -545,9 +547,9 @@ int32_t hyb_index_topk(const void* q_idx, int32_t q_dtype, const float* w, const
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-// Workspace of hyb_decode_step: [per-row bin counts of the selector (C4; zero between calls)]
-// [top-k rows (C4, when the caller keeps none)][indexer hand-off (C4)][attention partials], each
-// part 256-byte aligned.
+// Workspace of hyb_decode_step: [per-row bin counts and reader counts of the selection (C4; zero
+// between calls)][top-k rows (C4, when the caller keeps none)][indexer hand-off (C4)][attention
+// partials], each part 256-byte aligned.
 static size_t step_ws_bytes(int32_t batch, int32_t n_heads, int32_t dim, int32_t max_seq_len,
                             int32_t comp_ratio, int32_t k, int32_t window) {
   if (batch <= 0 || max_seq_len < 1 || window <= 0 || (comp_ratio != 4 && comp_ratio != 128)) return 0;
@@ -555,7 +557,7 @@ static size_t step_ws_bytes(int32_t batch, int32_t n_heads, int32_t dim, int32_t
   size_t n = 0;
   if (comp_ratio == 4) {
     if (k < 1 || k > HYB_KMAX) return 0;
-    n += hyb::kRowHistBytes;
+    n += hyb::kRowHistBytes + hyb::kRowDoneBytes;
     n += align256((size_t)batch * k * sizeof(int32_t));
     n += align256(topk_ws_bytes(batch, (int64_t)score_ld((int32_t)max_pos, window, comp_ratio)));
   }
@@ -610,9 +612,12 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
   hyb::SideWork side{};
   int n_side = 0;
   bool done[2] = {false, false};
+  bool fused = false;   // C4: the attention workgroups select their rows themselves
   if (sparse) {
     uint32_t* row_hist = reinterpret_cast<uint32_t*>(ws);
     ws += hyb::kRowHistBytes;
+    uint32_t* row_done = reinterpret_cast<uint32_t*>(ws);
+    ws += hyb::kRowDoneBytes;
     if (!topk) topk = reinterpret_cast<int32_t*>(ws);
     ws += align256((size_t)batch * k * sizeof(int32_t));
     const int64_t ld = (int64_t)score_ld((int32_t)max_pos, window, sa.pool.ratio);
@@ -627,10 +632,20 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
     sa.part_ld = (int32_t)topk_part_ld(ld);
     sa.row_hist = batch <= hyb::kRowHistRows ? row_hist : nullptr;
     ws += align256(topk_ws_bytes(batch, ld));
-    // compressor calls that four waves can run ride along with the indexer's one-query kernel
+    if (sa.row_hist) {
+      c.args.sel = hyb::SelDev{reinterpret_cast<const uint32_t*>(sa.scores), pld, sa.part_hist,
+                               sa.part_ld, row_hist, row_done, topk_out,
+                               (int32_t)visible(max_pos, sa.pool.ratio, window)};
+      c.args.k = k;
+      fused = hyb::attention_select_supported(c.args);
+      if (fused) c.args.topk = nullptr;   // the workgroups' own selections take its place
+      else c.args.sel = hyb::SelDev{};
+    }
+    // compressor calls that four waves can run ride along with the attention (fused selection)
+    // or with the indexer's one-query kernel
     const bool one_query_kernel = sa.n_heads == 64 && sa.pool.dim == 128 && sa.q_dtype == HYB_BF16 &&
                                   (sa.pool.dtype == HYB_BF16 || sa.pool.dtype == HYB_FP4_E2M1);
-    for (int j = 0; j < n_compress && one_query_kernel; ++j) {
+    for (int j = 0; j < n_compress && (one_query_kernel || fused); ++j) {
       if (hyb::compress_fusable(ca[j])) {
         side.c[n_side] = ca[j];
         side.n[n_side] = hyb::compress_fused_groups(ca[j]);
@@ -638,7 +653,11 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
         done[j] = true;
       }
     }
-    HYB_TRY(launch_status(hyb::launch_index_score(sa, st, n_side ? &side : nullptr), op));
+    HYB_TRY(launch_status(hyb::launch_index_score(sa, st, n_side && !fused ? &side : nullptr), op));
+  }
+  if (sparse && !fused) {
+    const int64_t ld = (int64_t)score_ld((int32_t)max_pos, window, sa.pool.ratio);
+    const int64_t pld = pair_words((int64_t)topk_part_ld(ld));
     hyb::TopkArgs t{};
     t.scores = sa.scores;
     t.ld = pld;
@@ -661,7 +680,9 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
   int first = -1;   // a C128 layer's first pending call rides along with the combine
   for (int j = 0; j < n_compress; ++j)
     if (!done[j]) { first = j; break; }
-  if (!sparse && first >= 0) {
+  if (fused) {
+    HYB_TRY(launch_status(hyb::launch_attention_select(c.args, n_side ? &side : nullptr, st), op));
+  } else if (!sparse && first >= 0) {
     HYB_TRY(launch_status(hyb::launch_attention_compress(c.args, ca[first], st), op));
     done[first] = true;
   } else {

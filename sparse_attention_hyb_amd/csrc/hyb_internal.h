@@ -109,9 +109,11 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s, const SideWork*
 constexpr int kTopBits = 10;                  // the selector's first radix pass (then 11 + 11)
 constexpr int kTopBins = 1 << kTopBits;
 constexpr int kScorePartKeys = 1024;          // keys per partial histogram (one indexer workgroup)
+constexpr int kMaxTopK = 2048;                // largest k of a top-k selection (HYB_KMAX)
 constexpr int kTopkMaxParts = 4096;           // parts per row the hand-off selector takes
 constexpr int kRowHistRows = 256;             // queries of one call with a per-row histogram
 constexpr size_t kRowHistBytes = (size_t)kRowHistRows * kTopBins * sizeof(uint32_t);
+constexpr size_t kRowDoneBytes = (size_t)kRowHistRows * sizeof(uint32_t);   // per-row reader counts
 
 // ---- top-k ----------------------------------------------------------------------------------
 // Row lengths come from `lengths` or, if null, from n_visible(p_i, ratio, window) of the queries.
@@ -137,6 +139,19 @@ struct TopkArgs {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 // ---- attention ------------------------------------------------------------------------------
+// The indexer's hand-off (see ScoreArgs) as a workgroup that selects one row's top k itself reads
+// it: the attention kernel of a decode step that fuses the selection.
+struct SelDev {
+  const uint32_t* pairs;        // row i: (key, index) word pairs at pairs + i * ld, part p at 2048 p
+  int64_t ld;                   // words per row (>= 2048 * part_ld)
+  const uint16_t* part_hist;    // [n_q][part_ld][kTopBins] cumulative counts per part
+  int32_t part_ld;
+  uint32_t* row_hist;           // [n_q][kTopBins] bin counts per row; zero again after the call
+  uint32_t* row_done;           // [n_q] workgroups done reading row_hist; zero again after the call
+  int32_t* out;                 // optional [n_q][k] selected rows (logical indices)
+  int32_t max_nv;               // host bound on any row's length
+};
+
 struct AttnArgs {
   const void* q;
   int32_t q_dtype;
@@ -165,6 +180,9 @@ struct AttnArgs {
   // bf16 already); m (natural-log units) and l per split and head in part_ml [n_q][n_split][2][n_heads].
   void* part_o;
   float* part_ml;
+  // Decode step with the selection fused (sel.pairs set): each workgroup of query i selects the
+  // top k of row i from the hand-off itself instead of reading topk.
+  SelDev sel;
 };
 
 // Split plan and workspace size for an attention call; identical for sizing and for launching.
@@ -178,6 +196,10 @@ struct AttnPlan {
 AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_keys,
                         int32_t q_dtype, int32_t pool_dtype);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// Attention with the selection fused (a.sel set, the MFMA kernel) and up to two compressor calls
+// riding along with its launch, then the combine.
+hipError_t launch_attention_select(const AttnArgs& a, const SideWork* side, hipStream_t s);
+bool attention_select_supported(const AttnArgs& a);
 hipError_t launch_attention_compress(const AttnArgs& a, const CompressArgs& c, hipStream_t s);
 
 }  // namespace hyb

@@ -17,6 +17,7 @@
 // those in it), they are compacted with their indices into LDS in index order and the other two
 // passes and the final selection run over that list instead of over every key of the row.
 #include "common.h"
+#include "select_dev.h"
 
 namespace hyb {
 
@@ -26,64 +27,7 @@ constexpr int kTopkWaves = kTopkThreads / 64;
 // Exclusive scan of a 32-bit value over the workgroup (thread order); also returns the total.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot,
                                                          uint32_t* total_out) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_inclusive_scan(v);
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    const uint32_t t = wave_tot[w];
-    before += w < wave ? t : 0u;
-    total += t;
-  }
-  __syncthreads();
-  if (total_out) *total_out = total;
-  return before + incl - v;
-}
-
-// Histograms live in LDS with one padding word after every 32 bins: bin b at hp(b). A lane that
-// reads 32 consecutive bins then starts 33 words after its neighbour, so the 64 lanes of a wave
-// hit 64 different banks.
-__device__ __forceinline__ int hp(uint32_t b) { return (int)(b + (b >> 5)); }
-constexpr int kHistWords = 2048 + 2048 / 32;   // padded 2048-bin histogram
-
-// Bin holding the `remaining`-th largest key of an nbins-bin histogram (nbins = 1024 or 2048,
-// bins in ascending key order) and the number of keys in the bins above it. Wave 0 searches:
-// lane l sums the 32-bin group [nbins - 32(l+1), nbins - 32l), one wave scan finds the group
-// that holds the bin, a second scan over that group's 32 bins (one per lane, descending) finds
-// the bin. The result reaches every thread through LDS (one barrier). The histogram must hold at
-// least `remaining` keys.
-__device__ __forceinline__ void select_bin(const uint32_t* hist, int nbins, uint32_t remaining,
-                                           uint32_t* res, uint32_t* bin, uint32_t* above) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int groups = nbins >> 5;
-    uint32_t sum = 0;
-    if (lane < groups) {
-      const uint32_t* g = hist + 33 * (groups - 1 - lane);
-#pragma unroll
-      for (int m = 0; m < 32; ++m) sum += g[m];
-    }
-    const uint32_t incl = wave_inclusive_scan(sum);
-    const uint32_t excl = incl - sum;
-    const uint64_t own = __ballot(excl < remaining && incl >= remaining);
-    const int grp = own ? __builtin_ctzll(own) : 0;
-    const uint32_t grp_above = (uint32_t)__builtin_amdgcn_readlane((int)excl, grp);
-    const int top = nbins - 1 - 32 * grp;
-    const uint32_t c = lane < 32 ? hist[hp(top - lane)] : 0u;
-    const uint32_t incl2 = wave_inclusive_scan(c) + grp_above;
-    const uint32_t excl2 = incl2 - c;
-    const uint64_t hit = __ballot(lane < 32 && excl2 < remaining && incl2 >= remaining);
-    const int j = hit ? __builtin_ctzll(hit) : 0;
-    if (lane == j) {
-      res[0] = (uint32_t)(top - j);
-      res[1] = excl2;
-    }
-  }
-  __syncthreads();
-  *bin = res[0];
-  *above = res[1];
+  return block_scan_excl<kTopkThreads>(v, wave_tot, total_out);
 }
 
 // Each thread owns kPer consecutive scores of a chunk of kChunk, held in registers as keys. A
@@ -100,8 +44,6 @@ constexpr int kTopWords = kTopBins + kTopBins / 32;   // padded first-pass histo
 constexpr size_t kTopkLds = sizeof(uint32_t) * ((size_t)kTopkThreads * kStagePitch + kHistWords);
 static_assert(kTopkWaves * kTopWords <= kTopkThreads * kStagePitch, "per-wave histograms fit");
 static_assert(kTopBins == kTopkThreads, "the counted first pass merges one bin per thread");
-constexpr int kShift0 = 32 - kTopBits;       // 22: first pass = key bits 22..31
-constexpr int kBits12 = kShift0 / 2;         // 11: second pass bits 11..21, third 0..10
 constexpr int kListCap = 16384;   // short-list entries: keys then indices in the staging area
 static_assert(2 * kListCap <= kTopkThreads * kStagePitch, "short list fits the staging area");
 

@@ -127,3 +127,51 @@ def test_c128_decode_step_equals_separate_calls(gpu_lib):
     for s in (0, 2):
         o = O.hybrid_query(q[s], lens[s] - 1, s, swa_o, comp_o, 128, 1 / math.sqrt(D), 64, 1e4, None)
         assert_abs_close(to_f64(out_b[s]), o)
+
+
+def _step_no_compress(hyb, wl, topk, out, ws):
+    hyb.hyb_decode_step(wl.q, wl.seq_lens, wl.max_seq_len, wl.swa, wl.comp, out, idx_q=wl.idx_q,
+                        idx_w=wl.idx_w, idx_pool=wl.idx_pool, k=wl.k, topk_out=topk, workspace=ws)
+
+
+@pytest.mark.parametrize("case", ["mixed", "long", "ties"])
+def test_c4_step_selects_in_attention_repeatedly(gpu_lib, case):
+    """The C4 step's attention workgroups select their rows from the indexer's hand-off. Over
+    three calls with one workspace the rows equal hyb_index_topk's and the outputs
+    hyb_attn_decode's bit for bit, and the workspace's leading zero block (per-row counts) is zero
+    again after every call. Cases: mixed lengths including rows no longer than k; a 2^18-token row
+    (64 parts of 64 prefetched pairs each, which a part's candidates can outrun); dyadic indexer
+    values whose scores tie heavily."""
+    hyb = gpu_lib
+    lens = {"mixed": [700, 2100, 2200, 40000, 131072],
+            "long": [262144, 150000],
+            "ties": [3000, 70001, 131072]}[case]
+    wl = W.sparse_decode(DEV, seed=31, batch=len(lens), ctx=lens)
+    if case == "ties":
+        g = torch.Generator(device=DEV).manual_seed(12)
+        vals = torch.tensor([0.0, 0.25, -0.25, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0], device=DEV)
+        wvals = torch.tensor([0.25, -0.25, 0.5, -0.5, 1.0, -1.0], device=DEV)
+        wl.idx_q = vals[torch.randint(0, 9, wl.idx_q.shape, generator=g, device=DEV)].to(torch.bfloat16)
+        wl.idx_w = wvals[torch.randint(0, 6, wl.idx_w.shape, generator=g, device=DEV)]
+        wl.idx_pool.data = vals[torch.randint(0, 9, wl.idx_pool.data.shape, generator=g,
+                                              device=DEV)].to(torch.bfloat16)
+    B, L = wl.batch, wl.max_seq_len
+    want_topk = torch.full((B, wl.k), -7, dtype=I32, device=DEV)
+    want_out = torch.empty_like(wl.q)
+    hyb.hyb_index_topk(wl.idx_q, wl.idx_w, wl.seq_lens - 1, L - 1, wl.idx_pool, wl.k, want_topk)
+    hyb.hyb_attn_decode(wl.q, wl.seq_lens, L, wl.swa, wl.comp, want_out, topk_idx=want_topk, k=wl.k)
+    ws = torch.zeros(hyb.hyb_decode_step_workspace_bytes(B, 64, wl.dim, L, 4, wl.k), dtype=torch.uint8,
+                     device=DEV)
+    zero = hyb.STEP_ZERO_BYTES
+    for call in range(3):
+        topk = torch.full((B, wl.k), -9, dtype=I32, device=DEV)
+        out = torch.empty_like(wl.q)
+        _step_no_compress(hyb, wl, topk, out, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(topk, want_topk), call
+        assert torch.equal(out, want_out), call
+        assert int(torch.count_nonzero(ws[:zero])) == 0, call
+    short = [b for b, n in enumerate(lens) if O.n_visible(n - 1, 4, 128) <= wl.k]
+    for b in short:   # rows no longer than k: every entry in order, then -1
+        nv = O.n_visible(lens[b] - 1, 4, 128)
+        assert list(topk[b].cpu().numpy()) == list(range(nv)) + [-1] * (wl.k - nv)
