@@ -25,7 +25,8 @@
  *     hyb_last_error() describes the most recent failure on the calling thread.
  *   - Faults inside kernels surface at the caller's next synchronisation. Kernels never
  *     dereference a block whose table entry is negative or >= num_blocks: such entries are
- *     treated as absent (skipped on write, masked out on read).
+ *     treated as absent (skipped on write, masked out on read); hyb_set_error_word makes the
+ *     kernels report entries >= num_blocks.
  *   - Positions are absolute, 0-based raw-token positions. A query at position p sees the
  *     raw window [max(0, p - window + 1), p] and the compressed entries 0 .. n_vis(p) - 1 with
  *     n_vis(p) = ceil(max(0, p - window + 1) / ratio) (every complete group that holds at least
@@ -101,6 +102,15 @@ typedef struct hyb_paged {
 
 int32_t hyb_abi_version(void);
 const char* hyb_status_str(int32_t status);
+
+/* hyb_set_error_word - optional detection of corrupt block tables: from now on, every kernel of
+ * the calling thread's current device that meets a block-table entry >= its pool's num_blocks ORs
+ * HYB_ERR_BAD_PAGE into *word (the entry still counts as absent, as the conventions say). word:
+ * a 4-byte-aligned device address on that device, owned by the caller, who zeroes it and reads it
+ * after synchronising; NULL turns the detection off for the device. Calls enqueued before this
+ * one are not affected. HYB_ELAUNCH when there is no current device. */
+#define HYB_ERR_BAD_PAGE 1u
+int32_t hyb_set_error_word(uint32_t* word);
 /* Thread-local description of the last non-OK status returned on this thread (host string,
  * owned by the library, valid until the next call on the thread). */
 const char* hyb_last_error(void);

@@ -28,7 +28,7 @@ KMAX = 2048
 DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp4": FP4_E2M1}
 
 EXPORTS = (
-    "hyb_abi_version", "hyb_status_str", "hyb_last_error", "hyb_compress", "hyb_swa_insert",
+    "hyb_abi_version", "hyb_status_str", "hyb_last_error", "hyb_set_error_word", "hyb_compress", "hyb_swa_insert",
     "hyb_q_norm_kv_insert", "hyb_gather_pages",
     "hyb_index_score", "hyb_topk", "hyb_index_score_keys", "hyb_topk_keys",
     "hyb_index_topk_workspace_bytes", "hyb_index_topk", "hyb_index_topk_noalloc",
@@ -85,6 +85,7 @@ _P, _I32, _I64, _SZ, _D, _F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, 
 _PP = ctypes.POINTER(hyb_paged)
 _SIGS = {
     "hyb_abi_version": (_I32, []),
+    "hyb_set_error_word": (_I32, [_P]),
     "hyb_status_str": (ctypes.c_char_p, [_I32]),
     "hyb_last_error": (ctypes.c_char_p, []),
     "hyb_compress": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _P, _P, _I32, _PP, _I32, _D, _F, _P]),
@@ -198,6 +199,15 @@ def _empty_workspace(nbytes: int, device):
 # ---------------------------------------------------------------------------------------------
 def hyb_abi_version() -> int:
     return load().hyb_abi_version()
+
+
+ERR_BAD_PAGE = 1   # HYB_ERR_BAD_PAGE
+
+
+def hyb_set_error_word(word) -> None:
+    """Report block-table entries >= num_blocks into `word` (a one-element int32 tensor on the
+    current device, zeroed by the caller), or stop reporting (None)."""
+    _check(load().hyb_set_error_word(_ptr(word)))
 
 
 def hyb_compress(x, cu_seqlens, start_pos, max_new_tokens: int, state, out_pool, rope_dim: int,

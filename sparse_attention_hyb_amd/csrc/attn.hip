@@ -419,6 +419,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0,
         const int per = w ? a.swa.per_block : a.comp.per_block;
         const int nbk = w ? a.swa.num_blocks : a.comp.num_blocks;
         idxr[r] = (lok[r] && phys[r] >= 0 && phys[r] < nbk) ? phys[r] * per + (g[r] - lb[r] * per) : -1;
+        if (lok[r]) note_bad_page(w ? a.swa : a.comp, phys[r]);
       }
 #pragma unroll
       for (int r = 0; r < kR; ++r) {

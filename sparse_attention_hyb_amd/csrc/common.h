@@ -56,6 +56,12 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
   return e == 0u ? 0x1p-127f : __uint_as_float(e << 23);
 }
 
+// A physical block id >= num_blocks in a table: recorded in the pool's error word when there is
+// one (the block still counts as absent).
+__device__ __forceinline__ void note_bad_page(const PoolDev& p, int phys) {
+  if (phys >= p.num_blocks && p.err != nullptr) atomicOr(p.err, kErrBadPage);
+}
+
 // Index of entry g of sequence `seq` in the flattened [num_blocks * per_block] entry array, or -1
 // when its block is absent or out of range (then nothing is read or written).
 __device__ __forceinline__ int64_t entry_index(const PoolDev& p, int seq, int g) {
@@ -63,6 +69,7 @@ __device__ __forceinline__ int64_t entry_index(const PoolDev& p, int seq, int g)
   int lb = g / p.per_block;
   if (lb >= p.max_blocks) return -1;
   int phys = p.block_table[(int64_t)seq * p.max_blocks + lb];
+  note_bad_page(p, phys);
   if (phys < 0 || phys >= p.num_blocks) return -1;
   return (int64_t)phys * p.per_block + (g - lb * p.per_block);
 }
@@ -77,9 +84,10 @@ __device__ __forceinline__ int n_visible(int p, int ratio, int window) {
   return (window_start(p, window) + ratio - 1) / ratio;
 }
 
-// RoPE angle brought to [-pi, pi] in double precision: k * 2pi is subtracted with 2pi split in
-// three parts (24 + 24 + 53 bits). For |angle| < 2^31, k < 2^29, so the first two products are
-// exact and the residue keeps full double precision.
+// RoPE angle brought to [-pi, pi] in double precision by Cody-Waite additive range reduction
+// (W. J. Cody and W. Waite, "Software Manual for the Elementary Functions", 1980): k * 2pi is
+// subtracted with 2pi split in three parts (24 + 24 + 53 bits). For |angle| < 2^31, k < 2^29, so
+// the first two products are exact and the residue keeps full double precision.
 __device__ __forceinline__ double rope_reduce(double ang) {
   constexpr double kInv2Pi = 0.15915494309189535;
   constexpr double kP1 = 6.2831854820251465;        // 2pi rounded to 24 bits

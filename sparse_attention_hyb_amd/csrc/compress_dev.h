@@ -322,6 +322,7 @@ __device__ __forceinline__ void compress_group(const CompressArgs& a, int gi, in
       }
       ss = wave_sum(ss);
       const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+      note_bad_page(a.out, phys);
       if (phys >= 0 && phys < a.out.num_blocks) {
         const int64_t idx = (int64_t)phys * a.out.per_block + (g - lb * a.out.per_block);
         const int rope_lo = D - a.rope_dim;

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -50,6 +51,19 @@ int64_t entry_bytes(int32_t dtype, int32_t dim) {
 }
 
 // Pool descriptor checks. ratio_mask bit 0: ratio 1, bit 1: ratio 4, bit 2: ratio 128.
+// Error words set by hyb_set_error_word, per device; g_err_set: whether any was ever set (until
+// then no call queries the current device for one).
+constexpr int kErrDevices = 64;
+std::atomic<uint32_t*> g_err_word[kErrDevices];
+std::atomic<bool> g_err_set{false};
+
+uint32_t* current_error_word() {
+  if (!g_err_set.load(std::memory_order_acquire)) return nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kErrDevices) return nullptr;
+  return g_err_word[dev].load(std::memory_order_acquire);
+}
+
 int check_pool(const hyb_paged* p, const char* op, const char* name, bool fp8_ok, bool fp4_ok,
                int ratio_mask, hyb::PoolDev* out) {
   if (!p) return fail(HYB_EINVAL, "%s: %s descriptor is NULL", op, name);
@@ -90,6 +104,7 @@ int check_pool(const hyb_paged* p, const char* op, const char* name, bool fp8_ok
   out->max_blocks = p->max_blocks;
   out->per_block = HYB_BLOCK_POSITIONS / r;
   out->entry_bytes = entry_bytes(p->dtype, p->dim);
+  out->err = current_error_word();
   return HYB_OK;
 }
 
@@ -251,6 +266,18 @@ size_t attn_ws(int32_t n_q, int32_t n_heads, int32_t dim, int64_t max_pos, int32
 }  // namespace
 
 extern "C" {
+
+int32_t hyb_set_error_word(uint32_t* word) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kErrDevices)
+    return fail(HYB_ELAUNCH, "hyb_set_error_word: no current device (%s)", hipGetErrorString(e));
+  if (word != nullptr && (reinterpret_cast<uintptr_t>(word) & 3u))
+    return fail(HYB_EINVAL, "hyb_set_error_word: the word must be 4-byte aligned");
+  g_err_word[dev].store(word, std::memory_order_release);
+  if (word != nullptr) g_err_set.store(true, std::memory_order_release);
+  return HYB_OK;
+}
 
 int32_t hyb_abi_version(void) { return HYB_ABI_VERSION; }
 

@@ -21,7 +21,11 @@ struct PoolDev {
   int32_t max_blocks;
   int32_t per_block;     // 256 / ratio
   int64_t entry_bytes;   // bytes of one entry in data
+  // Optional device word: a kernel that meets a table entry >= num_blocks ORs kErrBadPage into
+  // it (the entry still counts as absent). NULL: nothing is recorded.
+  uint32_t* err;
 };
+constexpr uint32_t kErrBadPage = 1u;
 
 // Query i -> (sequence, position): decode form (seq_lens != nullptr: seq = i, p = len - 1) or
 // prefill form (seq = q_seq ? q_seq[i] : i, p = q_pos[i]).

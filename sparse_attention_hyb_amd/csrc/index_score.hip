@@ -311,7 +311,9 @@ __global__ __launch_bounds__(256, 1) void score_mfma_reg(ScoreArgs a, CompressAr
       return bt[min(lb0 + j, a.pool.max_blocks - 1)];
     };
     auto phys_of = [&](int j, int v) {
-      return (lb0 + j < a.pool.max_blocks && v >= 0 && v < a.pool.num_blocks) ? v : -1;
+      if (lb0 + j >= a.pool.max_blocks) return -1;
+      note_bad_page(a.pool, v);
+      return (v >= 0 && v < a.pool.num_blocks) ? v : -1;
     };
     const int v0 = raw(min(tid, n_lb - 1));   // first entries: the load goes out before q and w's
     __builtin_amdgcn_sched_barrier(0);
@@ -607,6 +609,7 @@ __global__ __launch_bounds__(256, 3) void score_mfma_multi(ScoreArgs a) {
     for (int j = tid; j < n_lb; j += 256) {
       const int lb = lb0 + j;
       const int phys = lb < a.pool.max_blocks ? a.pool.block_table[(int64_t)sq * a.pool.max_blocks + lb] : -1;
+      note_bad_page(a.pool, phys);
       tbl[j] = (phys >= 0 && phys < a.pool.num_blocks) ? phys : -1;
     }
     __syncthreads();

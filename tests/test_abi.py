@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(hyb.EXPORTS) == names
@@ -340,3 +340,14 @@ def test_decode_step_validation(lib):
     assert lib.hyb_last_error().decode().startswith("hyb_decode_step")
     assert lib.hyb_decode_step_workspace_bytes(4, 64, 512, 100000, 128, 0, 128) == \
         lib.hyb_attn_decode_workspace_bytes(4, 64, 512, 100000, 128, 0, 128)
+
+
+def test_error_word_needs_a_device():
+    """hyb_set_error_word looks the current device up; with none it fails without side effects,
+    and pools checked afterwards carry no error word (argument checks never query a device)."""
+    lib = hyb.load()
+    st = lib.hyb_set_error_word(None)
+    if st == hyb.HYB_OK:
+        pytest.skip("a GPU is present")
+    assert st == hyb.HYB_ELAUNCH
+    assert lib.hyb_last_error().decode().startswith("hyb_set_error_word")
