@@ -39,15 +39,18 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_mfma_dma_c4_128k_hbm_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_mfma_reg_c4_128k_hbm_traffic.md")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the indexer score kernel from the committed counter summary, or None
-    when the kernel's sources have changed since the counters were taken (hash mismatch)."""
+C128_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_mfma_c128_1m_hbm_traffic.md")
+
+
+def measured_traffic(profile=TRAFFIC_PROFILE):
+    """HBM bytes per launch (or step) from a committed counter summary, or None when the kernels'
+    sources have changed since the counters were taken (hash mismatch)."""
     import hashlib
     try:
-        line = next(l for l in open(TRAFFIC_PROFILE) if l.startswith("traffic-json:"))
+        line = next(l for l in open(profile) if l.startswith("traffic-json:"))
     except (OSError, StopIteration):
         return None
     rec = json.loads(line.split(":", 1)[1])
@@ -290,7 +293,7 @@ def c128_dense(torch, hyb, W, BM, args, peak_meas):
         value=B * n / secs, unit="query-tokens/s", ms_per_step=ms, steps=n,
         hbm_frac_step=step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         roofline=roofline_hbm("C128 decode step (attn_mfma, then the combine with the compressor)",
-                              step_bytes, call_us, peak_meas, None,
+                              step_bytes, call_us, peak_meas, measured_traffic(C128_TRAFFIC_PROFILE),
                               attn_tflops=B * BM.attention_flops(8191 + 128) / (call_us * 1e-6) / 1e12),
         compress_raw_gbs=raw_bytes / comp_secs / 1e9,
         config={"workload": "c128_dense_decode", "batch": B, "context": L, "heads": 64, "dim": D,
