@@ -427,15 +427,18 @@ __global__ __launch_bounds__(256, 1) void score_mfma_reg(ScoreArgs a, CompressAr
         const int phys = __builtin_amdgcn_readfirstlane(tbl[(gb >> pb_shift) - lb0]);
         const int64_t e0 = (phys >= 0 ? ((int64_t)phys << pb_shift) : 0) + (gb & (per_block - 1));
         const uint8_t* kb = a.pool.data + e0 * kRow;
+        // every key is read once per query: nontemporal loads stream past the caches (a
+        // row-gather probe measured them 11-15 % faster than plain loads)
 #pragma unroll
         for (int j = 0; j < kLoads; ++j)
-          r.v[j] = *reinterpret_cast<const u32x4*>(kb + lane_off + j * (kFp4 ? 16 : 4) * kRow);
+          r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + lane_off + j * (kFp4 ? 16 : 4) * kRow));
         if constexpr (kFp4) r.sc = (reinterpret_cast<const uint32_t*>(a.pool.scale) + e0)[lane & 31];
       } else {
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
           const int n = (kFp4 ? 16 : 4) * j + nk;
-          r.v[j] = *reinterpret_cast<const u32x4*>(a.pool.data + entry_of(tb + n) * kRow + 16 * ck);
+          r.v[j] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(a.pool.data + entry_of(tb + n) * kRow + 16 * ck));
         }
         if constexpr (kFp4) r.sc = reinterpret_cast<const uint32_t*>(a.pool.scale)[entry_of(tb + (lane & 31))];
       }
