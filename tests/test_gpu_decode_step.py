@@ -129,6 +129,25 @@ def test_c128_decode_step_equals_separate_calls(gpu_lib):
         assert_abs_close(to_f64(out_b[s]), o)
 
 
+@pytest.mark.parametrize("lens", [[2048, 40959, 300000, 131072, 5000], [1 << 20] * 8])
+def test_c128_step_repeatedly(gpu_lib, lens):
+    """C128 steps over three calls with one workspace: the output equals hyb_attn_decode's bit for
+    bit every time. Five mixed lengths (1 to 8 splits of the longest); eight 2^20-token queries
+    (8 splits each, the benchmark's shape)."""
+    hyb = gpu_lib
+    wl = W.dense_decode(DEV, seed=23, batch=len(lens), ctx=lens)
+    B, D, L = wl.batch, wl.dim, wl.max_seq_len
+    want = torch.empty_like(wl.q)
+    hyb.hyb_attn_decode(wl.q, wl.seq_lens, L, wl.swa, wl.comp, want)
+    ws = torch.zeros(hyb.hyb_decode_step_workspace_bytes(B, 64, D, L, 128, 0), dtype=torch.uint8,
+                     device=DEV)
+    for call in range(3):
+        out = torch.empty_like(wl.q)
+        hyb.hyb_decode_step(wl.q, wl.seq_lens, L, wl.swa, wl.comp, out, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), call
+
+
 def _step_no_compress(hyb, wl, topk, out, ws):
     hyb.hyb_decode_step(wl.q, wl.seq_lens, wl.max_seq_len, wl.swa, wl.comp, out, idx_q=wl.idx_q,
                         idx_w=wl.idx_w, idx_pool=wl.idx_pool, k=wl.k, topk_out=topk, workspace=ws)

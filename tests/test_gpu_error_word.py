@@ -60,3 +60,24 @@ def test_bad_page_ids_are_reported(gpu_lib):
         bt[1, 3] = saved
     finally:
         hyb.hyb_set_error_word(None)
+
+
+def test_decode_steps_report_nothing_on_clean_inputs(gpu_lib):
+    """With the error word set, C4 and C128 decode steps over clean tables (mixed lengths, three
+    calls each) leave it zero."""
+    hyb = gpu_lib
+    word = torch.zeros(1, dtype=I32, device=DEV)
+    c4 = W.sparse_decode(DEV, seed=42, batch=11, ctx=[131072] * 6 + [9000, 20000, 3000, 70000, 65536])
+    c128 = W.dense_decode(DEV, seed=43, batch=9, ctx=[1 << 20] * 4 + [5000, 300000, 40000, 2048, 131072])
+    try:
+        hyb.hyb_set_error_word(word)
+        for _ in range(3):
+            out = torch.empty_like(c4.q)
+            hyb.hyb_decode_step(c4.q, c4.seq_lens, c4.max_seq_len, c4.swa, c4.comp, out, idx_q=c4.idx_q,
+                                idx_w=c4.idx_w, idx_pool=c4.idx_pool, k=c4.k)
+            out = torch.empty_like(c128.q)
+            hyb.hyb_decode_step(c128.q, c128.seq_lens, c128.max_seq_len, c128.swa, c128.comp, out)
+        torch.cuda.synchronize()
+        assert int(word.item()) == 0
+    finally:
+        hyb.hyb_set_error_word(None)
