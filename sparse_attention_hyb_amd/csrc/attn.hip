@@ -327,6 +327,14 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0,
   const QueryKeys qk = query_keys(a, i);
   const int j_begin = sp * a.chunk, j_end = min(qk.n_keys, j_begin + a.chunk);
   const int tid = threadIdx.x;
+  if constexpr (!kDirect) {
+    // the query's RoPE(-p) table for the combine, formed by its first split's last wave while the
+    // first loads are in flight (the combine then starts without this dependent chain)
+    if (sp == 0 && a.rope_tab != nullptr && tid >= 448 && tid - 448 < (a.rope_dim >> 1)) {
+      float* t = a.rope_tab + ((int64_t)i * kMaxRopePairs + (tid - 448)) * 2;
+      rope_cs(-(double)qk.p, tid - 448, a.rope_dim, a.rope_base, t, t + 1);
+    }
+  }
   if constexpr (kSel) {
     // Every workgroup of the query selects (the first one also writes the top-k row out); one with
     // no keys of its own (j_begin >= n_keys, uniform) does not. Then each counts itself as done
@@ -824,8 +832,6 @@ __device__ __forceinline__ void combine_group(const AttnArgs& a, int hpw, int lo
 #pragma unroll
     for (int q = 0; q < 8; ++q) pre[q] = load8<PT>(base + min(q, ns - 1) * sstride);
   }
-  int seq, p;
-  query_at(a.qd, i, &seq, &p);
   const float* pml = a.part_ml + (int64_t)i * ns * 2 * H;
   for (int e = tid; e < ns * 2 * nh; e += 256) {
     const int s2 = e / nh, hl = e % nh;   // s2 = 2 * split + (0: m, 1: l)
@@ -833,8 +839,18 @@ __device__ __forceinline__ void combine_group(const AttnArgs& a, int hpw, int lo
   }
   if (tid < kCombineHeads) lamax[tid] = 0u;
   const int rope_lo = D - a.rope_dim;
-  for (int t = tid; t < a.rope_dim / 2; t += 256)
-    rope_cs(-(double)p, t, a.rope_dim, a.rope_base, &rc[t], &rs[t]);
+  if (a.rope_tab != nullptr) {   // formed by the attention kernel with rope_cs
+    const float* tab = a.rope_tab + (int64_t)i * kMaxRopePairs * 2;
+    for (int t = tid; t < a.rope_dim / 2; t += 256) {
+      rc[t] = tab[2 * t];
+      rs[t] = tab[2 * t + 1];
+    }
+  } else {
+    int seq, p;
+    query_at(a.qd, i, &seq, &p);
+    for (int t = tid; t < a.rope_dim / 2; t += 256)
+      rope_cs(-(double)p, t, a.rope_dim, a.rope_base, &rc[t], &rs[t]);
+  }
   __syncthreads();
   for (int hl = tid; hl < nh; hl += 256) {
     float M = -INFINITY;
@@ -1043,6 +1059,10 @@ AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_k
   const size_t elem = pl.use_mfma ? sizeof(uint16_t) : sizeof(float);
   pl.o_bytes = ((size_t)n_q * ns * dim * n_heads * elem + 255) / 256 * 256;
   pl.ws_bytes = pl.o_bytes + (size_t)n_q * ns * 2 * n_heads * sizeof(float);
+  if (pl.use_mfma) {
+    pl.rope_off = (pl.ws_bytes + 255) / 256 * 256;
+    pl.ws_bytes = pl.rope_off + (size_t)n_q * kMaxRopePairs * 2 * sizeof(float);
+  }
   return pl;
 }
 

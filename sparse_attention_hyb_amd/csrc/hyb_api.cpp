@@ -246,6 +246,8 @@ int attach_workspace(const char* op, AttnCommon* c, void* ws, size_t ws_bytes) {
                 ws ? ws_bytes : (size_t)0);
   c->args.part_o = ws;
   c->args.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + c->plan.o_bytes);
+  c->args.rope_tab = c->plan.use_mfma ? reinterpret_cast<float*>(static_cast<char*>(ws) + c->plan.rope_off)
+                                      : nullptr;
   return HYB_OK;
 }
 

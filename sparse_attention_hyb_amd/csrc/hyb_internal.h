@@ -184,6 +184,9 @@ struct AttnArgs {
   // bf16 already); m (natural-log units) and l per split and head in part_ml [n_q][n_split][2][n_heads].
   void* part_o;
   float* part_ml;
+  // MFMA path: the RoPE(-p) table of every query, [n_q][64 pairs][cos, sin], written by the query's
+  // first split for the combine (which otherwise forms it itself).
+  float* rope_tab;
   // Decode step with the selection fused (sel.pairs set): each workgroup of query i selects the
   // top k of row i from the hand-off itself instead of reading topk.
   SelDev sel;
@@ -195,6 +198,7 @@ struct AttnPlan {
   int32_t n_split;
   int32_t chunk;
   size_t o_bytes;    // part_o bytes, rounded up to 256; part_ml follows
+  size_t rope_off;   // MFMA path: offset of rope_tab (after part_ml), else 0
   size_t ws_bytes;
 };
 AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_keys,
