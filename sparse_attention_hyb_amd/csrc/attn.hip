@@ -37,6 +37,9 @@ constexpr int kMD = 512;        // dims in the MFMA kernel
 constexpr int kKT = 32;         // keys per tile in the MFMA kernel
 constexpr int kGenTile = 64;    // keys per tile in the generic kernel
 constexpr int kMaxSplit = 64;
+constexpr int kBalancedSlots = 256;         // balanced plan: slots beyond one per query
+constexpr int kBalancedMaxQueries = 2048;   // balanced plan: queries per launch at most
+constexpr int kBalancedMinTiles = 4;        // balanced plan: 32-key tiles per piece at least
 constexpr int kMaxRopePairs = 64;   // rope_dim <= 128
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -63,6 +66,18 @@ __device__ __forceinline__ KeyRef resolve_key(const AttnArgs& a, int i, int seq,
 struct QueryKeys {
   int seq, p, ws, n_win, nv, n_keys;
 };
+
+// The keys of a query at sequence seq, position p.
+__device__ __forceinline__ QueryKeys query_keys_at(const AttnArgs& a, int seq, int p) {
+  QueryKeys k;
+  k.seq = seq;
+  k.p = p;
+  k.ws = window_start(k.p, a.window);
+  k.n_win = k.p - k.ws + 1;
+  k.nv = n_visible(k.p, a.comp.ratio, a.window);
+  k.n_keys = k.n_win + ((a.topk || a.sel.pairs) ? a.k : k.nv);
+  return k;
+}
 
 __device__ __forceinline__ QueryKeys query_keys(const AttnArgs& a, int i) {
   QueryKeys k;
@@ -258,6 +273,92 @@ __device__ __forceinline__ int xcd_logical(int L, int total) {
   return x < rem ? x * (per + 1) + s : rem * (per + 1) + (x - rem) * per + s;
 }
 
+// Balanced decode plan, formed alike by every workgroup of the launch (all 512 threads call it).
+// Query q has tiles_q = ceil(n_keys_q / 32) key tiles; with T = sum_q tiles_q and M = max_q tiles_q,
+// pieces hold share = max(kBalancedMinTiles, ceil(T / (n_slots - n_q)), ceil(M / n_split)) tiles,
+// so query q takes ns_q = ceil(tiles_q / share) <= n_split pieces and sum_q ns_q <= T / share + n_q
+// <= n_slots: one slot per piece. Slots go out in query order (query q: slots first_q .. first_q +
+// ns_q - 1). Workgroup `bid` takes slot w = xcd_logical(bid, total) when bid < total (so the used
+// slots spread evenly over the XCDs and a query's pieces share one XCD), and returns false
+// otherwise. Its query i, piece and key range [j_begin, j_end) (j_end not yet clamped to the
+// query's keys). The first piece's workgroup records (first_q, ns_q) in qplan for the combine.
+// qk: query i's keys (its position kept in LDS from the plan: no second read of its length).
+// lds: 3 n_q + 21 words.
+__device__ __forceinline__ bool balanced_piece(const AttnArgs& a, int bid, uint32_t* lds, int& i,
+                                               int& piece, int& j_begin, int& j_end, int& w,
+                                               QueryKeys& qk) {
+  const int tid = threadIdx.x, lane = tid & 63, nq = a.n_q;
+  uint32_t* first_s = lds;                            // [nq + 1]
+  int* seq_s = reinterpret_cast<int*>(lds + nq + 1);  // [nq]
+  int* pos_s = seq_s + nq;                            // [nq]
+  uint32_t* wt = lds + 3 * nq + 1;                    // [16] wave totals of the scan
+  uint32_t* red = wt + 16;                            // [2] T, M
+  uint32_t t4[4], sum = 0, mx = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {   // queries 4 tid .. 4 tid + 3 (n_q <= 2048)
+    const int q = 4 * tid + e;
+    uint32_t t = 0u;
+    if (q < nq) {
+      int seq, p;
+      query_at(a.qd, q, &seq, &p);
+      seq_s[q] = seq;
+      pos_s[q] = p;
+      t = (uint32_t)((query_keys_at(a, seq, p).n_keys + kKT - 1) / kKT);
+    }
+    t4[e] = t;
+    sum += t;
+    mx = max(mx, t);
+  }
+  if (tid == 0) red[0] = red[1] = 0u;
+  __syncthreads();
+  const uint32_t wsum = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(sum), 63);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  if (lane == 0) {
+    atomicAdd(&red[0], wsum);
+    atomicMax(&red[1], mx);
+  }
+  __syncthreads();
+  const uint32_t T = red[0], M = red[1];
+  const uint32_t free_slots = (uint32_t)(a.n_slots - nq);
+  const uint32_t share = max(max((uint32_t)kBalancedMinTiles, (T + free_slots - 1) / free_slots),
+                             (M + (uint32_t)a.n_split - 1) / (uint32_t)a.n_split);
+  uint32_t ns4[4], loc = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ns4[e] = (t4[e] + share - 1) / share;
+    loc += ns4[e];
+  }
+  uint32_t total = 0;
+  uint32_t run = block_scan_excl<512>(loc, wt, &total);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int q = 4 * tid + e;
+    if (q < nq) first_s[q] = run;
+    run += ns4[e];
+  }
+  if (tid == 0) first_s[nq] = total;
+  __syncthreads();
+  if (bid >= (int)total) return false;   // uniform
+  w = xcd_logical(bid, (int)total);
+  int lo = 0, hi = nq - 1;             // last query whose first slot is <= w (every ns_q >= 1)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int)first_s[mid] <= w) lo = mid; else hi = mid - 1;
+  }
+  i = lo;
+  qk = query_keys_at(a, seq_s[lo], pos_s[lo]);
+  piece = w - (int)first_s[lo];
+  j_begin = piece * (int)share * kKT;
+  j_end = j_begin + (int)share * kKT;
+  if (piece == 0 && tid == 0) {
+    a.qplan[2 * i] = (int32_t)first_s[lo];
+    a.qplan[2 * i + 1] = (int32_t)(first_s[lo + 1] - first_s[lo]);
+  }
+  return true;
+}
+
+
 // One thread's share of one 32-key tile between its global load and its LDS store: key t/16,
 // chunks t%16 + 16c (c < 4) of the row (bf16: 16 B each; fp8: 8 codes each).
 template <bool kFp8>
@@ -312,7 +413,8 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0,
   static_assert(sizeof(ktile) >= kCompressFusedLds, "a compressor workgroup fits the tile buffers");
   static_assert(!kSel || sizeof(ktile) >= kSelLdsWords * sizeof(uint32_t), "the selection fits the tile buffers");
 
-  const int n_attn = a.n_split * a.n_q;
+  const bool balanced = !kSel && a.qplan != nullptr;   // uniform
+  const int n_attn = balanced ? a.n_slots : a.n_split * a.n_q;
   const int bid = blockIdx.x + blockIdx.y * gridDim.x;
   if (bid >= n_attn) {   // compressor workgroups riding along (first four waves; all take barriers)
     const int k = bid - n_attn;
@@ -320,12 +422,25 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0,
     else compress_fused<4>(c1, k - n_c0, reinterpret_cast<float*>(ktile));
     return;
   }
-  const int logical = xcd_logical(bid, n_attn);
-  const int sp = logical % a.n_split, i = logical / a.n_split;
+  // the query, its piece (split) and the piece's key range; slot: where the partial goes
+  int i, sp, j_begin, j_end, slot;
+  QueryKeys qk;
+  if (balanced) {
+    if (!balanced_piece(a, bid, reinterpret_cast<uint32_t*>(ktile), i, sp, j_begin, j_end, slot, qk))
+      return;
+    __syncthreads();   // the plan's LDS words are read before the tiles reuse them
+  } else {
+    const int logical = xcd_logical(bid, n_attn);
+    sp = logical % a.n_split;
+    i = logical / a.n_split;
+    j_begin = sp * a.chunk;
+    j_end = j_begin + a.chunk;
+    slot = i * a.n_split + sp;
+  }
   SelRegs sreg;
   if constexpr (kSel) select_issue(a.sel, i, sreg);   // the hand-off loads go out first
-  const QueryKeys qk = query_keys(a, i);
-  const int j_begin = sp * a.chunk, j_end = min(qk.n_keys, j_begin + a.chunk);
+  if (!balanced) qk = query_keys(a, i);
+  j_end = min(qk.n_keys, j_end);
   const int tid = threadIdx.x;
   if constexpr (!kDirect) {
     // the query's RoPE(-p) table for the combine, formed by its first split's last wave while the
@@ -679,7 +794,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0,
     if (sg == 0) {
       const int h = 16 * wave + sh;
       if constexpr (!direct) {
-        float* pml = a.part_ml + ((int64_t)i * a.n_split + sp) * 2 * kMH;
+        float* pml = a.part_ml + (int64_t)slot * 2 * kMH;
         // m is kept in log2 units inside the kernel; store natural-log units for the combine
         pml[h] = m_run == -INFINITY ? -INFINITY : m_run / kLog2e;
         pml[kMH + h] = l_run;
@@ -721,7 +836,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0,
   // wave w stores rows 8w..8w+7, one row (64 lanes x 16 B) per instruction
   {
     uint16_t* po = direct ? reinterpret_cast<uint16_t*>(a.out) + (int64_t)i * kMH * kMD
-                          : reinterpret_cast<uint16_t*>(a.part_o) + ((int64_t)i * a.n_split + sp) * kMH * kMD;
+                          : reinterpret_cast<uint16_t*>(a.part_o) + (int64_t)slot * kMH * kMD;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int row = 8 * wave + c;
@@ -814,7 +929,14 @@ __device__ __forceinline__ void combine_group(const AttnArgs& a, int hpw, int lo
                                               float* sm) {
   const int i = logical / gx;
   const int h0 = (logical % gx) * hpw;
-  const int H = a.n_heads, D = a.dim, ns = a.n_split;
+  const int H = a.n_heads, D = a.dim;
+  // the query's partials: n_split of them from slot i * n_split, or as the balanced plan recorded
+  int ns = a.n_split;
+  int64_t first = (int64_t)i * ns;
+  if (a.qplan != nullptr) {
+    first = a.qplan[2 * i];
+    ns = a.qplan[2 * i + 1];
+  }
   const int nh = min(hpw, H - h0);
   float* wsp = sm;                              // [split][head of the group]
   float* mls = sm + ns * kCombineHeads;         // [split][m, l][head of the group]
@@ -822,7 +944,7 @@ __device__ __forceinline__ void combine_group(const AttnArgs& a, int hpw, int lo
   __shared__ uint32_t lamax[kCombineHeads];   // FP8 output: bits of each head's largest |value|
   const int tid = threadIdx.x;
   const int64_t sstride = (int64_t)H * D;
-  const PT* po = reinterpret_cast<const PT*>(a.part_o) + (int64_t)i * ns * sstride;
+  const PT* po = reinterpret_cast<const PT*>(a.part_o) + first * sstride;
   // the first eight splits' partials are requested before the weights are formed
   const bool oct = (D & 7) == 0;
   const int n8 = oct ? nh * (D / 8) : 0;
@@ -832,7 +954,7 @@ __device__ __forceinline__ void combine_group(const AttnArgs& a, int hpw, int lo
 #pragma unroll
     for (int q = 0; q < 8; ++q) pre[q] = load8<PT>(base + min(q, ns - 1) * sstride);
   }
-  const float* pml = a.part_ml + (int64_t)i * ns * 2 * H;
+  const float* pml = a.part_ml + first * 2 * H;
   for (int e = tid; e < ns * 2 * nh; e += 256) {
     const int s2 = e / nh, hl = e % nh;   // s2 = 2 * split + (0: m, 1: l)
     mls[e] = pml[s2 * H + h0 + hl];
@@ -1029,7 +1151,7 @@ __global__ __launch_bounds__(256, 4) void attn_combine_compress(AttnArgs a, int 
 constexpr int kMfmaMinChunk = 128;
 
 AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_keys,
-                        int32_t q_dtype, int32_t pool_dtype) {
+                        int32_t q_dtype, int32_t pool_dtype, bool balanced) {
   AttnPlan pl{};
   pl.use_mfma = n_heads == kMH && dim == kMD && q_dtype == BF16 &&
                 (pool_dtype == BF16 || pool_dtype == FP8);
@@ -1056,12 +1178,26 @@ AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_k
   if (ns < 1) ns = 1;
   pl.n_split = ns;
   pl.chunk = chunk;
+  // Decode launches with several splits take the balanced plan: n_q + kBalancedSlots slots, pieces
+  // cut on the device from the actual lengths (a batch of mixed lengths then spreads its long
+  // queries over many workgroups instead of sizing every query's splits by the longest).
+  pl.balanced = balanced && pl.use_mfma && ns > 1 && n_q <= kBalancedMaxQueries;
+  size_t slots = (size_t)n_q * ns;
+  if (pl.balanced) {
+    pl.n_split = kMaxSplit;   // pieces per query at most (the combine's LDS bound)
+    pl.n_slots = n_q + kBalancedSlots;
+    slots = (size_t)pl.n_slots;
+  }
   const size_t elem = pl.use_mfma ? sizeof(uint16_t) : sizeof(float);
-  pl.o_bytes = ((size_t)n_q * ns * dim * n_heads * elem + 255) / 256 * 256;
-  pl.ws_bytes = pl.o_bytes + (size_t)n_q * ns * 2 * n_heads * sizeof(float);
+  pl.o_bytes = (slots * dim * n_heads * elem + 255) / 256 * 256;
+  pl.ws_bytes = pl.o_bytes + slots * 2 * n_heads * sizeof(float);
   if (pl.use_mfma) {
     pl.rope_off = (pl.ws_bytes + 255) / 256 * 256;
     pl.ws_bytes = pl.rope_off + (size_t)n_q * kMaxRopePairs * 2 * sizeof(float);
+  }
+  if (pl.balanced) {
+    pl.qplan_off = (pl.ws_bytes + 255) / 256 * 256;
+    pl.ws_bytes = pl.qplan_off + (size_t)n_q * 2 * sizeof(int32_t);
   }
   return pl;
 }
@@ -1069,6 +1205,7 @@ AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_k
 namespace {
 hipError_t launch_attention_kernel(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.n_q);
+  if (a.qplan != nullptr) grid = dim3(a.n_slots);
   if (a.use_mfma) {
     const bool direct = a.n_split == 1 && a.out_dtype == BF16;   // writes_output(a)
     const CompressArgs none{};

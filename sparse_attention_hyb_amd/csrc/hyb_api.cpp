@@ -179,7 +179,7 @@ int check_attention(const char* op, const void* q, int32_t q_dtype, int32_t n_q,
                     const hyb_paged* swa, const hyb_paged* comp, const int32_t* topk_idx,
                     int32_t k, int32_t window, float softmax_scale, int32_t rope_dim,
                     double rope_base, void* out, int32_t out_dtype, float* out_scale,
-                    int64_t max_pos, AttnCommon* c) {
+                    int64_t max_pos, bool balanced, AttnCommon* c) {
   if (!q || !out) return fail(HYB_EINVAL, "%s: q and out must be non-NULL", op);
   if (n_q < 0) return fail(HYB_EINVAL, "%s: query count %d < 0", op, n_q);
   if (n_heads <= 0 || n_heads > 128) return fail(HYB_EINVAL, "%s: n_heads %d outside [1, 128]", op, n_heads);
@@ -211,7 +211,7 @@ int check_attention(const char* op, const void* q, int32_t q_dtype, int32_t n_q,
   const int64_t n_comp = topk_idx ? k : visible(max_pos, pc.ratio, window);
   const int64_t max_keys = n_win + n_comp;
   if (max_keys > (1LL << 30)) return fail(HYB_EINVAL, "%s: too many keys per query", op);
-  c->plan = hyb::plan_attention(n_q, n_heads, dim, (int32_t)max_keys, q_dtype, ps.dtype);
+  c->plan = hyb::plan_attention(n_q, n_heads, dim, (int32_t)max_keys, q_dtype, ps.dtype, balanced);
   if (!c->plan.use_mfma && ((int64_t)n_heads * dim > 4096 || n_heads > 64))
     return fail(HYB_ENOTSUP, "%s: heads x dim = %d x %d needs the 64 x 512 bf16 kernel (bf16 query, bf16/fp8 pools)",
                 op, n_heads, dim);
@@ -248,20 +248,23 @@ int attach_workspace(const char* op, AttnCommon* c, void* ws, size_t ws_bytes) {
   c->args.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + c->plan.o_bytes);
   c->args.rope_tab = c->plan.use_mfma ? reinterpret_cast<float*>(static_cast<char*>(ws) + c->plan.rope_off)
                                       : nullptr;
+  if (c->plan.balanced) {
+    c->args.qplan = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + c->plan.qplan_off);
+    c->args.n_slots = c->plan.n_slots;
+  }
   return HYB_OK;
 }
 
 size_t attn_ws(int32_t n_q, int32_t n_heads, int32_t dim, int64_t max_pos, int32_t ratio,
-               int32_t k, int32_t window, int32_t dtype_hint) {
+               int32_t k, int32_t window, bool balanced) {
   if (n_q <= 0 || n_heads <= 0 || dim <= 0 || window <= 0 || max_pos < 0 ||
       (ratio != 4 && ratio != 128))
     return 0;
   const int64_t n_win = max_pos + 1 < window ? max_pos + 1 : window;
   const int64_t n_comp = k > 0 ? k : visible(max_pos, ratio, window);
   // the plan depends on whether the MFMA kernel runs; size for the larger of the two plans
-  hyb::AttnPlan a = hyb::plan_attention(n_q, n_heads, dim, (int32_t)(n_win + n_comp), HYB_BF16, HYB_BF16);
-  hyb::AttnPlan b = hyb::plan_attention(n_q, n_heads, dim, (int32_t)(n_win + n_comp), HYB_F32, HYB_F32);
-  (void)dtype_hint;
+  hyb::AttnPlan a = hyb::plan_attention(n_q, n_heads, dim, (int32_t)(n_win + n_comp), HYB_BF16, HYB_BF16, balanced);
+  hyb::AttnPlan b = hyb::plan_attention(n_q, n_heads, dim, (int32_t)(n_win + n_comp), HYB_F32, HYB_F32, balanced);
   return a.ws_bytes > b.ws_bytes ? a.ws_bytes : b.ws_bytes;
 }
 
@@ -590,7 +593,8 @@ static size_t step_ws_bytes(int32_t batch, int32_t n_heads, int32_t dim, int32_t
     n += align256((size_t)batch * k * sizeof(int32_t));
     n += align256(topk_ws_bytes(batch, (int64_t)score_ld((int32_t)max_pos, window, comp_ratio)));
   }
-  return n + attn_ws(batch, n_heads, dim, max_pos, comp_ratio, comp_ratio == 4 ? k : 0, window, 0);
+  // a C128 step's attention takes the balanced plan; a C4 step's (equal key counts) does not
+  return n + attn_ws(batch, n_heads, dim, max_pos, comp_ratio, comp_ratio == 4 ? k : 0, window, comp_ratio == 128);
 }
 
 size_t hyb_decode_step_workspace_bytes(int32_t batch, int32_t n_heads, int32_t dim,
@@ -628,7 +632,7 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
   static const int32_t kSelected = 0;   // stands for the step's own top-k rows while checking
   HYB_TRY(check_attention(op, q, q_dtype, batch, n_heads, swa, comp, sparse ? &kSelected : nullptr, k,
                           window, softmax_scale, rope_dim, rope_base, out, out_dtype, out_scale,
-                          max_pos, &c));
+                          max_pos, !sparse, &c));
   hyb::CompressArgs ca[2];
   for (int j = 0; j < n_compress; ++j) HYB_TRY(check_compress(op, compress[j], &ca[j]));
   const size_t need = step_ws_bytes(batch, n_heads, c.args.dim, max_seq_len, comp->ratio, k, window);
@@ -784,7 +788,8 @@ int32_t hyb_index_topk_noalloc(const void* q_idx, int32_t q_dtype, const float* 
 size_t hyb_attn_decode_workspace_bytes(int32_t batch, int32_t n_heads, int32_t dim,
                                        int32_t max_seq_len, int32_t comp_ratio, int32_t k,
                                        int32_t window) {
-  return attn_ws(batch, n_heads, dim, (int64_t)max_seq_len - 1, comp_ratio, k, window, 0);
+  // dense layers (k = 0) take the balanced plan; sparse ones hold at most window + k keys a query
+  return attn_ws(batch, n_heads, dim, (int64_t)max_seq_len - 1, comp_ratio, k, window, k == 0);
 }
 
 int32_t hyb_attn_decode(const void* q, int32_t q_dtype, const int32_t* seq_lens, int32_t batch,
@@ -799,7 +804,7 @@ int32_t hyb_attn_decode(const void* q, int32_t q_dtype, const int32_t* seq_lens,
   AttnCommon c;
   HYB_TRY(check_attention(op, q, q_dtype, batch, n_heads, swa, comp, topk_idx, k, window,
                           softmax_scale, rope_dim, rope_base, out, out_dtype, out_scale,
-                          (int64_t)max_seq_len - 1, &c));
+                          (int64_t)max_seq_len - 1, topk_idx == nullptr, &c));
   HYB_TRY(attach_workspace(op, &c, workspace, workspace_bytes));
   if (batch == 0) return HYB_OK;
   c.args.qd = hyb::QueryDev{seq_lens, nullptr, nullptr};
@@ -821,7 +826,7 @@ int32_t hyb_attn_decode_compress(const void* q, int32_t q_dtype, const int32_t* 
   AttnCommon c;
   HYB_TRY(check_attention(op, q, q_dtype, batch, n_heads, swa, comp, topk_idx, k, window,
                           softmax_scale, rope_dim, rope_base, out, out_dtype, out_scale,
-                          (int64_t)max_seq_len - 1, &c));
+                          (int64_t)max_seq_len - 1, topk_idx == nullptr, &c));
   HYB_TRY(attach_workspace(op, &c, workspace, workspace_bytes));
   hyb::CompressArgs ca;
   HYB_TRY(check_compress(op, *compress, &ca));
@@ -832,7 +837,7 @@ int32_t hyb_attn_decode_compress(const void* q, int32_t q_dtype, const int32_t* 
 size_t hyb_attn_prefill_workspace_bytes(int32_t n_q, int32_t n_heads, int32_t dim,
                                         int32_t max_pos, int32_t comp_ratio, int32_t k,
                                         int32_t window) {
-  return attn_ws(n_q, n_heads, dim, max_pos, comp_ratio, k, window, 0);
+  return attn_ws(n_q, n_heads, dim, max_pos, comp_ratio, k, window, false);
 }
 
 int32_t hyb_attn_prefill(const void* q, int32_t q_dtype, const int32_t* q_seq,
@@ -847,7 +852,7 @@ int32_t hyb_attn_prefill(const void* q, int32_t q_dtype, const int32_t* q_seq,
   AttnCommon c;
   HYB_TRY(check_attention(op, q, q_dtype, n_q, n_heads, swa, comp, topk_idx, k, window,
                           softmax_scale, rope_dim, rope_base, out, out_dtype, out_scale, max_pos,
-                          &c));
+                          false, &c));
   HYB_TRY(attach_workspace(op, &c, workspace, workspace_bytes));
   if (n_q == 0) return HYB_OK;
   c.args.qd = hyb::QueryDev{nullptr, q_seq, q_pos};

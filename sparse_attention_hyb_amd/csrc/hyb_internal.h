@@ -187,6 +187,13 @@ struct AttnArgs {
   // MFMA path: the RoPE(-p) table of every query, [n_q][64 pairs][cos, sin], written by the query's
   // first split for the combine (which otherwise forms it itself).
   float* rope_tab;
+  // Balanced decode plan (MFMA path, set with qplan): the launch has n_slots workgroup slots and
+  // every workgroup derives from the queries' lengths how their keys are cut into pieces of equal
+  // size (at most n_split per query) and which piece is its own; the piece's partial goes to its
+  // slot, and the query's first slot and piece count to qplan [n_q][2] for the combine. NULL: n_split
+  // pieces of `chunk` keys per query, slot = query * n_split + piece.
+  int32_t* qplan;
+  int32_t n_slots;
   // Decode step with the selection fused (sel.pairs set): each workgroup of query i selects the
   // top k of row i from the hand-off itself instead of reading topk.
   SelDev sel;
@@ -199,10 +206,15 @@ struct AttnPlan {
   int32_t chunk;
   size_t o_bytes;    // part_o bytes, rounded up to 256; part_ml follows
   size_t rope_off;   // MFMA path: offset of rope_tab (after part_ml), else 0
+  int32_t balanced;  // the balanced decode plan (n_slots slots, qplan at qplan_off)
+  int32_t n_slots;
+  size_t qplan_off;
   size_t ws_bytes;
 };
+// balanced: a decode launch, whose queries may differ in length (the plan then balances the key
+// work over the workgroups on the device when the MFMA kernel runs with more than one split).
 AttnPlan plan_attention(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_keys,
-                        int32_t q_dtype, int32_t pool_dtype);
+                        int32_t q_dtype, int32_t pool_dtype, bool balanced);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // Attention with the selection fused (a.sel set, the MFMA kernel) and up to two compressor calls
 // riding along with its launch, then the combine.

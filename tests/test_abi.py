@@ -335,7 +335,8 @@ def test_decode_step_validation(lib):
     assert call(n_comp=1) == hyb.HYB_EINVAL                   # compress NULL
     assert call(k=0) == hyb.HYB_EINVAL
     need = lib.hyb_decode_step_workspace_bytes(4, 64, 512, 100000, 4, 512, 128)
-    assert need > lib.hyb_attn_decode_workspace_bytes(4, 64, 512, 100000, 4, 512, 128)
+    # the step holds the indexer's hand-off (with its zero block) and the attention's partials
+    assert need > lib.hyb_index_topk_workspace_bytes(4, 100000 - 1, 128, 4) + 4 * 5 * 64 * 512 * 2
     assert call(ws=need - 1) == hyb.HYB_EWORKSPACE
     assert lib.hyb_last_error().decode().startswith("hyb_decode_step")
     assert lib.hyb_decode_step_workspace_bytes(4, 64, 512, 100000, 128, 0, 128) == \

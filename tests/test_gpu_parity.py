@@ -318,6 +318,19 @@ def test_c128_dense_decode_two_resolution_segments(gpu_lib):
     assert_abs_close(to_f64(out), want)
 
 
+def test_c128_dense_decode_skewed_lengths(gpu_lib):
+    """One 2^20-token sequence among seventeen short ones (1 .. 5000 tokens): the balanced decode
+    plan cuts the long query into many pieces and gives each short one a single piece. The long
+    query, the shortest ones and one more are recomputed by the oracle."""
+    lens = [1 << 20] + [4096] * 13 + [1, 200, 129, 5000]
+    wl = W.dense_decode(DEV, seed=12, batch=len(lens), ctx=lens)
+    out = gpu_decode(gpu_lib, wl)
+    sync()
+    seqs = [0, 5, 14, 15, 16, 17]
+    want = oracle_out(wl, to_oracle_pool(wl.swa), to_oracle_pool(wl.comp), seqs)
+    assert_abs_close(to_f64(out)[seqs], want)
+
+
 def test_c4_with_k_at_least_visible_equals_dense(gpu_lib):
     """With k >= n_vis the sparse path selects every visible entry, so it must equal the dense
     path over the same C4 pool (up to the order of fp32 partial sums)."""
