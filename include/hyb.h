@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define HYB_ABI_VERSION 3
+#define HYB_ABI_VERSION 4
 
 /* [vLLM] "vLLM side": one logical block = 256 native (raw) positions for every compression
  * rate, i.e. 256 raw entries, 64 C4 entries or 2 C128 entries. */
@@ -216,6 +216,58 @@ int32_t hyb_q_norm_kv_insert(const void* q, int32_t q_dtype, int32_t n_heads, co
 int32_t hyb_gather_pages(const void* src_host, int32_t n_src_pages, void* dst, int32_t n_dst_pages,
                          const int32_t* src_page, const int32_t* dst_page, int32_t n,
                          int64_t page_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------------
+ * hyb_offload_admit - one step's working-set update of an offloaded C4 pool, on the device.
+ * [SGLang] "HiSparse": the C4 pool lives in a pinned host mirror; the device keeps a working set of
+ * pages, brings in every page the step's selection misses and evicts the least recently used pages
+ * the step does not need. Here no top-k row is read back: in stream order,
+ *   1. every page (logical block of `entries_per_page` entries; key = sequence * max_blocks +
+ *      block) that a row of topk selects, and every key in extra, is needed this step; a needed
+ *      resident page's slot gets stamp `step`;
+ *   2. the needed pages that are not resident, in ascending key order, take as many slots among
+ *      those the step does not need, the least recently used first (smallest stamp, then lowest
+ *      slot; a never-used slot has stamp 0), the i-th page the i-th of those slots in slot order;
+ *      dev_table, slot_owner and slot_stamp are updated (an evicted page's entry becomes -1);
+ *   3. each admitted page is copied from mirror page mirror_table[key] into its slot (and its
+ *      scale page, when scale_page_bytes > 0).
+ *   topk     int32 [batch][k] entry indices (device; < 0 ignored); k = 0 allowed
+ *   extra    int32 [n_extra] page keys (device; e.g. the pages receiving new entries), or NULL
+ *   dev_table    int32 [batch][max_blocks] (device): block -> slot, -1 absent (the working set's
+ *                block table, as the attention entry points read it)
+ *   mirror_table int32 [batch][max_blocks] (device): block -> mirror page
+ *   slot_owner   int32 [n_slots] (device): page key or -1; slot_stamp uint32 [n_slots] (device)
+ *   step     >= 1 and greater than every earlier call's step on this workspace
+ *   mirror_host  pinned host pages [n_mirror_pages][page_bytes] (read through the device alias);
+ *   pool     device pages [n_slots][page_bytes]; mirror_scale_host / pool_scale: the same for the
+ *            per-entry scales (scale_page_bytes > 0), else NULL and 0
+ *   workspace    hyb_offload_workspace_bytes(batch, max_blocks, n_slots) bytes, zero before its
+ *            first use; calls that share it must not overlap
+ *   result   int32 [2] (device): pages admitted, pages left out because the slots the step could
+ *            free were too few (then their blocks stay absent: size the working set for a step)
+ * 1 <= n_slots <= 16384; page_bytes and scale_page_bytes multiples of 16 and of entries_per_page;
+ * pool and mirror 16-byte aligned. Out-of-range keys and table entries are skipped.
+ *
+ * hyb_offload_write_back - back up new entries to the mirror, on the device: for each sequence b
+ * whose position p = seq_lens[b] - 1 completes a compressed entry ((p + 1) % ratio == 0), entry
+ * (p + 1) / ratio - 1 (and its scale) goes from its resident slot to its mirror page through the
+ * mirror's device alias (skipped when its page is not resident). Enqueued on any stream after the
+ * compressor that wrote the entry, it runs asynchronously to the host and to the next step.
+ * ------------------------------------------------------------------------------------------ */
+size_t hyb_offload_workspace_bytes(int32_t batch, int32_t max_blocks, int32_t n_slots);
+int32_t hyb_offload_admit(const int32_t* topk, int32_t batch, int32_t k, const int32_t* extra,
+                          int32_t n_extra, int32_t* dev_table, const int32_t* mirror_table,
+                          int32_t max_blocks, int32_t entries_per_page, int32_t* slot_owner,
+                          uint32_t* slot_stamp, int32_t n_slots, uint32_t step, void* mirror_host,
+                          int32_t n_mirror_pages, void* pool, int64_t page_bytes,
+                          void* mirror_scale_host, void* pool_scale, int64_t scale_page_bytes,
+                          void* workspace, size_t workspace_bytes, int32_t* result, void* stream);
+int32_t hyb_offload_write_back(const int32_t* seq_lens, int32_t batch, int32_t ratio,
+                               const int32_t* dev_table, const int32_t* mirror_table,
+                               int32_t max_blocks, int32_t entries_per_page, int32_t n_slots,
+                               const void* pool, int64_t page_bytes, void* mirror_host,
+                               int32_t n_mirror_pages, const void* pool_scale,
+                               void* mirror_scale_host, int64_t scale_page_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------------
  * hyb_index_score - indexer scores over the visible compressed entries.

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyb.so")
 
 HYB_OK, HYB_EINVAL, HYB_ENOTSUP, HYB_EWORKSPACE, HYB_ELAUNCH = 0, 1, 2, 3, 4
 F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
-ABI_VERSION = 3   # HYB_ABI_VERSION of include/hyb.h that these signatures follow
+ABI_VERSION = 4   # HYB_ABI_VERSION of include/hyb.h that these signatures follow
 POOL_MEAN, POOL_SOFTMAX_GATE = 0, 1
 BLOCK_POSITIONS = 256
 KMAX = 2048
@@ -36,6 +36,7 @@ EXPORTS = (
     "hyb_attn_prefill_workspace_bytes", "hyb_attn_prefill",
     "hyb_decode_step_workspace_bytes", "hyb_decode_step",
     "hyb_probe_granule", "hyb_probe",
+    "hyb_offload_workspace_bytes", "hyb_offload_admit", "hyb_offload_write_back",
 )
 
 
@@ -116,6 +117,11 @@ _SIGS = {
                                ctypes.POINTER(hyb_compress_call), _I32, _P, _SZ, _P]),
     "hyb_probe_granule": (ctypes.c_uint64, [_I32, _I32]),
     "hyb_probe": (_I32, [_I32, _I32, _I32, _P, _P, ctypes.c_uint64, _P, _P, _I32, _I64, _P, _P]),
+    "hyb_offload_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "hyb_offload_admit": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P, _P, _I32, ctypes.c_uint32,
+                                 _P, _I32, _P, _I64, _P, _P, _I64, _P, _SZ, _P, _P]),
+    "hyb_offload_write_back": (_I32, [_P, _I32, _I32, _P, _P, _I32, _I32, _I32, _P, _I64, _P, _I32, _P, _P,
+                                      _I64, _P]),
 }
 
 
@@ -267,6 +273,50 @@ def hyb_gather_pages(src_host, dst, src_page, dst_page, stream=None) -> None:
     _check(load().hyb_gather_pages(_ptr(src_host), int(src_host.shape[0]), _ptr(dst),
                                    int(dst.shape[0]), _ptr(src_page), _ptr(dst_page),
                                    int(src_page.numel()), int(page), _stream(stream)))
+
+
+def hyb_offload_workspace_bytes(batch: int, max_blocks: int, n_slots: int) -> int:
+    return int(load().hyb_offload_workspace_bytes(int(batch), int(max_blocks), int(n_slots)))
+
+
+def hyb_offload_admit(topk, dev_table, mirror_table, slot_owner, slot_stamp, step: int, mirror_host,
+                      pool, workspace, result, extra=None, entries_per_page: int = 64,
+                      mirror_scale_host=None, pool_scale=None, stream=None) -> None:
+    """One step's working-set update of an offloaded C4 pool on the device (see include/hyb.h).
+    topk [batch, k] int32 (device); dev_table / mirror_table [batch, max_blocks] int32 (device);
+    slot_owner int32 / slot_stamp int32 (as uint32) [n_slots] (device); mirror_host: a contiguous
+    pinned CPU tensor [pages, ...]; pool: a contiguous device tensor [n_slots, ...] of the same page
+    shape; optional scale pages alike; workspace: uint8 device tensor, zero before its first use;
+    result: int32 [2] device tensor (pages admitted, pages left out)."""
+    if not (mirror_host.is_contiguous() and pool.is_contiguous()):
+        raise TypeError("mirror_host and pool must be contiguous")
+    page = mirror_host[0].numel() * mirror_host.element_size()
+    if pool[0].numel() * pool.element_size() != page:
+        raise TypeError("mirror_host and pool pages differ in size")
+    spage = 0
+    if mirror_scale_host is not None:
+        spage = mirror_scale_host[0].numel() * mirror_scale_host.element_size()
+    batch, k = (int(topk.shape[0]), int(topk.shape[1])) if topk is not None else (int(dev_table.shape[0]), 0)
+    _check(load().hyb_offload_admit(
+        _ptr(topk), batch, k, _ptr(extra), 0 if extra is None else int(extra.numel()),
+        _ptr(dev_table), _ptr(mirror_table), int(dev_table.shape[1]), int(entries_per_page),
+        _ptr(slot_owner), _ptr(slot_stamp), int(slot_owner.numel()), int(step), _ptr(mirror_host),
+        int(mirror_host.shape[0]), _ptr(pool), int(page), _ptr(mirror_scale_host), _ptr(pool_scale),
+        int(spage), _ptr(workspace), int(workspace.numel()), _ptr(result), _stream(stream)))
+
+
+def hyb_offload_write_back(seq_lens, ratio: int, dev_table, mirror_table, pool, mirror_host,
+                           entries_per_page: int = 64, pool_scale=None, mirror_scale_host=None,
+                           stream=None) -> None:
+    """Back up each sequence's newly completed entry from its resident slot to the pinned host
+    mirror, on the device (see include/hyb.h)."""
+    page = mirror_host[0].numel() * mirror_host.element_size()
+    spage = 0 if mirror_scale_host is None else mirror_scale_host[0].numel() * mirror_scale_host.element_size()
+    _check(load().hyb_offload_write_back(
+        _ptr(seq_lens), int(seq_lens.numel()), int(ratio), _ptr(dev_table), _ptr(mirror_table),
+        int(dev_table.shape[1]), int(entries_per_page), int(pool.shape[0]), _ptr(pool), int(page),
+        _ptr(mirror_host), int(mirror_host.shape[0]), _ptr(pool_scale), _ptr(mirror_scale_host),
+        int(spage), _stream(stream)))
 
 
 def hyb_index_score(q_idx, w, q_pos, max_pos: int, idx_pool, scores, window: int = 128,

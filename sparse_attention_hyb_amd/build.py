@@ -21,7 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhyb.so")
 
-SOURCES = ["hyb_api.cpp", "compress.hip", "index_score.hip", "topk.hip", "attn.hip", "hbm_probe.hip"]
+SOURCES = ["hyb_api.cpp", "compress.hip", "index_score.hip", "topk.hip", "attn.hip", "hbm_probe.hip",
+           "offload.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

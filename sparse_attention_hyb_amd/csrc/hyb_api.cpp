@@ -385,6 +385,130 @@ int32_t hyb_gather_pages(const void* src_host, int32_t n_src_pages, void* dst, i
                                                 static_cast<hipStream_t>(stream)), op);
 }
 
+static int host_alias(const char* op, const char* what, void* host, uint8_t** dev) {
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, host, 0) != hipSuccess || !d) {
+    (void)hipGetLastError();
+    return fail(HYB_EINVAL, "%s: %s is not pinned host memory with a device alias", op, what);
+  }
+  *dev = static_cast<uint8_t*>(d);
+  return HYB_OK;
+}
+
+static int check_offload_tables(const char* op, int32_t batch, int32_t max_blocks,
+                                int32_t entries_per_page, int32_t n_slots, int64_t page_bytes,
+                                int64_t scale_page_bytes, const void* pool, const void* mirror) {
+  if (batch < 0) return fail(HYB_EINVAL, "%s: batch %d < 0", op, batch);
+  if (max_blocks < 1 || entries_per_page < 1)
+    return fail(HYB_EINVAL, "%s: max_blocks %d and entries_per_page %d must be positive", op, max_blocks,
+                entries_per_page);
+  if ((int64_t)batch * max_blocks >= (1LL << 31))
+    return fail(HYB_EINVAL, "%s: batch x max_blocks must stay below 2^31", op);
+  if (n_slots < 1 || n_slots > hyb::kMaxOffloadSlots)
+    return fail(HYB_EINVAL, "%s: n_slots %d outside [1, %d]", op, n_slots, hyb::kMaxOffloadSlots);
+  if (page_bytes <= 0 || page_bytes % 16 || page_bytes % entries_per_page)
+    return fail(HYB_EINVAL, "%s: page_bytes %lld must be a positive multiple of 16 and of entries_per_page",
+                op, (long long)page_bytes);
+  if (scale_page_bytes < 0 || scale_page_bytes % 16 || scale_page_bytes % entries_per_page)
+    return fail(HYB_EINVAL, "%s: scale_page_bytes %lld must be 0 or a multiple of 16 and of entries_per_page",
+                op, (long long)scale_page_bytes);
+  if ((reinterpret_cast<uintptr_t>(pool) | reinterpret_cast<uintptr_t>(mirror)) & 15u)
+    return fail(HYB_EINVAL, "%s: pool and mirror must be 16-byte aligned", op);
+  return HYB_OK;
+}
+
+size_t hyb_offload_workspace_bytes(int32_t batch, int32_t max_blocks, int32_t n_slots) {
+  if (batch < 0 || max_blocks < 1 || n_slots < 1 || n_slots > hyb::kMaxOffloadSlots) return 0;
+  return hyb::offload_ws_bytes(batch, max_blocks, n_slots);
+}
+
+int32_t hyb_offload_admit(const int32_t* topk, int32_t batch, int32_t k, const int32_t* extra,
+                          int32_t n_extra, int32_t* dev_table, const int32_t* mirror_table,
+                          int32_t max_blocks, int32_t entries_per_page, int32_t* slot_owner,
+                          uint32_t* slot_stamp, int32_t n_slots, uint32_t step, void* mirror_host,
+                          int32_t n_mirror_pages, void* pool, int64_t page_bytes,
+                          void* mirror_scale_host, void* pool_scale, int64_t scale_page_bytes,
+                          void* workspace, size_t workspace_bytes, int32_t* result, void* stream) {
+  const char* op = "hyb_offload_admit";
+  if (!dev_table || !mirror_table || !slot_owner || !slot_stamp || !mirror_host || !pool || !result)
+    return fail(HYB_EINVAL, "%s: tables, slots, mirror, pool and result must be non-NULL", op);
+  if (k < 0 || (k > 0 && !topk)) return fail(HYB_EINVAL, "%s: k %d with topk %s", op, k, topk ? "set" : "NULL");
+  if (n_extra < 0 || (n_extra > 0 && !extra)) return fail(HYB_EINVAL, "%s: n_extra %d with extra NULL", op, n_extra);
+  if (step < 1) return fail(HYB_EINVAL, "%s: step must be >= 1", op);
+  if (n_mirror_pages < 1) return fail(HYB_EINVAL, "%s: n_mirror_pages %d < 1", op, n_mirror_pages);
+  HYB_TRY(check_offload_tables(op, batch, max_blocks, entries_per_page, n_slots, page_bytes,
+                               scale_page_bytes, pool, mirror_host));
+  if ((scale_page_bytes > 0) != (mirror_scale_host != nullptr && pool_scale != nullptr))
+    return fail(HYB_EINVAL, "%s: scale pages need both mirror_scale_host and pool_scale, and only with "
+                "scale_page_bytes > 0", op);
+  const size_t need = hyb::offload_ws_bytes(batch, max_blocks, n_slots);
+  if (!workspace || workspace_bytes < need)
+    return fail(HYB_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", op, need,
+                workspace ? workspace_bytes : (size_t)0);
+  hyb::OffloadArgs a{};
+  HYB_TRY(host_alias(op, "mirror_host", mirror_host, &a.mirror));
+  if (scale_page_bytes > 0) HYB_TRY(host_alias(op, "mirror_scale_host", mirror_scale_host, &a.mirror_scale));
+  a.topk = topk;
+  a.batch = batch;
+  a.k = k;
+  a.extra = extra;
+  a.n_extra = n_extra;
+  a.dev_table = dev_table;
+  a.mirror_table = mirror_table;
+  a.max_blocks = max_blocks;
+  a.per_page = entries_per_page;
+  a.slot_owner = slot_owner;
+  a.slot_stamp = slot_stamp;
+  a.n_slots = n_slots;
+  a.step = step;
+  a.n_mirror_pages = n_mirror_pages;
+  a.pool = static_cast<uint8_t*>(pool);
+  a.page_bytes = page_bytes;
+  a.pool_scale = static_cast<uint8_t*>(pool_scale);
+  a.scale_page_bytes = scale_page_bytes;
+  a.result = result;
+  return launch_status(hyb::launch_offload_admit(a, workspace, static_cast<hipStream_t>(stream)), op);
+}
+
+int32_t hyb_offload_write_back(const int32_t* seq_lens, int32_t batch, int32_t ratio,
+                               const int32_t* dev_table, const int32_t* mirror_table,
+                               int32_t max_blocks, int32_t entries_per_page, int32_t n_slots,
+                               const void* pool, int64_t page_bytes, void* mirror_host,
+                               int32_t n_mirror_pages, const void* pool_scale,
+                               void* mirror_scale_host, int64_t scale_page_bytes, void* stream) {
+  const char* op = "hyb_offload_write_back";
+  if (!seq_lens || !dev_table || !mirror_table || !pool || !mirror_host)
+    return fail(HYB_EINVAL, "%s: seq_lens, tables, pool and mirror must be non-NULL", op);
+  if (ratio < 1) return fail(HYB_EINVAL, "%s: ratio %d < 1", op, ratio);
+  if (n_mirror_pages < 1) return fail(HYB_EINVAL, "%s: n_mirror_pages %d < 1", op, n_mirror_pages);
+  HYB_TRY(check_offload_tables(op, batch, max_blocks, entries_per_page, n_slots, page_bytes,
+                               scale_page_bytes, pool, mirror_host));
+  if ((page_bytes / entries_per_page) % 16)
+    return fail(HYB_EINVAL, "%s: entries of %lld bytes must be a multiple of 16", op,
+                (long long)(page_bytes / entries_per_page));
+  if ((scale_page_bytes > 0) != (mirror_scale_host != nullptr && pool_scale != nullptr))
+    return fail(HYB_EINVAL, "%s: scale pages need both mirror_scale_host and pool_scale, and only with "
+                "scale_page_bytes > 0", op);
+  if (batch == 0) return HYB_OK;
+  hyb::OffloadArgs a{};
+  HYB_TRY(host_alias(op, "mirror_host", mirror_host, &a.mirror));
+  if (scale_page_bytes > 0) HYB_TRY(host_alias(op, "mirror_scale_host", mirror_scale_host, &a.mirror_scale));
+  a.batch = batch;
+  a.dev_table = const_cast<int32_t*>(dev_table);
+  a.mirror_table = mirror_table;
+  a.max_blocks = max_blocks;
+  a.per_page = entries_per_page;
+  a.n_slots = n_slots;
+  a.n_mirror_pages = n_mirror_pages;
+  a.pool = const_cast<uint8_t*>(static_cast<const uint8_t*>(pool));
+  a.page_bytes = page_bytes;
+  a.pool_scale = const_cast<uint8_t*>(static_cast<const uint8_t*>(pool_scale));
+  a.scale_page_bytes = scale_page_bytes;
+  return launch_status(hyb::launch_offload_write_back(a, seq_lens, ratio, page_bytes / entries_per_page,
+                                                      scale_page_bytes / entries_per_page,
+                                                      static_cast<hipStream_t>(stream)), op);
+}
+
 static int check_score(const char* op, const void* q_idx, int32_t q_dtype, const float* w,
                        const int32_t* q_pos, int32_t n_q, int32_t n_heads, int32_t max_pos,
                        int32_t window, const hyb_paged* idx_pool, hyb::ScoreArgs* a) {

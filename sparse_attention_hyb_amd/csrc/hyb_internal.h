@@ -222,4 +222,32 @@ hipError_t launch_attention_select(const AttnArgs& a, const SideWork* side, hipS
 bool attention_select_supported(const AttnArgs& a);
 hipError_t launch_attention_compress(const AttnArgs& a, const CompressArgs& c, hipStream_t s);
 
+// Offloaded C4 pool: device-side working-set admission and write-back (offload.hip).
+constexpr int kMaxOffloadSlots = 16384;   // working-set slots at most (one workgroup assigns them)
+struct OffloadArgs {
+  const int32_t* topk;          // [batch][k] selected entries (< 0: none)
+  int32_t batch, k;
+  const int32_t* extra;         // [n_extra] page keys also needed
+  int32_t n_extra;
+  int32_t* dev_table;           // [batch][max_blocks] logical block -> slot, -1 absent
+  const int32_t* mirror_table;  // [batch][max_blocks] logical block -> mirror page
+  int32_t max_blocks, per_page; // entries per page
+  int32_t* slot_owner;          // [n_slots] page key or -1
+  uint32_t* slot_stamp;         // [n_slots] last step that needed the slot (0: never)
+  int32_t n_slots;
+  uint32_t step;
+  uint8_t* mirror;              // device alias of the pinned host pages
+  int32_t n_mirror_pages;
+  uint8_t* pool;                // [n_slots][page_bytes]
+  int64_t page_bytes;
+  uint8_t* mirror_scale;        // device alias of the mirror's scale pages, or NULL
+  uint8_t* pool_scale;
+  int64_t scale_page_bytes;     // 0: no scales
+  int32_t* result;              // [2] misses admitted, misses left out
+};
+size_t offload_ws_bytes(int32_t batch, int32_t max_blocks, int32_t n_slots);
+hipError_t launch_offload_admit(const OffloadArgs& a, void* ws, hipStream_t s);
+hipError_t launch_offload_write_back(const OffloadArgs& a, const int32_t* seq_lens, int ratio,
+                                     int64_t entry_bytes, int64_t scale_bytes, hipStream_t s);
+
 }  // namespace hyb

@@ -11,10 +11,16 @@ on the device.
 Here a page is one logical block of the C4 pool (256 native positions = 64 entries). The working
 set is a device pool of `slots` pages whose block table maps each sequence's logical blocks to
 slots (-1 = not resident), so the attention kernels read it like any pool: the step runs
-`hyb_attn_decode` with `pool()` as its compressed pool. The coordinator is host code: `admit` takes
-the step's top-k rows (on the host), copies the missing pages from the mirror (asynchronous
-host -> device copies on the given stream) and updates the block table; `write_back` copies pages
-the step changed (the one that receives a new entry) back to the mirror.
+`hyb_attn_decode` with `pool()` as its compressed pool. Two coordinators, one per instance:
+  * device (`device=True`): `admit_device` hands the step's top-k rows, still on the device, to
+    `hyb_offload_admit`, which finds the missing pages, picks the victims and copies the pages in
+    the step's stream (no host read-back, nothing on the host but the step counter);
+    `write_back_device` backs each new entry up to the mirror with `hyb_offload_write_back`;
+  * host: `admit` takes the rows on the host (a read-back), decides with numpy and copies the
+    pages with one gather launch; `write_back` copies changed pages back.
+Both follow one rule: the needed pages that miss, in ascending key order, take the least recently
+used slots the step does not need (smallest stamp, then lowest slot), the i-th page the i-th of
+those slots in slot order; so their tables and working sets agree step for step.
 """
 
 from dataclasses import dataclass
@@ -36,7 +42,7 @@ class AdmitStats:
 class C4Offload:
     """Pinned host mirror of a C4 pool plus a device working set of `slots` pages (LRU)."""
 
-    def __init__(self, mirror: PagedTensors, slots: int, device="cuda"):
+    def __init__(self, mirror: PagedTensors, slots: int, device="cuda", device_admission: bool = False):
         if mirror.ratio != 4:
             raise ValueError("the offload takes a C4 pool (ratio 4)")
         if mirror.dtype not in ("bf16", "f32", "fp8"):
@@ -65,6 +71,17 @@ class C4Offload:
         self.owner = np.full(self.slots, -1, dtype=np.int64)   # slot -> page key seq * max_blocks + block
         self.stamp = np.zeros(self.slots, dtype=np.int64)       # last step that needed the slot's page
         self.clock = 0
+        self.device_admission = bool(device_admission)
+        if self.device_admission:
+            # the device coordinator's state: slot owners and stamps, the mirror's table, the
+            # admission workspace (zero before the first call) and its per-step result
+            from . import hyb_offload_workspace_bytes
+            self.owner_dev = torch.full((self.slots,), -1, dtype=torch.int32, device=self.device)
+            self.stamp_dev = torch.zeros(self.slots, dtype=torch.int32, device=self.device)
+            self.mirror_table_dev = mirror.block_table.to(device=self.device, dtype=torch.int32).contiguous()
+            nb = hyb_offload_workspace_bytes(self.table.shape[0], self.table.shape[1], self.slots)
+            self._ws = torch.zeros(nb, dtype=torch.uint8, device=self.device)
+            self.result = torch.zeros(2, dtype=torch.int32, device=self.device)
 
     @property
     def where(self) -> dict:
@@ -115,6 +132,7 @@ class C4Offload:
             slots = np.concatenate([free, victims])
         else:
             slots = free[:miss.size]
+        slots = np.sort(slots)   # the i-th missing page (ascending key) takes the i-th slot
         src = self.table.reshape(-1)[miss]
         if (src < 0).any():
             raise RuntimeError("a selected page is not in the mirror")
@@ -146,6 +164,27 @@ class C4Offload:
             self._table_stage.copy_(torch.from_numpy(self.dev_table_host))
             self.dev_table.copy_(self._table_stage, non_blocking=True)
         return AdmitStats(int(need.size), int(miss.size), nbytes)
+
+    def admit_device(self, topk, extra=None, stream: Optional[torch.cuda.Stream] = None) -> None:
+        """Device coordinator: make every page the device rows topk [B, k] select (and the page
+        keys in `extra`, an int32 device tensor) resident, in `stream` order, with no host
+        read-back. self.result then holds (pages admitted, pages left out)."""
+        from . import hyb_offload_admit
+        if not self.device_admission:
+            raise RuntimeError("this offload was built for host admission")
+        self.clock += 1
+        hyb_offload_admit(topk, self.dev_table, self.mirror_table_dev, self.owner_dev, self.stamp_dev,
+                          self.clock, self.mirror.data, self.data, self._ws, self.result, extra=extra,
+                          entries_per_page=self.per, mirror_scale_host=self.mirror.scale,
+                          pool_scale=self.scale, stream=stream)
+
+    def write_back_device(self, seq_lens, stream: Optional[torch.cuda.Stream] = None) -> None:
+        """Device coordinator: back up the entry each sequence completes at position
+        seq_lens - 1 from its slot to the mirror (asynchronous to the host)."""
+        from . import hyb_offload_write_back
+        hyb_offload_write_back(seq_lens, 4, self.dev_table, self.mirror_table_dev, self.data,
+                               self.mirror.data, entries_per_page=self.per, pool_scale=self.scale,
+                               mirror_scale_host=self.mirror.scale, stream=stream)
 
     def write_back(self, pages: Iterable[Tuple[int, int]],
                    stream: Optional[torch.cuda.Stream] = None) -> None:

@@ -32,14 +32,14 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(hyb.EXPORTS) == names
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hyb_abi_version() == hyb.ABI_VERSION == 3
+    assert lib.hyb_abi_version() == hyb.ABI_VERSION == 4
     assert [lib.hyb_status_str(i).decode() for i in range(5)] == [
         "HYB_OK", "HYB_EINVAL", "HYB_ENOTSUP", "HYB_EWORKSPACE", "HYB_ELAUNCH"]
 

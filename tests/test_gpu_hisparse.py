@@ -82,3 +82,81 @@ def test_gather_pages_refuses_pageable_memory(gpu_lib):
     assert e.value.status == hyb.HYB_EINVAL
     torch.cuda.synchronize()
     assert torch.count_nonzero(dst) == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_device_admission_equals_host(gpu_lib, dtype):
+    """The device coordinator (hyb_offload_admit: misses found, victims chosen and pages copied on
+    the device, no read-back of the top-k) keeps the same block table, slot owners, stamps and
+    resident pages as the host coordinator, step after step, with evictions; and the attention
+    over its working set equals the attention over the resident pool bit for bit."""
+    hyb = gpu_lib
+    from tests.test_gpu_parity import gpu_decode, gpu_topk
+    lens = [20000, 50000, 131072, 7000]
+    wl = W.sparse_decode(DEV, seed=7, batch=len(lens), ctx=lens, dtype=dtype)
+    mirror = W.PagedTensors(wl.comp.data.cpu().pin_memory(),
+                            None if wl.comp.scale is None else wl.comp.scale.cpu().pin_memory(),
+                            wl.comp.block_table.cpu(), wl.comp.dtype, wl.dim, 4)
+    host = C4Offload(mirror, slots=700)
+    dev = C4Offload(mirror, slots=700, device_admission=True)
+    g = W.generator(97, 0, 0, DEV)
+    evicted = 0
+    for step in range(4):
+        wl.idx_q = W.to_storage(W.randn(tuple(wl.idx_q.shape), g, DEV), "bf16")
+        topk = gpu_topk(hyb, wl)
+        st = host.admit(topk.cpu().numpy())
+        dev.admit_device(topk)
+        want = gpu_decode(hyb, wl, topk)
+        comp = wl.comp
+        wl.comp = dev.pool()
+        got = gpu_decode(hyb, wl, topk)
+        wl.comp = comp
+        torch.cuda.synchronize()
+        assert torch.equal(dev.dev_table, host.dev_table), step
+        owner = dev.owner_dev.cpu().numpy()
+        assert (owner == host.owner).all(), step
+        assert (dev.stamp_dev.cpu().numpy() == host.stamp).all(), step
+        res = dev.result.cpu().tolist()
+        assert res == [st.misses, 0], (step, res, st)
+        used = torch.from_numpy(owner >= 0)
+        assert torch.equal(dev.data.cpu()[used], host.data.cpu()[used]), step
+        if dev.scale is not None:
+            assert torch.equal(dev.scale.cpu()[used], host.scale.cpu()[used]), step
+        assert torch.equal(got, want), step
+        evicted += int(step > 0 and st.misses > 0)
+    assert evicted > 0   # later steps brought pages in over evicted ones
+
+
+def test_device_write_back(gpu_lib):
+    """hyb_offload_write_back copies the entry each sequence completes at its position from its
+    resident slot to the mirror, and leaves sequences that complete none untouched."""
+    hyb = gpu_lib
+    lens = [20000, 50001, 8192]   # (p + 1) % 4 == 0 for sequences 0 and 2
+    wl = W.sparse_decode(DEV, seed=8, batch=len(lens), ctx=lens)
+    mirror = W.PagedTensors(wl.comp.data.cpu().pin_memory(), None, wl.comp.block_table.cpu(),
+                            wl.comp.dtype, wl.dim, 4)
+    before = mirror.data.clone()
+    dev = C4Offload(mirror, slots=64, device_admission=True)
+    mb = wl.comp.block_table.shape[1]
+    keys = [b * mb + ((L // 4 - 1) if L % 4 == 0 else (L // 4)) // 64 for b, L in enumerate(lens)]
+    extra = torch.tensor(keys, dtype=torch.int32, device=DEV)
+    dev.admit_device(None, extra=extra)
+    torch.cuda.synchronize()
+    assert dev.result.cpu().tolist() == [3, 0]
+    g = W.generator(96, 0, 0, DEV)
+    rows = {}
+    for b, L in enumerate(lens):
+        lb = keys[b] - b * mb
+        slot = int(dev.dev_table[b, lb])
+        assert slot >= 0
+        if L % 4 == 0:
+            row = (L // 4 - 1) % 64
+            new = W.to_storage(W.randn((wl.dim,), g, DEV), "bf16")
+            dev.data[slot, row] = new
+            rows[b] = (int(mirror.block_table[b, lb]), row, new.cpu())
+    dev.write_back_device(wl.seq_lens)
+    torch.cuda.synchronize()
+    for b, (mp, row, new) in rows.items():
+        assert torch.equal(mirror.data[mp, row], new), b
+    changed = (mirror.data.view(torch.int16) != before.view(torch.int16)).any(dim=-1).nonzero().tolist()
+    assert sorted(map(tuple, changed)) == sorted((mp, row) for mp, row, _ in rows.values())
