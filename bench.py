@@ -85,12 +85,27 @@ def parse():
 
 
 # ------------------------------------------------------------------------------------------
-def time_loop(torch, step, n_steps, warmup, n_rep):
-    """Runs warm-up steps, then times n_steps steps (cycling n_rep replicas) between two device
-    synchronisations. Returns seconds."""
-    for i in range(warmup):
+WARM_SECONDS = 0.3
+
+
+def warm_up(torch, step, n_min, n_rep):
+    """Untimed steps: at least n_min, and for at least WARM_SECONDS. Coming from idle the GPU runs
+    the first tens of milliseconds of a workload at lower clocks (the same C128 step measured
+    85 us in its first 60 steps and 70 us after about 0.1 s), so a count alone is not enough."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < n_min or time.perf_counter() - t0 < WARM_SECONDS:
         step(i % n_rep)
+        i += 1
+        if i % 32 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+
+
+def time_loop(torch, step, n_steps, warmup, n_rep):
+    """Runs warm-up steps (warm_up), then times n_steps steps (cycling n_rep replicas) between two
+    device synchronisations. Returns seconds."""
+    warm_up(torch, step, warmup, n_rep)
     t0 = time.perf_counter()
     for i in range(n_steps):
         step(i % n_rep)
@@ -103,9 +118,7 @@ def kernel_loop(torch, launch, n, n_rep):
     n back-to-back calls cycling n_rep replicas (three untimed calls first). Back-to-back calls
     include the short gap between two launches, so this errs high against a kernel trace."""
     n = max(50, n)
-    for i in range(3):
-        launch(i % n_rep)
-    torch.cuda.synchronize()
+    warm_up(torch, launch, 3, n_rep)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(n):

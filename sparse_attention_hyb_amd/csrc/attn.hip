@@ -359,6 +359,54 @@ __device__ __forceinline__ bool balanced_piece(const AttnArgs& a, int bid, uint3
 }
 
 
+// A value pinned to scalar registers: the optimiser can no longer trace it back to the kernel's
+// argument segment.
+template <typename T>
+__device__ __forceinline__ T in_sgpr(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "one or two scalar registers");
+  if constexpr (sizeof(T) == 8) {
+    uint64_t u = __builtin_bit_cast(uint64_t, v);
+    asm volatile("" : "+s"(u));
+    return __builtin_bit_cast(T, u);
+  } else {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    asm volatile("" : "+s"(u));
+    return __builtin_bit_cast(T, u);
+  }
+}
+
+// The fields of the window pool (w*) and the compressed pool (c*) that a lane chooses between per
+// key. A per-lane choice between two fields of the kernel argument is otherwise compiled into a
+// vector load from the argument segment at a per-lane address, and the wait for that load also
+// waits for every tile load in flight, which empties the load pipeline on every tile. The
+// compressed pool's data and scales are reached as byte offsets from the window pool's, so that
+// every address still derives from a kernel-argument pointer (global memory: loads stay global
+// loads, counted by the vector-memory counter alone).
+struct KeyPools {
+  int64_t cd_off;        // a.comp.data - a.swa.data, bytes
+  int64_t csc_off;       // a.comp.scale - a.swa.scale, bytes (fp8 pools)
+  int64_t web, ceb;
+  const int32_t* wbt;
+  const int32_t* cbt;
+  int wper, cper, wmb, cmb, wnb, cnb;
+};
+__device__ __forceinline__ KeyPools key_pools(const AttnArgs& a) {
+  KeyPools k;
+  k.cd_off = in_sgpr((int64_t)((uintptr_t)a.comp.data - (uintptr_t)a.swa.data));
+  k.csc_off = in_sgpr((int64_t)((uintptr_t)a.comp.scale - (uintptr_t)a.swa.scale));
+  k.web = in_sgpr(a.swa.entry_bytes);
+  k.ceb = in_sgpr(a.comp.entry_bytes);
+  k.wbt = a.swa.block_table;
+  k.cbt = a.comp.block_table;
+  k.wper = in_sgpr(a.swa.per_block);
+  k.cper = in_sgpr(a.comp.per_block);
+  k.wmb = in_sgpr(a.swa.max_blocks);
+  k.cmb = in_sgpr(a.comp.max_blocks);
+  k.wnb = in_sgpr(a.swa.num_blocks);
+  k.cnb = in_sgpr(a.comp.num_blocks);
+  return k;
+}
+
 // One thread's share of one 32-key tile between its global load and its LDS store: key t/16,
 // chunks t%16 + 16c (c < 4) of the row (bf16: 16 B each; fp8: 8 codes each).
 template <bool kFp8>
@@ -439,6 +487,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0,
   }
   SelRegs sreg;
   if constexpr (kSel) select_issue(a.sel, i, sreg);   // the hand-off loads go out first
+  const KeyPools kp = key_pools(a);
   if (!balanced) qk = query_keys(a, i);
   j_end = min(qk.n_keys, j_end);
   const int tid = threadIdx.x;
@@ -523,26 +572,29 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0,
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
         const bool w = win[r];
-        const int per = w ? a.swa.per_block : a.comp.per_block;
+        const int per = w ? kp.wper : kp.cper;
         const bool gok = r * 512 + tid < nseg && g[r] >= 0 && (w || g[r] < qk.nv);
         lb[r] = gok ? g[r] / per : 0;
-        lok[r] = gok && lb[r] < (w ? a.swa.max_blocks : a.comp.max_blocks);
+        lok[r] = gok && lb[r] < (w ? kp.wmb : kp.cmb);
       }
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
         const bool w = win[r];
-        const int32_t* bt = w ? a.swa.block_table : a.comp.block_table;
-        const int mbk = w ? a.swa.max_blocks : a.comp.max_blocks;
-        phys[r] = bt[(int64_t)qk.seq * mbk + (lok[r] ? lb[r] : 0)];
+        const int mbk = w ? kp.wmb : kp.cmb;
+        const int64_t off = (int64_t)qk.seq * mbk + (lok[r] ? lb[r] : 0);
+        phys[r] = w ? kp.wbt[off] : kp.cbt[off];
       }
       int idxr[kR];
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
         const bool w = win[r];
-        const int per = w ? a.swa.per_block : a.comp.per_block;
-        const int nbk = w ? a.swa.num_blocks : a.comp.num_blocks;
+        const int per = w ? kp.wper : kp.cper;
+        const int nbk = w ? kp.wnb : kp.cnb;
         idxr[r] = (lok[r] && phys[r] >= 0 && phys[r] < nbk) ? phys[r] * per + (g[r] - lb[r] * per) : -1;
-        if (lok[r]) note_bad_page(w ? a.swa : a.comp, phys[r]);
+        if (lok[r] && phys[r] >= nbk) {
+          uint32_t* err = w ? a.swa.err : a.comp.err;   // rare: a corrupt table entry
+          if (err != nullptr) atomicOr(err, kErrBadPage);
+        }
       }
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
@@ -567,9 +619,8 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0,
       const int idx = kidx[jl];
       const bool ok = jraw < nseg && idx >= 0;
       const bool win = (seg + jl) < qk.n_win;
-      const uint8_t* base = win ? a.swa.data : a.comp.data;
-      const int64_t eb = win ? a.swa.entry_bytes : a.comp.entry_bytes;
-      const uint8_t* entry = ok ? base + (int64_t)idx * eb : kZeroRow;
+      const int64_t eb = win ? kp.web : kp.ceb;
+      const uint8_t* entry = ok ? a.swa.data + ((win ? 0 : kp.cd_off) + (int64_t)idx * eb) : kZeroRow;
       // Decode launches read every entry once (nontemporal: streamed past the caches, which a
       // row-gather probe measured 11-15 % faster than plain loads); the one-split form also
       // serves prefill, where the queries of a sequence re-read the same entries from cache.
@@ -588,7 +639,8 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0,
           const u32x2* src = reinterpret_cast<const u32x2*>(row + 128 * c);
           st.v[c] = kDirect ? *src : __builtin_nontemporal_load(src);
         }
-        const float s = reinterpret_cast<const float*>(win ? a.swa.scale : a.comp.scale)[ok ? idx : 0];
+        const float s = *reinterpret_cast<const float*>(
+            reinterpret_cast<const uint8_t*>(a.swa.scale) + ((win ? 0 : kp.csc_off) + 4 * (int64_t)(ok ? idx : 0)));
         st.sc = ok ? s : 0.f;
       }
     };
@@ -727,11 +779,18 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0,
         const int off = 16 * t2 * kRow + 128 * (mb >> 2);
         return lds_tr_pair(ktile + vb[0][mb & 3] + off, ktile + vb[1][mb & 3] + off);
       };
+      // Step s: key half t2 = s / 8, dim block mb = s % 8 (consecutive products accumulate into
+      // different blocks). The A operands are read kAhead steps ahead into a small ring, so the
+      // transposed LDS reads overlap the products instead of each product waiting for its read.
+      constexpr int kAhead = 3;
+      bf16x8 opa[kAhead + 1];
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
+      for (int s = 0; s < kAhead; ++s) opa[s] = trf(s & 7, s >> 3);
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf(mb, t2), pbf[t2], o[mb], 0, 0, 0);
+      for (int s = 0; s < 16; ++s) {
+        if (s + kAhead < 16) opa[(s + kAhead) % (kAhead + 1)] = trf((s + kAhead) & 7, (s + kAhead) >> 3);
+        o[s & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[s % (kAhead + 1)], pbf[s >> 3], o[s & 7], 0, 0, 0);
+      }
     };
 
     if constexpr (kScore) {
@@ -765,12 +824,18 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, CompressArgs c0,
       }
       __syncthreads();
     };
-    for (int t = 0; t < n_tiles; t += 3) {
+    // One exit, at the bottom: an exit from the middle of the body makes the control-flow
+    // structuriser add a path into the loop header on which the stage stored there looks freshly
+    // loaded, and the header's wait then drains every load in flight.
+    int t = 0;
+    for (; t + 3 <= n_tiles; t += 3) {
       iter(t, s2);
-      if (t + 1 >= n_tiles) break;
       iter(t + 1, s0);
-      if (t + 2 >= n_tiles) break;
       iter(t + 2, s1);
+    }
+    if (t < n_tiles) {
+      iter(t, s2);
+      if (t + 1 < n_tiles) iter(t + 1, s0);
     }
   }
   // ---- partials: m and l per head from the score waves; O / l as bf16 [head][dim] (zero for a
