@@ -220,6 +220,31 @@ def c4_sparse(torch, hyb, W, BM, args, peak_meas):
     parts_us = {"step": kernel_loop(torch, step, n, R),
                 "index_score": kernel_loop(torch, score, n, R), "topk": kernel_loop(torch, select, n, R),
                 "attention_combine": kernel_loop(torch, attend, n, R)}
+    # the step with the step before the attention in front (query RMSNorm + RoPE of the new tokens
+    # and their window entries): its waves riding at the end of the indexer's launch, against its
+    # own launch before the step
+    for r, d in enumerate(reps):
+        g = W.generator(4, r, 99, dev)
+        d["q_raw"] = W.to_storage(W.randn((B, 64, 512), g, dev), "bf16")
+        d["kv_new"] = W.to_storage(W.randn((B, 512), g, dev), "bf16")
+        d["prep"] = hyb.prep_call(d["q_raw"], d["kv_new"], d["cu"], d["start"], 1, d["wl"].swa,
+                                  q_out=d["wl"].q)
+
+    def step_prep(r):
+        d = reps[r]
+        wl = d["wl"]
+        hyb.hyb_decode_step(wl.q, wl.seq_lens, L, wl.swa, wl.comp, d["out"], idx_q=wl.idx_q,
+                            idx_w=wl.idx_w, idx_pool=wl.idx_pool, k=wl.k, topk_out=d["topk"],
+                            compress=d["calls"], workspace=d["ws_step"], prep=d["prep"])
+
+    def prep_then_step(r):
+        d = reps[r]
+        hyb.hyb_q_norm_kv_insert(d["q_raw"], d["kv_new"], d["cu"], d["start"], 1, d["wl"].swa,
+                                 q_out=d["wl"].q)
+        step(r)
+
+    prep_us = {"prep_in_indexer_launch": kernel_loop(torch, step_prep, n, R),
+               "prep_launched_first": kernel_loop(torch, prep_then_step, n, R)}
     per_tok = BM.decode_query_bytes(L, ratio=4, sparse=True)
     comp_b = BM.compress_decode_bytes(4) + BM.compress_decode_bytes(4, dim=128)
     step_bytes = B * (per_tok.total + comp_b)
@@ -229,6 +254,7 @@ def c4_sparse(torch, hyb, W, BM, args, peak_meas):
         value=B * args.steps / secs, ms_per_step=ms, step_bytes=step_bytes,
         hbm_frac_step=step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         kernel_us=parts_us,
+        prep=dict(unit="us per step (HIP events over back-to-back steps)", **prep_us),
         roofline=roofline_hbm("score_mfma_reg (indexer scores + top-k hand-off)", score_bytes,
                               parts_us["index_score"], peak_meas, measured_traffic(),
                               handoff_bytes_per_launch=B * BM.handoff_bytes(L),
@@ -735,7 +761,8 @@ def main():
     res, rep0 = c4_sparse(torch, hyb, W, BM, args, peak)
     log(f"C4 sparse decode: {res['value']:.0f} q-tok/s, {res['ms_per_step'] * 1e3:.1f} us/step, "
         f"kernels (us) {json.dumps({k: round(v, 1) for k, v in res['kernel_us'].items()})}")
-    extra = {"hbm_probe": {"measured_peak": peak, "unit": "GB/s", **probe_rates}}
+    extra = {"hbm_probe": {"measured_peak": peak, "unit": "GB/s", **probe_rates},
+             "c4_step_with_query_prep": res.pop("prep")}
     if res.get("graph"):
         extra["c4_sparse_decode_graph"] = res.pop("graph")
     log("C128 dense decode: compressing 32 x 2^20 raw tokens, then timing")

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define HYB_ABI_VERSION 4
+#define HYB_ABI_VERSION 5
 
 /* [vLLM] "vLLM side": one logical block = 256 native (raw) positions for every compression
  * rate, i.e. 256 raw entries, 64 C4 entries or 2 C128 entries. */
@@ -197,6 +197,25 @@ int32_t hyb_q_norm_kv_insert(const void* q, int32_t q_dtype, int32_t n_heads, co
                              int32_t batch, int32_t max_new_tokens, void* q_out,
                              const hyb_paged* swa, int32_t rope_dim, double rope_base, float eps,
                              void* stream);
+
+/* The arguments of one hyb_q_norm_kv_insert call, as one struct (same meaning, layout and rules;
+ * the stream is the caller's of the entry point that takes the struct). */
+typedef struct hyb_prep_call {
+  const void* q;
+  int32_t q_dtype;
+  int32_t n_heads;
+  const void* kv;
+  int32_t kv_dtype;
+  const int32_t* cu_seqlens;
+  const int32_t* start_pos;
+  int32_t batch;
+  int32_t max_new_tokens;
+  void* q_out;
+  const hyb_paged* swa;
+  int32_t rope_dim;
+  double rope_base;
+  float eps;
+} hyb_prep_call;
 
 /* --------------------------------------------------------------------------------------------
  * hyb_gather_pages - fill pages of a device working set from a pinned host mirror in one launch
@@ -423,8 +442,15 @@ int32_t hyb_attn_decode_compress(const void* q, int32_t q_dtype, const int32_t* 
  *     topk_out [batch][k] when that is not NULL, then hyb_attn_decode over those rows;
  *   C128 layer (comp->ratio 128; q_idx, w and idx_pool NULL): hyb_attn_decode, dense;
  *   then the n_compress <= 2 compressor calls compress[0 .. n_compress), as hyb_compress (e.g.
- *     the new tokens into the C4 pool and their indexer-key rows into the indexer-key pool).
- * The result equals those calls made one after another. The compressor calls may run beside the
+ *     the new tokens into the C4 pool and their indexer-key rows into the indexer-key pool);
+ *   and first of all, when prep is not NULL, hyb_q_norm_kv_insert(*prep): the new tokens' query
+ *     RMSNorm + RoPE (into prep->q_out, normally the step's q) and their window entries. On a C4
+ *     layer its waves run as extra workgroups at the end of the indexer's launch, on the compute
+ *     units that the indexer's first finishers leave ([vLLM] "vLLM side": the window insert and
+ *     query prep overlap the indexer); the indexer reads nothing they write, so prep->q_out and
+ *     the window pool's data must not overlap q_idx, w, the indexer-key pool or seq_lens.
+ *     Otherwise it is launched first.
+ * The result equals those calls made one after another (the prep first). The compressor calls may run beside the
  * indexer or the attention: that is exact because nothing else in the step reads what they write
  * (the entry a token at p completes is not visible at p, for window >= ratio) or writes what they
  * read. Their x, state and output pools must not overlap q, out, topk_out or the workspace.
@@ -446,8 +472,8 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
                         const float* w, int32_t idx_heads, const hyb_paged* idx_pool, int32_t k,
                         int32_t* topk_out, int32_t window, float softmax_scale, int32_t rope_dim,
                         double rope_base, void* out, int32_t out_dtype, float* out_scale,
-                        const hyb_compress_call* compress, int32_t n_compress, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        const hyb_prep_call* prep, const hyb_compress_call* compress,
+                        int32_t n_compress, void* workspace, size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------------
  * hyb_attn_prefill - causal attention for a chunk of query tokens: query i of sequence q_seq[i]

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyb.so")
 
 HYB_OK, HYB_EINVAL, HYB_ENOTSUP, HYB_EWORKSPACE, HYB_ELAUNCH = 0, 1, 2, 3, 4
 F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
-ABI_VERSION = 4   # HYB_ABI_VERSION of include/hyb.h that these signatures follow
+ABI_VERSION = 5   # HYB_ABI_VERSION of include/hyb.h that these signatures follow
 POOL_MEAN, POOL_SOFTMAX_GATE = 0, 1
 BLOCK_POSITIONS = 256
 KMAX = 2048
@@ -79,6 +79,25 @@ class hyb_compress_call(ctypes.Structure):
     ]
 
 
+class hyb_prep_call(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("q_dtype", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("kv", ctypes.c_void_p),
+        ("kv_dtype", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("start_pos", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("max_new_tokens", ctypes.c_int32),
+        ("q_out", ctypes.c_void_p),
+        ("swa", ctypes.POINTER(hyb_paged)),
+        ("rope_dim", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+        ("eps", ctypes.c_float),
+    ]
+
+
 _lib = None
 
 _P, _I32, _I64, _SZ, _D, _F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
@@ -113,7 +132,7 @@ _SIGS = {
                                 _I32, _D, _P, _I32, _P, _P, _SZ, _P]),
     "hyb_decode_step_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "hyb_decode_step": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _PP, _PP, _P, _I32, _P, _I32, _PP, _I32,
-                               _P, _I32, _F, _I32, _D, _P, _I32, _P,
+                               _P, _I32, _F, _I32, _D, _P, _I32, _P, ctypes.POINTER(hyb_prep_call),
                                ctypes.POINTER(hyb_compress_call), _I32, _P, _SZ, _P]),
     "hyb_probe_granule": (ctypes.c_uint64, [_I32, _I32]),
     "hyb_probe": (_I32, [_I32, _I32, _I32, _P, _P, ctypes.c_uint64, _P, _P, _I32, _I64, _P, _P]),
@@ -468,6 +487,24 @@ def compress_call(x, cu_seqlens, start_pos, max_new_tokens: int, state, out_pool
     return call
 
 
+def prep_call(q, kv, cu_seqlens, start_pos, max_new_tokens: int, swa_pool, q_out=None,
+              rope_dim: int = 64, rope_base: float = 10000.0, eps: float = 1e-6):
+    """The arguments of one hyb_q_norm_kv_insert call as a hyb_prep_call struct (for
+    hyb_decode_step's prep). q_out defaults to q. Keep the returned object alive until the call is
+    enqueued: it holds the pool descriptor."""
+    q_out = q if q_out is None else q_out
+    if q_out.dtype != q.dtype or q_out.shape != q.shape:
+        raise TypeError("q_out must have q's shape and dtype")
+    d = paged(swa_pool)
+    call = hyb_prep_call(
+        q=_ptr(q), q_dtype=_tdtype(q), n_heads=int(q.shape[1]), kv=_ptr(kv), kv_dtype=_tdtype(kv),
+        cu_seqlens=_ptr(cu_seqlens), start_pos=_ptr(start_pos), batch=int(start_pos.shape[0]),
+        max_new_tokens=int(max_new_tokens), q_out=_ptr(q_out), swa=ctypes.pointer(d),
+        rope_dim=int(rope_dim), rope_base=float(rope_base), eps=float(eps))
+    call._keep = d
+    return call
+
+
 def hyb_decode_step_workspace_bytes(batch: int, n_heads: int, dim: int, max_seq_len: int,
                                     comp_ratio: int, k: int, window: int = 128) -> int:
     return int(load().hyb_decode_step_workspace_bytes(int(batch), int(n_heads), int(dim),
@@ -478,9 +515,11 @@ def hyb_decode_step_workspace_bytes(batch: int, n_heads: int, dim: int, max_seq_
 def hyb_decode_step(q, seq_lens, max_seq_len: int, swa_pool, comp_pool, out, idx_q=None, idx_w=None,
                     idx_pool=None, k: int = 512, topk_out=None, compress=(), window: int = 128,
                     softmax_scale: Optional[float] = None, rope_dim: int = 64,
-                    rope_base: float = 10000.0, workspace=None, out_scale=None, stream=None) -> None:
+                    rope_base: float = 10000.0, workspace=None, out_scale=None, stream=None,
+                    prep=None) -> None:
     """One decode step of a C4 layer (idx_q, idx_w, idx_pool given) or a C128 layer (none), with
-    up to two compressor calls (compress_call(...) structs); see include/hyb.h."""
+    up to two compressor calls (compress_call(...) structs) and optionally the query prep and
+    window insert in front (prep_call(...)); see include/hyb.h."""
     b, h, dim = (int(s) for s in q.shape)
     scale = float(softmax_scale) if softmax_scale is not None else dim ** -0.5
     if workspace is None:
@@ -495,7 +534,8 @@ def hyb_decode_step(q, seq_lens, max_seq_len: int, swa_pool, comp_pool, out, idx
         _ptr(idx_q), _tdtype(idx_q) if idx_q is not None else BF16, _ptr(idx_w),
         int(idx_q.shape[1]) if idx_q is not None else 0, ctypes.byref(di) if di is not None else None,
         int(k), _ptr(topk_out), int(window), scale, int(rope_dim), float(rope_base), _ptr(out),
-        _odtype(out, out_scale), _ptr(out_scale), arr, len(calls), _ptr(workspace),
+        _odtype(out, out_scale), _ptr(out_scale), ctypes.byref(prep) if prep is not None else None,
+        arr, len(calls), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 

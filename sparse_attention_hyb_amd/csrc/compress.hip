@@ -91,94 +91,11 @@ __global__ __launch_bounds__(64 * kInsertWaves) void swa_insert_fp8_kernel(Compr
   store_quantized<2, 16>(a.out, idx, lane, npairs, y);
 }
 
-// Fused step before the attention for new tokens ([vLLM] "vLLM side": fused Q-norm + KV RoPE +
-// K insert): per token, n_heads waves RMS-normalise and rotate one query head each, and one more
-// wave rotates the token's K=V row into the window pool (quantised for an FP8_E4M3 pool). A wave
-// holds its whole row (dim <= 2048: up to 16 element pairs per lane) before it writes, so q_out
-// may be q.
-template <typename T>
-__device__ __forceinline__ void store_pair_t(T* row, int d, float x0, float x1) {
-  if constexpr (sizeof(T) == 4) {
-    *reinterpret_cast<float2*>(row + d) = make_float2(x0, x1);
-  } else {
-    *reinterpret_cast<uint32_t*>(row + d) = pack_bf16x2(x0, x1);
-  }
-}
-
+// Fused step before the attention for new tokens (q_norm_kv_wave in compress_dev.h): kInsertWaves
+// of its waves per workgroup, workgroup row b = sequence b.
 template <typename TQ, typename TK>
 __global__ __launch_bounds__(64 * kInsertWaves) void q_norm_kv_insert_kernel(QNormArgs a) {
-  const CompressArgs& c = a.kv;
-  const int b = blockIdx.y;
-  const int roles = a.n_heads + 1;
-  const int wv = blockIdx.x * kInsertWaves + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int i = wv / roles, role = wv % roles;
-  const int c0 = c.cu_seqlens[b];
-  if (i >= c.cu_seqlens[b + 1] - c0) return;   // whole waves
-  const int t = c.start_pos[b] + i;
-  const int64_t tok = c0 + i;
-  const int D = c.out.dim;
-  const int npairs = D / 2;
-  const int rope_lo = D - c.rope_dim;
-  float y[16][2];
-  if (role < a.n_heads) {
-    const TQ* row = reinterpret_cast<const TQ*>(a.q) + (tok * a.n_heads + role) * D;
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int pi = lane + 64 * j;
-      float2 v = make_float2(0.f, 0.f);
-      if (pi < npairs) v = load_pair<TQ>(row, 2 * pi);
-      y[j][0] = v.x;
-      y[j][1] = v.y;
-      ss = fmaf(v.x, v.x, fmaf(v.y, v.y, ss));
-    }
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
-    TQ* orow = reinterpret_cast<TQ*>(a.q_out) + (tok * a.n_heads + role) * D;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int pi = lane + 64 * j;
-      if (pi < npairs) {
-        float y0 = y[j][0] * inv, y1 = y[j][1] * inv;
-        const int d = 2 * pi;
-        if (d >= rope_lo) {
-          float cs, sn;
-          rope_cs_theta((double)t, c.theta[(d - rope_lo) >> 1], &cs, &sn);
-          const float z0 = y0 * cs - y1 * sn;
-          const float z1 = y0 * sn + y1 * cs;
-          y0 = z0;
-          y1 = z1;
-        }
-        store_pair_t<TQ>(orow, d, y0, y1);
-      }
-    }
-  } else {
-    const int64_t idx = entry_index(c.out, b, t);
-    if (idx < 0) return;
-    const TK* row = reinterpret_cast<const TK*>(c.x) + tok * D;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int pi = lane + 64 * j;
-      float2 v = make_float2(0.f, 0.f);
-      if (pi < npairs) {
-        v = load_pair<TK>(row, 2 * pi);
-        const int d = 2 * pi;
-        if (d >= rope_lo) {
-          float cs, sn;
-          rope_cs_theta((double)t, c.theta[(d - rope_lo) >> 1], &cs, &sn);
-          const float z0 = v.x * cs - v.y * sn;
-          const float z1 = v.x * sn + v.y * cs;
-          v.x = z0;
-          v.y = z1;
-        }
-        if (c.out.dtype != FP8) store_pair(c.out, idx, d, v.x, v.y);
-      }
-      y[j][0] = v.x;
-      y[j][1] = v.y;
-    }
-    if (c.out.dtype == FP8) store_quantized<2, 16>(c.out, idx, lane, npairs, y);
-  }
+  q_norm_kv_wave<TQ, TK>(a, blockIdx.y, blockIdx.x * kInsertWaves + (threadIdx.x >> 6), threadIdx.x & 63);
 }
 
 namespace {

@@ -255,6 +255,32 @@ int attach_workspace(const char* op, AttnCommon* c, void* ws, size_t ws_bytes) {
   return HYB_OK;
 }
 
+// The checks of hyb_q_norm_kv_insert, and its launch arguments.
+int check_prep(const char* op, const hyb_prep_call& p, hyb::QNormArgs* out) {
+  HYB_TRY(check_compress_common(op, p.kv, p.kv_dtype, p.cu_seqlens, p.start_pos, p.batch,
+                                p.max_new_tokens));
+  if (!p.q || !p.q_out) return fail(HYB_EINVAL, "%s: q and q_out must be non-NULL", op);
+  if (!is_plain(p.q_dtype)) return fail(HYB_ENOTSUP, "%s: q_dtype must be F32 or BF16", op);
+  if (p.n_heads <= 0 || p.n_heads > 128)
+    return fail(HYB_EINVAL, "%s: n_heads %d outside [1, 128]", op, p.n_heads);
+  if (!(p.eps >= 0.f) || !std::isfinite(p.eps)) return fail(HYB_EINVAL, "%s: eps must be >= 0", op);
+  hyb::PoolDev ps{};
+  HYB_TRY(check_pool(p.swa, op, "swa", true, false, 1, &ps));
+  if (ps.dim > 2048) return fail(HYB_ENOTSUP, "%s: dim %d > 2048", op, ps.dim);
+  HYB_TRY(check_rope(op, p.rope_dim, p.rope_base, ps.dim));
+  hyb::QNormArgs& a = *out;
+  a = hyb::QNormArgs{};
+  a.kv = hyb::CompressArgs{p.kv, p.kv_dtype, nullptr, p.cu_seqlens, p.start_pos, p.batch,
+                           p.max_new_tokens, nullptr, nullptr, 0, ps, p.rope_dim, p.rope_base, 0.f, {}};
+  fill_theta(&a.kv, p.rope_dim, p.rope_base);
+  a.q = p.q;
+  a.q_dtype = p.q_dtype;
+  a.q_out = p.q_out;
+  a.n_heads = p.n_heads;
+  a.eps = p.eps;
+  return HYB_OK;
+}
+
 size_t attn_ws(int32_t n_q, int32_t n_heads, int32_t dim, int64_t max_pos, int32_t ratio,
                int32_t k, int32_t window, bool balanced) {
   if (n_q <= 0 || n_heads <= 0 || dim <= 0 || window <= 0 || max_pos < 0 ||
@@ -337,25 +363,11 @@ int32_t hyb_q_norm_kv_insert(const void* q, int32_t q_dtype, int32_t n_heads, co
                              const hyb_paged* swa, int32_t rope_dim, double rope_base, float eps,
                              void* stream) {
   const char* op = "hyb_q_norm_kv_insert";
-  HYB_TRY(check_compress_common(op, kv, kv_dtype, cu_seqlens, start_pos, batch, max_new_tokens));
-  if (!q || !q_out) return fail(HYB_EINVAL, "%s: q and q_out must be non-NULL", op);
-  if (!is_plain(q_dtype)) return fail(HYB_ENOTSUP, "%s: q_dtype must be F32 or BF16", op);
-  if (n_heads <= 0 || n_heads > 128) return fail(HYB_EINVAL, "%s: n_heads %d outside [1, 128]", op, n_heads);
-  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(HYB_EINVAL, "%s: eps must be >= 0", op);
-  hyb::PoolDev ps{};
-  HYB_TRY(check_pool(swa, op, "swa", true, false, 1, &ps));
-  if (ps.dim > 2048) return fail(HYB_ENOTSUP, "%s: dim %d > 2048", op, ps.dim);
-  HYB_TRY(check_rope(op, rope_dim, rope_base, ps.dim));
-  if (batch == 0 || max_new_tokens == 0) return HYB_OK;
+  const hyb_prep_call p{q, q_dtype, n_heads, kv, kv_dtype, cu_seqlens, start_pos, batch,
+                        max_new_tokens, q_out, swa, rope_dim, rope_base, eps};
   hyb::QNormArgs a{};
-  a.kv = hyb::CompressArgs{kv, kv_dtype, nullptr, cu_seqlens, start_pos, batch, max_new_tokens,
-                           nullptr, nullptr, 0, ps, rope_dim, rope_base, 0.f, {}};
-  fill_theta(&a.kv, rope_dim, rope_base);
-  a.q = q;
-  a.q_dtype = q_dtype;
-  a.q_out = q_out;
-  a.n_heads = n_heads;
-  a.eps = eps;
+  HYB_TRY(check_prep(op, p, &a));
+  if (batch == 0 || max_new_tokens == 0) return HYB_OK;
   return launch_status(hyb::launch_q_norm_kv_insert(a, static_cast<hipStream_t>(stream)), op);
 }
 
@@ -733,8 +745,8 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
                         const float* w, int32_t idx_heads, const hyb_paged* idx_pool, int32_t k,
                         int32_t* topk_out, int32_t window, float softmax_scale, int32_t rope_dim,
                         double rope_base, void* out, int32_t out_dtype, float* out_scale,
-                        const hyb_compress_call* compress, int32_t n_compress, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        const hyb_prep_call* prep, const hyb_compress_call* compress,
+                        int32_t n_compress, void* workspace, size_t workspace_bytes, void* stream) {
   const char* op = "hyb_decode_step";
   if (!seq_lens) return fail(HYB_EINVAL, "%s: seq_lens is NULL", op);
   if (max_seq_len < 1) return fail(HYB_EINVAL, "%s: max_seq_len %d < 1", op, max_seq_len);
@@ -759,15 +771,22 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
                           max_pos, !sparse, &c));
   hyb::CompressArgs ca[2];
   for (int j = 0; j < n_compress; ++j) HYB_TRY(check_compress(op, compress[j], &ca[j]));
+  hyb::QNormArgs pa{};
+  if (prep) HYB_TRY(check_prep(op, *prep, &pa));
+  const bool has_prep = prep && prep->batch > 0 && prep->max_new_tokens > 0;
   const size_t need = step_ws_bytes(batch, n_heads, c.args.dim, max_seq_len, comp->ratio, k, window);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(HYB_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", op, need,
                 workspace ? workspace_bytes : (size_t)0);
-  if (batch == 0) return HYB_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (batch == 0) {
+    if (has_prep) return launch_status(hyb::launch_q_norm_kv_insert(pa, st), op);
+    return HYB_OK;
+  }
   char* ws = static_cast<char*>(workspace);
   hyb::SideWork side{};
   int n_side = 0;
+  bool prep_done = false;
   bool done[2] = {false, false};
   bool fused = false;   // C4: the attention workgroups select their rows themselves
   if (sparse) {
@@ -800,8 +819,10 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
     }
     // compressor calls that four waves can run ride along with the attention (fused selection)
     // or with the indexer's one-query kernel
+    // (the one-query kernel runs only when some query sees a compressed entry)
     const bool one_query_kernel = sa.n_heads == 64 && sa.pool.dim == 128 && sa.q_dtype == HYB_BF16 &&
-                                  (sa.pool.dtype == HYB_BF16 || sa.pool.dtype == HYB_FP4_E2M1);
+                                  (sa.pool.dtype == HYB_BF16 || sa.pool.dtype == HYB_FP4_E2M1) &&
+                                  visible(max_pos, sa.pool.ratio, window) > 0;
     for (int j = 0; j < n_compress && (one_query_kernel || fused); ++j) {
       if (hyb::compress_fusable(ca[j])) {
         side.c[n_side] = ca[j];
@@ -810,7 +831,21 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
         done[j] = true;
       }
     }
-    HYB_TRY(launch_status(hyb::launch_index_score(sa, st, n_side && !fused ? &side : nullptr), op));
+    // the indexer's one-query kernel carries the compressor calls unless the attention does, and
+    // the prep's waves (four per workgroup) at the end of its grid
+    hyb::SideWork iside{};
+    if (n_side && !fused) iside = side;
+    if (has_prep && one_query_kernel) {
+      iside.prep = pa;
+      iside.prep_gx = (int32_t)(((int64_t)pa.kv.max_new_tokens * (pa.n_heads + 1) + 3) / 4);
+      iside.n_prep = iside.prep_gx * pa.kv.batch;
+      prep_done = true;
+    } else if (has_prep) {
+      HYB_TRY(launch_status(hyb::launch_q_norm_kv_insert(pa, st), op));
+      prep_done = true;
+    }
+    const bool any_side = iside.n[0] + iside.n[1] + iside.n_prep > 0;
+    HYB_TRY(launch_status(hyb::launch_index_score(sa, st, any_side ? &iside : nullptr), op));
   }
   if (sparse && !fused) {
     const int64_t ld = (int64_t)score_ld((int32_t)max_pos, window, sa.pool.ratio);
@@ -832,6 +867,7 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
     c.args.topk = topk;
     c.args.k = k;
   }
+  if (has_prep && !prep_done) HYB_TRY(launch_status(hyb::launch_q_norm_kv_insert(pa, st), op));
   HYB_TRY(attach_workspace(op, &c, ws, workspace_bytes - (size_t)(ws - static_cast<char*>(workspace))));
   c.args.qd = hyb::QueryDev{seq_lens, nullptr, nullptr};
   int first = -1;   // a C128 layer's first pending call rides along with the combine

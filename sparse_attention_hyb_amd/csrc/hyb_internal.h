@@ -57,16 +57,6 @@ struct CompressArgs {
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 
-// Up to two compressor calls riding along as extra workgroups of another launch (the indexer's or
-// the attention's): n[j] workgroups for call j, or 0. A call runs there only when nothing else in
-// that launch reads what it writes or writes what it reads. Kernels take the two calls as two
-// separate arguments (c0, c1): an array indexed at run time would be copied to scratch memory.
-struct SideWork {
-  CompressArgs c[2];
-  int32_t n[2];
-};
-hipError_t launch_swa_insert(const CompressArgs& a, hipStream_t s);
-
 // Query RMSNorm + RoPE of new tokens, with their window entries (kv: the tokens' K=V rows in x,
 // their window pool in out, positions and RoPE as in the insert).
 struct QNormArgs {
@@ -77,6 +67,21 @@ struct QNormArgs {
   int32_t n_heads;
   float eps;
 };
+// Up to two compressor calls riding along as extra workgroups of another launch (the indexer's or
+// the attention's): n[j] workgroups for call j, or 0. A call runs there only when nothing else in
+// that launch reads what it writes or writes what it reads. Kernels take the two calls as two
+// separate arguments (c0, c1): an array indexed at run time would be copied to scratch memory.
+struct SideWork {
+  CompressArgs c[2];
+  int32_t n[2];
+  // the step before the attention (query RMSNorm + RoPE and window insert) riding along with the
+  // indexer: n_prep workgroups of four of its waves, prep_gx per sequence
+  QNormArgs prep;
+  int32_t n_prep;
+  int32_t prep_gx;
+};
+hipError_t launch_swa_insert(const CompressArgs& a, hipStream_t s);
+
 hipError_t launch_q_norm_kv_insert(const QNormArgs& a, hipStream_t s);
 // n pages of page_bytes: dst + dst_page[j] * page_bytes <- src_dev + src_page[j] * page_bytes,
 // skipping every j whose source page is outside [0, n_src) or destination page outside [0, n_dst)

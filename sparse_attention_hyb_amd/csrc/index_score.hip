@@ -239,7 +239,8 @@ struct KeyFormat<true> {
 
 template <bool kTile, bool kHand, bool kFp4>
 __global__ __launch_bounds__(256, 1) void score_mfma_reg(ScoreArgs a, CompressArgs c0, CompressArgs c1,
-                                                          int n_c0, int n_c1) {
+                                                          int n_c0, int n_c1, QNormArgs prep, int n_prep,
+                                                          int prep_gx) {
   using KF = KeyFormat<kFp4>;
   constexpr int kLoads = KF::kLoads, kDepth = KF::kDepth;
   __shared__ __attribute__((aligned(1024))) uint8_t stage[4][8192];
@@ -260,10 +261,16 @@ __global__ __launch_bounds__(256, 1) void score_mfma_reg(ScoreArgs a, CompressAr
     return;
   }
   bid -= n_c0 + n_c1;
-  const int n_wg = gridDim.x - n_c0 - n_c1;
+  const int n_wg = gridDim.x - n_c0 - n_c1 - n_prep;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (bid >= n_wg) {   // the step before the attention, last in the grid: its workgroups take the
+                       // compute units that the indexer's first finishers leave
+    const int k = bid - n_wg;
+    q_norm_kv_wave_any(prep, k / prep_gx, (k % prep_gx) * 4 + wave, lane);
+    return;
+  }
   const int col = lane & 31;
   const int hf = lane >> 5;
   const int max_nv = n_visible(a.max_pos, a.pool.ratio, a.window);
@@ -750,7 +757,7 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s, const SideWork*
                          : 0;
   SideWork none{};
   const SideWork& sw = side ? *side : none;
-  const int n_side = sw.n[0] + sw.n[1];
+  const int n_side = sw.n[0] + sw.n[1] + sw.n_prep;
   if (n_side > 0 && (max_nv == 0 || a.n_q == 0 || (a.pool.dtype != BF16 && a.pool.dtype != FP4) || a.n_heads != kMfmaHeads ||
                      a.pool.dim != kMfmaDim || a.q_dtype != BF16 || (a.qd.q_seq && a.n_q >= kMultiMinQueries)))
     return hipErrorInvalidValue;   // the caller offers side work only to the one-query bf16 kernel
@@ -771,7 +778,8 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s, const SideWork*
       const dim3 g1(n_side + (items < kIndexWorkgroups ? items : kIndexWorkgroups));
       const bool tile = a.pool.per_block >= 32, hand = a.part_hist != nullptr;
 #define HYB_SCORE_REG(T, H, F) \
-  hipLaunchKernelGGL((score_mfma_reg<T, H, F>), g1, dim3(256), 0, s, a, sw.c[0], sw.c[1], sw.n[0], sw.n[1])
+  hipLaunchKernelGGL((score_mfma_reg<T, H, F>), g1, dim3(256), 0, s, a, sw.c[0], sw.c[1], sw.n[0], sw.n[1], \
+                     sw.prep, sw.n_prep, sw.prep_gx)
       if (a.pool.dtype == BF16) {
         if (tile && hand) HYB_SCORE_REG(true, true, false);
         else if (tile) HYB_SCORE_REG(true, false, false);

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hyb_abi_version() == hyb.ABI_VERSION == 4
+    assert lib.hyb_abi_version() == hyb.ABI_VERSION == 5
     assert [lib.hyb_status_str(i).decode() for i in range(5)] == [
         "HYB_OK", "HYB_EINVAL", "HYB_ENOTSUP", "HYB_EWORKSPACE", "HYB_ELAUNCH"]
 
@@ -323,17 +323,31 @@ def test_decode_step_validation(lib):
     attention partials)."""
     swa, c4, c128, ip = pool(ratio=1), pool(ratio=4), pool(ratio=128), pool(dim=128, ratio=4)
 
-    def call(comp=c4, q_idx=FAKE, n_comp=0, ws=1 << 40, k=512, idx=ip):
+    def call(comp=c4, q_idx=FAKE, n_comp=0, ws=1 << 40, k=512, idx=ip, prep=None):
         return lib.hyb_decode_step(FAKE, hyb.BF16, FAKE, 4, 64, 100000, ctypes.byref(swa),
                                    ctypes.byref(comp), q_idx, hyb.BF16, FAKE, 64,
                                    ctypes.byref(idx) if idx is not None else None, k, None, 128,
-                                   0.04, 64, 1e4, FAKE, hyb.BF16, None, None, n_comp, FAKE, ws, None)
+                                   0.04, 64, 1e4, FAKE, hyb.BF16, None,
+                                   ctypes.byref(prep) if prep is not None else None, None, n_comp,
+                                   FAKE, ws, None)
+
+    def prep(**kw):   # a query prep call in front of the step (hyb_q_norm_kv_insert's checks)
+        a = dict(q=FAKE, q_dtype=hyb.BF16, n_heads=64, kv=FAKE, kv_dtype=hyb.BF16, cu_seqlens=FAKE,
+                 start_pos=FAKE, batch=4, max_new_tokens=1, q_out=FAKE, swa=ctypes.pointer(swa),
+                 rope_dim=64, rope_base=1e4, eps=1e-6)
+        a.update(kw)
+        return hyb.hyb_prep_call(**a)
 
     assert call(q_idx=None) == hyb.HYB_EINVAL                 # C4 without the indexer
     assert call(comp=c128) == hyb.HYB_EINVAL                  # C128 with an indexer query
     assert call(n_comp=3) == hyb.HYB_EINVAL
     assert call(n_comp=1) == hyb.HYB_EINVAL                   # compress NULL
     assert call(k=0) == hyb.HYB_EINVAL
+    assert call(prep=prep(n_heads=0)) == hyb.HYB_EINVAL        # the prep is checked as its own call
+    assert call(prep=prep(q_out=None)) == hyb.HYB_EINVAL
+    assert call(prep=prep(eps=-1.0)) == hyb.HYB_EINVAL
+    assert call(prep=prep(rope_dim=3)) == hyb.HYB_EINVAL
+    assert lib.hyb_last_error().decode().startswith("hyb_decode_step")
     need = lib.hyb_decode_step_workspace_bytes(4, 64, 512, 100000, 4, 512, 128)
     # the step holds the indexer's hand-off (with its zero block) and the attention's partials
     assert need > lib.hyb_index_topk_workspace_bytes(4, 100000 - 1, 128, 4) + 4 * 5 * 64 * 512 * 2

@@ -194,3 +194,94 @@ def test_c4_step_selects_in_attention_repeatedly(gpu_lib, case):
     for b in short:   # rows no longer than k: every entry in order, then -1
         nv = O.n_visible(lens[b] - 1, 4, 128)
         assert list(topk[b].cpu().numpy()) == list(range(nv)) + [-1] * (wl.k - nv)
+
+
+@pytest.mark.parametrize("layer", ["c4", "c4_fp8", "c128"])
+def test_decode_step_with_prep_equals_separate_calls(gpu_lib, layer):
+    """The step before the attention given to hyb_decode_step (query RMSNorm + RoPE of the new
+    tokens into q, their window entries at p): on a C4 layer its waves ride at the end of the
+    indexer's launch, on a C128 layer it is launched first. Output, top-k rows, rotated queries
+    and window pool equal hyb_q_norm_kv_insert followed by the step, bit for bit, compressor calls
+    included; the query rows equal the oracle's RMSNorm + RoPE, and a sampled C4 sequence's output
+    the oracle's attention over the pools the prep wrote."""
+    hyb = gpu_lib
+    lens = [4096, 8191, 20000, 65535, 131072]
+    dtype = "fp8" if layer == "c4_fp8" else "bf16"
+    sparse = layer != "c128"
+    wl = (W.sparse_decode(DEV, seed=41, batch=len(lens), ctx=lens, dtype=dtype) if sparse
+          else W.dense_decode(DEV, seed=42, batch=len(lens), ctx=lens))
+    B, D, L = wl.batch, wl.dim, wl.max_seq_len
+    g = W.generator(96, 0, 0, DEV)
+    q_raw = W.to_storage(W.randn((B, 64, D), g, DEV), "bf16")
+    kv = W.to_storage(W.randn((B, D), g, DEV), "bf16")
+    x = W.to_storage(W.randn((B, D), g, DEV), "bf16")
+    ring = _rings(B, D, 4 if sparse else 128, torch.bfloat16, g)
+    cu = torch.arange(0, B + 1, dtype=I32, device=DEV)
+    start = (wl.seq_lens - 1).contiguous()
+    swa0 = _clone_pool(wl.swa)
+    comp0, ring0 = _clone_pool(wl.comp), ring.clone()
+    ratio = 4 if sparse else 128
+
+    def pools_back():
+        wl.swa.data.copy_(swa0.data)
+        if wl.swa.scale is not None:
+            wl.swa.scale.copy_(swa0.scale)
+        wl.comp.data.copy_(comp0.data)
+        if wl.comp.scale is not None:
+            wl.comp.scale.copy_(comp0.scale)
+        ring.copy_(ring0)
+
+    def run(q, out, topk, prep):
+        calls = [hyb.compress_call(x, cu, start, 1, ring, wl.comp, 64)]
+        ws = torch.zeros(hyb.hyb_decode_step_workspace_bytes(B, 64, D, L, ratio, wl.k if sparse else 0),
+                         dtype=torch.uint8, device=DEV)
+        if sparse:
+            hyb.hyb_decode_step(q, wl.seq_lens, L, wl.swa, wl.comp, out, idx_q=wl.idx_q, idx_w=wl.idx_w,
+                                idx_pool=wl.idx_pool, k=wl.k, topk_out=topk, compress=calls, workspace=ws,
+                                prep=prep)
+        else:
+            hyb.hyb_decode_step(q, wl.seq_lens, L, wl.swa, wl.comp, out, compress=calls, workspace=ws,
+                                prep=prep)
+
+    # separate calls: the prep, then the step
+    q_a = torch.empty_like(q_raw)
+    out_a = torch.empty_like(q_raw)
+    topk_a = torch.full((B, wl.k), -7, dtype=I32, device=DEV)
+    hyb.hyb_q_norm_kv_insert(q_raw, kv, cu, start, 1, wl.swa, q_out=q_a)
+    run(q_a, out_a, topk_a, None)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (q_a, out_a, topk_a, wl.swa.data, wl.comp.data, ring)]
+    swa_prepped = _clone_pool(wl.swa)
+    # one call with the prep
+    pools_back()
+    q_b = torch.full_like(q_raw, 3.0)
+    out_b = torch.empty_like(q_raw)
+    topk_b = torch.full((B, wl.k), -9, dtype=I32, device=DEV)
+    run(q_b, out_b, topk_b, hyb.prep_call(q_raw, kv, cu, start, 1, wl.swa, q_out=q_b))
+    torch.cuda.synchronize()
+    got = [q_b, out_b, topk_b, wl.swa.data, wl.comp.data, ring]
+    for n, (a, b) in enumerate(zip(want, got)):
+        if not sparse and n == 2:
+            continue   # no top-k on a C128 layer
+        assert torch.equal(a, b), n
+    if wl.swa.scale is not None:
+        assert torch.equal(swa_prepped.scale, wl.swa.scale)
+    assert not torch.equal(want[3], swa0.data)   # the window entries at p were written
+
+    # the query rows against the oracle's RMSNorm + RoPE at each p
+    qo = to_f64(q_b)
+    for s in (0, 3):   # bf16 rows: within half a bf16 ulp of the float64 values
+        want_q = O.q_norm_rope(to_f64(q_raw[s:s + 1]), [lens[s] - 1], 64, 1e4, 1e-6)[0]
+        assert np.all(np.abs(qo[s] - want_q) <= 2.0 ** -8 * np.abs(want_q) + 1e-5)
+    if sparse and dtype == "bf16":
+        swa_o, comp_o, idx_o = to_oracle_pool(swa_prepped), to_oracle_pool(comp0), to_oracle_pool(wl.idx_pool)
+        iq, iw = to_f64(wl.idx_q), wl.idx_w.cpu().double().numpy()
+        s = 2
+        p = lens[s] - 1
+        keys = O.pool_entries(idx_o, s, range(O.n_visible(p, 4, 128)))
+        sc = O.indexer_scores(iq[s], iw[s], keys)
+        sel = O.topk_select(sc, wl.k)
+        check_topk_set(topk_b[s].cpu().numpy(), sel, sc, topk_delta(iq[s], iw[s], keys), wl.k)
+        if list(topk_b[s].cpu().numpy()) == list(sel):
+            o = O.hybrid_query(qo[s], p, s, swa_o, comp_o, 128, 1 / math.sqrt(D), 64, 1e4, sel)
+            assert_abs_close(to_f64(out_b[s]), o)
