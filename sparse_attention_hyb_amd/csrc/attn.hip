@@ -40,6 +40,7 @@ constexpr int kMaxSplit = 64;
 constexpr int kBalancedSlots = 256;         // balanced plan: slots beyond one per query
 constexpr int kBalancedMaxQueries = 2048;   // balanced plan: queries per launch at most
 constexpr int kBalancedMinTiles = 4;        // balanced plan: 32-key tiles per piece at least
+constexpr int kShareCands = 8;              // balanced plan: piece sizes tried at once
 constexpr int kMaxRopePairs = 64;   // rope_dim <= 128
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -283,7 +284,7 @@ __device__ __forceinline__ int xcd_logical(int L, int total) {
 // otherwise. Its query i, piece and key range [j_begin, j_end) (j_end not yet clamped to the
 // query's keys). The first piece's workgroup records (first_q, ns_q) in qplan for the combine.
 // qk: query i's keys (its position kept in LDS from the plan: no second read of its length).
-// lds: 3 n_q + 21 words.
+// lds: 3 n_q + 27 words.
 __device__ __forceinline__ bool balanced_piece(const AttnArgs& a, int bid, uint32_t* lds, int& i,
                                                int& piece, int& j_begin, int& j_end, int& w,
                                                QueryKeys& qk) {
@@ -292,7 +293,7 @@ __device__ __forceinline__ bool balanced_piece(const AttnArgs& a, int bid, uint3
   int* seq_s = reinterpret_cast<int*>(lds + nq + 1);  // [nq]
   int* pos_s = seq_s + nq;                            // [nq]
   uint32_t* wt = lds + 3 * nq + 1;                    // [16] wave totals of the scan
-  uint32_t* red = wt + 16;                            // [2] T, M
+  uint32_t* red = wt + 16;                            // [2] T, M, [8] piece counts
   uint32_t t4[4], sum = 0, mx = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {   // queries 4 tid .. 4 tid + 3 (n_q <= 2048)
@@ -321,8 +322,14 @@ __device__ __forceinline__ bool balanced_piece(const AttnArgs& a, int bid, uint3
   __syncthreads();
   const uint32_t T = red[0], M = red[1];
   const uint32_t free_slots = (uint32_t)(a.n_slots - nq);
-  const uint32_t share = max(max((uint32_t)kBalancedMinTiles, (T + free_slots - 1) / free_slots),
-                             (M + (uint32_t)a.n_split - 1) / (uint32_t)a.n_split);
+  const uint32_t share0 = max(max((uint32_t)kBalancedMinTiles, (T + free_slots - 1) / free_slots),
+                              (M + (uint32_t)a.n_split - 1) / (uint32_t)a.n_split);
+  // share0 bounds the pieces by T / share0 + n_q <= n_slots, but the pieces beyond one per compute
+  // unit (kBalancedSlots of them, one workgroup each) would run as a second round. When they do not
+  // fit, of kShareCands piece sizes from share0 up to one whose bound is kBalancedSlots
+  // (T / (kBalancedSlots - n_q)), the smallest whose actual piece count fits is taken (the largest
+  // when none does).
+  uint32_t share = share0;
   uint32_t ns4[4], loc = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -331,6 +338,33 @@ __device__ __forceinline__ bool balanced_piece(const AttnArgs& a, int bid, uint3
   }
   uint32_t total = 0;
   uint32_t run = block_scan_excl<512>(loc, wt, &total);
+  const uint32_t room = nq < kBalancedSlots ? (uint32_t)(kBalancedSlots - nq) : 1u;
+  const uint32_t share_hi = max(share0, (T + room - 1) / room);
+  if (total > (uint32_t)kBalancedSlots && share_hi > share0) {   // uniform
+    if (tid < kShareCands) red[2 + tid] = 0u;
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 1; c < kShareCands; ++c) {
+      const uint32_t cand = share0 + ((share_hi - share0) * (uint32_t)c + kShareCands - 2) / (kShareCands - 1);
+      uint32_t cnt = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cnt += (t4[e] + cand - 1) / cand;
+      cnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(cnt), 63);
+      if (lane == 0) atomicAdd(&red[2 + c], cnt);
+    }
+    __syncthreads();
+    share = share_hi;
+    for (int c = kShareCands - 1; c >= 1; --c)
+      if (red[2 + c] <= (uint32_t)kBalancedSlots)
+        share = share0 + ((share_hi - share0) * (uint32_t)c + kShareCands - 2) / (kShareCands - 1);
+    loc = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ns4[e] = (t4[e] + share - 1) / share;
+      loc += ns4[e];
+    }
+    run = block_scan_excl<512>(loc, wt, &total);
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int q = 4 * tid + e;
@@ -1316,7 +1350,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 
 // The fused selection pays off while every part's candidates usually lie among its prefetched
 // pairs: at most kSelFusedParts parts per row (contexts up to 256K tokens at ratio 4), 64 or more
-// pairs per part. Longer rows go through the selection kernel.
+// pairs per part. Longer rows go through the selection kernel (measured: the quantised batch of
+// 64 rows of up to 2^20 tokens took 167 us per C4 step with the selection fused at 16 pairs per
+// part, 136 us with the selection kernel).
 constexpr int kSelFusedParts = kSelPrefetch / 64;
 bool attention_select_supported(const AttnArgs& a) {
   return a.use_mfma && a.sel.pairs != nullptr && a.k <= kMaxTopK && a.n_q <= kRowHistRows &&

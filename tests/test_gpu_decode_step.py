@@ -153,18 +153,20 @@ def _step_no_compress(hyb, wl, topk, out, ws):
                         idx_w=wl.idx_w, idx_pool=wl.idx_pool, k=wl.k, topk_out=topk, workspace=ws)
 
 
-@pytest.mark.parametrize("case", ["mixed", "long", "ties"])
+@pytest.mark.parametrize("case", ["mixed", "long", "ties", "longest"])
 def test_c4_step_selects_in_attention_repeatedly(gpu_lib, case):
     """The C4 step's attention workgroups select their rows from the indexer's hand-off. Over
     three calls with one workspace the rows equal hyb_index_topk's and the outputs
     hyb_attn_decode's bit for bit, and the workspace's leading zero block (per-row counts) is zero
     again after every call. Cases: mixed lengths including rows no longer than k; a 2^18-token row
     (64 parts of 64 prefetched pairs each, which a part's candidates can outrun); dyadic indexer
-    values whose scores tie heavily."""
+    values whose scores tie heavily; a 2^20-token row (256 parts: beyond the fused selection, so the
+    step runs the selection kernel for that batch)."""
     hyb = gpu_lib
     lens = {"mixed": [700, 2100, 2200, 40000, 131072],
             "long": [262144, 150000],
-            "ties": [3000, 70001, 131072]}[case]
+            "ties": [3000, 70001, 131072],
+            "longest": [1 << 20, 300000, 5000]}[case]
     wl = W.sparse_decode(DEV, seed=31, batch=len(lens), ctx=lens)
     if case == "ties":
         g = torch.Generator(device=DEV).manual_seed(12)
