@@ -17,7 +17,10 @@
  *   - Every pointer is a device pointer unless it says "host". The caller owns all memory:
  *     inputs, outputs, pools, block tables, state and workspace. The library never allocates,
  *     frees or synchronises, keeps no global mutable state (apart from a thread-local error
- *     string) and is re-entrant.
+ *     string and the process-wide settings of hyb_set_error_word) and is re-entrant.
+ *   - HYB_LOG set to anything but "" or "0" in the environment (read once, at the first call)
+ *     makes the entry points report on stderr what they launch: attention plans, the parts of
+ *     a decode step and where its side work runs, one line per launch.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
  *   - Return value: HYB_OK, or an error code. All argument checks run on the host before any
  *     HIP call, so a non-OK status means nothing was enqueued and outputs are untouched

@@ -9,6 +9,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <atomic>
 #include <mutex>
 #include <string>
@@ -33,7 +35,28 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+// Host-side launch logging: HYB_LOG set to anything but "" or "0" in the environment (read once,
+// at the first call) makes the entry points report what they launch on stderr, one line each.
+bool log_on() {
+  static const bool on = [] {
+    const char* v = std::getenv("HYB_LOG");
+    return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+void hyb_log(const char* fmt, ...) {
+  if (!log_on()) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[hyb] %s\n", buf);
+}
+
 int launch_status(hipError_t e, const char* what) {
+  hyb_log("%s: launched (%s)", what, e == hipSuccess ? "ok" : hipGetErrorString(e));
   if (e == hipSuccess) return HYB_OK;
   return fail(HYB_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
 }
@@ -251,6 +274,12 @@ int attach_workspace(const char* op, AttnCommon* c, void* ws, size_t ws_bytes) {
   if (c->plan.balanced) {
     c->args.qplan = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + c->plan.qplan_off);
     c->args.n_slots = c->plan.n_slots;
+    hyb_log("%s: attention over %d queries (up to %d keys each), MFMA kernel, balanced plan of %d "
+            "slots cut on the device", op, c->args.n_q, c->args.max_keys, c->plan.n_slots);
+  } else {
+    hyb_log("%s: attention over %d queries (up to %d keys each), %s kernel, %d splits of %d keys",
+            op, c->args.n_q, c->args.max_keys, c->plan.use_mfma ? "MFMA" : "generic",
+            c->plan.n_split, c->plan.chunk);
   }
   return HYB_OK;
 }
@@ -336,7 +365,12 @@ int32_t hyb_compress(const void* x, int32_t x_dtype, const float* gate_logits,
                                rope_base, eps};
   hyb::CompressArgs a;
   HYB_TRY(check_compress(op, call, &a));
-  if (batch == 0 || max_new_tokens == 0) return HYB_OK;
+  if (batch == 0 || max_new_tokens == 0) {
+    hyb_log("%s: %d sequences x %d new tokens: nothing to launch", op, batch, max_new_tokens);
+    return HYB_OK;
+  }
+  hyb_log("%s: %d sequences x up to %d new tokens, ratio %d, dim %d, %s pooling", op, batch,
+          max_new_tokens, a.out.ratio, a.out.dim, a.mode == 1 ? "softmax-gate" : "mean");
   return launch_status(hyb::launch_compress(a, static_cast<hipStream_t>(stream)), op);
 }
 
@@ -786,7 +820,7 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
   char* ws = static_cast<char*>(workspace);
   hyb::SideWork side{};
   int n_side = 0;
-  bool prep_done = false;
+  bool prep_done = false, prep_rides = false;
   bool done[2] = {false, false};
   bool fused = false;   // C4: the attention workgroups select their rows themselves
   if (sparse) {
@@ -839,7 +873,7 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
       iside.prep = pa;
       iside.prep_gx = (int32_t)(((int64_t)pa.kv.max_new_tokens * (pa.n_heads + 1) + 3) / 4);
       iside.n_prep = iside.prep_gx * pa.kv.batch;
-      prep_done = true;
+      prep_done = prep_rides = true;
     } else if (has_prep) {
       HYB_TRY(launch_status(hyb::launch_q_norm_kv_insert(pa, st), op));
       prep_done = true;
@@ -870,6 +904,10 @@ int32_t hyb_decode_step(const void* q, int32_t q_dtype, const int32_t* seq_lens,
   if (has_prep && !prep_done) HYB_TRY(launch_status(hyb::launch_q_norm_kv_insert(pa, st), op));
   HYB_TRY(attach_workspace(op, &c, ws, workspace_bytes - (size_t)(ws - static_cast<char*>(workspace))));
   c.args.qd = hyb::QueryDev{seq_lens, nullptr, nullptr};
+  hyb_log("%s: %s layer, %d sequences, %s%s", op, sparse ? "C4" : "C128", batch,
+          sparse ? (fused ? "selection in the attention workgroups, " : "selection kernel, ") : "",
+          has_prep ? (prep_rides ? "query prep riding with the indexer" : "query prep launched first")
+                   : "no query prep");
   int first = -1;   // a C128 layer's first pending call rides along with the combine
   for (int j = 0; j < n_compress; ++j)
     if (!done[j]) { first = j; break; }

@@ -366,3 +366,24 @@ def test_error_word_needs_a_device():
         pytest.skip("a GPU is present")
     assert st == hyb.HYB_ELAUNCH
     assert lib.hyb_last_error().decode().startswith("hyb_set_error_word")
+
+
+def test_launch_logging_on_request(lib):
+    """HYB_LOG=1 in the environment (read once per process) makes the entry points report what
+    they launch on stderr; unset, they print nothing. A compressor call with no sequences checks
+    its arguments and launches nothing, so this runs without a GPU (in fresh processes)."""
+    import subprocess
+    import sys
+    code = ("import ctypes, sys; sys.path.insert(0, {root!r}); import sparse_attention_hyb_amd as hyb; "
+            "from tests.test_abi import pool, FAKE; lib = hyb.load(); o = pool(ratio=4); "
+            "sys.exit(lib.hyb_compress(FAKE, hyb.BF16, None, FAKE, FAKE, 0, 4, FAKE, None, "
+            "hyb.POOL_MEAN, ctypes.byref(o), 64, 1e4, 1e-6, None))").format(root=ROOT)
+    for value, expect in (("1", True), ("0", False), (None, False)):
+        env = {k: v for k, v in os.environ.items() if k != "HYB_LOG"}
+        if value is not None:
+            env["HYB_LOG"] = value
+        r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                           text=True, timeout=120)
+        assert r.returncode == hyb.HYB_OK, r.stderr
+        logged = "[hyb] hyb_compress: 0 sequences x 4 new tokens: nothing to launch" in r.stderr
+        assert logged == expect, (value, r.stderr)
