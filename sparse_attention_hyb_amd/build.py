@@ -32,8 +32,11 @@ FLAGS = [
 # The attention kernel keeps 128 output accumulators live across the softmax rescale. With the
 # default heuristic the backend parks them in AGPRs and copies all of them to VGPRs and back on
 # every key tile (about 800 v_accvgpr moves per tile loop); forcing the VGPR form of the MFMAs
-# removes those moves (register use drops from 507 to 365, no spills).
-EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# removes those moves (register use drops from 507 to 365, no spills). The indexer's score tiles
+# end in a ReLU-weighted head sum on the VALU: in AGPRs their 32 accumulators took 32
+# v_accvgpr_read per tile and key block (fp4 keys: about a fifth of the loop's VALU work).
+_VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA = {"attn.hip": _VGPR_MFMA, "index_score.hip": _VGPR_MFMA}
 
 
 def hipcc() -> str:
