@@ -60,10 +60,11 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float sc) {
 // so that the selector, once it knows the bin b0 of the k-th largest key, reads only the leading
 // part_hist[b0] pairs of every part. The workgroup's keys are in lkeys[0, P * kScorePartKeys)
 // (index g - base) and its per-part counts in lhist[P][kTopBins], which become bucket cursors;
-// lsorted (P * kScorePartKeys uint2) is scratch. 256 threads.
+// each pair goes straight to its bucket slot in the output (slots from LDS atomics on the cursors;
+// a direct global scatter measured faster than sorting in LDS and copying out). 256 threads.
 template <int P, bool kPacked = false>
 __device__ __forceinline__ void finish_parts(const ScoreArgs& a, int i, int part0, int base, int end,
-                                             const uint32_t* lkeys, uint32_t* lhist, uint2* lsorted,
+                                             const uint32_t* lkeys, uint32_t* lhist,
                                              uint32_t* wtot) {
   static_assert(kTopBins == 4 * 256, "four bins per thread");
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -113,6 +114,8 @@ __device__ __forceinline__ void finish_parts(const ScoreArgs& a, int i, int part
   }
   __syncthreads();
   const int nk = min(P * kScorePartKeys, end - base);
+  uint2* pairs = reinterpret_cast<uint2*>(a.scores) + (int64_t)i * (a.ld / 2) +
+                 (int64_t)part0 * kScorePartKeys;
   for (int j = t; j < nk; j += 256) {
     const uint32_t key = lkeys[j];
     const int q = j / kScorePartKeys;
@@ -124,12 +127,8 @@ __device__ __forceinline__ void finish_parts(const ScoreArgs& a, int i, int part
     } else {
       slot = atomicAdd(&lhist[q * kTopBins + bin], 1u);
     }
-    lsorted[q * kScorePartKeys + slot] = make_uint2(key, (uint32_t)(base + j));
+    pairs[q * kScorePartKeys + slot] = make_uint2(key, (uint32_t)(base + j));   // straight to its bucket
   }
-  __syncthreads();
-  uint2* pairs = reinterpret_cast<uint2*>(a.scores) + (int64_t)i * (a.ld / 2) +
-                 (int64_t)part0 * kScorePartKeys;
-  for (int j = t; j < nk; j += 256) pairs[j] = lsorted[j];
 }
 
 // The hand-off of one part for one query by one wave (no workgroup barrier): the wave's 16-bit
@@ -522,9 +521,8 @@ __global__ __launch_bounds__(256, 1) void score_mfma_reg(ScoreArgs a, CompressAr
         }
       }
     }
-    if constexpr (kHand)   // the stages are free now: the sorted pairs use them
-      finish_parts<kScoreParts>(a, i, base / kScorePartKeys, base, end, lkeys, lhist,
-                                reinterpret_cast<uint2*>(&stage[0][0]), wtot);
+    if constexpr (kHand)
+      finish_parts<kScoreParts>(a, i, base / kScorePartKeys, base, end, lkeys, lhist, wtot);
   }
 }
 
@@ -691,7 +689,6 @@ __global__ __launch_bounds__(256) void score_generic(ScoreArgs a) {
   extern __shared__ float sm[];
   __shared__ uint32_t lhist[kTopBins];
   __shared__ uint32_t lkeys[kScorePartKeys];
-  __shared__ uint2 lsorted[kScorePartKeys];
   __shared__ uint32_t wtot[4];
   const int i = blockIdx.y;
   int seq, p;
@@ -748,7 +745,7 @@ __global__ __launch_bounds__(256) void score_generic(ScoreArgs a) {
     }
   }
   if (a.part_hist)
-    finish_parts<1>(a, i, blockIdx.x, base, min(nv, base + kScorePartKeys), lkeys, lhist, lsorted, wtot);
+    finish_parts<1>(a, i, blockIdx.x, base, min(nv, base + kScorePartKeys), lkeys, lhist, wtot);
 }
 
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t s, const SideWork* side) {
